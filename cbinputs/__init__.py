@@ -1,0 +1,335 @@
+"""Seeded synthetic inputs for the blended prefill (model shapes, weights, chunk
+workloads, cached KV, block tables).
+
+This module produces inputs only.  It holds none of the method's arithmetic:
+no RoPE, no attention, no deviation, no selection.  Both the CPU oracle and the
+GPU path draw their inputs from here, so both see exactly the same numbers.
+
+Conventions
+-----------
+* Linear weights are stored ``[out_features][in_features]`` (row-major), so a
+  projection of row vectors ``a`` is ``a @ W.T``.  ``w_qkv`` stacks Q, K, V
+  rows; ``w_gate_up`` stacks gate rows then up rows.
+* bf16 models draw every weight in fp32 and round it to bf16 (round to nearest
+  even); the values are returned as fp32 arrays holding bf16-representable
+  numbers, so a consumer may upcast them without loss.
+* Every tensor has its own ``SeedSequence`` stream keyed by (config seed,
+  layer, tensor id), so any single layer can be regenerated on its own.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "ModelShape", "Workload", "SHAPES", "WORKLOADS", "make_workload",
+    "layer_weights", "global_weights", "model_weights", "synthetic_chunk_kv",
+    "to_bf16_values", "bf16_bits", "recompute_count", "paged_layout",
+]
+
+
+# ----------------------------------------------------------------------------
+# numeric storage helpers (input quantisation only)
+# ----------------------------------------------------------------------------
+
+def to_bf16_values(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); return fp32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).reshape(np.shape(x))
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of fp32 values that are already bf16-representable."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return (u >> 16).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# model shapes
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class ModelShape:
+    name: str
+    n_layers: int
+    d_model: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    d_ff: int
+    vocab: int
+    rope_theta: float
+    rms_eps: float = 1e-5
+    dtype: str = "bf16"          # storage / compute dtype of the model: "f32" | "bf16"
+    init_std: float = 0.02
+
+    @property
+    def kv_width(self) -> int:
+        return self.n_kv_heads * self.head_dim
+
+    @property
+    def q_width(self) -> int:
+        return self.n_q_heads * self.head_dim
+
+    def with_layers(self, n_layers: int) -> "ModelShape":
+        return dataclasses.replace(self, n_layers=n_layers)
+
+    def with_dtype(self, dtype: str) -> "ModelShape":
+        return dataclasses.replace(self, dtype=dtype)
+
+    def params_per_layer(self) -> int:
+        d = self.d_model
+        return (d * (self.q_width + 2 * self.kv_width) + self.q_width * d
+                + d * 2 * self.d_ff + self.d_ff * d)
+
+    def kv_bytes_per_token(self) -> int:
+        """K and V bytes per token over all layers in the storage dtype."""
+        elt = 2 if self.dtype == "bf16" else 4
+        return self.n_layers * 2 * self.n_kv_heads * self.head_dim * elt
+
+
+SHAPES: Dict[str, ModelShape] = {
+    # tiny fp32 decoder: 2 layers, d 256, 4 x 64 MHA, MLP 1024, vocab 32000
+    "tiny-2l-d256": ModelShape("tiny-2l-d256", 2, 256, 4, 4, 64, 1024, 32000,
+                               10000.0, dtype="f32"),
+    # Llama-3-8B-shaped decoder
+    "llama3-8b": ModelShape("llama3-8b", 32, 4096, 32, 8, 128, 14336, 128256,
+                            500000.0, dtype="bf16"),
+    # Llama-70B-shaped decoder
+    "llama-70b": ModelShape("llama-70b", 80, 8192, 64, 8, 128, 28672, 128256,
+                            500000.0, dtype="bf16"),
+}
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+
+def recompute_count(ratio: float, n_ctx: int) -> int:
+    """Number of context tokens recomputed per layer: floor(r * N + 0.5)."""
+    return int(np.floor(ratio * n_ctx + 0.5))
+
+
+@dataclass
+class Workload:
+    name: str
+    shape: ModelShape
+    chunk_tokens: List[np.ndarray]      # int32 [len_c] per chunk (storage order)
+    old_starts: List[int]               # offset each chunk was prefilled at
+    new_starts: List[int]               # offset each chunk is placed at
+    query_tokens: np.ndarray            # int32 [Q]
+    ratio: float
+    seed: int
+    paged: bool = False
+    block_size: int = 16
+
+    @property
+    def chunk_lens(self) -> List[int]:
+        return [int(len(t)) for t in self.chunk_tokens]
+
+    @property
+    def n_ctx(self) -> int:
+        return int(sum(self.chunk_lens))
+
+    @property
+    def n_query(self) -> int:
+        return int(len(self.query_tokens))
+
+    @property
+    def n_total(self) -> int:
+        return self.n_ctx + self.n_query
+
+    @property
+    def k(self) -> int:
+        return recompute_count(self.ratio, self.n_ctx)
+
+    def schedule(self) -> Tuple[List[int], List[int]]:
+        """Constant schedule: layer 0 full; every later layer checks and keeps k."""
+        L = self.shape.n_layers
+        ks = [self.n_ctx] + [self.k] * (L - 1)
+        check = [0] + [1] * (L - 1)
+        return ks, check
+
+    def placement_order(self) -> List[int]:
+        """Chunk indices sorted by new_start."""
+        return sorted(range(len(self.chunk_tokens)), key=lambda c: self.new_starts[c])
+
+    def context_tokens(self) -> np.ndarray:
+        """Context tokens in placement (new position) order."""
+        return np.concatenate([self.chunk_tokens[c] for c in self.placement_order()]).astype(np.int32)
+
+
+def _rng(seed: int, *key: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(entropy=seed, spawn_key=tuple(key)))
+
+
+def _tile_offsets(lens: Sequence[int], order: Sequence[int]) -> List[int]:
+    starts = [0] * len(lens)
+    cur = 0
+    for c in order:
+        starts[c] = cur
+        cur += lens[c]
+    return starts
+
+
+WORKLOADS = {
+    # name -> (shape, description)
+    "tiny-2x256-q32": "tiny fp32 decoder; 2 chunks x 256 prefilled at 0, placed at 0 and 256; 32-token query",
+    "8b-4x1024-q64": "8B shape bf16; 4 chunks x 1024 prefilled at 0, shuffled placement; 64-token query",
+    "8b-16x512j-q64": "8B shape bf16; 16 chunks of 512 +-25%, cached at random offsets in [0,4096), shuffled; 64-token query",
+    "70b-4x1024-q64": "70B shape bf16; 4 chunks x 1024, shuffled placement; 64-token query",
+    "8b-32x1024-q128-paged": "8B shape bf16; 32 chunks x 1024, shuffled; 128-token query; paged KV, 16-token blocks",
+}
+
+
+def make_workload(name: str, seed: int = 0, ratio: float = 0.15, *,
+                  n_layers: Optional[int] = None, n_chunks: Optional[int] = None,
+                  chunk_len: Optional[int] = None, n_query: Optional[int] = None,
+                  shape: Optional[ModelShape] = None, paged: Optional[bool] = None) -> Workload:
+    """Build one of the named workloads; keyword overrides give reduced variants.
+
+    Chunk tokens are uniform over the vocabulary.  Placement order is a seeded
+    permutation except for the tiny workload, whose placement is fixed (chunk 0
+    at 0, chunk 1 at 256).
+    """
+    rng = _rng(seed, 7, 0)
+    if name == "tiny-2x256-q32":
+        shp = SHAPES["tiny-2l-d256"]
+        C, ln, Q = 2, 256, 32
+        lens = [ln] * (n_chunks or C) if chunk_len is None else [chunk_len] * (n_chunks or C)
+        old = [0] * len(lens)
+        order = list(range(len(lens)))
+        is_paged = False
+    elif name in ("8b-4x1024-q64", "70b-4x1024-q64"):
+        shp = SHAPES["llama3-8b" if name.startswith("8b") else "llama-70b"]
+        C, Q = 4, 64
+        lens = [chunk_len or 1024] * (n_chunks or C)
+        old = [0] * len(lens)
+        order = [int(i) for i in rng.permutation(len(lens))]
+        is_paged = False
+    elif name == "8b-16x512j-q64":
+        shp = SHAPES["llama3-8b"]
+        C, Q = 16, 64
+        base = chunk_len or 512
+        nc = n_chunks or C
+        jit = base // 4
+        lens = [int(base + rng.integers(-jit, jit + 1)) for _ in range(nc)]
+        old = [int(rng.integers(0, 4096)) for _ in range(nc)]
+        order = [int(i) for i in rng.permutation(nc)]
+        is_paged = False
+    elif name == "8b-32x1024-q128-paged":
+        shp = SHAPES["llama3-8b"]
+        C, Q = 32, 128
+        lens = [chunk_len or 1024] * (n_chunks or C)
+        old = [0] * len(lens)
+        order = [int(i) for i in rng.permutation(len(lens))]
+        is_paged = True
+    else:
+        raise KeyError(f"unknown workload {name!r}")
+    if shape is not None:
+        shp = shape
+    if n_layers is not None:
+        shp = shp.with_layers(n_layers)
+    if n_query is not None:
+        Q = n_query
+    if paged is not None:
+        is_paged = paged
+    trng = _rng(seed, 7, 1)
+    toks = [trng.integers(0, shp.vocab, size=l, dtype=np.int64).astype(np.int32) for l in lens]
+    qtok = trng.integers(0, shp.vocab, size=Q, dtype=np.int64).astype(np.int32)
+    new = _tile_offsets(lens, order)
+    return Workload(name=name, shape=shp, chunk_tokens=toks, old_starts=old, new_starts=new,
+                    query_tokens=qtok, ratio=ratio, seed=seed, paged=is_paged)
+
+
+# ----------------------------------------------------------------------------
+# weights
+# ----------------------------------------------------------------------------
+
+_TID = {"wq": 0, "wk": 1, "wv": 2, "wo": 3, "w_gate": 4, "w_up": 5, "w_down": 6}
+
+
+def _normal(shape: ModelShape, seed: int, layer_key: int, tid: int, dims) -> np.ndarray:
+    g = _rng(seed, 1, layer_key, tid)
+    w = g.standard_normal(size=dims, dtype=np.float32)
+    w *= np.float32(shape.init_std)
+    if shape.dtype == "bf16":
+        w = to_bf16_values(w)
+    return w
+
+
+def layer_weights(shape: ModelShape, seed: int, layer: int) -> Dict[str, np.ndarray]:
+    """Weights of one decoder layer; all matrices iid N(0, init_std^2), norm gains 1."""
+    d, F = shape.d_model, shape.d_ff
+    w = {
+        "wq": _normal(shape, seed, layer + 1, _TID["wq"], (shape.q_width, d)),
+        "wk": _normal(shape, seed, layer + 1, _TID["wk"], (shape.kv_width, d)),
+        "wv": _normal(shape, seed, layer + 1, _TID["wv"], (shape.kv_width, d)),
+        "wo": _normal(shape, seed, layer + 1, _TID["wo"], (d, shape.q_width)),
+        "w_gate": _normal(shape, seed, layer + 1, _TID["w_gate"], (F, d)),
+        "w_up": _normal(shape, seed, layer + 1, _TID["w_up"], (F, d)),
+        "w_down": _normal(shape, seed, layer + 1, _TID["w_down"], (d, F)),
+        "attn_norm": np.ones(d, dtype=np.float32),
+        "mlp_norm": np.ones(d, dtype=np.float32),
+    }
+    return w
+
+
+def global_weights(shape: ModelShape, seed: int) -> Dict[str, np.ndarray]:
+    d, V = shape.d_model, shape.vocab
+    return {
+        "embed": _normal(shape, seed, 0, 0, (V, d)),
+        "lm_head": _normal(shape, seed, 0, 1, (V, d)),
+        "final_norm": np.ones(d, dtype=np.float32),
+    }
+
+
+def model_weights(shape: ModelShape, seed: int) -> Dict[str, object]:
+    """All weights: {'layers': [per-layer dict], 'embed', 'lm_head', 'final_norm'}."""
+    out: Dict[str, object] = dict(global_weights(shape, seed))
+    out["layers"] = [layer_weights(shape, seed, l) for l in range(shape.n_layers)]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# cached KV and paging
+# ----------------------------------------------------------------------------
+
+def synthetic_chunk_kv(shape: ModelShape, lens: Sequence[int], seed: int,
+                       scale: Optional[float] = None) -> List[Tuple[np.ndarray, np.ndarray]]:
+    """Stand-in cached K/V per chunk, ``[L][len][H_kv][d_h]`` each, iid normal.
+
+    Used where a chunk prefill of the full model is too costly on the host.  The
+    default scale matches a projection of a unit-RMS row by N(0, init_std^2)
+    weights (std = init_std * sqrt(d_model)).
+    """
+    s = scale if scale is not None else shape.init_std * np.sqrt(shape.d_model)
+    out = []
+    for c, l in enumerate(lens):
+        dims = (shape.n_layers, l, shape.n_kv_heads, shape.head_dim)
+        g = _rng(seed, 3, c)
+        k = g.standard_normal(size=dims, dtype=np.float32) * np.float32(s)
+        v = g.standard_normal(size=dims, dtype=np.float32) * np.float32(s)
+        if shape.dtype == "bf16":
+            k, v = to_bf16_values(k), to_bf16_values(v)
+        out.append((k, v))
+    return out
+
+
+def paged_layout(n_tokens: int, block_size: int, seed: int, key: int,
+                 spare_blocks: int = 0) -> Tuple[np.ndarray, int]:
+    """Random block table for ``n_tokens`` tokens.
+
+    Returns (block_table int32 [ceil(n/bs)], n_physical).  Logical block b maps
+    to a distinct physical block drawn from a pool of ``n_logical +
+    spare_blocks`` blocks in random order.
+    """
+    n_log = (n_tokens + block_size - 1) // block_size
+    n_phys = n_log + spare_blocks
+    g = _rng(seed, 5, key)
+    table = g.permutation(n_phys)[:n_log].astype(np.int32)
+    return table, n_phys

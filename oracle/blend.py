@@ -1,0 +1,522 @@
+"""Plain CPU oracle of the CacheBlend blended prefill (float64, NumPy).
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the CPU
+baseline of the benchmark; never by the GPU library.
+
+Method source: "CacheBlend 完全拆解" (pinghaoyang.com.cn), cited below as [CB]
+with the section it comes from.  Model block: the Llama-3-shaped pre-norm
+decoder that the workloads name; the pages give only Q=hW_Q, K=hW_K (then
+RoPE), V=hW_V ([CB] "问题：拼接的 KV 缓存到底少了什么").
+
+Readings taken where the pages are silent (all listed in the design notes):
+  * layer 0 runs in full over every row; its context K/V are the re-RoPE'd
+    cache (they depend on the token alone); the first checked layer is 1;
+  * deviation = squared L2 over the concatenated K and V of all KV heads, K
+    compared after RoPE at the new position, fresh values unrounded;
+  * r counts context tokens only: k = floor(r*N + 0.5); the query suffix is
+    recomputed at every layer, written to the cache, never ranked;
+  * ties in the top-k go to the smaller position; sets are reported ascending;
+  * rows written at layer l are exactly S_l plus the suffix, before attention;
+  * RoPE rotates adjacent pairs (2i, 2i+1) by pos*theta_i,
+    theta_i = base^(-2i/d_h), angles and cos/sin in float64;
+  * RMSNorm eps from the model, gains as given; SiLU-gated MLP; no biases;
+    untied LM head after a final RMSNorm; attention scale 1/sqrt(d_h).
+
+Parity status: every public function below is pinned by a test in
+``tests/test_oracle_*.py`` against something other than itself (torch CPU
+library routines, complex-number rotation, brute-force sorting, closed forms,
+the method's own special cases r=0% / r=100% / single chunk).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Callable, Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ----------------------------------------------------------------------------
+# storage rounding
+# ----------------------------------------------------------------------------
+
+def store_round(x: np.ndarray, storage: str) -> np.ndarray:
+    """Round ``x`` to the storage dtype and return it as float64.
+
+    'f32' rounds to IEEE single (nearest even); 'bf16' keeps 7 explicit
+    mantissa bits, rounding the float64 value directly to nearest, ties to
+    even (normal range only, which is all this method produces).
+    """
+    x = np.asarray(x, dtype=F64)
+    if storage == "f32":
+        return x.astype(np.float32).astype(F64)
+    if storage == "bf16":
+        u = np.ascontiguousarray(x).view(np.uint64)
+        drop = np.uint64(52 - 7)
+        lsb = (u >> drop) & np.uint64(1)
+        half = np.uint64((1 << 44) - 1)
+        r = (u + half + lsb) & ~np.uint64((1 << 45) - 1)
+        return r.view(F64).reshape(x.shape)
+    if storage == "f64":
+        return x
+    raise ValueError(storage)
+
+
+# ----------------------------------------------------------------------------
+# model pieces
+# ----------------------------------------------------------------------------
+
+def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm: x / sqrt(mean(x^2) + eps) * g, per row."""
+    x = np.asarray(x, dtype=F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(g, dtype=F64)
+
+
+def rope_cos_sin(pos: np.ndarray, head_dim: int, theta: float) -> Tuple[np.ndarray, np.ndarray]:
+    """cos/sin of pos * theta_i, theta_i = base^(-2i/d_h), i < d_h/2, in float64.
+
+    [CB] "位置恢复": R_m is block diagonal with entries cos(m theta_i),
+    sin(m theta_i); d/2 rotation pairs.
+    """
+    i = np.arange(head_dim // 2, dtype=F64)
+    inv = np.power(F64(theta), -(2.0 * i) / head_dim)
+    ang = np.asarray(pos, dtype=F64)[:, None] * inv[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Apply R_pos to every head of every row: x [n, H, d_h], pos [n].
+
+    Pair (x_2i, x_2i+1) -> (x_2i c - x_2i+1 s, x_2i s + x_2i+1 c).
+    """
+    x = np.asarray(x, dtype=F64)
+    n, H, dh = x.shape
+    c, s = rope_cos_sin(pos, dh, theta)
+    c = c[:, None, :]
+    s = s[:, None, :]
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def rerope(k: np.ndarray, delta: int, theta: float, storage: str) -> np.ndarray:
+    """Re-RoPE cached keys from their stored offset to the new one.
+
+    [CB] "位置恢复": k' = R_{n-p} k_p = R_n k.  ``k`` is [..., n, H, d_h]
+    (leading layer axis allowed); every token moves by the same ``delta`` =
+    n - p.  The result is rounded to the storage dtype.  V is never rotated.
+    """
+    k = np.asarray(k, dtype=F64)
+    shp = k.shape
+    flat = k.reshape(-1, shp[-2], shp[-1])
+    out = rope(flat, np.full(flat.shape[0], delta, dtype=F64), theta)
+    return store_round(out.reshape(shp), storage)
+
+
+def causal_attention(q: np.ndarray, q_pos: np.ndarray, k: np.ndarray, v: np.ndarray,
+                     k_pos: np.ndarray, row_block: int = 1024) -> np.ndarray:
+    """softmax(q k^T / sqrt(d_h)) v over keys with k_pos <= q_pos, per head.
+
+    q [n, Hq, d_h]; k, v [P, Hkv, d_h]; GQA: q head h reads kv head
+    floor(h * Hkv / Hq).  Softmax subtracts the row maximum.
+    """
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    v = np.asarray(v, dtype=F64)
+    n, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / np.sqrt(dh)
+    out = np.zeros((n, Hq, dh), dtype=F64)
+    q_pos = np.asarray(q_pos)
+    k_pos = np.asarray(k_pos)
+    for r0 in range(0, n, row_block):
+        r1 = min(n, r0 + row_block)
+        qp = q_pos[r0:r1]
+        # keys any row of this block may see
+        kmax = qp.max()
+        kmask = k_pos <= kmax
+        kp = k_pos[kmask]
+        allowed = kp[None, :] <= qp[:, None]
+        for h in range(Hq):
+            g = (h * Hkv) // Hq
+            kk = k[kmask, g, :]
+            vv = v[kmask, g, :]
+            s = (q[r0:r1, h, :] @ kk.T) * scale
+            s = np.where(allowed, s, -np.inf)
+            m = np.max(s, axis=1, keepdims=True)
+            p = np.exp(s - m)
+            p /= np.sum(p, axis=1, keepdims=True)
+            out[r0:r1, h, :] = p @ vv
+    return out
+
+
+def swiglu_mlp(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """W_down (SiLU(a W_gate) * (a W_up)), SiLU(z) = z / (1 + e^-z)."""
+    a = np.asarray(a, dtype=F64)
+    g = a @ np.asarray(w_gate, dtype=F64).T
+    u = a @ np.asarray(w_up, dtype=F64).T
+    h = g / (1.0 + np.exp(-g)) * u
+    return h @ np.asarray(w_down, dtype=F64).T
+
+
+# ----------------------------------------------------------------------------
+# model container
+# ----------------------------------------------------------------------------
+
+@dataclass
+class OracleModel:
+    """Shape + weights.  ``layer(l)`` returns the layer's weight dict
+    (``wq, wk, wv, wo, w_gate, w_up, w_down`` as [out][in], ``attn_norm``,
+    ``mlp_norm``); ``glob`` holds ``embed`` [V][d], ``lm_head`` [V][d],
+    ``final_norm`` [d]."""
+    n_layers: int
+    d_model: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    d_ff: int
+    vocab: int
+    rope_theta: float
+    rms_eps: float
+    storage: str
+    layer: Callable[[int], Dict[str, np.ndarray]]
+    glob: Dict[str, np.ndarray]
+
+    @classmethod
+    def from_shape(cls, shape, weights_or_fn, glob=None) -> "OracleModel":
+        if callable(weights_or_fn):
+            fn, g = weights_or_fn, glob
+        else:
+            layers = weights_or_fn["layers"]
+            fn = lambda l: layers[l]  # noqa: E731
+            g = {k: weights_or_fn[k] for k in ("embed", "lm_head", "final_norm")}
+        return cls(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads,
+                   shape.head_dim, shape.d_ff, shape.vocab, shape.rope_theta,
+                   shape.rms_eps, shape.dtype, fn, g)
+
+    def heads(self, y: np.ndarray, H: int) -> np.ndarray:
+        return y.reshape(y.shape[0], H, self.head_dim)
+
+
+def _proj(a: np.ndarray, w: np.ndarray) -> np.ndarray:
+    return a @ np.asarray(w, dtype=F64).T
+
+
+def _logits(m: OracleModel, x_last: np.ndarray) -> np.ndarray:
+    a = rms_norm(x_last[None, :], m.glob["final_norm"], m.rms_eps)
+    return _proj(a, m.glob["lm_head"])[0]
+
+
+# ----------------------------------------------------------------------------
+# deviation and selection
+# ----------------------------------------------------------------------------
+
+def kv_deviation(k_fresh, v_fresh, k_cached, v_cached) -> np.ndarray:
+    """Per-token squared L2 distance between fresh and cached K and V.
+
+    [CB] "核心思想", eq. Δkv: Δ[j] = || KV_i[j] - KV_i^full[j] ||, taken over
+    the concatenation of K and V across every KV head; the square ranks the
+    same as the norm.  Inputs [n, H_kv, d_h]; output float64 [n].
+    """
+    dk = np.asarray(k_fresh, F64) - np.asarray(k_cached, F64)
+    dv = np.asarray(v_fresh, F64) - np.asarray(v_cached, F64)
+    ax = tuple(range(1, dk.ndim))
+    return np.sum(dk * dk, axis=ax) + np.sum(dv * dv, axis=ax)
+
+
+def select_hkvd(dev: np.ndarray, cand_pos: np.ndarray, k: int) -> np.ndarray:
+    """The k candidates with the largest deviation (HKVD tokens).
+
+    [CB] "选 token": rank the candidates by deviation and keep the top ones.
+    Ties go to the smaller position.  Returns the positions ascending.
+    """
+    dev = np.asarray(dev, dtype=F64)
+    cand_pos = np.asarray(cand_pos, dtype=np.int64)
+    if not (0 <= k <= len(cand_pos)):
+        raise ValueError("k out of range")
+    order = np.lexsort((cand_pos, -dev))      # primary: dev desc; secondary: pos asc
+    return np.sort(cand_pos[order[:k]])
+
+
+# ----------------------------------------------------------------------------
+# one decoder layer on a set of rows
+# ----------------------------------------------------------------------------
+
+def _attn_mlp(m: OracleModel, w, x_rows, a_rows, rows_pos, Kl, Vl, k_pos):
+    """Attention of the given rows over the layer cache, then O, residual, MLP."""
+    q = rope(m.heads(_proj(a_rows, w["wq"]), m.n_q_heads), rows_pos, m.rope_theta)
+    o = causal_attention(q, rows_pos, Kl, Vl, k_pos)
+    x = x_rows + _proj(o.reshape(o.shape[0], -1), w["wo"])
+    x = x + swiglu_mlp(rms_norm(x, w["mlp_norm"], m.rms_eps), w["w_gate"], w["w_up"], w["w_down"])
+    return x
+
+
+def full_prefill(m: OracleModel, tokens: np.ndarray, start: int = 0) -> Dict[str, np.ndarray]:
+    """One-shot prefill of ``tokens`` at positions start, start+1, ...
+
+    Returns K, V [L][n][H_kv][d_h] (storage dtype values), the final hidden
+    rows and the logits of the last row.  This is the full-KV-recompute
+    reference ([CB] "背景") and, with start = p, the chunk prefill that
+    produces a cached chunk.
+    """
+    tokens = np.asarray(tokens)
+    n = len(tokens)
+    pos = np.arange(start, start + n)
+    x = np.asarray(m.glob["embed"], dtype=F64)[tokens]
+    K = np.zeros((m.n_layers, n, m.n_kv_heads, m.head_dim), dtype=F64)
+    V = np.zeros_like(K)
+    for l in range(m.n_layers):
+        w = m.layer(l)
+        a = rms_norm(x, w["attn_norm"], m.rms_eps)
+        K[l] = store_round(rope(m.heads(_proj(a, w["wk"]), m.n_kv_heads), pos, m.rope_theta), m.storage)
+        V[l] = store_round(m.heads(_proj(a, w["wv"]), m.n_kv_heads), m.storage)
+        x = _attn_mlp(m, w, x, a, pos, K[l], V[l], pos)
+    return {"K": K, "V": V, "x": x, "logits": _logits(m, x[-1])}
+
+
+def chunk_prefill(m: OracleModel, tokens: np.ndarray, start: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Cached KV of one chunk prefilled alone at offset ``start``
+    ([CB] "背景": each retrieved chunk is prefilled separately)."""
+    r = full_prefill(m, tokens, start)
+    return r["K"], r["V"]
+
+
+def assemble_blended(m: OracleModel, chunks: Sequence[Tuple], n_query: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Concatenate cached chunks at their new offsets, re-RoPE'ing K.
+
+    ``chunks``: sequence of (tokens, K_c, V_c, old_start, new_start).  Returns
+    K_b, V_b [L][N+Q][H_kv][d_h]; query positions are left zero.
+    [CB] "位置恢复"; [BI] section 6.2 (old_st = source, cur_st = target).
+    """
+    N = sum(len(c[0]) for c in chunks)
+    T = N + n_query
+    Kb = np.zeros((m.n_layers, T, m.n_kv_heads, m.head_dim), dtype=F64)
+    Vb = np.zeros_like(Kb)
+    for tokens, Kc, Vc, old, new in chunks:
+        ln = len(tokens)
+        Kb[:, new:new + ln] = rerope(Kc, new - old, m.rope_theta, m.storage)
+        Vb[:, new:new + ln] = np.asarray(Vc, dtype=F64)
+    return Kb, Vb
+
+
+def _context_tokens(chunks) -> np.ndarray:
+    order = sorted(range(len(chunks)), key=lambda c: chunks[c][4])
+    return np.concatenate([np.asarray(chunks[c][0]) for c in order])
+
+
+def _check_tiling(chunks):
+    order = sorted(range(len(chunks)), key=lambda c: chunks[c][4])
+    cur = 0
+    for c in order:
+        if chunks[c][4] != cur or chunks[c][3] < 0:
+            raise ValueError("chunks must tile [0, N) with known stored offsets")
+        cur += len(chunks[c][0])
+    return cur
+
+
+def blend_layer(m: OracleModel, l: int, Kl: np.ndarray, Vl: np.ndarray, x_rows: np.ndarray,
+                cand_pos: np.ndarray, n_query: int, check: bool, k_keep: int,
+                force: Optional[np.ndarray] = None):
+    """One selective-recompute layer l >= 1 ([CB] Fig. 5 and "选 token").
+
+    ``x_rows`` holds the hidden rows of the candidates (positions
+    ``cand_pos``, ascending) followed by the ``n_query`` suffix rows at
+    positions N .. N+Q-1 with N = Kl.shape[0] - n_query.  ``Kl``/``Vl`` are the
+    layer's blended cache [T][H_kv][d_h] and are updated in place.
+
+    Steps: fresh K/V for every row; if ``check``, deviation over the candidates
+    and top-k_keep (or ``force``); scatter the fresh K/V of the kept rows and
+    the suffix; attention of those rows over the whole cache; O, residual,
+    MLP.  Returns (x_out rows for kept + suffix, kept positions, deviation or
+    None).
+    """
+    w = m.layer(l)
+    T = Kl.shape[0]
+    N = T - n_query
+    nc = len(cand_pos)
+    suffix = np.arange(N, T)
+    rows_pos = np.concatenate([np.asarray(cand_pos, dtype=np.int64), suffix])
+    a = rms_norm(x_rows, w["attn_norm"], m.rms_eps)
+    kf = rope(m.heads(_proj(a, w["wk"]), m.n_kv_heads), rows_pos, m.rope_theta)
+    vf = m.heads(_proj(a, w["wv"]), m.n_kv_heads)
+    dev = None
+    if check:
+        dev = kv_deviation(kf[:nc], vf[:nc], Kl[cand_pos], Vl[cand_pos])
+        keep = np.sort(np.asarray(force, dtype=np.int64)) if force is not None \
+            else select_hkvd(dev, cand_pos, k_keep)
+        if len(keep) != k_keep:
+            raise ValueError("forced set has the wrong size")
+    else:
+        if k_keep != nc:
+            raise ValueError("an unchecked layer keeps every candidate")
+        keep = np.asarray(cand_pos, dtype=np.int64)
+    slot = np.searchsorted(cand_pos, keep)
+    if np.any(slot >= nc) or np.any(np.asarray(cand_pos)[np.minimum(slot, nc - 1)] != keep):
+        raise ValueError("kept positions must be candidates")
+    sel = np.concatenate([slot, nc + np.arange(n_query)])
+    wpos = rows_pos[sel]
+    # fill: fresh K/V of the kept rows and the suffix replace the cache
+    Kl[wpos] = store_round(kf[sel], m.storage)
+    Vl[wpos] = store_round(vf[sel], m.storage)
+    x_out = _attn_mlp(m, w, x_rows[sel], a[sel], wpos, Kl, Vl, np.arange(T))
+    return x_out, keep, dev
+
+
+def blend_prefill(m: OracleModel, chunks: Sequence[Tuple], query_tokens: np.ndarray,
+                  k_sched: Sequence[int], check: Sequence[int],
+                  force_sets: Optional[Dict[int, np.ndarray]] = None,
+                  layers_limit: Optional[int] = None) -> Dict[str, object]:
+    """CacheBlend blended prefill, gathered-rows formulation.
+
+    ``chunks``: (tokens, K_c, V_c, old_start, new_start) per chunk; their new
+    offsets tile [0, N).  ``k_sched[l]`` is |S_l| (k_sched[0] must be N),
+    ``check[l]`` whether layer l re-ranks.  Layer 0 runs in full over every row
+    with the context K/V taken from the re-RoPE'd cache; each later layer runs
+    ``blend_layer`` on S_{l-1} plus the suffix, so S_l is a subset of S_{l-1}
+    ([CB] "核心思想": sets only shrink).  Returns K, V (blended cache),
+    logits of the last position, sets {l: S_l} and devs {l: (cand, Δ)}.
+    ``layers_limit`` stops after that many layers (timing samples only).
+    """
+    N = _check_tiling(chunks)
+    Q = len(query_tokens)
+    T = N + Q
+    L = m.n_layers
+    if k_sched[0] != N:
+        raise ValueError("layer 0 runs in full")
+    Kb, Vb = assemble_blended(m, chunks, Q)
+    tokens = np.concatenate([_context_tokens(chunks), np.asarray(query_tokens)])
+    pos = np.arange(T)
+    suffix = np.arange(N, T)
+    # layer 0: every row; context K/V are the re-RoPE'd cache
+    w = m.layer(0)
+    x = np.asarray(m.glob["embed"], dtype=F64)[tokens]
+    a = rms_norm(x, w["attn_norm"], m.rms_eps)
+    Kb[0, suffix] = store_round(rope(m.heads(_proj(a[N:], w["wk"]), m.n_kv_heads), suffix, m.rope_theta), m.storage)
+    Vb[0, suffix] = store_round(m.heads(_proj(a[N:], w["wv"]), m.n_kv_heads), m.storage)
+    x = _attn_mlp(m, w, x, a, pos, Kb[0], Vb[0], pos)
+    S = np.arange(N)
+    sets = {0: S}
+    devs = {}
+    nl = L if layers_limit is None else min(L, layers_limit)
+    for l in range(1, nl):
+        if k_sched[l] > len(S):
+            raise ValueError("sets may only shrink")
+        force = None if force_sets is None else force_sets.get(l)
+        x, S_new, dev = blend_layer(m, l, Kb[l], Vb[l], x, S, Q, bool(check[l]), int(k_sched[l]), force)
+        if dev is not None:
+            devs[l] = (S, dev)
+        S = S_new
+        sets[l] = S
+    logits = _logits(m, x[-1])
+    return {"K": Kb, "V": Vb, "logits": logits, "sets": sets, "devs": devs, "x_last": x[-1]}
+
+
+def blend_prefill_masked(m: OracleModel, chunks: Sequence[Tuple], query_tokens: np.ndarray,
+                         k_sched: Sequence[int], check: Sequence[int]) -> Dict[str, object]:
+    """Masked-dense twin of ``blend_prefill``: every row is computed at every
+    layer and the cache / hidden rows keep the fresh or old value by mask
+    ([CB] Fig. 5 drawn literally: mask the input, fill the unselected positions
+    from the cache, attend with every selected query).  It must agree with the
+    gathered-rows formulation."""
+    N = _check_tiling(chunks)
+    Q = len(query_tokens)
+    T = N + Q
+    Kb, Vb = assemble_blended(m, chunks, Q)
+    tokens = np.concatenate([_context_tokens(chunks), np.asarray(query_tokens)])
+    pos = np.arange(T)
+    x = np.asarray(m.glob["embed"], dtype=F64)[tokens]
+    cand = np.ones(T, dtype=bool)
+    cand[N:] = False
+    is_suffix = ~cand.copy()
+    is_suffix[:N] = False
+    sets, devs = {}, {}
+    for l in range(m.n_layers):
+        w = m.layer(l)
+        a = rms_norm(x, w["attn_norm"], m.rms_eps)
+        kf = rope(m.heads(_proj(a, w["wk"]), m.n_kv_heads), pos, m.rope_theta)
+        vf = m.heads(_proj(a, w["wv"]), m.n_kv_heads)
+        if l == 0:
+            keep = cand.copy()
+            write = is_suffix.copy()          # context K/V of layer 0 stay cached
+        else:
+            if check[l]:
+                d = kv_deviation(kf, vf, Kb[l], Vb[l])
+                devs[l] = (np.nonzero(cand)[0], d[cand])
+                # rank candidates: deviation desc, position asc
+                idx = np.nonzero(cand)[0]
+                ranked = sorted(idx.tolist(), key=lambda j: (-d[j], j))
+                keep = np.zeros(T, dtype=bool)
+                keep[ranked[:k_sched[l]]] = True
+            else:
+                keep = cand.copy()
+            write = keep | is_suffix
+        Kb[l] = np.where(write[:, None, None], store_round(kf, m.storage), Kb[l])
+        Vb[l] = np.where(write[:, None, None], store_round(vf, m.storage), Vb[l])
+        active = keep | is_suffix if l > 0 else np.ones(T, dtype=bool)
+        x_new = _attn_mlp(m, w, x, a, pos, Kb[l], Vb[l], pos)
+        x = np.where(active[:, None], x_new, x)
+        cand = keep
+        sets[l] = np.nonzero(keep)[0]
+    return {"K": Kb, "V": Vb, "logits": _logits(m, x[-1]), "sets": sets, "devs": devs}
+
+
+def full_reuse_prefill(m: OracleModel, Kb: np.ndarray, Vb: np.ndarray, query_tokens: np.ndarray) -> Dict[str, object]:
+    """Full KV reuse ([CB] "背景", PromptCache-style): the context cache is used
+    as-is at every layer and only the query suffix is computed.  ``Kb``/``Vb``
+    [L][N+Q][H_kv][d_h] hold the context; suffix rows are written here."""
+    Kb = Kb.copy()
+    Vb = Vb.copy()
+    L, T = Kb.shape[0], Kb.shape[1]
+    Q = len(query_tokens)
+    N = T - Q
+    suffix = np.arange(N, T)
+    x = np.asarray(m.glob["embed"], dtype=F64)[np.asarray(query_tokens)]
+    for l in range(L):
+        w = m.layer(l)
+        a = rms_norm(x, w["attn_norm"], m.rms_eps)
+        Kb[l, suffix] = store_round(rope(m.heads(_proj(a, w["wk"]), m.n_kv_heads), suffix, m.rope_theta), m.storage)
+        Vb[l, suffix] = store_round(m.heads(_proj(a, w["wv"]), m.n_kv_heads), m.storage)
+        x = _attn_mlp(m, w, x, a, suffix, Kb[l], Vb[l], np.arange(T))
+    return {"K": Kb, "V": Vb, "logits": _logits(m, x[-1])}
+
+
+# ----------------------------------------------------------------------------
+# work accounting
+# ----------------------------------------------------------------------------
+
+def flop_count(shape, n_ctx: int, n_query: int, k_sched: Sequence[int], check: Sequence[int]) -> Dict[str, float]:
+    """Multiply-add FLOPs (2 per MAC) of the blend and of a full prefill of
+    N+Q tokens.  Attention counts only the causally visible pairs.  Layer 0
+    skips the context K/V projection (it is taken from the cache)."""
+    d, Hq, Hkv, dh, F = shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.d_ff
+    qw, kvw = Hq * dh, Hkv * dh
+    T = n_ctx + n_query
+
+    def attn(pos_list_sum_plus_one):  # sum over rows of (pos+1) visible keys
+        return 4.0 * qw * pos_list_sum_plus_one
+
+    def per_row_rest():   # Q, O, MLP per row
+        return 2.0 * (d * qw + qw * d + 3 * d * F)
+
+    full = 0.0
+    vis_all = T * (T + 1) / 2.0
+    full_layer = T * (per_row_rest() + 2.0 * d * 2 * kvw) + attn(vis_all)
+    full = full_layer * shape.n_layers
+    blend = 0.0
+    # layer 0: Q/O/MLP on every row, K/V only for the suffix
+    blend += T * per_row_rest() + n_query * 2.0 * d * 2 * kvw + attn(vis_all)
+    cand = n_ctx
+    for l in range(1, shape.n_layers):
+        rows_kv = cand + n_query
+        keep = k_sched[l]
+        rows = keep + n_query
+        # mean visible keys: kept context rows average (N+1)/2, suffix rows N + i + 1
+        vis = keep * (n_ctx + 1) / 2.0 + sum(n_ctx + i + 1 for i in range(n_query))
+        blend += rows_kv * 2.0 * d * 2 * kvw + rows * per_row_rest() + attn(vis)
+        cand = keep
+    return {"blend": blend, "full": full, "ratio": blend / full}

@@ -1,0 +1,211 @@
+"""Pins for the oracle's blended prefill: the method's own special cases.
+
+* r = 100% equals a one-shot full prefill                      ([CB] "背景")
+* r = 0% equals the re-RoPE'd concatenation + full KV reuse     ([CB] "背景")
+* one chunk at offset 0 reproduces prefix reuse (causality)    ([CB] "问题")
+* a chunk prefilled at p, re-RoPE'd by -p, equals one prefilled at 0
+                                                                ([CB] "位置恢复")
+* sets nest, have the scheduled sizes, never contain the suffix ([CB] "核心思想")
+* a masked-dense formulation agrees with the gathered-rows one  ([CB] Fig. 5)
+* the compute share at the 8B, 4K, 15% point is about 18%      ([CB] "把账算细")
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import cbinputs
+from oracle import (OracleModel, assemble_blended, blend_prefill, blend_prefill_masked,
+                    chunk_prefill, flop_count, full_prefill, full_reuse_prefill, kv_deviation,
+                    store_round)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+# an MHA/GQA decoder small enough for many runs; fp32 storage
+GQA = cbinputs.ModelShape("gqa-small", 3, 64, 4, 2, 16, 96, 101, 10000.0, dtype="f32")
+
+
+def _sharpen(w):
+    # larger Q/K weights make attention peaked, so cross-chunk effects are not tiny
+    for lw in w["layers"]:
+        lw["wq"] = lw["wq"] * 15.0
+        lw["wk"] = lw["wk"] * 15.0
+    return w
+
+
+def _setup(shape, lens, old, new, n_query, seed):
+    w = _sharpen(cbinputs.model_weights(shape, seed))
+    m = OracleModel.from_shape(shape, w)
+    rng = np.random.default_rng(seed + 100)
+    chunks = []
+    for ln, p, n in zip(lens, old, new):
+        toks = rng.integers(0, shape.vocab, size=ln)
+        K, V = chunk_prefill(m, toks, p)
+        chunks.append((toks, K, V, p, n))
+    q = rng.integers(0, shape.vocab, size=n_query)
+    return m, chunks, q
+
+
+def _rel(a, b):
+    return np.max(np.abs(np.asarray(a) - np.asarray(b))) / max(np.max(np.abs(np.asarray(b))), 1e-300)
+
+
+def _sched(L, N, k):
+    return [N] + [k] * (L - 1), [0] + [1] * (L - 1)
+
+
+def _full_tokens(chunks, q):
+    order = sorted(range(len(chunks)), key=lambda c: chunks[c][4])
+    return np.concatenate([chunks[c][0] for c in order] + [q])
+
+
+@pytest.mark.parametrize("shape_name", ["gqa", "tiny"])
+def test_r100_equals_full_prefill(shape_name):
+    if shape_name == "gqa":
+        m, chunks, q = _setup(GQA, [20, 13, 17], [5, 0, 31], [17, 37, 0], 6, 1)
+    else:
+        wl = cbinputs.make_workload("tiny-2x256-q32", seed=0, chunk_len=64, n_query=8)
+        w = cbinputs.model_weights(wl.shape, 0)
+        m = OracleModel.from_shape(wl.shape, w)
+        chunks = [(t, *chunk_prefill(m, t, p), p, n)
+                  for t, p, n in zip(wl.chunk_tokens, wl.old_starts, wl.new_starts)]
+        q = wl.query_tokens
+    N = sum(len(c[0]) for c in chunks)
+    ks, ch = _sched(m.n_layers, N, N)
+    b = blend_prefill(m, chunks, q, ks, ch)
+    f = full_prefill(m, _full_tokens(chunks, q), 0)
+    assert _rel(b["K"], f["K"]) < 1e-5
+    assert _rel(b["V"], f["V"]) < 1e-5
+    assert _rel(b["logits"], f["logits"]) < 1e-5
+    for l in range(1, m.n_layers):
+        assert b["sets"][l].tolist() == list(range(N))
+
+
+def test_r0_equals_concatenation_and_full_reuse():
+    m, chunks, q = _setup(GQA, [20, 13, 17], [5, 0, 31], [17, 37, 0], 6, 2)
+    N = 50
+    ks, ch = _sched(m.n_layers, N, 0)
+    b = blend_prefill(m, chunks, q, ks, ch)
+    Kc, Vc = assemble_blended(m, chunks, len(q))
+    assert np.array_equal(b["K"][:, :N], Kc[:, :N])     # bitwise
+    assert np.array_equal(b["V"][:, :N], Vc[:, :N])
+    r = full_reuse_prefill(m, Kc, Vc, q)
+    assert _rel(b["logits"], r["logits"]) < 1e-12
+    assert _rel(b["K"], r["K"]) < 1e-12
+    # and the reuse really differs from the full prefill (cross-chunk attention is missing)
+    f = full_prefill(m, _full_tokens(chunks, q), 0)
+    assert _rel(r["logits"], f["logits"]) > 1e-3
+
+
+@pytest.mark.parametrize("ratio", [0.0, 0.15, 0.5, 1.0])
+def test_single_chunk_prefix_reuse(ratio):
+    m, chunks, q = _setup(GQA, [40], [0], [0], 5, 3)
+    N = 40
+    k = cbinputs.recompute_count(ratio, N)
+    ks, ch = _sched(m.n_layers, N, k)
+    b = blend_prefill(m, chunks, q, ks, ch)
+    f = full_prefill(m, _full_tokens(chunks, q), 0)
+    assert _rel(b["K"], f["K"]) < 1e-5
+    assert _rel(b["V"], f["V"]) < 1e-5
+    assert _rel(b["logits"], f["logits"]) < 1e-5
+    # every deviation is at the level of storage rounding
+    for l, (cand, dev) in b["devs"].items():
+        if len(cand) == 0:
+            continue
+        scale = np.mean(np.sum(b["K"][l, cand] ** 2, axis=(1, 2)) + np.sum(b["V"][l, cand] ** 2, axis=(1, 2)))
+        assert np.max(dev) <= 1e-6 * scale
+
+
+def test_rerope_of_chunk_prefill_is_position_shift():
+    # a chunk prefilled at p, re-RoPE'd by -p, equals the same chunk prefilled at 0
+    shape = GQA.with_dtype("f64")
+    w = _sharpen(cbinputs.model_weights(shape, 4))
+    m = OracleModel.from_shape(shape, w)
+    toks = np.random.default_rng(4).integers(0, shape.vocab, size=30)
+    K0, V0 = chunk_prefill(m, toks, 0)
+    Kp, Vp = chunk_prefill(m, toks, 777)
+    from oracle import rerope
+    assert _rel(rerope(Kp, -777, shape.rope_theta, "f64"), K0) < 1e-10
+    assert _rel(Vp, V0) < 1e-10
+    assert _rel(Kp, K0) > 1e-2        # the stored keys do carry their position
+
+
+def test_sets_nest_and_masked_twin_agrees():
+    m, chunks, q = _setup(GQA, [20, 13, 17], [5, 0, 31], [17, 37, 0], 6, 5)
+    N = 50
+    ks = [N, 30, 22]
+    ch = [0, 1, 1]
+    b = blend_prefill(m, chunks, q, ks, ch)
+    t = blend_prefill_masked(m, chunks, q, ks, ch)
+    prev = set(range(N))
+    for l in range(1, m.n_layers):
+        s = b["sets"][l]
+        assert len(s) == ks[l]
+        assert np.all(np.diff(s) > 0)
+        assert set(s.tolist()) <= prev
+        assert np.all(s < N)
+        assert s.tolist() == t["sets"][l].tolist()
+        prev = set(s.tolist())
+    assert _rel(b["K"], t["K"]) < 1e-12
+    assert _rel(b["V"], t["V"]) < 1e-12
+    assert _rel(b["logits"], t["logits"]) < 1e-12
+    for l in b["devs"]:
+        np.testing.assert_allclose(b["devs"][l][1], t["devs"][l][1], rtol=1e-12)
+
+
+def test_selected_rows_get_fresh_kv_others_keep_cache():
+    m, chunks, q = _setup(GQA, [20, 13, 17], [5, 0, 31], [17, 37, 0], 6, 6)
+    N = 50
+    ks, ch = _sched(m.n_layers, N, 8)
+    b = blend_prefill(m, chunks, q, ks, ch)
+    Kc, Vc = assemble_blended(m, chunks, len(q))
+    for l in range(1, m.n_layers):
+        s = set(b["sets"][l].tolist())
+        others = [j for j in range(N) if j not in s]
+        assert np.array_equal(b["K"][l, others], Kc[l, others])
+        assert np.array_equal(b["V"][l, others], Vc[l, others])
+        changed = [j for j in s if not np.array_equal(b["K"][l, j], Kc[l, j])]
+        assert len(changed) == len(s)
+    # layer-0 context K/V stay cached (re-RoPE'd) even at r = 100%
+    assert np.array_equal(b["K"][0, :N], Kc[0, :N])
+
+
+def test_deviation_is_top_ranked_set():
+    m, chunks, q = _setup(GQA, [20, 13, 17], [5, 0, 31], [17, 37, 0], 6, 7)
+    N = 50
+    ks, ch = _sched(m.n_layers, N, 10)
+    b = blend_prefill(m, chunks, q, ks, ch)
+    cand, dev = b["devs"][1]
+    thr = np.sort(dev)[::-1][9]
+    chosen = set(b["sets"][1].tolist())
+    for c, d in zip(cand, dev):
+        if d > thr:
+            assert c in chosen
+        elif d < thr:
+            assert c not in chosen
+
+
+def test_compute_share_about_18_percent():
+    # [CB] "把账算细": 4096 x 32 x 0.15 ~ 19660 of 131072 token-layers, plus one
+    # full layer -> about 18%
+    g = json.load(open(os.path.join(HERE, "golden", "token_layer_accounting.json")))
+    shape = cbinputs.SHAPES["llama3-8b"]
+    N, L, r = g["n_ctx"], g["n_layers"], g["ratio"]
+    assert int(N * L * r) == g["recomputed_token_layers"] or round(N * L * r) == g["recomputed_token_layers"]
+    assert N * L == g["full_token_layers"]
+    k = cbinputs.recompute_count(r, N)
+    ks, ch = _sched(L, N, k)
+    token_layers = N + sum(ks[1:])
+    assert abs(token_layers / (N * L) - g["ratio_with_first_layer"]) < 0.01
+    fc = flop_count(shape, N, 64, ks, ch)
+    assert abs(fc["ratio"] - g["ratio_with_first_layer"]) < 0.02
+
+
+def test_kv_bytes_per_token_golden():
+    # [KV] S_token = L x 2 x H_kv x D_head x B; [CB] "把账算细"
+    g = json.load(open(os.path.join(HERE, "golden", "kv_bytes_per_token.json")))
+    for case in g["cases"]:
+        b = case["layers"] * 2 * case["kv_heads"] * case["head_dim"] * case["bytes_per_element"]
+        assert b == case["bytes_per_token"]
+    assert cbinputs.SHAPES["llama3-8b"].kv_bytes_per_token() == 128 * 1024

@@ -1,0 +1,267 @@
+"""Python binding of libcacheblend: argument marshalling only.
+
+Functions carry the C names (``cb_rerope_k``, ``cb_kv_deviation``,
+``cb_select_hkvd``, ``cb_blend_layer``, ``cb_blend_prefill``,
+``cb_workspace_bytes``).  They take torch tensors that already live on the GPU,
+pack them into the C structs and call the library on the current torch stream.
+PyTorch provides device memory and streams only; every step of the blended
+prefill runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _abi
+from ._abi import (CB_BF16, CB_COPY_V, CB_F32, CB_OK, cb_blend_params, cb_chunk, cb_layer_w, cb_model,
+                   cb_model_cfg, cb_paged_kv)
+
+
+class CacheBlendError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _abi.load()
+        self.status = status
+        name = lib.cb_status_string(status).decode()
+        detail = lib.cb_last_error().decode()
+        super().__init__(f"{where}: {name}: {detail}")
+
+
+def _check(st: int, where: str):
+    if st != CB_OK:
+        raise CacheBlendError(st, where)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream: Optional[torch.cuda.Stream] = None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def torch_dtype(dt: str) -> torch.dtype:
+    return torch.bfloat16 if dt == "bf16" else torch.float32
+
+
+def make_cfg(shape) -> cb_model_cfg:
+    """cb_model_cfg of a cbinputs.ModelShape."""
+    return cb_model_cfg(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                        shape.d_ff, shape.vocab, float(shape.rope_theta), float(shape.rms_eps),
+                        CB_BF16 if shape.dtype == "bf16" else CB_F32)
+
+
+# ----------------------------------------------------------------------------
+# device-side containers
+# ----------------------------------------------------------------------------
+
+class DeviceModel:
+    """Decoder weights on the GPU in the library's layout.
+
+    ``layers`` are dicts of torch tensors: ``w_qkv`` [(Hq+2Hkv)dh][d],
+    ``w_o`` [d][Hq dh], ``w_gate_up`` [2F][d], ``w_down`` [d][F] in the model
+    dtype and fp32 ``attn_norm`` / ``mlp_norm``.
+    """
+
+    def __init__(self, shape, layers: List[dict], embed: torch.Tensor, lm_head: torch.Tensor,
+                 final_norm: torch.Tensor):
+        self.shape = shape
+        self.layers = layers
+        self.embed = embed
+        self.lm_head = lm_head
+        self.final_norm = final_norm
+        self.cfg = make_cfg(shape)
+        arr = (cb_layer_w * shape.n_layers)()
+        for l, w in enumerate(layers):
+            arr[l] = cb_layer_w(w["w_qkv"].data_ptr(), w["w_o"].data_ptr(), w["w_gate_up"].data_ptr(),
+                                w["w_down"].data_ptr(), w["attn_norm"].data_ptr(), w["mlp_norm"].data_ptr())
+        self._c_layers = arr
+        self.c = cb_model(self.cfg, embed.data_ptr(), final_norm.data_ptr(), lm_head.data_ptr(), arr)
+
+    @classmethod
+    def from_numpy(cls, shape, weights: dict, device="cuda") -> "DeviceModel":
+        """From cbinputs.model_weights (fp32 arrays holding model-dtype values)."""
+        td = torch_dtype(shape.dtype)
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device).to(td)
+
+        layers = []
+        for w in weights["layers"]:
+            layers.append({
+                "w_qkv": up(np.concatenate([w["wq"], w["wk"], w["wv"]], axis=0)),
+                "w_o": up(w["wo"]),
+                "w_gate_up": up(np.concatenate([w["w_gate"], w["w_up"]], axis=0)),
+                "w_down": up(w["w_down"]),
+                "attn_norm": torch.from_numpy(np.asarray(w["attn_norm"], np.float32)).to(device),
+                "mlp_norm": torch.from_numpy(np.asarray(w["mlp_norm"], np.float32)).to(device),
+            })
+        return cls(shape, layers, up(weights["embed"]), up(weights["lm_head"]),
+                   torch.from_numpy(np.asarray(weights["final_norm"], np.float32)).to(device))
+
+    @classmethod
+    def from_tensors(cls, shape, t: dict) -> "DeviceModel":
+        """From cbinputs.torch_device_weights output (already in the library layout)."""
+        return cls(shape, t["layers"], t["embed"], t["lm_head"], t["final_norm"])
+
+
+class PagedKV:
+    """Paged K/V pools [L][n_phys * bs][Hkv][dh] plus a block table."""
+
+    def __init__(self, shape, n_tokens: int, block_size: int = 16, block_table: Optional[np.ndarray] = None,
+                 n_phys: Optional[int] = None, device="cuda", fill: Optional[float] = None):
+        self.shape = shape
+        self.n_tokens = n_tokens
+        self.block_size = block_size
+        n_log = (n_tokens + block_size - 1) // block_size
+        if block_table is None:
+            block_table = np.arange(n_log, dtype=np.int32)
+        block_table = np.asarray(block_table, dtype=np.int32)
+        self.n_phys = int(n_phys if n_phys is not None else max(int(block_table.max(initial=-1)) + 1, n_log))
+        td = torch_dtype(shape.dtype)
+        dims = (shape.n_layers, self.n_phys * block_size, shape.n_kv_heads, shape.head_dim)
+        if fill is None:
+            self.k = torch.empty(dims, dtype=td, device=device)
+            self.v = torch.empty(dims, dtype=td, device=device)
+        else:
+            self.k = torch.full(dims, fill, dtype=td, device=device)
+            self.v = torch.full(dims, fill, dtype=td, device=device)
+        self.block_table_host = block_table
+        self.block_table = torch.from_numpy(block_table).to(device)
+        self.c = cb_paged_kv(self.k.data_ptr(), self.v.data_ptr(), self.block_table.data_ptr(), block_size,
+                             len(block_table), self.n_phys * block_size * shape.kv_width)
+
+    def slots(self, positions) -> torch.Tensor:
+        """Physical row of each logical position (host computation on the host copy of the table)."""
+        p = np.asarray(positions, dtype=np.int64)
+        rows = self.block_table_host[p // self.block_size].astype(np.int64) * self.block_size + p % self.block_size
+        return torch.from_numpy(rows).to(self.k.device)
+
+    def logical(self, n: Optional[int] = None):
+        """(K, V) [L][n][Hkv][dh] in logical position order (a copy)."""
+        n = self.n_tokens if n is None else n
+        idx = self.slots(np.arange(n))
+        return self.k[:, idx], self.v[:, idx]
+
+
+@dataclass
+class ChunkSource:
+    """One cached chunk on the GPU: tokens, K/V (contiguous [L][len][Hkv][dh] or a
+    paged pool with block ids), the stored offset and the new offset."""
+    tokens: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    old_start: int
+    new_start: int
+    block_ids: Optional[torch.Tensor] = None
+    block_size: int = 16
+    layer_stride: int = 0
+
+    @property
+    def len(self) -> int:
+        return int(self.tokens.numel())
+
+    def c(self) -> cb_chunk:
+        return cb_chunk(self.tokens.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                        self.block_ids.data_ptr() if self.block_ids is not None else None,
+                        self.len, int(self.old_start), int(self.new_start),
+                        int(self.block_size if self.block_ids is not None else 0), int(self.layer_stride))
+
+
+def _chunk_array(chunks: Sequence[ChunkSource]):
+    arr = (cb_chunk * max(1, len(chunks)))()
+    for i, c in enumerate(chunks):
+        arr[i] = c.c()
+    return arr
+
+
+class Workspace:
+    """A reusable device workspace (uint8 tensor)."""
+
+    def __init__(self, nbytes: int, device="cuda"):
+        self.t = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.t.data_ptr())
+
+    @property
+    def nbytes(self) -> int:
+        return self.t.numel()
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+
+def cb_workspace_bytes(cfg: cb_model_cfg, n_ctx: int, n_query: int, n_chunks: int) -> int:
+    return int(_abi.load().cb_workspace_bytes(ctypes.byref(cfg), n_ctx, n_query, n_chunks))
+
+
+def _ws(ws: Optional[Workspace], need: int, device) -> Workspace:
+    if ws is None or ws.nbytes < need:
+        ws = Workspace(need, device)
+    return ws
+
+
+def cb_rerope_k(cfg: cb_model_cfg, chunks: Sequence[ChunkSource], dst: PagedKV, flags: int = CB_COPY_V,
+                ws: Optional[Workspace] = None, stream=None) -> None:
+    lib = _abi.load()
+    w = _ws(ws, cb_workspace_bytes(cfg, 0, 0, len(chunks)), dst.k.device)
+    arr = _chunk_array(chunks)
+    _check(lib.cb_rerope_k(ctypes.byref(cfg), arr, len(chunks), ctypes.byref(dst.c), flags, w.ptr, w.nbytes,
+                           _stream(stream)), "cb_rerope_k")
+
+
+def cb_kv_deviation(cfg: cb_model_cfg, layer: int, k_fresh: torch.Tensor, v_fresh: torch.Tensor,
+                    pos: torch.Tensor, cache: PagedKV, dev_out: torch.Tensor, stream=None) -> None:
+    """k_fresh / v_fresh: fp32 [n][>= Hkv*dh] views sharing one row stride."""
+    assert k_fresh.dtype == torch.float32 and v_fresh.dtype == torch.float32
+    assert k_fresh.stride(0) == v_fresh.stride(0) and k_fresh.stride(-1) == 1
+    lib = _abi.load()
+    _check(lib.cb_kv_deviation(ctypes.byref(cfg), layer, _p(k_fresh), _p(v_fresh), k_fresh.stride(0), _p(pos),
+                               int(pos.numel()), ctypes.byref(cache.c), _p(dev_out), _stream(stream)),
+           "cb_kv_deviation")
+
+
+def cb_select_hkvd(dev: torch.Tensor, pos: torch.Tensor, k: int, sel_pos: torch.Tensor,
+                   sel_slot: Optional[torch.Tensor] = None, stream=None) -> None:
+    lib = _abi.load()
+    _check(lib.cb_select_hkvd(_p(dev), _p(pos), int(pos.numel()), int(k), _p(sel_pos), _p(sel_slot), None, 0,
+                              _stream(stream)), "cb_select_hkvd")
+
+
+def cb_blend_layer(model: DeviceModel, layer: int, kv: PagedKV, pos_in: torch.Tensor, n_ctx: int, n_query: int,
+                   x: torch.Tensor, check_flag: bool, k_keep: int, pos_out: torch.Tensor,
+                   dev_out: Optional[torch.Tensor] = None, ws: Optional[Workspace] = None, stream=None) -> None:
+    lib = _abi.load()
+    w = _ws(ws, cb_workspace_bytes(model.cfg, n_ctx, n_query, 0), x.device)
+    _check(lib.cb_blend_layer(ctypes.byref(model.c), layer, ctypes.byref(kv.c), _p(pos_in), int(pos_in.numel()),
+                              n_ctx, n_query, _p(x), int(bool(check_flag)), int(k_keep), _p(pos_out), _p(dev_out),
+                              w.ptr, w.nbytes, _stream(stream)), "cb_blend_layer")
+
+
+class BlendParams:
+    def __init__(self, k_per_layer: Sequence[int], check: Sequence[int], flags: int = 0):
+        L = len(k_per_layer)
+        self._k = (ctypes.c_int32 * L)(*[int(v) for v in k_per_layer])
+        self._c = (ctypes.c_uint8 * L)(*[1 if v else 0 for v in check])
+        self.c = cb_blend_params(self._k, self._c, flags)
+
+
+def cb_blend_prefill(model: DeviceModel, chunks: Sequence[ChunkSource], query_tokens: torch.Tensor,
+                     params: BlendParams, blended: PagedKV, logits: torch.Tensor,
+                     hkvd_out: Optional[torch.Tensor] = None, dev_out: Optional[torch.Tensor] = None,
+                     ws: Optional[Workspace] = None, stream=None, _arr=None) -> None:
+    lib = _abi.load()
+    n_ctx = sum(c.len for c in chunks)
+    w = _ws(ws, cb_workspace_bytes(model.cfg, n_ctx, int(query_tokens.numel()), len(chunks)), logits.device)
+    arr = _arr if _arr is not None else _chunk_array(chunks)
+    _check(lib.cb_blend_prefill(ctypes.byref(model.c), arr, len(chunks), _p(query_tokens),
+                                int(query_tokens.numel()), ctypes.byref(params.c), ctypes.byref(blended.c),
+                                _p(logits), _p(hkvd_out), _p(dev_out), w.ptr, w.nbytes, _stream(stream)),
+           "cb_blend_prefill")

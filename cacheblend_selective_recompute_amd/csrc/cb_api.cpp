@@ -1,0 +1,608 @@
+// C ABI of libcacheblend: argument validation, workspace carving and the
+// per-layer orchestration of the blended prefill.
+//
+// Method: "CacheBlend 完全拆解" (pinghaoyang.com.cn):
+//   * section "位置恢复": cached keys are rotated from their stored offset to
+//     the new one (k' = R_{n-p} k_p); values are copied;
+//   * section "核心思想" / "选 token": the first layer runs in full; each later
+//     layer recomputes only the tokens kept by the previous layer, measures
+//     the per-token KV deviation and keeps a top-k subset (sets only shrink);
+//   * Fig. 5: the fresh K/V of the kept tokens replace the cached ones, the
+//     kept queries attend to every token, only kept rows flow to the next layer;
+//   * section "位置恢复、KV 存储与加载流水线": the per-layer call mirrors
+//     prefill_layer(input_dict{check_flag, HKVD_indices}, KVCache).
+// Everything is enqueued on the caller's stream; nothing synchronises, nothing
+// allocates.  Validation runs before the first enqueue.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "cb_internal.h"
+
+using namespace cb;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cb_status fail(cb_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+cb_status ok() {
+  g_last_error.clear();
+  return CB_OK;
+}
+
+cb_status dev_fail(hipError_t e, const char* where) {
+  return fail(CB_ERR_DEVICE, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define CB_TRY(expr, where)                        \
+  do {                                             \
+    hipError_t _e = (expr);                        \
+    if (_e != hipSuccess) return dev_fail(_e, where); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int esize(cb_dtype dt) { return dt == CB_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------
+cb_status check_cfg(const cb_model_cfg* c) {
+  if (!c) return fail(CB_ERR_INVALID, "cfg is NULL");
+  if (c->dtype != CB_F32 && c->dtype != CB_BF16) return fail(CB_ERR_INVALID, "unknown dtype %d", (int)c->dtype);
+  if (c->n_layers < 2) return fail(CB_ERR_INVALID, "n_layers must be >= 2 (got %d)", c->n_layers);
+  if (c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->d_ff <= 0 ||
+      c->vocab <= 0)
+    return fail(CB_ERR_INVALID, "non-positive model dimension");
+  if (c->head_dim % 2) return fail(CB_ERR_INVALID, "head_dim must be even (got %d)", c->head_dim);
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(CB_ERR_INVALID, "n_q_heads %d not a multiple of n_kv_heads %d", c->n_q_heads, c->n_kv_heads);
+  if (!(c->rope_theta > 0.0)) return fail(CB_ERR_INVALID, "rope_theta must be > 0");
+  if (!(c->rms_eps >= 0.0f)) return fail(CB_ERR_INVALID, "rms_eps must be >= 0");
+  const int qw = c->n_q_heads * c->head_dim;
+  const int kvw = c->n_kv_heads * c->head_dim;
+  if (c->d_model % 64 || c->d_ff % 64 || qw % 64)
+    return fail(CB_ERR_UNSUPPORTED, "d_model, d_ff and n_q_heads*head_dim must be multiples of 64");
+  if (kvw % 8) return fail(CB_ERR_UNSUPPORTED, "n_kv_heads*head_dim must be a multiple of 8");
+  if (c->d_model > 16384) return fail(CB_ERR_UNSUPPORTED, "d_model above 16384");
+  if (!attention_supported(c->dtype, c->n_q_heads, c->n_kv_heads, c->head_dim))
+    return fail(CB_ERR_UNSUPPORTED, "attention kernel not built for head_dim %d, %d q / %d kv heads", c->head_dim,
+                c->n_q_heads, c->n_kv_heads);
+  return CB_OK;
+}
+
+cb_status check_paged(const cb_model_cfg* c, const cb_paged_kv* p, int64_t n_tokens, const char* what) {
+  if (!p) return fail(CB_ERR_INVALID, "%s is NULL", what);
+  if (!p->k || !p->v || !p->block_table) return fail(CB_ERR_INVALID, "%s: NULL pool or block table", what);
+  if (!aligned16(p->k) || !aligned16(p->v)) return fail(CB_ERR_INVALID, "%s: pools must be 16-byte aligned", what);
+  if (p->block_size < 1) return fail(CB_ERR_INVALID, "%s: block_size must be >= 1", what);
+  if (p->n_logical < 0) return fail(CB_ERR_INVALID, "%s: n_logical < 0", what);
+  if (static_cast<int64_t>(p->n_logical) * p->block_size < n_tokens)
+    return fail(CB_ERR_INVALID, "%s: block table covers %lld tokens, %lld needed", what,
+                (long long)p->n_logical * p->block_size, (long long)n_tokens);
+  const int64_t vec = 16 / esize(c->dtype);
+  if (p->layer_stride < 0 || p->layer_stride % vec)
+    return fail(CB_ERR_INVALID, "%s: layer_stride must be a non-negative multiple of %lld elements", what,
+                (long long)vec);
+  return CB_OK;
+}
+
+cb_status check_chunk_sources(const cb_model_cfg* c, const cb_chunk* ch, int n, bool need_tokens) {
+  if (n < 0) return fail(CB_ERR_INVALID, "n_chunks < 0");
+  if (n > 0 && !ch) return fail(CB_ERR_INVALID, "chunks is NULL");
+  const int64_t vec = 16 / esize(c->dtype);
+  for (int i = 0; i < n; ++i) {
+    const cb_chunk& x = ch[i];
+    if (x.len < 0) return fail(CB_ERR_INVALID, "chunk %d: len < 0", i);
+    if (x.old_start < 0)
+      return fail(CB_ERR_INVALID, "chunk %d: unknown stored offset %d (a wrong position gives wrong KV)", i,
+                  x.old_start);
+    if (x.new_start < 0) return fail(CB_ERR_INVALID, "chunk %d: new_start < 0", i);
+    if (x.len == 0) continue;
+    if (!x.k || !x.v) return fail(CB_ERR_INVALID, "chunk %d: NULL K/V", i);
+    if (!aligned16(x.k) || !aligned16(x.v)) return fail(CB_ERR_INVALID, "chunk %d: K/V not 16-byte aligned", i);
+    if (need_tokens && !x.tokens) return fail(CB_ERR_INVALID, "chunk %d: NULL tokens", i);
+    if (x.block_ids && x.block_size < 1) return fail(CB_ERR_INVALID, "chunk %d: paged source needs block_size >= 1", i);
+    if (x.layer_stride < 0 || x.layer_stride % vec)
+      return fail(CB_ERR_INVALID, "chunk %d: layer_stride must be a non-negative multiple of %lld", i, (long long)vec);
+  }
+  return CB_OK;
+}
+
+// new_start values must tile [0, N) exactly; returns N
+cb_status check_tiling(const cb_chunk* ch, int n, int64_t* n_ctx) {
+  std::vector<std::pair<int64_t, int64_t>> iv;
+  iv.reserve(n);
+  for (int i = 0; i < n; ++i)
+    if (ch[i].len > 0) iv.emplace_back(ch[i].new_start, ch[i].len);
+  std::sort(iv.begin(), iv.end());
+  int64_t cur = 0;
+  for (auto& e : iv) {
+    if (e.first < cur) return fail(CB_ERR_INVALID, "chunks overlap at position %lld", (long long)e.first);
+    if (e.first > cur) return fail(CB_ERR_INVALID, "gap in the context at position %lld", (long long)cur);
+    cur += e.second;
+  }
+  if (cur > (int64_t)1 << 30) return fail(CB_ERR_INVALID, "context too long");
+  *n_ctx = cur;
+  return CB_OK;
+}
+
+cb_status check_model(const cb_model* m) {
+  if (!m) return fail(CB_ERR_INVALID, "model is NULL");
+  cb_status st = check_cfg(&m->cfg);
+  if (st != CB_OK) return st;
+  if (!m->embed || !m->final_norm || !m->lm_head || !m->layers)
+    return fail(CB_ERR_INVALID, "model: NULL embed / final_norm / lm_head / layers");
+  if (!aligned16(m->embed) || !aligned16(m->final_norm) || !aligned16(m->lm_head))
+    return fail(CB_ERR_INVALID, "model: global tensors must be 16-byte aligned");
+  for (int l = 0; l < m->cfg.n_layers; ++l) {
+    const cb_layer_w& w = m->layers[l];
+    const void* ps[6] = {w.w_qkv, w.w_o, w.w_gate_up, w.w_down, w.attn_norm, w.mlp_norm};
+    for (const void* p : ps) {
+      if (!p) return fail(CB_ERR_INVALID, "layer %d: NULL weight", l);
+      if (!aligned16(p)) return fail(CB_ERR_INVALID, "layer %d: weight not 16-byte aligned", l);
+    }
+  }
+  return CB_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace
+// ---------------------------------------------------------------------------
+struct Ws {
+  float2* pos_tab;
+  float2* dtab;
+  int32_t* tokens;
+  float* x0;
+  float* x1;
+  void* act;
+  void* h;
+  void* q;
+  void* o;
+  float* kvf;
+  float* dev;
+  int32_t* posA;
+  int32_t* posB;
+  int32_t* slot;
+  int32_t* gmap;
+  int32_t* rowpos0;
+  int32_t* rowpos1;
+  float* a_last;
+};
+
+size_t carve(const cb_model_cfg& c, int64_t N, int64_t Q, int64_t C, void* base, Ws* w) {
+  const int64_t T = N + Q;
+  const int64_t half = c.head_dim / 2;
+  const int64_t es = esize(c.dtype);
+  const int64_t qw = (int64_t)c.n_q_heads * c.head_dim;
+  const int64_t kvw = (int64_t)c.n_kv_heads * c.head_dim;
+  size_t off = 0;
+  auto take = [&](int64_t bytes) -> void* {
+    off = (off + 255) & ~size_t(255);
+    void* p = base ? static_cast<char*>(base) + off : nullptr;
+    off += static_cast<size_t>(std::max<int64_t>(bytes, 0));
+    return p;
+  };
+  Ws t;
+  t.pos_tab = static_cast<float2*>(take(T * half * 8));
+  t.dtab = static_cast<float2*>(take(std::min<int64_t>(std::max<int64_t>(C, 1), kMaxChunksPerLaunch) * half * 8));
+  t.tokens = static_cast<int32_t*>(take(T * 4));
+  t.x0 = static_cast<float*>(take(T * c.d_model * 4));
+  t.x1 = static_cast<float*>(take(T * c.d_model * 4));
+  t.act = take(T * c.d_model * es);
+  t.h = take(T * c.d_ff * es);
+  t.q = take(T * qw * es);
+  t.o = take(T * qw * es);
+  t.kvf = static_cast<float*>(take(T * 2 * kvw * 4));
+  t.dev = static_cast<float*>(take(N * 4));
+  t.posA = static_cast<int32_t*>(take(N * 4));
+  t.posB = static_cast<int32_t*>(take(N * 4));
+  t.slot = static_cast<int32_t*>(take(N * 4));
+  t.gmap = static_cast<int32_t*>(take(T * 4));
+  t.rowpos0 = static_cast<int32_t*>(take(T * 4));
+  t.rowpos1 = static_cast<int32_t*>(take(T * 4));
+  t.a_last = static_cast<float*>(take(c.d_model * 4));
+  if (w) *w = t;
+  return (off + 255) & ~size_t(255);
+}
+
+PagedRef ref_of(const cb_paged_kv& p) { return PagedRef{p.k, p.v, p.block_table, p.block_size, p.layer_stride}; }
+
+// Chunk descriptors for one launch batch [first, first + count).
+ChunkBatch make_batch(const cb_model_cfg& c, const cb_chunk* ch, int first, int count) {
+  ChunkBatch b;
+  std::memset(&b, 0, sizeof(b));
+  const int64_t width = (int64_t)c.n_kv_heads * c.head_dim;
+  int tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    const cb_chunk& x = ch[first + i];
+    ChunkDesc& d = b.d[i];
+    d.k = x.k;
+    d.v = x.v;
+    d.blk = x.block_ids;
+    d.tokens = x.tokens;
+    d.layer_stride = x.layer_stride ? x.layer_stride : (int64_t)x.len * width;
+    d.len = x.len;
+    d.new_start = x.new_start;
+    d.block_size = x.block_ids ? x.block_size : 1;
+    d.delta = x.new_start - x.old_start;
+    d.tile_begin = tiles;
+    tiles += c.n_layers * ((x.len + 15) / 16);
+  }
+  b.n = count;
+  b.total_tiles = tiles;
+  return b;
+}
+
+cb_status enqueue_rerope(const cb_model_cfg& c, const cb_chunk* ch, int n, const cb_paged_kv& dst, int copy_v,
+                         float2* dtab, hipStream_t s) {
+  const PagedRef d = ref_of(dst);
+  const int width = c.n_kv_heads * c.head_dim;
+  for (int first = 0; first < n; first += kMaxChunksPerLaunch) {
+    const int cnt = std::min(kMaxChunksPerLaunch, n - first);
+    ChunkBatch b = make_batch(c, ch, first, cnt);
+    CB_TRY(launch_rope_delta_table(dtab, b, c.head_dim, c.rope_theta, s), "rope delta table");
+    CB_TRY(launch_rerope(c.dtype, b, d, dtab, c.n_layers, width, c.head_dim, copy_v, s), "rerope");
+  }
+  return CB_OK;
+}
+
+// One selective-recompute layer (l >= 1).
+//   x_in rows: candidates (rowpos_in[0..nc)) then suffix; x_mid receives the
+//   attention-block output of the kept rows, x_out the layer output (may equal x_mid).
+struct LayerIo {
+  const float* x_in;
+  float* x_mid;
+  float* x_out;
+  const int32_t* cand_pos;
+  const int32_t* rowpos_in;
+  int32_t* rowpos_out;
+  int32_t* pos_out;
+  float* dev_slot;    // nullable [nc]
+  float* dev_by_pos;  // nullable [N]
+  int32_t* hkvd_row;  // nullable [k]
+};
+
+cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, int N, int Q, int check, int k,
+                        const LayerIo& io, const Ws& w, hipStream_t s) {
+  const cb_model_cfg& c = m.cfg;
+  const cb_layer_w& lw = m.layers[l];
+  const int d = c.d_model, F = c.d_ff;
+  const int qw = c.n_q_heads * c.head_dim;
+  const int kvw = c.n_kv_heads * c.head_dim;
+  const int es = esize(c.dtype);
+  const int rin = nc + Q;
+  const int rout = k + Q;
+
+  // fresh K (rotated at the rows' positions) and V for every candidate and suffix row
+  CB_TRY(launch_rmsnorm(c.dtype, io.x_in, nullptr, d, rin, d, lw.attn_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
+  GemmArgs g{};
+  g.A = w.act; g.lda = d; g.a_rows = nullptr;
+  g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * es; g.ldb = d;
+  g.M = rin; g.N = 2 * kvw; g.K = d;
+  g.C = w.kvf; g.ldc = 2 * kvw;
+  g.rope_cols = kvw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = io.rowpos_in;
+  CB_TRY(launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "kv gemm");
+
+  const int32_t* sel_slot = nullptr;
+  const int32_t* sel_pos = io.cand_pos;
+  int32_t* copy_out = io.pos_out;
+  if (check) {
+    float* dev = io.dev_slot ? io.dev_slot : w.dev;
+    CB_TRY(launch_deviation(c.dtype, w.kvf, w.kvf + kvw, 2 * kvw, io.cand_pos, nc, kv, l, kvw, dev, io.dev_by_pos, s),
+           "deviation");
+    CB_TRY(launch_select(dev, io.cand_pos, nc, k, io.pos_out, w.slot, s), "select");
+    sel_slot = w.slot;
+    sel_pos = io.pos_out;
+    copy_out = nullptr;
+  }
+  // row maps of the kept rows (+ suffix); an unchecked layer keeps every candidate
+  CB_TRY(launch_build_rows(sel_slot, sel_pos, k, nc, N, Q, w.gmap, io.rowpos_out, copy_out, io.hkvd_row, s),
+         "build rows");
+
+  // fill: fresh K/V of the kept rows and of the suffix replace the cache
+  CB_TRY(launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, w.gmap, io.rowpos_out, rout, kv, l, kvw, s), "scatter");
+
+  // queries of the kept rows
+  g = GemmArgs{};
+  g.A = w.act; g.lda = d; g.a_rows = w.gmap;
+  g.B = lw.w_qkv; g.ldb = d;
+  g.M = rout; g.N = qw; g.K = d;
+  g.C = w.q; g.ldc = qw;
+  g.rope_cols = qw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = io.rowpos_out;
+  CB_TRY(launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
+
+  AttnArgs at{};
+  at.q = w.q; at.ldq = qw; at.o = w.o; at.ldo = qw; at.rowpos = io.rowpos_out; at.R = rout;
+  at.cache = kv; at.layer = l; at.n_q_heads = c.n_q_heads; at.n_kv_heads = c.n_kv_heads; at.head_dim = c.head_dim;
+  at.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
+  CB_TRY(launch_attention(c.dtype, at, s), "attention");
+
+  // O projection + residual (rows gathered from x_in), then the MLP
+  g = GemmArgs{};
+  g.A = w.o; g.lda = qw; g.B = lw.w_o; g.ldb = qw; g.M = rout; g.N = d; g.K = qw;
+  g.C = io.x_mid; g.ldc = d; g.resid = io.x_in; g.resid_rows = w.gmap; g.ld_resid = d;
+  CB_TRY(launch_gemm(c.dtype, EPI_RESID, g, s), "o gemm");
+  CB_TRY(launch_rmsnorm(c.dtype, io.x_mid, nullptr, d, rout, d, lw.mlp_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
+  g = GemmArgs{};
+  g.A = w.act; g.lda = d; g.B = lw.w_gate_up; g.ldb = d; g.M = rout; g.N = F; g.K = d;
+  g.C = w.h; g.ldc = F; g.ff = F;
+  CB_TRY(launch_gemm(c.dtype, EPI_SWIGLU, g, s), "gate/up gemm");
+  g = GemmArgs{};
+  g.A = w.h; g.lda = F; g.B = lw.w_down; g.ldb = F; g.M = rout; g.N = d; g.K = F;
+  g.C = io.x_out; g.ldc = d; g.resid = io.x_mid; g.resid_rows = nullptr; g.ld_resid = d;
+  CB_TRY(launch_gemm(c.dtype, EPI_RESID, g, s), "down gemm");
+  return CB_OK;
+}
+
+// Layer 0 over every row: context K/V stay the re-RoPE'd cache, suffix K/V are computed.
+cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, float* x, const Ws& w, hipStream_t s) {
+  const cb_model_cfg& c = m.cfg;
+  const cb_layer_w& lw = m.layers[0];
+  const int d = c.d_model, F = c.d_ff;
+  const int qw = c.n_q_heads * c.head_dim;
+  const int kvw = c.n_kv_heads * c.head_dim;
+  const int es = esize(c.dtype);
+  const int T = N + Q;
+  CB_TRY(launch_rmsnorm(c.dtype, x, nullptr, d, T, d, lw.attn_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
+  GemmArgs g{};
+  g.A = w.act; g.lda = d; g.B = lw.w_qkv; g.ldb = d; g.M = T; g.N = qw; g.K = d;
+  g.C = w.q; g.ldc = qw; g.rope_cols = qw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = w.rowpos0;
+  CB_TRY(launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
+  g = GemmArgs{};
+  g.A = static_cast<const char*>(w.act) + (int64_t)N * d * es; g.lda = d;
+  g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * es; g.ldb = d;
+  g.M = Q; g.N = 2 * kvw; g.K = d; g.C = w.kvf; g.ldc = 2 * kvw;
+  g.rope_cols = kvw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = w.rowpos0 + N;
+  CB_TRY(launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "suffix kv gemm");
+  CB_TRY(launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, nullptr, w.rowpos0 + N, Q, kv, 0, kvw, s), "suffix scatter");
+  AttnArgs at{};
+  at.q = w.q; at.ldq = qw; at.o = w.o; at.ldo = qw; at.rowpos = w.rowpos0; at.R = T;
+  at.cache = kv; at.layer = 0; at.n_q_heads = c.n_q_heads; at.n_kv_heads = c.n_kv_heads; at.head_dim = c.head_dim;
+  at.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
+  CB_TRY(launch_attention(c.dtype, at, s), "attention");
+  g = GemmArgs{};
+  g.A = w.o; g.lda = qw; g.B = lw.w_o; g.ldb = qw; g.M = T; g.N = d; g.K = qw;
+  g.C = x; g.ldc = d; g.resid = x; g.ld_resid = d;
+  CB_TRY(launch_gemm(c.dtype, EPI_RESID, g, s), "o gemm");
+  CB_TRY(launch_rmsnorm(c.dtype, x, nullptr, d, T, d, lw.mlp_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
+  g = GemmArgs{};
+  g.A = w.act; g.lda = d; g.B = lw.w_gate_up; g.ldb = d; g.M = T; g.N = F; g.K = d; g.C = w.h; g.ldc = F; g.ff = F;
+  CB_TRY(launch_gemm(c.dtype, EPI_SWIGLU, g, s), "gate/up gemm");
+  g = GemmArgs{};
+  g.A = w.h; g.lda = F; g.B = lw.w_down; g.ldb = F; g.M = T; g.N = d; g.K = F;
+  g.C = x; g.ldc = d; g.resid = x; g.ld_resid = d;
+  CB_TRY(launch_gemm(c.dtype, EPI_RESID, g, s), "down gemm");
+  return CB_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// public entry points
+// ===========================================================================
+extern "C" {
+
+int32_t cb_abi_version(void) { return CB_ABI_VERSION; }
+
+const char* cb_last_error(void) { return g_last_error.c_str(); }
+
+const char* cb_status_string(int32_t st) {
+  switch (st) {
+    case CB_OK: return "CB_OK";
+    case CB_ERR_INVALID: return "CB_ERR_INVALID";
+    case CB_ERR_UNSUPPORTED: return "CB_ERR_UNSUPPORTED";
+    case CB_ERR_WORKSPACE: return "CB_ERR_WORKSPACE";
+    case CB_ERR_DEVICE: return "CB_ERR_DEVICE";
+    default: return "CB_UNKNOWN_STATUS";
+  }
+}
+
+size_t cb_workspace_bytes(const cb_model_cfg* cfg, int32_t n_ctx, int32_t n_query, int32_t n_chunks) {
+  if (check_cfg(cfg) != CB_OK || n_ctx < 0 || n_query < 0 || n_chunks < 0) return 0;
+  return carve(*cfg, n_ctx, n_query, n_chunks, nullptr, nullptr);
+}
+
+cb_status cb_rerope_k(const cb_model_cfg* cfg, const cb_chunk* chunks, int32_t n_chunks, const cb_paged_kv* dst,
+                      uint32_t flags, void* ws, size_t ws_bytes, cb_stream_t stream) {
+  cb_status st = check_cfg(cfg);
+  if (st != CB_OK) return st;
+  if ((st = check_chunk_sources(cfg, chunks, n_chunks, false)) != CB_OK) return st;
+  int64_t end = 0;
+  for (int i = 0; i < n_chunks; ++i) end = std::max<int64_t>(end, (int64_t)chunks[i].new_start + chunks[i].len);
+  if ((st = check_paged(cfg, dst, end, "dst")) != CB_OK) return st;
+  if (flags & ~CB_COPY_V) return fail(CB_ERR_INVALID, "unknown flags 0x%x", flags);
+  const size_t need = cb_workspace_bytes(cfg, 0, 0, n_chunks);
+  if (n_chunks > 0 && (!ws || ws_bytes < need))
+    return fail(CB_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, need);
+  if (ws && !aligned16(ws)) return fail(CB_ERR_INVALID, "workspace not 16-byte aligned");
+  Ws w;
+  carve(*cfg, 0, 0, n_chunks, ws, &w);
+  st = enqueue_rerope(*cfg, chunks, n_chunks, *dst, (flags & CB_COPY_V) ? 1 : 0, w.dtab,
+                      reinterpret_cast<hipStream_t>(stream));
+  return st == CB_OK ? ok() : st;
+}
+
+cb_status cb_kv_deviation(const cb_model_cfg* cfg, int32_t layer, const float* k_fresh, const float* v_fresh,
+                          int64_t row_stride, const int32_t* pos, int32_t n_rows, const cb_paged_kv* cache,
+                          float* dev_out, cb_stream_t stream) {
+  cb_status st = check_cfg(cfg);
+  if (st != CB_OK) return st;
+  if (layer < 0 || layer >= cfg->n_layers) return fail(CB_ERR_INVALID, "layer %d out of range", layer);
+  if (n_rows < 0) return fail(CB_ERR_INVALID, "n_rows < 0");
+  if ((st = check_paged(cfg, cache, 0, "cache")) != CB_OK) return st;
+  if (n_rows == 0) return ok();
+  if (!k_fresh || !v_fresh || !pos || !dev_out) return fail(CB_ERR_INVALID, "NULL pointer");
+  const int64_t kvw = (int64_t)cfg->n_kv_heads * cfg->head_dim;
+  if (row_stride < kvw || row_stride % 4) return fail(CB_ERR_INVALID, "row_stride must be >= %lld and a multiple of 4", (long long)kvw);
+  if (!aligned16(k_fresh) || !aligned16(v_fresh)) return fail(CB_ERR_INVALID, "fresh rows not 16-byte aligned");
+  CB_TRY(launch_deviation(cfg->dtype, k_fresh, v_fresh, row_stride, pos, n_rows, ref_of(*cache), layer, (int)kvw,
+                          dev_out, nullptr, reinterpret_cast<hipStream_t>(stream)),
+         "deviation");
+  return ok();
+}
+
+cb_status cb_select_hkvd(const float* dev, const int32_t* pos, int32_t n_cand, int32_t k, int32_t* sel_pos,
+                         int32_t* sel_slot, void* ws, size_t ws_bytes, cb_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (n_cand < 0) return fail(CB_ERR_INVALID, "n_cand < 0");
+  if (k < 0 || k > n_cand) return fail(CB_ERR_INVALID, "k = %d outside [0, %d]", k, n_cand);
+  if (k == 0) return ok();
+  if (!dev || !pos || !sel_pos) return fail(CB_ERR_INVALID, "NULL pointer");
+  CB_TRY(launch_select(dev, pos, n_cand, k, sel_pos, sel_slot, reinterpret_cast<hipStream_t>(stream)), "select");
+  return ok();
+}
+
+cb_status cb_blend_layer(const cb_model* model, int32_t layer, const cb_paged_kv* kv, const int32_t* pos_in,
+                         int32_t n_cand, int32_t n_ctx, int32_t n_query, float* x, int32_t check_flag, int32_t k_keep,
+                         int32_t* pos_out, float* dev_out, void* ws, size_t ws_bytes, cb_stream_t stream) {
+  cb_status st = check_model(model);
+  if (st != CB_OK) return st;
+  const cb_model_cfg& c = model->cfg;
+  if (layer < 1 || layer >= c.n_layers) return fail(CB_ERR_INVALID, "layer %d outside [1, %d)", layer, c.n_layers);
+  if (n_cand < 0 || n_ctx < 0 || n_cand > n_ctx) return fail(CB_ERR_INVALID, "need 0 <= n_cand <= n_ctx");
+  if (n_query < 1) return fail(CB_ERR_INVALID, "n_query must be >= 1");
+  if (k_keep < 0 || k_keep > n_cand) return fail(CB_ERR_INVALID, "k_keep %d outside [0, %d]", k_keep, n_cand);
+  if (!check_flag && k_keep != n_cand) return fail(CB_ERR_INVALID, "an unchecked layer keeps every candidate");
+  if ((st = check_paged(&c, kv, (int64_t)n_ctx + n_query, "kv")) != CB_OK) return st;
+  if (!x || (n_cand > 0 && !pos_in) || (k_keep > 0 && !pos_out)) return fail(CB_ERR_INVALID, "NULL pointer");
+  if (!aligned16(x)) return fail(CB_ERR_INVALID, "x not 16-byte aligned");
+  const size_t need = cb_workspace_bytes(&c, n_ctx, n_query, 0);
+  if (!ws || ws_bytes < need) return fail(CB_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(CB_ERR_INVALID, "workspace not 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Ws w;
+  carve(c, n_ctx, n_query, 0, ws, &w);
+  const PagedRef r = ref_of(*kv);
+  CB_TRY(launch_rope_pos_table(w.pos_tab, n_ctx + n_query, c.head_dim, c.rope_theta, s), "rope table");
+  CB_TRY(launch_build_rows(nullptr, pos_in, n_cand, n_cand, n_ctx, n_query, nullptr, w.rowpos0, nullptr, nullptr, s),
+         "rows");
+  LayerIo io{};
+  io.x_in = x;
+  io.x_mid = w.x1;
+  io.x_out = x;
+  io.cand_pos = pos_in;
+  io.rowpos_in = w.rowpos0;
+  io.rowpos_out = w.rowpos1;
+  io.pos_out = pos_out;
+  io.dev_slot = dev_out;
+  st = enqueue_layer(*model, layer, r, n_cand, n_ctx, n_query, check_flag ? 1 : 0, k_keep, io, w, s);
+  return st == CB_OK ? ok() : st;
+}
+
+cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_t n_chunks,
+                           const int32_t* query_tokens, int32_t n_query, const cb_blend_params* params,
+                           const cb_paged_kv* blended, float* logits, int32_t* hkvd_out, float* dev_out, void* ws,
+                           size_t ws_bytes, cb_stream_t stream) {
+  cb_status st = check_model(model);
+  if (st != CB_OK) return st;
+  const cb_model_cfg& c = model->cfg;
+  if ((st = check_chunk_sources(&c, chunks, n_chunks, true)) != CB_OK) return st;
+  int64_t N64 = 0;
+  if ((st = check_tiling(chunks, n_chunks, &N64)) != CB_OK) return st;
+  const int N = static_cast<int>(N64);
+  if (n_query < 1) return fail(CB_ERR_INVALID, "n_query must be >= 1");
+  if (!query_tokens || !logits) return fail(CB_ERR_INVALID, "NULL query_tokens or logits");
+  if (!params || !params->k_per_layer || !params->check) return fail(CB_ERR_INVALID, "NULL params");
+  if (params->flags) return fail(CB_ERR_INVALID, "unknown params flags 0x%x", params->flags);
+  const int L = c.n_layers;
+  if (params->k_per_layer[0] != N)
+    return fail(CB_ERR_INVALID, "k_per_layer[0] = %d, layer 0 runs in full (N = %d)", params->k_per_layer[0], N);
+  for (int l = 1; l < L; ++l) {
+    const int k = params->k_per_layer[l], kp = params->k_per_layer[l - 1];
+    if (k < 0 || k > kp)
+      return fail(CB_ERR_INVALID, "k_per_layer[%d] = %d must lie in [0, k_per_layer[%d] = %d]", l, k, l - 1, kp);
+    if (!params->check[l] && k != kp)
+      return fail(CB_ERR_INVALID, "layer %d is unchecked but shrinks the set (%d -> %d)", l, kp, k);
+  }
+  if ((st = check_paged(&c, blended, N64 + n_query, "blended")) != CB_OK) return st;
+  if (!aligned16(logits)) return fail(CB_ERR_INVALID, "logits not 16-byte aligned");
+  const size_t need = cb_workspace_bytes(&c, N, n_query, n_chunks);
+  if (!ws || ws_bytes < need) return fail(CB_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(CB_ERR_INVALID, "workspace not 16-byte aligned");
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int Q = n_query;
+  const int T = N + Q;
+  Ws w;
+  carve(c, N, Q, n_chunks, ws, &w);
+  const PagedRef kv = ref_of(*blended);
+
+  // a1: assemble + re-RoPE every layer of every chunk
+  if ((st = enqueue_rerope(c, chunks, n_chunks, *blended, 1, w.dtab, s)) != CB_OK) return st;
+  CB_TRY(launch_rope_pos_table(w.pos_tab, T, c.head_dim, c.rope_theta, s), "rope table");
+  // a2: tokens in new-position order, then embeddings
+  {
+    std::vector<cb_chunk> all(chunks, chunks + n_chunks);
+    cb_chunk qc{};
+    qc.tokens = query_tokens;
+    qc.len = Q;
+    qc.new_start = N;
+    all.push_back(qc);
+    for (size_t first = 0; first < all.size(); first += kMaxChunksPerLaunch) {
+      const int cnt = std::min<int>(kMaxChunksPerLaunch, static_cast<int>(all.size() - first));
+      ChunkBatch b = make_batch(c, all.data(), static_cast<int>(first), cnt);
+      CB_TRY(launch_gather_tokens(b, w.tokens, s), "gather tokens");
+    }
+  }
+  CB_TRY(launch_embed(c.dtype, w.tokens, T, model->embed, c.d_model, w.x0, s), "embed");
+  CB_TRY(launch_iota(w.rowpos0, T, 0, s), "iota");
+  CB_TRY(launch_iota(w.posA, N, 0, s), "iota");
+  if (hkvd_out) CB_TRY(launch_iota(hkvd_out, N, 0, s), "iota");
+
+  // a3: layer 0 in full
+  if ((st = enqueue_layer0(*model, kv, N, Q, w.x0, w, s)) != CB_OK) return st;
+
+  // layers 1 .. L-1
+  float* xcur = w.x0;
+  float* xoth = w.x1;
+  int32_t* cand = w.posA;
+  int32_t* nxt = w.posB;
+  int32_t* rp_in = w.rowpos0;
+  int32_t* rp_out = w.rowpos1;
+  int nc = N;
+  for (int l = 1; l < L; ++l) {
+    const int k = params->k_per_layer[l];
+    const int chk = params->check[l] ? 1 : 0;
+    LayerIo io{};
+    io.x_in = xcur;
+    io.x_mid = xoth;
+    io.x_out = xoth;
+    io.cand_pos = cand;
+    io.rowpos_in = rp_in;
+    io.rowpos_out = rp_out;
+    io.pos_out = nxt;
+    io.dev_slot = nullptr;
+    io.dev_by_pos = (chk && dev_out) ? dev_out + (int64_t)l * N : nullptr;
+    io.hkvd_row = hkvd_out ? hkvd_out + (int64_t)l * N : nullptr;
+    if ((st = enqueue_layer(*model, l, kv, nc, N, Q, chk, k, io, w, s)) != CB_OK) return st;
+    std::swap(xcur, xoth);
+    std::swap(cand, nxt);
+    std::swap(rp_in, rp_out);
+    nc = k;
+  }
+
+  // a12: final norm of the last position, LM head
+  const int R = nc + Q;
+  CB_TRY(launch_rmsnorm(c.dtype, xcur + (int64_t)(R - 1) * c.d_model, nullptr, c.d_model, 1, c.d_model,
+                        model->final_norm, c.rms_eps, w.a_last, c.d_model, 1, s),
+         "final norm");
+  CB_TRY(launch_lmhead(c.dtype, w.a_last, model->lm_head, c.vocab, c.d_model, logits, s), "lm head");
+  return ok();
+}
+
+}  // extern "C"

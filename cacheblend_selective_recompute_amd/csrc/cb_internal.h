@@ -1,0 +1,162 @@
+// Internal declarations shared by the HIP translation units of libcacheblend.
+// Not part of the public ABI (include/cacheblend.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cacheblend.h"
+
+namespace cb {
+
+// bf16 is carried as its 16-bit pattern; arithmetic is always fp32.
+using bf16_t = uint16_t;
+
+__host__ __device__ __forceinline__ float bf2f(bf16_t u) {
+  union { uint32_t i; float f; } c;
+  c.i = static_cast<uint32_t>(u) << 16;
+  return c.f;
+}
+
+// fp32 -> bf16, round to nearest even.
+__host__ __device__ __forceinline__ bf16_t f2bf(float f) {
+  union { uint32_t i; float f; } c;
+  c.f = f;
+  uint32_t u = c.i;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+// Reference to a paged cache (see cb_paged_kv).
+struct PagedRef {
+  void* k;
+  void* v;
+  const int32_t* bt;   // block table; NULL = identity (contiguous)
+  int32_t bs;          // block size
+  int64_t layer_stride;
+};
+
+// Element offset of token `pos` in one layer of a paged pool.
+__device__ __forceinline__ int64_t paged_row(const int32_t* bt, int32_t bs, int32_t pos) {
+  if (bt == nullptr) return pos;
+  return static_cast<int64_t>(bt[pos / bs]) * bs + (pos % bs);
+}
+
+// Chunk descriptors are passed by value in kernel arguments.
+constexpr int kMaxChunksPerLaunch = 32;
+struct ChunkDesc {
+  const void* k;
+  const void* v;
+  const int32_t* blk;     // NULL = contiguous source
+  const int32_t* tokens;
+  int64_t layer_stride;   // elements
+  int32_t len;
+  int32_t new_start;
+  int32_t block_size;
+  int32_t delta;          // new_start - old_start
+  int32_t tile_begin;     // first flat tile of this chunk (re-RoPE grid)
+  int32_t pad;
+};
+struct ChunkBatch {
+  ChunkDesc d[kMaxChunksPerLaunch];
+  int32_t n;
+  int32_t total_tiles;
+};
+
+// ---------------------------------------------------------------------------
+// launchers (return hipSuccess or the launch error)
+// ---------------------------------------------------------------------------
+
+// cos/sin(pos * theta_i) for pos in [0, rows): float2 [rows][dh/2]
+hipError_t launch_rope_pos_table(float2* out, int rows, int head_dim, double theta, hipStream_t s);
+// cos/sin(delta_c * theta_i) per chunk of the batch: float2 [n][dh/2]
+hipError_t launch_rope_delta_table(float2* out, const ChunkBatch& b, int head_dim, double theta,
+                                   hipStream_t s);
+// assemble + rotate: K rotated by the chunk's delta, V copied when copy_v
+hipError_t launch_rerope(cb_dtype dt, const ChunkBatch& b, const PagedRef& dst, const float2* dtab,
+                         int n_layers, int width, int head_dim, int copy_v, hipStream_t s);
+// tokens of the batch's chunks placed at their new_start (plus any extra desc)
+hipError_t launch_gather_tokens(const ChunkBatch& b, int32_t* out, hipStream_t s);
+// x[t][:] = embed[tok[t]][:] (fp32 out)
+hipError_t launch_embed(cb_dtype dt, const int32_t* tok, int rows, const void* embed, int d, float* x,
+                        hipStream_t s);
+// out[i] = RMSNorm(x[ridx ? ridx[i] : i]) * g, out in model dtype (or fp32 when out_f32)
+hipError_t launch_rmsnorm(cb_dtype dt, const float* x, const int32_t* ridx, int64_t ldx, int rows, int d,
+                          const float* g, float eps, void* out, int64_t ldo, int out_f32, hipStream_t s);
+// dev[i] = ||kf[i]-K[pos[i]]||^2 + ||vf[i]-V[pos[i]]||^2 ; optionally dev_by_pos[pos[i]] = dev[i]
+hipError_t launch_deviation(cb_dtype dt, const float* kf, const float* vf, int64_t ldf, const int32_t* pos,
+                            int n, const PagedRef& cache, int layer, int width, float* dev,
+                            float* dev_by_pos, hipStream_t s);
+// exact top-k by (dev desc, pos asc); outputs ascending
+hipError_t launch_select(const float* dev, const int32_t* pos, int n, int k, int32_t* sel_pos,
+                         int32_t* sel_slot, hipStream_t s);
+// row maps after selection: gmap[i] (source row), rowpos[i] (position), for i < k + nq
+// copy_a / copy_b (nullable) also receive the kept positions [k]
+hipError_t launch_build_rows(const int32_t* sel_slot, const int32_t* sel_pos, int k, int nc, int n_ctx,
+                             int nq, int32_t* gmap, int32_t* rowpos, int32_t* copy_a, int32_t* copy_b,
+                             hipStream_t s);
+// cache[layer][rowpos[i]] <- model dtype of kvf[gmap ? gmap[i] : i] (K: cols [0,W), V: cols [W,2W))
+hipError_t launch_scatter_kv(cb_dtype dt, const float* kvf, int64_t ldf, const int32_t* gmap,
+                             const int32_t* rowpos, int n, const PagedRef& cache, int layer, int width,
+                             hipStream_t s);
+// logits[v] = sum_d a[d] * W[v][d]
+hipError_t launch_lmhead(cb_dtype dt, const float* a, const void* w, int vocab, int d, float* logits,
+                         hipStream_t s);
+hipError_t launch_iota(int32_t* out, int n, int32_t base, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// GEMM: C[M][N] = A[M][K] * B[N][K]^T with a fused epilogue.
+// ---------------------------------------------------------------------------
+enum GemmEpi : int {
+  EPI_STORE_ROPE = 0,   // C (model dtype) = acc, RoPE on columns < rope_cols at row_pos
+  EPI_F32_ROPE = 1,     // C (fp32) = acc, RoPE on columns < rope_cols at row_pos
+  EPI_RESID = 2,        // C (fp32)[i] = resid[resid_rows ? resid_rows[i] : i] + acc
+  EPI_SWIGLU = 3,       // C (model dtype)[i][f] = SiLU(A.Wg[f]) * (A.Wu[f]); B rows [0,ff) gate, [ff,2ff) up
+};
+struct GemmArgs {
+  const void* A;
+  int64_t lda;
+  const int32_t* a_rows;   // row gather for A (NULL = identity)
+  const void* B;
+  int64_t ldb;
+  int M, N, K;             // N = output columns (features for SWIGLU)
+  void* C;
+  int64_t ldc;
+  int rope_cols;
+  int head_dim;
+  const float2* rope_tab;  // [pos][head_dim/2]
+  const int32_t* row_pos;  // [M]
+  const float* resid;
+  const int32_t* resid_rows;
+  int64_t ld_resid;
+  int ff;                  // SWIGLU: row offset of the up half in B
+};
+hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Attention of query rows over a paged cache (causal by absolute position).
+// q/o: [R][Hq*dh] in the model dtype; rowpos[R] ascending.
+// ---------------------------------------------------------------------------
+struct AttnArgs {
+  const void* q;
+  int64_t ldq;
+  void* o;
+  int64_t ldo;
+  const int32_t* rowpos;
+  int R;
+  PagedRef cache;
+  int layer;
+  int n_q_heads, n_kv_heads, head_dim;
+  float scale;
+};
+hipError_t launch_attention(cb_dtype dt, const AttnArgs& a, hipStream_t s);
+bool attention_supported(cb_dtype dt, int n_q_heads, int n_kv_heads, int head_dim);
+
+}  // namespace cb

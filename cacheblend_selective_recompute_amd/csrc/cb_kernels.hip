@@ -1,0 +1,536 @@
+// HBM-bound kernels of the blended prefill: rotation tables, re-RoPE +
+// assembly, embedding, RMSNorm, KV deviation, exact top-k, row maps, the
+// paged K/V scatter and the LM-head GEMV.
+//
+// Method: "CacheBlend 完全拆解" (pinghaoyang.com.cn) -- section "位置恢复"
+// (k' = R_{n-p} k_p, V untouched), section "核心思想" (eq. Δkv, per-token KV
+// deviation), section "选 token" (keep the highest-deviation tokens, sets only
+// shrink), Fig. 5 (fresh K/V of the selected tokens fill the cache).
+#include "cb_internal.h"
+
+namespace cb {
+
+namespace {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// 16-byte vector helpers: 8 bf16 or 4 fp32 elements.
+template <typename T> struct V16;
+template <> struct V16<bf16_t> { static constexpr int N = 8; };
+template <> struct V16<float> { static constexpr int N = 4; };
+
+__device__ __forceinline__ void unpack(const uint4& v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf2f(static_cast<bf16_t>(w[i] & 0xFFFFu));
+    f[2 * i + 1] = bf2f(static_cast<bf16_t>(w[i] >> 16));
+  }
+}
+__device__ __forceinline__ uint4 pack(const float (&f)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = static_cast<uint32_t>(f2bf(f[2 * i])) | (static_cast<uint32_t>(f2bf(f[2 * i + 1])) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ---------------------------------------------------------------------------
+// rotation tables: cos/sin of (multiplier * theta_i), theta_i = base^(-2i/dh),
+// evaluated in fp64 and rounded once to fp32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float2 rot_entry(double mult, int i, int dh, double theta) {
+  const double inv = pow(theta, -(2.0 * i) / static_cast<double>(dh));
+  const double ang = mult * inv;
+  double s, c;
+  sincos(ang, &s, &c);
+  return make_float2(static_cast<float>(c), static_cast<float>(s));
+}
+
+__global__ void rope_pos_table_kernel(float2* out, int rows, int half, int dh, double theta) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(rows) * half) return;
+  const int r = static_cast<int>(idx / half);
+  const int i = static_cast<int>(idx % half);
+  out[idx] = rot_entry(static_cast<double>(r), i, dh, theta);
+}
+
+__global__ void rope_delta_table_kernel(float2* out, ChunkBatch b, int half, int dh, double theta) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= b.n * half) return;
+  const int c = idx / half;
+  const int i = idx % half;
+  out[idx] = rot_entry(static_cast<double>(b.d[c].delta), i, dh, theta);
+}
+
+// ---------------------------------------------------------------------------
+// re-RoPE + assembly.  One block = kTokTile tokens of one (chunk, layer);
+// every thread moves 16-byte vectors, four in flight.
+// ---------------------------------------------------------------------------
+constexpr int kTokTile = 16;
+constexpr int kRerope = 256;
+
+template <typename T>
+__global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef dst, const float2* dtab,
+                                                         int n_layers, int width, int dh, int copy_v) {
+  constexpr int VN = V16<T>::N;
+  const int tile = blockIdx.x;
+  int c = 0;
+  while (c + 1 < b.n && tile >= b.d[c + 1].tile_begin) ++c;
+  const ChunkDesc cd = b.d[c];
+  const int ntile = (cd.len + kTokTile - 1) / kTokTile;
+  const int local = tile - cd.tile_begin;
+  const int layer = local / ntile;
+  const int t0 = (local % ntile) * kTokTile;
+  const int ntok = min(kTokTile, cd.len - t0);
+  const int vpr = width / VN;                   // vectors per token row
+  const int nvec = ntok * vpr;
+  const int64_t src_stride = cd.layer_stride;
+  const T* srck = static_cast<const T*>(cd.k) + layer * src_stride;
+  const T* srcv = static_cast<const T*>(cd.v) + layer * src_stride;
+  T* dk = static_cast<T*>(dst.k) + layer * dst.layer_stride;
+  T* dv = static_cast<T*>(dst.v) + layer * dst.layer_stride;
+  const float2* tab = dtab + static_cast<int64_t>(c) * (dh / 2);
+
+  constexpr int U = 4;
+  for (int base = threadIdx.x; base < nvec; base += kRerope * U) {
+    uint4 kv[U], vv[U];
+    int64_t so[U], dof[U];
+    int e0[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = base + u * kRerope;
+      ok[u] = v < nvec;
+      const int tt = ok[u] ? v / vpr : 0;
+      e0[u] = (v % vpr) * VN;
+      const int t = t0 + tt;
+      const int64_t srow = cd.blk ? static_cast<int64_t>(cd.blk[t / cd.block_size]) * cd.block_size + t % cd.block_size
+                                  : static_cast<int64_t>(t);
+      so[u] = srow * width + e0[u];
+      dof[u] = paged_row(dst.bt, dst.bs, cd.new_start + t) * width + e0[u];
+      if (ok[u]) {
+        kv[u] = *reinterpret_cast<const uint4*>(srck + so[u]);
+        if (copy_v) vv[u] = *reinterpret_cast<const uint4*>(srcv + so[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!ok[u]) continue;
+      float f[8];
+      if constexpr (VN == 8) {
+        unpack(kv[u], f);
+      } else {
+        f[0] = __uint_as_float(kv[u].x); f[1] = __uint_as_float(kv[u].y);
+        f[2] = __uint_as_float(kv[u].z); f[3] = __uint_as_float(kv[u].w);
+      }
+#pragma unroll
+      for (int j = 0; j < VN; j += 2) {
+        const float2 cs = tab[((e0[u] + j) % dh) >> 1];
+        const float x0 = f[j], x1 = f[j + 1];
+        f[j] = x0 * cs.x - x1 * cs.y;
+        f[j + 1] = x0 * cs.y + x1 * cs.x;
+      }
+      uint4 o;
+      if constexpr (VN == 8) {
+        o = pack(f);
+      } else {
+        o = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+      }
+      *reinterpret_cast<uint4*>(dk + dof[u]) = o;
+      if (copy_v) *reinterpret_cast<uint4*>(dv + dof[u]) = vv[u];
+    }
+  }
+}
+
+__global__ void gather_tokens_kernel(ChunkBatch b, int32_t* out) {
+  const ChunkDesc cd = b.d[blockIdx.y];
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < cd.len; i += gridDim.x * blockDim.x)
+    out[cd.new_start + i] = cd.tokens[i];
+}
+
+// ---------------------------------------------------------------------------
+// embedding gather (fp32 residual stream)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void embed_kernel(const int32_t* tok, const T* emb, int d, float* x) {
+  const int r = blockIdx.x;
+  const T* src = emb + static_cast<int64_t>(tok[r]) * d;
+  float* dst = x + static_cast<int64_t>(r) * d;
+  for (int e = threadIdx.x; e < d; e += blockDim.x) dst[e] = to_f<T>(src[e]);
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm: one 256-thread block per row; fp32 statistics reduced in fixed order
+// ---------------------------------------------------------------------------
+template <typename TO>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const int32_t* ridx, int64_t ldx, int d,
+                                                      const float* g, float eps, TO* out, int64_t ldo) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const int src = ridx ? ridx[r] : r;
+  const float* xr = x + static_cast<int64_t>(src) * ldx;
+  float ss = 0.f;
+  for (int e = threadIdx.x * 4; e < d; e += 256 * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + e);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
+  TO* o = out + static_cast<int64_t>(r) * ldo;
+  for (int e = threadIdx.x * 4; e < d; e += 256 * 4) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + e);
+    const float4 gg = *reinterpret_cast<const float4*>(g + e);
+    o[e + 0] = from_f<TO>(v.x * inv * gg.x);
+    o[e + 1] = from_f<TO>(v.y * inv * gg.y);
+    o[e + 2] = from_f<TO>(v.z * inv * gg.z);
+    o[e + 3] = from_f<TO>(v.w * inv * gg.w);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KV deviation: one wave per row, fp32 accumulation in fixed order
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void deviation_kernel(const float* kf, const float* vf, int64_t ldf,
+                                                        const int32_t* pos, int n, PagedRef cache, int layer,
+                                                        int width, float* dev, float* dev_by_pos) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const int p = pos[row];
+  const int64_t off = static_cast<int64_t>(layer) * cache.layer_stride + paged_row(cache.bt, cache.bs, p) * width;
+  const T* ck = static_cast<const T*>(cache.k) + off;
+  const T* cv = static_cast<const T*>(cache.v) + off;
+  const float* fk = kf + static_cast<int64_t>(row) * ldf;
+  const float* fv = vf + static_cast<int64_t>(row) * ldf;
+  float acc = 0.f;
+  for (int e = lane * 4; e < width; e += 64 * 4) {
+    const float4 a = *reinterpret_cast<const float4*>(fk + e);
+    const float4 b = *reinterpret_cast<const float4*>(fv + e);
+    float c0[4], c1[4];
+    if constexpr (sizeof(T) == 2) {
+      const uint2 u = *reinterpret_cast<const uint2*>(ck + e);
+      const uint2 w = *reinterpret_cast<const uint2*>(cv + e);
+      c0[0] = bf2f(u.x & 0xFFFFu); c0[1] = bf2f(u.x >> 16); c0[2] = bf2f(u.y & 0xFFFFu); c0[3] = bf2f(u.y >> 16);
+      c1[0] = bf2f(w.x & 0xFFFFu); c1[1] = bf2f(w.x >> 16); c1[2] = bf2f(w.y & 0xFFFFu); c1[3] = bf2f(w.y >> 16);
+    } else {
+      const float4 u = *reinterpret_cast<const float4*>(ck + e);
+      const float4 w = *reinterpret_cast<const float4*>(cv + e);
+      c0[0] = u.x; c0[1] = u.y; c0[2] = u.z; c0[3] = u.w;
+      c1[0] = w.x; c1[1] = w.y; c1[2] = w.z; c1[3] = w.w;
+    }
+    const float dk0 = a.x - c0[0], dk1 = a.y - c0[1], dk2 = a.z - c0[2], dk3 = a.w - c0[3];
+    const float dv0 = b.x - c1[0], dv1 = b.y - c1[1], dv2 = b.z - c1[2], dv3 = b.w - c1[3];
+    acc += (dk0 * dk0 + dk1 * dk1) + (dk2 * dk2 + dk3 * dk3);
+    acc += (dv0 * dv0 + dv1 * dv1) + (dv2 * dv2 + dv3 * dv3);
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) {
+    dev[row] = acc;
+    if (dev_by_pos) dev_by_pos[p] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// exact top-k (one 1024-thread block): radix select of the k-th largest key on
+// the order-preserving bit pattern of dev, then a stable compaction in
+// candidate order (ties: the first ones, i.e. the smaller positions).
+// ---------------------------------------------------------------------------
+constexpr int kSel = 1024;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// exclusive block scan of a 0/1 flag; returns prefix, writes total
+__device__ __forceinline__ int block_flag_scan(bool flag, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const uint64_t m = __ballot(flag);
+  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[wid] = __popcll(m);
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int w = 0; w < kSel / 64; ++w) {
+    const int c = wsum[w];
+    if (w < wid) before += c;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + in_wave;
+}
+
+__global__ __launch_bounds__(kSel) void select_kernel(const float* dev, const int32_t* pos, int n, int k,
+                                                      int32_t* sel_pos, int32_t* sel_slot) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_digit, s_rem;
+  __shared__ int wsum[kSel / 64];
+  if (k <= 0) return;
+  if (k >= n) {
+    for (int i = threadIdx.x; i < n; i += kSel) {
+      sel_pos[i] = pos[i];
+      if (sel_slot) sel_slot[i] = i;
+    }
+    return;
+  }
+  uint32_t prefix = 0, mask = 0;
+  uint32_t rem = static_cast<uint32_t>(k);
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = threadIdx.x; i < 256; i += kSel) hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += kSel) {
+      const uint32_t key = order_key(dev[i]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t cum = 0;
+      for (int dg = 255; dg >= 0; --dg) {
+        const uint32_t h = hist[dg];
+        if (cum + h >= rem) {
+          s_digit = static_cast<uint32_t>(dg);
+          s_rem = rem - cum;
+          break;
+        }
+        cum += h;
+      }
+    }
+    __syncthreads();
+    prefix |= s_digit << shift;
+    mask |= 255u << shift;
+    rem = s_rem;
+    __syncthreads();
+  }
+  // prefix = key of the k-th largest; take every larger key and the first `rem` equal ones
+  int out_base = 0, eq_base = 0;
+  for (int base = 0; base < n; base += kSel) {
+    const int i = base + threadIdx.x;
+    uint32_t key = 0;
+    if (i < n) key = order_key(dev[i]);
+    const bool gt = i < n && key > prefix;
+    const bool eq = i < n && key == prefix;
+    int eq_tot = 0;
+    const int eq_before = block_flag_scan(eq, wsum, &eq_tot) + eq_base;
+    const bool take = gt || (eq && eq_before < static_cast<int>(rem));
+    int take_tot = 0;
+    const int o = block_flag_scan(take, wsum, &take_tot) + out_base;
+    if (take && o < k) {
+      sel_pos[o] = pos[i];
+      if (sel_slot) sel_slot[o] = i;
+    }
+    out_base += take_tot;
+    eq_base += eq_tot;
+  }
+}
+
+__global__ void build_rows_kernel(const int32_t* sel_slot, const int32_t* sel_pos, int k, int nc, int n_ctx, int nq,
+                                  int32_t* gmap, int32_t* rowpos, int32_t* copy_a, int32_t* copy_b) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= k + nq) return;
+  int g, p;
+  if (i < k) {
+    g = sel_slot ? sel_slot[i] : i;
+    p = sel_pos[i];
+    if (copy_a) copy_a[i] = p;
+    if (copy_b) copy_b[i] = p;
+  } else {
+    g = nc + (i - k);
+    p = n_ctx + (i - k);
+  }
+  if (gmap) gmap[i] = g;
+  rowpos[i] = p;
+}
+
+// ---------------------------------------------------------------------------
+// scatter fresh K/V rows (fp32) into the paged cache in the model dtype
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void scatter_kv_kernel(const float* kvf, int64_t ldf, const int32_t* gmap,
+                                                         const int32_t* rowpos, int n, PagedRef cache, int layer,
+                                                         int width) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const int src = gmap ? gmap[row] : row;
+  const float* f = kvf + static_cast<int64_t>(src) * ldf;
+  const int64_t off = static_cast<int64_t>(layer) * cache.layer_stride +
+                      paged_row(cache.bt, cache.bs, rowpos[row]) * width;
+  T* ck = static_cast<T*>(cache.k) + off;
+  T* cv = static_cast<T*>(cache.v) + off;
+  for (int e = lane * 4; e < width; e += 256) {
+    const float4 a = *reinterpret_cast<const float4*>(f + e);
+    const float4 b = *reinterpret_cast<const float4*>(f + width + e);
+    if constexpr (sizeof(T) == 2) {
+      uint2 u, w;
+      u.x = f2bf(a.x) | (static_cast<uint32_t>(f2bf(a.y)) << 16);
+      u.y = f2bf(a.z) | (static_cast<uint32_t>(f2bf(a.w)) << 16);
+      w.x = f2bf(b.x) | (static_cast<uint32_t>(f2bf(b.y)) << 16);
+      w.y = f2bf(b.z) | (static_cast<uint32_t>(f2bf(b.w)) << 16);
+      *reinterpret_cast<uint2*>(ck + e) = u;
+      *reinterpret_cast<uint2*>(cv + e) = w;
+    } else {
+      *reinterpret_cast<float4*>(ck + e) = a;
+      *reinterpret_cast<float4*>(cv + e) = b;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LM head GEMV: one wave per vocabulary row, 16-byte loads, fixed-order sum
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void lmhead_kernel(const float* a, const T* w, int vocab, int d, float* logits) {
+  extern __shared__ float sa[];
+  for (int e = threadIdx.x; e < d; e += 256) sa[e] = a[e];
+  __syncthreads();
+  constexpr int VN = V16<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int waves = gridDim.x * 4;
+  for (int v = blockIdx.x * 4 + (threadIdx.x >> 6); v < vocab; v += waves) {
+    const T* row = w + static_cast<int64_t>(v) * d;
+    float acc = 0.f;
+    for (int e = lane * VN; e < d; e += 64 * VN) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + e);
+      if constexpr (VN == 8) {
+        float f[8];
+        unpack(u, f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += f[j] * sa[e + j];
+      } else {
+        acc += __uint_as_float(u.x) * sa[e] + __uint_as_float(u.y) * sa[e + 1] +
+               __uint_as_float(u.z) * sa[e + 2] + __uint_as_float(u.w) * sa[e + 3];
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) logits[v] = acc;
+  }
+}
+
+__global__ void iota_kernel(int32_t* out, int n, int32_t base) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = base + i;
+}
+
+inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_rope_pos_table(float2* out, int rows, int head_dim, double theta, hipStream_t s) {
+  const int half = head_dim / 2;
+  const int64_t n = static_cast<int64_t>(rows) * half;
+  if (n == 0) return hipSuccess;
+  rope_pos_table_kernel<<<cdiv(n, 256), 256, 0, s>>>(out, rows, half, head_dim, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_delta_table(float2* out, const ChunkBatch& b, int head_dim, double theta, hipStream_t s) {
+  const int half = head_dim / 2;
+  const int n = b.n * half;
+  if (n == 0) return hipSuccess;
+  rope_delta_table_kernel<<<cdiv(n, 256), 256, 0, s>>>(out, b, half, head_dim, theta);
+  return hipGetLastError();
+}
+
+hipError_t launch_rerope(cb_dtype dt, const ChunkBatch& b, const PagedRef& dst, const float2* dtab, int n_layers,
+                         int width, int head_dim, int copy_v, hipStream_t s) {
+  if (b.total_tiles == 0) return hipSuccess;
+  if (dt == CB_BF16)
+    rerope_kernel<bf16_t><<<b.total_tiles, kRerope, 0, s>>>(b, dst, dtab, n_layers, width, head_dim, copy_v);
+  else
+    rerope_kernel<float><<<b.total_tiles, kRerope, 0, s>>>(b, dst, dtab, n_layers, width, head_dim, copy_v);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_tokens(const ChunkBatch& b, int32_t* out, hipStream_t s) {
+  if (b.n == 0) return hipSuccess;
+  gather_tokens_kernel<<<dim3(8, b.n), 256, 0, s>>>(b, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(cb_dtype dt, const int32_t* tok, int rows, const void* embed, int d, float* x, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (dt == CB_BF16)
+    embed_kernel<bf16_t><<<rows, 256, 0, s>>>(tok, static_cast<const bf16_t*>(embed), d, x);
+  else
+    embed_kernel<float><<<rows, 256, 0, s>>>(tok, static_cast<const float*>(embed), d, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(cb_dtype dt, const float* x, const int32_t* ridx, int64_t ldx, int rows, int d,
+                          const float* g, float eps, void* out, int64_t ldo, int out_f32, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (out_f32 || dt == CB_F32)
+    rmsnorm_kernel<float><<<rows, 256, 0, s>>>(x, ridx, ldx, d, g, eps, static_cast<float*>(out), ldo);
+  else
+    rmsnorm_kernel<bf16_t><<<rows, 256, 0, s>>>(x, ridx, ldx, d, g, eps, static_cast<bf16_t*>(out), ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_deviation(cb_dtype dt, const float* kf, const float* vf, int64_t ldf, const int32_t* pos, int n,
+                            const PagedRef& cache, int layer, int width, float* dev, float* dev_by_pos,
+                            hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (dt == CB_BF16)
+    deviation_kernel<bf16_t><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
+  else
+    deviation_kernel<float><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const float* dev, const int32_t* pos, int n, int k, int32_t* sel_pos, int32_t* sel_slot,
+                         hipStream_t s) {
+  if (k == 0 || n == 0) return hipSuccess;
+  select_kernel<<<1, kSel, 0, s>>>(dev, pos, n, k, sel_pos, sel_slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_rows(const int32_t* sel_slot, const int32_t* sel_pos, int k, int nc, int n_ctx, int nq,
+                             int32_t* gmap, int32_t* rowpos, int32_t* copy_a, int32_t* copy_b, hipStream_t s) {
+  if (k + nq == 0) return hipSuccess;
+  build_rows_kernel<<<cdiv(k + nq, 256), 256, 0, s>>>(sel_slot, sel_pos, k, nc, n_ctx, nq, gmap, rowpos, copy_a,
+                                                        copy_b);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_kv(cb_dtype dt, const float* kvf, int64_t ldf, const int32_t* gmap, const int32_t* rowpos,
+                             int n, const PagedRef& cache, int layer, int width, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (dt == CB_BF16)
+    scatter_kv_kernel<bf16_t><<<cdiv(n, 4), 256, 0, s>>>(kvf, ldf, gmap, rowpos, n, cache, layer, width);
+  else
+    scatter_kv_kernel<float><<<cdiv(n, 4), 256, 0, s>>>(kvf, ldf, gmap, rowpos, n, cache, layer, width);
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead(cb_dtype dt, const float* a, const void* w, int vocab, int d, float* logits, hipStream_t s) {
+  const int grid = std::min(2048, cdiv(vocab, 4));
+  const size_t lds = static_cast<size_t>(d) * sizeof(float);
+  if (dt == CB_BF16)
+    lmhead_kernel<bf16_t><<<grid, 256, lds, s>>>(a, static_cast<const bf16_t*>(w), vocab, d, logits);
+  else
+    lmhead_kernel<float><<<grid, 256, lds, s>>>(a, static_cast<const float*>(w), vocab, d, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_iota(int32_t* out, int n, int32_t base, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  iota_kernel<<<cdiv(n, 256), 256, 0, s>>>(out, n, base);
+  return hipGetLastError();
+}
+
+}  // namespace cb

@@ -333,3 +333,70 @@ def paged_layout(n_tokens: int, block_size: int, seed: int, key: int,
     g = _rng(seed, 5, key)
     table = g.permutation(n_phys)[:n_log].astype(np.int32)
     return table, n_phys
+
+
+def synthetic_layer_rows(shape: ModelShape, n_rows: int, seed: int, key: int = 0) -> np.ndarray:
+    """Hidden rows (fp32 residual stream) for a single-layer test, iid N(0, 1)."""
+    g = _rng(seed, 9, key)
+    return g.standard_normal(size=(n_rows, shape.d_model), dtype=np.float32)
+
+
+def synthetic_layer_cache(shape: ModelShape, n_tokens: int, seed: int, spread: float = 0.5,
+                          key: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """One layer of cached K/V [n][H_kv][d_h] whose per-token scale varies
+    (lognormal with sigma ``spread``), so per-token deviations are spread out."""
+    g = _rng(seed, 10, key)
+    s0 = shape.init_std * np.sqrt(shape.d_model)
+    scale = (s0 * np.exp(spread * g.standard_normal(size=(n_tokens, 1, 1)))).astype(np.float32)
+    k = g.standard_normal(size=(n_tokens, shape.n_kv_heads, shape.head_dim), dtype=np.float32) * scale
+    v = g.standard_normal(size=(n_tokens, shape.n_kv_heads, shape.head_dim), dtype=np.float32) * scale
+    if shape.dtype == "bf16":
+        k, v = to_bf16_values(k), to_bf16_values(v)
+    return k, v
+
+
+def torch_device_weights(shape: ModelShape, seed: int, device="cuda") -> Dict[str, object]:
+    """Seeded N(0, init_std^2) weights drawn directly on the GPU with torch's
+    generator, in the library layout (w_qkv, w_o, w_gate_up, w_down; norm gains
+    1).  Used where host generation of a full model would take minutes; the
+    values differ from ``model_weights``."""
+    import torch
+    td = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=device)
+    d, F = shape.d_model, shape.d_ff
+
+    def draw(*dims):
+        t = torch.randn(*dims, generator=gen, device=device, dtype=torch.float32)
+        t.mul_(shape.init_std)
+        return t.to(td)
+
+    gen.manual_seed(int(seed) * 1000003 + 17)
+    layers = []
+    for _ in range(shape.n_layers):
+        layers.append({
+            "w_qkv": draw(shape.q_width + 2 * shape.kv_width, d),
+            "w_o": draw(d, shape.q_width),
+            "w_gate_up": draw(2 * F, d),
+            "w_down": draw(d, F),
+            "attn_norm": torch.ones(d, device=device, dtype=torch.float32),
+            "mlp_norm": torch.ones(d, device=device, dtype=torch.float32),
+        })
+    return {"layers": layers, "embed": draw(shape.vocab, d), "lm_head": draw(shape.vocab, d),
+            "final_norm": torch.ones(d, device=device, dtype=torch.float32)}
+
+
+def torch_device_chunk_kv(shape: ModelShape, lens: Sequence[int], seed: int, device="cuda"):
+    """Stand-in cached K/V per chunk drawn on the GPU ([L][len][H_kv][d_h],
+    N(0, (init_std*sqrt(d))^2)), for throughput runs."""
+    import torch
+    td = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 7919 + 3)
+    s = shape.init_std * float(np.sqrt(shape.d_model))
+    out = []
+    for l in lens:
+        dims = (shape.n_layers, l, shape.n_kv_heads, shape.head_dim)
+        k = (torch.randn(dims, generator=gen, device=device) * s).to(td)
+        v = (torch.randn(dims, generator=gen, device=device) * s).to(td)
+        out.append((k, v))
+    return out

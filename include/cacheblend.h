@@ -1,0 +1,253 @@
+/*
+ * cacheblend.h -- C ABI of the CacheBlend blended-prefill library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method ("CacheBlend 完全拆解", pinghaoyang.com.cn):
+ *   - chunks of context are prefilled separately and their KV cached; a request
+ *     concatenates the cached chunks, rotating each cached key from the
+ *     offset it was stored at to its new offset (section "位置恢复":
+ *     k' = R_{n-p} k_p = R_n k; values are not rotated);
+ *   - the first layer is computed in full; at every later layer only the
+ *     high-KV-deviation (HKVD) tokens chosen at the previous layer are
+ *     recomputed: their Q/K/V, their attention over every token, the per-token
+ *     deviation between fresh and cached K/V (section "核心思想", eq. Δkv),
+ *     and a top-k that keeps a shrinking subset (section "选 token", Fig. 9);
+ *     the fresh K/V of the kept tokens replace the cached ones (Fig. 5);
+ *   - the per-layer call mirrors the paper's prefill_layer(input_dict{check_flag,
+ *     HKVD_indices}, KVCache) (section "位置恢复、KV 存储与加载流水线");
+ *   - on any failure the caller falls back to a full prefill (section
+ *     "工程落地清单": failures sink unconditionally to full prefill), which
+ *     is cb_blend_prefill with k_per_layer[l] = N for every l.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers unless marked HOST.  The caller
+ *     owns every buffer; the library never allocates or frees memory and keeps
+ *     no pointer after the call returns.  Host arrays are read during the
+ *     call only.
+ *   - Calls are asynchronous: they validate their arguments on the host,
+ *     enqueue kernels on `stream` and return.  Device buffers must stay alive
+ *     until that stream work has completed.  No call synchronises the device.
+ *   - Validation happens before anything is enqueued.  CB_ERR_INVALID,
+ *     CB_ERR_UNSUPPORTED and CB_ERR_WORKSPACE mean nothing was written.
+ *     CB_ERR_DEVICE means a launch failed; outputs are then undefined.
+ *     cb_last_error() returns a thread-local description of the last failure.
+ *   - Device-resident values (token ids, positions, block tables) are
+ *     preconditions and are not checked: token ids in [0, vocab), candidate
+ *     positions strictly ascending and < N, block-table entries inside the
+ *     pools.
+ *   - Pointers must be 16-byte aligned; row widths are multiples of 8 elements.
+ *   - All kernels are deterministic: no floating-point atomics.
+ *   - Calls on different streams with disjoint buffers may run concurrently.
+ *   - Model storage dtype: CB_BF16 (bf16 weights and KV, bf16 x bf16 products
+ *     with fp32 accumulation on the matrix cores) or CB_F32 (fp32 throughout).
+ *     The residual stream, softmax and norm statistics are always fp32.
+ */
+#ifndef CACHEBLEND_H
+#define CACHEBLEND_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CB_ABI_VERSION 1
+
+/* A HIP stream (hipStream_t); NULL is the null stream. */
+typedef struct ihipStream_t* cb_stream_t;
+
+typedef enum {
+  CB_OK = 0,
+  CB_ERR_INVALID = -1,     /* bad argument; nothing enqueued                  */
+  CB_ERR_UNSUPPORTED = -2, /* shape outside the compiled kernels; nothing enqueued */
+  CB_ERR_WORKSPACE = -3,   /* workspace smaller than cb_workspace_bytes()     */
+  CB_ERR_DEVICE = -4       /* a kernel launch failed; outputs undefined       */
+} cb_status;
+
+typedef enum { CB_F32 = 0, CB_BF16 = 1 } cb_dtype;
+
+/* Flags */
+#define CB_COPY_V 1u /* cb_rerope_k: also copy V into the destination */
+
+/* Decoder shape.  Llama-style pre-norm block: x += Attn(RMSNorm(x)),
+ * x += W_down(SiLU(W_gate a) * W_up a) with a = RMSNorm(x); RoPE on adjacent
+ * pairs (2i, 2i+1) with theta_i = rope_theta^(-2i/head_dim); GQA with q head
+ * h reading kv head h / (n_q_heads / n_kv_heads); no biases. */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ff, vocab;
+  double rope_theta;
+  float rms_eps;
+  cb_dtype dtype;
+} cb_model_cfg;
+
+/* One decoder layer.  Matrices are row-major [out_features][in_features] in
+ * the model dtype; norm gains are fp32. */
+typedef struct {
+  const void* w_qkv;      /* [(Hq + 2 Hkv) * dh][d]: Q heads, then K heads, then V heads */
+  const void* w_o;        /* [d][Hq * dh]                                             */
+  const void* w_gate_up;  /* [2 F][d]: rows [0, F) gate, rows [F, 2F) up              */
+  const void* w_down;     /* [d][F]                                                   */
+  const float* attn_norm; /* [d]                                                      */
+  const float* mlp_norm;  /* [d]                                                      */
+} cb_layer_w;
+
+typedef struct {
+  cb_model_cfg cfg;
+  const void* embed;        /* [vocab][d] model dtype                  */
+  const float* final_norm;  /* [d]                                      */
+  const void* lm_head;      /* [vocab][d] model dtype (untied)          */
+  const cb_layer_w* layers; /* HOST array [n_layers] of device pointers */
+} cb_model;
+
+/* Paged KV cache: K and V pools laid out [layer][physical block][block_size]
+ * [n_kv_heads][head_dim] in the model dtype.  Token at logical position p of
+ * layer l lives at element offset
+ *   l * layer_stride + (block_table[p / block_size] * block_size + p % block_size) * Hkv * dh. */
+typedef struct {
+  void* k;
+  void* v;
+  const int32_t* block_table; /* [n_logical] logical -> physical block */
+  int32_t block_size;         /* tokens per block, >= 1                */
+  int32_t n_logical;          /* entries in block_table                */
+  int64_t layer_stride;       /* elements between layers               */
+} cb_paged_kv;
+
+/* One cached chunk: tokens and the KV it was prefilled into at old_start.
+ * Source KV is either contiguous [n_layers][len][Hkv][dh] (block_ids == NULL;
+ * layer_stride 0 means len * Hkv * dh) or paged like cb_paged_kv with
+ * block_ids[ceil(len / block_size)] naming the chunk's physical blocks.
+ * old_start is the offset the chunk was prefilled at (the re-RoPE source);
+ * new_start the offset it takes in this request (the target).  An unknown
+ * stored offset (-1) is rejected: a wrong position yields wrong KV. */
+typedef struct {
+  const int32_t* tokens;    /* [len] */
+  const void* k;
+  const void* v;
+  const int32_t* block_ids; /* NULL = contiguous */
+  int32_t len, old_start, new_start;
+  int32_t block_size;       /* paged source only */
+  int64_t layer_stride;     /* elements; 0 = contiguous default */
+} cb_chunk;
+
+/* Recompute schedule.  k_per_layer[0] must equal N (layer 0 runs in full);
+ * for l >= 1, k_per_layer[l] <= k_per_layer[l-1] (sets only shrink) and
+ * check[l] = 0 requires k_per_layer[l] == k_per_layer[l-1]. */
+typedef struct {
+  const int32_t* k_per_layer; /* HOST [n_layers] */
+  const uint8_t* check;       /* HOST [n_layers]; check[0] ignored */
+  uint32_t flags;             /* reserved, 0 */
+} cb_blend_params;
+
+/* ---------------------------------------------------------------------------
+ * cb_rerope_k -- assemble chunks into a paged blended cache, rotating K.
+ * ("CacheBlend 完全拆解", section "位置恢复": k' = R_{n-p} k_p.)
+ * For every chunk c, layer l and token i < len_c:
+ *   dst.K[l][new_start + i] = R_{delta_c} K_c[l][i],  delta_c = new_start - old_start,
+ * computed in fp32 from fp64 angles and rounded to the model dtype;
+ *   dst.V[l][new_start + i] = V_c[l][i] (bitwise) when flags & CB_COPY_V.
+ * dst may alias a chunk's K/V (each element is read then written by the same
+ * thread).  Chunks may be given in any order and need not tile.
+ * ws: at least cb_workspace_bytes(cfg, 0, 0, n_chunks) bytes.
+ * Errors: CB_ERR_INVALID for null pointers, old_start < 0, new_start < 0, a
+ * chunk ending beyond dst.n_logical * block_size, n_chunks < 0.
+ * ------------------------------------------------------------------------- */
+cb_status cb_rerope_k(const cb_model_cfg* cfg, const cb_chunk* chunks, int32_t n_chunks,
+                      const cb_paged_kv* dst, uint32_t flags, void* ws, size_t ws_bytes,
+                      cb_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * cb_kv_deviation -- per-token KV deviation ("CacheBlend 完全拆解", section
+ * "核心思想", eq. Δkv), squared L2 over the concatenated K and V of every KV head:
+ *   dev_out[i] = sum_e (k_fresh[i][e] - K[layer][pos[i]][e])^2
+ *              + sum_e (v_fresh[i][e] - V[layer][pos[i]][e])^2
+ * k_fresh / v_fresh: fp32 rows of Hkv * dh elements, row i at offset
+ * i * row_stride; k_fresh already rotated to pos[i].  Accumulated in fp32.
+ * Errors: CB_ERR_INVALID for null pointers, n_rows < 0, layer out of range,
+ * row_stride < Hkv * dh.
+ * ------------------------------------------------------------------------- */
+cb_status cb_kv_deviation(const cb_model_cfg* cfg, int32_t layer, const float* k_fresh,
+                          const float* v_fresh, int64_t row_stride, const int32_t* pos,
+                          int32_t n_rows, const cb_paged_kv* cache, float* dev_out,
+                          cb_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * cb_select_hkvd -- exact top-k of the candidates by deviation (section
+ * "选 token"): key = (dev descending, position ascending).  Writes the k kept
+ * positions ascending to sel_pos[k] and, when sel_slot is not NULL, their
+ * indices into the candidate arrays to sel_slot[k].  pos must be strictly
+ * ascending.  dev values are ordered by their IEEE bit pattern (a NaN ranks
+ * above +inf).  ws / ws_bytes are unused (may be NULL / 0).
+ * Errors: CB_ERR_INVALID for null pointers, k < 0, k > n_cand, n_cand < 0.
+ * ------------------------------------------------------------------------- */
+cb_status cb_select_hkvd(const float* dev, const int32_t* pos, int32_t n_cand, int32_t k,
+                         int32_t* sel_pos, int32_t* sel_slot, void* ws, size_t ws_bytes,
+                         cb_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * cb_blend_layer -- one selective-recompute layer, layer >= 1 (Fig. 5; the
+ * paper's prefill_layer(input_dict{check_flag, HKVD_indices}, KVCache)).
+ *   pos_in[n_cand]: this layer's candidates (HKVD_indices from the previous
+ *     layer), strictly ascending, < n_ctx.
+ *   x: fp32 [(n_cand + n_query)][d]: the hidden rows of the candidates in
+ *     pos_in order, then the n_query suffix rows (positions n_ctx ..
+ *     n_ctx + n_query - 1).  On return the first k_keep + n_query rows hold
+ *     the layer outputs of pos_out followed by the suffix (compacted in place).
+ *   Steps: RMSNorm; fresh K (rotated) and V for every row; when check_flag,
+ *   deviation over the candidates and top-k_keep; otherwise every candidate
+ *   is kept (k_keep must equal n_cand).  The fresh K/V of the kept rows and
+ *   of the suffix are written into kv at their positions; the other
+ *   candidates keep the cached K/V.  Then attention of the kept rows and the
+ *   suffix over positions [0, own position], O projection, residual, MLP.
+ *   pos_out[k_keep]: kept positions, ascending.
+ *   dev_out: NULL or fp32 [n_cand] deviations (written when check_flag).
+ * kv must cover positions [0, n_ctx + n_query).
+ * ws: at least cb_workspace_bytes(&model->cfg, n_ctx, n_query, 0) bytes.
+ * ------------------------------------------------------------------------- */
+cb_status cb_blend_layer(const cb_model* model, int32_t layer, const cb_paged_kv* kv,
+                         const int32_t* pos_in, int32_t n_cand, int32_t n_ctx, int32_t n_query,
+                         float* x, int32_t check_flag, int32_t k_keep, int32_t* pos_out,
+                         float* dev_out, void* ws, size_t ws_bytes, cb_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * cb_blend_prefill -- the whole blended prefill.
+ *   chunks[n_chunks]: their new_start values must tile [0, N) with no gap or
+ *     overlap (overlap resolution is the caller's, leftmost-greedy as in the
+ *     "Blend Index" article, section 6.2); old_start >= 0.
+ *   query_tokens[n_query] (n_query >= 1) sit at positions N .. N + n_query - 1.
+ *   Steps: cb_rerope_k into `blended` (K rotated, V copied); embeddings;
+ *   layer 0 in full over every row (context K/V are the re-RoPE'd cache;
+ *   suffix K/V computed); layers 1 .. L-1 as cb_blend_layer with
+ *   params->k_per_layer / check; final RMSNorm of the last row and LM head.
+ *   blended: receives every layer for positions [0, N + n_query).
+ *   logits: fp32 [vocab] of the last position.
+ *   hkvd_out: NULL or int32 [n_layers][N]; row l starts with S_l ascending
+ *     (k_per_layer[l] entries; row 0 is 0 .. N-1).
+ *   dev_out: NULL or fp32 [n_layers][N]; at a checked layer l,
+ *     dev_out[l][p] = deviation of candidate position p (other entries untouched).
+ * ws: at least cb_workspace_bytes(&model->cfg, N, n_query, n_chunks) bytes.
+ * ------------------------------------------------------------------------- */
+cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_t n_chunks,
+                           const int32_t* query_tokens, int32_t n_query,
+                           const cb_blend_params* params, const cb_paged_kv* blended,
+                           float* logits, int32_t* hkvd_out, float* dev_out, void* ws,
+                           size_t ws_bytes, cb_stream_t stream);
+
+/* Workspace bytes sufficient for every call above on a context of n_ctx
+ * tokens, n_query suffix tokens and n_chunks chunks.  Returns 0 for an invalid cfg. */
+size_t cb_workspace_bytes(const cb_model_cfg* cfg, int32_t n_ctx, int32_t n_query, int32_t n_chunks);
+
+/* Static name of a status code. */
+const char* cb_status_string(int32_t status);
+
+/* Thread-local description of the last error returned on this thread ("" if none). */
+const char* cb_last_error(void);
+
+/* CB_ABI_VERSION of the built library. */
+int32_t cb_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CACHEBLEND_H */

@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Blended-prefill throughput on one MI355X.
+
+One step = one cb_blend_prefill call over a whole request: re-RoPE assembly of
+the cached chunks into the blended cache, layer 0 in full, selective recompute
+at every later layer (K/V projection, deviation, top-k, scatter, Q projection,
+attention, O and MLP) and the final-position logits.  Chunk caches, weights and
+tokens are resident in HBM before the timed region starts.
+
+Prints one JSON line: context tokens/s (N / step time), the roofline position
+of the dominant kernel (its duration measured with HIP events on the library's
+stream during the timed region), a per-kind breakdown from an untimed traced
+step, and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps 10] [--warmup 3] [--workload 8b-4x1024-q64] [--ratio 0.15]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "blended-prefill context tokens/s @15% recompute; % HBM / MFMA roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # fp32 vector
+
+MFMA_KINDS = {"gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="8b-4x1024-q64")
+    ap.add_argument("--ratio", type=float, default=0.15)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (counter calibration)")
+    return ap.parse_args()
+
+
+class Hip:
+    """hipEvent helpers straight from the HIP runtime (the library records the events)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+            arr[i] = e
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+
+def work_per_kind(shape, N, Q, ks, sets, chunk_lens):
+    """Algorithmic FLOPs (MFMA kinds) or HBM bytes (the others) of one step.
+
+    sets[l]: positions kept at layer l (ascending), for the attention count."""
+    d, F = shape.d_model, shape.d_ff
+    qw, kvw = shape.q_width, shape.kv_width
+    es = 2 if shape.dtype == "bf16" else 4
+    L = shape.n_layers
+    T = N + Q
+    w = {k: 0.0 for k in ("rerope", "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention",
+                          "deviation", "select", "scatter", "norm", "lm_head")}
+    # layer 0: every row; context K/V from the cache
+    w["gemm_qkv"] += 2.0 * T * d * qw + 2.0 * Q * d * 2 * kvw
+    w["gemm_o"] += 2.0 * T * qw * d
+    w["gemm_gate_up"] += 2.0 * T * d * 2 * F
+    w["gemm_down"] += 2.0 * T * F * d
+    w["attention"] += 4.0 * shape.head_dim * shape.n_q_heads * (T * (T + 1) / 2.0)
+    w["scatter"] += Q * kvw * (2 * 4 + 2 * es)
+    w["norm"] += 2 * T * d * (4 + es)
+    nc = N
+    for l in range(1, L):
+        k = ks[l]
+        w["gemm_qkv"] += 2.0 * (nc + Q) * d * 2 * kvw + 2.0 * (k + Q) * d * qw
+        w["gemm_o"] += 2.0 * (k + Q) * qw * d
+        w["gemm_gate_up"] += 2.0 * (k + Q) * d * 2 * F
+        w["gemm_down"] += 2.0 * (k + Q) * F * d
+        vis = float(sum(int(p) + 1 for p in sets[l])) + sum(N + i + 1 for i in range(Q))
+        w["attention"] += 4.0 * shape.head_dim * shape.n_q_heads * vis
+        w["deviation"] += nc * (kvw * (2 * 4 + 2 * es) + 4 + 4)
+        w["select"] += nc * 8 + k * 8
+        w["scatter"] += (k + Q) * kvw * (2 * 4 + 2 * es)
+        w["norm"] += ((nc + Q) + (k + Q)) * d * (4 + es)
+        nc = k
+    w["norm"] += d * (4 + 4)
+    w["lm_head"] += shape.vocab * d * es
+    w["rerope"] += sum(chunk_lens) * L * kvw * es * 4        # K and V, read + write
+    return w
+
+
+def cpu_baseline(wl, seed):
+    """The oracle on a bounded sample of the same workload: layers 0..2 timed
+    (2 and 3 layers, the difference gives one selective layer), extrapolated to
+    the full depth."""
+    import numpy as np
+    import cbinputs
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 0) for p in threadpool_info() if p.get("internal_api") == "openblas"]
+                    or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    L = wl.shape.n_layers
+    sh3 = wl.shape.with_layers(3)
+    glob = cbinputs.global_weights(sh3, seed)
+    layers = [cbinputs.layer_weights(sh3, seed, l) for l in range(3)]
+    m = oracle.OracleModel.from_shape(sh3, {"layers": layers, **glob})
+    kvs = cbinputs.synthetic_chunk_kv(sh3, wl.chunk_lens, seed)
+    chunks = [(wl.chunk_tokens[c], kvs[c][0], kvs[c][1], wl.old_starts[c], wl.new_starts[c]) for c in range(len(kvs))]
+    ks, ch = wl.schedule()
+    times = {}
+    for nl in (2, 3):
+        t0 = time.perf_counter()
+        oracle.blend_prefill(m, chunks, wl.query_tokens, ks[:3], ch[:3], layers_limit=nl)
+        times[nl] = time.perf_counter() - t0
+    per_layer = max(times[3] - times[2], 1e-9)
+    total = times[3] + (L - 3) * per_layer
+    return {"value": wl.n_ctx / total, "unit": "context tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"float64 NumPy oracle, layers 0-2 of the {wl.name} blend timed ({times[3]:.1f} s; "
+                       f"one selective layer {per_layer:.2f} s), extrapolated to {L} layers "
+                       f"({total:.1f} s per request)")}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}); the blended prefill of one "
+              f"request is not sharded here, and independent requests scale by running one process per GPU.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import cbinputs
+    from cacheblend_selective_recompute_amd import api, _abi
+
+    torch.cuda.set_device(0)
+    wl = cbinputs.make_workload(args.workload, seed=args.seed, ratio=args.ratio)
+    shape = wl.shape
+    N, Q, T = wl.n_ctx, wl.n_query, wl.n_total
+    ks, ch = wl.schedule()
+    dev = "cuda"
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    weights = cbinputs.torch_device_weights(shape, args.seed, dev)
+    model = api.DeviceModel.from_tensors(shape, weights)
+    kvs = cbinputs.torch_device_chunk_kv(shape, wl.chunk_lens, args.seed, dev)
+    ints = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    if wl.paged:
+        chunks = []
+        for c, (K, V) in enumerate(kvs):
+            ln = wl.chunk_lens[c]
+            nb = (ln + 15) // 16
+            ids, n_phys = cbinputs.paged_layout(ln, 16, args.seed, key=1000 + c, spare_blocks=2)
+            Kp = torch.zeros((shape.n_layers, n_phys * 16, shape.n_kv_heads, shape.head_dim), dtype=K.dtype, device=dev)
+            Vp = torch.zeros_like(Kp)
+            rows = torch.from_numpy((np.repeat(ids.astype(np.int64), 16) * 16 + np.tile(np.arange(16), nb))[:ln]).to(dev)
+            Kp[:, rows] = K
+            Vp[:, rows] = V
+            chunks.append(api.ChunkSource(ints(wl.chunk_tokens[c]), Kp, Vp, wl.old_starts[c], wl.new_starts[c],
+                                          block_ids=ints(ids), block_size=16,
+                                          layer_stride=n_phys * 16 * shape.kv_width))
+        del kvs
+        table, n_phys = cbinputs.paged_layout(T, 16, args.seed, key=77, spare_blocks=8)
+        blended = api.PagedKV(shape, T, 16, table, n_phys)
+    else:
+        chunks = [api.ChunkSource(ints(wl.chunk_tokens[c]), kvs[c][0], kvs[c][1], wl.old_starts[c], wl.new_starts[c])
+                  for c in range(len(kvs))]
+        blended = api.PagedKV(shape, T, 16)
+    qtok = ints(wl.query_tokens)
+    logits = torch.empty(shape.vocab, device=dev)
+    hkvd = torch.empty((shape.n_layers, N), dtype=torch.int32, device=dev)
+    ws = api.Workspace(api.cb_workspace_bytes(model.cfg, N, Q, len(chunks)), dev)
+    arr = api._chunk_array(chunks)
+    hip = Hip()
+
+    def run(params):
+        api.cb_blend_prefill(model, chunks, qtok, params, blended, logits, hkvd, None, ws, _arr=arr)
+
+    plain = api.BlendParams(ks, ch)
+
+    # warmup; the last warmup step traces every launch kind for the breakdown
+    for _ in range(max(0, args.warmup - 1)):
+        run(plain)
+    cap = 4096
+    ev_all = hip.events(cap)
+    kinds_all = (ctypes.c_int32 * (cap // 2))()
+    tr_all = _abi.cb_trace(ev_all, cap, 0, (1 << len(_abi.KINDS)) - 1, kinds_all)
+    p_all = api.BlendParams(ks, ch)
+    p_all.c.trace = ctypes.pointer(tr_all)
+    run(p_all)
+    torch.cuda.synchronize()
+    sets = {l: hkvd[l, :ks[l]].cpu().numpy() for l in range(1, shape.n_layers)}
+    work = work_per_kind(shape, N, Q, ks, sets, wl.chunk_lens)
+    kind_ms = {}
+    kind_n = {}
+    for i in range(tr_all.used // 2):
+        k = _abi.KINDS[kinds_all[i]]
+        kind_ms[k] = kind_ms.get(k, 0.0) + hip.elapsed_ms(ev_all[2 * i], ev_all[2 * i + 1])
+        kind_n[k] = kind_n.get(k, 0) + 1
+    dominant = max((k for k in kind_ms if k in work), key=lambda k: kind_ms[k])
+    dom_id = _abi.KINDS.index(dominant)
+
+    # timed region: K steps; the dominant kind is bracketed by events on the library's stream
+    per_step = 2 * kind_n[dominant]
+    ev = hip.events(per_step * args.steps)
+    traces, params = [], []
+    for s in range(args.steps):
+        sub = ctypes.cast(ctypes.byref(ev, s * per_step * ctypes.sizeof(ctypes.c_void_p)),
+                          ctypes.POINTER(ctypes.c_void_p))
+        t = _abi.cb_trace(sub, per_step, 0, 1 << dom_id, None)
+        p = api.BlendParams(ks, ch)
+        p.c.trace = ctypes.pointer(t)
+        traces.append(t)
+        params.append(p)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run(params[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    dom_ms = 0.0
+    launches = 0
+    for s in range(args.steps):
+        for i in range(traces[s].used // 2):
+            dom_ms += hip.elapsed_ms(ev[s * per_step + 2 * i], ev[s * per_step + 2 * i + 1])
+            launches += 1
+    avg_launch_ms = dom_ms / max(launches, 1)
+    work_per_launch = work[dominant] / kind_n[dominant]
+    if dominant in MFMA_KINDS:
+        peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
+        achieved = work_per_launch / (avg_launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "unit": "TFLOP/s"}
+    else:
+        peak = PEAK_HBM_GBS
+        achieved = work_per_launch / (avg_launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "unit": "GB/s"}
+    roof.update({"kernel": dominant, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
+                 "traffic": None, "launches_per_step": kind_n[dominant], "avg_launch_ms": round(avg_launch_ms, 4),
+                 "work_per_launch": work_per_launch})
+
+    breakdown = {}
+    for k, ms in sorted(kind_ms.items(), key=lambda kv: -kv[1]):
+        e = {"ms": round(ms, 4), "launches": kind_n[k]}
+        if k in work and ms > 0:
+            if k in MFMA_KINDS:
+                e["tflops"] = round(work[k] / (ms * 1e-3) / 1e12, 1)
+            else:
+                e["gbs"] = round(work[k] / (ms * 1e-3) / 1e9, 1)
+        breakdown[k] = e
+
+    out = {
+        "metric": METRIC,
+        "value": round(N / (ms_per_step * 1e-3), 1),
+        "unit": "context tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic (seeded random-init weights and chunk caches drawn on the GPU)",
+        "config": {"workload": wl.name, "shape": f"{shape.n_layers}L d{shape.d_model} {shape.n_q_heads}q/"
+                                                   f"{shape.n_kv_heads}kv x{shape.head_dim} F{shape.d_ff}",
+                   "n_ctx": N, "n_query": Q, "chunks": len(chunks), "ratio": args.ratio, "k": ks[1],
+                   "paged": bool(wl.paged), "block_size": 16},
+        "roofline": roof,
+        "kernels_ms_per_step": breakdown,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -51,8 +51,18 @@ class cb_chunk(ctypes.Structure):
                 ("block_size", c_int32), ("layer_stride", c_int64)]
 
 
+class cb_trace(ctypes.Structure):
+    _fields_ = [("events", POINTER(c_void_p)), ("capacity", c_int32), ("used", c_int32),
+                ("kind_mask", c_uint32), ("kinds", POINTER(c_int32))]
+
+
 class cb_blend_params(ctypes.Structure):
-    _fields_ = [("k_per_layer", POINTER(c_int32)), ("check", POINTER(c_uint8)), ("flags", c_uint32)]
+    _fields_ = [("k_per_layer", POINTER(c_int32)), ("check", POINTER(c_uint8)), ("flags", c_uint32),
+                ("trace", POINTER(cb_trace))]
+
+
+KINDS = ["rerope", "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention", "deviation", "select",
+         "scatter", "norm", "lm_head", "other"]
 
 
 _PROTOS = {

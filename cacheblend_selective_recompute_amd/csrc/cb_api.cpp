@@ -53,6 +53,28 @@ cb_status dev_fail(hipError_t e, const char* where) {
     if (_e != hipSuccess) return dev_fail(_e, where); \
   } while (0)
 
+
+// Optional launch trace (cb_trace): events recorded around launches of the selected kinds.
+struct Tracer {
+  cb_trace* t = nullptr;
+  hipStream_t s = nullptr;
+  bool on(int kind) const {
+    return t && t->events && ((t->kind_mask >> kind) & 1u) && t->used + 2 <= t->capacity;
+  }
+};
+
+#define CB_LAUNCH(tr, kind, expr, where)                                                          \
+  do {                                                                                          \
+    const bool _on = (tr) != nullptr && (tr)->on(kind);                                         \
+    if (_on) CB_TRY(hipEventRecord(static_cast<hipEvent_t>((tr)->t->events[(tr)->t->used]), (tr)->s), "trace"); \
+    CB_TRY(expr, where);                                                                        \
+    if (_on) {                                                                                  \
+      CB_TRY(hipEventRecord(static_cast<hipEvent_t>((tr)->t->events[(tr)->t->used + 1]), (tr)->s), "trace"); \
+      if ((tr)->t->kinds) (tr)->t->kinds[(tr)->t->used / 2] = (kind);                          \
+      (tr)->t->used += 2;                                                                       \
+    }                                                                                           \
+  } while (0)
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int esize(cb_dtype dt) { return dt == CB_BF16 ? 2 : 4; }
@@ -248,14 +270,14 @@ ChunkBatch make_batch(const cb_model_cfg& c, const cb_chunk* ch, int first, int 
 }
 
 cb_status enqueue_rerope(const cb_model_cfg& c, const cb_chunk* ch, int n, const cb_paged_kv& dst, int copy_v,
-                         float2* dtab, hipStream_t s) {
+                         float2* dtab, hipStream_t s, Tracer* tr) {
   const PagedRef d = ref_of(dst);
   const int width = c.n_kv_heads * c.head_dim;
   for (int first = 0; first < n; first += kMaxChunksPerLaunch) {
     const int cnt = std::min(kMaxChunksPerLaunch, n - first);
     ChunkBatch b = make_batch(c, ch, first, cnt);
-    CB_TRY(launch_rope_delta_table(dtab, b, c.head_dim, c.rope_theta, s), "rope delta table");
-    CB_TRY(launch_rerope(c.dtype, b, d, dtab, c.n_layers, width, c.head_dim, copy_v, s), "rerope");
+    CB_LAUNCH(tr, CB_KIND_OTHER, launch_rope_delta_table(dtab, b, c.head_dim, c.rope_theta, s), "rope delta table");
+    CB_LAUNCH(tr, CB_KIND_REROPE, launch_rerope(c.dtype, b, d, dtab, c.n_layers, width, c.head_dim, copy_v, s), "rerope");
   }
   return CB_OK;
 }
@@ -277,7 +299,7 @@ struct LayerIo {
 };
 
 cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, int N, int Q, int check, int k,
-                        const LayerIo& io, const Ws& w, hipStream_t s) {
+                        const LayerIo& io, const Ws& w, hipStream_t s, Tracer* tr) {
   const cb_model_cfg& c = m.cfg;
   const cb_layer_w& lw = m.layers[l];
   const int d = c.d_model, F = c.d_ff;
@@ -288,33 +310,31 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   const int rout = k + Q;
 
   // fresh K (rotated at the rows' positions) and V for every candidate and suffix row
-  CB_TRY(launch_rmsnorm(c.dtype, io.x_in, nullptr, d, rin, d, lw.attn_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
+  CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, io.x_in, nullptr, d, rin, d, lw.attn_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
   GemmArgs g{};
   g.A = w.act; g.lda = d; g.a_rows = nullptr;
   g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * es; g.ldb = d;
   g.M = rin; g.N = 2 * kvw; g.K = d;
   g.C = w.kvf; g.ldc = 2 * kvw;
   g.rope_cols = kvw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = io.rowpos_in;
-  CB_TRY(launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "kv gemm");
+  CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "kv gemm");
 
   const int32_t* sel_slot = nullptr;
   const int32_t* sel_pos = io.cand_pos;
   int32_t* copy_out = io.pos_out;
   if (check) {
     float* dev = io.dev_slot ? io.dev_slot : w.dev;
-    CB_TRY(launch_deviation(c.dtype, w.kvf, w.kvf + kvw, 2 * kvw, io.cand_pos, nc, kv, l, kvw, dev, io.dev_by_pos, s),
-           "deviation");
-    CB_TRY(launch_select(dev, io.cand_pos, nc, k, io.pos_out, w.slot, s), "select");
+    CB_LAUNCH(tr, CB_KIND_DEVIATION, launch_deviation(c.dtype, w.kvf, w.kvf + kvw, 2 * kvw, io.cand_pos, nc, kv, l, kvw, dev, io.dev_by_pos, s), "deviation");
+    CB_LAUNCH(tr, CB_KIND_SELECT, launch_select(dev, io.cand_pos, nc, k, io.pos_out, w.slot, s), "select");
     sel_slot = w.slot;
     sel_pos = io.pos_out;
     copy_out = nullptr;
   }
   // row maps of the kept rows (+ suffix); an unchecked layer keeps every candidate
-  CB_TRY(launch_build_rows(sel_slot, sel_pos, k, nc, N, Q, w.gmap, io.rowpos_out, copy_out, io.hkvd_row, s),
-         "build rows");
+  CB_LAUNCH(tr, CB_KIND_OTHER, launch_build_rows(sel_slot, sel_pos, k, nc, N, Q, w.gmap, io.rowpos_out, copy_out, io.hkvd_row, s), "build rows");
 
   // fill: fresh K/V of the kept rows and of the suffix replace the cache
-  CB_TRY(launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, w.gmap, io.rowpos_out, rout, kv, l, kvw, s), "scatter");
+  CB_LAUNCH(tr, CB_KIND_SCATTER, launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, w.gmap, io.rowpos_out, rout, kv, l, kvw, s), "scatter");
 
   // queries of the kept rows
   g = GemmArgs{};
@@ -323,33 +343,34 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   g.M = rout; g.N = qw; g.K = d;
   g.C = w.q; g.ldc = qw;
   g.rope_cols = qw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = io.rowpos_out;
-  CB_TRY(launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
+  CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
 
   AttnArgs at{};
   at.q = w.q; at.ldq = qw; at.o = w.o; at.ldo = qw; at.rowpos = io.rowpos_out; at.R = rout;
   at.cache = kv; at.layer = l; at.n_q_heads = c.n_q_heads; at.n_kv_heads = c.n_kv_heads; at.head_dim = c.head_dim;
   at.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
-  CB_TRY(launch_attention(c.dtype, at, s), "attention");
+  CB_LAUNCH(tr, CB_KIND_ATTENTION, launch_attention(c.dtype, at, s), "attention");
 
   // O projection + residual (rows gathered from x_in), then the MLP
   g = GemmArgs{};
   g.A = w.o; g.lda = qw; g.B = lw.w_o; g.ldb = qw; g.M = rout; g.N = d; g.K = qw;
   g.C = io.x_mid; g.ldc = d; g.resid = io.x_in; g.resid_rows = w.gmap; g.ld_resid = d;
-  CB_TRY(launch_gemm(c.dtype, EPI_RESID, g, s), "o gemm");
-  CB_TRY(launch_rmsnorm(c.dtype, io.x_mid, nullptr, d, rout, d, lw.mlp_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
+  CB_LAUNCH(tr, CB_KIND_GEMM_O, launch_gemm(c.dtype, EPI_RESID, g, s), "o gemm");
+  CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, io.x_mid, nullptr, d, rout, d, lw.mlp_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
   g = GemmArgs{};
   g.A = w.act; g.lda = d; g.B = lw.w_gate_up; g.ldb = d; g.M = rout; g.N = F; g.K = d;
   g.C = w.h; g.ldc = F; g.ff = F;
-  CB_TRY(launch_gemm(c.dtype, EPI_SWIGLU, g, s), "gate/up gemm");
+  CB_LAUNCH(tr, CB_KIND_GEMM_GATE_UP, launch_gemm(c.dtype, EPI_SWIGLU, g, s), "gate/up gemm");
   g = GemmArgs{};
   g.A = w.h; g.lda = F; g.B = lw.w_down; g.ldb = F; g.M = rout; g.N = d; g.K = F;
   g.C = io.x_out; g.ldc = d; g.resid = io.x_mid; g.resid_rows = nullptr; g.ld_resid = d;
-  CB_TRY(launch_gemm(c.dtype, EPI_RESID, g, s), "down gemm");
+  CB_LAUNCH(tr, CB_KIND_GEMM_DOWN, launch_gemm(c.dtype, EPI_RESID, g, s), "down gemm");
   return CB_OK;
 }
 
 // Layer 0 over every row: context K/V stay the re-RoPE'd cache, suffix K/V are computed.
-cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, float* x, const Ws& w, hipStream_t s) {
+cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, float* x, const Ws& w, hipStream_t s,
+                         Tracer* tr) {
   const cb_model_cfg& c = m.cfg;
   const cb_layer_w& lw = m.layers[0];
   const int d = c.d_model, F = c.d_ff;
@@ -357,35 +378,35 @@ cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, fl
   const int kvw = c.n_kv_heads * c.head_dim;
   const int es = esize(c.dtype);
   const int T = N + Q;
-  CB_TRY(launch_rmsnorm(c.dtype, x, nullptr, d, T, d, lw.attn_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
+  CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, x, nullptr, d, T, d, lw.attn_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
   GemmArgs g{};
   g.A = w.act; g.lda = d; g.B = lw.w_qkv; g.ldb = d; g.M = T; g.N = qw; g.K = d;
   g.C = w.q; g.ldc = qw; g.rope_cols = qw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = w.rowpos0;
-  CB_TRY(launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
+  CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
   g = GemmArgs{};
   g.A = static_cast<const char*>(w.act) + (int64_t)N * d * es; g.lda = d;
   g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * es; g.ldb = d;
   g.M = Q; g.N = 2 * kvw; g.K = d; g.C = w.kvf; g.ldc = 2 * kvw;
   g.rope_cols = kvw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = w.rowpos0 + N;
-  CB_TRY(launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "suffix kv gemm");
-  CB_TRY(launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, nullptr, w.rowpos0 + N, Q, kv, 0, kvw, s), "suffix scatter");
+  CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "suffix kv gemm");
+  CB_LAUNCH(tr, CB_KIND_SCATTER, launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, nullptr, w.rowpos0 + N, Q, kv, 0, kvw, s), "suffix scatter");
   AttnArgs at{};
   at.q = w.q; at.ldq = qw; at.o = w.o; at.ldo = qw; at.rowpos = w.rowpos0; at.R = T;
   at.cache = kv; at.layer = 0; at.n_q_heads = c.n_q_heads; at.n_kv_heads = c.n_kv_heads; at.head_dim = c.head_dim;
   at.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
-  CB_TRY(launch_attention(c.dtype, at, s), "attention");
+  CB_LAUNCH(tr, CB_KIND_ATTENTION, launch_attention(c.dtype, at, s), "attention");
   g = GemmArgs{};
   g.A = w.o; g.lda = qw; g.B = lw.w_o; g.ldb = qw; g.M = T; g.N = d; g.K = qw;
   g.C = x; g.ldc = d; g.resid = x; g.ld_resid = d;
-  CB_TRY(launch_gemm(c.dtype, EPI_RESID, g, s), "o gemm");
-  CB_TRY(launch_rmsnorm(c.dtype, x, nullptr, d, T, d, lw.mlp_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
+  CB_LAUNCH(tr, CB_KIND_GEMM_O, launch_gemm(c.dtype, EPI_RESID, g, s), "o gemm");
+  CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, x, nullptr, d, T, d, lw.mlp_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
   g = GemmArgs{};
   g.A = w.act; g.lda = d; g.B = lw.w_gate_up; g.ldb = d; g.M = T; g.N = F; g.K = d; g.C = w.h; g.ldc = F; g.ff = F;
-  CB_TRY(launch_gemm(c.dtype, EPI_SWIGLU, g, s), "gate/up gemm");
+  CB_LAUNCH(tr, CB_KIND_GEMM_GATE_UP, launch_gemm(c.dtype, EPI_SWIGLU, g, s), "gate/up gemm");
   g = GemmArgs{};
   g.A = w.h; g.lda = F; g.B = lw.w_down; g.ldb = F; g.M = T; g.N = d; g.K = F;
   g.C = x; g.ldc = d; g.resid = x; g.ld_resid = d;
-  CB_TRY(launch_gemm(c.dtype, EPI_RESID, g, s), "down gemm");
+  CB_LAUNCH(tr, CB_KIND_GEMM_DOWN, launch_gemm(c.dtype, EPI_RESID, g, s), "down gemm");
   return CB_OK;
 }
 
@@ -432,7 +453,7 @@ cb_status cb_rerope_k(const cb_model_cfg* cfg, const cb_chunk* chunks, int32_t n
   Ws w;
   carve(*cfg, 0, 0, n_chunks, ws, &w);
   st = enqueue_rerope(*cfg, chunks, n_chunks, *dst, (flags & CB_COPY_V) ? 1 : 0, w.dtab,
-                      reinterpret_cast<hipStream_t>(stream));
+                      reinterpret_cast<hipStream_t>(stream), nullptr);
   return st == CB_OK ? ok() : st;
 }
 
@@ -500,7 +521,7 @@ cb_status cb_blend_layer(const cb_model* model, int32_t layer, const cb_paged_kv
   io.rowpos_out = w.rowpos1;
   io.pos_out = pos_out;
   io.dev_slot = dev_out;
-  st = enqueue_layer(*model, layer, r, n_cand, n_ctx, n_query, check_flag ? 1 : 0, k_keep, io, w, s);
+  st = enqueue_layer(*model, layer, r, n_cand, n_ctx, n_query, check_flag ? 1 : 0, k_keep, io, w, s, nullptr);
   return st == CB_OK ? ok() : st;
 }
 
@@ -541,10 +562,15 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
   Ws w;
   carve(c, N, Q, n_chunks, ws, &w);
   const PagedRef kv = ref_of(*blended);
+  Tracer tracer;
+  tracer.t = params->trace;
+  tracer.s = s;
+  if (tracer.t) tracer.t->used = 0;
+  Tracer* tr = &tracer;
 
   // a1: assemble + re-RoPE every layer of every chunk
-  if ((st = enqueue_rerope(c, chunks, n_chunks, *blended, 1, w.dtab, s)) != CB_OK) return st;
-  CB_TRY(launch_rope_pos_table(w.pos_tab, T, c.head_dim, c.rope_theta, s), "rope table");
+  if ((st = enqueue_rerope(c, chunks, n_chunks, *blended, 1, w.dtab, s, tr)) != CB_OK) return st;
+  CB_LAUNCH(tr, CB_KIND_OTHER, launch_rope_pos_table(w.pos_tab, T, c.head_dim, c.rope_theta, s), "rope table");
   // a2: tokens in new-position order, then embeddings
   {
     std::vector<cb_chunk> all(chunks, chunks + n_chunks);
@@ -556,16 +582,16 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
     for (size_t first = 0; first < all.size(); first += kMaxChunksPerLaunch) {
       const int cnt = std::min<int>(kMaxChunksPerLaunch, static_cast<int>(all.size() - first));
       ChunkBatch b = make_batch(c, all.data(), static_cast<int>(first), cnt);
-      CB_TRY(launch_gather_tokens(b, w.tokens, s), "gather tokens");
+      CB_LAUNCH(tr, CB_KIND_OTHER, launch_gather_tokens(b, w.tokens, s), "gather tokens");
     }
   }
-  CB_TRY(launch_embed(c.dtype, w.tokens, T, model->embed, c.d_model, w.x0, s), "embed");
-  CB_TRY(launch_iota(w.rowpos0, T, 0, s), "iota");
-  CB_TRY(launch_iota(w.posA, N, 0, s), "iota");
-  if (hkvd_out) CB_TRY(launch_iota(hkvd_out, N, 0, s), "iota");
+  CB_LAUNCH(tr, CB_KIND_OTHER, launch_embed(c.dtype, w.tokens, T, model->embed, c.d_model, w.x0, s), "embed");
+  CB_LAUNCH(tr, CB_KIND_OTHER, launch_iota(w.rowpos0, T, 0, s), "iota");
+  CB_LAUNCH(tr, CB_KIND_OTHER, launch_iota(w.posA, N, 0, s), "iota");
+  if (hkvd_out) CB_LAUNCH(tr, CB_KIND_OTHER, launch_iota(hkvd_out, N, 0, s), "iota");
 
   // a3: layer 0 in full
-  if ((st = enqueue_layer0(*model, kv, N, Q, w.x0, w, s)) != CB_OK) return st;
+  if ((st = enqueue_layer0(*model, kv, N, Q, w.x0, w, s, tr)) != CB_OK) return st;
 
   // layers 1 .. L-1
   float* xcur = w.x0;
@@ -589,7 +615,7 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
     io.dev_slot = nullptr;
     io.dev_by_pos = (chk && dev_out) ? dev_out + (int64_t)l * N : nullptr;
     io.hkvd_row = hkvd_out ? hkvd_out + (int64_t)l * N : nullptr;
-    if ((st = enqueue_layer(*model, l, kv, nc, N, Q, chk, k, io, w, s)) != CB_OK) return st;
+    if ((st = enqueue_layer(*model, l, kv, nc, N, Q, chk, k, io, w, s, tr)) != CB_OK) return st;
     std::swap(xcur, xoth);
     std::swap(cand, nxt);
     std::swap(rp_in, rp_out);
@@ -598,10 +624,9 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
 
   // a12: final norm of the last position, LM head
   const int R = nc + Q;
-  CB_TRY(launch_rmsnorm(c.dtype, xcur + (int64_t)(R - 1) * c.d_model, nullptr, c.d_model, 1, c.d_model,
-                        model->final_norm, c.rms_eps, w.a_last, c.d_model, 1, s),
-         "final norm");
-  CB_TRY(launch_lmhead(c.dtype, w.a_last, model->lm_head, c.vocab, c.d_model, logits, s), "lm head");
+  CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, xcur + (int64_t)(R - 1) * c.d_model, nullptr, c.d_model, 1, c.d_model,
+                        model->final_norm, c.rms_eps, w.a_last, c.d_model, 1, s), "final norm");
+  CB_LAUNCH(tr, CB_KIND_LM_HEAD, launch_lmhead(c.dtype, w.a_last, model->lm_head, c.vocab, c.d_model, logits, s), "lm head");
   return ok();
 }
 

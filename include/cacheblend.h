@@ -130,6 +130,34 @@ typedef struct {
   int64_t layer_stride;     /* elements; 0 = contiguous default */
 } cb_chunk;
 
+/* Launch kinds, for cb_trace. */
+typedef enum {
+  CB_KIND_REROPE = 0,     /* re-RoPE + assembly of the chunk caches            */
+  CB_KIND_GEMM_QKV = 1,   /* Q and K/V projections (RoPE fused)                 */
+  CB_KIND_GEMM_O = 2,     /* output projection + residual                      */
+  CB_KIND_GEMM_GATE_UP = 3, /* gate/up projection + SiLU-gated product           */
+  CB_KIND_GEMM_DOWN = 4,  /* down projection + residual                        */
+  CB_KIND_ATTENTION = 5,  /* causal attention of the recomputed rows           */
+  CB_KIND_DEVIATION = 6,  /* per-token KV deviation                            */
+  CB_KIND_SELECT = 7,     /* top-k of the deviations                           */
+  CB_KIND_SCATTER = 8,    /* fresh K/V rows into the paged cache               */
+  CB_KIND_NORM = 9,       /* RMSNorm                                           */
+  CB_KIND_LM_HEAD = 10,   /* final-position logits                             */
+  CB_KIND_OTHER = 11      /* tables, embeddings, row maps                      */
+} cb_kind;
+
+/* Optional launch trace: the library records events[2i] / events[2i+1] on the
+ * stream right before / after the i-th launch whose kind bit is set in
+ * kind_mask, and stores that kind in kinds[i].  Events are hipEvent_t handles
+ * the caller created; recording stops when the capacity is reached. */
+typedef struct {
+  void** events;      /* HOST [capacity] */
+  int32_t capacity;
+  int32_t used;       /* out: events recorded (an even number) */
+  uint32_t kind_mask; /* bit k traces kind k */
+  int32_t* kinds;     /* HOST [capacity / 2] or NULL */
+} cb_trace;
+
 /* Recompute schedule.  k_per_layer[0] must equal N (layer 0 runs in full);
  * for l >= 1, k_per_layer[l] <= k_per_layer[l-1] (sets only shrink) and
  * check[l] = 0 requires k_per_layer[l] == k_per_layer[l-1]. */
@@ -137,6 +165,7 @@ typedef struct {
   const int32_t* k_per_layer; /* HOST [n_layers] */
   const uint8_t* check;       /* HOST [n_layers]; check[0] ignored */
   uint32_t flags;             /* reserved, 0 */
+  cb_trace* trace;            /* HOST, nullable: launch trace (see cb_trace) */
 } cb_blend_params;
 
 /* ---------------------------------------------------------------------------

@@ -267,7 +267,7 @@ def full_prefill(m: OracleModel, tokens: np.ndarray, start: int = 0) -> Dict[str
     tokens = np.asarray(tokens)
     n = len(tokens)
     pos = np.arange(start, start + n)
-    x = np.asarray(m.glob["embed"], dtype=F64)[tokens]
+    x = np.asarray(m.glob["embed"][np.asarray(tokens)], dtype=F64)
     K = np.zeros((m.n_layers, n, m.n_kv_heads, m.head_dim), dtype=F64)
     V = np.zeros_like(K)
     for l in range(m.n_layers):
@@ -394,7 +394,7 @@ def blend_prefill(m: OracleModel, chunks: Sequence[Tuple], query_tokens: np.ndar
     suffix = np.arange(N, T)
     # layer 0: every row; context K/V are the re-RoPE'd cache
     w = m.layer(0)
-    x = np.asarray(m.glob["embed"], dtype=F64)[tokens]
+    x = np.asarray(m.glob["embed"][np.asarray(tokens)], dtype=F64)
     a = rms_norm(x, w["attn_norm"], m.rms_eps)
     Kb[0, suffix] = store_round(rope(m.heads(_proj(a[N:], w["wk"]), m.n_kv_heads), suffix, m.rope_theta), m.storage)
     Vb[0, suffix] = store_round(m.heads(_proj(a[N:], w["wv"]), m.n_kv_heads), m.storage)
@@ -429,7 +429,7 @@ def blend_prefill_masked(m: OracleModel, chunks: Sequence[Tuple], query_tokens: 
     Kb, Vb = assemble_blended(m, chunks, Q)
     tokens = np.concatenate([_context_tokens(chunks), np.asarray(query_tokens)])
     pos = np.arange(T)
-    x = np.asarray(m.glob["embed"], dtype=F64)[tokens]
+    x = np.asarray(m.glob["embed"][np.asarray(tokens)], dtype=F64)
     cand = np.ones(T, dtype=bool)
     cand[N:] = False
     is_suffix = ~cand.copy()
@@ -475,7 +475,7 @@ def full_reuse_prefill(m: OracleModel, Kb: np.ndarray, Vb: np.ndarray, query_tok
     Q = len(query_tokens)
     N = T - Q
     suffix = np.arange(N, T)
-    x = np.asarray(m.glob["embed"], dtype=F64)[np.asarray(query_tokens)]
+    x = np.asarray(m.glob["embed"][np.asarray(query_tokens)], dtype=F64)
     for l in range(L):
         w = m.layer(l)
         a = rms_norm(x, w["attn_norm"], m.rms_eps)

@@ -53,7 +53,8 @@ int main(void) {
   P(cb_model) O(cb_model, embed) O(cb_model, layers)
   P(cb_paged_kv) O(cb_paged_kv, block_size) O(cb_paged_kv, layer_stride)
   P(cb_chunk) O(cb_chunk, len) O(cb_chunk, new_start) O(cb_chunk, layer_stride)
-  P(cb_blend_params) O(cb_blend_params, flags)
+  P(cb_blend_params) O(cb_blend_params, flags) O(cb_blend_params, trace)
+  P(cb_trace) O(cb_trace, used) O(cb_trace, kinds)
   return 0;
 }
 '''
@@ -64,7 +65,7 @@ int main(void) {
         subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
         lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
     got = dict(l.split() for l in lines if l.strip())
-    for name in ("cb_model_cfg", "cb_layer_w", "cb_model", "cb_paged_kv", "cb_chunk", "cb_blend_params"):
+    for name in ("cb_model_cfg", "cb_layer_w", "cb_model", "cb_paged_kv", "cb_chunk", "cb_blend_params", "cb_trace"):
         cls = getattr(_abi, name)
         assert ctypes.sizeof(cls) == int(got[name]), name
     for key, v in got.items():

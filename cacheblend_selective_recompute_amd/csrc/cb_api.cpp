@@ -203,6 +203,9 @@ struct Ws {
   int32_t* rowpos0;
   int32_t* rowpos1;
   float* a_last;
+  float* attn_o;
+  float2* attn_ml;
+  float* gemm_part;
 };
 
 size_t carve(const cb_model_cfg& c, int64_t N, int64_t Q, int64_t C, void* base, Ws* w) {
@@ -237,6 +240,9 @@ size_t carve(const cb_model_cfg& c, int64_t N, int64_t Q, int64_t C, void* base,
   t.rowpos0 = static_cast<int32_t*>(take(T * 4));
   t.rowpos1 = static_cast<int32_t*>(take(T * 4));
   t.a_last = static_cast<float*>(take(c.d_model * 4));
+  t.attn_o = static_cast<float*>(take(T > 0 ? attn_partial_floats(c.head_dim) * 4 : 0));
+  t.attn_ml = static_cast<float2*>(take(T > 0 ? kAttnPartialRows * 8 : 0));
+  t.gemm_part = static_cast<float*>(take(T > 0 ? kGemmPartFloats * 4 : 0));
   if (w) *w = t;
   return (off + 255) & ~size_t(255);
 }
@@ -317,6 +323,8 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   g.M = rin; g.N = 2 * kvw; g.K = d;
   g.C = w.kvf; g.ldc = 2 * kvw;
   g.rope_cols = kvw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = io.rowpos_in;
+  g.part = w.gemm_part;
+  g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "kv gemm");
 
   const int32_t* sel_slot = nullptr;
@@ -343,27 +351,38 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   g.M = rout; g.N = qw; g.K = d;
   g.C = w.q; g.ldc = qw;
   g.rope_cols = qw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = io.rowpos_out;
+  g.part = w.gemm_part;
+  g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
 
   AttnArgs at{};
   at.q = w.q; at.ldq = qw; at.o = w.o; at.ldo = qw; at.rowpos = io.rowpos_out; at.R = rout;
   at.cache = kv; at.layer = l; at.n_q_heads = c.n_q_heads; at.n_kv_heads = c.n_kv_heads; at.head_dim = c.head_dim;
   at.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
+  at.kv_bound = N + Q;
+  at.part_o = w.attn_o;
+  at.part_ml = w.attn_ml;
   CB_LAUNCH(tr, CB_KIND_ATTENTION, launch_attention(c.dtype, at, s), "attention");
 
   // O projection + residual (rows gathered from x_in), then the MLP
   g = GemmArgs{};
   g.A = w.o; g.lda = qw; g.B = lw.w_o; g.ldb = qw; g.M = rout; g.N = d; g.K = qw;
   g.C = io.x_mid; g.ldc = d; g.resid = io.x_in; g.resid_rows = w.gmap; g.ld_resid = d;
+  g.part = w.gemm_part;
+  g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_O, launch_gemm(c.dtype, EPI_RESID, g, s), "o gemm");
   CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, io.x_mid, nullptr, d, rout, d, lw.mlp_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
   g = GemmArgs{};
   g.A = w.act; g.lda = d; g.B = lw.w_gate_up; g.ldb = d; g.M = rout; g.N = F; g.K = d;
   g.C = w.h; g.ldc = F; g.ff = F;
+  g.part = w.gemm_part;
+  g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_GATE_UP, launch_gemm(c.dtype, EPI_SWIGLU, g, s), "gate/up gemm");
   g = GemmArgs{};
   g.A = w.h; g.lda = F; g.B = lw.w_down; g.ldb = F; g.M = rout; g.N = d; g.K = F;
   g.C = io.x_out; g.ldc = d; g.resid = io.x_mid; g.resid_rows = nullptr; g.ld_resid = d;
+  g.part = w.gemm_part;
+  g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_DOWN, launch_gemm(c.dtype, EPI_RESID, g, s), "down gemm");
   return CB_OK;
 }
@@ -382,30 +401,43 @@ cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, fl
   GemmArgs g{};
   g.A = w.act; g.lda = d; g.B = lw.w_qkv; g.ldb = d; g.M = T; g.N = qw; g.K = d;
   g.C = w.q; g.ldc = qw; g.rope_cols = qw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = w.rowpos0;
+  g.part = w.gemm_part;
+  g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
   g = GemmArgs{};
   g.A = static_cast<const char*>(w.act) + (int64_t)N * d * es; g.lda = d;
   g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * es; g.ldb = d;
   g.M = Q; g.N = 2 * kvw; g.K = d; g.C = w.kvf; g.ldc = 2 * kvw;
   g.rope_cols = kvw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = w.rowpos0 + N;
+  g.part = w.gemm_part;
+  g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "suffix kv gemm");
   CB_LAUNCH(tr, CB_KIND_SCATTER, launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, nullptr, w.rowpos0 + N, Q, kv, 0, kvw, s), "suffix scatter");
   AttnArgs at{};
   at.q = w.q; at.ldq = qw; at.o = w.o; at.ldo = qw; at.rowpos = w.rowpos0; at.R = T;
   at.cache = kv; at.layer = 0; at.n_q_heads = c.n_q_heads; at.n_kv_heads = c.n_kv_heads; at.head_dim = c.head_dim;
   at.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
+  at.kv_bound = N + Q;
+  at.part_o = w.attn_o;
+  at.part_ml = w.attn_ml;
   CB_LAUNCH(tr, CB_KIND_ATTENTION, launch_attention(c.dtype, at, s), "attention");
   g = GemmArgs{};
   g.A = w.o; g.lda = qw; g.B = lw.w_o; g.ldb = qw; g.M = T; g.N = d; g.K = qw;
   g.C = x; g.ldc = d; g.resid = x; g.ld_resid = d;
+  g.part = w.gemm_part;
+  g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_O, launch_gemm(c.dtype, EPI_RESID, g, s), "o gemm");
   CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, x, nullptr, d, T, d, lw.mlp_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
   g = GemmArgs{};
   g.A = w.act; g.lda = d; g.B = lw.w_gate_up; g.ldb = d; g.M = T; g.N = F; g.K = d; g.C = w.h; g.ldc = F; g.ff = F;
+  g.part = w.gemm_part;
+  g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_GATE_UP, launch_gemm(c.dtype, EPI_SWIGLU, g, s), "gate/up gemm");
   g = GemmArgs{};
   g.A = w.h; g.lda = F; g.B = lw.w_down; g.ldb = F; g.M = T; g.N = d; g.K = F;
   g.C = x; g.ldc = d; g.resid = x; g.ld_resid = d;
+  g.part = w.gemm_part;
+  g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_DOWN, launch_gemm(c.dtype, EPI_RESID, g, s), "down gemm");
   return CB_OK;
 }

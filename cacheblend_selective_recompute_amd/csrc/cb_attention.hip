@@ -14,6 +14,8 @@
 // probabilities feed the P.V product (O^T = V^T P^T) straight from registers.
 // K blocks are staged row-major in LDS, V blocks transposed.  Query tiles run
 // longest-first (their rows are sorted by position).
+#include <algorithm>
+
 #include "cb_internal.h"
 
 namespace cb {
@@ -28,10 +30,15 @@ constexpr int QROWS = 64;          // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int DH, int G>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits, int ksplit) {
   constexpr int QT = QROWS / G;          // query tokens per tile
-  constexpr int KP = DH + 8;             // K row pitch (bf16)
-  constexpr int VP = KVB + 8;            // V^T row pitch (bf16)
+  constexpr int KP = DH + 8;             // K row pitch (bf16): 16 rows of a fragment read hit distinct banks
+  constexpr int VP = KVB + 4;            // V^T row pitch (bf16)
+  constexpr int CPR = DH / 8;            // 16-byte chunks per key row
+  constexpr int KCH = KVB * CPR / 256;   // K chunks per thread per block
+  static_assert(KVB * CPR == 256 * KCH, "K staging");
+  static_assert((KVB / 4) * CPR == 256 || (KVB / 4) * CPR == 128, "V staging");
+  constexpr int VTHREADS = (KVB / 4) * CPR;    // threads that stage V (4 keys x 8 dims each)
   __shared__ __attribute__((aligned(16))) bf16_t Ks[KVB * KP];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[DH * VP];
 
@@ -39,11 +46,15 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int n_tiles = (a.R + QT - 1) / QT;
-  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x);   // longest first
+  const int split = blockIdx.x % n_splits;
+  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x / n_splits);   // longest first
   const int kvh = blockIdx.y;
   const int t0 = tile * QT;
   const int t_last = min(t0 + QT, a.R) - 1;
-  const int kv_end = a.rowpos[t_last] + 1;                        // keys [0, kv_end)
+  const int kv_end = a.rowpos[t_last] + 1;                                   // keys [0, kv_end)
+  const int j_begin = split * ksplit;
+  const int j_end = min(kv_end, j_begin + ksplit);
+  if (j_begin >= j_end) return;                                              // uniform per workgroup
 
   // this lane's query row: wave w owns tile rows 16w..16w+15; row r -> token r % QT, head r / QT
   const int qr = wid * 16 + (lane & 15);
@@ -73,27 +84,62 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const bf16_t* vbase = static_cast<const bf16_t*>(a.cache.v) + static_cast<int64_t>(a.layer) * a.cache.layer_stride;
   const int width = a.n_kv_heads * DH;
 
-  for (int j0 = 0; j0 < kv_end; j0 += KVB) {
-    // ---- stage K (row-major) and V (transposed) for keys j0 .. j0+63 ----
-    constexpr int CPR = DH / 8;              // 16-byte chunks per key row
-    for (int c = tid; c < KVB * CPR; c += 256) {
-      const int r = c / CPR, e = (c % CPR) * 8;
-      const int p = j0 + r;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (p < kv_end) {
-        const int64_t off = paged_row(a.cache.bt, a.cache.bs, p) * width + kvh * DH + e;
-        kv = *reinterpret_cast<const uint4*>(kbase + off);
-        vv = *reinterpret_cast<const uint4*>(vbase + off);
-      }
-      *reinterpret_cast<uint4*>(&Ks[r * KP + e]) = kv;
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+  // staging roles: K chunk c = tid + 256*u -> key c / CPR, dims (c % CPR)*8;
+  // V: thread tid < VTHREADS takes keys 4*(tid / CPR) .. +3, dims (tid % CPR)*8 .. +7
+  const int vkey = 4 * (tid / CPR);
+  const int vdim = (tid % CPR) * 8;
+  uint4 kreg[KCH], vreg[4];
+  auto gload = [&](int j0) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        Vt[(e + 2 * h) * VP + r] = static_cast<bf16_t>(w[h] & 0xFFFFu);
-        Vt[(e + 2 * h + 1) * VP + r] = static_cast<bf16_t>(w[h] >> 16);
+    for (int u = 0; u < KCH; ++u) {
+      const int c = tid + 256 * u;
+      const int p = j0 + c / CPR;
+      kreg[u] = make_uint4(0, 0, 0, 0);
+      if (p < j_end)
+        kreg[u] = *reinterpret_cast<const uint4*>(kbase + paged_row(a.cache.bt, a.cache.bs, p) * width + kvh * DH +
+                                                  (c % CPR) * 8);
+    }
+    if (tid < VTHREADS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = j0 + vkey + i;
+        vreg[i] = make_uint4(0, 0, 0, 0);
+        if (p < j_end)
+          vreg[i] = *reinterpret_cast<const uint4*>(vbase + paged_row(a.cache.bt, a.cache.bs, p) * width + kvh * DH +
+                                                    vdim);
       }
     }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int c = tid + 256 * u;
+      *reinterpret_cast<uint4*>(&Ks[(c / CPR) * KP + (c % CPR) * 8]) = kreg[u];
+    }
+    if (tid < VTHREADS) {
+      // V^T[vdim + e][vkey .. vkey+3] as one 8-byte word per dim
+      const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
+      const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+      const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
+      const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        uint2 lo, hi;
+        lo.x = (w0[h] & 0xFFFFu) | (w1[h] << 16);
+        lo.y = (w2[h] & 0xFFFFu) | (w3[h] << 16);
+        hi.x = (w0[h] >> 16) | (w1[h] & 0xFFFF0000u);
+        hi.y = (w2[h] >> 16) | (w3[h] & 0xFFFF0000u);
+        *reinterpret_cast<uint2*>(&Vt[(vdim + 2 * h) * VP + vkey]) = lo;
+        *reinterpret_cast<uint2*>(&Vt[(vdim + 2 * h + 1) * VP + vkey]) = hi;
+      }
+    }
+  };
+
+  gload(j_begin);
+  for (int j0 = j_begin; j0 < j_end; j0 += KVB) {
+    lstore();
     __syncthreads();
+    if (j0 + KVB < j_end) gload(j0 + KVB);     // next block in flight during the math
 
     // ---- S^T tiles: 4 x (16 keys x 16 queries) ----
     f32x4_t s[4];
@@ -113,14 +159,16 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = j0 + 16 * t + 4 * kgrp + i;
-        const float v = (key <= qpos) ? s[t][i] * sc : -INFINITY;
+        const float v = (key <= qpos && key < j_end) ? s[t][i] * sc : -INFINITY;
         s[t][i] = v;
         mblk = fmaxf(mblk, v);
       }
     mblk = fmaxf(mblk, __shfl_xor(mblk, 16, 64));
     mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64));
-    const float m_new = fmaxf(m_run, mblk);          // finite: key 0 <= qpos always
-    const float alpha = exp2f(m_run - m_new);
+    const float m_new = fmaxf(m_run, mblk);
+    // a row with no visible key yet keeps m = -inf; guard the exponent base
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
     m_run = m_new;
     float psum = 0.f;
     bf16x8_t pf[2];
@@ -128,7 +176,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s[t][i] - m_new);
+        const float p = exp2f(s[t][i] - m_use);
         psum += p;
         pf[t >> 1][(t & 1) * 4 + i] = static_cast<__bf16>(p);
       }
@@ -155,8 +203,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   float l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
-  const float inv = 1.0f / l_tot;
-  if (qvalid) {
+  if (!qvalid) return;
+  if (n_splits == 1) {
+    const float inv = 1.0f / l_tot;
     bf16_t* op = static_cast<bf16_t*>(a.o) + static_cast<int64_t>(qtok) * a.ldo + qhead * DH;
     // o[dt][i] = O[q][16*dt + 4*kgrp + i]
 #pragma unroll
@@ -166,7 +215,45 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       w.y = static_cast<uint32_t>(f2bf(o[dt][2] * inv)) | (static_cast<uint32_t>(f2bf(o[dt][3] * inv)) << 16);
       *reinterpret_cast<uint2*>(op + 16 * dt + 4 * kgrp) = w;
     }
+  } else {
+    // unnormalised partial for (split, row, head); m in log2 units
+    const int64_t pr = (static_cast<int64_t>(split) * a.R + qtok) * a.n_q_heads + qhead;
+    float* op = a.part_o + pr * DH;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt)
+      *reinterpret_cast<float4*>(op + 16 * dt + 4 * kgrp) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+    if (kgrp == 0) a.part_ml[pr] = make_float2(m_run, l_tot);
   }
+}
+
+// Merge the split-KV partials of one (row, q head) per wave, in split order.
+template <int DH>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_splits, int ksplit, int QT) {
+  const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);   // row * Hq + head
+  const int lane = threadIdx.x & 63;
+  if (idx >= a.R * a.n_q_heads) return;
+  const int row = idx / a.n_q_heads;
+  const int head = idx % a.n_q_heads;
+  const int t_last = min((row / QT + 1) * QT, a.R) - 1;
+  const int kv_end = a.rowpos[t_last] + 1;
+  const int ns = min(n_splits, (kv_end + ksplit - 1) / ksplit);
+  float M = -INFINITY;
+  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, a.part_ml[(static_cast<int64_t>(sp) * a.R + row) * a.n_q_heads + head].x);
+  constexpr int PER = DH / 64;
+  float acc[PER] = {};
+  float lsum = 0.f;
+  for (int sp = 0; sp < ns; ++sp) {
+    const int64_t pr = (static_cast<int64_t>(sp) * a.R + row) * a.n_q_heads + head;
+    const float2 ml = a.part_ml[pr];
+    const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+    lsum += w * ml.y;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] += w * a.part_o[pr * DH + lane * PER + e];
+  }
+  const float inv = 1.0f / lsum;
+  bf16_t* op = static_cast<bf16_t*>(a.o) + static_cast<int64_t>(row) * a.ldo + head * DH + lane * PER;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) op[e] = f2bf(acc[e] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -235,7 +322,21 @@ template <int DH, int G>
 hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   constexpr int QT = QROWS / G;
   const int n_tiles = (a.R + QT - 1) / QT;
-  attn_bf16_kernel<DH, G><<<dim3(n_tiles, a.n_kv_heads), 256, 0, s>>>(a);
+  const int base = n_tiles * a.n_kv_heads;
+  const int kv_blocks = (a.kv_bound + KVB - 1) / KVB;
+  // split the keys only when the (tile, head) grid cannot fill the chip
+  int n_splits = 1;
+  if (base < 512 && a.part_o != nullptr) {
+    n_splits = std::min(kAttnMaxSplits, std::max(1, (768 + base - 1) / base));
+    n_splits = std::min(n_splits, kv_blocks);
+    if (static_cast<int64_t>(n_splits) * a.R * a.n_q_heads > kAttnPartialRows) n_splits = 1;
+  }
+  const int ksplit = ((kv_blocks + n_splits - 1) / n_splits) * KVB;
+  attn_bf16_kernel<DH, G><<<dim3(n_tiles * n_splits, a.n_kv_heads), 256, 0, s>>>(a, n_splits, ksplit);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_splits == 1) return e;
+  const int pairs = a.R * a.n_q_heads;
+  attn_combine_kernel<DH><<<(pairs + 3) / 4, 256, 0, s>>>(a, n_splits, ksplit, QT);
   return hipGetLastError();
 }
 

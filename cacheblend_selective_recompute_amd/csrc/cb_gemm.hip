@@ -6,14 +6,19 @@
 // selected tokens go through the projections; the recompute cost is
 // proportional to the selected share (section "选 token").
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, 128x128x64 block tile, 4 waves in a
-// 2x2 grid of 64x64 wave tiles, A and B tiles staged through LDS (row pitch
-// padded by 16 B so the 32 rows a fragment read touches fall in distinct
-// banks), two LDS buffers so the next global tile is in flight while the
-// current one is multiplied.  Tiles are ordered M-fastest and mapped so that
-// consecutive tiles land on the same XCD: the M tiles that share one weight
-// tile then share that XCD's L2.
+// bf16 path: v_mfma_f32_32x32x16_bf16, 4 waves in a 2x2 grid, block tile
+// (2 WTM) x (2 WTN) x 64.  Weight tiles are staged through LDS (row pitch padded
+// by 16 B so the 32 rows one fragment read touches fall in distinct banks; two
+// buffers so the next tile is in flight while the current one is multiplied);
+// activation rows are gathered straight into MFMA fragments.  The tile shape is
+// chosen per call (256x256, 128x256 or 128x128) so the grid fills the 256 CUs;
+// small-N projections split K and reduce the fp32 partials in a fixed order
+// in a second kernel that also applies the epilogue.  Tiles are ordered
+// M-fastest and mapped so consecutive tiles land on the same XCD, so the M
+// tiles that share one weight tile share that XCD's L2.
 // fp32 path: a plain LDS-tiled FMA kernel (fp32 models are small).
+#include <algorithm>
+
 #include "cb_internal.h"
 
 namespace cb {
@@ -23,7 +28,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BK = 64;
 constexpr int LDSP = BK + 8;   // LDS row pitch in bf16 elements (144 B)
 constexpr int kThreads = 256;
 constexpr int kXcd = 8;
@@ -38,9 +43,16 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDSP];
+// Weights (B) are staged through LDS; the gathered activation rows (A) go
+// straight from global memory into MFMA A-fragments: every wave owns WTM rows
+// and WTN columns, waves sharing a row range read the same A lines (L1/L2 hits).
+// WTM x WTN = 128 x 128 keeps 256 fp32 accumulators per lane (AGPRs) and needs
+// 3/8 of the LDS bandwidth of the matrix cores per k step.
+template <int EPI, int WTM, int WTN, bool SPLIT>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g, int splits, int kps) {
+  constexpr int BM = 2 * WTM, BN = 2 * WTN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int NB = BN * (BK / 8) / kThreads;      // 16-byte B chunks per thread per k block
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDSP];
 
   const int tid = threadIdx.x;
@@ -49,120 +61,152 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g) {
   const int wm = wid >> 1, wn = wid & 1;
 
   const int m_tiles = (g.M + BM - 1) / BM;
-  const int nb = gridDim.x;
-  const int t = xcd_remap(blockIdx.x, nb);
-  const int mt = t % m_tiles, nt = t / m_tiles;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt = t % m_tiles;
+  const int rest = t / m_tiles;
+  const int split = rest % splits;
+  const int nt = rest / splits;
   const int m0 = mt * BM;
-  // SWIGLU: a tile covers 64 features (32 gate + 32 up rows per wave column)
   const int n0 = (EPI == EPI_SWIGLU) ? nt * (BN / 2) : nt * BN;
+  const int kbeg = split * kps;
+  const int kend = min(g.K, kbeg + kps);
+  const int nk = (kend - kbeg) / BK;
 
   const bf16_t* __restrict__ A = static_cast<const bf16_t*>(g.A);
   const bf16_t* __restrict__ B = static_cast<const bf16_t*>(g.B);
 
-  // per-thread global source rows for its 4 A chunks and 4 B chunks
-  const bf16_t* arow[4];
-  const bf16_t* brow[4];
-  int lrow[4], lcol[4];
+  // A fragment rows of this lane
+  const bf16_t* arow[FM];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int c = tid + u * kThreads;  // 0..1023
-    lrow[u] = c >> 3;
-    lcol[u] = (c & 7) * 8;
-    const int m = m0 + lrow[u];
-    arow[u] = nullptr;
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+    arow[i] = nullptr;
     if (m < g.M) {
       const int src = g.a_rows ? g.a_rows[m] : m;
-      arow[u] = A + static_cast<int64_t>(src) * g.lda + lcol[u];
+      arow[i] = A + static_cast<int64_t>(src) * g.lda + (lane >> 5) * 8;
     }
-    int brow_idx;
-    bool bvalid;
+  }
+  // B staging chunks of this thread
+  const bf16_t* brow[NB];
+  int lrow[NB], lcol[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int c = tid + u * kThreads;
+    lrow[u] = c >> 3;
+    lcol[u] = (c & 7) * 8;
+    int bi;
+    bool ok;
     if (EPI == EPI_SWIGLU) {
       const int r = lrow[u];
-      const int f = n0 + (r >> 6) * 32 + (r & 31);
-      bvalid = f < g.N;
-      brow_idx = ((r >> 5) & 1) ? g.ff + f : f;
+      const int g32 = r >> 5;
+      const int f = n0 + (g32 >> 1) * 32 + (r & 31);
+      ok = f < g.N;
+      bi = (g32 & 1) ? g.ff + f : f;
     } else {
-      brow_idx = n0 + lrow[u];
-      bvalid = brow_idx < g.N;
+      bi = n0 + lrow[u];
+      ok = bi < g.N;
     }
-    brow[u] = bvalid ? B + static_cast<int64_t>(brow_idx) * g.ldb + lcol[u] : nullptr;
+    brow[u] = ok ? B + static_cast<int64_t>(bi) * g.ldb + lcol[u] : nullptr;
   }
 
-  uint4 ra[4], rb[4];
-  auto gload = [&](int k0) {
+  typedef uint4 AFrag[BK / 16][FM];
+  AFrag acur, anxt;
+  uint4 breg[NB];
+  auto load_a = [&](AFrag& dst, int k0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ra[u] = arow[u] ? *reinterpret_cast<const uint4*>(arow[u] + k0) : make_uint4(0, 0, 0, 0);
-      rb[u] = brow[u] ? *reinterpret_cast<const uint4*>(brow[u] + k0) : make_uint4(0, 0, 0, 0);
-    }
+    for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        dst[ks][i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + ks * 16) : make_uint4(0, 0, 0, 0);
   };
-  auto lstore = [&](int buf) {
+  auto load_b = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *reinterpret_cast<uint4*>(&As[buf][lrow[u] * LDSP + lcol[u]]) = ra[u];
-      *reinterpret_cast<uint4*>(&Bs[buf][lrow[u] * LDSP + lcol[u]]) = rb[u];
-    }
+    for (int u = 0; u < NB; ++u)
+      breg[u] = brow[u] ? *reinterpret_cast<const uint4*>(brow[u] + k0) : make_uint4(0, 0, 0, 0);
+  };
+  auto store_b = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) *reinterpret_cast<uint4*>(&Bs[buf][lrow[u] * LDSP + lcol[u]]) = breg[u];
   };
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = g.K / BK;
-  gload(0);
-  lstore(0);
+  if (nk > 0) {
+    load_b(kbeg);
+    load_a(acur, kbeg);
+    store_b(0);
+  }
   __syncthreads();
-
-  const int fr = lane & 31;          // fragment row (A) / column (B)
-  const int fk = (lane >> 5) * 8;    // fragment k offset
+  const int fr = lane & 31;
+  const int fk = (lane >> 5) * 8;
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const bf16_t* as = As[buf];
+    const int knext = kbeg + (kt + 1) * BK;
+    if (kt + 1 < nk) {
+      load_b(knext);
+      load_a(anxt, knext);
+    }
     const bf16_t* bs = Bs[buf];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t af[2], bfr[2];
+      bf16x8_t bfr[FN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&as[(wm * 64 + i * 32 + fr) * LDSP + ks * 16 + fk]);
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&bs[(wn * WTN + j * 32 + fr) * LDSP + ks * 16 + fk]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&bs[(wn * 64 + j * 32 + fr) * LDSP + ks * 16 + fk]);
+      for (int i = 0; i < FM; ++i) {
+        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, acur[ks][i]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+      }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+    if (kt + 1 < nk) {
+      store_b(buf ^ 1);
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acur[ks][i] = anxt[ks][i];
+    }
     __syncthreads();
   }
 
   // ---------------- epilogue ----------------
   // acc[i][j][v] holds C[row][col] with
-  //   row = m0 + wm*64 + i*32 + 8*(v/4) + 4*(lane/32) + v%4,  col = wn*64 + j*32 + lane%32
+  //   row = m0 + wm*WTM + i*32 + 8*(v/4) + 4*(lane/32) + v%4,  col = wn*WTN + j*32 + lane%32
   const int half = g.head_dim >> 1;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int row = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       const bool rok = row < g.M;
-      if constexpr (EPI == EPI_SWIGLU) {
-        const int f = n0 + wn * 32 + (lane & 31);
-        if (rok && f < g.N) {
-          const float h = silu(acc[i][0][v]) * acc[i][1][v];
-          static_cast<bf16_t*>(g.C)[static_cast<int64_t>(row) * g.ldc + f] = f2bf(h);
+      if constexpr (SPLIT) {
+        float* prow = g.part + (static_cast<int64_t>(split) * g.M + row) * g.N;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+          if (rok && col < g.N) prow[col] = acc[i][j][v];
+        }
+      } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < FN; j += 2) {
+          const int f = n0 + wn * (WTN / 2) + (j / 2) * 32 + (lane & 31);
+          if (rok && f < g.N) {
+            const float h = silu(acc[i][j][v]) * acc[i][j + 1][v];
+            static_cast<bf16_t*>(g.C)[static_cast<int64_t>(row) * g.ldc + f] = f2bf(h);
+          }
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+        for (int j = 0; j < FN; ++j) {
+          const int col = n0 + wn * WTN + j * 32 + (lane & 31);
           float val = acc[i][j][v];
           if constexpr (EPI == EPI_STORE_ROPE || EPI == EPI_F32_ROPE) {
             const float other = __shfl_xor(val, 1, 64);
@@ -186,6 +230,49 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g) {
           }
         }
       }
+    }
+  }
+}
+
+// Split-K reduction in fixed split order, then the epilogue (4 columns per thread).
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int splits) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int n4 = g.N / 4;
+  if (idx >= static_cast<int64_t>(g.M) * n4) return;
+  const int row = static_cast<int>(idx / n4);
+  const int col = static_cast<int>(idx % n4) * 4;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < splits; ++sp) {
+    const float4 p = *reinterpret_cast<const float4*>(g.part + (static_cast<int64_t>(sp) * g.M + row) * g.N + col);
+    s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+  }
+  float v[4] = {s.x, s.y, s.z, s.w};
+  if constexpr (EPI == EPI_RESID) {
+    const int rr = g.resid_rows ? g.resid_rows[row] : row;
+    const float4 r = *reinterpret_cast<const float4*>(g.resid + static_cast<int64_t>(rr) * g.ld_resid + col);
+    *reinterpret_cast<float4*>(static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + col) =
+        make_float4(r.x + v[0], r.y + v[1], r.z + v[2], r.w + v[3]);
+  } else {
+    if (col < g.rope_cols) {
+      const int p = g.row_pos[row];
+      const int half = g.head_dim >> 1;
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const float2 cs = g.rope_tab[static_cast<int64_t>(p) * half + (((col + j) % g.head_dim) >> 1)];
+        const float x0 = v[j], x1 = v[j + 1];
+        v[j] = x0 * cs.x - x1 * cs.y;
+        v[j + 1] = x0 * cs.y + x1 * cs.x;
+      }
+    }
+    if constexpr (EPI == EPI_STORE_ROPE) {
+      uint2 w;
+      w.x = static_cast<uint32_t>(f2bf(v[0])) | (static_cast<uint32_t>(f2bf(v[1])) << 16);
+      w.y = static_cast<uint32_t>(f2bf(v[2])) | (static_cast<uint32_t>(f2bf(v[3])) << 16);
+      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.C) + static_cast<int64_t>(row) * g.ldc + col) = w;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + col) =
+          make_float4(v[0], v[1], v[2], v[3]);
     }
   }
 }
@@ -293,19 +380,64 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
+template <int EPI, int WTM, int WTN, bool SPLIT>
+hipError_t launch_cfg(const GemmArgs& a, int tiles, int splits, int kps, hipStream_t s) {
+  gemm_bf16_kernel<EPI, WTM, WTN, SPLIT><<<tiles * splits, kThreads, 0, s>>>(a, splits, kps);
+  return hipGetLastError();
+}
+
+inline int tiles_of(const GemmArgs& a, int epi, int bm, int bn) {
+  const int mt = (a.M + bm - 1) / bm;
+  const int nt = (epi == EPI_SWIGLU) ? (a.N + bn / 2 - 1) / (bn / 2) : (a.N + bn - 1) / bn;
+  return mt * nt;
+}
+
+// fraction of the last wave of workgroups that is busy (256 CUs, 1 workgroup each)
+inline double wave_eff(int wgs) {
+  const int waves = (wgs + 255) / 256;
+  return static_cast<double>(wgs) / (256.0 * waves);
+}
+
 template <int EPI>
 hipError_t run_gemm(cb_dtype dt, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
-  if (dt == CB_BF16) {
-    const int m_tiles = (a.M + BM - 1) / BM;
-    const int n_tiles = (EPI == EPI_SWIGLU) ? (a.N + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
-    gemm_bf16_kernel<EPI><<<m_tiles * n_tiles, kThreads, 0, s>>>(a);
-  } else {
+  if (dt != CB_BF16) {
     const int m_tiles = (a.M + FM - 1) / FM;
     const int n_tiles = (EPI == EPI_SWIGLU) ? (a.N + FN / 2 - 1) / (FN / 2) : (a.N + FN - 1) / FN;
     gemm_f32_kernel<EPI><<<m_tiles * n_tiles, 256, 0, s>>>(a);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  const int t256 = tiles_of(a, EPI, 256, 256);
+  if (t256 >= 240) return launch_cfg<EPI, 128, 128, false>(a, t256, 1, a.K, s);
+  const int t128x256 = tiles_of(a, EPI, 128, 256);
+  if (t128x256 >= 240) return launch_cfg<EPI, 64, 128, false>(a, t128x256, 1, a.K, s);
+  const int t128 = tiles_of(a, EPI, 128, 128);
+  int splits = 1;
+  if constexpr (EPI != EPI_SWIGLU) {
+    if (t128 < 240 && a.part != nullptr) {
+      double best = wave_eff(t128);
+      for (int sp = 2; sp <= 8; ++sp) {
+        if (a.K / sp < 512) break;
+        if (static_cast<int64_t>(sp) * a.M * a.N > a.part_floats) break;
+        const double e = wave_eff(t128 * sp) * std::min(1.0, t128 * sp / 256.0);
+        if (e > best + 1e-9) {
+          best = e;
+          splits = sp;
+        }
+      }
+      if (wave_eff(t128) * std::min(1.0, t128 / 256.0) >= best) splits = 1;
+    }
+  }
+  if (splits == 1) return launch_cfg<EPI, 64, 64, false>(a, t128, 1, a.K, s);
+  const int kps = ((a.K / BK + splits - 1) / splits) * BK;
+  hipError_t e = launch_cfg<EPI, 64, 64, true>(a, t128, splits, kps, s);
+  if (e != hipSuccess) return e;
+  if constexpr (EPI != EPI_SWIGLU) {
+    const int64_t n = static_cast<int64_t>(a.M) * (a.N / 4);
+    splitk_reduce_kernel<EPI><<<static_cast<int>((n + 255) / 256), 256, 0, s>>>(a, splits);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace

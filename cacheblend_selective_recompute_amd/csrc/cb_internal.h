@@ -137,7 +137,10 @@ struct GemmArgs {
   const int32_t* resid_rows;
   int64_t ld_resid;
   int ff;                  // SWIGLU: row offset of the up half in B
+  float* part;             // split-K partial sums (fp32), may be NULL (no split)
+  int64_t part_floats;     // capacity of part
 };
+constexpr int64_t kGemmPartFloats = int64_t(32) << 20;   // 128 MiB of split-K partials
 hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------------------
@@ -155,8 +158,15 @@ struct AttnArgs {
   int layer;
   int n_q_heads, n_kv_heads, head_dim;
   float scale;
+  int kv_bound;            // host-known bound: every row position is < kv_bound
+  float* part_o;           // split-KV partials, attn_partial_floats(head_dim) floats
+  float2* part_ml;         // split-KV (max, sum) pairs, attn_partial_rows() entries
 };
 hipError_t launch_attention(cb_dtype dt, const AttnArgs& a, hipStream_t s);
+// workspace bound of the split-KV partials
+constexpr int kAttnMaxSplits = 8;
+constexpr int64_t kAttnPartialRows = int64_t(kAttnMaxSplits) * 32768;   // (split, row, q head) triples
+inline int64_t attn_partial_floats(int head_dim) { return kAttnPartialRows * head_dim; }
 bool attention_supported(cb_dtype dt, int n_q_heads, int n_kv_heads, int head_dim);
 
 }  // namespace cb

@@ -94,6 +94,7 @@ def test_workspace_bytes(lib):
     T = 4160
     # residual stream x2, activations, MLP hidden, q, o, fresh K/V (fp32): the bulk
     bulk = T * 4096 * 4 * 2 + T * 4096 * 2 + T * 14336 * 2 + T * 4096 * 2 * 2 + T * 2048 * 4
+    bulk += 8 * 32768 * (128 * 4 + 8) + (32 << 20) * 4   # split-KV attention and split-K GEMM partials
     assert bulk < b < bulk * 1.05
     assert lib.cb_workspace_bytes(ctypes.byref(c), 8192, 64, 4) > b
     assert lib.cb_workspace_bytes(ctypes.byref(cfg8b(n_layers=1)), 4096, 64, 4) == 0

@@ -4,9 +4,9 @@ oracle chunk tuples, and the comparison rules.
 Tolerances (normwise, max|gpu - ref| / max|ref|):
   * bf16 models (bf16 products, fp32 accumulation): blended K/V and logits 2e-2;
   * fp32 models: 1e-4.
-HKVD sets: at least 99% of the k kept positions agree; every disagreement
-lies within the tie band |Δ_j - Δ_(k)| <= 1e-3 * Δ_(k) + eps_abs of the
-oracle's own deviations.
+HKVD sets: the keep/drop decision agrees on at least 99% of the candidate
+tokens, and every disagreement lies within the tie band
+|Δ_j - Δ_(k)| <= 1e-3 * Δ_(k) + eps_abs of the oracle's own deviations.
 """
 from __future__ import annotations
 
@@ -105,6 +105,7 @@ def check_sets(gpu_set, ora_set, cand, dev_ora, k, kv_scale_sq, label=""):
         assert p in dmap, f"{label}: position {p} is not a candidate"
         assert abs(dmap[p] - dk) <= 1e-3 * dk + eps_abs, \
             f"{label}: disagreement at {p}: dev {dmap[p]:.6g} vs k-th {dk:.6g}"
-    frac = inter / k
-    assert frac >= 0.99, f"{label}: only {frac:.4f} of the kept set agrees"
+    frac = 1.0 - len(g ^ o) / len(cand)
+    assert frac >= 0.99, f"{label}: the keep/drop decision agrees on only {frac:.4f} of the candidates"
+    say(f"  {label}: {inter}/{k} kept positions shared, decision agreement {frac:.4f}")
     return frac

@@ -227,10 +227,11 @@ size_t carve(const cb_model_cfg& c, int64_t N, int64_t Q, int64_t C, void* base,
   t.tokens = static_cast<int32_t*>(take(T * 4));
   t.x0 = static_cast<float*>(take(T * c.d_model * 4));
   t.x1 = static_cast<float*>(take(T * c.d_model * 4));
-  t.act = take(T * c.d_model * es);
-  t.h = take(T * c.d_ff * es);
+  const int64_t TP = pk_rows(T);   // fragment-major activations hold whole 32-row blocks
+  t.act = take(TP * c.d_model * es);
+  t.h = take(TP * std::max(c.d_ff, c.d_model) * es);
   t.q = take(T * qw * es);
-  t.o = take(T * qw * es);
+  t.o = take(TP * qw * es);
   t.kvf = static_cast<float*>(take(T * 2 * kvw * 4));
   t.dev = static_cast<float*>(take(N * 4));
   t.posA = static_cast<int32_t*>(take(N * 4));
@@ -344,9 +345,16 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   // fill: fresh K/V of the kept rows and of the suffix replace the cache
   CB_LAUNCH(tr, CB_KIND_SCATTER, launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, w.gmap, io.rowpos_out, rout, kv, l, kvw, s), "scatter");
 
-  // queries of the kept rows
+  // queries of the kept rows: when the set shrank, normalise the kept rows into
+  // their own (fragment-major) buffer
+  const void* aq = w.act;
+  if (k != nc) {
+    CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, io.x_in, w.gmap, d, rout, d, lw.attn_norm, c.rms_eps, w.h, d, 0, s),
+              "rmsnorm");
+    aq = w.h;
+  }
   g = GemmArgs{};
-  g.A = w.act; g.lda = d; g.a_rows = w.gmap;
+  g.A = aq; g.lda = d; g.a_rows = nullptr;
   g.B = lw.w_qkv; g.ldb = d;
   g.M = rout; g.N = qw; g.K = d;
   g.C = w.q; g.ldc = qw;
@@ -404,15 +412,19 @@ cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, fl
   g.part = w.gemm_part;
   g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
+  // suffix K/V: rows from the 32-row block holding position N (fragment-major A
+  // starts on a block), the extra leading rows are computed and not scattered
+  const int N32 = N & ~31;
+  const int64_t a_off = (c.dtype == CB_BF16) ? pk_off(N32, 0, d) : (int64_t)N32 * d;
   g = GemmArgs{};
-  g.A = static_cast<const char*>(w.act) + (int64_t)N * d * es; g.lda = d;
+  g.A = static_cast<const char*>(w.act) + a_off * es; g.lda = d;
   g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * es; g.ldb = d;
-  g.M = Q; g.N = 2 * kvw; g.K = d; g.C = w.kvf; g.ldc = 2 * kvw;
-  g.rope_cols = kvw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = w.rowpos0 + N;
+  g.M = T - N32; g.N = 2 * kvw; g.K = d; g.C = w.kvf; g.ldc = 2 * kvw;
+  g.rope_cols = kvw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = w.rowpos0 + N32;
   g.part = w.gemm_part;
   g.part_floats = kGemmPartFloats;
   CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "suffix kv gemm");
-  CB_LAUNCH(tr, CB_KIND_SCATTER, launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, nullptr, w.rowpos0 + N, Q, kv, 0, kvw, s), "suffix scatter");
+  CB_LAUNCH(tr, CB_KIND_SCATTER, launch_scatter_kv(c.dtype, w.kvf + (int64_t)(N - N32) * 2 * kvw, 2 * kvw, nullptr, w.rowpos0 + N, Q, kv, 0, kvw, s), "suffix scatter");
   AttnArgs at{};
   at.q = w.q; at.ldq = qw; at.o = w.o; at.ldo = qw; at.rowpos = w.rowpos0; at.R = T;
   at.cache = kv; at.layer = 0; at.n_q_heads = c.n_q_heads; at.n_kv_heads = c.n_kv_heads; at.head_dim = c.head_dim;

@@ -206,14 +206,15 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits
   if (!qvalid) return;
   if (n_splits == 1) {
     const float inv = 1.0f / l_tot;
-    bf16_t* op = static_cast<bf16_t*>(a.o) + static_cast<int64_t>(qtok) * a.ldo + qhead * DH;
-    // o[dt][i] = O[q][16*dt + 4*kgrp + i]
+    bf16_t* ob = static_cast<bf16_t*>(a.o);
+    const int KO = a.n_q_heads * DH;
+    // o[dt][i] = O[q][16*dt + 4*kgrp + i]; written fragment-major (4 consecutive columns = 8 bytes)
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) {
       uint2 w;
       w.x = static_cast<uint32_t>(f2bf(o[dt][0] * inv)) | (static_cast<uint32_t>(f2bf(o[dt][1] * inv)) << 16);
       w.y = static_cast<uint32_t>(f2bf(o[dt][2] * inv)) | (static_cast<uint32_t>(f2bf(o[dt][3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(op + 16 * dt + 4 * kgrp) = w;
+      *reinterpret_cast<uint2*>(ob + pk_off(qtok, qhead * DH + 16 * dt + 4 * kgrp, KO)) = w;
     }
   } else {
     // unnormalised partial for (split, row, head); m in log2 units
@@ -251,9 +252,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_spl
     for (int e = 0; e < PER; ++e) acc[e] += w * a.part_o[pr * DH + lane * PER + e];
   }
   const float inv = 1.0f / lsum;
-  bf16_t* op = static_cast<bf16_t*>(a.o) + static_cast<int64_t>(row) * a.ldo + head * DH + lane * PER;
+  bf16_t* ob = static_cast<bf16_t*>(a.o);
+  const int KO = a.n_q_heads * DH;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) op[e] = f2bf(acc[e] * inv);
+  for (int e = 0; e < PER; ++e) ob[pk_off(row, head * DH + lane * PER + e, KO)] = f2bf(acc[e] * inv);
 }
 
 // ---------------------------------------------------------------------------

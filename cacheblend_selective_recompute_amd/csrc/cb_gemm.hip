@@ -1,6 +1,6 @@
-// Gather-GEMM of the selected rows: C[M][N] = A[a_rows[m]][:] . B[n][:]
-// with the epilogues the decoder block needs fused in (RoPE of Q/K at the
-// rows' positions, residual add with a row gather, SiLU-gated MLP).
+// Gather-GEMM of the selected rows: C[M][N] = A[M][:] . B[n][:] with the
+// epilogues the decoder block needs fused in (RoPE of Q/K at the rows'
+// positions, residual add with a row gather, SiLU-gated MLP).
 //
 // Method: "CacheBlend 完全拆解" (pinghaoyang.com.cn), Fig. 5 -- only the
 // selected tokens go through the projections; the recompute cost is
@@ -10,12 +10,13 @@
 // (2 WTM) x (2 WTN) x 64.  Weight tiles are staged through LDS (row pitch padded
 // by 16 B so the 32 rows one fragment read touches fall in distinct banks; two
 // buffers so the next tile is in flight while the current one is multiplied);
-// activation rows are gathered straight into MFMA fragments.  The tile shape is
-// chosen per call (256x256, 128x256 or 128x128) so the grid fills the 256 CUs;
-// small-N projections split K and reduce the fp32 partials in a fixed order
-// in a second kernel that also applies the epilogue.  Tiles are ordered
-// M-fastest and mapped so consecutive tiles land on the same XCD, so the M
-// tiles that share one weight tile share that XCD's L2.
+// activations arrive fragment-major (see pk_off) from the kernels that produce
+// them, so each A fragment is one contiguous 1 KiB wave load straight into
+// registers.  The tile shape and a split of K are chosen per call from measured
+// per-configuration rates so the grid fills the 256 CUs; split-K partials are
+// reduced in a fixed order by a second kernel that also applies the epilogue.
+// Tiles are ordered M-fastest and mapped so consecutive tiles land on the same
+// XCD, so the M tiles that share one weight tile share that XCD's L2.
 // fp32 path: a plain LDS-tiled FMA kernel (fp32 models are small).
 #include <algorithm>
 
@@ -75,16 +76,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g, int spl
   const bf16_t* __restrict__ A = static_cast<const bf16_t*>(g.A);
   const bf16_t* __restrict__ B = static_cast<const bf16_t*>(g.B);
 
-  // A fragment rows of this lane
+  const int kb_per_row = g.K >> 4;
+  const int mb_valid = (g.M + 31) >> 5;
   const bf16_t* arow[FM];
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * WTM + i * 32 + (lane & 31);
-    arow[i] = nullptr;
-    if (m < g.M) {
-      const int src = g.a_rows ? g.a_rows[m] : m;
-      arow[i] = A + static_cast<int64_t>(src) * g.lda + (lane >> 5) * 8;
-    }
+    const int mb = (m0 + wm * WTM + i * 32) >> 5;
+    arow[i] = (mb < mb_valid) ? A + (static_cast<int64_t>(mb) * kb_per_row * 64 + lane) * 8 : nullptr;
   }
   // B staging chunks of this thread
   const bf16_t* brow[NB];
@@ -117,7 +115,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g, int spl
     for (int ks = 0; ks < BK / 16; ++ks)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        dst[ks][i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0 + ks * 16) : make_uint4(0, 0, 0, 0);
+        dst[ks][i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + static_cast<int64_t>((k0 >> 4) + ks) * 512)
+                             : make_uint4(0, 0, 0, 0);
   };
   auto load_b = [&](int k0) {
 #pragma unroll
@@ -200,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g, int spl
           const int f = n0 + wn * (WTN / 2) + (j / 2) * 32 + (lane & 31);
           if (rok && f < g.N) {
             const float h = silu(acc[i][j][v]) * acc[i][j + 1][v];
-            static_cast<bf16_t*>(g.C)[static_cast<int64_t>(row) * g.ldc + f] = f2bf(h);
+            static_cast<bf16_t*>(g.C)[pk_off(row, f, static_cast<int>(g.ldc))] = f2bf(h);
           }
         }
       } else {
@@ -392,10 +391,60 @@ inline int tiles_of(const GemmArgs& a, int epi, int bm, int bn) {
   return mt * nt;
 }
 
-// fraction of the last wave of workgroups that is busy (256 CUs, 1 workgroup each)
-inline double wave_eff(int wgs) {
-  const int waves = (wgs + 255) / 256;
-  return static_cast<double>(wgs) / (256.0 * waves);
+// Split-K cost model for the 128x128 tile, calibrated on the GEMM
+// microbenchmark: a workgroup computes 2*128*128*k FLOP at ~2.2 TFLOP/s when it
+// has a CU to itself and ~1.65 TFLOP/s when two share one (two fit per CU);
+// workgroups run in rounds of 512; the fixed-order reduction moves the fp32
+// partials once (write + read) at ~5 TB/s plus a launch.
+inline double est_time_128(const GemmArgs& a, int epi, int splits) {
+  const int64_t wgs = static_cast<int64_t>(tiles_of(a, epi, 128, 128)) * splits;
+  const double flop_wg = 2.0 * 128 * 128 * (static_cast<double>(a.K) / splits);
+  double tm;
+  if (wgs <= 256) tm = flop_wg / 2.2e12;
+  else tm = static_cast<double>((wgs + 511) / 512) * flop_wg / 1.65e12;
+  if (splits > 1) tm += static_cast<double>(splits) * a.M * a.N * 8.0 / 5e12 + 3e-6;
+  return tm;
+}
+
+}  // namespace
+
+void choose_gemm_cfg(const GemmArgs& a, int epi, int* cfg, int* splits) {
+  // the 128x128 tile (two workgroups per CU) is at least as fast per CU as the
+  // larger tiles at every blend shape measured, and quantises better
+  *cfg = GEMM_CFG_128x128;
+  *splits = 1;
+  if (epi == EPI_SWIGLU || a.part == nullptr) return;
+  double best = est_time_128(a, epi, 1);
+  for (int sp = 2; sp <= 8; ++sp) {
+    if (a.K / sp < 512) break;
+    if (static_cast<int64_t>(sp) * a.M * a.N > a.part_floats) break;
+    const double tm = est_time_128(a, epi, sp);
+    if (tm < best * 0.97) {
+      best = tm;
+      *splits = sp;
+    }
+  }
+}
+
+namespace {
+
+template <int EPI>
+hipError_t run_cfg(const GemmArgs& a, int cfg, int splits, hipStream_t s) {
+  if (splits > 1) {
+    if constexpr (EPI == EPI_SWIGLU) return hipErrorInvalidValue;
+    const int t = tiles_of(a, EPI, 128, 128);
+    const int kps = ((a.K / BK + splits - 1) / splits) * BK;
+    hipError_t e = launch_cfg<EPI, 64, 64, true>(a, t, splits, kps, s);
+    if (e != hipSuccess) return e;
+    const int64_t n = static_cast<int64_t>(a.M) * (a.N / 4);
+    splitk_reduce_kernel<EPI><<<static_cast<int>((n + 255) / 256), 256, 0, s>>>(a, splits);
+    return hipGetLastError();
+  }
+  switch (cfg) {
+    case GEMM_CFG_256x256: return launch_cfg<EPI, 128, 128, false>(a, tiles_of(a, EPI, 256, 256), 1, a.K, s);
+    case GEMM_CFG_128x256: return launch_cfg<EPI, 64, 128, false>(a, tiles_of(a, EPI, 128, 256), 1, a.K, s);
+    default: return launch_cfg<EPI, 64, 64, false>(a, tiles_of(a, EPI, 128, 128), 1, a.K, s);
+  }
 }
 
 template <int EPI>
@@ -407,40 +456,22 @@ hipError_t run_gemm(cb_dtype dt, const GemmArgs& a, hipStream_t s) {
     gemm_f32_kernel<EPI><<<m_tiles * n_tiles, 256, 0, s>>>(a);
     return hipGetLastError();
   }
-  const int t256 = tiles_of(a, EPI, 256, 256);
-  if (t256 >= 240) return launch_cfg<EPI, 128, 128, false>(a, t256, 1, a.K, s);
-  const int t128x256 = tiles_of(a, EPI, 128, 256);
-  if (t128x256 >= 240) return launch_cfg<EPI, 64, 128, false>(a, t128x256, 1, a.K, s);
-  const int t128 = tiles_of(a, EPI, 128, 128);
-  int splits = 1;
-  if constexpr (EPI != EPI_SWIGLU) {
-    if (t128 < 240 && a.part != nullptr) {
-      double best = wave_eff(t128);
-      for (int sp = 2; sp <= 8; ++sp) {
-        if (a.K / sp < 512) break;
-        if (static_cast<int64_t>(sp) * a.M * a.N > a.part_floats) break;
-        const double e = wave_eff(t128 * sp) * std::min(1.0, t128 * sp / 256.0);
-        if (e > best + 1e-9) {
-          best = e;
-          splits = sp;
-        }
-      }
-      if (wave_eff(t128) * std::min(1.0, t128 / 256.0) >= best) splits = 1;
-    }
-  }
-  if (splits == 1) return launch_cfg<EPI, 64, 64, false>(a, t128, 1, a.K, s);
-  const int kps = ((a.K / BK + splits - 1) / splits) * BK;
-  hipError_t e = launch_cfg<EPI, 64, 64, true>(a, t128, splits, kps, s);
-  if (e != hipSuccess) return e;
-  if constexpr (EPI != EPI_SWIGLU) {
-    const int64_t n = static_cast<int64_t>(a.M) * (a.N / 4);
-    splitk_reduce_kernel<EPI><<<static_cast<int>((n + 255) / 256), 256, 0, s>>>(a, splits);
-    e = hipGetLastError();
-  }
-  return e;
+  int cfg, splits;
+  choose_gemm_cfg(a, EPI, &cfg, &splits);
+  return run_cfg<EPI>(a, cfg, splits, s);
 }
 
 }  // namespace
+
+hipError_t launch_gemm_cfg(GemmEpi epi, const GemmArgs& a, int cfg, int splits, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE_ROPE: return run_cfg<EPI_STORE_ROPE>(a, cfg, splits, s);
+    case EPI_F32_ROPE: return run_cfg<EPI_F32_ROPE>(a, cfg, splits, s);
+    case EPI_RESID: return run_cfg<EPI_RESID>(a, cfg, splits, s);
+    case EPI_SWIGLU: return run_cfg<EPI_SWIGLU>(a, cfg, splits, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {

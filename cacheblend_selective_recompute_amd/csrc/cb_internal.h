@@ -49,6 +49,16 @@ __device__ __forceinline__ int64_t paged_row(const int32_t* bt, int32_t bs, int3
   return static_cast<int64_t>(bt[pos / bs]) * bs + (pos % bs);
 }
 
+// Fragment-major layout of bf16 GEMM A operands (activations).  A matrix of
+// K columns is stored as blocks of 32 rows x 16 columns; each block is the
+// 64 x 16-byte A fragment of one v_mfma_f32_32x32x16_bf16 (lane l holds row
+// l % 32, columns 8 * (l / 32) .. +7), so one wave loads a fragment as a single
+// contiguous 1 KiB read.  Buffers hold ceil(rows / 32) * 32 rows.
+__host__ __device__ __forceinline__ int64_t pk_off(int m, int k, int K) {
+  return ((static_cast<int64_t>(m >> 5) * (K >> 4) + (k >> 4)) * 64 + ((k >> 3) & 1) * 32 + (m & 31)) * 8 + (k & 7);
+}
+__host__ __device__ __forceinline__ int64_t pk_rows(int64_t rows) { return (rows + 31) / 32 * 32; }
+
 // Chunk descriptors are passed by value in kernel arguments.
 constexpr int kMaxChunksPerLaunch = 32;
 struct ChunkDesc {
@@ -87,7 +97,8 @@ hipError_t launch_gather_tokens(const ChunkBatch& b, int32_t* out, hipStream_t s
 // x[t][:] = embed[tok[t]][:] (fp32 out)
 hipError_t launch_embed(cb_dtype dt, const int32_t* tok, int rows, const void* embed, int d, float* x,
                         hipStream_t s);
-// out[i] = RMSNorm(x[ridx ? ridx[i] : i]) * g, out in model dtype (or fp32 when out_f32)
+// out[i] = RMSNorm(x[ridx ? ridx[i] : i]) * g, out in model dtype (or fp32 when out_f32);
+// bf16 output is written in the fragment-major layout (K = d), fp32 output row-major
 hipError_t launch_rmsnorm(cb_dtype dt, const float* x, const int32_t* ridx, int64_t ldx, int rows, int d,
                           const float* g, float eps, void* out, int64_t ldo, int out_f32, hipStream_t s);
 // dev[i] = ||kf[i]-K[pos[i]]||^2 + ||vf[i]-V[pos[i]]||^2 ; optionally dev_by_pos[pos[i]] = dev[i]
@@ -120,10 +131,12 @@ enum GemmEpi : int {
   EPI_RESID = 2,        // C (fp32)[i] = resid[resid_rows ? resid_rows[i] : i] + acc
   EPI_SWIGLU = 3,       // C (model dtype)[i][f] = SiLU(A.Wg[f]) * (A.Wu[f]); B rows [0,ff) gate, [ff,2ff) up
 };
+// bf16: A is fragment-major (K columns), SWIGLU output C is fragment-major (ldc = its K);
+// fp32: everything row-major.
 struct GemmArgs {
   const void* A;
   int64_t lda;
-  const int32_t* a_rows;   // row gather for A (NULL = identity)
+  const int32_t* a_rows;   // row gather for A (fp32 path only; NULL = identity)
   const void* B;
   int64_t ldb;
   int M, N, K;             // N = output columns (features for SWIGLU)
@@ -142,10 +155,17 @@ struct GemmArgs {
 };
 constexpr int64_t kGemmPartFloats = int64_t(32) << 20;   // 128 MiB of split-K partials
 hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s);
+// bf16 tile configurations (block tile M x N); launch_gemm picks one per call
+enum GemmCfg : int { GEMM_CFG_256x256 = 0, GEMM_CFG_128x256 = 1, GEMM_CFG_128x128 = 2 };
+// bf16 GEMM with an explicit configuration (splits > 1: 128x128 tiles, split K)
+hipError_t launch_gemm_cfg(GemmEpi epi, const GemmArgs& a, int cfg, int splits, hipStream_t s);
+// the configuration launch_gemm would use for these arguments
+void choose_gemm_cfg(const GemmArgs& a, int epi, int* cfg, int* splits);
 
 // ---------------------------------------------------------------------------
 // Attention of query rows over a paged cache (causal by absolute position).
-// q/o: [R][Hq*dh] in the model dtype; rowpos[R] ascending.
+// q: [R][Hq*dh] row-major in the model dtype; o: bf16 fragment-major (K = Hq*dh),
+// fp32 row-major; rowpos[R] ascending.
 // ---------------------------------------------------------------------------
 struct AttnArgs {
   const void* q;

@@ -169,7 +169,7 @@ __global__ void embed_kernel(const int32_t* tok, const T* emb, int d, float* x) 
 // ---------------------------------------------------------------------------
 // RMSNorm: one 256-thread block per row; fp32 statistics reduced in fixed order
 // ---------------------------------------------------------------------------
-template <typename TO>
+template <typename TO, bool PACKED>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const int32_t* ridx, int64_t ldx, int d,
                                                       const float* g, float eps, TO* out, int64_t ldo) {
   __shared__ float red[4];
@@ -186,14 +186,21 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const int3
   __syncthreads();
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
-  TO* o = out + static_cast<int64_t>(r) * ldo;
   for (int e = threadIdx.x * 4; e < d; e += 256 * 4) {
     const float4 v = *reinterpret_cast<const float4*>(xr + e);
     const float4 gg = *reinterpret_cast<const float4*>(g + e);
-    o[e + 0] = from_f<TO>(v.x * inv * gg.x);
-    o[e + 1] = from_f<TO>(v.y * inv * gg.y);
-    o[e + 2] = from_f<TO>(v.z * inv * gg.z);
-    o[e + 3] = from_f<TO>(v.w * inv * gg.w);
+    if constexpr (PACKED) {
+      uint2 w;
+      w.x = static_cast<uint32_t>(f2bf(v.x * inv * gg.x)) | (static_cast<uint32_t>(f2bf(v.y * inv * gg.y)) << 16);
+      w.y = static_cast<uint32_t>(f2bf(v.z * inv * gg.z)) | (static_cast<uint32_t>(f2bf(v.w * inv * gg.w)) << 16);
+      *reinterpret_cast<uint2*>(out + pk_off(r, e, d)) = w;
+    } else {
+      TO* o = out + static_cast<int64_t>(r) * ldo;
+      o[e + 0] = from_f<TO>(v.x * inv * gg.x);
+      o[e + 1] = from_f<TO>(v.y * inv * gg.y);
+      o[e + 2] = from_f<TO>(v.z * inv * gg.z);
+      o[e + 3] = from_f<TO>(v.w * inv * gg.w);
+    }
   }
 }
 
@@ -475,9 +482,9 @@ hipError_t launch_rmsnorm(cb_dtype dt, const float* x, const int32_t* ridx, int6
                           const float* g, float eps, void* out, int64_t ldo, int out_f32, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (out_f32 || dt == CB_F32)
-    rmsnorm_kernel<float><<<rows, 256, 0, s>>>(x, ridx, ldx, d, g, eps, static_cast<float*>(out), ldo);
+    rmsnorm_kernel<float, false><<<rows, 256, 0, s>>>(x, ridx, ldx, d, g, eps, static_cast<float*>(out), ldo);
   else
-    rmsnorm_kernel<bf16_t><<<rows, 256, 0, s>>>(x, ridx, ldx, d, g, eps, static_cast<bf16_t*>(out), ldo);
+    rmsnorm_kernel<bf16_t, true><<<rows, 256, 0, s>>>(x, ridx, ldx, d, g, eps, static_cast<bf16_t*>(out), ldo);
   return hipGetLastError();
 }
 

@@ -248,7 +248,9 @@ size_t carve(const cb_model_cfg& c, int64_t N, int64_t Q, int64_t C, void* base,
   return (off + 255) & ~size_t(255);
 }
 
-PagedRef ref_of(const cb_paged_kv& p) { return PagedRef{p.k, p.v, p.block_table, p.block_size, p.layer_stride}; }
+PagedRef ref_of(const cb_paged_kv& p) {
+  return PagedRef{p.k, p.v, p.block_table, p.block_size, p.layer_stride, block_shift(p.block_size)};
+}
 
 // Chunk descriptors for one launch batch [first, first + count).
 ChunkBatch make_batch(const cb_model_cfg& c, const cb_chunk* ch, int first, int count) {

@@ -23,13 +23,16 @@ namespace cb {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int KVB = 64;            // keys per block
+constexpr int kBtCache = 4096;     // block-table entries a workgroup stages in LDS
 constexpr int QROWS = 64;          // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int DH, int G>
+template <int DH, int G, bool STAGED>
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits, int ksplit) {
   constexpr int QT = QROWS / G;          // query tokens per tile
   constexpr int KP = DH + 8;             // K row pitch (bf16): 16 rows of a fragment read hit distinct banks
@@ -41,6 +44,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits
   constexpr int VTHREADS = (KVB / 4) * CPR;    // threads that stage V (4 keys x 8 dims each)
   __shared__ __attribute__((aligned(16))) bf16_t Ks[KVB * KP];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[DH * VP];
+  __shared__ int32_t btab[kBtCache];     // block-table entries of this workgroup's key range
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -62,6 +66,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits
   const int qhead = kvh * G + qr / QT;
   const bool qvalid = qtok < a.R;
   const int qpos = qvalid ? a.rowpos[qtok] : kv_end - 1;
+  const int qpos_min = a.rowpos[t0];     // rows are sorted: the tile's first row sees the fewest keys
   const int kgrp = lane >> 4;            // 0..3
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[q][32*ks + 8*kgrp .. +7]
@@ -80,14 +85,30 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits
   float l_run = 0.f;   // this lane's partial row sum
   const float sc = a.scale * kLog2e;
 
+  // page-table entries of keys [j_begin, j_end) staged once in LDS (the launcher
+  // sizes the key splits so they fit), so K/V loads never wait on a table load
+  const int bs = a.cache.bs;
+  const int sh = a.cache.bs_shift;
+  const int blk0 = j_begin / bs;
+  const int nblk = (j_end - 1) / bs - blk0 + 1;
+  if constexpr (STAGED) {
+    for (int i = tid; i < nblk; i += 256) btab[i] = a.cache.bt[blk0 + i];
+    __syncthreads();
+  }
+  auto krow = [&](int p) -> int64_t {
+    const int b = sh >= 0 ? (p >> sh) : p / bs;
+    const int e = STAGED ? btab[b - blk0] : a.cache.bt[b];
+    return sh >= 0 ? (static_cast<int64_t>(e) << sh) + (p & (bs - 1)) : static_cast<int64_t>(e) * bs + (p - b * bs);
+  };
   const bf16_t* kbase = static_cast<const bf16_t*>(a.cache.k) + static_cast<int64_t>(a.layer) * a.cache.layer_stride;
   const bf16_t* vbase = static_cast<const bf16_t*>(a.cache.v) + static_cast<int64_t>(a.layer) * a.cache.layer_stride;
   const int width = a.n_kv_heads * DH;
 
   // staging roles: K chunk c = tid + 256*u -> key c / CPR, dims (c % CPR)*8;
-  // V: thread tid < VTHREADS takes keys 4*(tid / CPR) .. +3, dims (tid % CPR)*8 .. +7
-  const int vkey = 4 * (tid / CPR);
-  const int vdim = (tid % CPR) * 8;
+  // V: thread tid < VTHREADS takes keys 4*(tid % 16) .. +3, dims 8*(tid / 16) .. +7,
+  // so the 16 lanes of an LDS write phase cover one V^T row's 64 keys (no bank conflicts)
+  const int vkey = 4 * (tid % (KVB / 4));
+  const int vdim = 8 * (tid / (KVB / 4));
   uint4 kreg[KCH], vreg[4];
   auto gload = [&](int j0) {
 #pragma unroll
@@ -96,8 +117,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits
       const int p = j0 + c / CPR;
       kreg[u] = make_uint4(0, 0, 0, 0);
       if (p < j_end)
-        kreg[u] = *reinterpret_cast<const uint4*>(kbase + paged_row(a.cache.bt, a.cache.bs, p) * width + kvh * DH +
-                                                  (c % CPR) * 8);
+        kreg[u] = *reinterpret_cast<const uint4*>(kbase + krow(p) * width + kvh * DH + (c % CPR) * 8);
     }
     if (tid < VTHREADS) {
 #pragma unroll
@@ -105,8 +125,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits
         const int p = j0 + vkey + i;
         vreg[i] = make_uint4(0, 0, 0, 0);
         if (p < j_end)
-          vreg[i] = *reinterpret_cast<const uint4*>(vbase + paged_row(a.cache.bt, a.cache.bs, p) * width + kvh * DH +
-                                                    vdim);
+          vreg[i] = *reinterpret_cast<const uint4*>(vbase + krow(p) * width + kvh * DH + vdim);
       }
     }
   };
@@ -152,37 +171,52 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits
         s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[t], 0, 0, 0);
       }
     }
-    // lane holds s[t][i] for key j0 + 16t + 4*kgrp + i, query column lane&15
+    // lane holds s[t][i] for key j0 + 16t + 4*kgrp + i, query column lane&15.
+    // Only blocks that reach past the tile's first row or the split end need a mask.
+    if (j0 + KVB - 1 > qpos_min || j0 + KVB > j_end) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = j0 + 16 * t + 4 * kgrp + i;
+          if (key > qpos || key >= j_end) s[t][i] = -INFINITY;
+        }
+    }
     float mblk = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = j0 + 16 * t + 4 * kgrp + i;
-        const float v = (key <= qpos && key < j_end) ? s[t][i] * sc : -INFINITY;
-        s[t][i] = v;
-        mblk = fmaxf(mblk, v);
-      }
+      mblk = fmaxf(fmaxf(mblk, fmaxf(s[t][0], s[t][1])), fmaxf(s[t][2], s[t][3]));
     mblk = fmaxf(mblk, __shfl_xor(mblk, 16, 64));
     mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64));
-    const float m_new = fmaxf(m_run, mblk);
+    const float m_new = fmaxf(m_run, mblk * sc);             // running max in scaled log2 units
     // a row with no visible key yet keeps m = -inf; guard the exponent base
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    // rescale the output only when some row's maximum moved (wave vote)
+    if (__any(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DH / 16; ++t) o[t] *= alpha;
+    }
     m_run = m_new;
     float psum = 0.f;
     bf16x8_t pf[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+      float p4[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s[t][i] - m_use);
-        psum += p;
-        pf[t >> 1][(t & 1) * 4 + i] = static_cast<__bf16>(p);
+        p4[i] = __builtin_amdgcn_exp2f(fmaf(s[t][i], sc, -m_use));
+        psum += p4[i];
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int t = 0; t < DH / 16; ++t) o[t] *= alpha;
+      const bf16x2_t lo = __builtin_convertvector(f32x2_t{p4[0], p4[1]}, bf16x2_t);
+      const bf16x2_t hi = __builtin_convertvector(f32x2_t{p4[2], p4[3]}, bf16x2_t);
+      pf[t >> 1][(t & 1) * 4 + 0] = lo[0];
+      pf[t >> 1][(t & 1) * 4 + 1] = lo[1];
+      pf[t >> 1][(t & 1) * 4 + 2] = hi[0];
+      pf[t >> 1][(t & 1) * 4 + 3] = hi[1];
+    }
+    l_run += psum;
 
     // ---- O^T += V^T P^T: k-slot (kgrp, j) <-> key 32*s2 + (j<4 ? 4kgrp+j : 16+4kgrp+j-4) ----
 #pragma unroll
@@ -334,7 +368,11 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
     if (static_cast<int64_t>(n_splits) * a.R * a.n_q_heads > kAttnPartialRows) n_splits = 1;
   }
   const int ksplit = ((kv_blocks + n_splits - 1) / n_splits) * KVB;
-  attn_bf16_kernel<DH, G><<<dim3(n_tiles * n_splits, a.n_kv_heads), 256, 0, s>>>(a, n_splits, ksplit);
+  // workgroups stage the table entries of their key range in LDS when they fit
+  if (ksplit / a.cache.bs + 2 <= kBtCache)
+    attn_bf16_kernel<DH, G, true><<<dim3(n_tiles * n_splits, a.n_kv_heads), 256, 0, s>>>(a, n_splits, ksplit);
+  else
+    attn_bf16_kernel<DH, G, false><<<dim3(n_tiles * n_splits, a.n_kv_heads), 256, 0, s>>>(a, n_splits, ksplit);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;
   const int pairs = a.R * a.n_q_heads;
@@ -351,8 +389,10 @@ bool attention_supported(cb_dtype dt, int n_q_heads, int n_kv_heads, int head_di
   return (head_dim == 64 || head_dim == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
-hipError_t launch_attention(cb_dtype dt, const AttnArgs& a, hipStream_t s) {
-  if (a.R == 0) return hipSuccess;
+hipError_t launch_attention(cb_dtype dt, const AttnArgs& a_in, hipStream_t s) {
+  if (a_in.R == 0) return hipSuccess;
+  AttnArgs a = a_in;
+  a.cache.bs_shift = block_shift(a.cache.bs);   // derived here so it always matches bs
   if (dt == CB_F32) {
     attn_f32_kernel<<<dim3(a.R, a.n_q_heads), 64, 0, s>>>(a);
     return hipGetLastError();

@@ -41,12 +41,25 @@ struct PagedRef {
   const int32_t* bt;   // block table; NULL = identity (contiguous)
   int32_t bs;          // block size
   int64_t layer_stride;
+  int32_t bs_shift;    // log2(bs) when bs is a power of two, else -1
 };
 
-// Element offset of token `pos` in one layer of a paged pool.
+inline int32_t block_shift(int32_t bs) {
+  int sh = 0;
+  while ((1 << sh) < bs && sh < 30) ++sh;
+  return (1 << sh) == bs ? sh : -1;
+}
+
+// Token row of logical position `pos` in one layer of a paged pool.
 __device__ __forceinline__ int64_t paged_row(const int32_t* bt, int32_t bs, int32_t pos) {
   if (bt == nullptr) return pos;
   return static_cast<int64_t>(bt[pos / bs]) * bs + (pos % bs);
+}
+__device__ __forceinline__ int64_t paged_row(const PagedRef& r, int32_t pos) {
+  if (r.bt == nullptr) return pos;
+  if (r.bs_shift >= 0)
+    return (static_cast<int64_t>(r.bt[pos >> r.bs_shift]) << r.bs_shift) + (pos & (r.bs - 1));
+  return static_cast<int64_t>(r.bt[pos / r.bs]) * r.bs + (pos % r.bs);
 }
 
 // Fragment-major layout of bf16 GEMM A operands (activations).  A matrix of

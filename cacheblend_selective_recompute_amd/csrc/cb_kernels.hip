@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
       const int64_t srow = cd.blk ? static_cast<int64_t>(cd.blk[t / cd.block_size]) * cd.block_size + t % cd.block_size
                                   : static_cast<int64_t>(t);
       so[u] = srow * width + e0[u];
-      dof[u] = paged_row(dst.bt, dst.bs, cd.new_start + t) * width + e0[u];
+      dof[u] = paged_row(dst, cd.new_start + t) * width + e0[u];
       if (ok[u]) {
         kv[u] = *reinterpret_cast<const uint4*>(srck + so[u]);
         if (copy_v) vv[u] = *reinterpret_cast<const uint4*>(srcv + so[u]);
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void deviation_kernel(const float* kf, const f
   const int lane = threadIdx.x & 63;
   if (row >= n) return;
   const int p = pos[row];
-  const int64_t off = static_cast<int64_t>(layer) * cache.layer_stride + paged_row(cache.bt, cache.bs, p) * width;
+  const int64_t off = static_cast<int64_t>(layer) * cache.layer_stride + paged_row(cache, p) * width;
   const T* ck = static_cast<const T*>(cache.k) + off;
   const T* cv = static_cast<const T*>(cache.v) + off;
   const float* fk = kf + static_cast<int64_t>(row) * ldf;
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256) void scatter_kv_kernel(const float* kvf, int64
   const int src = gmap ? gmap[row] : row;
   const float* f = kvf + static_cast<int64_t>(src) * ldf;
   const int64_t off = static_cast<int64_t>(layer) * cache.layer_stride +
-                      paged_row(cache.bt, cache.bs, rowpos[row]) * width;
+                      paged_row(cache, rowpos[row]) * width;
   T* ck = static_cast<T*>(cache.k) + off;
   T* cv = static_cast<T*>(cache.v) + off;
   for (int e = lane * 4; e < width; e += 256) {
@@ -453,9 +453,11 @@ hipError_t launch_rope_delta_table(float2* out, const ChunkBatch& b, int head_di
   return hipGetLastError();
 }
 
-hipError_t launch_rerope(cb_dtype dt, const ChunkBatch& b, const PagedRef& dst, const float2* dtab, int n_layers,
+hipError_t launch_rerope(cb_dtype dt, const ChunkBatch& b, const PagedRef& dst_in, const float2* dtab, int n_layers,
                          int width, int head_dim, int copy_v, hipStream_t s) {
   if (b.total_tiles == 0) return hipSuccess;
+  PagedRef dst = dst_in;
+  dst.bs_shift = block_shift(dst.bs);
   if (dt == CB_BF16)
     rerope_kernel<bf16_t><<<b.total_tiles, kRerope, 0, s>>>(b, dst, dtab, n_layers, width, head_dim, copy_v);
   else
@@ -489,9 +491,11 @@ hipError_t launch_rmsnorm(cb_dtype dt, const float* x, const int32_t* ridx, int6
 }
 
 hipError_t launch_deviation(cb_dtype dt, const float* kf, const float* vf, int64_t ldf, const int32_t* pos, int n,
-                            const PagedRef& cache, int layer, int width, float* dev, float* dev_by_pos,
+                            const PagedRef& cache_in, int layer, int width, float* dev, float* dev_by_pos,
                             hipStream_t s) {
   if (n == 0) return hipSuccess;
+  PagedRef cache = cache_in;
+  cache.bs_shift = block_shift(cache.bs);
   if (dt == CB_BF16)
     deviation_kernel<bf16_t><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
   else
@@ -515,8 +519,10 @@ hipError_t launch_build_rows(const int32_t* sel_slot, const int32_t* sel_pos, in
 }
 
 hipError_t launch_scatter_kv(cb_dtype dt, const float* kvf, int64_t ldf, const int32_t* gmap, const int32_t* rowpos,
-                             int n, const PagedRef& cache, int layer, int width, hipStream_t s) {
+                             int n, const PagedRef& cache_in, int layer, int width, hipStream_t s) {
   if (n == 0) return hipSuccess;
+  PagedRef cache = cache_in;
+  cache.bs_shift = block_shift(cache.bs);
   if (dt == CB_BF16)
     scatter_kv_kernel<bf16_t><<<cdiv(n, 4), 256, 0, s>>>(kvf, ldf, gmap, rowpos, n, cache, layer, width);
   else

@@ -37,7 +37,7 @@ class cb_layer_w(ctypes.Structure):
 
 class cb_model(ctypes.Structure):
     _fields_ = [("cfg", cb_model_cfg), ("embed", c_void_p), ("final_norm", c_void_p),
-                ("lm_head", c_void_p), ("layers", POINTER(cb_layer_w))]
+                ("lm_head", c_void_p), ("layers", POINTER(cb_layer_w)), ("weights_packed", c_int32)]
 
 
 class cb_paged_kv(ctypes.Structure):
@@ -78,6 +78,8 @@ _PROTOS = {
     "cb_blend_prefill": (c_int, [POINTER(cb_model), POINTER(cb_chunk), c_int32, c_void_p, c_int32,
                                  POINTER(cb_blend_params), POINTER(cb_paged_kv), c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_size_t, c_void_p]),
+    "cb_pack_weight": (c_int, [c_int, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
+    "cb_packed_weight_bytes": (c_size_t, [c_int, c_int64, c_int64]),
     "cb_workspace_bytes": (c_size_t, [POINTER(cb_model_cfg), c_int32, c_int32, c_int32]),
     "cb_status_string": (ctypes.c_char_p, [c_int32]),
     "cb_last_error": (ctypes.c_char_p, []),

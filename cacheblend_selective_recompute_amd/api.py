@@ -59,28 +59,55 @@ def make_cfg(shape) -> cb_model_cfg:
 # device-side containers
 # ----------------------------------------------------------------------------
 
+def cb_packed_weight_bytes(dtype: str, rows: int, cols: int) -> int:
+    return int(_abi.load().cb_packed_weight_bytes(CB_BF16 if dtype == "bf16" else CB_F32, rows, cols))
+
+
+def cb_pack_weight(w: torch.Tensor, gate_up: bool = False, stream=None) -> torch.Tensor:
+    """Packed copy of a bf16 row-major [rows][cols] device matrix (cb_pack_weight)."""
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("cb_pack_weight: a contiguous 2-D bf16 tensor is required")
+    rows, cols = w.shape
+    nbytes = cb_packed_weight_bytes("bf16", rows, cols)
+    out = torch.empty(max(nbytes // 2, 1), dtype=torch.bfloat16, device=w.device)
+    _check(_abi.load().cb_pack_weight(CB_BF16, _p(w), rows, cols, 1 if gate_up else 0, _p(out), _stream(stream)),
+           "cb_pack_weight")
+    return out
+
+
 class DeviceModel:
     """Decoder weights on the GPU in the library's layout.
 
     ``layers`` are dicts of torch tensors: ``w_qkv`` [(Hq+2Hkv)dh][d],
     ``w_o`` [d][Hq dh], ``w_gate_up`` [2F][d], ``w_down`` [d][F] in the model
-    dtype and fp32 ``attn_norm`` / ``mlp_norm``.
+    dtype and fp32 ``attn_norm`` / ``mlp_norm``, all row-major.  For bf16
+    models the four matrices of every layer dict are replaced, in place, by
+    their packed copies (cb_pack_weight) as the model is built, so the
+    row-major originals can be freed; ``packed=True`` says they already are.
     """
 
+    MATS = ("w_qkv", "w_o", "w_gate_up", "w_down")
+
     def __init__(self, shape, layers: List[dict], embed: torch.Tensor, lm_head: torch.Tensor,
-                 final_norm: torch.Tensor):
+                 final_norm: torch.Tensor, packed: bool = False):
         self.shape = shape
-        self.layers = layers
         self.embed = embed
         self.lm_head = lm_head
         self.final_norm = final_norm
         self.cfg = make_cfg(shape)
+        self.weights_packed = 1 if shape.dtype == "bf16" else 0
+        if self.weights_packed and not packed:
+            for w in layers:
+                for name in self.MATS:
+                    w[name] = cb_pack_weight(w[name], gate_up=(name == "w_gate_up"))
+        self.layers = layers
         arr = (cb_layer_w * shape.n_layers)()
         for l, w in enumerate(layers):
             arr[l] = cb_layer_w(w["w_qkv"].data_ptr(), w["w_o"].data_ptr(), w["w_gate_up"].data_ptr(),
                                 w["w_down"].data_ptr(), w["attn_norm"].data_ptr(), w["mlp_norm"].data_ptr())
         self._c_layers = arr
-        self.c = cb_model(self.cfg, embed.data_ptr(), final_norm.data_ptr(), lm_head.data_ptr(), arr)
+        self.c = cb_model(self.cfg, embed.data_ptr(), final_norm.data_ptr(), lm_head.data_ptr(), arr,
+                          self.weights_packed)
 
     @classmethod
     def from_numpy(cls, shape, weights: dict, device="cuda") -> "DeviceModel":

@@ -170,6 +170,9 @@ cb_status check_model(const cb_model* m) {
     return fail(CB_ERR_INVALID, "model: NULL embed / final_norm / lm_head / layers");
   if (!aligned16(m->embed) || !aligned16(m->final_norm) || !aligned16(m->lm_head))
     return fail(CB_ERR_INVALID, "model: global tensors must be 16-byte aligned");
+  if (m->weights_packed != (m->cfg.dtype == CB_BF16 ? 1 : 0))
+    return fail(CB_ERR_INVALID, "model: weights_packed must be %d for this dtype (bf16 layer matrices are read packed)",
+                m->cfg.dtype == CB_BF16 ? 1 : 0);
   for (int l = 0; l < m->cfg.n_layers; ++l) {
     const cb_layer_w& w = m->layers[l];
     const void* ps[6] = {w.w_qkv, w.w_o, w.w_gate_up, w.w_down, w.attn_norm, w.mlp_norm};
@@ -476,6 +479,27 @@ const char* cb_status_string(int32_t st) {
     case CB_ERR_DEVICE: return "CB_ERR_DEVICE";
     default: return "CB_UNKNOWN_STATUS";
   }
+}
+
+size_t cb_packed_weight_bytes(cb_dtype dtype, int64_t rows, int64_t cols) {
+  if (dtype != CB_BF16 || rows < 1 || cols < 1) return 0;
+  return static_cast<size_t>(pk_rows(rows)) * static_cast<size_t>(cols) * 2;
+}
+
+cb_status cb_pack_weight(cb_dtype dtype, const void* src, int64_t rows, int64_t cols, int32_t gate_up, void* dst,
+                         cb_stream_t stream) {
+  if (dtype != CB_BF16) return fail(CB_ERR_UNSUPPORTED, "only CB_BF16 matrices are packed");
+  if (!src || !dst) return fail(CB_ERR_INVALID, "NULL src or dst");
+  if (!aligned16(src) || !aligned16(dst)) return fail(CB_ERR_INVALID, "src and dst must be 16-byte aligned");
+  if (rows < 1 || cols < 16 || cols % 16) return fail(CB_ERR_INVALID, "rows >= 1 and cols a positive multiple of 16 required");
+  if (gate_up && rows % 64) return fail(CB_ERR_INVALID, "gate_up: rows = 2 F with F a multiple of 32 required");
+  const size_t nb = cb_packed_weight_bytes(dtype, rows, cols);
+  const char* s0 = static_cast<const char*>(src);
+  const char* d0 = static_cast<const char*>(dst);
+  if (s0 < d0 + nb && d0 < s0 + static_cast<size_t>(rows) * cols * 2) return fail(CB_ERR_INVALID, "src and dst overlap");
+  if (launch_pack_weight(src, rows, cols, gate_up ? 1 : 0, dst, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return fail(CB_ERR_DEVICE, "pack kernel launch failed");
+  return CB_OK;
 }
 
 size_t cb_workspace_bytes(const cb_model_cfg* cfg, int32_t n_ctx, int32_t n_query, int32_t n_chunks) {

@@ -6,17 +6,22 @@
 // selected tokens go through the projections; the recompute cost is
 // proportional to the selected share (section "选 token").
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, 4 waves in a 2x2 grid, block tile
-// (2 WTM) x (2 WTN) x 64.  Weight tiles are staged through LDS (row pitch padded
-// by 16 B so the 32 rows one fragment read touches fall in distinct banks; two
-// buffers so the next tile is in flight while the current one is multiplied);
-// activations arrive fragment-major (see pk_off) from the kernels that produce
-// them, so each A fragment is one contiguous 1 KiB wave load straight into
-// registers.  The tile shape and a split of K are chosen per call from measured
-// per-configuration rates so the grid fills the 256 CUs; split-K partials are
-// reduced in a fixed order by a second kernel that also applies the epilogue.
-// Tiles are ordered M-fastest and mapped so consecutive tiles land on the same
-// XCD, so the M tiles that share one weight tile share that XCD's L2.
+// bf16 path: v_mfma_f32_32x32x16_bf16, 4 waves in a 2x2 grid, block tile BM x 256
+// (BM = 256: one workgroup per CU, wave tile 128 x 128; BM = 128: two per CU,
+// wave tile 64 x 128).  Both operands are fragment-major in memory (see pk_off:
+// activations are written that way by the kernels that produce them, weights are
+// packed once by cb_pack_weight), so one 32-row x 16-column block is 1 KiB laid
+// out in MFMA lane order.  k advances in stages of 32 columns; each stage is
+// copied global -> LDS by buffer loads that write LDS directly (one 1 KiB block
+// per instruction, no VGPR staging, hardware range check returns zero past the
+// last row block), into a ring of NS stages.  The copies for a stage are spread
+// evenly among the MFMAs of the stages before it, so the load path is never
+// flooded; the barrier that makes stage t+1 visible sits in the middle of stage
+// t, so the first fragments of t+1 are read while t's last MFMAs run.  The tile
+// shape and a split of K are chosen per call from a cost model so the grid fills
+// the 256 CUs; split-K partials are reduced in a fixed order by a second kernel
+// that also applies the epilogue.  Tiles are ordered M-fastest and mapped so
+// consecutive tiles land on the same XCD (they share a weight tile in its L2).
 // fp32 path: a plain LDS-tiled FMA kernel (fp32 models are small).
 #include <algorithm>
 
@@ -29,10 +34,27 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int BK = 64;
-constexpr int LDSP = BK + 8;   // LDS row pitch in bf16 elements (144 B)
+constexpr int BK = 32;          // k columns per stage
+constexpr int BN = 256;         // block tile columns (B rows)
 constexpr int kThreads = 256;
 constexpr int kXcd = 8;
+
+// s_waitcnt with only the vector-memory counter constrained (n outstanding allowed)
+#define CB_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+template <int BM>
+struct Tile {
+  static constexpr int FM = BM / 64;              // A fragments per wave (wave tile BM/2 x 128)
+  static constexpr int ABLK = BM / 16;            // A blocks per stage: BM/32 row blocks x 2 k blocks
+  static constexpr int kStageA = ABLK * 1024;
+  static constexpr int kStage = kStageA + 16384;  // + B: 8 row blocks x 2 k blocks
+  static constexpr int NS = BM == 256 ? 4 : 3;    // stages in the LDS ring
+  static constexpr int DA = ABLK / 4;             // A copies per wave per stage
+  static constexpr int DQ = DA + 4;               // all copies per wave per stage
+  static constexpr int H0 = DQ / 2;               // issued during the second half of a stage
+  static constexpr int H1 = DQ - H0;              // ... and during the first half of the next
+  static constexpr int WGS_PER_CU = BM == 256 ? 1 : 2;
+};
 
 // Linear block id -> logical tile id such that the hardware's round-robin
 // dispatch over XCDs gives each XCD a contiguous range of logical tiles.
@@ -44,17 +66,23 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-// Weights (B) are staged through LDS; the gathered activation rows (A) go
-// straight from global memory into MFMA A-fragments: every wave owns WTM rows
-// and WTN columns, waves sharing a row range read the same A lines (L1/L2 hits).
-// WTM x WTN = 128 x 128 keeps 256 fp32 accumulators per lane (AGPRs) and needs
-// 3/8 of the LDS bandwidth of the matrix cores per k step.
-template <int EPI, int WTM, int WTN, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g, int splits, int kps) {
-  constexpr int BM = 2 * WTM, BN = 2 * WTN;
-  constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int NB = BN * (BK / 8) / kThreads;      // 16-byte B chunks per thread per k block
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDSP];
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(p)));
+}
+
+// One 1 KiB fragment block global -> LDS: lane i's 16 bytes land at lds + 16 i.
+__device__ __forceinline__ void copy_block(uint32_t lds, __amdgpu_buffer_rsrc_t rsrc, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+// B is fragment-major with virtual rows: for SWIGLU, 32-row block 2b holds gate
+// features [32b, 32b+32) and block 2b+1 the matching up features.
+template <int EPI, int BM, bool SPLIT>
+__global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kernel(GemmArgs g, int splits, int kps) {
+  using T = Tile<BM>;
+  constexpr int FM = T::FM, NS = T::NS, DA = T::DA, DQ = T::DQ, H0 = T::H0, H1 = T::H1;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * T::kStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -68,168 +96,174 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g, int spl
   const int split = rest % splits;
   const int nt = rest / splits;
   const int m0 = mt * BM;
-  const int n0 = (EPI == EPI_SWIGLU) ? nt * (BN / 2) : nt * BN;
+  const int n0 = nt * BN;                              // first virtual B row of the tile
   const int kbeg = split * kps;
-  const int kend = min(g.K, kbeg + kps);
-  const int nk = (kend - kbeg) / BK;
+  const int nk = (min(g.K, kbeg + kps) - kbeg) / BK;   // >= 1 (host drops empty splits)
 
-  const bf16_t* __restrict__ A = static_cast<const bf16_t*>(g.A);
-  const bf16_t* __restrict__ B = static_cast<const bf16_t*>(g.B);
+  const int kbr = g.K >> 4;                            // 16-column blocks per row block
+  const int b_rows = (EPI == EPI_SWIGLU) ? 2 * g.N : g.N;
+  const int mb0 = m0 >> 5, nb0 = n0 >> 5;
+  const int mb_valid = (g.M + 31) >> 5, nb_valid = (b_rows + 31) >> 5;
+  const int kb0 = kbeg >> 4;
+  const bf16_t* A = static_cast<const bf16_t*>(g.A);
+  const bf16_t* B = static_cast<const bf16_t*>(g.B);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(A + (static_cast<int64_t>(mb0) * kbr + kb0) * 512), static_cast<short>(0),
+      max(0, (mb_valid - mb0) * kbr - kb0) * 1024, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(B + (static_cast<int64_t>(nb0) * kbr + kb0) * 512), static_cast<short>(0),
+      max(0, (nb_valid - nb0) * kbr - kb0) * 1024, 0x00020000);
 
-  const int kb_per_row = g.K >> 4;
-  const int mb_valid = (g.M + 31) >> 5;
-  const bf16_t* arow[FM];
+  // copy u of a stage: u < DA -> A block wid*DA+u, else B block wid*4+u-DA;
+  // block q of a stage = row block q/2, k block q%2
+  int voff[DQ];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int mb = (m0 + wm * WTM + i * 32) >> 5;
-    arow[i] = (mb < mb_valid) ? A + (static_cast<int64_t>(mb) * kb_per_row * 64 + lane) * 8 : nullptr;
+  for (int u = 0; u < DQ; ++u) {
+    const int q = u < DA ? wid * DA + u : wid * 4 + (u - DA);
+    voff[u] = ((q >> 1) * kbr + (q & 1)) * 1024 + lane * 16;
   }
-  // B staging chunks of this thread
-  const bf16_t* brow[NB];
-  int lrow[NB], lcol[NB];
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    const int c = tid + u * kThreads;
-    lrow[u] = c >> 3;
-    lcol[u] = (c & 7) * 8;
-    int bi;
-    bool ok;
-    if (EPI == EPI_SWIGLU) {
-      const int r = lrow[u];
-      const int g32 = r >> 5;
-      const int f = n0 + (g32 >> 1) * 32 + (r & 31);
-      ok = f < g.N;
-      bi = (g32 & 1) ? g.ff + f : f;
-    } else {
-      bi = n0 + lrow[u];
-      ok = bi < g.N;
-    }
-    brow[u] = ok ? B + static_cast<int64_t>(bi) * g.ldb + lcol[u] : nullptr;
-  }
-
-  typedef uint4 AFrag[BK / 16][FM];
-  AFrag acur, anxt;
-  uint4 breg[NB];
-  auto load_a = [&](AFrag& dst, int k0) {
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        dst[ks][i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + static_cast<int64_t>((k0 >> 4) + ks) * 512)
-                             : make_uint4(0, 0, 0, 0);
-  };
-  auto load_b = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u)
-      breg[u] = brow[u] ? *reinterpret_cast<const uint4*>(brow[u] + k0) : make_uint4(0, 0, 0, 0);
-  };
-  auto store_b = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < NB; ++u) *reinterpret_cast<uint4*>(&Bs[buf][lrow[u] * LDSP + lcol[u]]) = breg[u];
+  const uint32_t lds0 = lds_addr(smem);
+  auto copy = [&](int s, int u) {
+    const int q = u < DA ? wid * DA + u : wid * 4 + (u - DA);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (s % NS) * T::kStage + (u < DA ? 0 : T::kStageA) + q * 1024);
+    const int soff = min(s, nk - 1) * (BK * 64);      // stages past the last re-read it into a retired slot
+    if (u < DA) copy_block(dst, ra, voff[u], soff);
+    else copy_block(dst, rb, voff[u], soff);
   };
 
-  f32x16_t acc[FM][FN];
+  f32x16_t acc[FM][4];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  if (nk > 0) {
-    load_b(kbeg);
-    load_a(acur, kbeg);
-    store_b(0);
-  }
+  bf16x8_t af[2][FM], bfr[2][4];
+  auto frag = [&](int s, int ks, int slot) {
+    const uint8_t* st = smem + (s % NS) * T::kStage;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[slot][i] = *reinterpret_cast<const bf16x8_t*>(st + ((wm * FM + i) * 2 + ks) * 1024 + lane * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bfr[slot][j] = *reinterpret_cast<const bf16x8_t*>(st + T::kStageA + ((wn * 4 + j) * 2 + ks) * 1024 + lane * 16);
+  };
+  // the MFMAs of one 16-column step, with copies u0 .. u0+cnt-1 of stage cs spread among them
+  auto mma = [&](int slot, int cs, int u0, int cnt) {
+    constexpr int NM = 4 * FM;
+#pragma unroll
+    for (int x = 0; x < NM; ++x) {
+      acc[x >> 2][x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][x >> 2], bfr[slot][x & 3], acc[x >> 2][x & 3], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < cnt; ++c)
+        if (x == (c * NM) / cnt + NM / cnt - 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          copy(cs, u0 + c);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  };
+
+  // prologue: stages 0 .. NS-2 and the first half of stage NS-1 in flight
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+#pragma unroll
+    for (int u = 0; u < DQ; ++u) copy(s, u);
+#pragma unroll
+  for (int u = 0; u < H0; ++u) copy(NS - 1, u);
+  CB_WAIT_VM(DQ * (NS - 2) + H0);
   __syncthreads();
-  const int fr = lane & 31;
-  const int fk = (lane >> 5) * 8;
+  frag(0, 0, 0);
+  // Stage t lives in slot t % NS.  Copies of stage s go out during the second half
+  // of stage s-NS and the first half of stage s-NS+1, i.e. after every wave has
+  // read stage s-NS (its reads all precede the barrier in the middle of s-NS).
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const int knext = kbeg + (kt + 1) * BK;
-    if (kt + 1 < nk) {
-      load_b(knext);
-      load_a(anxt, knext);
-    }
-    const bf16_t* bs = Bs[buf];
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t bfr[FN];
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&bs[(wn * WTN + j * 32 + fr) * LDSP + ks * 16 + fk]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const bf16x8_t af = __builtin_bit_cast(bf16x8_t, acur[ks][i]);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
-      }
-    }
-    if (kt + 1 < nk) {
-      store_b(buf ^ 1);
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) acur[ks][i] = anxt[ks][i];
-    }
-    __syncthreads();
+    frag(kt, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0, kt + NS - 1, H0, H1);
+    __builtin_amdgcn_sched_barrier(0);
+    CB_WAIT_VM(DQ * (NS - 2));     // this wave's copies of stage kt+1 have landed
+    __syncthreads();               // ... everyone's
+    frag(kt + 1, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1, kt + NS, 0, H0);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  CB_WAIT_VM(0);                   // no copy may still be writing LDS when the workgroup ends
 
   // ---------------- epilogue ----------------
   // acc[i][j][v] holds C[row][col] with
-  //   row = m0 + wm*WTM + i*32 + 8*(v/4) + 4*(lane/32) + v%4,  col = wn*WTN + j*32 + lane%32
+  //   row = m0 + wm*BM/2 + i*32 + 8*(v/4) + 4*(lane/32) + v%4,  col = n0 + wn*128 + j*32 + lane%32.
+  // Each 32-row slab of the wave's tile goes through the (now idle) LDS ring as a
+  // row-major 32 x 128 fp32 block, so every lane then owns 4 adjacent columns:
+  // RoPE pairs and SwiGLU gate/up partners are local, and rows are stored whole.
+  __syncthreads();                                   // every wave is done with the ring
+  constexpr int EP = 136;                            // row pitch (floats): the two half-waves hit different banks
+  float* stg = reinterpret_cast<float*>(smem) + wid * (32 * EP);
   const int half = g.head_dim >> 1;
+  const int row0 = m0 + wm * (BM / 2);
+  const int col0 = n0 + wn * 128;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = m0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const bool rok = row < g.M;
-      if constexpr (SPLIT) {
-        float* prow = g.part + (static_cast<int64_t>(split) * g.M + row) * g.N;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-          if (rok && col < g.N) prow[col] = acc[i][j][v];
+      for (int v = 0; v < 16; ++v)
+        stg[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EP + j * 32 + (lane & 31)] = acc[i][j][v];
+    __builtin_amdgcn_wave_barrier();
+    if constexpr (EPI == EPI_SWIGLU && !SPLIT) {
+      // gate columns [0,32) and [64,96) of the block pair with up columns +32
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int r = p * 4 + (lane >> 4);
+        const int gc = ((lane >> 3) & 1) * 64 + (lane & 7) * 4;
+        const float4 gt = *reinterpret_cast<const float4*>(stg + r * EP + gc);
+        const float4 up = *reinterpret_cast<const float4*>(stg + r * EP + gc + 32);
+        const int row = row0 + i * 32 + r;
+        const int f = ((col0 + (gc & 64)) >> 6) * 32 + (gc & 31);
+        if (row < g.M && f < g.N) {
+          uint2 w;
+          w.x = static_cast<uint32_t>(f2bf(silu(gt.x) * up.x)) | (static_cast<uint32_t>(f2bf(silu(gt.y) * up.y)) << 16);
+          w.y = static_cast<uint32_t>(f2bf(silu(gt.z) * up.z)) | (static_cast<uint32_t>(f2bf(silu(gt.w) * up.w)) << 16);
+          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.C) + pk_off(row, f, static_cast<int>(g.ldc))) = w;
         }
-      } else if constexpr (EPI == EPI_SWIGLU) {
+      }
+    } else {
 #pragma unroll
-        for (int j = 0; j < FN; j += 2) {
-          const int f = n0 + wn * (WTN / 2) + (j / 2) * 32 + (lane & 31);
-          if (rok && f < g.N) {
-            const float h = silu(acc[i][j][v]) * acc[i][j + 1][v];
-            static_cast<bf16_t*>(g.C)[pk_off(row, f, static_cast<int>(g.ldc))] = f2bf(h);
+      for (int p = 0; p < 16; ++p) {
+        const int r = p * 2 + (lane >> 5);
+        const int c = (lane & 31) * 4;
+        float4 x = *reinterpret_cast<const float4*>(stg + r * EP + c);
+        const int row = row0 + i * 32 + r;
+        const int col = col0 + c;
+        if (row >= g.M || col >= g.N) continue;
+        if constexpr (SPLIT) {
+          *reinterpret_cast<float4*>(g.part + (static_cast<int64_t>(split) * g.M + row) * g.N + col) = x;
+        } else if constexpr (EPI == EPI_RESID) {
+          const int rr = g.resid_rows ? g.resid_rows[row] : row;
+          const float4 rv = *reinterpret_cast<const float4*>(g.resid + static_cast<int64_t>(rr) * g.ld_resid + col);
+          *reinterpret_cast<float4*>(static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + col) =
+              make_float4(rv.x + x.x, rv.y + x.y, rv.z + x.z, rv.w + x.w);
+        } else {   // EPI_STORE_ROPE / EPI_F32_ROPE
+          if (col < g.rope_cols) {
+            const int pos = g.row_pos[row];
+            const float4 cs = *reinterpret_cast<const float4*>(g.rope_tab + static_cast<int64_t>(pos) * half + ((col % g.head_dim) >> 1));
+            x = make_float4(x.x * cs.x - x.y * cs.y, x.x * cs.y + x.y * cs.x,
+                            x.z * cs.z - x.w * cs.w, x.z * cs.w + x.w * cs.z);
           }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-          float val = acc[i][j][v];
-          if constexpr (EPI == EPI_STORE_ROPE || EPI == EPI_F32_ROPE) {
-            const float other = __shfl_xor(val, 1, 64);
-            if (rok && col < g.rope_cols) {
-              const int p = g.row_pos[row];
-              const float2 cs = g.rope_tab[static_cast<int64_t>(p) * half + ((col % g.head_dim) >> 1)];
-              val = (col & 1) ? (other * cs.y + val * cs.x) : (val * cs.x - other * cs.y);
-            }
-            if (rok && col < g.N) {
-              if constexpr (EPI == EPI_STORE_ROPE)
-                static_cast<bf16_t*>(g.C)[static_cast<int64_t>(row) * g.ldc + col] = f2bf(val);
-              else
-                static_cast<float*>(g.C)[static_cast<int64_t>(row) * g.ldc + col] = val;
-            }
-          } else {  // EPI_RESID
-            if (rok && col < g.N) {
-              const int rr = g.resid_rows ? g.resid_rows[row] : row;
-              const float r = g.resid[static_cast<int64_t>(rr) * g.ld_resid + col];
-              static_cast<float*>(g.C)[static_cast<int64_t>(row) * g.ldc + col] = r + val;
-            }
+          if constexpr (EPI == EPI_STORE_ROPE) {
+            uint2 w;
+            w.x = static_cast<uint32_t>(f2bf(x.x)) | (static_cast<uint32_t>(f2bf(x.y)) << 16);
+            w.y = static_cast<uint32_t>(f2bf(x.z)) | (static_cast<uint32_t>(f2bf(x.w)) << 16);
+            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.C) + static_cast<int64_t>(row) * g.ldc + col) = w;
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + col) = x;
           }
         }
       }
     }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -379,72 +413,102 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
-template <int EPI, int WTM, int WTN, bool SPLIT>
+template <int EPI, int BM, bool SPLIT>
 hipError_t launch_cfg(const GemmArgs& a, int tiles, int splits, int kps, hipStream_t s) {
-  gemm_bf16_kernel<EPI, WTM, WTN, SPLIT><<<tiles * splits, kThreads, 0, s>>>(a, splits, kps);
+  gemm_bf16_kernel<EPI, BM, SPLIT><<<tiles * splits, kThreads, 0, s>>>(a, splits, kps);
   return hipGetLastError();
 }
 
-inline int tiles_of(const GemmArgs& a, int epi, int bm, int bn) {
+inline int bm_of(int cfg) { return cfg == GEMM_CFG_256 ? 256 : 128; }
+
+inline int tiles_of(const GemmArgs& a, int epi, int bm) {
   const int mt = (a.M + bm - 1) / bm;
-  const int nt = (epi == EPI_SWIGLU) ? (a.N + bn / 2 - 1) / (bn / 2) : (a.N + bn - 1) / bn;
-  return mt * nt;
+  const int rows = (epi == EPI_SWIGLU) ? 2 * a.N : a.N;
+  return mt * ((rows + BN - 1) / BN);
 }
 
-// Split-K cost model for the 128x128 tile, calibrated on the GEMM
-// microbenchmark: a workgroup computes 2*128*128*k FLOP at ~2.2 TFLOP/s when it
-// has a CU to itself and ~1.65 TFLOP/s when two share one (two fit per CU);
-// workgroups run in rounds of 512; the fixed-order reduction moves the fp32
-// partials once (write + read) at ~5 TB/s plus a launch.
-inline double est_time_128(const GemmArgs& a, int epi, int splits) {
-  const int64_t wgs = static_cast<int64_t>(tiles_of(a, epi, 128, 128)) * splits;
-  const double flop_wg = 2.0 * 128 * 128 * (static_cast<double>(a.K) / splits);
-  double tm;
-  if (wgs <= 256) tm = flop_wg / 2.2e12;
-  else tm = static_cast<double>((wgs + 511) / 512) * flop_wg / 1.65e12;
-  if (splits > 1) tm += static_cast<double>(splits) * a.M * a.N * 8.0 / 5e12 + 3e-6;
+// k columns per split (a multiple of BK) and the number of non-empty splits
+inline void split_k(int K, int splits, int* kps, int* eff) {
+  const int nkb = K / BK;
+  const int per = (nkb + splits - 1) / splits;
+  *kps = per * BK;
+  *eff = (nkb + per - 1) / per;
+}
+
+// Cost model, calibrated on the GEMM microbenchmark with random bf16 data at the
+// 8B blend shapes: a 256-row tile computes at ~4.8 TFLOP/s on a CU of its own;
+// 128-row tiles run two per CU at ~2.5 TFLOP/s each and ~3.8 when alone;
+// workgroups run in rounds of (256 CUs x workgroups per CU); the fixed-order
+// reduction moves the fp32 partials once (write + read) at ~8 TB/s plus a launch.
+inline double est_time(const GemmArgs& a, int epi, int cfg, int splits) {
+  const int bm = bm_of(cfg);
+  int kps, eff;
+  split_k(a.K, splits, &kps, &eff);
+  const int64_t wgs = static_cast<int64_t>(tiles_of(a, epi, bm)) * eff;
+  const double flop_wg = 2.0 * bm * BN * kps;
+  double tm = 0.0;
+  if (bm == 256) {
+    tm = static_cast<double>((wgs + 255) / 256) * flop_wg / 4.8e12;
+  } else {
+    const int64_t full = wgs / 512, rem = wgs % 512;
+    tm = static_cast<double>(full) * flop_wg / 2.5e12;
+    if (rem > 0) tm += flop_wg / (rem > 256 ? 2.5e12 : 3.8e12);
+  }
+  if (eff > 1) tm += static_cast<double>(eff) * a.M * a.N * 8.0 / 8e12 + 3e-6;
   return tm;
 }
 
 }  // namespace
 
 void choose_gemm_cfg(const GemmArgs& a, int epi, int* cfg, int* splits) {
-  // the 128x128 tile (two workgroups per CU) is at least as fast per CU as the
-  // larger tiles at every blend shape measured, and quantises better
-  *cfg = GEMM_CFG_128x128;
+  *cfg = GEMM_CFG_256;
   *splits = 1;
-  if (epi == EPI_SWIGLU || a.part == nullptr) return;
-  double best = est_time_128(a, epi, 1);
-  for (int sp = 2; sp <= 8; ++sp) {
-    if (a.K / sp < 512) break;
-    if (static_cast<int64_t>(sp) * a.M * a.N > a.part_floats) break;
-    const double tm = est_time_128(a, epi, sp);
-    if (tm < best * 0.97) {
-      best = tm;
-      *splits = sp;
+  double best = est_time(a, epi, GEMM_CFG_256, 1);
+  for (int c : {GEMM_CFG_256, GEMM_CFG_128}) {
+    for (int sp = 1; sp <= 8; ++sp) {
+      if (sp > 1 && (epi == EPI_SWIGLU || a.part == nullptr)) break;
+      if (a.K / sp < 256) break;
+      int kps, eff;
+      split_k(a.K, sp, &kps, &eff);
+      if (eff > 1 && static_cast<int64_t>(eff) * a.M * a.N > a.part_floats) break;
+      const double tm = est_time(a, epi, c, sp);
+      if (tm < best * 0.97) {
+        best = tm;
+        *cfg = c;
+        *splits = sp;
+      }
     }
   }
 }
 
 namespace {
 
+template <int EPI, int BM>
+hipError_t run_bm(const GemmArgs& a, int splits, hipStream_t s) {
+  int kps, eff;
+  split_k(a.K, splits, &kps, &eff);
+  const int t = tiles_of(a, EPI, BM);
+  if (eff > 1) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      return hipErrorInvalidValue;
+    } else {
+      if (a.part == nullptr || static_cast<int64_t>(eff) * a.M * a.N > a.part_floats) return hipErrorInvalidValue;
+      hipError_t e = launch_cfg<EPI, BM, true>(a, t, eff, kps, s);
+      if (e != hipSuccess) return e;
+      const int64_t n = static_cast<int64_t>(a.M) * (a.N / 4);
+      splitk_reduce_kernel<EPI><<<static_cast<int>((n + 255) / 256), 256, 0, s>>>(a, eff);
+      return hipGetLastError();
+    }
+  }
+  return launch_cfg<EPI, BM, false>(a, t, 1, a.K, s);
+}
+
 template <int EPI>
 hipError_t run_cfg(const GemmArgs& a, int cfg, int splits, hipStream_t s) {
-  if (splits > 1) {
-    if constexpr (EPI == EPI_SWIGLU) return hipErrorInvalidValue;
-    const int t = tiles_of(a, EPI, 128, 128);
-    const int kps = ((a.K / BK + splits - 1) / splits) * BK;
-    hipError_t e = launch_cfg<EPI, 64, 64, true>(a, t, splits, kps, s);
-    if (e != hipSuccess) return e;
-    const int64_t n = static_cast<int64_t>(a.M) * (a.N / 4);
-    splitk_reduce_kernel<EPI><<<static_cast<int>((n + 255) / 256), 256, 0, s>>>(a, splits);
-    return hipGetLastError();
-  }
-  switch (cfg) {
-    case GEMM_CFG_256x256: return launch_cfg<EPI, 128, 128, false>(a, tiles_of(a, EPI, 256, 256), 1, a.K, s);
-    case GEMM_CFG_128x256: return launch_cfg<EPI, 64, 128, false>(a, tiles_of(a, EPI, 128, 256), 1, a.K, s);
-    default: return launch_cfg<EPI, 64, 64, false>(a, tiles_of(a, EPI, 128, 128), 1, a.K, s);
-  }
+  if (a.K % BK != 0 || a.K <= 0) return hipErrorInvalidValue;
+  if (EPI == EPI_SWIGLU && a.N % 32 != 0) return hipErrorInvalidValue;
+  if (splits > 1 && a.N % 4 != 0) return hipErrorInvalidValue;
+  return cfg == GEMM_CFG_256 ? run_bm<EPI, 256>(a, splits, s) : run_bm<EPI, 128>(a, splits, s);
 }
 
 template <int EPI>

@@ -134,6 +134,8 @@ hipError_t launch_scatter_kv(cb_dtype dt, const float* kvf, int64_t ldf, const i
 hipError_t launch_lmhead(cb_dtype dt, const float* a, const void* w, int vocab, int d, float* logits,
                          hipStream_t s);
 hipError_t launch_iota(int32_t* out, int n, int32_t base, hipStream_t s);
+// bf16 row-major [rows][cols] -> the packed layout of cb_pack_weight
+hipError_t launch_pack_weight(const void* src, int64_t rows, int64_t cols, int gate_up, void* dst, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // GEMM: C[M][N] = A[M][K] * B[N][K]^T with a fused epilogue.
@@ -142,10 +144,12 @@ enum GemmEpi : int {
   EPI_STORE_ROPE = 0,   // C (model dtype) = acc, RoPE on columns < rope_cols at row_pos
   EPI_F32_ROPE = 1,     // C (fp32) = acc, RoPE on columns < rope_cols at row_pos
   EPI_RESID = 2,        // C (fp32)[i] = resid[resid_rows ? resid_rows[i] : i] + acc
-  EPI_SWIGLU = 3,       // C (model dtype)[i][f] = SiLU(A.Wg[f]) * (A.Wu[f]); B rows [0,ff) gate, [ff,2ff) up
+  EPI_SWIGLU = 3,       // C (model dtype)[i][f] = SiLU(A.Wg[f]) * (A.Wu[f])
 };
-// bf16: A is fragment-major (K columns), SWIGLU output C is fragment-major (ldc = its K);
-// fp32: everything row-major.
+// bf16: A and B are fragment-major (pk_off, K columns); B is a packed weight
+// (cb_pack_weight), for SWIGLU with gate and up 32-row blocks interleaved; the
+// SWIGLU output C is fragment-major (ldc = its K).  lda / ldb / ff are unused.
+// fp32: everything row-major; SWIGLU B rows [0, ff) gate, [ff, 2 ff) up.
 struct GemmArgs {
   const void* A;
   int64_t lda;
@@ -162,17 +166,16 @@ struct GemmArgs {
   const float* resid;
   const int32_t* resid_rows;
   int64_t ld_resid;
-  int ff;                  // SWIGLU: row offset of the up half in B
+  int ff;                  // fp32 SWIGLU: row offset of the up half in B
   float* part;             // split-K partial sums (fp32), may be NULL (no split)
   int64_t part_floats;     // capacity of part
 };
 constexpr int64_t kGemmPartFloats = int64_t(32) << 20;   // 128 MiB of split-K partials
 hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s);
-// bf16 tile configurations (block tile M x N); launch_gemm picks one per call
-enum GemmCfg : int { GEMM_CFG_256x256 = 0, GEMM_CFG_128x256 = 1, GEMM_CFG_128x128 = 2 };
-// bf16 GEMM with an explicit configuration (splits > 1: 128x128 tiles, split K)
+// bf16 block tiles: 256 x 256 (one workgroup per CU) or 128 x 256 (two per CU)
+enum GemmCfg : int { GEMM_CFG_256 = 0, GEMM_CFG_128 = 1 };
+// bf16 GEMM with an explicit tile and split of K
 hipError_t launch_gemm_cfg(GemmEpi epi, const GemmArgs& a, int cfg, int splits, hipStream_t s);
-// the configuration launch_gemm would use for these arguments
 void choose_gemm_cfg(const GemmArgs& a, int epi, int* cfg, int* splits);
 
 // ---------------------------------------------------------------------------

@@ -540,6 +540,38 @@ hipError_t launch_lmhead(cb_dtype dt, const float* a, const void* w, int vocab, 
   return hipGetLastError();
 }
 
+// Weight packing: one thread per 16-byte lane chunk of the packed matrix.
+// Chunk c of block (rb, cb) is lane l = c % 64: packed row rb*32 + l%32, columns
+// cb*16 + (l/32)*8 .. +7.  With gate_up, packed row block 2b is gate rows
+// 32b.. and block 2b+1 up rows F+32b.. (F = rows / 2).  Rows past `rows` are 0.
+__global__ __launch_bounds__(256) void pack_weight_kernel(const bf16_t* __restrict__ src, int64_t rows, int64_t cols,
+                                                          int gate_up, bf16_t* __restrict__ dst, int64_t n_chunks) {
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (c >= n_chunks) return;
+  const int64_t cblocks = cols >> 4;
+  const int64_t blk = c >> 6;
+  const int l = static_cast<int>(c & 63);
+  const int64_t rb = blk / cblocks, cb = blk % cblocks;
+  const int64_t prow = rb * 32 + (l & 31);
+  int64_t srow = prow;
+  if (gate_up) {
+    const int64_t F = rows >> 1;
+    srow = ((rb & 1) ? F : 0) + (rb >> 1) * 32 + (l & 31);
+  }
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (prow < rows) v = *reinterpret_cast<const uint4*>(src + srow * cols + cb * 16 + (l >> 5) * 8);
+  *reinterpret_cast<uint4*>(dst + c * 8) = v;
+}
+
+hipError_t launch_pack_weight(const void* src, int64_t rows, int64_t cols, int gate_up, void* dst, hipStream_t s) {
+  const int64_t n_chunks = pk_rows(rows) * cols / 8;
+  const int64_t grid = (n_chunks + 255) / 256;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  pack_weight_kernel<<<static_cast<unsigned>(grid), 256, 0, s>>>(static_cast<const bf16_t*>(src), rows, cols, gate_up,
+                                                                  static_cast<bf16_t*>(dst), n_chunks);
+  return hipGetLastError();
+}
+
 hipError_t launch_iota(int32_t* out, int n, int32_t base, hipStream_t s) {
   if (n == 0) return hipSuccess;
   iota_kernel<<<cdiv(n, 256), 256, 0, s>>>(out, n, base);

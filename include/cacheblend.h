@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 1
+#define CB_ABI_VERSION 2
 
 /* A HIP stream (hipStream_t); NULL is the null stream. */
 typedef struct ihipStream_t* cb_stream_t;
@@ -81,8 +81,10 @@ typedef struct {
   cb_dtype dtype;
 } cb_model_cfg;
 
-/* One decoder layer.  Matrices are row-major [out_features][in_features] in
- * the model dtype; norm gains are fp32. */
+/* One decoder layer; norm gains are fp32.  Matrices [out_features][in_features]:
+ * CB_F32 models pass them row-major; CB_BF16 models pass them packed by
+ * cb_pack_weight (the layout the matrix-core GEMMs read), w_gate_up with
+ * gate_up = 1. */
 typedef struct {
   const void* w_qkv;      /* [(Hq + 2 Hkv) * dh][d]: Q heads, then K heads, then V heads */
   const void* w_o;        /* [d][Hq * dh]                                             */
@@ -98,6 +100,8 @@ typedef struct {
   const float* final_norm;  /* [d]                                      */
   const void* lm_head;      /* [vocab][d] model dtype (untied)          */
   const cb_layer_w* layers; /* HOST array [n_layers] of device pointers */
+  int32_t weights_packed;   /* 1: layer matrices packed by cb_pack_weight
+                               (required for CB_BF16); 0: row-major (CB_F32) */
 } cb_model;
 
 /* Paged KV cache: K and V pools laid out [layer][physical block][block_size]
@@ -261,6 +265,33 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
                            const cb_blend_params* params, const cb_paged_kv* blended,
                            float* logits, int32_t* hkvd_out, float* dev_out, void* ws,
                            size_t ws_bytes, cb_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * cb_pack_weight -- one layer matrix of a CB_BF16 model into the layout its
+ * GEMM reads.  The projections are the paper's per-layer Q/K/V, O and MLP
+ * matrices ("CacheBlend 完全拆解", Fig. 5); packing changes only where each
+ * element is stored.
+ *   src: bf16 row-major [rows][cols] (rows = out_features, cols = in_features).
+ *   dst: cb_packed_weight_bytes(dtype, rows, cols) bytes.  The rows are
+ *     grouped in blocks of 32 (the last block zero-padded) and the columns in
+ *     blocks of 16; block (rb, cb) is 1 KiB at element offset
+ *     (rb * cols / 16 + cb) * 512, and within it element (r, c) sits at
+ *     ((c / 8 % 2) * 32 + r % 32) * 8 + c % 8, i.e. the order in which the
+ *     64 lanes of a 32x32x16 MFMA read their 16-byte operand fragments.
+ *   gate_up = 1 (w_gate_up, rows = 2 F, F a multiple of 32): packed row block
+ *     2b holds gate rows 32b .. 32b+31 and block 2b+1 the up rows F+32b ..,
+ *     so every gate feature and its up partner land in one GEMM tile.
+ * Ownership: src and dst are the caller's and must not overlap.
+ * Errors: CB_ERR_INVALID for null pointers, rows < 1, cols < 16,
+ * cols % 16 != 0, gate_up with rows % 64 != 0; CB_ERR_UNSUPPORTED for a dtype
+ * other than CB_BF16 (CB_F32 matrices are used row-major as they are).
+ * ------------------------------------------------------------------------- */
+cb_status cb_pack_weight(cb_dtype dtype, const void* src, int64_t rows, int64_t cols, int32_t gate_up,
+                         void* dst, cb_stream_t stream);
+
+/* Bytes of a packed [rows][cols] matrix: ceil(rows / 32) * 32 * cols * 2 for
+ * CB_BF16; 0 for other dtypes or non-positive sizes. */
+size_t cb_packed_weight_bytes(cb_dtype dtype, int64_t rows, int64_t cols);
 
 /* Workspace bytes sufficient for every call above on a context of n_ctx
  * tokens, n_query suffix tokens and n_chunks chunks.  Returns 0 for an invalid cfg. */

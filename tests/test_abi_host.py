@@ -31,7 +31,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = _abi.header_functions()
     assert {"cb_rerope_k", "cb_kv_deviation", "cb_select_hkvd", "cb_blend_layer", "cb_blend_prefill",
-            "cb_workspace_bytes", "cb_status_string", "cb_last_error", "cb_abi_version"} <= set(names)
+            "cb_workspace_bytes", "cb_status_string", "cb_last_error", "cb_abi_version",
+            "cb_pack_weight", "cb_packed_weight_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True, text=True).stdout
@@ -50,7 +51,7 @@ def test_struct_layout_matches_header():
 int main(void) {
   P(cb_model_cfg) O(cb_model_cfg, rope_theta) O(cb_model_cfg, rms_eps) O(cb_model_cfg, dtype)
   P(cb_layer_w) O(cb_layer_w, mlp_norm)
-  P(cb_model) O(cb_model, embed) O(cb_model, layers)
+  P(cb_model) O(cb_model, embed) O(cb_model, layers) O(cb_model, weights_packed)
   P(cb_paged_kv) O(cb_paged_kv, block_size) O(cb_paged_kv, layer_stride)
   P(cb_chunk) O(cb_chunk, len) O(cb_chunk, new_start) O(cb_chunk, layer_stride)
   P(cb_blend_params) O(cb_blend_params, flags) O(cb_blend_params, trace)
@@ -75,7 +76,7 @@ int main(void) {
 
 
 def test_status_strings_and_version(lib):
-    assert lib.cb_abi_version() == 1
+    assert lib.cb_abi_version() == 2
     for code, name in [(0, "CB_OK"), (-1, "CB_ERR_INVALID"), (-2, "CB_ERR_UNSUPPORTED"),
                        (-3, "CB_ERR_WORKSPACE"), (-4, "CB_ERR_DEVICE")]:
         assert lib.cb_status_string(code).decode() == name
@@ -101,10 +102,12 @@ def test_workspace_bytes(lib):
     assert lib.cb_workspace_bytes(ctypes.byref(c), -1, 64, 4) == 0
 
 
-def _model(cfg, L=None):
+def _model(cfg, L=None, packed=None):
     L = L or cfg.n_layers
     layers = (_abi.cb_layer_w * L)(*[_abi.cb_layer_w(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) for _ in range(L)])
-    m = _abi.cb_model(cfg, FAKE, FAKE, FAKE, layers)
+    if packed is None:
+        packed = 1 if cfg.dtype == _abi.CB_BF16 else 0
+    m = _abi.cb_model(cfg, FAKE, FAKE, FAKE, layers, packed)
     m._keep = layers
     return m
 
@@ -130,9 +133,9 @@ def _params(ks, check):
 
 
 def _prefill(lib, cfg=None, specs=((64, 0, 0), (64, 5, 64)), nq=8, ks=None, check=None, paged=None,
-             ws_bytes=None):
+             ws_bytes=None, packed=None):
     cfg = cfg or cfg8b(n_layers=3)
-    m = _model(cfg)
+    m = _model(cfg, packed=packed)
     ch = _chunks(specs)
     N = sum(s[0] for s in specs)
     ks = ks or [N, 19, 19]
@@ -231,3 +234,34 @@ def test_rerope_validation(lib):
     ch = _chunks([(64, 0, 0)])
     st = lib.cb_rerope_k(ctypes.byref(c), ch, 1, ctypes.byref(kv), 4, FAKE, 1 << 20, None)
     assert st == _abi.CB_ERR_INVALID and "flags" in lib.cb_last_error().decode()
+
+
+def test_prefill_requires_packed_bf16_weights(lib):
+    st, msg = _prefill(lib, packed=0)
+    assert st == _abi.CB_ERR_INVALID and "weights_packed" in msg
+    c = cfg8b(n_layers=3)
+    c.dtype = _abi.CB_F32
+    st, msg = _prefill(lib, cfg=c, packed=1)
+    assert st == _abi.CB_ERR_INVALID and "weights_packed" in msg
+
+
+def test_packed_weight_bytes(lib):
+    # rows are padded to whole 32-row blocks; two bytes per element
+    assert lib.cb_packed_weight_bytes(_abi.CB_BF16, 6144, 4096) == 6144 * 4096 * 2
+    assert lib.cb_packed_weight_bytes(_abi.CB_BF16, 70, 48) == 96 * 48 * 2
+    assert lib.cb_packed_weight_bytes(_abi.CB_BF16, 1, 16) == 32 * 16 * 2
+    assert lib.cb_packed_weight_bytes(_abi.CB_F32, 64, 64) == 0
+    assert lib.cb_packed_weight_bytes(_abi.CB_BF16, 0, 64) == 0
+
+
+def test_pack_weight_validation(lib):
+    P = lib.cb_pack_weight
+    big = 1 << 30
+    assert P(_abi.CB_F32, FAKE, 64, 64, 0, FAKE + big, None) == _abi.CB_ERR_UNSUPPORTED
+    assert P(_abi.CB_BF16, None, 64, 64, 0, FAKE, None) == _abi.CB_ERR_INVALID
+    assert P(_abi.CB_BF16, FAKE, 64, 40, 0, FAKE + big, None) == _abi.CB_ERR_INVALID      # cols % 16
+    assert P(_abi.CB_BF16, FAKE, 0, 64, 0, FAKE + big, None) == _abi.CB_ERR_INVALID       # rows < 1
+    assert P(_abi.CB_BF16, FAKE, 96, 64, 1, FAKE + big, None) == _abi.CB_ERR_INVALID      # gate_up: 2F, F % 32
+    st = P(_abi.CB_BF16, FAKE, 64, 64, 0, FAKE + 1024, None)                              # overlap
+    assert st == _abi.CB_ERR_INVALID and "overlap" in lib.cb_last_error().decode()
+    assert P(_abi.CB_BF16, FAKE + 8, 64, 64, 0, FAKE + big, None) == _abi.CB_ERR_INVALID  # alignment

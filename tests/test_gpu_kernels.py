@@ -153,3 +153,38 @@ def test_select_all_equal_takes_smallest_positions():
     api.cb_select_hkvd(torch.from_numpy(dev).cuda(), ints(pos), k, sel)
     torch.cuda.synchronize()
     assert sel.cpu().numpy().tolist() == (np.arange(k) * 2).tolist()
+
+
+def _pack_reference(bits: np.ndarray, gate_up: bool) -> np.ndarray:
+    """The packed layout as the header defines it, by index arithmetic on the host:
+    32-row x 16-column blocks, element (r, c) of a block at ((c/8 % 2)*32 + r%32)*8 + c%8,
+    gate/up 32-row blocks interleaved for gate_up, rows past the matrix zero."""
+    R, C = bits.shape
+    Rp = (R + 31) // 32 * 32
+    prow = np.arange(Rp)
+    if gate_up:
+        F = R // 2
+        blk = prow // 32
+        src = np.where(blk % 2 == 1, F, 0) + (blk // 2) * 32 + prow % 32
+    else:
+        src = prow
+    out = np.zeros(Rp * C, dtype=np.uint16)
+    p, c = np.meshgrid(prow, np.arange(C), indexing="ij")
+    off = ((p // 32) * (C // 16) + c // 16) * 512 + (((c // 8) % 2) * 32 + p % 32) * 8 + c % 8
+    valid = src[p] < R
+    out[off[valid]] = bits[src[p][valid], c[valid]]
+    return out
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,cols,gate_up", [(70, 48, False), (32, 16, False), (256, 4096, False),
+                                               (128, 80, True), (2 * 3584, 1024, True)])
+def test_pack_weight_bit_exact(rows, cols, gate_up):
+    say(f"cb_pack_weight rows {rows} cols {cols} gate_up {gate_up}")
+    rng = np.random.default_rng(rows * 31 + cols)
+    bits = rng.integers(0, 1 << 16, size=(rows, cols), dtype=np.uint16)
+    w = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    got = api.cb_pack_weight(w, gate_up=gate_up)
+    torch.cuda.synchronize()
+    got_bits = got.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got_bits, _pack_reference(bits, gate_up))

@@ -29,11 +29,11 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int KVB = 64;            // keys per block
 constexpr int kBtCache = 4096;     // block-table entries a workgroup stages in LDS
-constexpr int QROWS = 64;          // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int DH, int G, bool STAGED>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits, int ksplit) {
+template <int DH, int G, bool STAGED, int NG>
+__global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_bf16_kernel(AttnArgs a, int n_splits, int ksplit) {
+  constexpr int QROWS = 64 * NG;         // query rows per workgroup (NG groups of 16 per wave)
   constexpr int QT = QROWS / G;          // query tokens per tile
   constexpr int KP = DH + 8;             // K row pitch (bf16): 16 rows of a fragment read hit distinct banks
   constexpr int VP = KVB + 4;            // V^T row pitch (bf16)
@@ -60,29 +60,39 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits
   const int j_end = min(kv_end, j_begin + ksplit);
   if (j_begin >= j_end) return;                                              // uniform per workgroup
 
-  // this lane's query row: wave w owns tile rows 16w..16w+15; row r -> token r % QT, head r / QT
-  const int qr = wid * 16 + (lane & 15);
-  const int qtok = t0 + (qr % QT);
-  const int qhead = kvh * G + qr / QT;
-  const bool qvalid = qtok < a.R;
-  const int qpos = qvalid ? a.rowpos[qtok] : kv_end - 1;
-  const int qpos_min = a.rowpos[t0];     // rows are sorted: the tile's first row sees the fewest keys
+  // this lane's query rows: group g of wave w owns tile rows 16 (w NG + g) .. +15;
+  // row r -> token r % QT, head r / QT
   const int kgrp = lane >> 4;            // 0..3
+  int qtok[NG], qhead[NG], qpos[NG];
+  bool qvalid[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int qr = (wid * NG + g) * 16 + (lane & 15);
+    qtok[g] = t0 + (qr % QT);
+    qhead[g] = kvh * G + qr / QT;
+    qvalid[g] = qtok[g] < a.R;
+    qpos[g] = qvalid[g] ? a.rowpos[qtok[g]] : kv_end - 1;
+  }
+  const int qpos_min = a.rowpos[t0];     // rows are sorted: the tile's first row sees the fewest keys
 
   // Q fragments (B operand of S^T = K Q^T): lane holds Q[q][32*ks + 8*kgrp .. +7]
-  bf16x8_t qf[DH / 32];
-  {
-    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + static_cast<int64_t>(qvalid ? qtok : t_last) * a.ldq +
-                       qhead * DH + 8 * kgrp;
+  bf16x8_t qf[NG][DH / 32];
 #pragma unroll
-    for (int ks = 0; ks < DH / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * ks);
+  for (int g = 0; g < NG; ++g) {
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + static_cast<int64_t>(qvalid[g] ? qtok[g] : t_last) * a.ldq +
+                       qhead[g] * DH + 8 * kgrp;
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) qf[g][ks] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * ks);
   }
-
-  f32x4_t o[DH / 16];
+  f32x4_t o[NG][DH / 16];
+  float m_run[NG], l_run[NG];
 #pragma unroll
-  for (int t = 0; t < DH / 16; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_run = 0.f;   // this lane's partial row sum
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t) o[g][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;      // this lane's partial row sum
+  }
   const float sc = a.scale * kLog2e;
 
   // page-table entries of keys [j_begin, j_end) staged once in LDS (the launcher
@@ -160,63 +170,69 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits
     __syncthreads();
     if (j0 + KVB < j_end) gload(j0 + KVB);     // next block in flight during the math
 
-    // ---- S^T tiles: 4 x (16 keys x 16 queries) ----
-    f32x4_t s[4];
+    // ---- S^T tiles: 4 x (16 keys x 16 queries) per group; each K fragment serves every group ----
+    f32x4_t s[NG][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < NG; ++g) s[g][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DH / 32; ++ks) {
         const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(&Ks[(16 * t + (lane & 15)) * KP + 32 * ks + 8 * kgrp]);
-        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[t], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) s[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[g][ks], s[g][t], 0, 0, 0);
       }
     }
-    // lane holds s[t][i] for key j0 + 16t + 4*kgrp + i, query column lane&15.
+    // lane holds s[g][t][i] for key j0 + 16t + 4*kgrp + i, query column lane&15 of group g.
     // Only blocks that reach past the tile's first row or the split end need a mask.
-    if (j0 + KVB - 1 > qpos_min || j0 + KVB > j_end) {
+    const bool edge = j0 + KVB - 1 > qpos_min || j0 + KVB > j_end;
+    bf16x8_t pf[NG][2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (edge) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = j0 + 16 * t + 4 * kgrp + i;
+            if (key > qpos[g] || key >= j_end) s[g][t][i] = -INFINITY;
+          }
+      }
+      float mblk = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
+        mblk = fmaxf(fmaxf(mblk, fmaxf(s[g][t][0], s[g][t][1])), fmaxf(s[g][t][2], s[g][t][3]));
+      mblk = fmaxf(mblk, __shfl_xor(mblk, 16, 64));
+      mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64));
+      const float m_new = fmaxf(m_run[g], mblk * sc);          // running max in scaled log2 units
+      // a row with no visible key yet keeps m = -inf; guard the exponent base
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      // rescale the output only when some row's maximum moved (wave vote)
+      if (__any(m_new != m_run[g])) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_use);
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int t = 0; t < DH / 16; ++t) o[g][t] *= alpha;
+      }
+      m_run[g] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float p4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = j0 + 16 * t + 4 * kgrp + i;
-          if (key > qpos || key >= j_end) s[t][i] = -INFINITY;
+          p4[i] = __builtin_amdgcn_exp2f(fmaf(s[g][t][i], sc, -m_use));
+          psum += p4[i];
         }
-    }
-    float mblk = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      mblk = fmaxf(fmaxf(mblk, fmaxf(s[t][0], s[t][1])), fmaxf(s[t][2], s[t][3]));
-    mblk = fmaxf(mblk, __shfl_xor(mblk, 16, 64));
-    mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64));
-    const float m_new = fmaxf(m_run, mblk * sc);             // running max in scaled log2 units
-    // a row with no visible key yet keeps m = -inf; guard the exponent base
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    // rescale the output only when some row's maximum moved (wave vote)
-    if (__any(m_new != m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < DH / 16; ++t) o[t] *= alpha;
-    }
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x8_t pf[2];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float p4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p4[i] = __builtin_amdgcn_exp2f(fmaf(s[t][i], sc, -m_use));
-        psum += p4[i];
+        const bf16x2_t lo = __builtin_convertvector(f32x2_t{p4[0], p4[1]}, bf16x2_t);
+        const bf16x2_t hi = __builtin_convertvector(f32x2_t{p4[2], p4[3]}, bf16x2_t);
+        pf[g][t >> 1][(t & 1) * 4 + 0] = lo[0];
+        pf[g][t >> 1][(t & 1) * 4 + 1] = lo[1];
+        pf[g][t >> 1][(t & 1) * 4 + 2] = hi[0];
+        pf[g][t >> 1][(t & 1) * 4 + 3] = hi[1];
       }
-      const bf16x2_t lo = __builtin_convertvector(f32x2_t{p4[0], p4[1]}, bf16x2_t);
-      const bf16x2_t hi = __builtin_convertvector(f32x2_t{p4[2], p4[3]}, bf16x2_t);
-      pf[t >> 1][(t & 1) * 4 + 0] = lo[0];
-      pf[t >> 1][(t & 1) * 4 + 1] = lo[1];
-      pf[t >> 1][(t & 1) * 4 + 2] = hi[0];
-      pf[t >> 1][(t & 1) * 4 + 3] = hi[1];
+      l_run[g] += psum;
     }
-    l_run += psum;
 
     // ---- O^T += V^T P^T: k-slot (kgrp, j) <-> key 32*s2 + (j<4 ? 4kgrp+j : 16+4kgrp+j-4) ----
 #pragma unroll
@@ -228,36 +244,277 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a, int n_splits
         const uint2 hi = *reinterpret_cast<const uint2*>(vr + 16);
         const uint4 packed = make_uint4(lo.x, lo.y, hi.x, hi.y);
         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, packed);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[s2], o[dt], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) o[g][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[g][s2], o[g][dt], 0, 0, 0);
       }
     }
     __syncthreads();
   }
 
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (!qvalid) return;
-  if (n_splits == 1) {
-    const float inv = 1.0f / l_tot;
-    bf16_t* ob = static_cast<bf16_t*>(a.o);
-    const int KO = a.n_q_heads * DH;
-    // o[dt][i] = O[q][16*dt + 4*kgrp + i]; written fragment-major (4 consecutive columns = 8 bytes)
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float l_tot = l_run[g];
+    l_tot += __shfl_xor(l_tot, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (!qvalid[g]) continue;
+    if (n_splits == 1) {
+      const float inv = 1.0f / l_tot;
+      bf16_t* ob = static_cast<bf16_t*>(a.o);
+      const int KO = a.n_q_heads * DH;
+      // o[g][dt][i] = O[q][16*dt + 4*kgrp + i]; written fragment-major (4 consecutive columns = 8 bytes)
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) {
+        uint2 w;
+        w.x = static_cast<uint32_t>(f2bf(o[g][dt][0] * inv)) | (static_cast<uint32_t>(f2bf(o[g][dt][1] * inv)) << 16);
+        w.y = static_cast<uint32_t>(f2bf(o[g][dt][2] * inv)) | (static_cast<uint32_t>(f2bf(o[g][dt][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(ob + pk_off(qtok[g], qhead[g] * DH + 16 * dt + 4 * kgrp, KO)) = w;
+      }
+    } else {
+      // unnormalised partial for (split, row, head); m in log2 units
+      const int64_t pr = (static_cast<int64_t>(split) * a.R + qtok[g]) * a.n_q_heads + qhead[g];
+      float* op = a.part_o + pr * DH;
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt)
+        *reinterpret_cast<float4*>(op + 16 * dt + 4 * kgrp) = make_float4(o[g][dt][0], o[g][dt][1], o[g][dt][2], o[g][dt][3]);
+      if (kgrp == 0) a.part_ml[pr] = make_float2(m_run[g], l_tot);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// head_dim 128: K and V blocks are copied global -> LDS by buffer loads that
+// write LDS directly (no VGPR staging), 16-byte chunks of each 256-byte key
+// row placed at swizzled slots so both fragment reads are free of bank
+// conflicts; V^T fragments come straight out of the key-major V block with the
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Two stages: block j+1 is
+// in flight while block j is multiplied.
+// ---------------------------------------------------------------------------
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void attn_copy(uint32_t lds, __amdgpu_buffer_rsrc_t rsrc, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rsrc) : "memory");
+}
+
+template <int G, bool STAGED, int NG>
+__global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_dma_kernel(AttnArgs a, int n_splits, int ksplit) {
+  constexpr int DH = 128;
+  constexpr int QROWS = 64 * NG;
+  constexpr int QT = QROWS / G;
+  constexpr int kBlk = KVB * DH * 2;     // bytes of one K (or V) block: 64 rows x 256 B
+  constexpr int kBt = 1024;              // staged block-table entries
+  __shared__ __attribute__((aligned(1024))) uint8_t kv[2][2 * kBlk];   // [stage][K | V]
+  __shared__ int32_t btab[kBt];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int n_tiles = (a.R + QT - 1) / QT;
+  const int split = blockIdx.x % n_splits;
+  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x / n_splits);   // longest first
+  const int kvh = blockIdx.y;
+  const int t0 = tile * QT;
+  const int t_last = min(t0 + QT, a.R) - 1;
+  const int kv_end = a.rowpos[t_last] + 1;
+  const int j_begin = split * ksplit;
+  const int j_end = min(kv_end, j_begin + ksplit);
+  if (j_begin >= j_end) return;
+
+  const int kgrp = lane >> 4;
+  int qtok[NG], qhead[NG], qpos[NG];
+  bool qvalid[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int qr = (wid * NG + g) * 16 + (lane & 15);
+    qtok[g] = t0 + (qr % QT);
+    qhead[g] = kvh * G + qr / QT;
+    qvalid[g] = qtok[g] < a.R;
+    qpos[g] = qvalid[g] ? a.rowpos[qtok[g]] : kv_end - 1;
+  }
+  const int qpos_min = a.rowpos[t0];
+  bf16x8_t qf[NG][DH / 32];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + static_cast<int64_t>(qvalid[g] ? qtok[g] : t_last) * a.ldq +
+                       qhead[g] * DH + 8 * kgrp;
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) qf[g][ks] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * ks);
+  }
+  f32x4_t o[NG][DH / 16];
+  float m_run[NG], l_run[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t) o[g][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+  }
+  const float sc = a.scale * kLog2e;
+
+  const int bs = a.cache.bs;
+  const int sh = a.cache.bs_shift;
+  const int blk0 = j_begin / bs;
+  if constexpr (STAGED) {
+    const int nblk = (j_end - 1) / bs - blk0 + 1;
+    for (int i = tid; i < nblk; i += 256) btab[i] = a.cache.bt[blk0 + i];
+    __syncthreads();
+  }
+  auto krow = [&](int p) -> int {
+    const int b = sh >= 0 ? (p >> sh) : p / bs;
+    const int e = STAGED ? btab[b - blk0] : a.cache.bt[b];
+    return sh >= 0 ? (e << sh) + (p & (bs - 1)) : e * bs + (p - b * bs);
+  };
+  const int width = a.n_kv_heads * DH;
+  const bf16_t* kbase = static_cast<const bf16_t*>(a.cache.k) + static_cast<int64_t>(a.layer) * a.cache.layer_stride;
+  const bf16_t* vbase = static_cast<const bf16_t*>(a.cache.v) + static_cast<int64_t>(a.layer) * a.cache.layer_stride;
+  // the launcher guarantees the layer's pool spans < 2^31 bytes
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kbase), static_cast<short>(0),
+                                                                      0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vbase), static_cast<short>(0),
+                                                                      0x7fffffff, 0x00020000);
+  // copy u (0..3) of this wave: keys 4 (4 wid + u) + lane / 16 of the block, LDS slot lane % 16
+  // of the key row; K slot p holds chunk p ^ (key % 16), V slot p chunk p ^ 2 (key % 8)
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(&kv[0][0])));
+  auto issue = [&](int jb, int stage) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kr = 4 * (4 * wid + u) + (lane >> 4);
+      const int key = jb + kr;
+      const int slot = lane & 15;
+      int ko = static_cast<int>(0x80000000u), vo = static_cast<int>(0x80000000u);   // past the range: zeros
+      if (key < j_end) {
+        const int rowb = krow(key) * width * 2 + kvh * DH * 2;
+        ko = rowb + ((slot ^ (key & 15)) << 4);
+        vo = rowb + ((slot ^ ((key & 7) << 1)) << 4);
+      }
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + stage * (2 * kBlk) + (4 * wid + u) * 1024);
+      attn_copy(dst, rk, ko);
+      attn_copy(dst + kBlk, rv, vo);
+    }
+  };
+
+  issue(j_begin, 0);
+  int stage = 0;
+  for (int j0 = j_begin; j0 < j_end; j0 += KVB) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of block j0 have landed
+    __syncthreads();                      // ... everyone's; block j0 - 64 is no longer read
+    if (j0 + KVB < j_end) issue(j0 + KVB, stage ^ 1);
+    const uint8_t* Kb = kv[stage];
+    const uint8_t* Vb = kv[stage] + kBlk;
+
+    f32x4_t s[NG][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) s[g][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int key = 16 * t + (lane & 15);
+#pragma unroll
+      for (int ks = 0; ks < DH / 32; ++ks) {
+        const int c = 4 * ks + kgrp;
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Kb + key * 256 + ((c ^ (key & 15)) << 4));
+#pragma unroll
+        for (int g = 0; g < NG; ++g) s[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[g][ks], s[g][t], 0, 0, 0);
+      }
+    }
+    const bool edge = j0 + KVB - 1 > qpos_min || j0 + KVB > j_end;
+    bf16x8_t pf[NG][2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (edge) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = j0 + 16 * t + 4 * kgrp + i;
+            if (key > qpos[g] || key >= j_end) s[g][t][i] = -INFINITY;
+          }
+      }
+      float mblk = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        mblk = fmaxf(fmaxf(mblk, fmaxf(s[g][t][0], s[g][t][1])), fmaxf(s[g][t][2], s[g][t][3]));
+      mblk = fmaxf(mblk, __shfl_xor(mblk, 16, 64));
+      mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64));
+      const float m_new = fmaxf(m_run[g], mblk * sc);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      if (__any(m_new != m_run[g])) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_use);
+        l_run[g] *= alpha;
+#pragma unroll
+        for (int t = 0; t < DH / 16; ++t) o[g][t] *= alpha;
+      }
+      m_run[g] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float p4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p4[i] = __builtin_amdgcn_exp2f(fmaf(s[g][t][i], sc, -m_use));
+          psum += p4[i];
+        }
+        const bf16x2_t lo = __builtin_convertvector(f32x2_t{p4[0], p4[1]}, bf16x2_t);
+        const bf16x2_t hi = __builtin_convertvector(f32x2_t{p4[2], p4[3]}, bf16x2_t);
+        pf[g][t >> 1][(t & 1) * 4 + 0] = lo[0];
+        pf[g][t >> 1][(t & 1) * 4 + 1] = lo[1];
+        pf[g][t >> 1][(t & 1) * 4 + 2] = hi[0];
+        pf[g][t >> 1][(t & 1) * 4 + 3] = hi[1];
+      }
+      l_run[g] += psum;
+    }
+
+    // O^T += V^T P^T.  k-slot 8 kgrp + j of P^T holds key 32 s2 + 16 (j / 4) + 4 kgrp + j % 4; the
+    // transposing read gives lane (group kg, index i) element e from source lane 4 e + i / 4 of
+    // its 16-lane group, column i % 4, so source lane s points at key 32 s2 + 16 h + 4 kg + s / 4,
+    // dims 16 dt + 4 (s % 4) .. +3
+    const int sl = lane & 15;
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) {
-      uint2 w;
-      w.x = static_cast<uint32_t>(f2bf(o[dt][0] * inv)) | (static_cast<uint32_t>(f2bf(o[dt][1] * inv)) << 16);
-      w.y = static_cast<uint32_t>(f2bf(o[dt][2] * inv)) | (static_cast<uint32_t>(f2bf(o[dt][3] * inv)) << 16);
-      *reinterpret_cast<uint2*>(ob + pk_off(qtok, qhead * DH + 16 * dt + 4 * kgrp, KO)) = w;
-    }
-  } else {
-    // unnormalised partial for (split, row, head); m in log2 units
-    const int64_t pr = (static_cast<int64_t>(split) * a.R + qtok) * a.n_q_heads + qhead;
-    float* op = a.part_o + pr * DH;
 #pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt)
-      *reinterpret_cast<float4*>(op + 16 * dt + 4 * kgrp) = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
-    if (kgrp == 0) a.part_ml[pr] = make_float2(m_run, l_tot);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        s16x4_t half[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int key = 32 * s2 + 16 * h + 4 * kgrp + (sl >> 2);
+          const int d = 16 * dt + 4 * (sl & 3);
+          const int c = d >> 3;
+          const uint8_t* src = Vb + key * 256 + ((c ^ ((key & 7) << 1)) << 4) + ((d & 7) << 1);
+          half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(const __attribute__((address_space(3))) void*)(src));
+        }
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int g = 0; g < NG; ++g) o[g][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[g][s2], o[g][dt], 0, 0, 0);
+      }
+    }
+    stage ^= 1;
+  }
+
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float l_tot = l_run[g];
+    l_tot += __shfl_xor(l_tot, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (!qvalid[g]) continue;
+    if (n_splits == 1) {
+      const float inv = 1.0f / l_tot;
+      bf16_t* ob = static_cast<bf16_t*>(a.o);
+      const int KO = a.n_q_heads * DH;
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) {
+        uint2 w;
+        w.x = static_cast<uint32_t>(f2bf(o[g][dt][0] * inv)) | (static_cast<uint32_t>(f2bf(o[g][dt][1] * inv)) << 16);
+        w.y = static_cast<uint32_t>(f2bf(o[g][dt][2] * inv)) | (static_cast<uint32_t>(f2bf(o[g][dt][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(ob + pk_off(qtok[g], qhead[g] * DH + 16 * dt + 4 * kgrp, KO)) = w;
+      }
+    } else {
+      const int64_t pr = (static_cast<int64_t>(split) * a.R + qtok[g]) * a.n_q_heads + qhead[g];
+      float* op = a.part_o + pr * DH;
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt)
+        *reinterpret_cast<float4*>(op + 16 * dt + 4 * kgrp) = make_float4(o[g][dt][0], o[g][dt][1], o[g][dt][2], o[g][dt][3]);
+      if (kgrp == 0) a.part_ml[pr] = make_float2(m_run[g], l_tot);
+    }
   }
 }
 
@@ -354,9 +611,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int DH, int G>
+template <int DH, int G, int NG, bool DMA>
 hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
-  constexpr int QT = QROWS / G;
+  constexpr int QT = 64 * NG / G;
   const int n_tiles = (a.R + QT - 1) / QT;
   const int base = n_tiles * a.n_kv_heads;
   const int kv_blocks = (a.kv_bound + KVB - 1) / KVB;
@@ -368,16 +625,36 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
     if (static_cast<int64_t>(n_splits) * a.R * a.n_q_heads > kAttnPartialRows) n_splits = 1;
   }
   const int ksplit = ((kv_blocks + n_splits - 1) / n_splits) * KVB;
-  // workgroups stage the table entries of their key range in LDS when they fit
-  if (ksplit / a.cache.bs + 2 <= kBtCache)
-    attn_bf16_kernel<DH, G, true><<<dim3(n_tiles * n_splits, a.n_kv_heads), 256, 0, s>>>(a, n_splits, ksplit);
-  else
-    attn_bf16_kernel<DH, G, false><<<dim3(n_tiles * n_splits, a.n_kv_heads), 256, 0, s>>>(a, n_splits, ksplit);
+  const dim3 grid(n_tiles * n_splits, a.n_kv_heads);
+  if (DMA) {
+    // workgroups stage the table entries of their key range in LDS when they fit
+    if (ksplit / a.cache.bs + 2 <= 1024)
+      attn_dma_kernel<G, true, NG><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
+    else
+      attn_dma_kernel<G, false, NG><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
+  } else if (ksplit / a.cache.bs + 2 <= kBtCache) {
+    attn_bf16_kernel<DH, G, true, NG><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
+  } else {
+    attn_bf16_kernel<DH, G, false, NG><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;
   const int pairs = a.R * a.n_q_heads;
   attn_combine_kernel<DH><<<(pairs + 3) / 4, 256, 0, s>>>(a, n_splits, ksplit, QT);
   return hipGetLastError();
+}
+
+// variant: 1 / 2 = register-staged kernel with 1 / 2 query groups per wave,
+// 3 / 4 = LDS-DMA kernel (head_dim 128, a layer's pool below 2 GiB) with 1 / 2
+template <int DH, int G>
+hipError_t run_bf16_variant(const AttnArgs& a, int variant, hipStream_t s) {
+  if constexpr (DH == 128) {
+    const bool dma_ok = a.cache.layer_stride * 2 < (int64_t(1) << 31);
+    if (variant == 3 && dma_ok) return run_bf16<DH, G, 1, true>(a, s);
+    if (variant == 4 && dma_ok) return run_bf16<DH, G, 2, true>(a, s);
+  }
+  if (variant == 1) return run_bf16<DH, G, 1, false>(a, s);
+  return run_bf16<DH, G, 2, false>(a, s);
 }
 
 }  // namespace
@@ -389,7 +666,7 @@ bool attention_supported(cb_dtype dt, int n_q_heads, int n_kv_heads, int head_di
   return (head_dim == 64 || head_dim == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
 }
 
-hipError_t launch_attention(cb_dtype dt, const AttnArgs& a_in, hipStream_t s) {
+hipError_t launch_attention_ng(cb_dtype dt, const AttnArgs& a_in, int ng, hipStream_t s) {  // ng: variant
   if (a_in.R == 0) return hipSuccess;
   AttnArgs a = a_in;
   a.cache.bs_shift = block_shift(a.cache.bs);   // derived here so it always matches bs
@@ -399,11 +676,15 @@ hipError_t launch_attention(cb_dtype dt, const AttnArgs& a_in, hipStream_t s) {
   }
   const int G = a.n_q_heads / a.n_kv_heads;
 #define CB_ATTN_CASE(D, GG) \
-  if (a.head_dim == D && G == GG) return run_bf16<D, GG>(a, s);
+  if (a.head_dim == D && G == GG) return run_bf16_variant<D, GG>(a, ng, s);
   CB_ATTN_CASE(128, 1) CB_ATTN_CASE(128, 2) CB_ATTN_CASE(128, 4) CB_ATTN_CASE(128, 8) CB_ATTN_CASE(128, 16)
   CB_ATTN_CASE(64, 1) CB_ATTN_CASE(64, 2) CB_ATTN_CASE(64, 4) CB_ATTN_CASE(64, 8) CB_ATTN_CASE(64, 16)
 #undef CB_ATTN_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention(cb_dtype dt, const AttnArgs& a, hipStream_t s) {
+  return launch_attention_ng(dt, a, 4, s);
 }
 
 }  // namespace cb

@@ -199,6 +199,9 @@ struct AttnArgs {
   float2* part_ml;         // split-KV (max, sum) pairs, attn_partial_rows() entries
 };
 hipError_t launch_attention(cb_dtype dt, const AttnArgs& a, hipStream_t s);
+// with an explicit kernel variant: 1 / 2 register-staged K/V with 1 / 2 query groups
+// of 16 rows per wave; 3 / 4 LDS-DMA staged K/V (head_dim 128) with 1 / 2 groups
+hipError_t launch_attention_ng(cb_dtype dt, const AttnArgs& a, int ng, hipStream_t s);
 // workspace bound of the split-KV partials
 constexpr int kAttnMaxSplits = 8;
 constexpr int64_t kAttnPartialRows = int64_t(kAttnMaxSplits) * 32768;   // (split, row, q head) triples

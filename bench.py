@@ -71,6 +71,30 @@ class Hip:
         return float(ms.value)
 
 
+def traffic_from_profile(kind, workload):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (profiles/<kind>_<workload>_traffic.md: FETCH_SIZE + WRITE_SIZE
+    passes scaled by a plain copy of known size), or None when there is no
+    summary or the kernel source changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"{kind}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].strip().split(": ", 1)
+            fields[k] = v
+    try:
+        src = os.path.join(root, fields["kernel_source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields["kernel_source_sha256"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
 def work_per_kind(shape, N, Q, ks, sets, chunk_lens):
     """Algorithmic FLOPs (MFMA kinds) or HBM bytes (the others) of one step.
 
@@ -268,7 +292,7 @@ def main():
         achieved = work_per_launch / (avg_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "unit": "GB/s"}
     roof.update({"kernel": dominant, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
-                 "traffic": None, "launches_per_step": kind_n[dominant], "avg_launch_ms": round(avg_launch_ms, 4),
+                 "traffic": traffic_from_profile(dominant, wl.name), "launches_per_step": kind_n[dominant], "avg_launch_ms": round(avg_launch_ms, 4),
                  "work_per_launch": work_per_launch})
 
     breakdown = {}

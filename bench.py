@@ -113,8 +113,8 @@ def work_per_kind(shape, N, Q, ks, sets, chunk_lens):
     w["gemm_down"] += 2.0 * T * F * d
     w["attention"] += 4.0 * shape.head_dim * shape.n_q_heads * (T * (T + 1) / 2.0)
     w["scatter"] += Q * kvw * (2 * 4 + 2 * es)
-    w["norm"] += 2 * T * d * (4 + es)
-    nc = N
+    w["norm"] += T * d * (4 + es)          # layer 0 attention norm; every other layer-wide norm
+    nc = N                                  # rides on the O / down projection launches
     for l in range(1, L):
         k = ks[l]
         w["gemm_qkv"] += 2.0 * (nc + Q) * d * 2 * kvw + 2.0 * (k + Q) * d * qw
@@ -126,7 +126,8 @@ def work_per_kind(shape, N, Q, ks, sets, chunk_lens):
         w["deviation"] += nc * (kvw * (2 * 4 + 2 * es) + 4 + 4)
         w["select"] += nc * 8 + k * 8
         w["scatter"] += (k + Q) * kvw * (2 * 4 + 2 * es)
-        w["norm"] += ((nc + Q) + (k + Q)) * d * (4 + es)
+        if k != nc:
+            w["norm"] += (k + Q) * d * (4 + es)     # the kept rows' queries, normalised apart
         nc = k
     w["norm"] += d * (4 + 4)
     w["lm_head"] += shape.vocab * d * es

@@ -308,6 +308,8 @@ struct LayerIo {
   float* dev_slot;    // nullable [nc]
   float* dev_by_pos;  // nullable [N]
   int32_t* hkvd_row;  // nullable [k]
+  bool act_ready;     // w.act already holds RMSNorm(x_in) with this layer's attn_norm
+  const float* next_norm;  // nullable: attn_norm of the next layer, fused after the down projection
 };
 
 cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, int N, int Q, int check, int k,
@@ -322,7 +324,8 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   const int rout = k + Q;
 
   // fresh K (rotated at the rows' positions) and V for every candidate and suffix row
-  CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, io.x_in, nullptr, d, rin, d, lw.attn_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
+  if (!io.act_ready)
+    CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, io.x_in, nullptr, d, rin, d, lw.attn_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
   GemmArgs g{};
   g.A = w.act; g.lda = d; g.a_rows = nullptr;
   g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * es; g.ldb = d;
@@ -383,8 +386,8 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   g.C = io.x_mid; g.ldc = d; g.resid = io.x_in; g.resid_rows = w.gmap; g.ld_resid = d;
   g.part = w.gemm_part;
   g.part_floats = kGemmPartFloats;
+  g.norm_gain = lw.mlp_norm; g.norm_eps = c.rms_eps; g.norm_out = w.act;   // the MLP's RMSNorm rides on the O projection
   CB_LAUNCH(tr, CB_KIND_GEMM_O, launch_gemm(c.dtype, EPI_RESID, g, s), "o gemm");
-  CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, io.x_mid, nullptr, d, rout, d, lw.mlp_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
   g = GemmArgs{};
   g.A = w.act; g.lda = d; g.B = lw.w_gate_up; g.ldb = d; g.M = rout; g.N = F; g.K = d;
   g.C = w.h; g.ldc = F; g.ff = F;
@@ -396,13 +399,14 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   g.C = io.x_out; g.ldc = d; g.resid = io.x_mid; g.resid_rows = nullptr; g.ld_resid = d;
   g.part = w.gemm_part;
   g.part_floats = kGemmPartFloats;
+  if (io.next_norm) { g.norm_gain = io.next_norm; g.norm_eps = c.rms_eps; g.norm_out = w.act; }
   CB_LAUNCH(tr, CB_KIND_GEMM_DOWN, launch_gemm(c.dtype, EPI_RESID, g, s), "down gemm");
   return CB_OK;
 }
 
 // Layer 0 over every row: context K/V stay the re-RoPE'd cache, suffix K/V are computed.
-cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, float* x, const Ws& w, hipStream_t s,
-                         Tracer* tr) {
+cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, float* x, const float* next_norm,
+                         const Ws& w, hipStream_t s, Tracer* tr) {
   const cb_model_cfg& c = m.cfg;
   const cb_layer_w& lw = m.layers[0];
   const int d = c.d_model, F = c.d_ff;
@@ -443,8 +447,8 @@ cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, fl
   g.C = x; g.ldc = d; g.resid = x; g.ld_resid = d;
   g.part = w.gemm_part;
   g.part_floats = kGemmPartFloats;
+  g.norm_gain = lw.mlp_norm; g.norm_eps = c.rms_eps; g.norm_out = w.act;
   CB_LAUNCH(tr, CB_KIND_GEMM_O, launch_gemm(c.dtype, EPI_RESID, g, s), "o gemm");
-  CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, x, nullptr, d, T, d, lw.mlp_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
   g = GemmArgs{};
   g.A = w.act; g.lda = d; g.B = lw.w_gate_up; g.ldb = d; g.M = T; g.N = F; g.K = d; g.C = w.h; g.ldc = F; g.ff = F;
   g.part = w.gemm_part;
@@ -455,6 +459,7 @@ cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, fl
   g.C = x; g.ldc = d; g.resid = x; g.ld_resid = d;
   g.part = w.gemm_part;
   g.part_floats = kGemmPartFloats;
+  if (next_norm) { g.norm_gain = next_norm; g.norm_eps = c.rms_eps; g.norm_out = w.act; }
   CB_LAUNCH(tr, CB_KIND_GEMM_DOWN, launch_gemm(c.dtype, EPI_RESID, g, s), "down gemm");
   return CB_OK;
 }
@@ -661,7 +666,7 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
   if (hkvd_out) CB_LAUNCH(tr, CB_KIND_OTHER, launch_iota(hkvd_out, N, 0, s), "iota");
 
   // a3: layer 0 in full
-  if ((st = enqueue_layer0(*model, kv, N, Q, w.x0, w, s, tr)) != CB_OK) return st;
+  if ((st = enqueue_layer0(*model, kv, N, Q, w.x0, model->layers[1].attn_norm, w, s, tr)) != CB_OK) return st;
 
   // layers 1 .. L-1
   float* xcur = w.x0;
@@ -685,6 +690,8 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
     io.dev_slot = nullptr;
     io.dev_by_pos = (chk && dev_out) ? dev_out + (int64_t)l * N : nullptr;
     io.hkvd_row = hkvd_out ? hkvd_out + (int64_t)l * N : nullptr;
+    io.act_ready = true;   // the previous layer's down projection normalised its output rows
+    io.next_norm = (l + 1 < L) ? model->layers[l + 1].attn_norm : nullptr;
     if ((st = enqueue_layer(*model, l, kv, nc, N, Q, chk, k, io, w, s, tr)) != CB_OK) return st;
     std::swap(xcur, xoth);
     std::swap(cand, nxt);

@@ -310,6 +310,58 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int spli
   }
 }
 
+// Split-K reduction of a residual GEMM fused with the RMSNorm that follows it:
+// one workgroup per row; x = resid + (partials summed in split order) is
+// written fp32, then normalised (same reduction order as the RMSNorm kernel)
+// into the fragment-major bf16 activations of the next GEMM.
+constexpr int kNormChunks = 16;   // 16 x 1024 columns: d_model <= 16384
+
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs g, int splits) {
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const int rr = g.resid_rows ? g.resid_rows[row] : row;
+  float4 v[kNormChunks];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < kNormChunks; ++c) {
+    const int e = threadIdx.x * 4 + c * 1024;
+    if (e < g.N) {
+      float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int sp = 0; sp < splits; ++sp) {
+        const float4 p = *reinterpret_cast<const float4*>(g.part + (static_cast<int64_t>(sp) * g.M + row) * g.N + e);
+        s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+      }
+      const float4 r = *reinterpret_cast<const float4*>(g.resid + static_cast<int64_t>(rr) * g.ld_resid + e);
+      v[c] = make_float4(r.x + s.x, r.y + s.y, r.z + s.z, r.w + s.w);
+      *reinterpret_cast<float4*>(static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + e) = v[c];
+      ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+    }
+  }
+  ss = wave_sum64(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float inv = 1.0f / sqrtf(tot / static_cast<float>(g.N) + g.norm_eps);
+  bf16_t* out = static_cast<bf16_t*>(g.norm_out);
+#pragma unroll
+  for (int c = 0; c < kNormChunks; ++c) {
+    const int e = threadIdx.x * 4 + c * 1024;
+    if (e < g.N) {
+      const float4 gg = *reinterpret_cast<const float4*>(g.norm_gain + e);
+      uint2 w;
+      w.x = static_cast<uint32_t>(f2bf(v[c].x * inv * gg.x)) | (static_cast<uint32_t>(f2bf(v[c].y * inv * gg.y)) << 16);
+      w.y = static_cast<uint32_t>(f2bf(v[c].z * inv * gg.z)) | (static_cast<uint32_t>(f2bf(v[c].w * inv * gg.w)) << 16);
+      *reinterpret_cast<uint2*>(out + pk_off(row, e, g.N)) = w;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 SIMT GEMM: 64x64x16 tiles, 256 threads, 4x4 outputs per thread
 // ---------------------------------------------------------------------------
@@ -483,8 +535,9 @@ void choose_gemm_cfg(const GemmArgs& a, int epi, int* cfg, int* splits) {
 
 namespace {
 
+// *normed: set when the RMSNorm of a residual GEMM's output was fused into the reduction
 template <int EPI, int BM>
-hipError_t run_bm(const GemmArgs& a, int splits, hipStream_t s) {
+hipError_t run_bm(const GemmArgs& a, int splits, hipStream_t s, bool* normed) {
   int kps, eff;
   split_k(a.K, splits, &kps, &eff);
   const int t = tiles_of(a, EPI, BM);
@@ -495,8 +548,13 @@ hipError_t run_bm(const GemmArgs& a, int splits, hipStream_t s) {
       if (a.part == nullptr || static_cast<int64_t>(eff) * a.M * a.N > a.part_floats) return hipErrorInvalidValue;
       hipError_t e = launch_cfg<EPI, BM, true>(a, t, eff, kps, s);
       if (e != hipSuccess) return e;
-      const int64_t n = static_cast<int64_t>(a.M) * (a.N / 4);
-      splitk_reduce_kernel<EPI><<<static_cast<int>((n + 255) / 256), 256, 0, s>>>(a, eff);
+      if (EPI == EPI_RESID && a.norm_out != nullptr && a.N <= kNormChunks * 1024) {
+        splitk_reduce_norm_kernel<<<a.M, 256, 0, s>>>(a, eff);
+        *normed = true;
+      } else {
+        const int64_t n = static_cast<int64_t>(a.M) * (a.N / 4);
+        splitk_reduce_kernel<EPI><<<static_cast<int>((n + 255) / 256), 256, 0, s>>>(a, eff);
+      }
       return hipGetLastError();
     }
   }
@@ -504,35 +562,42 @@ hipError_t run_bm(const GemmArgs& a, int splits, hipStream_t s) {
 }
 
 template <int EPI>
-hipError_t run_cfg(const GemmArgs& a, int cfg, int splits, hipStream_t s) {
+hipError_t run_cfg(const GemmArgs& a, int cfg, int splits, hipStream_t s, bool* normed) {
   if (a.K % BK != 0 || a.K <= 0) return hipErrorInvalidValue;
   if (EPI == EPI_SWIGLU && a.N % 32 != 0) return hipErrorInvalidValue;
   if (splits > 1 && a.N % 4 != 0) return hipErrorInvalidValue;
-  return cfg == GEMM_CFG_256 ? run_bm<EPI, 256>(a, splits, s) : run_bm<EPI, 128>(a, splits, s);
+  return cfg == GEMM_CFG_256 ? run_bm<EPI, 256>(a, splits, s, normed) : run_bm<EPI, 128>(a, splits, s, normed);
 }
 
 template <int EPI>
 hipError_t run_gemm(cb_dtype dt, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
+  bool normed = false;
+  hipError_t e;
   if (dt != CB_BF16) {
     const int m_tiles = (a.M + FM - 1) / FM;
     const int n_tiles = (EPI == EPI_SWIGLU) ? (a.N + FN / 2 - 1) / (FN / 2) : (a.N + FN - 1) / FN;
     gemm_f32_kernel<EPI><<<m_tiles * n_tiles, 256, 0, s>>>(a);
-    return hipGetLastError();
+    e = hipGetLastError();
+  } else {
+    int cfg, splits;
+    choose_gemm_cfg(a, EPI, &cfg, &splits);
+    e = run_cfg<EPI>(a, cfg, splits, s, &normed);
   }
-  int cfg, splits;
-  choose_gemm_cfg(a, EPI, &cfg, &splits);
-  return run_cfg<EPI>(a, cfg, splits, s);
+  if (e != hipSuccess || EPI != EPI_RESID || a.norm_out == nullptr || normed) return e;
+  return launch_rmsnorm(dt, static_cast<const float*>(a.C), nullptr, a.ldc, a.M, a.N, a.norm_gain, a.norm_eps, a.norm_out,
+                        a.N, 0, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_cfg(GemmEpi epi, const GemmArgs& a, int cfg, int splits, hipStream_t s) {
+  bool normed = false;
   switch (epi) {
-    case EPI_STORE_ROPE: return run_cfg<EPI_STORE_ROPE>(a, cfg, splits, s);
-    case EPI_F32_ROPE: return run_cfg<EPI_F32_ROPE>(a, cfg, splits, s);
-    case EPI_RESID: return run_cfg<EPI_RESID>(a, cfg, splits, s);
-    case EPI_SWIGLU: return run_cfg<EPI_SWIGLU>(a, cfg, splits, s);
+    case EPI_STORE_ROPE: return run_cfg<EPI_STORE_ROPE>(a, cfg, splits, s, &normed);
+    case EPI_F32_ROPE: return run_cfg<EPI_F32_ROPE>(a, cfg, splits, s, &normed);
+    case EPI_RESID: return run_cfg<EPI_RESID>(a, cfg, splits, s, &normed);
+    case EPI_SWIGLU: return run_cfg<EPI_SWIGLU>(a, cfg, splits, s, &normed);
   }
   return hipErrorInvalidValue;
 }

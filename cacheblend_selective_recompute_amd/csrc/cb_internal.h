@@ -169,6 +169,12 @@ struct GemmArgs {
   int ff;                  // fp32 SWIGLU: row offset of the up half in B
   float* part;             // split-K partial sums (fp32), may be NULL (no split)
   int64_t part_floats;     // capacity of part
+  // EPI_RESID only, optional: RMSNorm of the output rows (gain norm_gain, eps
+  // norm_eps) into norm_out (the next GEMM's activations: bf16 fragment-major
+  // or fp32 row-major, K = N); fused into the split-K reduction when K is split
+  const float* norm_gain;
+  float norm_eps;
+  void* norm_out;
 };
 constexpr int64_t kGemmPartFloats = int64_t(32) << 20;   // 128 MiB of split-K partials
 hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s);

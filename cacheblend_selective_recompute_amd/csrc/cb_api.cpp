@@ -326,15 +326,28 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   // fresh K (rotated at the rows' positions) and V for every candidate and suffix row
   if (!io.act_ready)
     CB_LAUNCH(tr, CB_KIND_NORM, launch_rmsnorm(c.dtype, io.x_in, nullptr, d, rin, d, lw.attn_norm, c.rms_eps, w.act, d, 0, s), "rmsnorm");
+  // when every candidate is kept, the queries come from the same rows: one GEMM
+  // over the whole Q/K/V weight writes Q (bf16) and the fresh K/V (fp32) at once
+  const bool fused_qkv = (k == nc) && c.dtype == CB_BF16;
   GemmArgs g{};
   g.A = w.act; g.lda = d; g.a_rows = nullptr;
-  g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * es; g.ldb = d;
-  g.M = rin; g.N = 2 * kvw; g.K = d;
-  g.C = w.kvf; g.ldc = 2 * kvw;
-  g.rope_cols = kvw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = io.rowpos_in;
+  g.K = d; g.M = rin;
+  g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = io.rowpos_in;
   g.part = w.gemm_part;
   g.part_floats = kGemmPartFloats;
-  CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "kv gemm");
+  if (fused_qkv) {
+    g.B = lw.w_qkv; g.ldb = d;
+    g.N = qw + 2 * kvw;
+    g.C = w.q; g.ldc = qw; g.q_cols = qw;
+    g.C2 = w.kvf; g.ldc2 = 2 * kvw; g.rope2_cols = kvw;
+    CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_QKV, g, s), "qkv gemm");
+  } else {
+    g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * es; g.ldb = d;
+    g.N = 2 * kvw;
+    g.C = w.kvf; g.ldc = 2 * kvw;
+    g.rope_cols = kvw;
+    CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "kv gemm");
+  }
 
   const int32_t* sel_slot = nullptr;
   const int32_t* sel_pos = io.cand_pos;
@@ -361,15 +374,17 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
               "rmsnorm");
     aq = w.h;
   }
-  g = GemmArgs{};
-  g.A = aq; g.lda = d; g.a_rows = nullptr;
-  g.B = lw.w_qkv; g.ldb = d;
-  g.M = rout; g.N = qw; g.K = d;
-  g.C = w.q; g.ldc = qw;
-  g.rope_cols = qw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = io.rowpos_out;
-  g.part = w.gemm_part;
-  g.part_floats = kGemmPartFloats;
-  CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
+  if (!fused_qkv) {
+    g = GemmArgs{};
+    g.A = aq; g.lda = d; g.a_rows = nullptr;
+    g.B = lw.w_qkv; g.ldb = d;
+    g.M = rout; g.N = qw; g.K = d;
+    g.C = w.q; g.ldc = qw;
+    g.rope_cols = qw; g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = io.rowpos_out;
+    g.part = w.gemm_part;
+    g.part_floats = kGemmPartFloats;
+    CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
+  }
 
   AttnArgs at{};
   at.q = w.q; at.ldq = qw; at.o = w.o; at.ldo = qw; at.rowpos = io.rowpos_out; at.R = rout;

@@ -245,6 +245,25 @@ __global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kern
           const float4 rv = *reinterpret_cast<const float4*>(g.resid + static_cast<int64_t>(rr) * g.ld_resid + col);
           *reinterpret_cast<float4*>(static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + col) =
               make_float4(rv.x + x.x, rv.y + x.y, rv.z + x.z, rv.w + x.w);
+        } else if constexpr (EPI == EPI_QKV) {
+          const int pos = g.row_pos[row];
+          if (col < g.q_cols) {
+            const float4 cs = *reinterpret_cast<const float4*>(g.rope_tab + static_cast<int64_t>(pos) * half + ((col % g.head_dim) >> 1));
+            x = make_float4(x.x * cs.x - x.y * cs.y, x.x * cs.y + x.y * cs.x,
+                            x.z * cs.z - x.w * cs.w, x.z * cs.w + x.w * cs.z);
+            uint2 w;
+            w.x = static_cast<uint32_t>(f2bf(x.x)) | (static_cast<uint32_t>(f2bf(x.y)) << 16);
+            w.y = static_cast<uint32_t>(f2bf(x.z)) | (static_cast<uint32_t>(f2bf(x.w)) << 16);
+            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.C) + static_cast<int64_t>(row) * g.ldc + col) = w;
+          } else {
+            const int c2 = col - g.q_cols;
+            if (c2 < g.rope2_cols) {
+              const float4 cs = *reinterpret_cast<const float4*>(g.rope_tab + static_cast<int64_t>(pos) * half + ((c2 % g.head_dim) >> 1));
+              x = make_float4(x.x * cs.x - x.y * cs.y, x.x * cs.y + x.y * cs.x,
+                              x.z * cs.z - x.w * cs.w, x.z * cs.w + x.w * cs.z);
+            }
+            *reinterpret_cast<float4*>(g.C2 + static_cast<int64_t>(row) * g.ldc2 + c2) = x;
+          }
         } else {   // EPI_STORE_ROPE / EPI_F32_ROPE
           if (col < g.rope_cols) {
             const int pos = g.row_pos[row];
@@ -281,7 +300,29 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int spli
     s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
   }
   float v[4] = {s.x, s.y, s.z, s.w};
-  if constexpr (EPI == EPI_RESID) {
+  if constexpr (EPI == EPI_QKV) {
+    const int p = g.row_pos[row];
+    const int half = g.head_dim >> 1;
+    const bool isq = col < g.q_cols;
+    const int c = isq ? col : col - g.q_cols;
+    if (isq || c < g.rope2_cols) {
+#pragma unroll
+      for (int j = 0; j < 4; j += 2) {
+        const float2 cs = g.rope_tab[static_cast<int64_t>(p) * half + (((c + j) % g.head_dim) >> 1)];
+        const float x0 = v[j], x1 = v[j + 1];
+        v[j] = x0 * cs.x - x1 * cs.y;
+        v[j + 1] = x0 * cs.y + x1 * cs.x;
+      }
+    }
+    if (isq) {
+      uint2 w;
+      w.x = static_cast<uint32_t>(f2bf(v[0])) | (static_cast<uint32_t>(f2bf(v[1])) << 16);
+      w.y = static_cast<uint32_t>(f2bf(v[2])) | (static_cast<uint32_t>(f2bf(v[3])) << 16);
+      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.C) + static_cast<int64_t>(row) * g.ldc + c) = w;
+    } else {
+      *reinterpret_cast<float4*>(g.C2 + static_cast<int64_t>(row) * g.ldc2 + c) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  } else if constexpr (EPI == EPI_RESID) {
     const int rr = g.resid_rows ? g.resid_rows[row] : row;
     const float4 r = *reinterpret_cast<const float4*>(g.resid + static_cast<int64_t>(rr) * g.ld_resid + col);
     *reinterpret_cast<float4*>(static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + col) =
@@ -575,6 +616,7 @@ hipError_t run_gemm(cb_dtype dt, const GemmArgs& a, hipStream_t s) {
   bool normed = false;
   hipError_t e;
   if (dt != CB_BF16) {
+    if constexpr (EPI == EPI_QKV) return hipErrorInvalidValue;   // bf16 only
     const int m_tiles = (a.M + FM - 1) / FM;
     const int n_tiles = (EPI == EPI_SWIGLU) ? (a.N + FN / 2 - 1) / (FN / 2) : (a.N + FN - 1) / FN;
     gemm_f32_kernel<EPI><<<m_tiles * n_tiles, 256, 0, s>>>(a);
@@ -598,6 +640,7 @@ hipError_t launch_gemm_cfg(GemmEpi epi, const GemmArgs& a, int cfg, int splits, 
     case EPI_F32_ROPE: return run_cfg<EPI_F32_ROPE>(a, cfg, splits, s, &normed);
     case EPI_RESID: return run_cfg<EPI_RESID>(a, cfg, splits, s, &normed);
     case EPI_SWIGLU: return run_cfg<EPI_SWIGLU>(a, cfg, splits, s, &normed);
+    case EPI_QKV: return run_cfg<EPI_QKV>(a, cfg, splits, s, &normed);
   }
   return hipErrorInvalidValue;
 }
@@ -608,6 +651,7 @@ hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t 
     case EPI_F32_ROPE: return run_gemm<EPI_F32_ROPE>(dt, a, s);
     case EPI_RESID: return run_gemm<EPI_RESID>(dt, a, s);
     case EPI_SWIGLU: return run_gemm<EPI_SWIGLU>(dt, a, s);
+    case EPI_QKV: return run_gemm<EPI_QKV>(dt, a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -145,6 +145,8 @@ enum GemmEpi : int {
   EPI_F32_ROPE = 1,     // C (fp32) = acc, RoPE on columns < rope_cols at row_pos
   EPI_RESID = 2,        // C (fp32)[i] = resid[resid_rows ? resid_rows[i] : i] + acc
   EPI_SWIGLU = 3,       // C (model dtype)[i][f] = SiLU(A.Wg[f]) * (A.Wu[f])
+  EPI_QKV = 4,          // columns < q_cols: C (model dtype, RoPE); the rest: C2 (fp32) at col - q_cols,
+                        // RoPE on its first rope2_cols columns; both at row_pos
 };
 // bf16: A and B are fragment-major (pk_off, K columns); B is a packed weight
 // (cb_pack_weight), for SWIGLU with gate and up 32-row blocks interleaved; the
@@ -175,6 +177,11 @@ struct GemmArgs {
   const float* norm_gain;
   float norm_eps;
   void* norm_out;
+  // EPI_QKV: second output (fp32) for the columns from q_cols on
+  float* C2;
+  int64_t ldc2;
+  int q_cols;
+  int rope2_cols;
 };
 constexpr int64_t kGemmPartFloats = int64_t(32) << 20;   // 128 MiB of split-K partials
 hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s);

@@ -393,9 +393,25 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_dma_kernel(AttnArgs
     }
   };
 
-  issue(j_begin, 0);
-  int stage = 0;
-  for (int j0 = j_begin; j0 < j_end; j0 += KVB) {
+  // per-lane LDS byte offsets of the fragment reads inside a stage (block-relative keys):
+  // K fragment (t, ks): key 16 t + lane % 16, chunk 4 ks + kgrp at slot chunk ^ (key % 16);
+  // V^T source of (dt, s2, h): key 32 s2 + 16 h + 4 kgrp + sl / 4, dims 16 dt + 4 (sl % 4)
+  int koff[DH / 32], voffs[DH / 16];
+  {
+    const int kk = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) koff[ks] = kk * 256 + (((4 * ks + kgrp) ^ kk) << 4);
+    const int sl = lane & 15;
+    const int vkey = 4 * kgrp + (sl >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) {
+      const int d = 16 * dt + 4 * (sl & 3);
+      voffs[dt] = vkey * 256 + (((d >> 3) ^ ((vkey & 7) << 1)) << 4) + ((d & 7) << 1);
+    }
+  }
+  // one 64-key block held in LDS stage `stage` (a constant at both call sites, so
+  // every LDS address is a per-lane base plus an immediate offset)
+  auto block = [&](int j0, int stage) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of block j0 have landed
     __syncthreads();                      // ... everyone's; block j0 - 64 is no longer read
     if (j0 + KVB < j_end) issue(j0 + KVB, stage ^ 1);
@@ -407,11 +423,9 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_dma_kernel(AttnArgs
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) s[g][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int key = 16 * t + (lane & 15);
 #pragma unroll
       for (int ks = 0; ks < DH / 32; ++ks) {
-        const int c = 4 * ks + kgrp;
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Kb + key * 256 + ((c ^ (key & 15)) << 4));
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Kb + koff[ks] + t * (16 * 256));
 #pragma unroll
         for (int g = 0; g < NG; ++g) s[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[g][ks], s[g][t], 0, 0, 0);
       }
@@ -435,15 +449,18 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_dma_kernel(AttnArgs
         mblk = fmaxf(fmaxf(mblk, fmaxf(s[g][t][0], s[g][t][1])), fmaxf(s[g][t][2], s[g][t][3]));
       mblk = fmaxf(mblk, __shfl_xor(mblk, 16, 64));
       mblk = fmaxf(mblk, __shfl_xor(mblk, 32, 64));
-      const float m_new = fmaxf(m_run[g], mblk * sc);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      if (__any(m_new != m_run[g])) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_use);
+      // the reference max moves only when some row's block max exceeds it by more than
+      // 2^8 in exp2 units, so exp2 of every score stays <= 256 and rescaling is rare
+      const float m_blk = mblk * sc;
+      if (__any(m_blk > m_run[g] + 8.f)) {
+        const float m_new = fmaxf(m_run[g], m_blk);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[g] - m_new);
         l_run[g] *= alpha;
 #pragma unroll
         for (int t = 0; t < DH / 16; ++t) o[g][t] *= alpha;
+        m_run[g] = m_new;
       }
-      m_run[g] = m_new;
+      const float m_use = (m_run[g] == -INFINITY) ? 0.f : m_run[g];
       float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -467,7 +484,6 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_dma_kernel(AttnArgs
     // transposing read gives lane (group kg, index i) element e from source lane 4 e + i / 4 of
     // its 16-lane group, column i % 4, so source lane s points at key 32 s2 + 16 h + 4 kg + s / 4,
     // dims 16 dt + 4 (s % 4) .. +3
-    const int sl = lane & 15;
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt) {
 #pragma unroll
@@ -475,10 +491,7 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_dma_kernel(AttnArgs
         s16x4_t half[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int key = 32 * s2 + 16 * h + 4 * kgrp + (sl >> 2);
-          const int d = 16 * dt + 4 * (sl & 3);
-          const int c = d >> 3;
-          const uint8_t* src = Vb + key * 256 + ((c ^ ((key & 7) << 1)) << 4) + ((d & 7) << 1);
+          const uint8_t* src = Vb + voffs[dt] + (32 * s2 + 16 * h) * 256;
           half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) s16x4_t*)(const __attribute__((address_space(3))) void*)(src));
         }
@@ -487,7 +500,11 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_dma_kernel(AttnArgs
         for (int g = 0; g < NG; ++g) o[g][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[g][s2], o[g][dt], 0, 0, 0);
       }
     }
-    stage ^= 1;
+  };
+  issue(j_begin, 0);
+  for (int j0 = j_begin; j0 < j_end; j0 += 2 * KVB) {
+    block(j0, 0);
+    if (j0 + KVB < j_end) block(j0 + KVB, 1);
   }
 
 #pragma unroll

@@ -122,10 +122,13 @@ __global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kern
     const int q = u < DA ? wid * DA + u : wid * 4 + (u - DA);
     voff[u] = ((q >> 1) * kbr + (q & 1)) * 1024 + lane * 16;
   }
-  const uint32_t lds0 = lds_addr(smem);
-  auto copy = [&](int s, int u) {
-    const int q = u < DA ? wid * DA + u : wid * 4 + (u - DA);
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + (s % NS) * T::kStage + (u < DA ? 0 : T::kStageA) + q * 1024);
+  // LDS byte address of the ring and the wave index, both wave-uniform (scalar registers)
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem));
+  const int wid_s = __builtin_amdgcn_readfirstlane(wid);
+  // copy u of stage s into ring slot `slot` (a compile-time constant at every call)
+  auto copy = [&](int s, int slot, int u) {
+    const int q = u < DA ? wid_s * DA + u : wid_s * 4 + (u - DA);
+    const uint32_t dst = lds0 + slot * T::kStage + (u < DA ? 0 : T::kStageA) + q * 1024;
     const int soff = min(s, nk - 1) * (BK * 64);      // stages past the last re-read it into a retired slot
     if (u < DA) copy_block(dst, ra, voff[u], soff);
     else copy_block(dst, rb, voff[u], soff);
@@ -139,57 +142,68 @@ __global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kern
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // per-lane fragment offsets within a slot; the slot offset is an immediate
+  const uint8_t* fa = smem + (wm * FM * 2) * 1024 + lane * 16;
+  const uint8_t* fb = smem + T::kStageA + (wn * 4 * 2) * 1024 + lane * 16;
   bf16x8_t af[2][FM], bfr[2][4];
-  auto frag = [&](int s, int ks, int slot) {
-    const uint8_t* st = smem + (s % NS) * T::kStage;
+  auto frag = [&](int slot, int ks, int reg) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      af[slot][i] = *reinterpret_cast<const bf16x8_t*>(st + ((wm * FM + i) * 2 + ks) * 1024 + lane * 16);
+      af[reg][i] = *reinterpret_cast<const bf16x8_t*>(fa + slot * T::kStage + (i * 2 + ks) * 1024);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      bfr[slot][j] = *reinterpret_cast<const bf16x8_t*>(st + T::kStageA + ((wn * 4 + j) * 2 + ks) * 1024 + lane * 16);
+      bfr[reg][j] = *reinterpret_cast<const bf16x8_t*>(fb + slot * T::kStage + (j * 2 + ks) * 1024);
   };
-  // the MFMAs of one 16-column step, with copies u0 .. u0+cnt-1 of stage cs spread among them
-  auto mma = [&](int slot, int cs, int u0, int cnt) {
+  // the MFMAs of one 16-column step, with copies u0 .. u0+cnt-1 of stage cs (slot cslot) spread among them
+  auto mma = [&](int reg, int cs, int cslot, int u0, int cnt) {
     constexpr int NM = 4 * FM;
 #pragma unroll
     for (int x = 0; x < NM; ++x) {
-      acc[x >> 2][x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][x >> 2], bfr[slot][x & 3], acc[x >> 2][x & 3], 0, 0, 0);
+      acc[x >> 2][x & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[reg][x >> 2], bfr[reg][x & 3], acc[x >> 2][x & 3], 0, 0, 0);
 #pragma unroll
       for (int c = 0; c < cnt; ++c)
         if (x == (c * NM) / cnt + NM / cnt - 1) {
           __builtin_amdgcn_sched_barrier(0);
-          copy(cs, u0 + c);
+          copy(cs, cslot, u0 + c);
           __builtin_amdgcn_sched_barrier(0);
         }
     }
+  };
+  // one stage: t in slot `slot`.  Copies of stage s go out during the second half of
+  // stage s-NS and the first half of stage s-NS+1 (slot s % NS), i.e. after every wave
+  // has read stage s-NS (its reads all precede the barrier in the middle of s-NS).
+  auto stage = [&](int kt, int slot) __attribute__((always_inline)) {
+    frag(slot, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0, kt + NS - 1, (slot + NS - 1) % NS, H0, H1);
+    __builtin_amdgcn_sched_barrier(0);
+    CB_WAIT_VM(DQ * (NS - 2));     // this wave's copies of stage kt+1 have landed
+    __syncthreads();               // ... everyone's
+    frag((slot + 1) % NS, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1, kt + NS, slot, 0, H0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // prologue: stages 0 .. NS-2 and the first half of stage NS-1 in flight
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
 #pragma unroll
-    for (int u = 0; u < DQ; ++u) copy(s, u);
+    for (int u = 0; u < DQ; ++u) copy(s, s, u);
 #pragma unroll
-  for (int u = 0; u < H0; ++u) copy(NS - 1, u);
+  for (int u = 0; u < H0; ++u) copy(NS - 1, NS - 1, u);
   CB_WAIT_VM(DQ * (NS - 2) + H0);
   __syncthreads();
   frag(0, 0, 0);
-  // Stage t lives in slot t % NS.  Copies of stage s go out during the second half
-  // of stage s-NS and the first half of stage s-NS+1, i.e. after every wave has
-  // read stage s-NS (its reads all precede the barrier in the middle of s-NS).
-  for (int kt = 0; kt < nk; ++kt) {
-    frag(kt, 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(0, kt + NS - 1, H0, H1);
-    __builtin_amdgcn_sched_barrier(0);
-    CB_WAIT_VM(DQ * (NS - 2));     // this wave's copies of stage kt+1 have landed
-    __syncthreads();               // ... everyone's
-    frag(kt + 1, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(1, kt + NS, 0, H0);
-    __builtin_amdgcn_sched_barrier(0);
+  // unrolled by NS so every ring slot is a compile-time constant
+  int kt = 0;
+  for (; kt + NS <= nk; kt += NS) {
+#pragma unroll
+    for (int r = 0; r < NS; ++r) stage(kt + r, r);
   }
+#pragma unroll
+  for (int r = 0; r < NS - 1; ++r)
+    if (kt + r < nk) stage(kt + r, r);
   CB_WAIT_VM(0);                   // no copy may still be writing LDS when the workgroup ends
 
   // ---------------- epilogue ----------------

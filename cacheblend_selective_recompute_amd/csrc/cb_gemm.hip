@@ -24,6 +24,7 @@
 // consecutive tiles land on the same XCD (they share a weight tile in its L2).
 // fp32 path: a plain LDS-tiled FMA kernel (fp32 models are small).
 #include <algorithm>
+#include <cmath>
 
 #include "cb_internal.h"
 
@@ -543,10 +544,13 @@ inline void split_k(int K, int splits, int* kps, int* eff) {
 }
 
 // Cost model, calibrated on the GEMM microbenchmark with random bf16 data at the
-// 8B blend shapes: a 256-row tile computes at ~4.8 TFLOP/s on a CU of its own;
-// 128-row tiles run two per CU at ~2.5 TFLOP/s each and ~3.8 when alone;
-// workgroups run in rounds of (256 CUs x workgroups per CU); the fixed-order
-// reduction moves the fp32 partials once (write + read) at ~8 TB/s plus a launch.
+// 8B blend shapes.  A round of workgroups on b CUs runs at a per-workgroup rate
+// that rises as fewer CUs are busy (the chip is power-limited under MFMA load):
+// 256-row tiles (one per CU) ~5.0 TFLOP/s x (256/b)^0.4; 128-row tiles two per CU
+// ~2.6 each, one per CU ~3.9 x (256/b)^0.4 (the gain capped at 1.25).  The fixed-order reduction moves the
+// fp32 partials once (write + read) at ~8 TB/s plus a launch.
+inline double busy_scale(int64_t b) { return b >= 256 ? 1.0 : fmin(1.25, pow(256.0 / static_cast<double>(b), 0.4)); }
+
 inline double est_time(const GemmArgs& a, int epi, int cfg, int splits) {
   const int bm = bm_of(cfg);
   int kps, eff;
@@ -555,11 +559,14 @@ inline double est_time(const GemmArgs& a, int epi, int cfg, int splits) {
   const double flop_wg = 2.0 * bm * BN * kps;
   double tm = 0.0;
   if (bm == 256) {
-    tm = static_cast<double>((wgs + 255) / 256) * flop_wg / 4.8e12;
+    const int64_t full = wgs / 256, rem = wgs % 256;
+    tm = static_cast<double>(full) * flop_wg / 5.0e12;
+    if (rem > 0) tm += flop_wg / (5.0e12 * busy_scale(rem));
   } else {
     const int64_t full = wgs / 512, rem = wgs % 512;
-    tm = static_cast<double>(full) * flop_wg / 2.5e12;
-    if (rem > 0) tm += flop_wg / (rem > 256 ? 2.5e12 : 3.8e12);
+    tm = static_cast<double>(full) * flop_wg / 2.6e12;
+    if (rem > 256) tm += flop_wg / 2.6e12;
+    else if (rem > 0) tm += flop_wg / (3.9e12 * busy_scale(rem));
   }
   if (eff > 1) tm += static_cast<double>(eff) * a.M * a.N * 8.0 / 8e12 + 3e-6;
   return tm;

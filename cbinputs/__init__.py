@@ -385,6 +385,31 @@ def torch_device_weights(shape: ModelShape, seed: int, device="cuda") -> Dict[st
             "final_norm": torch.ones(d, device=device, dtype=torch.float32)}
 
 
+def torch_device_layer(shape: ModelShape, seed: int, device="cuda") -> Dict[str, object]:
+    """One decoder layer's weights drawn on the GPU (library layout, as in
+    ``torch_device_weights``), for single-layer tests at full width where host
+    generation would take minutes."""
+    import torch
+    td = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1000003 + 29)
+    d, F = shape.d_model, shape.d_ff
+
+    def draw(*dims):
+        t = torch.randn(*dims, generator=gen, device=device, dtype=torch.float32)
+        t.mul_(shape.init_std)
+        return t.to(td)
+
+    return {
+        "w_qkv": draw(shape.q_width + 2 * shape.kv_width, d),
+        "w_o": draw(d, shape.q_width),
+        "w_gate_up": draw(2 * F, d),
+        "w_down": draw(d, F),
+        "attn_norm": torch.ones(d, device=device, dtype=torch.float32),
+        "mlp_norm": torch.ones(d, device=device, dtype=torch.float32),
+    }
+
+
 def torch_device_chunk_kv(shape: ModelShape, lens: Sequence[int], seed: int, device="cuda"):
     """Stand-in cached K/V per chunk drawn on the GPU ([L][len][H_kv][d_h],
     N(0, (init_std*sqrt(d))^2)), for throughput runs."""

@@ -321,7 +321,7 @@ def _check_tiling(chunks):
 
 def blend_layer(m: OracleModel, l: int, Kl: np.ndarray, Vl: np.ndarray, x_rows: np.ndarray,
                 cand_pos: np.ndarray, n_query: int, check: bool, k_keep: int,
-                force: Optional[np.ndarray] = None):
+                force: Optional[np.ndarray] = None, out_rows: Optional[np.ndarray] = None):
     """One selective-recompute layer l >= 1 ([CB] Fig. 5 and "选 token").
 
     ``x_rows`` holds the hidden rows of the candidates (positions
@@ -334,6 +334,12 @@ def blend_layer(m: OracleModel, l: int, Kl: np.ndarray, Vl: np.ndarray, x_rows: 
     the suffix; attention of those rows over the whole cache; O, residual,
     MLP.  Returns (x_out rows for kept + suffix, kept positions, deviation or
     None).
+
+    ``out_rows`` (indices into the kept + suffix rows) limits the attention,
+    O and MLP to those rows; x_out then holds only them, in that order.  Every
+    K/V row is still written first, so each returned row is exactly the one the
+    full call would give: a row's output depends on its own hidden state and on
+    the updated cache alone.
     """
     w = m.layer(l)
     T = Kl.shape[0]
@@ -363,7 +369,9 @@ def blend_layer(m: OracleModel, l: int, Kl: np.ndarray, Vl: np.ndarray, x_rows: 
     # fill: fresh K/V of the kept rows and the suffix replace the cache
     Kl[wpos] = store_round(kf[sel], m.storage)
     Vl[wpos] = store_round(vf[sel], m.storage)
-    x_out = _attn_mlp(m, w, x_rows[sel], a[sel], wpos, Kl, Vl, np.arange(T))
+    if out_rows is not None:
+        sel = sel[np.asarray(out_rows, dtype=np.int64)]
+    x_out = _attn_mlp(m, w, x_rows[sel], a[sel], rows_pos[sel], Kl, Vl, np.arange(T))
     return x_out, keep, dev
 
 

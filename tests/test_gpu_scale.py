@@ -1,0 +1,159 @@
+"""GPU parity at the largest shapes: the 70B width (d 8192, 64 q / 8 kv
+heads, F 28672) and the 32K-token paged context of the 8B shape.
+
+A full oracle run at these sizes takes hours on the host, so:
+* cb_blend_layer is run for one selective layer at full width and full
+  context; the oracle computes fresh K/V and the deviation of every candidate
+  (so the whole HKVD set and every scattered row are compared), but the
+  attention, O and MLP only for a sample of the kept and suffix rows, which is
+  exact because a row's output depends only on its own hidden state and the
+  updated cache;
+* the whole 32-layer, 32K-token paged blend is checked through properties that
+  hold at any size (sorted, nested sets; untouched rows keep the re-RoPE'd
+  cache; changed rows are exactly the kept ones; finite logits).
+Weights are drawn on the GPU by torch's seeded generator (host generation at
+70B width takes about a minute per layer) and copied to the host for the
+oracle before the library packs them."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import cbinputs
+import oracle
+from cacheblend_selective_recompute_amd import api
+
+from gpu_helpers import blended_cache, check_sets, ints, rel, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _host_layer(t, shape):
+    """Oracle-layout fp32 host copies of a library-layout (unpacked) layer."""
+    qw, kvw, F = shape.q_width, shape.kv_width, shape.d_ff
+    h = lambda x: x.float().cpu().numpy()
+    qkv = h(t["w_qkv"])
+    gu = h(t["w_gate_up"])
+    return {"wq": qkv[:qw], "wk": qkv[qw:qw + kvw], "wv": qkv[qw + kvw:], "wo": h(t["w_o"]),
+            "w_gate": gu[:F], "w_up": gu[F:], "w_down": h(t["w_down"]),
+            "attn_norm": h(t["attn_norm"]), "mlp_norm": h(t["mlp_norm"])}
+
+
+def _layer_sampled(base, N, Q, k, seed, paged, n_sample=24):
+    shape = dataclasses.replace(base, n_layers=2, vocab=64)
+    T = N + Q
+    lt = cbinputs.torch_device_layer(shape, seed)
+    lw = _host_layer(lt, shape)
+    glob = cbinputs.global_weights(shape, seed)
+    m_ora = oracle.OracleModel.from_shape(shape, {"layers": [lw, lw], **glob})
+    # two shallow copies: packing replaces the matrices in each copy only
+    m_gpu = api.DeviceModel(shape, [dict(lt), dict(lt)], to_dev(glob["embed"], "bf16"),
+                            to_dev(glob["lm_head"], "bf16"), torch.ones(shape.d_model, device="cuda"))
+    del lt
+    x = cbinputs.synthetic_layer_rows(shape, T, seed=seed)
+    Kc, Vc = cbinputs.synthetic_layer_cache(shape, T, seed=seed)
+    kv = blended_cache(shape, T, paged=paged, seed=seed + 4, fill=0.0)
+    idx = kv.slots(np.arange(T))
+    kv.k[1, idx] = to_dev(Kc, "bf16")
+    kv.v[1, idx] = to_dev(Vc, "bf16")
+    xg = torch.from_numpy(x).cuda()
+    pos_out = torch.full((k,), -1, dtype=torch.int32, device="cuda")
+    dev = torch.empty(N, device="cuda")
+    api.cb_blend_layer(m_gpu, 1, kv, ints(np.arange(N)), N, Q, xg, True, k, pos_out, dev)
+    torch.cuda.synchronize()
+    gpos = pos_out.cpu().numpy()
+    assert np.all(np.diff(gpos) > 0) and gpos[0] >= 0 and gpos[-1] < N
+    # the oracle with the GPU's kept set imposed; its deviations are its own
+    rows = np.unique(np.concatenate([np.linspace(0, k - 1, n_sample).astype(np.int64),
+                                     k + np.array([0, Q // 2, Q - 1])]))
+    Kl = Kc.astype(np.float64)
+    Vl = Vc.astype(np.float64)
+    x_ora, keep, dev_ora = oracle.blend_layer(m_ora, 1, Kl, Vl, x.astype(np.float64), np.arange(N), Q, True, k,
+                                              force=gpos, out_rows=rows)
+    own = oracle.select_hkvd(dev_ora, np.arange(N), k)
+    sc = float(np.mean(np.sum(Kc.astype(np.float64) ** 2, axis=(1, 2)) +
+                       np.sum(Vc.astype(np.float64) ** 2, axis=(1, 2))))
+    frac = check_sets(gpos, own, np.arange(N), dev_ora, k, sc, "layer 1")
+    ed = rel(to_np(dev), dev_ora)
+    xo = to_np(xg[torch.from_numpy(rows).cuda()])
+    ex = rel(xo, x_ora)
+    K1, V1 = kv.logical(T)
+    K1 = to_np(K1[1])
+    V1 = to_np(V1[1])
+    written = np.concatenate([gpos, np.arange(N, T)])
+    ek = rel(K1[written], Kl[written])
+    ev = rel(V1[written], Vl[written])
+    say(f"  decision agreement {frac:.4f}, deviation rel {ed:.2e}, sampled x rows rel {ex:.2e}, "
+        f"scattered K {ek:.2e} V {ev:.2e}")
+    assert ed < 1e-2
+    assert ex < 2e-2
+    assert ek < 2e-2 and ev < 2e-2
+    untouched = np.setdiff1d(np.arange(N), gpos)
+    assert np.array_equal(K1[untouched], Kc[untouched].astype(np.float64))
+    assert np.array_equal(V1[untouched], Vc[untouched].astype(np.float64))
+
+
+def test_blend_layer_70b_width_sampled():
+    say("cb_blend_layer: 70B width, layer 1, 4096 candidates + 64 query rows, keep 614, paged")
+    _layer_sampled(cbinputs.SHAPES["llama-70b"], 4096, 64, 614, seed=5, paged=True)
+
+
+def test_blend_layer_32k_context_paged_sampled():
+    say("cb_blend_layer: 8B width, layer 1, 32768 candidates + 128 query rows, keep 4915, paged")
+    _layer_sampled(cbinputs.SHAPES["llama3-8b"], 32768, 128, 4915, seed=6, paged=True)
+
+
+def _paged_chunks(shape, wl, kvs, seed):
+    """Chunk sources whose K/V sit in private pools of 16-token blocks."""
+    out = []
+    for c, (K, V) in enumerate(kvs):
+        ln = wl.chunk_lens[c]
+        nb = (ln + 15) // 16
+        ids, n_phys = cbinputs.paged_layout(ln, 16, seed, key=1000 + c, spare_blocks=2)
+        Kp = torch.zeros((shape.n_layers, n_phys * 16, shape.n_kv_heads, shape.head_dim), dtype=K.dtype, device="cuda")
+        Vp = torch.zeros_like(Kp)
+        rows = torch.from_numpy((np.repeat(ids.astype(np.int64), 16) * 16 + np.tile(np.arange(16), nb))[:ln]).cuda()
+        Kp[:, rows] = K
+        Vp[:, rows] = V
+        out.append(api.ChunkSource(ints(wl.chunk_tokens[c]), Kp, Vp, wl.old_starts[c], wl.new_starts[c],
+                                   block_ids=ints(ids), block_size=16, layer_stride=n_phys * 16 * shape.kv_width))
+    return out
+
+
+def test_blend_full_32k_paged_properties():
+    say("blend: full 8B shape, 32 x 1024 + 128, paged source and destination, r 15% (properties)")
+    wl = cbinputs.make_workload("8b-32x1024-q128-paged", seed=0)
+    shape = wl.shape
+    m = api.DeviceModel.from_tensors(shape, cbinputs.torch_device_weights(shape, 0))
+    chunks = _paged_chunks(shape, wl, cbinputs.torch_device_chunk_kv(shape, wl.chunk_lens, 0), 0)
+    T, N = wl.n_total, wl.n_ctx
+    kv = blended_cache(shape, T, paged=True, seed=3, fill=0.0)
+    ks, ch = wl.schedule()
+    logits = torch.empty(shape.vocab, device="cuda")
+    hk = torch.full((shape.n_layers, N), -1, dtype=torch.int32, device="cuda")
+    api.cb_blend_prefill(m, chunks, ints(wl.query_tokens), api.BlendParams(ks, ch), kv, logits, hk)
+    torch.cuda.synchronize()
+    assert torch.isfinite(logits).all()
+    h = hk.cpu().numpy()
+    assert np.array_equal(h[0], np.arange(N))
+    prev = set(range(N))
+    for l in range(1, shape.n_layers):
+        s = h[l, :ks[l]]
+        assert np.all(np.diff(s) > 0) and s.min() >= 0 and s.max() < N
+        assert set(s.tolist()) <= prev
+        prev = set(s.tolist())
+    ref = blended_cache(shape, T, paged=True, seed=3, fill=0.0)
+    api.cb_rerope_k(api.make_cfg(shape), chunks, ref, api.CB_COPY_V)
+    torch.cuda.synchronize()
+    for l in (0, 1, 16, 31):
+        Kg, Vg = kv.k[l][kv.slots(np.arange(T))], kv.v[l][kv.slots(np.arange(T))]
+        Kr, Vr = ref.k[l][ref.slots(np.arange(T))], ref.v[l][ref.slots(np.arange(T))]
+        kept = h[l, :ks[l]] if l > 0 else np.zeros(0, dtype=np.int64)
+        out = np.setdiff1d(np.arange(N), kept)
+        assert torch.equal(Kg[out], Kr[out]) and torch.equal(Vg[out], Vr[out]), f"layer {l}: untouched rows changed"
+        if l > 0:
+            diff = (Kg[kept] != Kr[kept]).flatten(1).any(dim=1)
+            assert bool(diff.all()), f"layer {l}: a kept row still holds the cached K"
+        # the suffix rows hold fresh, finite K/V
+        assert torch.isfinite(Kg[N:].float()).all() and (Kg[N:] != 0).flatten(1).any(dim=1).all()

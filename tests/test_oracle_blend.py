@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import cbinputs
-from oracle import (OracleModel, assemble_blended, blend_prefill, blend_prefill_masked,
+from oracle import (OracleModel, assemble_blended, blend_layer, blend_prefill, blend_prefill_masked,
                     chunk_prefill, flop_count, full_prefill, full_reuse_prefill, kv_deviation,
                     store_round)
 
@@ -209,3 +209,26 @@ def test_kv_bytes_per_token_golden():
         b = case["layers"] * 2 * case["kv_heads"] * case["head_dim"] * case["bytes_per_element"]
         assert b == case["bytes_per_token"]
     assert cbinputs.SHAPES["llama3-8b"].kv_bytes_per_token() == 128 * 1024
+
+
+def test_blend_layer_out_rows_are_rows_of_the_full_call():
+    # a row's output depends on its own hidden state and the updated cache
+    # only, so computing a subset must return exactly those rows
+    w = _sharpen(cbinputs.model_weights(GQA, 9))
+    m = OracleModel.from_shape(GQA, w)
+    rng = np.random.default_rng(9)
+    N, Q, k = 40, 5, 9
+    T = N + Q
+    cand = np.sort(rng.choice(N, 30, replace=False))
+    Kl = rng.standard_normal((T, GQA.n_kv_heads, GQA.head_dim))
+    Vl = rng.standard_normal((T, GQA.n_kv_heads, GQA.head_dim))
+    x = rng.standard_normal((len(cand) + Q, GQA.d_model))
+    full = blend_layer(m, 1, Kl.copy(), Vl.copy(), x, cand, Q, True, k)
+    rows = np.array([k + Q - 1, 0, 4, k, k - 1])
+    K2, V2 = Kl.copy(), Vl.copy()
+    part = blend_layer(m, 1, K2, V2, x, cand, Q, True, k, out_rows=rows)
+    assert np.array_equal(part[1], full[1])
+    np.testing.assert_allclose(part[0], full[0][rows], rtol=1e-12, atol=1e-12)
+    K3, V3 = Kl.copy(), Vl.copy()
+    blend_layer(m, 1, K3, V3, x, cand, Q, True, k)
+    assert np.array_equal(K2, K3) and np.array_equal(V2, V3)

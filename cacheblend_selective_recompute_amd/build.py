@@ -30,6 +30,11 @@ COMMON = [
 ]
 
 
+# per-source additions: the attention kernels take maxima of scores that are finite
+# or -inf (masked keys), never NaN, so NaN quieting around every max is dropped
+EXTRA = {"cb_attention.hip": ["-fno-honor-nans"]}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -43,7 +48,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

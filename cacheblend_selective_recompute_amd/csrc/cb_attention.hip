@@ -535,6 +535,267 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_dma_kernel(AttnArgs
   }
 }
 
+// Leaner variant of the LDS-DMA kernel, for pages of 16 or more keys (a power of
+// two).  Per block and wave it trims the vector work that otherwise outweighs
+// the matrix work:
+//  * row sums of P come from the matrix cores (an all-ones A operand against the
+//    same P^T fragments as the PV product), so every lane ends with the full sum
+//    of its query column and no adds or shuffles are spent on them;
+//  * each lane compares its own block maximum with the row's threshold
+//    (reference max + 8, in score units) and the wave votes; only when some score
+//    crosses it does the wave reduce the block maxima across lanes and move the
+//    reference (rescaling O and the sums);
+//  * the 16 keys a wave copies share a page, so one block-table entry per wave
+//    and block gives every copy address, and that entry is fetched a block ahead.
+// ---------------------------------------------------------------------------
+template <int G, int NG>
+__global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs a, int n_splits, int ksplit) {
+  constexpr int DH = 128;
+  constexpr int QROWS = 64 * NG;
+  constexpr int QT = QROWS / G;
+  constexpr int kBlk = KVB * DH * 2;     // bytes of one K (or V) block: 64 rows x 256 B
+  __shared__ __attribute__((aligned(1024))) uint8_t kv[2][2 * kBlk];   // [stage][K | V]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int n_tiles = (a.R + QT - 1) / QT;
+  const int split = blockIdx.x % n_splits;
+  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x / n_splits);   // longest first
+  const int kvh = blockIdx.y;
+  const int t0 = tile * QT;
+  const int t_last = min(t0 + QT, a.R) - 1;
+  const int kv_end = a.rowpos[t_last] + 1;
+  const int j_begin = split * ksplit;
+  const int j_end = min(kv_end, j_begin + ksplit);
+  if (j_begin >= j_end) return;
+
+  const int kgrp = lane >> 4;
+  int qtok[NG], qhead[NG], qpos[NG];
+  bool qvalid[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int qr = (wid * NG + g) * 16 + (lane & 15);
+    qtok[g] = t0 + (qr % QT);
+    qhead[g] = kvh * G + qr / QT;
+    qvalid[g] = qtok[g] < a.R;
+    qpos[g] = qvalid[g] ? a.rowpos[qtok[g]] : kv_end - 1;
+  }
+  const int qpos_min = a.rowpos[t0];
+  bf16x8_t qf[NG][DH / 32];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const bf16_t* qp = static_cast<const bf16_t*>(a.q) + static_cast<int64_t>(qvalid[g] ? qtok[g] : t_last) * a.ldq +
+                       qhead[g] * DH + 8 * kgrp;
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) qf[g][ks] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * ks);
+  }
+  f32x4_t o[NG][DH / 16];
+  f32x4_t lsum[NG];                      // every element: the running sum of the lane's query column
+  float m_run[NG], m_neg[NG], thr[NG];   // reference max (exp2 units), its negation (0 if none), threshold
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t) o[g][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    lsum[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[g] = -INFINITY;
+    m_neg[g] = 0.f;
+    thr[g] = -INFINITY;
+  }
+  const float sc = a.scale * kLog2e;
+  const float inv_sc = 1.0f / sc;
+  bf16x8_t ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<__bf16>(1.0f);
+
+  const int sh = a.cache.bs_shift;       // >= 4: the launcher checks it
+  const int width = a.n_kv_heads * DH;
+  const bf16_t* kbase = static_cast<const bf16_t*>(a.cache.k) + static_cast<int64_t>(a.layer) * a.cache.layer_stride;
+  const bf16_t* vbase = static_cast<const bf16_t*>(a.cache.v) + static_cast<int64_t>(a.layer) * a.cache.layer_stride;
+  // the launcher guarantees the layer's pool spans < 2^31 bytes
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(kbase), static_cast<short>(0),
+                                                                      0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(vbase), static_cast<short>(0),
+                                                                      0x7fffffff, 0x00020000);
+  // copy u (0..3) of this wave: key 16 wid + 4 u + lane / 16 of the block, LDS slot lane % 16 of
+  // the key row; K slot p holds chunk p ^ (key % 16), V slot p chunk p ^ 2 (key % 8)
+  const int sub = lane >> 4;
+  const int slot = lane & 15;
+  int kx[4], vx[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int kr = 4 * u + sub;          // key within the wave's 16
+    kx[u] = kr * width * 2 + ((slot ^ kr) << 4);
+    vx[u] = kr * width * 2 + ((slot ^ ((kr & 7) << 1)) << 4);
+  }
+  const uint32_t ldsw = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(&kv[0][0]))) +
+      wid * 4096);
+  const int pmask = (1 << sh) - 1;
+  auto page_of = [&](int jb) -> int {   // block-table entry of this wave's 16 keys of block jb
+    const int k0 = jb + 16 * wid;
+    return k0 < j_end ? a.cache.bt[k0 >> sh] : 0;
+  };
+  int pe = page_of(j_begin);
+  auto issue = [&](int jb, int stage) {
+    const int k0 = jb + 16 * wid;
+    const int rowb = ((pe << sh) + (k0 & pmask)) * width * 2 + kvh * DH * 2;
+    pe = page_of(jb + KVB);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = k0 + 4 * u + sub < j_end;
+      const int ko = ok ? rowb + kx[u] : static_cast<int>(0x80000000u);   // past the range: zeros
+      const int vo = ok ? rowb + vx[u] : static_cast<int>(0x80000000u);
+      const uint32_t dst = ldsw + stage * (2 * kBlk) + u * 1024;
+      attn_copy(dst, rk, ko);
+      attn_copy(dst + kBlk, rv, vo);
+    }
+  };
+
+  // per-lane LDS byte offsets of the fragment reads inside a stage (block-relative keys):
+  // K fragment (t, ks): key 16 t + lane % 16, chunk 4 ks + kgrp at slot chunk ^ (key % 16);
+  // V^T source of (dt, s2, h): key 32 s2 + 16 h + 4 kgrp + sl / 4, dims 16 dt + 4 (sl % 4)
+  int koff[DH / 32], voffs[DH / 16];
+  {
+    const int kk = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks) koff[ks] = kk * 256 + (((4 * ks + kgrp) ^ kk) << 4);
+    const int sl = lane & 15;
+    const int vkey = 4 * kgrp + (sl >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) {
+      const int d = 16 * dt + 4 * (sl & 3);
+      voffs[dt] = vkey * 256 + (((d >> 3) ^ ((vkey & 7) << 1)) << 4) + ((d & 7) << 1);
+    }
+  }
+  auto block = [&](int j0, int stage) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of block j0 have landed
+    __syncthreads();                      // ... everyone's; block j0 - 64 is no longer read
+    if (j0 + KVB < j_end) issue(j0 + KVB, stage ^ 1);
+    const uint8_t* Kb = kv[stage];
+    const uint8_t* Vb = kv[stage] + kBlk;
+
+    f32x4_t s[NG][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) s[g][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DH / 32; ++ks) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(Kb + koff[ks] + t * (16 * 256));
+#pragma unroll
+        for (int g = 0; g < NG; ++g) s[g][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[g][ks], s[g][t], 0, 0, 0);
+      }
+    }
+    const bool edge = j0 + KVB - 1 > qpos_min || j0 + KVB > j_end;
+    float mx[NG];
+    bool over = false;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (edge) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = j0 + 16 * t + 4 * kgrp + i;
+            if (key > qpos[g] || key >= j_end) s[g][t][i] = -INFINITY;
+          }
+      }
+      float m = fmaxf(fmaxf(s[g][0][0], s[g][0][1]), fmaxf(s[g][0][2], s[g][0][3]));
+#pragma unroll
+      for (int t = 1; t < 4; ++t) m = fmaxf(fmaxf(m, fmaxf(s[g][t][0], s[g][t][1])), fmaxf(s[g][t][2], s[g][t][3]));
+      mx[g] = m;
+      over |= m > thr[g];
+    }
+    // the reference max of a row moves only when a score exceeds it by more than 2^8 in
+    // exp2 units, so every exp2 below stays <= 256 and rescaling is rare
+    if (__any(over)) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        float mb = mx[g];
+        mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+        const float m_blk = mb * sc;
+        if (m_blk > m_run[g] + 8.f) {
+          const float alpha = (m_run[g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - m_blk);
+          lsum[g] *= alpha;
+#pragma unroll
+          for (int t = 0; t < DH / 16; ++t) o[g][t] *= alpha;
+          m_run[g] = m_blk;
+          m_neg[g] = -m_blk;
+          thr[g] = (m_blk + 8.f) * inv_sc;
+        }
+      }
+    }
+    bf16x8_t pf[NG][2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float p4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p4[i] = __builtin_amdgcn_exp2f(fmaf(s[g][t][i], sc, m_neg[g]));
+        const bf16x2_t lo = __builtin_convertvector(f32x2_t{p4[0], p4[1]}, bf16x2_t);
+        const bf16x2_t hi = __builtin_convertvector(f32x2_t{p4[2], p4[3]}, bf16x2_t);
+        pf[g][t >> 1][(t & 1) * 4 + 0] = lo[0];
+        pf[g][t >> 1][(t & 1) * 4 + 1] = lo[1];
+        pf[g][t >> 1][(t & 1) * 4 + 2] = hi[0];
+        pf[g][t >> 1][(t & 1) * 4 + 3] = hi[1];
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) lsum[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[g][s2], lsum[g], 0, 0, 0);
+    }
+
+    // O^T += V^T P^T (fragment layout as in attn_dma_kernel)
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        s16x4_t half[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint8_t* src = Vb + voffs[dt] + (32 * s2 + 16 * h) * 256;
+          half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t*)(const __attribute__((address_space(3))) void*)(src));
+        }
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int g = 0; g < NG; ++g) o[g][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[g][s2], o[g][dt], 0, 0, 0);
+      }
+    }
+  };
+  issue(j_begin, 0);
+  for (int j0 = j_begin; j0 < j_end; j0 += 2 * KVB) {
+    block(j0, 0);
+    if (j0 + KVB < j_end) block(j0 + KVB, 1);
+  }
+
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (!qvalid[g]) continue;
+    const float l_tot = lsum[g][0];
+    if (n_splits == 1) {
+      const float inv = 1.0f / l_tot;
+      bf16_t* ob = static_cast<bf16_t*>(a.o);
+      const int KO = a.n_q_heads * DH;
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) {
+        uint2 w;
+        w.x = static_cast<uint32_t>(f2bf(o[g][dt][0] * inv)) | (static_cast<uint32_t>(f2bf(o[g][dt][1] * inv)) << 16);
+        w.y = static_cast<uint32_t>(f2bf(o[g][dt][2] * inv)) | (static_cast<uint32_t>(f2bf(o[g][dt][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(ob + pk_off(qtok[g], qhead[g] * DH + 16 * dt + 4 * kgrp, KO)) = w;
+      }
+    } else {
+      const int64_t pr = (static_cast<int64_t>(split) * a.R + qtok[g]) * a.n_q_heads + qhead[g];
+      float* op = a.part_o + pr * DH;
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt)
+        *reinterpret_cast<float4*>(op + 16 * dt + 4 * kgrp) = make_float4(o[g][dt][0], o[g][dt][1], o[g][dt][2], o[g][dt][3]);
+      if (kgrp == 0) a.part_ml[pr] = make_float2(m_run[g], l_tot);
+    }
+  }
+}
+
 // Merge the split-KV partials of one (row, q head) per wave, in split order.
 template <int DH>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_splits, int ksplit, int QT) {
@@ -628,7 +889,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int DH, int G, int NG, bool DMA>
+template <int DH, int G, int NG, int KIND>   // KIND 0 register-staged, 1 LDS-DMA, 2 lean LDS-DMA
 hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   constexpr int QT = 64 * NG / G;
   const int n_tiles = (a.R + QT - 1) / QT;
@@ -643,7 +904,9 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   }
   const int ksplit = ((kv_blocks + n_splits - 1) / n_splits) * KVB;
   const dim3 grid(n_tiles * n_splits, a.n_kv_heads);
-  if (DMA) {
+  if constexpr (KIND == 2) {
+    attn_fa_kernel<G, NG><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
+  } else if (KIND == 1) {
     // workgroups stage the table entries of their key range in LDS when they fit
     if (ksplit / a.cache.bs + 2 <= 1024)
       attn_dma_kernel<G, true, NG><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
@@ -662,16 +925,19 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
 }
 
 // variant: 1 / 2 = register-staged kernel with 1 / 2 query groups per wave,
-// 3 / 4 = LDS-DMA kernel (head_dim 128, a layer's pool below 2 GiB) with 1 / 2
+// 3 / 4 = LDS-DMA kernel (head_dim 128, a layer's pool below 2 GiB) with 1 / 2,
+// 5 / 6 = lean LDS-DMA kernel (as 3 / 4, pages a power of two >= 16 keys) with 1 / 2
 template <int DH, int G>
 hipError_t run_bf16_variant(const AttnArgs& a, int variant, hipStream_t s) {
   if constexpr (DH == 128) {
     const bool dma_ok = a.cache.layer_stride * 2 < (int64_t(1) << 31);
-    if (variant == 3 && dma_ok) return run_bf16<DH, G, 1, true>(a, s);
-    if (variant == 4 && dma_ok) return run_bf16<DH, G, 2, true>(a, s);
+    const bool fa_ok = dma_ok && a.cache.bs_shift >= 4;   // pages of 16 or more keys, a power of two
+    if (variant >= 5 && fa_ok) return variant == 5 ? run_bf16<DH, G, 1, 2>(a, s) : run_bf16<DH, G, 2, 2>(a, s);
+    if (variant >= 3 && dma_ok) return variant % 2 ? run_bf16<DH, G, 1, 1>(a, s) : run_bf16<DH, G, 2, 1>(a, s);
   }
-  if (variant == 1) return run_bf16<DH, G, 1, false>(a, s);
-  return run_bf16<DH, G, 2, false>(a, s);
+  // a variant whose conditions do not hold falls back to the next simpler kernel
+  if (variant % 2) return run_bf16<DH, G, 1, 0>(a, s);
+  return run_bf16<DH, G, 2, 0>(a, s);
 }
 
 }  // namespace
@@ -701,7 +967,7 @@ hipError_t launch_attention_ng(cb_dtype dt, const AttnArgs& a_in, int ng, hipStr
 }
 
 hipError_t launch_attention(cb_dtype dt, const AttnArgs& a, hipStream_t s) {
-  return launch_attention_ng(dt, a, 4, s);
+  return launch_attention_ng(dt, a, 6, s);
 }
 
 }  // namespace cb

@@ -560,9 +560,13 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs 
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int n_tiles = (a.R + QT - 1) / QT;
-  const int split = blockIdx.x % n_splits;
-  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x / n_splits);   // longest first
-  const int kvh = blockIdx.y;
+  // one-dimensional grid over (KV head, tile, split): each XCD takes a contiguous run
+  // of work items, i.e. mostly one KV head, whose K/V stream then stays in its L2
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_head = n_tiles * n_splits;
+  const int kvh = w / per_head;
+  const int split = (w % per_head) % n_splits;
+  const int tile = n_tiles - 1 - (w % per_head) / n_splits;   // longest first
   const int t0 = tile * QT;
   const int t_last = min(t0 + QT, a.R) - 1;
   const int kv_end = a.rowpos[t_last] + 1;
@@ -905,7 +909,7 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   const int ksplit = ((kv_blocks + n_splits - 1) / n_splits) * KVB;
   const dim3 grid(n_tiles * n_splits, a.n_kv_heads);
   if constexpr (KIND == 2) {
-    attn_fa_kernel<G, NG><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
+    attn_fa_kernel<G, NG><<<dim3(n_tiles * n_splits * a.n_kv_heads), 256, 0, s>>>(a, n_splits, ksplit);
   } else if (KIND == 1) {
     // workgroups stage the table entries of their key range in LDS when they fit
     if (ksplit / a.cache.bs + 2 <= 1024)

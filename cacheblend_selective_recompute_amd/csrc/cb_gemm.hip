@@ -38,7 +38,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int BK = 32;          // k columns per stage
 constexpr int BN = 256;         // block tile columns (B rows)
 constexpr int kThreads = 256;
-constexpr int kXcd = 8;
 
 // s_waitcnt with only the vector-memory counter constrained (n outstanding allowed)
 #define CB_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
@@ -56,14 +55,6 @@ struct Tile {
   static constexpr int H1 = DQ - H0;              // ... and during the first half of the next
   static constexpr int WGS_PER_CU = BM == 256 ? 1 : 2;
 };
-
-// Linear block id -> logical tile id such that the hardware's round-robin
-// dispatch over XCDs gives each XCD a contiguous range of logical tiles.
-__device__ __forceinline__ int xcd_remap(int b, int nb) {
-  const int q = nb / kXcd, r = nb % kXcd;
-  const int x = b % kXcd, i = b / kXcd;
-  return x * q + min(x, r) + i;
-}
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 

@@ -50,6 +50,17 @@ inline int32_t block_shift(int32_t bs) {
   return (1 << sh) == bs ? sh : -1;
 }
 
+// The hardware hands workgroups of one launch to the 8 XCDs (each with its own
+// L2) in round-robin order of their linear id.  xcd_remap turns a linear id into
+// a logical work index such that every XCD receives one contiguous range of work
+// indices, so neighbouring work (sharing operands) shares an L2.
+constexpr int kXcd = 8;
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  const int q = nb / kXcd, r = nb % kXcd;
+  const int x = b % kXcd, i = b / kXcd;
+  return x * q + min(x, r) + i;
+}
+
 // Token row of logical position `pos` in one layer of a paged pool.
 __device__ __forceinline__ int64_t paged_row(const int32_t* bt, int32_t bs, int32_t pos) {
   if (bt == nullptr) return pos;

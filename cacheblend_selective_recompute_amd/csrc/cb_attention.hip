@@ -906,6 +906,9 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
     n_splits = std::min(n_splits, kv_blocks);
     if (static_cast<int64_t>(n_splits) * a.R * a.n_q_heads > kAttnPartialRows) n_splits = 1;
   }
+  if (a.n_splits_req > 0 && a.part_o != nullptr &&
+      static_cast<int64_t>(a.n_splits_req) * a.R * a.n_q_heads <= kAttnPartialRows)
+    n_splits = std::min(a.n_splits_req, kv_blocks);
   const int ksplit = ((kv_blocks + n_splits - 1) / n_splits) * KVB;
   const dim3 grid(n_tiles * n_splits, a.n_kv_heads);
   if constexpr (KIND == 2) {

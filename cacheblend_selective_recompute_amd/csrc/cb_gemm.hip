@@ -70,8 +70,17 @@ __device__ __forceinline__ void copy_block(uint32_t lds, __amdgpu_buffer_rsrc_t 
 
 // B is fragment-major with virtual rows: for SWIGLU, 32-row block 2b holds gate
 // features [32b, 32b+32) and block 2b+1 the matching up features.
+//
+// Work of one launch: m_tiles x n_tiles output tiles.  Without SPLIT every
+// workgroup computes one tile over all of K.  With SPLIT the tiles of the first
+// dp_cols tile columns still do (dp_cols * m_tiles workgroups, launched first),
+// and each tile of the remaining columns is cut into `splits` pieces of kps
+// columns of K whose fp32 partials go to g.part as [split][M][W], W = the virtual
+// columns past dp_cols * BN; a reduction kernel then sums them in split order
+// and applies the epilogue.  dp_cols = 0 is plain split-K.
 template <int EPI, int BM, bool SPLIT>
-__global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kernel(GemmArgs g, int splits, int kps) {
+__global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kernel(GemmArgs g, int splits, int kps,
+                                                                                  int dp_cols) {
   using T = Tile<BM>;
   constexpr int FM = T::FM, NS = T::NS, DA = T::DA, DQ = T::DQ, H0 = T::H0, H1 = T::H1;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * T::kStage];
@@ -82,15 +91,27 @@ __global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kern
   const int wm = wid >> 1, wn = wid & 1;
 
   const int m_tiles = (g.M + BM - 1) / BM;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = t % m_tiles;
-  const int rest = t / m_tiles;
-  const int split = rest % splits;
-  const int nt = rest / splits;
+  // whole tiles first, then the pieces; each range is spread over the XCDs in
+  // contiguous runs so neighbouring tiles (sharing B columns) share an L2
+  const int n_dp = SPLIT ? m_tiles * dp_cols : static_cast<int>(gridDim.x);
+  const int b = blockIdx.x;
+  const bool part = SPLIT && b >= n_dp;
+  int mt, nt, split = 0;
+  if (!part) {
+    const int t = xcd_remap(b, n_dp);
+    mt = t % m_tiles;
+    nt = t / m_tiles;
+  } else {
+    const int r = xcd_remap(b - n_dp, static_cast<int>(gridDim.x) - n_dp);
+    mt = r % m_tiles;
+    const int rest = r / m_tiles;
+    split = rest % splits;
+    nt = dp_cols + rest / splits;
+  }
   const int m0 = mt * BM;
   const int n0 = nt * BN;                              // first virtual B row of the tile
-  const int kbeg = split * kps;
-  const int nk = (min(g.K, kbeg + kps) - kbeg) / BK;   // >= 1 (host drops empty splits)
+  const int kbeg = part ? split * kps : 0;
+  const int nk = ((part ? min(g.K, kbeg + kps) : g.K) - kbeg) / BK;   // >= 1 (host drops empty splits)
 
   const int kbr = g.K >> 4;                            // 16-column blocks per row block
   const int b_rows = (EPI == EPI_SWIGLU) ? 2 * g.N : g.N;
@@ -218,7 +239,20 @@ __global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kern
       for (int v = 0; v < 16; ++v)
         stg[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * EP + j * 32 + (lane & 31)] = acc[i][j][v];
     __builtin_amdgcn_wave_barrier();
-    if constexpr (EPI == EPI_SWIGLU && !SPLIT) {
+    if (part) {
+      const int c_part = dp_cols * BN;
+      const int64_t wpart = b_rows - c_part;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int r = p * 2 + (lane >> 5);
+        const int c = (lane & 31) * 4;
+        const int row = row0 + i * 32 + r;
+        const int col = col0 + c;
+        if (row < g.M && col < b_rows)
+          *reinterpret_cast<float4*>(g.part + (static_cast<int64_t>(split) * g.M + row) * wpart + (col - c_part)) =
+              *reinterpret_cast<const float4*>(stg + r * EP + c);
+      }
+    } else if constexpr (EPI == EPI_SWIGLU) {
       // gate columns [0,32) and [64,96) of the block pair with up columns +32
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
@@ -244,9 +278,7 @@ __global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kern
         const int row = row0 + i * 32 + r;
         const int col = col0 + c;
         if (row >= g.M || col >= g.N) continue;
-        if constexpr (SPLIT) {
-          *reinterpret_cast<float4*>(g.part + (static_cast<int64_t>(split) * g.M + row) * g.N + col) = x;
-        } else if constexpr (EPI == EPI_RESID) {
+        if constexpr (EPI == EPI_RESID) {
           const int rr = g.resid_rows ? g.resid_rows[row] : row;
           const float4 rv = *reinterpret_cast<const float4*>(g.resid + static_cast<int64_t>(rr) * g.ld_resid + col);
           *reinterpret_cast<float4*>(static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + col) =
@@ -292,17 +324,42 @@ __global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kern
   }
 }
 
-// Split-K reduction in fixed split order, then the epilogue (4 columns per thread).
+// Split-K reduction in fixed split order, then the epilogue, over the virtual
+// columns from c_part on (4 output columns per thread).  SWIGLU pairs gate
+// column 64 k + j with up column 64 k + 32 + j into feature 32 k + j.
 template <int EPI>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int splits) {
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int splits, int c_part) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int n4 = g.N / 4;
+  const int b_rows = (EPI == EPI_SWIGLU) ? 2 * g.N : g.N;
+  const int64_t wpart = b_rows - c_part;
+  if constexpr (EPI == EPI_SWIGLU) {
+    const int f4 = (g.N - c_part / 2) / 4;             // output feature quads per row
+    if (idx >= static_cast<int64_t>(g.M) * f4) return;
+    const int row = static_cast<int>(idx / f4);
+    const int fl = static_cast<int>(idx % f4) * 4;     // feature past c_part / 2
+    const int gc = (fl >> 5) * 64 + (fl & 31);         // its gate column past c_part
+    float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
+    for (int sp = 0; sp < splits; ++sp) {
+      const float* pr = g.part + (static_cast<int64_t>(sp) * g.M + row) * wpart + gc;
+      const float4 a = *reinterpret_cast<const float4*>(pr);
+      const float4 u = *reinterpret_cast<const float4*>(pr + 32);
+      gs.x += a.x; gs.y += a.y; gs.z += a.z; gs.w += a.w;
+      us.x += u.x; us.y += u.y; us.z += u.z; us.w += u.w;
+    }
+    uint2 w;
+    w.x = static_cast<uint32_t>(f2bf(silu(gs.x) * us.x)) | (static_cast<uint32_t>(f2bf(silu(gs.y) * us.y)) << 16);
+    w.y = static_cast<uint32_t>(f2bf(silu(gs.z) * us.z)) | (static_cast<uint32_t>(f2bf(silu(gs.w) * us.w)) << 16);
+    *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.C) + pk_off(row, c_part / 2 + fl, static_cast<int>(g.ldc))) = w;
+    return;
+  }
+  const int64_t n4 = wpart / 4;
   if (idx >= static_cast<int64_t>(g.M) * n4) return;
   const int row = static_cast<int>(idx / n4);
-  const int col = static_cast<int>(idx % n4) * 4;
+  const int lc = static_cast<int>(idx % n4) * 4;
+  const int col = c_part + lc;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int sp = 0; sp < splits; ++sp) {
-    const float4 p = *reinterpret_cast<const float4*>(g.part + (static_cast<int64_t>(sp) * g.M + row) * g.N + col);
+    const float4 p = *reinterpret_cast<const float4*>(g.part + (static_cast<int64_t>(sp) * g.M + row) * wpart + lc);
     s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
   }
   float v[4] = {s.x, s.y, s.z, s.w};
@@ -369,24 +426,32 @@ __device__ __forceinline__ float wave_sum64(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs g, int splits) {
+// Columns below c_part were finished by whole-tile workgroups of the same GEMM
+// (resid added) and are read back from C.
+__global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs g, int splits, int c_part) {
   __shared__ float red[4];
   const int row = blockIdx.x;
   const int rr = g.resid_rows ? g.resid_rows[row] : row;
+  const int64_t wpart = g.N - c_part;
   float4 v[kNormChunks];
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < kNormChunks; ++c) {
     const int e = threadIdx.x * 4 + c * 1024;
     if (e < g.N) {
-      float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int sp = 0; sp < splits; ++sp) {
-        const float4 p = *reinterpret_cast<const float4*>(g.part + (static_cast<int64_t>(sp) * g.M + row) * g.N + e);
-        s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+      float* cp = static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + e;
+      if (e < c_part) {
+        v[c] = *reinterpret_cast<const float4*>(cp);
+      } else {
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int sp = 0; sp < splits; ++sp) {
+          const float4 p = *reinterpret_cast<const float4*>(g.part + (static_cast<int64_t>(sp) * g.M + row) * wpart + (e - c_part));
+          s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+        }
+        const float4 r = *reinterpret_cast<const float4*>(g.resid + static_cast<int64_t>(rr) * g.ld_resid + e);
+        v[c] = make_float4(r.x + s.x, r.y + s.y, r.z + s.z, r.w + s.w);
+        *reinterpret_cast<float4*>(cp) = v[c];
       }
-      const float4 r = *reinterpret_cast<const float4*>(g.resid + static_cast<int64_t>(rr) * g.ld_resid + e);
-      v[c] = make_float4(r.x + s.x, r.y + s.y, r.z + s.z, r.w + s.w);
-      *reinterpret_cast<float4*>(static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + e) = v[c];
       ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
     }
   }
@@ -513,18 +578,16 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 }
 
 template <int EPI, int BM, bool SPLIT>
-hipError_t launch_cfg(const GemmArgs& a, int tiles, int splits, int kps, hipStream_t s) {
-  gemm_bf16_kernel<EPI, BM, SPLIT><<<tiles * splits, kThreads, 0, s>>>(a, splits, kps);
+hipError_t launch_cfg(int wgs, const GemmArgs& a, int splits, int kps, int dp_cols, hipStream_t s) {
+  gemm_bf16_kernel<EPI, BM, SPLIT><<<wgs, kThreads, 0, s>>>(a, splits, kps, dp_cols);
   return hipGetLastError();
 }
 
 inline int bm_of(int cfg) { return cfg == GEMM_CFG_256 ? 256 : 128; }
 
-inline int tiles_of(const GemmArgs& a, int epi, int bm) {
-  const int mt = (a.M + bm - 1) / bm;
-  const int rows = (epi == EPI_SWIGLU) ? 2 * a.N : a.N;
-  return mt * ((rows + BN - 1) / BN);
-}
+inline int b_rows_of(const GemmArgs& a, int epi) { return (epi == EPI_SWIGLU) ? 2 * a.N : a.N; }
+inline int m_tiles_of(const GemmArgs& a, int bm) { return (a.M + bm - 1) / bm; }
+inline int n_tiles_of(const GemmArgs& a, int epi) { return (b_rows_of(a, epi) + BN - 1) / BN; }
 
 // k columns per split (a multiple of BK) and the number of non-empty splits
 inline void split_k(int K, int splits, int* kps, int* eff) {
@@ -535,54 +598,105 @@ inline void split_k(int K, int splits, int* kps, int* eff) {
 }
 
 // Cost model, calibrated on the GEMM microbenchmark with random bf16 data at the
-// 8B blend shapes.  A round of workgroups on b CUs runs at a per-workgroup rate
-// that rises as fewer CUs are busy (the chip is power-limited under MFMA load):
-// 256-row tiles (one per CU) ~5.0 TFLOP/s x (256/b)^0.4; 128-row tiles two per CU
-// ~2.6 each, one per CU ~3.9 x (256/b)^0.4 (the gain capped at 1.25).  The fixed-order reduction moves the
-// fp32 partials once (write + read) at ~8 TB/s plus a launch.
+// 8B blend shapes.  Workgroups run at a per-workgroup rate that rises as fewer
+// CUs are busy (the chip is power-limited under MFMA load): 256-row tiles (one
+// per CU) ~5.0 TFLOP/s x (256/b)^0.4 on b busy CUs; 128-row tiles two per CU ~2.6
+// each, one per CU ~3.9 x (256/b)^0.4 (the gain capped at 1.25).  The fixed-order
+// reduction moves the fp32 partials once (write + read) at ~8 TB/s plus a launch.
 inline double busy_scale(int64_t b) { return b >= 256 ? 1.0 : fmin(1.25, pow(256.0 / static_cast<double>(b), 0.4)); }
 
-inline double est_time(const GemmArgs& a, int epi, int cfg, int splits) {
+inline double wg_rate(int bm, int64_t wgs) {   // FLOP/s of one workgroup while `wgs` run at once
+  if (bm == 256) return 5.0e12 * busy_scale(std::min<int64_t>(wgs, 256));
+  return wgs > 256 ? 2.6e12 : 3.9e12 * busy_scale(wgs);
+}
+
+// Whole tiles (nk k-steps each) are dispatched first, in full rounds of S
+// workgroups; the r left over run beside the pieces (pk steps each), whose
+// slots meanwhile take further pieces; what is left of the pieces then runs in
+// rounds of S.
+inline double est_time(const GemmArgs& a, int epi, int cfg, int splits, int dp_cols) {
   const int bm = bm_of(cfg);
   int kps, eff;
   split_k(a.K, splits, &kps, &eff);
-  const int64_t wgs = static_cast<int64_t>(tiles_of(a, epi, bm)) * eff;
-  const double flop_wg = 2.0 * bm * BN * kps;
-  double tm = 0.0;
-  if (bm == 256) {
-    const int64_t full = wgs / 256, rem = wgs % 256;
-    tm = static_cast<double>(full) * flop_wg / 5.0e12;
-    if (rem > 0) tm += flop_wg / (5.0e12 * busy_scale(rem));
-  } else {
-    const int64_t full = wgs / 512, rem = wgs % 512;
-    tm = static_cast<double>(full) * flop_wg / 2.6e12;
-    if (rem > 256) tm += flop_wg / 2.6e12;
-    else if (rem > 0) tm += flop_wg / (3.9e12 * busy_scale(rem));
+  const int64_t mtl = m_tiles_of(a, bm), ntl = n_tiles_of(a, epi);
+  const int64_t dpc = eff > 1 ? std::min<int64_t>(dp_cols, ntl) : ntl;
+  const int64_t S = bm == 256 ? 256 : 512;
+  const double sf = 2.0 * bm * BN * BK;            // FLOP of one k-step of a workgroup
+  const int64_t nk = a.K / BK, pk = kps / BK;
+  const int64_t n_dp = mtl * dpc, np = mtl * (ntl - dpc) * eff;
+  const int64_t r = n_dp % S;
+  double tm = static_cast<double>(n_dp / S) * nk * sf / wg_rate(bm, S);
+  int64_t left = np;
+  if (r > 0) {
+    tm += nk * sf / wg_rate(bm, std::min(S, r + np));
+    left -= std::min(left, (S - r) * (nk / pk));
   }
-  if (eff > 1) tm += static_cast<double>(eff) * a.M * a.N * 8.0 / 8e12 + 3e-6;
+  tm += static_cast<double>(left / S) * pk * sf / wg_rate(bm, S);
+  if (left % S) tm += pk * sf / wg_rate(bm, left % S);
+  if (eff > 1) tm += static_cast<double>(eff) * a.M * (b_rows_of(a, epi) - dpc * BN) * 8.0 / 8e12 + 3e-6;
   return tm;
+}
+
+inline bool part_fits(const GemmArgs& a, int epi, int eff, int dp_cols) {
+  return a.part != nullptr &&
+         static_cast<int64_t>(eff) * a.M * (b_rows_of(a, epi) - static_cast<int64_t>(dp_cols) * BN) <= a.part_floats;
 }
 
 }  // namespace
 
-void choose_gemm_cfg(const GemmArgs& a, int epi, int* cfg, int* splits) {
+// A hybrid plan (whole tiles plus split remainder) must beat the best plain plan
+// by 10%: its short pieces and their partials cost more than the model counts
+// (measured: 678 x 28672 x 4096 SwiGLU, predicted 3% faster, ran 5% slower).
+void choose_gemm_cfg(const GemmArgs& a, int epi, int* cfg, int* splits, int* dp_cols) {
   *cfg = GEMM_CFG_256;
   *splits = 1;
-  double best = est_time(a, epi, GEMM_CFG_256, 1);
+  *dp_cols = 0;
+  double best = est_time(a, epi, GEMM_CFG_256, 1, 0);
+  int h_cfg = 0, h_splits = 0, h_dp = 0;
+  double h_best = 0.0;
   for (int c : {GEMM_CFG_256, GEMM_CFG_128}) {
+    const int bm = bm_of(c);
+    const int mtl = m_tiles_of(a, bm), ntl = n_tiles_of(a, epi);
+    const int64_t S = bm == 256 ? 256 : 512;
     for (int sp = 1; sp <= 8; ++sp) {
-      if (sp > 1 && (epi == EPI_SWIGLU || a.part == nullptr)) break;
+      if (sp > 1 && a.part == nullptr) break;
       if (a.K / sp < 256) break;
       int kps, eff;
       split_k(a.K, sp, &kps, &eff);
-      if (eff > 1 && static_cast<int64_t>(eff) * a.M * a.N > a.part_floats) break;
-      const double tm = est_time(a, epi, c, sp);
-      if (tm < best * 0.97) {
-        best = tm;
-        *cfg = c;
-        *splits = sp;
+      // whole-tile column counts: none (plain split-K) or as many as fill k full rounds
+      int opts[9];
+      int n_opts = 0;
+      if (eff == 1) {
+        opts[n_opts++] = 0;
+      } else {
+        opts[n_opts++] = 0;
+        for (int64_t k = 1; k * S <= static_cast<int64_t>(mtl) * ntl && n_opts < 9; ++k) {
+          const int d = static_cast<int>(k * S / mtl);
+          if (d > 0 && d < ntl) opts[n_opts++] = d;
+        }
+      }
+      for (int o = 0; o < n_opts; ++o) {
+        if (eff > 1 && !part_fits(a, epi, eff, opts[o])) continue;
+        const double tm = est_time(a, epi, c, sp, opts[o]);
+        if (opts[o] > 0) {
+          if (h_splits == 0 || tm < h_best) {
+            h_best = tm;
+            h_cfg = c;
+            h_splits = sp;
+            h_dp = opts[o];
+          }
+        } else if (tm < best * 0.97) {
+          best = tm;
+          *cfg = c;
+          *splits = sp;
+        }
       }
     }
+  }
+  if (h_splits > 0 && h_best < 0.9 * best) {
+    *cfg = h_cfg;
+    *splits = h_splits;
+    *dp_cols = h_dp;
   }
 }
 
@@ -590,36 +704,36 @@ namespace {
 
 // *normed: set when the RMSNorm of a residual GEMM's output was fused into the reduction
 template <int EPI, int BM>
-hipError_t run_bm(const GemmArgs& a, int splits, hipStream_t s, bool* normed) {
+hipError_t run_bm(const GemmArgs& a, int splits, int dp_cols, hipStream_t s, bool* normed) {
   int kps, eff;
   split_k(a.K, splits, &kps, &eff);
-  const int t = tiles_of(a, EPI, BM);
-  if (eff > 1) {
-    if constexpr (EPI == EPI_SWIGLU) {
-      return hipErrorInvalidValue;
+  const int mtl = m_tiles_of(a, BM), ntl = n_tiles_of(a, EPI);
+  if (eff > 1 && dp_cols < ntl) {
+    if (dp_cols < 0 || !part_fits(a, EPI, eff, dp_cols)) return hipErrorInvalidValue;
+    const int wgs = mtl * dp_cols + mtl * (ntl - dp_cols) * eff;
+    hipError_t e = launch_cfg<EPI, BM, true>(wgs, a, eff, kps, dp_cols, s);
+    if (e != hipSuccess) return e;
+    const int c_part = dp_cols * BN;
+    if (EPI == EPI_RESID && a.norm_out != nullptr && a.N <= kNormChunks * 1024) {
+      splitk_reduce_norm_kernel<<<a.M, 256, 0, s>>>(a, eff, c_part);
+      *normed = true;
     } else {
-      if (a.part == nullptr || static_cast<int64_t>(eff) * a.M * a.N > a.part_floats) return hipErrorInvalidValue;
-      hipError_t e = launch_cfg<EPI, BM, true>(a, t, eff, kps, s);
-      if (e != hipSuccess) return e;
-      if (EPI == EPI_RESID && a.norm_out != nullptr && a.N <= kNormChunks * 1024) {
-        splitk_reduce_norm_kernel<<<a.M, 256, 0, s>>>(a, eff);
-        *normed = true;
-      } else {
-        const int64_t n = static_cast<int64_t>(a.M) * (a.N / 4);
-        splitk_reduce_kernel<EPI><<<static_cast<int>((n + 255) / 256), 256, 0, s>>>(a, eff);
-      }
-      return hipGetLastError();
+      const int64_t n = (EPI == EPI_SWIGLU) ? static_cast<int64_t>(a.M) * ((a.N - c_part / 2) / 4)
+                                            : static_cast<int64_t>(a.M) * ((b_rows_of(a, EPI) - c_part) / 4);
+      splitk_reduce_kernel<EPI><<<static_cast<int>((n + 255) / 256), 256, 0, s>>>(a, eff, c_part);
     }
+    return hipGetLastError();
   }
-  return launch_cfg<EPI, BM, false>(a, t, 1, a.K, s);
+  return launch_cfg<EPI, BM, false>(mtl * ntl, a, 1, a.K, ntl, s);
 }
 
 template <int EPI>
-hipError_t run_cfg(const GemmArgs& a, int cfg, int splits, hipStream_t s, bool* normed) {
+hipError_t run_cfg(const GemmArgs& a, int cfg, int splits, int dp_cols, hipStream_t s, bool* normed) {
   if (a.K % BK != 0 || a.K <= 0) return hipErrorInvalidValue;
   if (EPI == EPI_SWIGLU && a.N % 32 != 0) return hipErrorInvalidValue;
   if (splits > 1 && a.N % 4 != 0) return hipErrorInvalidValue;
-  return cfg == GEMM_CFG_256 ? run_bm<EPI, 256>(a, splits, s, normed) : run_bm<EPI, 128>(a, splits, s, normed);
+  return cfg == GEMM_CFG_256 ? run_bm<EPI, 256>(a, splits, dp_cols, s, normed)
+                             : run_bm<EPI, 128>(a, splits, dp_cols, s, normed);
 }
 
 template <int EPI>
@@ -634,9 +748,9 @@ hipError_t run_gemm(cb_dtype dt, const GemmArgs& a, hipStream_t s) {
     gemm_f32_kernel<EPI><<<m_tiles * n_tiles, 256, 0, s>>>(a);
     e = hipGetLastError();
   } else {
-    int cfg, splits;
-    choose_gemm_cfg(a, EPI, &cfg, &splits);
-    e = run_cfg<EPI>(a, cfg, splits, s, &normed);
+    int cfg, splits, dp_cols;
+    choose_gemm_cfg(a, EPI, &cfg, &splits, &dp_cols);
+    e = run_cfg<EPI>(a, cfg, splits, dp_cols, s, &normed);
   }
   if (e != hipSuccess || EPI != EPI_RESID || a.norm_out == nullptr || normed) return e;
   return launch_rmsnorm(dt, static_cast<const float*>(a.C), nullptr, a.ldc, a.M, a.N, a.norm_gain, a.norm_eps, a.norm_out,
@@ -645,14 +759,14 @@ hipError_t run_gemm(cb_dtype dt, const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gemm_cfg(GemmEpi epi, const GemmArgs& a, int cfg, int splits, hipStream_t s) {
+hipError_t launch_gemm_cfg(GemmEpi epi, const GemmArgs& a, int cfg, int splits, int dp_cols, hipStream_t s) {
   bool normed = false;
   switch (epi) {
-    case EPI_STORE_ROPE: return run_cfg<EPI_STORE_ROPE>(a, cfg, splits, s, &normed);
-    case EPI_F32_ROPE: return run_cfg<EPI_F32_ROPE>(a, cfg, splits, s, &normed);
-    case EPI_RESID: return run_cfg<EPI_RESID>(a, cfg, splits, s, &normed);
-    case EPI_SWIGLU: return run_cfg<EPI_SWIGLU>(a, cfg, splits, s, &normed);
-    case EPI_QKV: return run_cfg<EPI_QKV>(a, cfg, splits, s, &normed);
+    case EPI_STORE_ROPE: return run_cfg<EPI_STORE_ROPE>(a, cfg, splits, dp_cols, s, &normed);
+    case EPI_F32_ROPE: return run_cfg<EPI_F32_ROPE>(a, cfg, splits, dp_cols, s, &normed);
+    case EPI_RESID: return run_cfg<EPI_RESID>(a, cfg, splits, dp_cols, s, &normed);
+    case EPI_SWIGLU: return run_cfg<EPI_SWIGLU>(a, cfg, splits, dp_cols, s, &normed);
+    case EPI_QKV: return run_cfg<EPI_QKV>(a, cfg, splits, dp_cols, s, &normed);
   }
   return hipErrorInvalidValue;
 }

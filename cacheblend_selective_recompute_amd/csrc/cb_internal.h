@@ -198,9 +198,11 @@ constexpr int64_t kGemmPartFloats = int64_t(32) << 20;   // 128 MiB of split-K p
 hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s);
 // bf16 block tiles: 256 x 256 (one workgroup per CU) or 128 x 256 (two per CU)
 enum GemmCfg : int { GEMM_CFG_256 = 0, GEMM_CFG_128 = 1 };
-// bf16 GEMM with an explicit tile and split of K
-hipError_t launch_gemm_cfg(GemmEpi epi, const GemmArgs& a, int cfg, int splits, hipStream_t s);
-void choose_gemm_cfg(const GemmArgs& a, int epi, int* cfg, int* splits);
+// bf16 GEMM with an explicit plan: block tile, split of K, and the number of
+// tile columns computed whole (the rest split; dp_cols = 0 is plain split-K,
+// ignored when splits = 1)
+hipError_t launch_gemm_cfg(GemmEpi epi, const GemmArgs& a, int cfg, int splits, int dp_cols, hipStream_t s);
+void choose_gemm_cfg(const GemmArgs& a, int epi, int* cfg, int* splits, int* dp_cols);
 
 // ---------------------------------------------------------------------------
 // Attention of query rows over a paged cache (causal by absolute position).
@@ -221,6 +223,7 @@ struct AttnArgs {
   int kv_bound;            // host-known bound: every row position is < kv_bound
   float* part_o;           // split-KV partials, attn_partial_floats(head_dim) floats
   float2* part_ml;         // split-KV (max, sum) pairs, attn_partial_rows() entries
+  int n_splits_req;        // key splits to use; 0 = chosen by the launcher
 };
 hipError_t launch_attention(cb_dtype dt, const AttnArgs& a, hipStream_t s);
 // with an explicit kernel variant: 1 / 2 register-staged K/V with 1 / 2 query groups

@@ -6,9 +6,11 @@
 // selected tokens go through the projections; the recompute cost is
 // proportional to the selected share (section "选 token").
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, 4 waves in a 2x2 grid, block tile BM x 256
-// (BM = 256: one workgroup per CU, wave tile 128 x 128; BM = 128: two per CU,
-// wave tile 64 x 128).  Both operands are fragment-major in memory (see pk_off:
+// bf16 path: v_mfma_f32_32x32x16_bf16, block tile BM x 256 with the waves in a
+// (waves/2) x 2 grid and a 64 x 128 tile per wave: 256 x 256 with 8 waves (one
+// workgroup per CU) or 128 x 256 with 4 waves (two per CU), so every SIMD holds
+// two waves that hide each other's waits; the 256-row tile moves a third less
+// global data per MFMA.  Both operands are fragment-major in memory (see pk_off:
 // activations are written that way by the kernels that produce them, weights are
 // packed once by cb_pack_weight), so one 32-row x 16-column block is 1 KiB laid
 // out in MFMA lane order.  k advances in stages of 32 columns; each stage is
@@ -37,23 +39,31 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 32;          // k columns per stage
 constexpr int BN = 256;         // block tile columns (B rows)
-constexpr int kThreads = 256;
 
 // s_waitcnt with only the vector-memory counter constrained (n outstanding allowed)
 #define CB_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
-template <int BM>
+// Block-tile configurations (GemmCfg): 0 = 256 x 256 with 8 waves (one workgroup
+// per CU), 1 = 128 x 256 with 4 waves (two per CU).  Waves form a (WV/2) x 2 grid,
+// so a wave's tile is (BM / (WV/2)) x 128 = 64 x 128 in both.
+template <int CFG>
 struct Tile {
-  static constexpr int FM = BM / 64;              // A fragments per wave (wave tile BM/2 x 128)
+  static constexpr int BM = CFG == 1 ? 128 : 256;
+  static constexpr int WV = CFG == 1 ? 4 : 8;     // waves per workgroup
+  static constexpr int kThreads = WV * 64;
+  static constexpr int FM = 2 * BM / (32 * WV);   // A fragments (32-row blocks) per wave
   static constexpr int ABLK = BM / 16;            // A blocks per stage: BM/32 row blocks x 2 k blocks
   static constexpr int kStageA = ABLK * 1024;
   static constexpr int kStage = kStageA + 16384;  // + B: 8 row blocks x 2 k blocks
   static constexpr int NS = BM == 256 ? 4 : 3;    // stages in the LDS ring
-  static constexpr int DA = ABLK / 4;             // A copies per wave per stage
-  static constexpr int DQ = DA + 4;               // all copies per wave per stage
+  static constexpr int DA = ABLK / WV;            // A copies per wave per stage
+  static constexpr int DB = 16 / WV;              // B copies per wave per stage
+  static constexpr int DQ = DA + DB;              // all copies per wave per stage
   static constexpr int H0 = DQ / 2;               // issued during the second half of a stage
   static constexpr int H1 = DQ - H0;              // ... and during the first half of the next
   static constexpr int WGS_PER_CU = BM == 256 ? 1 : 2;
+  static constexpr int EP = 136;                  // epilogue staging row pitch (floats)
+  static constexpr int kSmem = NS * kStage > WV * 32 * EP * 4 ? NS * kStage : WV * 32 * EP * 4;
 };
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -78,12 +88,13 @@ __device__ __forceinline__ void copy_block(uint32_t lds, __amdgpu_buffer_rsrc_t 
 // columns of K whose fp32 partials go to g.part as [split][M][W], W = the virtual
 // columns past dp_cols * BN; a reduction kernel then sums them in split order
 // and applies the epilogue.  dp_cols = 0 is plain split-K.
-template <int EPI, int BM, bool SPLIT>
-__global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kernel(GemmArgs g, int splits, int kps,
-                                                                                  int dp_cols) {
-  using T = Tile<BM>;
-  constexpr int FM = T::FM, NS = T::NS, DA = T::DA, DQ = T::DQ, H0 = T::H0, H1 = T::H1;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * T::kStage];
+template <int EPI, int CFG, bool SPLIT>
+__global__ __launch_bounds__(Tile<CFG>::kThreads, Tile<CFG>::WGS_PER_CU) void gemm_bf16_kernel(GemmArgs g, int splits,
+                                                                                              int kps, int dp_cols) {
+  using T = Tile<CFG>;
+  constexpr int BM = T::BM;
+  constexpr int FM = T::FM, NS = T::NS, DA = T::DA, DB = T::DB, DQ = T::DQ, H0 = T::H0, H1 = T::H1;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::kSmem];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -127,12 +138,12 @@ __global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kern
       const_cast<bf16_t*>(B + (static_cast<int64_t>(nb0) * kbr + kb0) * 512), static_cast<short>(0),
       max(0, (nb_valid - nb0) * kbr - kb0) * 1024, 0x00020000);
 
-  // copy u of a stage: u < DA -> A block wid*DA+u, else B block wid*4+u-DA;
+  // copy u of a stage: u < DA -> A block wid*DA+u, else B block wid*DB+u-DA;
   // block q of a stage = row block q/2, k block q%2
   int voff[DQ];
 #pragma unroll
   for (int u = 0; u < DQ; ++u) {
-    const int q = u < DA ? wid * DA + u : wid * 4 + (u - DA);
+    const int q = u < DA ? wid * DA + u : wid * DB + (u - DA);
     voff[u] = ((q >> 1) * kbr + (q & 1)) * 1024 + lane * 16;
   }
   // LDS byte address of the ring and the wave index, both wave-uniform (scalar registers)
@@ -140,7 +151,7 @@ __global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kern
   const int wid_s = __builtin_amdgcn_readfirstlane(wid);
   // copy u of stage s into ring slot `slot` (a compile-time constant at every call)
   auto copy = [&](int s, int slot, int u) {
-    const int q = u < DA ? wid_s * DA + u : wid_s * 4 + (u - DA);
+    const int q = u < DA ? wid_s * DA + u : wid_s * DB + (u - DA);
     const uint32_t dst = lds0 + slot * T::kStage + (u < DA ? 0 : T::kStageA) + q * 1024;
     const int soff = min(s, nk - 1) * (BK * 64);      // stages past the last re-read it into a retired slot
     if (u < DA) copy_block(dst, ra, voff[u], soff);
@@ -221,15 +232,15 @@ __global__ __launch_bounds__(kThreads, Tile<BM>::WGS_PER_CU) void gemm_bf16_kern
 
   // ---------------- epilogue ----------------
   // acc[i][j][v] holds C[row][col] with
-  //   row = m0 + wm*BM/2 + i*32 + 8*(v/4) + 4*(lane/32) + v%4,  col = n0 + wn*128 + j*32 + lane%32.
+  //   row = m0 + wm*FM*32 + i*32 + 8*(v/4) + 4*(lane/32) + v%4,  col = n0 + wn*128 + j*32 + lane%32.
   // Each 32-row slab of the wave's tile goes through the (now idle) LDS ring as a
   // row-major 32 x 128 fp32 block, so every lane then owns 4 adjacent columns:
   // RoPE pairs and SwiGLU gate/up partners are local, and rows are stored whole.
   __syncthreads();                                   // every wave is done with the ring
-  constexpr int EP = 136;                            // row pitch (floats): the two half-waves hit different banks
+  constexpr int EP = T::EP;                          // row pitch (floats): the two half-waves hit different banks
   float* stg = reinterpret_cast<float*>(smem) + wid * (32 * EP);
   const int half = g.head_dim >> 1;
-  const int row0 = m0 + wm * (BM / 2);
+  const int row0 = m0 + wm * (FM * 32);
   const int col0 = n0 + wn * 128;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -577,13 +588,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
-template <int EPI, int BM, bool SPLIT>
+template <int EPI, int CFG, bool SPLIT>
 hipError_t launch_cfg(int wgs, const GemmArgs& a, int splits, int kps, int dp_cols, hipStream_t s) {
-  gemm_bf16_kernel<EPI, BM, SPLIT><<<wgs, kThreads, 0, s>>>(a, splits, kps, dp_cols);
+  gemm_bf16_kernel<EPI, CFG, SPLIT><<<wgs, Tile<CFG>::kThreads, 0, s>>>(a, splits, kps, dp_cols);
   return hipGetLastError();
 }
 
-inline int bm_of(int cfg) { return cfg == GEMM_CFG_256 ? 256 : 128; }
+inline int bm_of(int cfg) { return cfg == GEMM_CFG_128 ? 128 : 256; }
 
 inline int b_rows_of(const GemmArgs& a, int epi) { return (epi == EPI_SWIGLU) ? 2 * a.N : a.N; }
 inline int m_tiles_of(const GemmArgs& a, int bm) { return (a.M + bm - 1) / bm; }
@@ -600,13 +611,13 @@ inline void split_k(int K, int splits, int* kps, int* eff) {
 // Cost model, calibrated on the GEMM microbenchmark with random bf16 data at the
 // 8B blend shapes.  Workgroups run at a per-workgroup rate that rises as fewer
 // CUs are busy (the chip is power-limited under MFMA load): 256-row tiles (one
-// per CU) ~5.0 TFLOP/s x (256/b)^0.4 on b busy CUs; 128-row tiles two per CU ~2.6
+// per CU) ~5.2 TFLOP/s x (256/b)^0.4 on b busy CUs; 128-row tiles two per CU ~2.6
 // each, one per CU ~3.9 x (256/b)^0.4 (the gain capped at 1.25).  The fixed-order
 // reduction moves the fp32 partials once (write + read) at ~8 TB/s plus a launch.
 inline double busy_scale(int64_t b) { return b >= 256 ? 1.0 : fmin(1.25, pow(256.0 / static_cast<double>(b), 0.4)); }
 
 inline double wg_rate(int bm, int64_t wgs) {   // FLOP/s of one workgroup while `wgs` run at once
-  if (bm == 256) return 5.0e12 * busy_scale(std::min<int64_t>(wgs, 256));
+  if (bm == 256) return 5.2e12 * busy_scale(std::min<int64_t>(wgs, 256));
   return wgs > 256 ? 2.6e12 : 3.9e12 * busy_scale(wgs);
 }
 
@@ -703,15 +714,16 @@ void choose_gemm_cfg(const GemmArgs& a, int epi, int* cfg, int* splits, int* dp_
 namespace {
 
 // *normed: set when the RMSNorm of a residual GEMM's output was fused into the reduction
-template <int EPI, int BM>
+template <int EPI, int CFG>
 hipError_t run_bm(const GemmArgs& a, int splits, int dp_cols, hipStream_t s, bool* normed) {
+  constexpr int BM = Tile<CFG>::BM;
   int kps, eff;
   split_k(a.K, splits, &kps, &eff);
   const int mtl = m_tiles_of(a, BM), ntl = n_tiles_of(a, EPI);
   if (eff > 1 && dp_cols < ntl) {
     if (dp_cols < 0 || !part_fits(a, EPI, eff, dp_cols)) return hipErrorInvalidValue;
     const int wgs = mtl * dp_cols + mtl * (ntl - dp_cols) * eff;
-    hipError_t e = launch_cfg<EPI, BM, true>(wgs, a, eff, kps, dp_cols, s);
+    hipError_t e = launch_cfg<EPI, CFG, true>(wgs, a, eff, kps, dp_cols, s);
     if (e != hipSuccess) return e;
     const int c_part = dp_cols * BN;
     if (EPI == EPI_RESID && a.norm_out != nullptr && a.N <= kNormChunks * 1024) {
@@ -724,7 +736,7 @@ hipError_t run_bm(const GemmArgs& a, int splits, int dp_cols, hipStream_t s, boo
     }
     return hipGetLastError();
   }
-  return launch_cfg<EPI, BM, false>(mtl * ntl, a, 1, a.K, ntl, s);
+  return launch_cfg<EPI, CFG, false>(mtl * ntl, a, 1, a.K, ntl, s);
 }
 
 template <int EPI>
@@ -732,8 +744,9 @@ hipError_t run_cfg(const GemmArgs& a, int cfg, int splits, int dp_cols, hipStrea
   if (a.K % BK != 0 || a.K <= 0) return hipErrorInvalidValue;
   if (EPI == EPI_SWIGLU && a.N % 32 != 0) return hipErrorInvalidValue;
   if (splits > 1 && a.N % 4 != 0) return hipErrorInvalidValue;
-  return cfg == GEMM_CFG_256 ? run_bm<EPI, 256>(a, splits, dp_cols, s, normed)
-                             : run_bm<EPI, 128>(a, splits, dp_cols, s, normed);
+  if (cfg == GEMM_CFG_256) return run_bm<EPI, GEMM_CFG_256>(a, splits, dp_cols, s, normed);
+  if (cfg == GEMM_CFG_128) return run_bm<EPI, GEMM_CFG_128>(a, splits, dp_cols, s, normed);
+  return hipErrorInvalidValue;
 }
 
 template <int EPI>

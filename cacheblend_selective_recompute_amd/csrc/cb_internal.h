@@ -196,7 +196,8 @@ struct GemmArgs {
 };
 constexpr int64_t kGemmPartFloats = int64_t(32) << 20;   // 128 MiB of split-K partials
 hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s);
-// bf16 block tiles: 256 x 256 (one workgroup per CU) or 128 x 256 (two per CU)
+// bf16 block tiles: 256 x 256 with 8 waves (one workgroup per CU) or 128 x 256
+// with 4 waves (two per CU)
 enum GemmCfg : int { GEMM_CFG_256 = 0, GEMM_CFG_128 = 1 };
 // bf16 GEMM with an explicit plan: block tile, split of K, and the number of
 // tile columns computed whole (the rest split; dp_cols = 0 is plain split-K,

@@ -43,6 +43,12 @@ def parse():
     ap.add_argument("--ratio", type=float, default=0.15)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-runs", type=int, default=5,
+                    help="extra untimed-by-contract runs, each after evicting the Infinity Cache")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the size sweep of cb_rerope_k and cb_kv_deviation (one JSON line per size)")
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false",
+                    help="skip the copy / library GEMM measurement of achievable peaks")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     return ap.parse_args()
@@ -169,6 +175,100 @@ def cpu_baseline(wl, seed):
                        f"({total:.1f} s per request)")}
 
 
+def measured_peaks(torch, dev):
+    """What the box sustains with random data: a plain device copy (1 GiB read +
+    1 GiB written) and torch's bf16 GEMM (hipBLASLt) at 8192^3, for the
+    roofline fractions against measured rather than datasheet peaks."""
+    a = torch.empty(256 << 20, dtype=torch.float32, device=dev).uniform_()
+    b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b.copy_(a)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * a.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    n = 8192
+    x = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    w = (torch.randn(n, n, device=dev) * 0.03).to(torch.bfloat16)
+    for _ in range(3):
+        y = x @ w
+    e0.record()
+    for _ in range(10):
+        y = x @ w
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tflops = 10 * 2.0 * n ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del x, w, y
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(copy_gbs, 1), "bf16_gemm_tflops": round(gemm_tflops, 1),
+            "how": "torch copy_ of 1 GiB fp32 (read + write); torch bf16 matmul 8192^3, random data"}
+
+
+def kernel_sweep(torch, dev):
+    """Size sweep (about 1 MB to 1 GB of algorithmic traffic) of the two
+    bandwidth-bound entry points that run alone: cb_rerope_k (K rotated, V
+    copied; 4 x L x H_kv x d_h x 2 B per token) and cb_kv_deviation (fresh fp32
+    K/V read, cached bf16 K/V gathered; 12 KiB per row at the 8B width).  Each
+    run follows a 512 MiB read that evicts the Infinity Cache (a read, so no
+    dirty lines are left to write back); one JSON line per size with the median
+    of 10 runs."""
+    import numpy as np
+    import cbinputs
+    from cacheblend_selective_recompute_amd import api
+    ints = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    evict = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps=10):
+        ts = []
+        for r in range(reps + 2):
+            evict.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    shape = cbinputs.SHAPES["llama3-8b"]
+    cfg = api.make_cfg(shape)
+    per_tok = 4 * shape.n_layers * shape.kv_width * 2
+    for n in (4, 16, 64, 256, 1024, 4096):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(n)
+        dims = (shape.n_layers, n, shape.n_kv_heads, shape.head_dim)
+        k = torch.randn(dims, generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn(dims, generator=gen, device=dev).to(torch.bfloat16)
+        ch = [api.ChunkSource(ints(np.zeros(n)), k, v, 0, 0)]
+        dst = api.PagedKV(shape, n, 16)
+        ws = api.Workspace(api.cb_workspace_bytes(cfg, 0, 0, 1), dev)
+        ms = timed(lambda: api.cb_rerope_k(cfg, ch, dst, api.CB_COPY_V, ws))
+        b = n * per_tok
+        print(json.dumps({"sweep": "cb_rerope_k", "tokens": n, "bytes": b, "us": round(ms * 1e3, 2),
+                          "gbs": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}),
+              flush=True)
+        del k, v, ch, dst
+    sh2 = shape.with_layers(2)
+    cfg2 = api.make_cfg(sh2)
+    kvw = shape.kv_width
+    per_row = kvw * (2 * 4 + 2 * 2) + 4 + 4
+    for n in (85, 341, 1365, 5461, 21845, 87381):
+        cache = api.PagedKV(sh2, n, 16, fill=0.5)
+        kf = torch.randn(n, 2 * kvw, device=dev)
+        pos = ints(np.arange(n))
+        out = torch.empty(n, device=dev)
+        ms = timed(lambda: api.cb_kv_deviation(cfg2, 1, kf[:, :kvw], kf[:, kvw:], pos, cache, out))
+        b = n * per_row
+        print(json.dumps({"sweep": "cb_kv_deviation", "rows": n, "bytes": b, "us": round(ms * 1e3, 2),
+                          "gbs": round(b / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}),
+              flush=True)
+        del cache, kf, pos, out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -189,6 +289,9 @@ def main():
     N, Q, T = wl.n_ctx, wl.n_query, wl.n_total
     ks, ch = wl.schedule()
     dev = "cuda"
+    if args.sweep:
+        kernel_sweep(torch, dev)
+        return
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -292,9 +395,27 @@ def main():
         peak = PEAK_HBM_GBS
         achieved = work_per_launch / (avg_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "unit": "GB/s"}
+    # cold runs: a 512 MiB read between runs evicts the 256 MiB Infinity Cache (the
+    # chunk caches and weights then come from HBM, as for a request that just arrived)
+    evict = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    cold = []
+    for s in range(args.cold_runs):
+        evict.sum()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        run(plain)
+        c1.record()
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1))
+    del evict
+    peaks = measured_peaks(torch, dev) if args.peaks else None
+
     roof.update({"kernel": dominant, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
                  "traffic": traffic_from_profile(dominant, wl.name), "launches_per_step": kind_n[dominant], "avg_launch_ms": round(avg_launch_ms, 4),
                  "work_per_launch": work_per_launch})
+    if peaks:
+        mp = peaks["bf16_gemm_tflops"] if roof["bound"] == "mfma" else peaks["copy_gbs"]
+        roof["frac_of_measured_peak"] = round(achieved / mp, 4)
 
     breakdown = {}
     for k, ms in sorted(kind_ms.items(), key=lambda kv: -kv[1]):
@@ -325,6 +446,9 @@ def main():
                    "paged": bool(wl.paged), "block_size": 16},
         "roofline": roof,
         "kernels_ms_per_step": breakdown,
+        "cold_ms_per_step": ({"median": round(float(np.median(cold)), 4), "min": round(min(cold), 4), "runs": len(cold)}
+                             if cold else None),
+        "measured_peaks": peaks,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -21,6 +21,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // 16-byte vector helpers: 8 bf16 or 4 fp32 elements.
+// 16-byte loads and stores that stream past the caches: every byte of the chunk
+// caches is read once and every byte of the blended cache written once
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(void* p, const uint4& v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+
 template <typename T> struct V16;
 template <> struct V16<bf16_t> { static constexpr int N = 8; };
 template <> struct V16<float> { static constexpr int N = 4; };
@@ -97,6 +108,15 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
   T* dk = static_cast<T*>(dst.k) + layer * dst.layer_stride;
   T* dv = static_cast<T*>(dst.v) + layer * dst.layer_stride;
   const float2* tab = dtab + static_cast<int64_t>(c) * (dh / 2);
+  // source and destination rows of the tile's tokens, looked up once per block
+  __shared__ int64_t srow_s[kTokTile], drow_s[kTokTile];
+  if (threadIdx.x < ntok) {
+    const int t = t0 + threadIdx.x;
+    srow_s[threadIdx.x] = cd.blk ? static_cast<int64_t>(cd.blk[t / cd.block_size]) * cd.block_size + t % cd.block_size
+                                 : static_cast<int64_t>(t);
+    drow_s[threadIdx.x] = paged_row(dst, cd.new_start + t);
+  }
+  __syncthreads();
 
   constexpr int U = 4;
   for (int base = threadIdx.x; base < nvec; base += kRerope * U) {
@@ -110,14 +130,11 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
       ok[u] = v < nvec;
       const int tt = ok[u] ? v / vpr : 0;
       e0[u] = (v % vpr) * VN;
-      const int t = t0 + tt;
-      const int64_t srow = cd.blk ? static_cast<int64_t>(cd.blk[t / cd.block_size]) * cd.block_size + t % cd.block_size
-                                  : static_cast<int64_t>(t);
-      so[u] = srow * width + e0[u];
-      dof[u] = paged_row(dst, cd.new_start + t) * width + e0[u];
+      so[u] = srow_s[tt] * width + e0[u];
+      dof[u] = drow_s[tt] * width + e0[u];
       if (ok[u]) {
-        kv[u] = *reinterpret_cast<const uint4*>(srck + so[u]);
-        if (copy_v) vv[u] = *reinterpret_cast<const uint4*>(srcv + so[u]);
+        kv[u] = ld_stream(srck + so[u]);
+        if (copy_v) vv[u] = ld_stream(srcv + so[u]);
       }
     }
 #pragma unroll
@@ -143,8 +160,8 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
       } else {
         o = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
       }
-      *reinterpret_cast<uint4*>(dk + dof[u]) = o;
-      if (copy_v) *reinterpret_cast<uint4*>(dv + dof[u]) = vv[u];
+      st_stream(dk + dof[u], o);
+      if (copy_v) st_stream(dv + dof[u], vv[u]);
     }
   }
 }
@@ -205,9 +222,23 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const int3
 }
 
 // ---------------------------------------------------------------------------
-// KV deviation: one wave per row, fp32 accumulation in fixed order
+// KV deviation: one wave per row, fp32 accumulation in fixed order.  W > 0: the
+// row width is known at compile time and every lane takes 8 consecutive values
+// per pass (fresh: two 16-byte loads each for K and V; cached bf16: one), all of
+// its loads issued before the first use.  W = 0: any width (a multiple of 4).
 // ---------------------------------------------------------------------------
 template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&f)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    unpack(*reinterpret_cast<const uint4*>(p), f);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+}
+
+template <typename T, int W>
 __global__ __launch_bounds__(256) void deviation_kernel(const float* kf, const float* vf, int64_t ldf,
                                                         const int32_t* pos, int n, PagedRef cache, int layer,
                                                         int width, float* dev, float* dev_by_pos) {
@@ -221,25 +252,40 @@ __global__ __launch_bounds__(256) void deviation_kernel(const float* kf, const f
   const float* fk = kf + static_cast<int64_t>(row) * ldf;
   const float* fv = vf + static_cast<int64_t>(row) * ldf;
   float acc = 0.f;
-  for (int e = lane * 4; e < width; e += 64 * 4) {
-    const float4 a = *reinterpret_cast<const float4*>(fk + e);
-    const float4 b = *reinterpret_cast<const float4*>(fv + e);
-    float c0[4], c1[4];
-    if constexpr (sizeof(T) == 2) {
-      const uint2 u = *reinterpret_cast<const uint2*>(ck + e);
-      const uint2 w = *reinterpret_cast<const uint2*>(cv + e);
-      c0[0] = bf2f(u.x & 0xFFFFu); c0[1] = bf2f(u.x >> 16); c0[2] = bf2f(u.y & 0xFFFFu); c0[3] = bf2f(u.y >> 16);
-      c1[0] = bf2f(w.x & 0xFFFFu); c1[1] = bf2f(w.x >> 16); c1[2] = bf2f(w.y & 0xFFFFu); c1[3] = bf2f(w.y >> 16);
-    } else {
-      const float4 u = *reinterpret_cast<const float4*>(ck + e);
-      const float4 w = *reinterpret_cast<const float4*>(cv + e);
-      c0[0] = u.x; c0[1] = u.y; c0[2] = u.z; c0[3] = u.w;
-      c1[0] = w.x; c1[1] = w.y; c1[2] = w.z; c1[3] = w.w;
+  if constexpr (W > 0) {
+    constexpr int P = W / 512;              // passes of 64 lanes x 8 values
+    float a[P][8], b[P][8], c0[P][8], c1[P][8];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      const int e = q * 512 + lane * 8;
+      load8<float>(fk + e, a[q]);
+      load8<float>(fv + e, b[q]);
+      load8<T>(ck + e, c0[q]);
+      load8<T>(cv + e, c1[q]);
     }
-    const float dk0 = a.x - c0[0], dk1 = a.y - c0[1], dk2 = a.z - c0[2], dk3 = a.w - c0[3];
-    const float dv0 = b.x - c1[0], dv1 = b.y - c1[1], dv2 = b.z - c1[2], dv3 = b.w - c1[3];
-    acc += (dk0 * dk0 + dk1 * dk1) + (dk2 * dk2 + dk3 * dk3);
-    acc += (dv0 * dv0 + dv1 * dv1) + (dv2 * dv2 + dv3 * dv3);
+#pragma unroll
+    for (int q = 0; q < P; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const float dk0 = a[q][j] - c0[q][j], dk1 = a[q][j + 1] - c0[q][j + 1];
+        const float dv0 = b[q][j] - c1[q][j], dv1 = b[q][j + 1] - c1[q][j + 1];
+        acc += (dk0 * dk0 + dk1 * dk1) + (dv0 * dv0 + dv1 * dv1);
+      }
+  } else {
+    for (int e = lane * 4; e < width; e += 64 * 4) {
+      const float4 a = *reinterpret_cast<const float4*>(fk + e);
+      const float4 b = *reinterpret_cast<const float4*>(fv + e);
+      float c0[4], c1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c0[j] = to_f<T>(ck[e + j]);
+        c1[j] = to_f<T>(cv[e + j]);
+      }
+      const float dk0 = a.x - c0[0], dk1 = a.y - c0[1], dk2 = a.z - c0[2], dk3 = a.w - c0[3];
+      const float dv0 = b.x - c1[0], dv1 = b.y - c1[1], dv2 = b.z - c1[2], dv3 = b.w - c1[3];
+      acc += (dk0 * dk0 + dk1 * dk1) + (dk2 * dk2 + dk3 * dk3);
+      acc += (dv0 * dv0 + dv1 * dv1) + (dv2 * dv2 + dv3 * dv3);
+    }
   }
   acc = wave_sum(acc);
   if (lane == 0) {
@@ -363,7 +409,7 @@ __global__ void build_rows_kernel(const int32_t* sel_slot, const int32_t* sel_po
 // ---------------------------------------------------------------------------
 // scatter fresh K/V rows (fp32) into the paged cache in the model dtype
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int W>
 __global__ __launch_bounds__(256) void scatter_kv_kernel(const float* kvf, int64_t ldf, const int32_t* gmap,
                                                          const int32_t* rowpos, int n, PagedRef cache, int layer,
                                                          int width) {
@@ -376,20 +422,36 @@ __global__ __launch_bounds__(256) void scatter_kv_kernel(const float* kvf, int64
                       paged_row(cache, rowpos[row]) * width;
   T* ck = static_cast<T*>(cache.k) + off;
   T* cv = static_cast<T*>(cache.v) + off;
-  for (int e = lane * 4; e < width; e += 256) {
-    const float4 a = *reinterpret_cast<const float4*>(f + e);
-    const float4 b = *reinterpret_cast<const float4*>(f + width + e);
-    if constexpr (sizeof(T) == 2) {
-      uint2 u, w;
-      u.x = f2bf(a.x) | (static_cast<uint32_t>(f2bf(a.y)) << 16);
-      u.y = f2bf(a.z) | (static_cast<uint32_t>(f2bf(a.w)) << 16);
-      w.x = f2bf(b.x) | (static_cast<uint32_t>(f2bf(b.y)) << 16);
-      w.y = f2bf(b.z) | (static_cast<uint32_t>(f2bf(b.w)) << 16);
-      *reinterpret_cast<uint2*>(ck + e) = u;
-      *reinterpret_cast<uint2*>(cv + e) = w;
-    } else {
-      *reinterpret_cast<float4*>(ck + e) = a;
-      *reinterpret_cast<float4*>(cv + e) = b;
+  if constexpr (W > 0 && sizeof(T) == 2) {
+    // 8 consecutive values per lane and pass, every load issued first, 16-byte stores
+    constexpr int P = W / 512;
+    float a[P][8], b[P][8];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      load8<float>(f + q * 512 + lane * 8, a[q]);
+      load8<float>(f + width + q * 512 + lane * 8, b[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      *reinterpret_cast<uint4*>(ck + q * 512 + lane * 8) = pack(a[q]);
+      *reinterpret_cast<uint4*>(cv + q * 512 + lane * 8) = pack(b[q]);
+    }
+  } else {
+    for (int e = lane * 4; e < width; e += 256) {
+      const float4 a = *reinterpret_cast<const float4*>(f + e);
+      const float4 b = *reinterpret_cast<const float4*>(f + width + e);
+      if constexpr (sizeof(T) == 2) {
+        uint2 u, w;
+        u.x = f2bf(a.x) | (static_cast<uint32_t>(f2bf(a.y)) << 16);
+        u.y = f2bf(a.z) | (static_cast<uint32_t>(f2bf(a.w)) << 16);
+        w.x = f2bf(b.x) | (static_cast<uint32_t>(f2bf(b.y)) << 16);
+        w.y = f2bf(b.z) | (static_cast<uint32_t>(f2bf(b.w)) << 16);
+        *reinterpret_cast<uint2*>(ck + e) = u;
+        *reinterpret_cast<uint2*>(cv + e) = w;
+      } else {
+        *reinterpret_cast<float4*>(ck + e) = a;
+        *reinterpret_cast<float4*>(cv + e) = b;
+      }
     }
   }
 }
@@ -496,10 +558,18 @@ hipError_t launch_deviation(cb_dtype dt, const float* kf, const float* vf, int64
   if (n == 0) return hipSuccess;
   PagedRef cache = cache_in;
   cache.bs_shift = block_shift(cache.bs);
-  if (dt == CB_BF16)
-    deviation_kernel<bf16_t><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
-  else
-    deviation_kernel<float><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
+  const bool w1k = width == 1024 && ldf % 4 == 0;   // 8 KV heads x 128: 16-byte aligned rows
+  if (dt == CB_BF16) {
+    if (w1k)
+      deviation_kernel<bf16_t, 1024><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
+    else
+      deviation_kernel<bf16_t, 0><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
+  } else {
+    if (w1k)
+      deviation_kernel<float, 1024><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
+    else
+      deviation_kernel<float, 0><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
+  }
   return hipGetLastError();
 }
 
@@ -523,10 +593,12 @@ hipError_t launch_scatter_kv(cb_dtype dt, const float* kvf, int64_t ldf, const i
   if (n == 0) return hipSuccess;
   PagedRef cache = cache_in;
   cache.bs_shift = block_shift(cache.bs);
-  if (dt == CB_BF16)
-    scatter_kv_kernel<bf16_t><<<cdiv(n, 4), 256, 0, s>>>(kvf, ldf, gmap, rowpos, n, cache, layer, width);
+  if (dt == CB_BF16 && width == 1024 && ldf % 4 == 0)
+    scatter_kv_kernel<bf16_t, 1024><<<cdiv(n, 4), 256, 0, s>>>(kvf, ldf, gmap, rowpos, n, cache, layer, width);
+  else if (dt == CB_BF16)
+    scatter_kv_kernel<bf16_t, 0><<<cdiv(n, 4), 256, 0, s>>>(kvf, ldf, gmap, rowpos, n, cache, layer, width);
   else
-    scatter_kv_kernel<float><<<cdiv(n, 4), 256, 0, s>>>(kvf, ldf, gmap, rowpos, n, cache, layer, width);
+    scatter_kv_kernel<float, 0><<<cdiv(n, 4), 256, 0, s>>>(kvf, ldf, gmap, rowpos, n, cache, layer, width);
   return hipGetLastError();
 }
 

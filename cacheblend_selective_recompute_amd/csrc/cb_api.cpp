@@ -355,13 +355,14 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   if (check) {
     float* dev = io.dev_slot ? io.dev_slot : w.dev;
     CB_LAUNCH(tr, CB_KIND_DEVIATION, launch_deviation(c.dtype, w.kvf, w.kvf + kvw, 2 * kvw, io.cand_pos, nc, kv, l, kvw, dev, io.dev_by_pos, s), "deviation");
-    CB_LAUNCH(tr, CB_KIND_SELECT, launch_select(dev, io.cand_pos, nc, k, io.pos_out, w.slot, s), "select");
-    sel_slot = w.slot;
-    sel_pos = io.pos_out;
-    copy_out = nullptr;
+    // the top-k also writes the row maps of the kept rows and the suffix
+    CB_LAUNCH(tr, CB_KIND_SELECT, launch_select_rows(dev, io.cand_pos, nc, k, io.pos_out, w.slot, N, Q, w.gmap,
+                                                     io.rowpos_out, io.hkvd_row, s), "select");
+  } else {
+    // row maps of the kept rows (+ suffix); an unchecked layer keeps every candidate
+    CB_LAUNCH(tr, CB_KIND_OTHER, launch_build_rows(sel_slot, sel_pos, k, nc, N, Q, w.gmap, io.rowpos_out, copy_out,
+                                                   io.hkvd_row, s), "build rows");
   }
-  // row maps of the kept rows (+ suffix); an unchecked layer keeps every candidate
-  CB_LAUNCH(tr, CB_KIND_OTHER, launch_build_rows(sel_slot, sel_pos, k, nc, N, Q, w.gmap, io.rowpos_out, copy_out, io.hkvd_row, s), "build rows");
 
   // fill: fresh K/V of the kept rows and of the suffix replace the cache
   CB_LAUNCH(tr, CB_KIND_SCATTER, launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, w.gmap, io.rowpos_out, rout, kv, l, kvw, s), "scatter");

@@ -134,6 +134,9 @@ hipError_t launch_select(const float* dev, const int32_t* pos, int n, int k, int
                          int32_t* sel_slot, hipStream_t s);
 // row maps after selection: gmap[i] (source row), rowpos[i] (position), for i < k + nq
 // copy_a / copy_b (nullable) also receive the kept positions [k]
+// top-k plus the layer's row maps in one launch (kept rows, then the nq suffix rows)
+hipError_t launch_select_rows(const float* dev, const int32_t* pos, int n, int k, int32_t* sel_pos, int32_t* sel_slot,
+                              int n_ctx, int nq, int32_t* gmap, int32_t* rowpos, int32_t* copy, hipStream_t s);
 hipError_t launch_build_rows(const int32_t* sel_slot, const int32_t* sel_pos, int k, int nc, int n_ctx,
                              int nq, int32_t* gmap, int32_t* rowpos, int32_t* copy_a, int32_t* copy_b,
                              hipStream_t s);

@@ -325,17 +325,41 @@ __device__ __forceinline__ int block_flag_scan(bool flag, int* wsum, int* total)
   return before + in_wave;
 }
 
+// With rm.rowpos set it also writes the layer's row maps, as build_rows_kernel
+// would from its output: kept row o comes from candidate slot i at position
+// pos[i]; suffix row k + j from input row nc + j at position n_ctx + j.
+struct RowMaps {
+  int32_t* gmap;
+  int32_t* rowpos;
+  int32_t* copy;      // kept positions again (e.g. the per-layer HKVD output), or NULL
+  int n_ctx, nq;
+};
+
 __global__ __launch_bounds__(kSel) void select_kernel(const float* dev, const int32_t* pos, int n, int k,
-                                                      int32_t* sel_pos, int32_t* sel_slot) {
+                                                      int32_t* sel_pos, int32_t* sel_slot, RowMaps rm) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_digit, s_rem;
   __shared__ int wsum[kSel / 64];
+  auto keep = [&](int o, int i) {
+    const int p = pos[i];
+    sel_pos[o] = p;
+    if (sel_slot) sel_slot[o] = i;
+    if (rm.rowpos) {
+      rm.gmap[o] = i;
+      rm.rowpos[o] = p;
+      if (rm.copy) rm.copy[o] = p;
+    }
+  };
+  if (rm.rowpos) {
+    const int kk = max(k, 0);
+    for (int j = threadIdx.x; j < rm.nq; j += kSel) {
+      rm.gmap[kk + j] = n + j;
+      rm.rowpos[kk + j] = rm.n_ctx + j;
+    }
+  }
   if (k <= 0) return;
   if (k >= n) {
-    for (int i = threadIdx.x; i < n; i += kSel) {
-      sel_pos[i] = pos[i];
-      if (sel_slot) sel_slot[i] = i;
-    }
+    for (int i = threadIdx.x; i < n; i += kSel) keep(i, i);
     return;
   }
   uint32_t prefix = 0, mask = 0;
@@ -379,10 +403,7 @@ __global__ __launch_bounds__(kSel) void select_kernel(const float* dev, const in
     const bool take = gt || (eq && eq_before < static_cast<int>(rem));
     int take_tot = 0;
     const int o = block_flag_scan(take, wsum, &take_tot) + out_base;
-    if (take && o < k) {
-      sel_pos[o] = pos[i];
-      if (sel_slot) sel_slot[o] = i;
-    }
+    if (take && o < k) keep(o, i);
     out_base += take_tot;
     eq_base += eq_tot;
   }
@@ -576,7 +597,14 @@ hipError_t launch_deviation(cb_dtype dt, const float* kf, const float* vf, int64
 hipError_t launch_select(const float* dev, const int32_t* pos, int n, int k, int32_t* sel_pos, int32_t* sel_slot,
                          hipStream_t s) {
   if (k == 0 || n == 0) return hipSuccess;
-  select_kernel<<<1, kSel, 0, s>>>(dev, pos, n, k, sel_pos, sel_slot);
+  select_kernel<<<1, kSel, 0, s>>>(dev, pos, n, k, sel_pos, sel_slot, RowMaps{nullptr, nullptr, nullptr, 0, 0});
+  return hipGetLastError();
+}
+
+hipError_t launch_select_rows(const float* dev, const int32_t* pos, int n, int k, int32_t* sel_pos, int32_t* sel_slot,
+                              int n_ctx, int nq, int32_t* gmap, int32_t* rowpos, int32_t* copy, hipStream_t s) {
+  if (k + nq == 0) return hipSuccess;
+  select_kernel<<<1, kSel, 0, s>>>(dev, pos, n, k, sel_pos, sel_slot, RowMaps{gmap, rowpos, copy, n_ctx, nq});
   return hipGetLastError();
 }
 

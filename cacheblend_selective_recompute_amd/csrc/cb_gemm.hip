@@ -438,32 +438,67 @@ __device__ __forceinline__ float wave_sum64(float v) {
 }
 
 // Columns below c_part were finished by whole-tile workgroups of the same GEMM
-// (resid added) and are read back from C.
+// (resid added) and are read back from C.  NC > 0: the row is NC x 1024 columns
+// and there are SP splits, both compile-time, so every load of the row (all
+// partials, the residual) is issued before the first add; the sums keep split
+// order.  NC = 0: any width and split count.
+template <int NC, int SP>
 __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs g, int splits, int c_part) {
   __shared__ float red[4];
   const int row = blockIdx.x;
   const int rr = g.resid_rows ? g.resid_rows[row] : row;
   const int64_t wpart = g.N - c_part;
-  float4 v[kNormChunks];
+  constexpr int NCH = NC > 0 ? NC : kNormChunks;
+  float4 v[NCH];
   float ss = 0.f;
+  if constexpr (NC > 0) {
+    float4 pp[NC][SP], rv[NC];
 #pragma unroll
-  for (int c = 0; c < kNormChunks; ++c) {
-    const int e = threadIdx.x * 4 + c * 1024;
-    if (e < g.N) {
-      float* cp = static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + e;
+    for (int c = 0; c < NC; ++c) {
+      const int e = threadIdx.x * 4 + c * 1024;
       if (e < c_part) {
-        v[c] = *reinterpret_cast<const float4*>(cp);
+        v[c] = *reinterpret_cast<const float4*>(static_cast<const float*>(g.C) + static_cast<int64_t>(row) * g.ldc + e);
       } else {
-        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int sp = 0; sp < splits; ++sp) {
-          const float4 p = *reinterpret_cast<const float4*>(g.part + (static_cast<int64_t>(sp) * g.M + row) * wpart + (e - c_part));
-          s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+#pragma unroll
+        for (int sp = 0; sp < SP; ++sp)
+          pp[c][sp] = *reinterpret_cast<const float4*>(g.part + (static_cast<int64_t>(sp) * g.M + row) * wpart + (e - c_part));
+        rv[c] = *reinterpret_cast<const float4*>(g.resid + static_cast<int64_t>(rr) * g.ld_resid + e);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e = threadIdx.x * 4 + c * 1024;
+      if (e >= c_part) {
+        float4 sm = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int sp = 0; sp < SP; ++sp) {
+          sm.x += pp[c][sp].x; sm.y += pp[c][sp].y; sm.z += pp[c][sp].z; sm.w += pp[c][sp].w;
         }
-        const float4 r = *reinterpret_cast<const float4*>(g.resid + static_cast<int64_t>(rr) * g.ld_resid + e);
-        v[c] = make_float4(r.x + s.x, r.y + s.y, r.z + s.z, r.w + s.w);
-        *reinterpret_cast<float4*>(cp) = v[c];
+        v[c] = make_float4(rv[c].x + sm.x, rv[c].y + sm.y, rv[c].z + sm.z, rv[c].w + sm.w);
+        *reinterpret_cast<float4*>(static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + e) = v[c];
       }
       ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < kNormChunks; ++c) {
+      const int e = threadIdx.x * 4 + c * 1024;
+      if (e < g.N) {
+        float* cp = static_cast<float*>(g.C) + static_cast<int64_t>(row) * g.ldc + e;
+        if (e < c_part) {
+          v[c] = *reinterpret_cast<const float4*>(cp);
+        } else {
+          float4 sm = make_float4(0.f, 0.f, 0.f, 0.f);
+          for (int sp = 0; sp < splits; ++sp) {
+            const float4 p = *reinterpret_cast<const float4*>(g.part + (static_cast<int64_t>(sp) * g.M + row) * wpart + (e - c_part));
+            sm.x += p.x; sm.y += p.y; sm.z += p.z; sm.w += p.w;
+          }
+          const float4 r = *reinterpret_cast<const float4*>(g.resid + static_cast<int64_t>(rr) * g.ld_resid + e);
+          v[c] = make_float4(r.x + sm.x, r.y + sm.y, r.z + sm.z, r.w + sm.w);
+          *reinterpret_cast<float4*>(cp) = v[c];
+        }
+        ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+      }
     }
   }
   ss = wave_sum64(ss);
@@ -473,9 +508,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs g, int
   const float inv = 1.0f / sqrtf(tot / static_cast<float>(g.N) + g.norm_eps);
   bf16_t* out = static_cast<bf16_t*>(g.norm_out);
 #pragma unroll
-  for (int c = 0; c < kNormChunks; ++c) {
+  for (int c = 0; c < NCH; ++c) {
     const int e = threadIdx.x * 4 + c * 1024;
-    if (e < g.N) {
+    if (NC > 0 || e < g.N) {
       const float4 gg = *reinterpret_cast<const float4*>(g.norm_gain + e);
       uint2 w;
       w.x = static_cast<uint32_t>(f2bf(v[c].x * inv * gg.x)) | (static_cast<uint32_t>(f2bf(v[c].y * inv * gg.y)) << 16);
@@ -483,6 +518,28 @@ __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs g, int
       *reinterpret_cast<uint2*>(out + pk_off(row, e, g.N)) = w;
     }
   }
+}
+
+template <int NC>
+hipError_t launch_reduce_norm_nc(const GemmArgs& a, int eff, int c_part, hipStream_t s) {
+  switch (eff) {
+    case 2: splitk_reduce_norm_kernel<NC, 2><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
+    case 3: splitk_reduce_norm_kernel<NC, 3><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
+    case 4: splitk_reduce_norm_kernel<NC, 4><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
+    case 5: splitk_reduce_norm_kernel<NC, 5><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
+    case 6: splitk_reduce_norm_kernel<NC, 6><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
+    case 7: splitk_reduce_norm_kernel<NC, 7><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
+    case 8: splitk_reduce_norm_kernel<NC, 8><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
+    default: splitk_reduce_norm_kernel<0, 0><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_norm(const GemmArgs& a, int eff, int c_part, hipStream_t s) {
+  if (a.N == 4096) return launch_reduce_norm_nc<4>(a, eff, c_part, s);
+  if (a.N == 8192 && eff <= 4) return launch_reduce_norm_nc<8>(a, eff, c_part, s);   // more would spill
+  splitk_reduce_norm_kernel<0, 0><<<a.M, 256, 0, s>>>(a, eff, c_part);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -727,7 +784,8 @@ hipError_t run_bm(const GemmArgs& a, int splits, int dp_cols, hipStream_t s, boo
     if (e != hipSuccess) return e;
     const int c_part = dp_cols * BN;
     if (EPI == EPI_RESID && a.norm_out != nullptr && a.N <= kNormChunks * 1024) {
-      splitk_reduce_norm_kernel<<<a.M, 256, 0, s>>>(a, eff, c_part);
+      e = launch_reduce_norm(a, eff, c_part, s);
+      if (e != hipSuccess) return e;
       *normed = true;
     } else {
       const int64_t n = (EPI == EPI_SWIGLU) ? static_cast<int64_t>(a.M) * ((a.N - c_part / 2) / 4)

@@ -51,6 +51,11 @@ class cb_chunk(ctypes.Structure):
                 ("block_size", c_int32), ("layer_stride", c_int64)]
 
 
+class cb_host_chunk(ctypes.Structure):
+    _fields_ = [("tokens", c_void_p), ("k", c_void_p), ("v", c_void_p),
+                ("len", c_int32), ("old_start", c_int32), ("new_start", c_int32)]
+
+
 class cb_trace(ctypes.Structure):
     _fields_ = [("events", POINTER(c_void_p)), ("capacity", c_int32), ("used", c_int32),
                 ("kind_mask", c_uint32), ("kinds", POINTER(c_int32))]
@@ -78,6 +83,11 @@ _PROTOS = {
     "cb_blend_prefill": (c_int, [POINTER(cb_model), POINTER(cb_chunk), c_int32, c_void_p, c_int32,
                                  POINTER(cb_blend_params), POINTER(cb_paged_kv), c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_size_t, c_void_p]),
+    "cb_blend_prefill_streamed": (c_int, [POINTER(cb_model), POINTER(cb_host_chunk), c_int32, c_void_p, c_int32,
+                                          POINTER(cb_blend_params), POINTER(cb_paged_kv), c_void_p, c_void_p,
+                                          c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, POINTER(c_void_p)]),
+    "cb_streamed_workspace_bytes": (c_size_t, [POINTER(cb_model_cfg), c_int32, c_int32, c_int32]),
+    "cb_loading_ratio": (c_double, [c_double, c_double, c_double, c_double, c_double]),
     "cb_pack_weight": (c_int, [c_int, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
     "cb_packed_weight_bytes": (c_size_t, [c_int, c_int64, c_int64]),
     "cb_workspace_bytes": (c_size_t, [POINTER(cb_model_cfg), c_int32, c_int32, c_int32]),

@@ -17,7 +17,7 @@ import numpy as np
 import torch
 
 from . import _abi
-from ._abi import (CB_BF16, CB_COPY_V, CB_F32, CB_OK, cb_blend_params, cb_chunk, cb_layer_w, cb_model,
+from ._abi import (CB_BF16, CB_COPY_V, CB_F32, CB_OK, cb_blend_params, cb_chunk, cb_host_chunk, cb_layer_w, cb_model,
                    cb_model_cfg, cb_paged_kv)
 
 
@@ -199,6 +199,39 @@ class ChunkSource:
                         int(self.block_size if self.block_ids is not None else 0), int(self.layer_stride))
 
 
+@dataclass
+class HostChunk:
+    """One cached chunk whose K/V stay in page-locked host memory (contiguous
+    [L][len][Hkv][dh] CPU tensors with pin_memory) for the layer-pipelined
+    prefill; tokens are on the GPU."""
+    tokens: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    old_start: int
+    new_start: int
+
+    @property
+    def len(self) -> int:
+        return int(self.tokens.numel())
+
+    def c(self) -> cb_host_chunk:
+        if not (self.k.is_pinned() and self.v.is_pinned() and self.k.is_contiguous() and self.v.is_contiguous()):
+            raise ValueError("HostChunk: K/V must be contiguous page-locked CPU tensors")
+        return cb_host_chunk(self.tokens.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.len,
+                             int(self.old_start), int(self.new_start))
+
+
+class LayerEvents:
+    """2 x n_layers HIP events for cb_blend_prefill_streamed (created through
+    torch, so they belong to the runtime the library's streams come from)."""
+
+    def __init__(self, n_layers: int):
+        self.ev = [torch.cuda.Event() for _ in range(2 * n_layers)]
+        for e in self.ev:
+            e.record()            # materialises the underlying event
+        self.arr = (ctypes.c_void_p * len(self.ev))(*[e.cuda_event for e in self.ev])
+
+
 def _chunk_array(chunks: Sequence[ChunkSource]):
     arr = (cb_chunk * max(1, len(chunks)))()
     for i, c in enumerate(chunks):
@@ -278,6 +311,40 @@ class BlendParams:
         self._k = (ctypes.c_int32 * L)(*[int(v) for v in k_per_layer])
         self._c = (ctypes.c_uint8 * L)(*[1 if v else 0 for v in check])
         self.c = cb_blend_params(self._k, self._c, flags)
+
+
+def cb_streamed_workspace_bytes(cfg: cb_model_cfg, n_ctx: int, n_query: int, n_chunks: int) -> int:
+    return int(_abi.load().cb_streamed_workspace_bytes(ctypes.byref(cfg), n_ctx, n_query, n_chunks))
+
+
+def cb_loading_ratio(kv_bytes_per_token: float, n_tokens: float, load_bytes_per_s: float, prefill_seconds: float,
+                     r_min: float = 0.15) -> float:
+    return float(_abi.load().cb_loading_ratio(float(kv_bytes_per_token), float(n_tokens), float(load_bytes_per_s),
+                                              float(prefill_seconds), float(r_min)))
+
+
+def cb_blend_prefill_streamed(model: DeviceModel, chunks: Sequence[HostChunk], query_tokens: torch.Tensor,
+                              params: BlendParams, blended: PagedKV, logits: torch.Tensor,
+                              hkvd_out: Optional[torch.Tensor] = None, dev_out: Optional[torch.Tensor] = None,
+                              ws: Optional[Workspace] = None, stream=None, copy_stream=None,
+                              events: Optional[LayerEvents] = None):
+    """Enqueues the layer-pipelined prefill and returns (events, copy_stream, workspace):
+    the caller keeps them, and the host chunks, alive until `stream` has finished."""
+    lib = _abi.load()
+    n_ctx = sum(c.len for c in chunks)
+    w = _ws(ws, cb_streamed_workspace_bytes(model.cfg, n_ctx, int(query_tokens.numel()), len(chunks)),
+            logits.device)
+    arr = (cb_host_chunk * max(1, len(chunks)))()
+    for i, c in enumerate(chunks):
+        arr[i] = c.c()
+    ev = events if events is not None else LayerEvents(model.shape.n_layers)
+    cs = copy_stream if copy_stream is not None else torch.cuda.Stream()
+    _check(lib.cb_blend_prefill_streamed(ctypes.byref(model.c), arr, len(chunks), _p(query_tokens),
+                                         int(query_tokens.numel()), ctypes.byref(params.c), ctypes.byref(blended.c),
+                                         _p(logits), _p(hkvd_out), _p(dev_out), w.ptr, w.nbytes, _stream(stream),
+                                         _stream(cs), ev.arr),
+           "cb_blend_prefill_streamed")
+    return ev, cs, w
 
 
 def cb_blend_prefill(model: DeviceModel, chunks: Sequence[ChunkSource], query_tokens: torch.Tensor,

@@ -281,14 +281,16 @@ ChunkBatch make_batch(const cb_model_cfg& c, const cb_chunk* ch, int first, int 
   return b;
 }
 
+// table_ready: dtab already holds the deltas of this (single) batch of chunks
 cb_status enqueue_rerope(const cb_model_cfg& c, const cb_chunk* ch, int n, const cb_paged_kv& dst, int copy_v,
-                         float2* dtab, hipStream_t s, Tracer* tr) {
+                         float2* dtab, hipStream_t s, Tracer* tr, bool table_ready = false) {
   const PagedRef d = ref_of(dst);
   const int width = c.n_kv_heads * c.head_dim;
   for (int first = 0; first < n; first += kMaxChunksPerLaunch) {
     const int cnt = std::min(kMaxChunksPerLaunch, n - first);
     ChunkBatch b = make_batch(c, ch, first, cnt);
-    CB_LAUNCH(tr, CB_KIND_OTHER, launch_rope_delta_table(dtab, b, c.head_dim, c.rope_theta, s), "rope delta table");
+    if (!table_ready || n > kMaxChunksPerLaunch)
+      CB_LAUNCH(tr, CB_KIND_OTHER, launch_rope_delta_table(dtab, b, c.head_dim, c.rope_theta, s), "rope delta table");
     CB_LAUNCH(tr, CB_KIND_REROPE, launch_rerope(c.dtype, b, d, dtab, c.n_layers, width, c.head_dim, copy_v, s), "rerope");
   }
   return CB_OK;
@@ -616,38 +618,89 @@ cb_status cb_blend_layer(const cb_model* model, int32_t layer, const cb_paged_kv
   return st == CB_OK ? ok() : st;
 }
 
-cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_t n_chunks,
-                           const int32_t* query_tokens, int32_t n_query, const cb_blend_params* params,
-                           const cb_paged_kv* blended, float* logits, int32_t* hkvd_out, float* dev_out, void* ws,
-                           size_t ws_bytes, cb_stream_t stream) {
-  cb_status st = check_model(model);
-  if (st != CB_OK) return st;
-  const cb_model_cfg& c = model->cfg;
-  if ((st = check_chunk_sources(&c, chunks, n_chunks, true)) != CB_OK) return st;
-  int64_t N64 = 0;
-  if ((st = check_tiling(chunks, n_chunks, &N64)) != CB_OK) return st;
-  const int N = static_cast<int>(N64);
-  if (n_query < 1) return fail(CB_ERR_INVALID, "n_query must be >= 1");
-  if (!query_tokens || !logits) return fail(CB_ERR_INVALID, "NULL query_tokens or logits");
-  if (!params || !params->k_per_layer || !params->check) return fail(CB_ERR_INVALID, "NULL params");
-  if (params->flags) return fail(CB_ERR_INVALID, "unknown params flags 0x%x", params->flags);
-  const int L = c.n_layers;
-  if (params->k_per_layer[0] != N)
-    return fail(CB_ERR_INVALID, "k_per_layer[0] = %d, layer 0 runs in full (N = %d)", params->k_per_layer[0], N);
-  for (int l = 1; l < L; ++l) {
-    const int k = params->k_per_layer[l], kp = params->k_per_layer[l - 1];
-    if (k < 0 || k > kp)
-      return fail(CB_ERR_INVALID, "k_per_layer[%d] = %d must lie in [0, k_per_layer[%d] = %d]", l, k, l - 1, kp);
-    if (!params->check[l] && k != kp)
-      return fail(CB_ERR_INVALID, "layer %d is unchecked but shrinks the set (%d -> %d)", l, kp, k);
-  }
-  if ((st = check_paged(&c, blended, N64 + n_query, "blended")) != CB_OK) return st;
-  if (!aligned16(logits)) return fail(CB_ERR_INVALID, "logits not 16-byte aligned");
-  const size_t need = cb_workspace_bytes(&c, N, n_query, n_chunks);
-  if (!ws || ws_bytes < need) return fail(CB_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, need);
-  if (!aligned16(ws)) return fail(CB_ERR_INVALID, "workspace not 16-byte aligned");
+namespace {
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+// Layer-by-layer supply of the context KV from host memory (streamed prefill):
+// layer l of every chunk is copied into ring slot l % S on the copy stream, then
+// re-RoPE'd into layer l of the blended cache on the compute stream.
+struct StreamFeed {
+  const cb_host_chunk* hc = nullptr;
+  int n = 0;
+  int L = 0;
+  int S = 0;
+  hipStream_t copy = nullptr;
+  hipEvent_t* ev = nullptr;         // [2L]: copied[l], consumed[l]
+  char* ring_k = nullptr;
+  char* ring_v = nullptr;
+  int64_t slot_bytes = 0;
+  int64_t row_bytes = 0;            // one token's K (or V) row of one layer
+  std::vector<int64_t> pre;         // rows of the slot before chunk i
+  bool table_ready = false;
+};
+
+constexpr int kStreamSlots = 3;
+
+int stream_slots(const cb_model_cfg& c) { return std::min(c.n_layers, kStreamSlots); }
+
+int64_t stream_ring_bytes(const cb_model_cfg& c, int64_t n_ctx) {
+  return (int64_t)stream_slots(c) * 2 * n_ctx * c.n_kv_heads * c.head_dim * esize(c.dtype);
+}
+
+cb_status feed_copy(StreamFeed& f, int l) {
+  const int slot = l % f.S;
+  if (l >= f.S && hipStreamWaitEvent(f.copy, f.ev[f.L + l - f.S], 0) != hipSuccess)
+    return fail(CB_ERR_DEVICE, "copy stream: wait for layer %d", l - f.S);
+  for (int i = 0; i < f.n; ++i) {
+    const int64_t bytes = (int64_t)f.hc[i].len * f.row_bytes;
+    if (bytes == 0) continue;
+    const int64_t off = (int64_t)slot * f.slot_bytes + f.pre[i] * f.row_bytes;
+    if (hipMemcpyAsync(f.ring_k + off, static_cast<const char*>(f.hc[i].k) + l * bytes, bytes, hipMemcpyHostToDevice,
+                       f.copy) != hipSuccess ||
+        hipMemcpyAsync(f.ring_v + off, static_cast<const char*>(f.hc[i].v) + l * bytes, bytes, hipMemcpyHostToDevice,
+                       f.copy) != hipSuccess)
+      return fail(CB_ERR_DEVICE, "host -> device copy of layer %d, chunk %d", l, i);
+  }
+  if (hipEventRecord(f.ev[l], f.copy) != hipSuccess) return fail(CB_ERR_DEVICE, "record copy event of layer %d", l);
+  return CB_OK;
+}
+
+cb_status feed_layer(StreamFeed& f, const cb_model_cfg& c, const cb_paged_kv& blended, int l, float2* dtab,
+                     hipStream_t s, Tracer* tr) {
+  if (hipStreamWaitEvent(s, f.ev[l], 0) != hipSuccess) return fail(CB_ERR_DEVICE, "wait for the copy of layer %d", l);
+  const int slot = l % f.S;
+  std::vector<cb_chunk> ch(f.n);
+  for (int i = 0; i < f.n; ++i) {
+    cb_chunk& x = ch[i];
+    std::memset(&x, 0, sizeof(x));
+    const int64_t off = (int64_t)slot * f.slot_bytes + f.pre[i] * f.row_bytes;
+    x.tokens = f.hc[i].tokens;
+    x.k = f.ring_k + off;
+    x.v = f.ring_v + off;
+    x.len = f.hc[i].len;
+    x.old_start = f.hc[i].old_start;
+    x.new_start = f.hc[i].new_start;
+  }
+  cb_model_cfg c1 = c;
+  c1.n_layers = 1;
+  cb_paged_kv d = blended;
+  d.k = static_cast<char*>(d.k) + (int64_t)l * d.layer_stride * esize(c.dtype);
+  d.v = static_cast<char*>(d.v) + (int64_t)l * d.layer_stride * esize(c.dtype);
+  cb_status st = enqueue_rerope(c1, ch.data(), f.n, d, 1, dtab, s, tr, f.table_ready);
+  if (st != CB_OK) return st;
+  f.table_ready = f.n <= kMaxChunksPerLaunch;   // one batch: the delta table stays valid
+  if (hipEventRecord(f.ev[f.L + l], s) != hipSuccess) return fail(CB_ERR_DEVICE, "record consumed event of layer %d", l);
+  return l + f.S < f.L ? feed_copy(f, l + f.S) : CB_OK;
+}
+
+// The blended prefill after validation.  feed == NULL: chunk caches on the
+// device, re-RoPE'd for every layer up front; else supplied layer by layer.
+cb_status blend_run(const cb_model* model, const cb_chunk* chunks, int32_t n_chunks, int N,
+                    const int32_t* query_tokens, int32_t n_query, const cb_blend_params* params,
+                    const cb_paged_kv* blended, float* logits, int32_t* hkvd_out, float* dev_out, void* ws,
+                    hipStream_t s, StreamFeed* feed) {
+  cb_status st;
+  const cb_model_cfg& c = model->cfg;
+  const int L = c.n_layers;
   const int Q = n_query;
   const int T = N + Q;
   Ws w;
@@ -659,8 +712,13 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
   if (tracer.t) tracer.t->used = 0;
   Tracer* tr = &tracer;
 
-  // a1: assemble + re-RoPE every layer of every chunk
-  if ((st = enqueue_rerope(c, chunks, n_chunks, *blended, 1, w.dtab, s, tr)) != CB_OK) return st;
+  // a1: assemble + re-RoPE every layer of every chunk (or start the layer feed)
+  if (!feed) {
+    if ((st = enqueue_rerope(c, chunks, n_chunks, *blended, 1, w.dtab, s, tr)) != CB_OK) return st;
+  } else {
+    for (int l = 0; l < feed->S; ++l)
+      if ((st = feed_copy(*feed, l)) != CB_OK) return st;
+  }
   CB_LAUNCH(tr, CB_KIND_OTHER, launch_rope_pos_table(w.pos_tab, T, c.head_dim, c.rope_theta, s), "rope table");
   // a2: tokens in new-position order, then embeddings
   {
@@ -682,6 +740,7 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
   if (hkvd_out) CB_LAUNCH(tr, CB_KIND_OTHER, launch_iota(hkvd_out, N, 0, s), "iota");
 
   // a3: layer 0 in full
+  if (feed && (st = feed_layer(*feed, c, *blended, 0, w.dtab, s, tr)) != CB_OK) return st;
   if ((st = enqueue_layer0(*model, kv, N, Q, w.x0, model->layers[1].attn_norm, w, s, tr)) != CB_OK) return st;
 
   // layers 1 .. L-1
@@ -693,6 +752,7 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
   int32_t* rp_out = w.rowpos1;
   int nc = N;
   for (int l = 1; l < L; ++l) {
+    if (feed && (st = feed_layer(*feed, c, *blended, l, w.dtab, s, tr)) != CB_OK) return st;
     const int k = params->k_per_layer[l];
     const int chk = params->check[l] ? 1 : 0;
     LayerIo io{};
@@ -721,6 +781,121 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
                         model->final_norm, c.rms_eps, w.a_last, c.d_model, 1, s), "final norm");
   CB_LAUNCH(tr, CB_KIND_LM_HEAD, launch_lmhead(c.dtype, w.a_last, model->lm_head, c.vocab, c.d_model, logits, s), "lm head");
   return ok();
+}
+
+// Validation shared by both prefills (chunk sources are checked by the caller).
+cb_status check_blend_call(const cb_model* model, int N, const int32_t* query_tokens, int32_t n_query,
+                           const cb_blend_params* params, const cb_paged_kv* blended, const float* logits) {
+  const cb_model_cfg& c = model->cfg;
+  if (n_query < 1) return fail(CB_ERR_INVALID, "n_query must be >= 1");
+  if (!query_tokens || !logits) return fail(CB_ERR_INVALID, "NULL query_tokens or logits");
+  if (!params || !params->k_per_layer || !params->check) return fail(CB_ERR_INVALID, "NULL params");
+  if (params->flags) return fail(CB_ERR_INVALID, "unknown params flags 0x%x", params->flags);
+  const int L = c.n_layers;
+  if (params->k_per_layer[0] != N)
+    return fail(CB_ERR_INVALID, "k_per_layer[0] = %d, layer 0 runs in full (N = %d)", params->k_per_layer[0], N);
+  for (int l = 1; l < L; ++l) {
+    const int k = params->k_per_layer[l], kp = params->k_per_layer[l - 1];
+    if (k < 0 || k > kp)
+      return fail(CB_ERR_INVALID, "k_per_layer[%d] = %d must lie in [0, k_per_layer[%d] = %d]", l, k, l - 1, kp);
+    if (!params->check[l] && k != kp)
+      return fail(CB_ERR_INVALID, "layer %d is unchecked but shrinks the set (%d -> %d)", l, kp, k);
+  }
+  cb_status st;
+  if ((st = check_paged(&c, blended, (int64_t)N + n_query, "blended")) != CB_OK) return st;
+  if (!aligned16(logits)) return fail(CB_ERR_INVALID, "logits not 16-byte aligned");
+  return CB_OK;
+}
+
+}  // namespace
+
+cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_t n_chunks,
+                           const int32_t* query_tokens, int32_t n_query, const cb_blend_params* params,
+                           const cb_paged_kv* blended, float* logits, int32_t* hkvd_out, float* dev_out, void* ws,
+                           size_t ws_bytes, cb_stream_t stream) {
+  cb_status st = check_model(model);
+  if (st != CB_OK) return st;
+  const cb_model_cfg& c = model->cfg;
+  if ((st = check_chunk_sources(&c, chunks, n_chunks, true)) != CB_OK) return st;
+  int64_t N64 = 0;
+  if ((st = check_tiling(chunks, n_chunks, &N64)) != CB_OK) return st;
+  const int N = static_cast<int>(N64);
+  if ((st = check_blend_call(model, N, query_tokens, n_query, params, blended, logits)) != CB_OK) return st;
+  const size_t need = cb_workspace_bytes(&c, N, n_query, n_chunks);
+  if (!ws || ws_bytes < need) return fail(CB_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(CB_ERR_INVALID, "workspace not 16-byte aligned");
+  return blend_run(model, chunks, n_chunks, N, query_tokens, n_query, params, blended, logits, hkvd_out, dev_out, ws,
+                   reinterpret_cast<hipStream_t>(stream), nullptr);
+}
+
+size_t cb_streamed_workspace_bytes(const cb_model_cfg* cfg, int32_t n_ctx, int32_t n_query, int32_t n_chunks) {
+  const size_t base = cb_workspace_bytes(cfg, n_ctx, n_query, n_chunks);
+  if (base == 0) return 0;
+  return base + static_cast<size_t>(stream_ring_bytes(*cfg, n_ctx));
+}
+
+cb_status cb_blend_prefill_streamed(const cb_model* model, const cb_host_chunk* chunks, int32_t n_chunks,
+                                    const int32_t* query_tokens, int32_t n_query, const cb_blend_params* params,
+                                    const cb_paged_kv* blended, float* logits, int32_t* hkvd_out, float* dev_out,
+                                    void* ws, size_t ws_bytes, cb_stream_t stream, cb_stream_t copy_stream,
+                                    void* const* events) {
+  cb_status st = check_model(model);
+  if (st != CB_OK) return st;
+  const cb_model_cfg& c = model->cfg;
+  if (n_chunks < 0) return fail(CB_ERR_INVALID, "n_chunks < 0");
+  if (n_chunks > 0 && !chunks) return fail(CB_ERR_INVALID, "chunks is NULL");
+  std::vector<cb_chunk> dev(n_chunks);
+  for (int i = 0; i < n_chunks; ++i) {
+    const cb_host_chunk& x = chunks[i];
+    if (x.len < 0) return fail(CB_ERR_INVALID, "chunk %d: len < 0", i);
+    if (x.old_start < 0)
+      return fail(CB_ERR_INVALID, "chunk %d: unknown stored offset %d (a wrong position gives wrong KV)", i, x.old_start);
+    if (x.new_start < 0) return fail(CB_ERR_INVALID, "chunk %d: new_start < 0", i);
+    if (x.len > 0 && (!x.k || !x.v || !x.tokens)) return fail(CB_ERR_INVALID, "chunk %d: NULL tokens or host K/V", i);
+    std::memset(&dev[i], 0, sizeof(cb_chunk));
+    dev[i].tokens = x.tokens;
+    dev[i].len = x.len;
+    dev[i].old_start = x.old_start;
+    dev[i].new_start = x.new_start;
+  }
+  int64_t N64 = 0;
+  if ((st = check_tiling(dev.data(), n_chunks, &N64)) != CB_OK) return st;
+  const int N = static_cast<int>(N64);
+  if ((st = check_blend_call(model, N, query_tokens, n_query, params, blended, logits)) != CB_OK) return st;
+  if (!events) return fail(CB_ERR_INVALID, "NULL events");
+  for (int i = 0; i < 2 * c.n_layers; ++i)
+    if (!events[i]) return fail(CB_ERR_INVALID, "event %d is NULL", i);
+  const size_t base = cb_workspace_bytes(&c, N, n_query, n_chunks);
+  const size_t need = cb_streamed_workspace_bytes(&c, N, n_query, n_chunks);
+  if (!ws || ws_bytes < need) return fail(CB_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(CB_ERR_INVALID, "workspace not 16-byte aligned");
+
+  StreamFeed f;
+  f.hc = chunks;
+  f.n = n_chunks;
+  f.L = c.n_layers;
+  f.S = stream_slots(c);
+  f.copy = reinterpret_cast<hipStream_t>(copy_stream);
+  f.ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(events));
+  f.row_bytes = (int64_t)c.n_kv_heads * c.head_dim * esize(c.dtype);
+  f.slot_bytes = (int64_t)N * f.row_bytes;
+  f.ring_k = static_cast<char*>(ws) + base;
+  f.ring_v = f.ring_k + f.S * f.slot_bytes;
+  f.pre.resize(n_chunks);
+  int64_t acc = 0;
+  for (int i = 0; i < n_chunks; ++i) {
+    f.pre[i] = acc;
+    acc += chunks[i].len;
+  }
+  return blend_run(model, dev.data(), n_chunks, N, query_tokens, n_query, params, blended, logits, hkvd_out, dev_out,
+                   ws, reinterpret_cast<hipStream_t>(stream), &f);
+}
+
+double cb_loading_ratio(double kv_bytes_per_token, double n_tokens, double load_bytes_per_s, double prefill_seconds,
+                        double r_min) {
+  if (!(prefill_seconds > 0) || !(load_bytes_per_s > 0) || kv_bytes_per_token < 0 || n_tokens < 0) return -1.0;
+  const double t_load = kv_bytes_per_token * n_tokens / load_bytes_per_s;
+  return std::max(r_min, std::min(1.0, t_load / prefill_seconds));
 }
 
 }  // extern "C"

@@ -338,8 +338,9 @@ __global__ __launch_bounds__(Tile<CFG>::kThreads, Tile<CFG>::WGS_PER_CU) void ge
 // Split-K reduction in fixed split order, then the epilogue, over the virtual
 // columns from c_part on (4 output columns per thread).  SWIGLU pairs gate
 // column 64 k + j with up column 64 k + 32 + j into feature 32 k + j.
-template <int EPI>
+template <int EPI, int SP>   // SP > 0: the split count, known at compile time
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int splits, int c_part) {
+  if constexpr (SP > 0) splits = SP;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int b_rows = (EPI == EPI_SWIGLU) ? 2 * g.N : g.N;
   const int64_t wpart = b_rows - c_part;
@@ -350,6 +351,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int spli
     const int fl = static_cast<int>(idx % f4) * 4;     // feature past c_part / 2
     const int gc = (fl >> 5) * 64 + (fl & 31);         // its gate column past c_part
     float4 gs = make_float4(0.f, 0.f, 0.f, 0.f), us = gs;
+#pragma unroll
     for (int sp = 0; sp < splits; ++sp) {
       const float* pr = g.part + (static_cast<int64_t>(sp) * g.M + row) * wpart + gc;
       const float4 a = *reinterpret_cast<const float4*>(pr);
@@ -369,6 +371,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int spli
   const int lc = static_cast<int>(idx % n4) * 4;
   const int col = c_part + lc;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
   for (int sp = 0; sp < splits; ++sp) {
     const float4 p = *reinterpret_cast<const float4*>(g.part + (static_cast<int64_t>(sp) * g.M + row) * wpart + lc);
     s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
@@ -790,7 +793,13 @@ hipError_t run_bm(const GemmArgs& a, int splits, int dp_cols, hipStream_t s, boo
     } else {
       const int64_t n = (EPI == EPI_SWIGLU) ? static_cast<int64_t>(a.M) * ((a.N - c_part / 2) / 4)
                                             : static_cast<int64_t>(a.M) * ((b_rows_of(a, EPI) - c_part) / 4);
-      splitk_reduce_kernel<EPI><<<static_cast<int>((n + 255) / 256), 256, 0, s>>>(a, eff, c_part);
+      const int nb = static_cast<int>((n + 255) / 256);
+      switch (eff) {
+        case 2: splitk_reduce_kernel<EPI, 2><<<nb, 256, 0, s>>>(a, eff, c_part); break;
+        case 3: splitk_reduce_kernel<EPI, 3><<<nb, 256, 0, s>>>(a, eff, c_part); break;
+        case 4: splitk_reduce_kernel<EPI, 4><<<nb, 256, 0, s>>>(a, eff, c_part); break;
+        default: splitk_reduce_kernel<EPI, 0><<<nb, 256, 0, s>>>(a, eff, c_part); break;
+      }
     }
     return hipGetLastError();
   }

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 2
+#define CB_ABI_VERSION 3
 
 /* A HIP stream (hipStream_t); NULL is the null stream. */
 typedef struct ihipStream_t* cb_stream_t;
@@ -265,6 +265,60 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
                            const cb_blend_params* params, const cb_paged_kv* blended,
                            float* logits, int32_t* hkvd_out, float* dev_out, void* ws,
                            size_t ws_bytes, cb_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Layer-pipelined prefill from host-resident chunk caches.  The pages'
+ * loading pipeline ("CacheBlend 完全拆解", section 位置恢复、KV 存储与加载流水线):
+ * KV is fetched one layer at a time and the recompute of layer l overlaps the
+ * loading of the layers after it; the wait between layers is per layer.
+ *
+ * cb_host_chunk: as cb_chunk, but k / v are HOST pointers to page-locked
+ * memory (hipHostMalloc, or torch pin_memory), contiguous
+ * [n_layers][len][Hkv][dh] in the model dtype; tokens stay on the device.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const int32_t* tokens;    /* device [len] */
+  const void* k;            /* host, page-locked */
+  const void* v;            /* host, page-locked */
+  int32_t len, old_start, new_start;
+} cb_host_chunk;
+
+/* Workspace of cb_blend_prefill_streamed: cb_workspace_bytes plus a ring of
+ * min(n_layers, 3) slots, each one layer of every chunk's K and V. */
+size_t cb_streamed_workspace_bytes(const cb_model_cfg* cfg, int32_t n_ctx, int32_t n_query, int32_t n_chunks);
+
+/* cb_blend_prefill with the chunk caches in host memory.  For every layer l,
+ * each chunk's K and V of that layer are copied host -> device on copy_stream
+ * into a workspace ring slot; `stream` waits for that copy (events[l]), re-RoPEs
+ * the slot into layer l of `blended` and records events[n_layers + l], which the
+ * copy of layer l + 3 (reusing the slot) waits for.  Every copy is enqueued
+ * before the compute that needs it, so the copies of later layers run while
+ * earlier layers are recomputed.
+ *   events: HOST array of 2 * n_layers HIP events created by the caller
+ *     (hipEventCreateWithFlags with hipEventDisableTiming is enough); they are
+ *     recorded and waited on, never created or destroyed here.
+ *   copy_stream: the stream for the host -> device copies (it should differ
+ *     from `stream`, else nothing overlaps; the result is the same).
+ * Results are bitwise those of cb_blend_prefill on the same chunk contents.
+ * The host chunk memory, the events and both streams must stay valid until
+ * `stream` has completed the call's work (the copies are ordered before it). 
+ * Errors as cb_blend_prefill, plus CB_ERR_INVALID for a NULL host pointer or
+ * event; ws: at least cb_streamed_workspace_bytes(...). */
+cb_status cb_blend_prefill_streamed(const cb_model* model, const cb_host_chunk* chunks, int32_t n_chunks,
+                                    const int32_t* query_tokens, int32_t n_query,
+                                    const cb_blend_params* params, const cb_paged_kv* blended,
+                                    float* logits, int32_t* hkvd_out, float* dev_out, void* ws,
+                                    size_t ws_bytes, cb_stream_t stream, cb_stream_t copy_stream,
+                                    void* const* events);
+
+/* The loading controller of the same section: recomputing a share r of the
+ * tokens costs r * prefill_seconds, loading the cache costs
+ * kv_bytes_per_token * n_tokens / load_bytes_per_s; the controller takes the r
+ * at which the two match, but never less than the quality floor r_min (the
+ * pages use 15%).  Returns max(r_min, min(1, T_load / T_prefill)), or -1 for
+ * non-positive prefill_seconds or load_bytes_per_s or negative sizes. */
+double cb_loading_ratio(double kv_bytes_per_token, double n_tokens, double load_bytes_per_s,
+                        double prefill_seconds, double r_min);
 
 /* ---------------------------------------------------------------------------
  * cb_pack_weight -- one layer matrix of a CB_BF16 model into the layout its

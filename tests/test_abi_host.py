@@ -32,7 +32,8 @@ def test_exports_every_declared_function(lib):
     names = _abi.header_functions()
     assert {"cb_rerope_k", "cb_kv_deviation", "cb_select_hkvd", "cb_blend_layer", "cb_blend_prefill",
             "cb_workspace_bytes", "cb_status_string", "cb_last_error", "cb_abi_version",
-            "cb_pack_weight", "cb_packed_weight_bytes"} <= set(names)
+            "cb_pack_weight", "cb_packed_weight_bytes", "cb_blend_prefill_streamed",
+            "cb_streamed_workspace_bytes", "cb_loading_ratio"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True, text=True).stdout
@@ -56,6 +57,7 @@ int main(void) {
   P(cb_chunk) O(cb_chunk, len) O(cb_chunk, new_start) O(cb_chunk, layer_stride)
   P(cb_blend_params) O(cb_blend_params, flags) O(cb_blend_params, trace)
   P(cb_trace) O(cb_trace, used) O(cb_trace, kinds)
+  P(cb_host_chunk) O(cb_host_chunk, v) O(cb_host_chunk, len) O(cb_host_chunk, new_start)
   return 0;
 }
 '''
@@ -66,7 +68,8 @@ int main(void) {
         subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
         lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
     got = dict(l.split() for l in lines if l.strip())
-    for name in ("cb_model_cfg", "cb_layer_w", "cb_model", "cb_paged_kv", "cb_chunk", "cb_blend_params", "cb_trace"):
+    for name in ("cb_model_cfg", "cb_layer_w", "cb_model", "cb_paged_kv", "cb_chunk", "cb_blend_params", "cb_trace",
+                 "cb_host_chunk"):
         cls = getattr(_abi, name)
         assert ctypes.sizeof(cls) == int(got[name]), name
     for key, v in got.items():
@@ -76,7 +79,7 @@ int main(void) {
 
 
 def test_status_strings_and_version(lib):
-    assert lib.cb_abi_version() == 2
+    assert lib.cb_abi_version() == 3
     for code, name in [(0, "CB_OK"), (-1, "CB_ERR_INVALID"), (-2, "CB_ERR_UNSUPPORTED"),
                        (-3, "CB_ERR_WORKSPACE"), (-4, "CB_ERR_DEVICE")]:
         assert lib.cb_status_string(code).decode() == name
@@ -265,3 +268,41 @@ def test_pack_weight_validation(lib):
     st = P(_abi.CB_BF16, FAKE, 64, 64, 0, FAKE + 1024, None)                              # overlap
     assert st == _abi.CB_ERR_INVALID and "overlap" in lib.cb_last_error().decode()
     assert P(_abi.CB_BF16, FAKE + 8, 64, 64, 0, FAKE + big, None) == _abi.CB_ERR_INVALID  # alignment
+
+
+def _streamed(lib, specs=((64, 0, 0), (64, 5, 64)), nq=8, events=True, ws_bytes=None, host_k=True):
+    cfg = cfg8b(n_layers=3)
+    m = _model(cfg)
+    arr = (_abi.cb_host_chunk * len(specs))()
+    for i, (ln, old, new) in enumerate(specs):
+        arr[i] = _abi.cb_host_chunk(FAKE, FAKE if host_k else None, FAKE, ln, old, new)
+    N = sum(s[0] for s in specs)
+    p = _params([N, 19, 19], [0, 1, 1])
+    kv = _paged(N + nq)
+    ev = (ctypes.c_void_p * 6)(*([FAKE] * 6)) if events else None
+    need = lib.cb_streamed_workspace_bytes(ctypes.byref(cfg), N, nq, len(specs))
+    ws = ws_bytes if ws_bytes is not None else need
+    st = lib.cb_blend_prefill_streamed(ctypes.byref(m), arr, len(specs), FAKE, nq, ctypes.byref(p), ctypes.byref(kv),
+                                       FAKE, None, None, FAKE, ws, None, None, ev)
+    return st, lib.cb_last_error().decode()
+
+
+def test_streamed_workspace_bytes(lib):
+    c = cfg8b()
+    base = lib.cb_workspace_bytes(ctypes.byref(c), 4096, 64, 4)
+    # three ring slots, each one layer of every chunk's K and V (4096 x 1024 bf16 each)
+    assert lib.cb_streamed_workspace_bytes(ctypes.byref(c), 4096, 64, 4) == base + 3 * 2 * 4096 * 1024 * 2
+    assert lib.cb_streamed_workspace_bytes(ctypes.byref(cfg8b(n_layers=1)), 4096, 64, 4) == 0
+
+
+def test_streamed_validation(lib):
+    st, msg = _streamed(lib, events=False)
+    assert st == _abi.CB_ERR_INVALID and "events" in msg
+    st, msg = _streamed(lib, host_k=False)
+    assert st == _abi.CB_ERR_INVALID and "K/V" in msg
+    st, msg = _streamed(lib, specs=((64, -1, 0), (64, 5, 64)))
+    assert st == _abi.CB_ERR_INVALID and "unknown stored offset" in msg
+    st, msg = _streamed(lib, specs=((64, 0, 0), (64, 5, 60)))
+    assert st == _abi.CB_ERR_INVALID and "overlap" in msg
+    st, msg = _streamed(lib, ws_bytes=1024)
+    assert st == _abi.CB_ERR_WORKSPACE

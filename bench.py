@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-runs", type=int, default=5,
                     help="extra untimed-by-contract runs, each after evicting the Infinity Cache")
+    ap.add_argument("--streamed-runs", type=int, default=3,
+                    help="runs of the layer-pipelined prefill from host memory (0: skip)")
     ap.add_argument("--sweep", action="store_true",
                     help="only the size sweep of cb_rerope_k and cb_kv_deviation (one JSON line per size)")
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
@@ -269,6 +271,50 @@ def kernel_sweep(torch, dev):
         del cache, kf, pos, out
 
 
+def streamed_runs(torch, api, model, chunks, qtok, params, blended, logits, hkvd, N, runs):
+    """The layer-pipelined prefill with the chunk caches in page-locked host
+    memory: per-run time (host -> device copies included), the time a plain copy
+    of the same bytes takes alone, and how much of it the recompute hides."""
+    import numpy as np
+    host = []
+    for c in chunks:
+        hk = torch.empty(c.k.shape, dtype=c.k.dtype, pin_memory=True)
+        hv = torch.empty(c.v.shape, dtype=c.v.dtype, pin_memory=True)
+        hk.copy_(c.k.cpu())
+        hv.copy_(c.v.cpu())
+        host.append(api.HostChunk(c.tokens, hk, hv, c.old_start, c.new_start))
+    kv_bytes = sum(2 * h.k.numel() * h.k.element_size() for h in host)
+    # a plain copy of the same bytes, alone
+    dst = [torch.empty(h.k.shape, dtype=h.k.dtype, device="cuda") for h in host]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        e0.record()
+        for h, d in zip(host, dst):
+            d.copy_(h.k, non_blocking=True)
+            d.copy_(h.v, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1)
+    del dst
+    cs = torch.cuda.Stream()
+    ev = api.LayerEvents(model.shape.n_layers)
+    ws = api.Workspace(api.cb_streamed_workspace_bytes(model.cfg, N, int(qtok.numel()), len(host)))
+    ts = []
+    for r in range(runs + 1):
+        e0.record()
+        api.cb_blend_prefill_streamed(model, host, qtok, params, blended, logits, hkvd, None, ws, copy_stream=cs,
+                                      events=ev)
+        e1.record()
+        torch.cuda.synchronize()
+        if r > 0:
+            ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    return {"ms_per_step": round(ms, 4), "context_tokens_per_s": round(N / (ms * 1e-3), 1),
+            "kv_bytes_from_host": kv_bytes, "plain_h2d_copy_ms": round(copy_ms, 4),
+            "h2d_gbs": round(kv_bytes / (copy_ms * 1e-3) / 1e9, 1), "runs": runs,
+            "note": "chunk caches in page-locked host memory, copied layer by layer inside the timed call"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -409,6 +455,9 @@ def main():
         cold.append(c0.elapsed_time(c1))
     del evict
     peaks = measured_peaks(torch, dev) if args.peaks else None
+    streamed = None
+    if args.streamed_runs > 0 and not wl.paged:
+        streamed = streamed_runs(torch, api, model, chunks, qtok, plain, blended, logits, hkvd, N, args.streamed_runs)
 
     roof.update({"kernel": dominant, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
                  "traffic": traffic_from_profile(dominant, wl.name), "launches_per_step": kind_n[dominant], "avg_launch_ms": round(avg_launch_ms, 4),
@@ -449,6 +498,7 @@ def main():
         "cold_ms_per_step": ({"median": round(float(np.median(cold)), 4), "min": round(min(cold), 4), "runs": len(cold)}
                              if cold else None),
         "measured_peaks": peaks,
+        "streamed": streamed,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

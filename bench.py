@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-runs", type=int, default=5,
                     help="extra untimed-by-contract runs, each after evicting the Infinity Cache")
+    ap.add_argument("--decode-steps", type=int, default=16,
+                    help="decode steps timed on the blended cache after the runs (0: skip)")
     ap.add_argument("--streamed-runs", type=int, default=3,
                     help="runs of the layer-pipelined prefill from host memory (0: skip)")
     ap.add_argument("--sweep", action="store_true",
@@ -271,6 +273,34 @@ def kernel_sweep(torch, dev):
         del cache, kf, pos, out
 
 
+def decode_runs(torch, api, model, shape, blended, logits, T, steps):
+    """Decode steps straight on the blended cache (positions T, T+1, ...): time
+    per token and the HBM rate of what one step must read (every weight matrix,
+    the LM head and the cache of every layer up to the position)."""
+    import numpy as np
+    ws = api.Workspace(api.cb_decode_workspace_bytes(model.cfg))
+    tok = torch.tensor([1234], dtype=torch.int32, device="cuda")
+    if blended.n_tokens < T + steps + 1:
+        return None
+    api.cb_decode_step(model, blended, T, tok, logits, ws)       # warm-up (position T)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        api.cb_decode_step(model, blended, T + i, tok, logits, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    es = 2 if shape.dtype == "bf16" else 4
+    d, F, qw, kvw = shape.d_model, shape.d_ff, shape.q_width, shape.kv_width
+    w_bytes = shape.n_layers * (d * (qw + 2 * kvw) + qw * d + 2 * F * d + F * d) * es + shape.vocab * d * es
+    kv_bytes = shape.n_layers * (T + steps / 2) * kvw * 2 * es
+    gbs = (w_bytes + kv_bytes) / (ms * 1e-3) / 1e9
+    return {"ms_per_token": round(ms, 4), "tokens_per_s": round(1e3 / ms, 1), "steps": steps, "from_position": T,
+            "bytes_per_token": int(w_bytes + kv_bytes), "achieved_gbs": round(gbs, 1),
+            "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def streamed_runs(torch, api, model, chunks, qtok, params, blended, logits, hkvd, N, runs):
     """The layer-pipelined prefill with the chunk caches in page-locked host
     memory: per-run time (host -> device copies included), the time a plain copy
@@ -366,12 +396,12 @@ def main():
                                           block_ids=ints(ids), block_size=16,
                                           layer_stride=n_phys * 16 * shape.kv_width))
         del kvs
-        table, n_phys = cbinputs.paged_layout(T, 16, args.seed, key=77, spare_blocks=8)
-        blended = api.PagedKV(shape, T, 16, table, n_phys)
+        table, n_phys = cbinputs.paged_layout(T + 64, 16, args.seed, key=77, spare_blocks=8)
+        blended = api.PagedKV(shape, T + 64, 16, table, n_phys)
     else:
         chunks = [api.ChunkSource(ints(wl.chunk_tokens[c]), kvs[c][0], kvs[c][1], wl.old_starts[c], wl.new_starts[c])
                   for c in range(len(kvs))]
-        blended = api.PagedKV(shape, T, 16)
+        blended = api.PagedKV(shape, T + 64, 16)   # room for the decode steps after the prefill
     qtok = ints(wl.query_tokens)
     logits = torch.empty(shape.vocab, device=dev)
     hkvd = torch.empty((shape.n_layers, N), dtype=torch.int32, device=dev)
@@ -455,6 +485,7 @@ def main():
         cold.append(c0.elapsed_time(c1))
     del evict
     peaks = measured_peaks(torch, dev) if args.peaks else None
+    decode = decode_runs(torch, api, model, shape, blended, logits, T, args.decode_steps) if args.decode_steps else None
     streamed = None
     if args.streamed_runs > 0 and not wl.paged:
         streamed = streamed_runs(torch, api, model, chunks, qtok, plain, blended, logits, hkvd, N, args.streamed_runs)
@@ -499,6 +530,7 @@ def main():
                              if cold else None),
         "measured_peaks": peaks,
         "streamed": streamed,
+        "decode": decode,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

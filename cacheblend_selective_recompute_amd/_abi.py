@@ -88,6 +88,9 @@ _PROTOS = {
                                           c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, POINTER(c_void_p)]),
     "cb_streamed_workspace_bytes": (c_size_t, [POINTER(cb_model_cfg), c_int32, c_int32, c_int32]),
     "cb_loading_ratio": (c_double, [c_double, c_double, c_double, c_double, c_double]),
+    "cb_decode_step": (c_int, [POINTER(cb_model), POINTER(cb_paged_kv), c_int32, c_void_p, c_void_p, c_void_p,
+                               c_size_t, c_void_p]),
+    "cb_decode_workspace_bytes": (c_size_t, [POINTER(cb_model_cfg)]),
     "cb_pack_weight": (c_int, [c_int, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
     "cb_packed_weight_bytes": (c_size_t, [c_int, c_int64, c_int64]),
     "cb_workspace_bytes": (c_size_t, [POINTER(cb_model_cfg), c_int32, c_int32, c_int32]),

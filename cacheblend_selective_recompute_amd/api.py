@@ -347,6 +347,19 @@ def cb_blend_prefill_streamed(model: DeviceModel, chunks: Sequence[HostChunk], q
     return ev, cs, w
 
 
+def cb_decode_workspace_bytes(cfg: cb_model_cfg) -> int:
+    return int(_abi.load().cb_decode_workspace_bytes(ctypes.byref(cfg)))
+
+
+def cb_decode_step(model: DeviceModel, kv: PagedKV, pos: int, token: torch.Tensor, logits: torch.Tensor,
+                   ws: Optional[Workspace] = None, stream=None) -> None:
+    """One token at position `pos` through every layer over the cache [0, pos); its K/V land at pos."""
+    lib = _abi.load()
+    w = _ws(ws, cb_decode_workspace_bytes(model.cfg), logits.device)
+    _check(lib.cb_decode_step(ctypes.byref(model.c), ctypes.byref(kv.c), int(pos), _p(token), _p(logits), w.ptr,
+                              w.nbytes, _stream(stream)), "cb_decode_step")
+
+
 def cb_blend_prefill(model: DeviceModel, chunks: Sequence[ChunkSource], query_tokens: torch.Tensor,
                      params: BlendParams, blended: PagedKV, logits: torch.Tensor,
                      hkvd_out: Optional[torch.Tensor] = None, dev_out: Optional[torch.Tensor] = None,

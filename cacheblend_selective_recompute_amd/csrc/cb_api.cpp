@@ -891,6 +891,87 @@ cb_status cb_blend_prefill_streamed(const cb_model* model, const cb_host_chunk* 
                    ws, reinterpret_cast<hipStream_t>(stream), &f);
 }
 
+size_t cb_decode_workspace_bytes(const cb_model_cfg* cfg) {
+  if (check_cfg(cfg) != CB_OK) return 0;
+  return carve(*cfg, 0, 1, 0, nullptr, nullptr);
+}
+
+cb_status cb_decode_step(const cb_model* model, const cb_paged_kv* kv, int32_t pos, const int32_t* token,
+                         float* logits, void* ws, size_t ws_bytes, cb_stream_t stream) {
+  cb_status st = check_model(model);
+  if (st != CB_OK) return st;
+  const cb_model_cfg& c = model->cfg;
+  if (pos < 0) return fail(CB_ERR_INVALID, "pos < 0");
+  if (!token || !logits) return fail(CB_ERR_INVALID, "NULL token or logits");
+  if (!aligned16(logits)) return fail(CB_ERR_INVALID, "logits not 16-byte aligned");
+  if ((st = check_paged(&c, kv, (int64_t)pos + 1, "kv")) != CB_OK) return st;
+  const size_t need = cb_decode_workspace_bytes(&c);
+  if (!ws || ws_bytes < need) return fail(CB_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, need);
+  if (!aligned16(ws)) return fail(CB_ERR_INVALID, "workspace not 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Ws w;
+  carve(c, 0, 1, 0, ws, &w);
+  const PagedRef r = ref_of(*kv);
+  const int L = c.n_layers, d = c.d_model, F = c.d_ff;
+  const int qw = c.n_q_heads * c.head_dim;
+  const int kvw = c.n_kv_heads * c.head_dim;
+  // one row at position pos: the GEMM epilogues rotate with a one-row table and
+  // row position 0 (w.rowpos1); scatter and attention use the real position (w.rowpos0)
+  CB_TRY(launch_rope_pos_table(w.pos_tab, 1, c.head_dim, c.rope_theta, s, pos), "rope table");
+  CB_TRY(launch_iota(w.rowpos0, 1, pos, s), "position");
+  CB_TRY(launch_iota(w.rowpos1, 1, 0, s), "table row");
+  CB_TRY(launch_embed(c.dtype, token, 1, model->embed, d, w.x0, s), "embed");
+  CB_TRY(launch_rmsnorm(c.dtype, w.x0, nullptr, d, 1, d, model->layers[0].attn_norm, c.rms_eps, w.act, d, 0, s),
+         "rmsnorm");
+  for (int l = 0; l < L; ++l) {
+    const cb_layer_w& lw = model->layers[l];
+    GemmArgs g{};
+    g.A = w.act; g.lda = d; g.a_rows = nullptr; g.K = d; g.M = 1;
+    g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = w.rowpos1;
+    g.part = w.gemm_part; g.part_floats = kGemmPartFloats;
+    if (c.dtype == CB_BF16) {
+      g.B = lw.w_qkv; g.ldb = d; g.N = qw + 2 * kvw;
+      g.C = w.q; g.ldc = qw; g.q_cols = qw;
+      g.C2 = w.kvf; g.ldc2 = 2 * kvw; g.rope2_cols = kvw;
+      CB_TRY(launch_gemm(c.dtype, EPI_QKV, g, s), "qkv gemm");
+    } else {
+      g.B = lw.w_qkv; g.ldb = d; g.N = qw; g.C = w.q; g.ldc = qw; g.rope_cols = qw;
+      CB_TRY(launch_gemm(c.dtype, EPI_STORE_ROPE, g, s), "q gemm");
+      g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * esize(c.dtype); g.N = 2 * kvw;
+      g.C = w.kvf; g.ldc = 2 * kvw; g.rope_cols = kvw;
+      CB_TRY(launch_gemm(c.dtype, EPI_F32_ROPE, g, s), "kv gemm");
+    }
+    CB_TRY(launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, nullptr, w.rowpos0, 1, r, l, kvw, s), "scatter");
+    AttnArgs at{};
+    at.q = w.q; at.ldq = qw; at.o = w.o; at.ldo = qw; at.rowpos = w.rowpos0; at.R = 1;
+    at.cache = r; at.layer = l; at.n_q_heads = c.n_q_heads; at.n_kv_heads = c.n_kv_heads; at.head_dim = c.head_dim;
+    at.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
+    at.kv_bound = pos + 1;
+    at.part_o = w.attn_o;
+    at.part_ml = w.attn_ml;
+    CB_TRY(launch_attention(c.dtype, at, s), "attention");
+    g = GemmArgs{};
+    g.A = w.o; g.lda = qw; g.B = lw.w_o; g.ldb = qw; g.M = 1; g.N = d; g.K = qw;
+    g.C = w.x1; g.ldc = d; g.resid = w.x0; g.ld_resid = d;
+    g.part = w.gemm_part; g.part_floats = kGemmPartFloats;
+    g.norm_gain = lw.mlp_norm; g.norm_eps = c.rms_eps; g.norm_out = w.act;
+    CB_TRY(launch_gemm(c.dtype, EPI_RESID, g, s), "o gemm");
+    g = GemmArgs{};
+    g.A = w.act; g.lda = d; g.B = lw.w_gate_up; g.ldb = d; g.M = 1; g.N = F; g.K = d; g.C = w.h; g.ldc = F; g.ff = F;
+    g.part = w.gemm_part; g.part_floats = kGemmPartFloats;
+    CB_TRY(launch_gemm(c.dtype, EPI_SWIGLU, g, s), "gate/up gemm");
+    g = GemmArgs{};
+    g.A = w.h; g.lda = F; g.B = lw.w_down; g.ldb = F; g.M = 1; g.N = d; g.K = F;
+    g.C = w.x0; g.ldc = d; g.resid = w.x1; g.ld_resid = d;
+    g.part = w.gemm_part; g.part_floats = kGemmPartFloats;
+    if (l + 1 < L) { g.norm_gain = model->layers[l + 1].attn_norm; g.norm_eps = c.rms_eps; g.norm_out = w.act; }
+    CB_TRY(launch_gemm(c.dtype, EPI_RESID, g, s), "down gemm");
+  }
+  CB_TRY(launch_rmsnorm(c.dtype, w.x0, nullptr, d, 1, d, model->final_norm, c.rms_eps, w.a_last, d, 1, s), "final norm");
+  CB_TRY(launch_lmhead(c.dtype, w.a_last, model->lm_head, c.vocab, d, logits, s), "lm head");
+  return ok();
+}
+
 double cb_loading_ratio(double kv_bytes_per_token, double n_tokens, double load_bytes_per_s, double prefill_seconds,
                         double r_min) {
   if (!(prefill_seconds > 0) || !(load_bytes_per_s > 0) || kv_bytes_per_token < 0 || n_tokens < 0) return -1.0;

@@ -109,7 +109,8 @@ struct ChunkBatch {
 // ---------------------------------------------------------------------------
 
 // cos/sin(pos * theta_i) for pos in [0, rows): float2 [rows][dh/2]
-hipError_t launch_rope_pos_table(float2* out, int rows, int head_dim, double theta, hipStream_t s);
+// rows of cos/sin for positions first .. first + rows - 1
+hipError_t launch_rope_pos_table(float2* out, int rows, int head_dim, double theta, hipStream_t s, int first = 0);
 // cos/sin(delta_c * theta_i) per chunk of the batch: float2 [n][dh/2]
 hipError_t launch_rope_delta_table(float2* out, const ChunkBatch& b, int head_dim, double theta,
                                    hipStream_t s);

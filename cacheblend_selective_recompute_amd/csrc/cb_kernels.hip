@@ -64,12 +64,13 @@ __device__ __forceinline__ float2 rot_entry(double mult, int i, int dh, double t
   return make_float2(static_cast<float>(c), static_cast<float>(s));
 }
 
-__global__ void rope_pos_table_kernel(float2* out, int rows, int half, int dh, double theta) {
+// row r of the table holds the rotation of position first + r
+__global__ void rope_pos_table_kernel(float2* out, int rows, int first, int half, int dh, double theta) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= static_cast<int64_t>(rows) * half) return;
   const int r = static_cast<int>(idx / half);
   const int i = static_cast<int>(idx % half);
-  out[idx] = rot_entry(static_cast<double>(r), i, dh, theta);
+  out[idx] = rot_entry(static_cast<double>(first) + r, i, dh, theta);
 }
 
 __global__ void rope_delta_table_kernel(float2* out, ChunkBatch b, int half, int dh, double theta) {
@@ -520,11 +521,11 @@ inline int cdiv(int64_t a, int64_t b) { return static_cast<int>((a + b - 1) / b)
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_rope_pos_table(float2* out, int rows, int head_dim, double theta, hipStream_t s) {
+hipError_t launch_rope_pos_table(float2* out, int rows, int head_dim, double theta, hipStream_t s, int first) {
   const int half = head_dim / 2;
   const int64_t n = static_cast<int64_t>(rows) * half;
   if (n == 0) return hipSuccess;
-  rope_pos_table_kernel<<<cdiv(n, 256), 256, 0, s>>>(out, rows, half, head_dim, theta);
+  rope_pos_table_kernel<<<cdiv(n, 256), 256, 0, s>>>(out, rows, first, half, head_dim, theta);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 3
+#define CB_ABI_VERSION 4
 
 /* A HIP stream (hipStream_t); NULL is the null stream. */
 typedef struct ihipStream_t* cb_stream_t;
@@ -319,6 +319,29 @@ cb_status cb_blend_prefill_streamed(const cb_model* model, const cb_host_chunk* 
  * non-positive prefill_seconds or load_bytes_per_s or negative sizes. */
 double cb_loading_ratio(double kv_bytes_per_token, double n_tokens, double load_bytes_per_s,
                         double prefill_seconds, double r_min);
+
+/* ---------------------------------------------------------------------------
+ * cb_decode_step -- one decoding step straight on the blended cache ("CacheBlend
+ * 完全拆解": Fig. 11, the fused KV is handed to the engine, which starts from
+ * decoding; section 问题, a new token's query is dotted with the stored K and
+ * weights the stored V, no earlier hidden state is recomputed).
+ *   kv: positions [0, pos) of every layer are filled (e.g. by cb_blend_prefill
+ *     with N + n_query = pos); the block table must cover pos + 1 tokens.
+ *   token: device int32 [1], the token at position pos.
+ *   Steps, for every layer: RMSNorm, Q/K/V projection with RoPE at pos, the
+ *   token's K/V written at pos, causal attention over [0, pos] through the
+ *   block table, O projection + residual, RMSNorm, SwiGLU MLP + residual; then
+ *   the final RMSNorm and the LM head.
+ *   logits: fp32 [vocab].
+ * ws: at least cb_decode_workspace_bytes(&model->cfg) bytes.
+ * Errors: CB_ERR_INVALID for NULL pointers, pos < 0, a short block table;
+ * CB_ERR_WORKSPACE for a small workspace.
+ * ------------------------------------------------------------------------- */
+cb_status cb_decode_step(const cb_model* model, const cb_paged_kv* kv, int32_t pos, const int32_t* token,
+                         float* logits, void* ws, size_t ws_bytes, cb_stream_t stream);
+
+/* Workspace bytes of cb_decode_step (0 for an invalid cfg). */
+size_t cb_decode_workspace_bytes(const cb_model_cfg* cfg);
 
 /* ---------------------------------------------------------------------------
  * cb_pack_weight -- one layer matrix of a CB_BF16 model into the layout its

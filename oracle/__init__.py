@@ -26,5 +26,5 @@ from .blend import (  # noqa: F401
     OracleModel, store_round, rms_norm, rope_cos_sin, rope, rerope, causal_attention,
     swiglu_mlp, kv_deviation, select_hkvd, full_prefill, chunk_prefill,
     assemble_blended, full_reuse_prefill, blend_prefill, blend_prefill_masked,
-    blend_layer, flop_count,
+    blend_layer, flop_count, decode_step,
 )

@@ -279,6 +279,27 @@ def full_prefill(m: OracleModel, tokens: np.ndarray, start: int = 0) -> Dict[str
     return {"K": K, "V": V, "x": x, "logits": _logits(m, x[-1])}
 
 
+def decode_step(m: OracleModel, Kb: np.ndarray, Vb: np.ndarray, token: int, pos: int) -> np.ndarray:
+    """One decoding step on a filled cache ([CB] 问题: the new token's query is
+    dotted with the stored K and weights the stored V, no earlier hidden state
+    is recomputed; Fig. 11: decoding starts from the fused KV).
+
+    ``Kb``/``Vb`` [L][>= pos+1][H_kv][d_h] hold positions [0, pos); the token's
+    own K/V (storage dtype) are written at ``pos`` in place, then it attends to
+    [0, pos].  Returns the token's logits.
+    """
+    x = np.asarray(m.glob["embed"][[int(token)]], dtype=F64)
+    p = np.array([int(pos)])
+    keys = np.arange(int(pos) + 1)
+    for l in range(m.n_layers):
+        w = m.layer(l)
+        a = rms_norm(x, w["attn_norm"], m.rms_eps)
+        Kb[l, pos] = store_round(rope(m.heads(_proj(a, w["wk"]), m.n_kv_heads), p, m.rope_theta), m.storage)[0]
+        Vb[l, pos] = store_round(m.heads(_proj(a, w["wv"]), m.n_kv_heads), m.storage)[0]
+        x = _attn_mlp(m, w, x, a, p, Kb[l, :pos + 1], Vb[l, :pos + 1], keys)
+    return _logits(m, x[0])
+
+
 def chunk_prefill(m: OracleModel, tokens: np.ndarray, start: int) -> Tuple[np.ndarray, np.ndarray]:
     """Cached KV of one chunk prefilled alone at offset ``start``
     ([CB] "背景": each retrieved chunk is prefilled separately)."""

@@ -33,7 +33,8 @@ def test_exports_every_declared_function(lib):
     assert {"cb_rerope_k", "cb_kv_deviation", "cb_select_hkvd", "cb_blend_layer", "cb_blend_prefill",
             "cb_workspace_bytes", "cb_status_string", "cb_last_error", "cb_abi_version",
             "cb_pack_weight", "cb_packed_weight_bytes", "cb_blend_prefill_streamed",
-            "cb_streamed_workspace_bytes", "cb_loading_ratio"} <= set(names)
+            "cb_streamed_workspace_bytes", "cb_loading_ratio", "cb_decode_step",
+            "cb_decode_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True, text=True).stdout
@@ -79,7 +80,7 @@ int main(void) {
 
 
 def test_status_strings_and_version(lib):
-    assert lib.cb_abi_version() == 3
+    assert lib.cb_abi_version() == 4
     for code, name in [(0, "CB_OK"), (-1, "CB_ERR_INVALID"), (-2, "CB_ERR_UNSUPPORTED"),
                        (-3, "CB_ERR_WORKSPACE"), (-4, "CB_ERR_DEVICE")]:
         assert lib.cb_status_string(code).decode() == name
@@ -305,4 +306,23 @@ def test_streamed_validation(lib):
     st, msg = _streamed(lib, specs=((64, 0, 0), (64, 5, 60)))
     assert st == _abi.CB_ERR_INVALID and "overlap" in msg
     st, msg = _streamed(lib, ws_bytes=1024)
+    assert st == _abi.CB_ERR_WORKSPACE
+
+
+def test_decode_step_validation(lib):
+    cfg = cfg8b(n_layers=3)
+    m = _model(cfg)
+    need = lib.cb_decode_workspace_bytes(ctypes.byref(cfg))
+    assert need > 0 and lib.cb_decode_workspace_bytes(ctypes.byref(cfg8b(n_layers=1))) == 0
+    kv = _paged(100)
+    def call(pos=10, token=FAKE, kvp=kv, ws=need):
+        st = lib.cb_decode_step(ctypes.byref(m), ctypes.byref(kvp), pos, token, FAKE, FAKE, ws, None)
+        return st, lib.cb_last_error().decode()
+    st, msg = call(pos=-1)
+    assert st == _abi.CB_ERR_INVALID and "pos" in msg
+    st, msg = call(token=None)
+    assert st == _abi.CB_ERR_INVALID
+    st, msg = call(pos=112)          # the table covers 112 tokens: position 111 is the last one
+    assert st == _abi.CB_ERR_INVALID and "covers" in msg
+    st, msg = call(ws=need - 256)
     assert st == _abi.CB_ERR_WORKSPACE

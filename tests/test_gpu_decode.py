@@ -1,0 +1,108 @@
+"""GPU checks of cb_decode_step: decoding straight from the blended cache.
+
+* tiny fp32 and a reduced-width bf16 decoder: blended prefill on the GPU, then
+  three decode steps; the oracle's decode steps run on a host copy of the very
+  cache the GPU blended (so only the decode is compared), logits and the K/V
+  rows each step writes;
+* full 8B shape: a decode step of token u after the blend of query q equals the
+  last row of the blend of q + [u] (causality: the context never sees the
+  suffix, so both attend to the same cache), logits and the K/V row at that
+  position, within twice the bf16 tolerance (both sides carry bf16 error)."""
+import numpy as np
+import pytest
+import torch
+
+import cbinputs
+import oracle
+from cacheblend_selective_recompute_amd import api
+
+from gpu_helpers import blended_cache, check_sets, device_chunks, ints, rel, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+MINI8B = cbinputs.ModelShape("mini-8b-heads", 4, 1024, 8, 2, 128, 3584, 32000, 500000.0, dtype="bf16")
+
+
+def _blend_then_decode(shape, wl, w, kvs, steps, paged, tol, label, seed):
+    m = api.DeviceModel.from_numpy(shape, w)
+    chunks = device_chunks(shape, wl, kvs, seed=seed)
+    T = wl.n_total
+    kv = blended_cache(shape, T + steps, paged=paged, seed=seed, fill=0.0)
+    logits = torch.empty(shape.vocab, device="cuda")
+    ks, ch = wl.schedule()
+    api.cb_blend_prefill(m, chunks, ints(wl.query_tokens), api.BlendParams(ks, ch), kv, logits)
+    torch.cuda.synchronize()
+    K, V = kv.logical(T + steps)
+    Kb, Vb = to_np(K), to_np(V)          # the GPU's blended cache, positions [0, T)
+    om = oracle.OracleModel.from_shape(shape, w)
+    rng = np.random.default_rng(seed + 5)
+    ws = api.Workspace(api.cb_decode_workspace_bytes(m.cfg))
+    for i in range(steps):
+        tok = int(rng.integers(0, shape.vocab))
+        pos = T + i
+        api.cb_decode_step(m, kv, pos, ints([tok]), logits, ws)
+        torch.cuda.synchronize()
+        lo = oracle.decode_step(om, Kb, Vb, tok, pos)
+        K, V = kv.logical(pos + 1)
+        el = rel(to_np(logits), lo)
+        ek = rel(to_np(K[:, pos]), Kb[:, pos])
+        ev = rel(to_np(V[:, pos]), Vb[:, pos])
+        say(f"  {label} step {i} (pos {pos}): logits {el:.2e}, written K {ek:.2e} V {ev:.2e}")
+        assert el < tol and ek < tol and ev < tol
+        # the GPU's row feeds the next step on both sides
+        Kb[:, pos], Vb[:, pos] = to_np(K[:, pos]), to_np(V[:, pos])
+
+
+def test_decode_tiny_fp32_against_oracle():
+    say("decode: tiny fp32 after a 2 x 256 + 32 blend, 3 steps")
+    wl = cbinputs.make_workload("tiny-2x256-q32", seed=0)
+    shape = wl.shape
+    w = cbinputs.model_weights(shape, 0)
+    om = oracle.OracleModel.from_shape(shape, w)
+    kvs = [oracle.chunk_prefill(om, t, p) for t, p in zip(wl.chunk_tokens, wl.old_starts)]
+    kvs = [(K.astype(np.float32), V.astype(np.float32)) for K, V in kvs]
+    _blend_then_decode(shape, wl, w, kvs, 3, False, 1e-4, "tiny", 0)
+
+
+def test_decode_mini8b_bf16_paged_against_oracle():
+    say("decode: mini-8B bf16 after a paged 4 x 96 + 8 blend, 3 steps")
+    wl = cbinputs.make_workload("8b-4x1024-q64", seed=4, shape=MINI8B, chunk_len=96, n_query=8)
+    w = cbinputs.model_weights(MINI8B, 4)
+    kvs = cbinputs.synthetic_chunk_kv(MINI8B, wl.chunk_lens, 4)
+    _blend_then_decode(MINI8B, wl, w, kvs, 3, True, 2e-2, "mini-8B", 4)
+
+
+def test_decode_continues_the_blend_full_8b():
+    say("decode: full 8B shape, one step after the 4 x 1024 + 64 blend vs the blend with 65 query tokens")
+    shape = cbinputs.SHAPES["llama3-8b"]
+    wl = cbinputs.make_workload("8b-4x1024-q64", seed=0)
+    m = api.DeviceModel.from_tensors(shape, cbinputs.torch_device_weights(shape, 0))
+    kvs = cbinputs.torch_device_chunk_kv(shape, wl.chunk_lens, 0)
+    chunks = [api.ChunkSource(ints(wl.chunk_tokens[c]), kvs[c][0], kvs[c][1], wl.old_starts[c], wl.new_starts[c])
+              for c in range(len(kvs))]
+    N, Q = wl.n_ctx, wl.n_query
+    ks, ch = wl.schedule()
+    u = 4242
+    out = []
+    for q in (list(wl.query_tokens), list(wl.query_tokens) + [u]):
+        kv = blended_cache(shape, N + Q + 1, paged=True, seed=2, fill=0.0)
+        logits = torch.empty(shape.vocab, device="cuda")
+        hk = torch.full((shape.n_layers, N), -1, dtype=torch.int32, device="cuda")
+        api.cb_blend_prefill(m, chunks, ints(q), api.BlendParams(ks, ch), kv, logits, hk)
+        out.append((kv, logits, hk))
+    kv_a, lg_a, hk_a = out[0]
+    api.cb_decode_step(m, kv_a, N + Q, ints([u]), lg_a)
+    torch.cuda.synchronize()
+    kv_b, lg_b, hk_b = out[1]
+    for l in range(1, shape.n_layers):
+        a, b = set(hk_a[l, :ks[l]].tolist()), set(hk_b[l, :ks[l]].tolist())
+        assert len(a & b) >= 0.99 * ks[l], f"layer {l}: the two blends kept different sets"
+    el = rel(to_np(lg_a), to_np(lg_b))
+    Ka, Va = kv_a.logical(N + Q + 1)
+    Kb, Vb = kv_b.logical(N + Q + 1)
+    ek = rel(to_np(Ka[:, N + Q]), to_np(Kb[:, N + Q]))
+    ev = rel(to_np(Va[:, N + Q]), to_np(Vb[:, N + Q]))
+    say(f"  decode vs blend with the token appended: logits {el:.2e}, K row {ek:.2e}, V row {ev:.2e}")
+    # two bf16 paths (different GEMM plans and row counts), each held to 2e-2 of the exact
+    # values by the oracle tests: their difference is bounded by 4e-2
+    assert el < 4e-2 and ek < 4e-2 and ev < 4e-2

@@ -232,3 +232,27 @@ def test_blend_layer_out_rows_are_rows_of_the_full_call():
     K3, V3 = Kl.copy(), Vl.copy()
     blend_layer(m, 1, K3, V3, x, cand, Q, True, k)
     assert np.array_equal(K2, K3) and np.array_equal(V2, V3)
+
+
+def test_decode_step_continues_a_full_prefill():
+    # causality: the last row of a one-shot prefill over t_0..t_T is a decode step of
+    # t_T on the cache the prefill of t_0..t_{T-1} wrote (and writes the same K/V row)
+    from oracle import decode_step
+    w = _sharpen(cbinputs.model_weights(GQA, 11))
+    m = OracleModel.from_shape(GQA, w)
+    rng = np.random.default_rng(11)
+    toks = rng.integers(0, GQA.vocab, size=23)
+    T = 20
+    ref = full_prefill(m, toks[:T + 1])
+    part = full_prefill(m, toks[:T])
+    L, _, H, dh = part["K"].shape
+    Kb = np.zeros((L, T + 3, H, dh))
+    Vb = np.zeros_like(Kb)
+    Kb[:, :T], Vb[:, :T] = part["K"], part["V"]
+    lg = decode_step(m, Kb, Vb, int(toks[T]), T)
+    assert _rel(lg, ref["logits"]) < 1e-10
+    assert _rel(Kb[:, T], ref["K"][:, T]) < 1e-12 and _rel(Vb[:, T], ref["V"][:, T]) < 1e-12
+    # two more steps equal the prefill over the longer sequence
+    decode_step(m, Kb, Vb, int(toks[T + 1]), T + 1)
+    lg2 = decode_step(m, Kb, Vb, int(toks[T + 2]), T + 2)
+    assert _rel(lg2, full_prefill(m, toks[:T + 3])["logits"]) < 1e-10

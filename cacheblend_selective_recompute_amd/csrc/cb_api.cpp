@@ -921,6 +921,38 @@ cb_status cb_decode_step(const cb_model* model, const cb_paged_kv* kv, int32_t p
   CB_TRY(launch_iota(w.rowpos0, 1, pos, s), "position");
   CB_TRY(launch_iota(w.rowpos1, 1, 0, s), "table row");
   CB_TRY(launch_embed(c.dtype, token, 1, model->embed, d, w.x0, s), "embed");
+  if (c.dtype == CB_BF16) {
+    // matrix-vector products over the packed weights; the RMSNorms, the SwiGLU and the
+    // residual adds ride on their inputs and outputs
+    float* xcur = w.x0;
+    float* x1 = w.x1;                                        // xcur + O projection
+    float* xnext = static_cast<float*>(w.act);              // [d] fp32 (the activation block is unused here)
+    float* yqkv = static_cast<float*>(w.h);                  // fused Q/K/V product [qw + 2 kvw] fp32
+    bf16_t* hs = reinterpret_cast<bf16_t*>(yqkv + qw + 2 * (int64_t)kvw);   // SiLU(gate) * up [F] bf16
+    for (int l = 0; l < L; ++l) {
+      const cb_layer_w& lw = model->layers[l];
+      CB_TRY(launch_gemv(1, false, lw.w_qkv, qw + 2 * kvw, d, xcur, nullptr, lw.attn_norm, c.rms_eps, yqkv, nullptr,
+                         nullptr, s), "qkv");
+      CB_TRY(launch_decode_qkv(yqkv, qw, kvw, c.head_dim, w.pos_tab, w.q, r, l, pos, c.dtype, s), "qkv rope");
+      AttnArgs at{};
+      at.q = w.q; at.ldq = qw; at.o = w.o; at.ldo = qw; at.rowpos = w.rowpos0; at.R = 1;
+      at.cache = r; at.layer = l; at.n_q_heads = c.n_q_heads; at.n_kv_heads = c.n_kv_heads; at.head_dim = c.head_dim;
+      at.scale = 1.0f / sqrtf(static_cast<float>(c.head_dim));
+      at.kv_bound = pos + 1;
+      at.part_o = w.attn_o;
+      at.part_ml = w.attn_ml;
+      CB_TRY(launch_attention(c.dtype, at, s), "attention");
+      CB_TRY(launch_gemv(0, false, lw.w_o, d, qw, w.o, nullptr, nullptr, 0.f, x1, xcur, nullptr, s), "o");
+      CB_TRY(launch_gemv(1, true, lw.w_gate_up, 2 * F, d, x1, nullptr, lw.mlp_norm, c.rms_eps, hs, nullptr, nullptr,
+                         s), "gate/up");
+      CB_TRY(launch_gemv(2, false, lw.w_down, d, F, hs, nullptr, nullptr, 0.f, xnext, x1, nullptr, s), "down");
+      std::swap(xcur, xnext);
+    }
+    CB_TRY(launch_rmsnorm(c.dtype, xcur, nullptr, d, 1, d, model->final_norm, c.rms_eps, w.a_last, d, 1, s),
+           "final norm");
+    CB_TRY(launch_lmhead(c.dtype, w.a_last, model->lm_head, c.vocab, d, logits, s), "lm head");
+    return ok();
+  }
   CB_TRY(launch_rmsnorm(c.dtype, w.x0, nullptr, d, 1, d, model->layers[0].attn_norm, c.rms_eps, w.act, d, 0, s),
          "rmsnorm");
   for (int l = 0; l < L; ++l) {

@@ -800,7 +800,11 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs 
   }
 }
 
-// Merge the split-KV partials of one (row, q head) per wave, in split order.
+// Merge the split-KV partials of one (row, q head) per wave.  The lanes take
+// the splits' (max, sum) pairs side by side (one split per lane and pass), so a
+// row with many splits (a single decode row) costs a few dependent loads, not
+// one per split; the output sums then run over the splits in order, eight
+// loads in flight at a time.
 template <int DH>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_splits, int ksplit, int QT) {
   const int idx = blockIdx.x * 4 + (threadIdx.x >> 6);   // row * Hq + head
@@ -811,19 +815,33 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_spl
   const int t_last = min((row / QT + 1) * QT, a.R) - 1;
   const int kv_end = a.rowpos[t_last] + 1;
   const int ns = min(n_splits, (kv_end + ksplit - 1) / ksplit);
+  auto prow = [&](int sp) { return (static_cast<int64_t>(sp) * a.R + row) * a.n_q_heads + head; };
   float M = -INFINITY;
-  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, a.part_ml[(static_cast<int64_t>(sp) * a.R + row) * a.n_q_heads + head].x);
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) M = fmaxf(M, a.part_ml[prow(s0 + lane)].x);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
   constexpr int PER = DH / 64;
   float acc[PER] = {};
   float lsum = 0.f;
-  for (int sp = 0; sp < ns; ++sp) {
-    const int64_t pr = (static_cast<int64_t>(sp) * a.R + row) * a.n_q_heads + head;
-    const float2 ml = a.part_ml[pr];
-    const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
-    lsum += w * ml.y;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    float wl = 0.f;
+    if (s0 + lane < ns) {
+      const float2 ml = a.part_ml[prow(s0 + lane)];
+      wl = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+      lsum += wl * ml.y;
+    }
+    const int cnt = min(64, ns - s0);
+#pragma unroll 8
+    for (int j = 0; j < cnt; ++j) {
+      const float w = __shfl(wl, j, 64);
+      const float* po = a.part_o + prow(s0 + j) * DH + lane * PER;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] += w * a.part_o[pr * DH + lane * PER + e];
+      for (int e = 0; e < PER; ++e) acc[e] += w * po[e];
+    }
   }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) lsum += __shfl_xor(lsum, m, 64);
   const float inv = 1.0f / lsum;
   bf16_t* ob = static_cast<bf16_t*>(a.o);
   const int KO = a.n_q_heads * DH;
@@ -905,7 +923,7 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   // 5 splits 67 us, 2 splits 70 us)
   int n_splits = 1;
   if (base < 512 && a.part_o != nullptr) {
-    n_splits = std::min(kAttnMaxSplits, std::max(1, (512 + base - 1) / base));
+    n_splits = std::min(kAttnSplitCap, std::max(1, (512 + base - 1) / base));
     n_splits = std::min(n_splits, kv_blocks);
     if (static_cast<int64_t>(n_splits) * a.R * a.n_q_heads > kAttnPartialRows) n_splits = 1;
   }

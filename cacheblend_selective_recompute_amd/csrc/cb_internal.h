@@ -133,11 +133,25 @@ hipError_t launch_deviation(cb_dtype dt, const float* kf, const float* vf, int64
 // exact top-k by (dev desc, pos asc); outputs ascending
 hipError_t launch_select(const float* dev, const int32_t* pos, int n, int k, int32_t* sel_pos,
                          int32_t* sel_slot, hipStream_t s);
-// row maps after selection: gmap[i] (source row), rowpos[i] (position), for i < k + nq
-// copy_a / copy_b (nullable) also receive the kept positions [k]
-// top-k plus the layer's row maps in one launch (kept rows, then the nq suffix rows)
+// Decode-step matrix-vector product over a packed bf16 matrix (rows x K, K * 2
+// bytes at most 64 KiB): the input is bf16 packed row 0 (in_mode 0), bf16 of
+// RMSNorm(x + x2) * gain of fp32 vectors (1), or a plain bf16 vector (2).  Output
+// y[r] = (r1[r] + r2[r]) + W[r] . x in fp32 (r1, r2 nullable), or with
+// swiglu_out (rows a multiple of 64, row blocks alternating 32 gate and 32 up
+// rows) bf16 SiLU(gate) * up of rows / 2 features.
+hipError_t launch_gemv(int in_mode, bool swiglu_out, const void* w, int rows, int K, const void* x, const float* x2,
+                       const float* gain, float eps, void* y, const float* r1, const float* r2, hipStream_t s);
+// RoPE of the token's Q/K (rotation row `rot`), Q to bf16 row-major, K/V into
+// the paged cache at `pos` of `layer`
+hipError_t launch_decode_qkv(const float* y, int qw, int kvw, int head_dim, const float2* rot, void* q,
+                             const PagedRef& cache, int layer, int pos, cb_dtype dt, hipStream_t s);
+
+// top-k plus the layer's row maps in one launch (kept rows, then the nq suffix rows):
+// gmap[i] (source row), rowpos[i] (position), for i < k + nq; copy (nullable)
+// also receives the kept positions [k]
 hipError_t launch_select_rows(const float* dev, const int32_t* pos, int n, int k, int32_t* sel_pos, int32_t* sel_slot,
                               int n_ctx, int nq, int32_t* gmap, int32_t* rowpos, int32_t* copy, hipStream_t s);
+// the same row maps for an already selected set (copy_a / copy_b nullable)
 hipError_t launch_build_rows(const int32_t* sel_slot, const int32_t* sel_pos, int k, int nc, int n_ctx,
                              int nq, int32_t* gmap, int32_t* rowpos, int32_t* copy_a, int32_t* copy_b,
                              hipStream_t s);
@@ -237,6 +251,7 @@ hipError_t launch_attention_ng(cb_dtype dt, const AttnArgs& a, int ng, hipStream
 // workspace bound of the split-KV partials
 constexpr int kAttnMaxSplits = 8;
 constexpr int64_t kAttnPartialRows = int64_t(kAttnMaxSplits) * 32768;   // (split, row, q head) triples
+constexpr int kAttnSplitCap = 64;   // key splits of one launch (a single decode row uses many)
 inline int64_t attn_partial_floats(int head_dim) { return kAttnPartialRows * head_dim; }
 bool attention_supported(cb_dtype dt, int n_q_heads, int n_kv_heads, int head_dim);
 

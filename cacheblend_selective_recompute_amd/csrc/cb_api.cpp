@@ -927,13 +927,11 @@ cb_status cb_decode_step(const cb_model* model, const cb_paged_kv* kv, int32_t p
     float* xcur = w.x0;
     float* x1 = w.x1;                                        // xcur + O projection
     float* xnext = static_cast<float*>(w.act);              // [d] fp32 (the activation block is unused here)
-    float* yqkv = static_cast<float*>(w.h);                  // fused Q/K/V product [qw + 2 kvw] fp32
-    bf16_t* hs = reinterpret_cast<bf16_t*>(yqkv + qw + 2 * (int64_t)kvw);   // SiLU(gate) * up [F] bf16
+    bf16_t* hs = static_cast<bf16_t*>(w.h);                  // SiLU(gate) * up [F] bf16
     for (int l = 0; l < L; ++l) {
       const cb_layer_w& lw = model->layers[l];
-      CB_TRY(launch_gemv(1, false, lw.w_qkv, qw + 2 * kvw, d, xcur, nullptr, lw.attn_norm, c.rms_eps, yqkv, nullptr,
-                         nullptr, s), "qkv");
-      CB_TRY(launch_decode_qkv(yqkv, qw, kvw, c.head_dim, w.pos_tab, w.q, r, l, pos, c.dtype, s), "qkv rope");
+      CB_TRY(launch_gemv_qkv(lw.w_qkv, d, xcur, lw.attn_norm, c.rms_eps, qw, kvw, c.head_dim, w.pos_tab, w.q, r, l,
+                             pos, s), "qkv");
       AttnArgs at{};
       at.q = w.q; at.ldq = qw; at.o = w.o; at.ldo = qw; at.rowpos = w.rowpos0; at.R = 1;
       at.cache = r; at.layer = l; at.n_q_heads = c.n_q_heads; at.n_kv_heads = c.n_kv_heads; at.head_dim = c.head_dim;

@@ -27,6 +27,14 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+  return acc;
+}
+
 constexpr int KVB = 64;            // keys per block
 constexpr int kBtCache = 4096;     // block-table entries a workgroup stages in LDS
 constexpr float kLog2e = 1.4426950408889634f;
@@ -952,6 +960,233 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// One query row (a decode step): the G query heads of a KV head read each K/V
+// row once.  A workgroup takes one KV head and a range of keys, 64 per pass:
+// thread t scores key t / 4 on the 32 dims (t % 4) * 32 .. +31 for all G
+// heads (a quad adds its four parts), each wave redoes the pass's softmax
+// update in registers (lane = key), and wave w then adds keys 16 w .. 16 w + 15
+// into its lanes' two output dims per head; the V rows of the pass are loaded
+// while the scores are made.  Partials (unnormalised sums, running max in
+// log2 units, sum of weights) go to the split-KV buffers.
+// ---------------------------------------------------------------------------
+template <int DH, int G, bool RUN16>
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int ksplit) {
+  static_assert(DH == 128, "two output dims per lane");
+  __shared__ uint4 qs[G][DH / 8];        // bf16 query heads, 8 dims per entry
+  __shared__ float sc[G][64];
+  __shared__ float red[4][G][DH];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kvh = blockIdx.x % a.n_kv_heads;
+  const int split = blockIdx.x / a.n_kv_heads;
+  const int j_begin = split * ksplit;
+  const int j_lim = min(a.kv_bound, j_begin + ksplit);          // the table covers every key below kv_bound
+  if (j_begin >= j_lim) return;                                  // uniform per workgroup
+  const uint4* qrow = reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.q) + static_cast<int64_t>(kvh) * G * DH);
+  uint4 qv = {};
+  if (tid < G * DH / 8) qv = qrow[tid];   // stored to LDS once the first K/V loads are out
+  const float sc_l2 = a.scale * kLog2e;
+  const int width = a.n_kv_heads * DH;
+  const int64_t lbase = static_cast<int64_t>(a.layer) * a.cache.layer_stride + kvh * DH;
+  const bf16_t* kc = static_cast<const bf16_t*>(a.cache.k) + lbase;
+  const bf16_t* vc = static_cast<const bf16_t*>(a.cache.v) + lbase;
+  const int kk = tid >> 2, quarter = tid & 3;
+  // loads run to j_lim without waiting for the row's position; keys past it are masked
+  const int j_end = min(a.rowpos[0] + 1, j_lim);
+  float m_run[G], l_run[G], acc[G][2];
+#pragma unroll
+  for (int g = 0; g < G; ++g) { m_run[g] = -INFINITY; l_run[g] = 0.f; acc[g][0] = acc[g][1] = 0.f; }
+  for (int t0 = j_begin; t0 < j_lim; t0 += 64) {
+    // K: this thread's 32 dims of key t0 + kk; V: keys t0 + 16 wid + i, dims 2 lane, 2 lane + 1.
+    // Both are wave w's 16 keys from t0 + 16 w, a multiple of 16: with pages of 16
+    // keys or more they are 16 consecutive rows, found with one table lookup.
+    // Keys at or past j_lim are clamped to j_lim - 1, so every load is in range
+    // and issued unconditionally; their scores and values are masked below.
+    const int key = t0 + kk;
+    const int kw0 = t0 + 16 * wid;
+    const int last = j_lim - 1;
+    int64_t krow, vrow[16];
+    if constexpr (RUN16) {
+      const int g0 = min(kw0, last & ~15);                       // the 16-key run holding the clamped keys
+      const int64_t rbase = paged_row(a.cache, g0);
+      krow = rbase + (min(key, last) - g0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vrow[i] = rbase + (min(kw0 + i, last) - g0);
+    } else {
+      krow = paged_row(a.cache, min(key, last));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vrow[i] = paged_row(a.cache, min(kw0 + i, last));
+    }
+    uint4 kr[4];
+    const uint4* kp = reinterpret_cast<const uint4*>(kc + krow * width + quarter * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kr[i] = kp[i];
+    uint32_t vr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) vr[i] = *reinterpret_cast<const uint32_t*>(vc + vrow[i] * width + 2 * lane);
+    if (t0 == j_begin) {
+      if (tid < G * DH / 8) qs[tid / (DH / 8)][tid % (DH / 8)] = qv;
+      __syncthreads();
+    }
+    if (t0 >= j_end) break;               // no key of this pass is visible (uniform)
+    float s[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      s[g] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[g] = dot8_bf16(kr[i], qs[g][quarter * 4 + i], s[g]);
+      s[g] += __shfl_xor(s[g], 1, 64);
+      s[g] += __shfl_xor(s[g], 2, 64);
+    }
+    if (quarter == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) sc[g][kk] = key < j_end ? s[g] * sc_l2 : -INFINITY;
+    }
+    float vf[16][2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = kw0 + i < j_end;
+      vf[i][0] = ok ? bf2f(static_cast<bf16_t>(vr[i] & 0xFFFFu)) : 0.f;
+      vf[i][1] = ok ? bf2f(static_cast<bf16_t>(vr[i] >> 16)) : 0.f;
+    }
+    __syncthreads();
+    // softmax update, lane = key of the pass (every wave alike)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float v = sc[g][lane];
+      float mt = v;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) mt = fmaxf(mt, __shfl_xor(mt, m, 64));
+      const float m_new = fmaxf(m_run[g], mt);                   // finite: key t0 is in range
+      const float alpha = exp2f(m_run[g] - m_new);
+      const float p = exp2f(v - m_new);
+      float ps = p;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) ps += __shfl_xor(ps, m, 64);
+      l_run[g] = l_run[g] * alpha + ps;
+      m_run[g] = m_new;
+      float o0 = acc[g][0] * alpha, o1 = acc[g][1] * alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), 16 * wid + i));
+        o0 += pi * vf[i][0];
+        o1 += pi * vf[i][1];
+      }
+      acc[g][0] = o0;
+      acc[g][1] = o1;
+    }
+    __syncthreads();                                             // sc[] is rewritten by the next pass
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    red[wid][g][2 * lane] = acc[g][0];
+    red[wid][g][2 * lane + 1] = acc[g][1];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * DH; e += 256) {
+    const int g = e / DH, d = e % DH;
+    const int64_t pr = static_cast<int64_t>(split) * a.n_q_heads + kvh * G + g;   // (split, row 0, head)
+    a.part_o[pr * DH + d] = ((red[0][g][d] + red[1][g][d]) + red[2][g][d]) + red[3][g][d];
+    if (d == 0) a.part_ml[pr] = make_float2(m_run[g], l_run[g]);
+  }
+}
+
+// Merge many split-KV partials of one query row: one workgroup per q head;
+// thread t takes dims 2 (t % 64) .. +1 of the splits t / 64, t / 64 + 4, ..., so
+// all partial loads are in flight at once, and the four waves add up in LDS.
+template <int DH>
+__global__ __launch_bounds__(256) void attn_combine_row_kernel(AttnArgs a, int ksplit) {
+  static_assert(DH == 128, "two output dims per lane");
+  constexpr int PER = 16;                 // splits per wave held in registers
+  __shared__ float wmax[4];
+  __shared__ float red[4][DH + 1];
+  const int head = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // every split below kv_bound wrote a partial (an empty one has max -inf, sum 0)
+  const int ns = (a.kv_bound + ksplit - 1) / ksplit;
+  float o0 = 0.f, o1 = 0.f, ls = 0.f;
+  float M = -INFINITY;
+  if (ns <= 4 * PER) {
+    // one round of loads: wave w holds splits w, w + 4, ...
+    float2 ml[PER], po[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int sp = wid + 4 * i;
+      if (sp < ns) {
+        const int64_t pr = static_cast<int64_t>(sp) * a.n_q_heads + head;
+        ml[i] = a.part_ml[pr];
+        po[i] = *reinterpret_cast<const float2*>(a.part_o + pr * DH + 2 * lane);
+        M = fmaxf(M, ml[i].x);
+      }
+    }
+    if (lane == 0) wmax[wid] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (wid + 4 * i < ns) {
+        const float w = exp2f(ml[i].x - M);
+        ls += w * ml[i].y;
+        o0 += w * po[i].x;
+        o1 += w * po[i].y;
+      }
+    }
+  } else {
+    for (int sp = tid; sp < ns; sp += 256) M = fmaxf(M, a.part_ml[static_cast<int64_t>(sp) * a.n_q_heads + head].x);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
+    if (lane == 0) wmax[wid] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    for (int sp = wid; sp < ns; sp += 4) {
+      const int64_t pr = static_cast<int64_t>(sp) * a.n_q_heads + head;
+      const float2 ml = a.part_ml[pr];
+      const float2 po = *reinterpret_cast<const float2*>(a.part_o + pr * DH + 2 * lane);
+      const float w = exp2f(ml.x - M);
+      ls += w * ml.y;
+      o0 += w * po.x;
+      o1 += w * po.y;
+    }
+  }
+  red[wid][2 * lane] = o0;
+  red[wid][2 * lane + 1] = o1;
+  if (lane == 0) red[wid][DH] = ls;
+  __syncthreads();
+  if (wid == 0) {
+    const float l = ((red[0][DH] + red[1][DH]) + red[2][DH]) + red[3][DH];
+    const float inv = 1.0f / l;
+    bf16_t* ob = static_cast<bf16_t*>(a.o);
+    const int KO = a.n_q_heads * DH;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = 2 * lane + e;
+      const float v = ((red[0][d] + red[1][d]) + red[2][d]) + red[3][d];
+      ob[pk_off(0, head * DH + d, KO)] = f2bf(v * inv);
+    }
+  }
+}
+
+template <int G>
+hipError_t run_decode(const AttnArgs& a, hipStream_t s) {
+  const int kv_blocks = (a.kv_bound + KVB - 1) / KVB;
+  // one 64-key pass per workgroup up to about 1024 workgroups
+  int n_splits = std::max(1, std::min(kv_blocks, (1024 + a.n_kv_heads - 1) / a.n_kv_heads));
+  while (static_cast<int64_t>(n_splits) * a.n_q_heads > kAttnPartialRows) --n_splits;
+  const int ksplit = ((kv_blocks + n_splits - 1) / n_splits) * KVB;
+  n_splits = (a.kv_bound + ksplit - 1) / ksplit;
+  // pages of 16 keys or more (a power of two): a wave's 16 keys are consecutive rows
+  if (a.cache.bt == nullptr || a.cache.bs_shift >= 4)
+    attn_decode_kernel<128, G, true><<<n_splits * a.n_kv_heads, 256, 0, s>>>(a, ksplit);
+  else
+    attn_decode_kernel<128, G, false><<<n_splits * a.n_kv_heads, 256, 0, s>>>(a, ksplit);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attn_combine_row_kernel<128><<<a.n_q_heads, 256, 0, s>>>(a, ksplit);
+  return hipGetLastError();
+}
+
 // variant: 1 / 2 = register-staged kernel with 1 / 2 query groups per wave,
 // 3 / 4 = LDS-DMA kernel (head_dim 128, a layer's pool below 2 GiB) with 1 / 2,
 // 5 / 6 = lean LDS-DMA kernel (as 3 / 4, pages a power of two >= 16 keys) with 1 / 2
@@ -986,6 +1221,13 @@ hipError_t launch_attention_ng(cb_dtype dt, const AttnArgs& a_in, int ng, hipStr
     return hipGetLastError();
   }
   const int G = a.n_q_heads / a.n_kv_heads;
+  // a single query row (a decode step) with split-KV buffers: the one-row kernel
+  if (a.R == 1 && a.head_dim == 128 && a.part_o != nullptr && a.n_splits_req == 0 && (G == 1 || G == 2 || G == 4 || G == 8)) {
+    if (G == 1) return run_decode<1>(a, s);
+    if (G == 2) return run_decode<2>(a, s);
+    if (G == 4) return run_decode<4>(a, s);
+    return run_decode<8>(a, s);
+  }
 #define CB_ATTN_CASE(D, GG) \
   if (a.head_dim == D && G == GG) return run_bf16_variant<D, GG>(a, ng, s);
   CB_ATTN_CASE(128, 1) CB_ATTN_CASE(128, 2) CB_ATTN_CASE(128, 4) CB_ATTN_CASE(128, 8) CB_ATTN_CASE(128, 16)

@@ -22,10 +22,12 @@
 //              bf16 like the prefill's activations; each workgroup reduces the
 //              sum of squares itself in a fixed order, so all agree bitwise;
 //   IN_BF16    a plain bf16 vector.
-// Outputs: fp32 y[r], or y[r] + r1[r] (+ r2[r]) for the residual stream; or, for
+// Outputs: fp32 y[r], or y[r] + r1[r] (+ r2[r]) for the residual stream; for
 // the gate/up matrix (whose row blocks alternate 32 gate rows and their 32 up
 // rows), a workgroup takes one gate block and its up block together and writes
-// bf16(SiLU(gate) * up), the down projection's input.
+// bf16(SiLU(gate) * up), the down projection's input; for the fused Q/K/V
+// matrix, the rows of a dim pair meet in one workgroup, which applies RoPE and
+// writes Q and the cache's new K/V row.
 #include "cb_internal.h"
 
 namespace cb {
@@ -33,7 +35,16 @@ namespace cb {
 namespace {
 
 enum { IN_PACKED = 0, IN_NORM = 1, IN_BF16 = 2 };
-enum { OUT_F32 = 0, OUT_SWIGLU = 1 };
+enum { OUT_F32 = 0, OUT_SWIGLU = 1, OUT_QKV = 2 };
+
+// Where the fused Q/K/V product of one token goes: Q, rotated, to bf16 q;
+// K, rotated, and V into the paged cache at the token's position.
+struct QkvOut {
+  bf16_t* q;
+  const float2* rot;    // rotation row of the position: (cos, sin) per dim pair
+  PagedRef cache;
+  int layer, pos, qw, kvw, head_dim;
+};
 
 struct GemvArgs {
   const bf16_t* w;      // packed [rows padded to 32][K]
@@ -45,6 +56,7 @@ struct GemvArgs {
   void* y;              // OUT_F32: fp32 [rows]; OUT_SWIGLU: bf16 [rows / 2]
   const float* r1;      // OUT_F32: optional residual terms added to y
   const float* r2;
+  QkvOut qkv;           // OUT_QKV
 };
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
@@ -125,7 +137,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_packed_kernel(GemvArgs g) {
   extern __shared__ uint4 xs[];          // [K / 8] groups of 8 bf16 inputs
   constexpr int NR = OUT == OUT_SWIGLU ? 2 : 1;   // row blocks per workgroup: the gate/up pair takes two
   constexpr int NB = 32 / RB;            // column blocks per wave load
-  static_assert(OUT == OUT_F32 || RB == 32, "the gate/up pair takes whole row blocks");
+  static_assert(OUT != OUT_SWIGLU || RB == 32, "the gate/up pair takes whole row blocks");
   __shared__ float red[WAVES][32 * NR];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -178,7 +190,35 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_packed_kernel(GemvArgs g) {
     for (int r = 0; r < NR; ++r) red[wid][r * 32 + lane] = acc[r];
   }
   __syncthreads();
-  if (wid == 0 && lane < RB) {
+  if constexpr (OUT == OUT_QKV) {
+    static_assert(RB % 2 == 0, "RoPE pairs stay in the workgroup");
+    if (wid == 0) {
+      float t = 0.f;
+      if (lane < RB) {
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) t += red[w][lane];
+      }
+      const float o = __shfl_xor(t, 1, 64);   // the other row of the dim pair
+      const int r = row0 + lane;
+      const QkvOut& d = g.qkv;
+      if (lane < RB && r < g.rows) {
+        float v = t;
+        if (r < d.qw + d.kvw) {                  // Q and K are rotated, V is not
+          const float2 cs = d.rot[(r % d.head_dim) >> 1];
+          v = (r & 1) ? o * cs.y + t * cs.x : t * cs.x - o * cs.y;
+        }
+        if (r < d.qw) {
+          d.q[r] = f2bf(v);
+        } else {
+          const int e = r - d.qw;
+          const bool isv = e >= d.kvw;
+          const int64_t off = static_cast<int64_t>(d.layer) * d.cache.layer_stride +
+                              paged_row(d.cache, d.pos) * d.kvw + (isv ? e - d.kvw : e);
+          static_cast<bf16_t*>(isv ? d.cache.v : d.cache.k)[off] = f2bf(v);
+        }
+      }
+    }
+  } else if (wid == 0 && lane < RB) {
     float t[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
@@ -201,43 +241,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_packed_kernel(GemvArgs g) {
   }
 }
 
-// Q/K/V of the token from the fused projection's output: RoPE of Q and K with
-// the rotation row of the token's position, Q to bf16 (row-major, what the
-// attention kernel reads), and K/V written into the paged cache at the token's
-// position.
-__global__ __launch_bounds__(256) void decode_qkv_kernel(const float* y, int qw, int kvw, int head_dim,
-                                                         const float2* rot, bf16_t* q, PagedRef cache, int layer,
-                                                         int pos, int kv_bf16) {
-  const int64_t off = static_cast<int64_t>(layer) * cache.layer_stride + paged_row(cache, pos) * kvw;
-  for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < (qw + 2 * kvw) / 2; p += gridDim.x * blockDim.x) {
-    const int c = 2 * p;
-    float x0 = y[c], x1 = y[c + 1];
-    if (c < qw + kvw) {                       // Q and K are rotated, V is not
-      const float2 cs = rot[(c % head_dim) >> 1];
-      const float a = x0 * cs.x - x1 * cs.y, b = x0 * cs.y + x1 * cs.x;
-      x0 = a;
-      x1 = b;
-    }
-    if (c < qw) {
-      q[c] = f2bf(x0);
-      q[c + 1] = f2bf(x1);
-    } else {
-      const int e = c - qw;                   // [K | V] row of width 2 kvw
-      const bool isv = e >= kvw;
-      const int f = isv ? e - kvw : e;
-      if (kv_bf16) {
-        bf16_t* dst = static_cast<bf16_t*>(isv ? cache.v : cache.k) + off + f;
-        dst[0] = f2bf(x0);
-        dst[1] = f2bf(x1);
-      } else {
-        float* dst = static_cast<float*>(isv ? cache.v : cache.k) + off + f;
-        dst[0] = x0;
-        dst[1] = x1;
-      }
-    }
-  }
-}
-
 template <int IN, int OUT, int RB, int WAVES>
 hipError_t gemv_launch(const GemvArgs& g, int n_wg, hipStream_t s) {
   gemv_packed_kernel<IN, OUT, RB, WAVES><<<n_wg, WAVES * 64, static_cast<size_t>(g.K) * 2, s>>>(g);
@@ -255,28 +258,29 @@ hipError_t gemv_pick(const GemvArgs& g, bool swiglu, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_gemv_qkv(const void* w, int K, const void* x, const float* gain, float eps, int qw, int kvw,
+                           int head_dim, const float2* rot, void* q, const PagedRef& cache_in, int layer, int pos,
+                           hipStream_t s) {
+  const int rows = qw + 2 * kvw;
+  if (K % 16 != 0 || static_cast<int64_t>(K) * 2 > 64 * 1024 || head_dim % 8 != 0) return hipErrorInvalidValue;
+  GemvArgs g{static_cast<const bf16_t*>(w), rows, K, x, nullptr, gain, eps, nullptr, nullptr, nullptr, {}};
+  g.qkv = QkvOut{static_cast<bf16_t*>(q), rot, cache_in, layer, pos, qw, kvw, head_dim};
+  g.qkv.cache.bs_shift = block_shift(cache_in.bs);
+  return gemv_launch<IN_NORM, OUT_QKV, 8, 8>(g, (rows + 7) / 8, s);
+}
+
 hipError_t launch_gemv(int in_mode, bool swiglu_out, const void* w, int rows, int K, const void* x, const float* x2,
                        const float* gain, float eps, void* y, const float* r1, const float* r2, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (K % 16 != 0 || in_mode < 0 || in_mode > 2) return hipErrorInvalidValue;
   if (static_cast<int64_t>(K) * 2 > 64 * 1024) return hipErrorInvalidValue;   // the input vector must fit in LDS
   if (swiglu_out && rows % 64 != 0) return hipErrorInvalidValue;
-  GemvArgs g{static_cast<const bf16_t*>(w), rows, K, x, x2, gain, eps, y, r1, r2};
+  GemvArgs g{static_cast<const bf16_t*>(w), rows, K, x, x2, gain, eps, y, r1, r2, {}};
   switch (in_mode) {
     case 0: return gemv_pick<IN_PACKED>(g, swiglu_out, s);
     case 1: return gemv_pick<IN_NORM>(g, swiglu_out, s);
     default: return gemv_pick<IN_BF16>(g, swiglu_out, s);
   }
-}
-
-hipError_t launch_decode_qkv(const float* y, int qw, int kvw, int head_dim, const float2* rot, void* q,
-                             const PagedRef& cache_in, int layer, int pos, cb_dtype dt, hipStream_t s) {
-  PagedRef cache = cache_in;
-  cache.bs_shift = block_shift(cache.bs);
-  const int pairs = (qw + 2 * kvw) / 2;
-  decode_qkv_kernel<<<(pairs + 255) / 256, 256, 0, s>>>(y, qw, kvw, head_dim, rot, static_cast<bf16_t*>(q), cache,
-                                                        layer, pos, dt == CB_BF16 ? 1 : 0);
-  return hipGetLastError();
 }
 
 }  // namespace cb

@@ -141,10 +141,12 @@ hipError_t launch_select(const float* dev, const int32_t* pos, int n, int k, int
 // rows) bf16 SiLU(gate) * up of rows / 2 features.
 hipError_t launch_gemv(int in_mode, bool swiglu_out, const void* w, int rows, int K, const void* x, const float* x2,
                        const float* gain, float eps, void* y, const float* r1, const float* r2, hipStream_t s);
-// RoPE of the token's Q/K (rotation row `rot`), Q to bf16 row-major, K/V into
-// the paged cache at `pos` of `layer`
-hipError_t launch_decode_qkv(const float* y, int qw, int kvw, int head_dim, const float2* rot, void* q,
-                             const PagedRef& cache, int layer, int pos, cb_dtype dt, hipStream_t s);
+// The fused Q/K/V product of one token (rows qw + 2 kvw, input bf16 of
+// RMSNorm(x) * gain), with RoPE of Q/K by the rotation row `rot`: Q to bf16 q,
+// K/V (bf16 cache) into the paged cache at `pos` of `layer`.
+hipError_t launch_gemv_qkv(const void* w, int K, const void* x, const float* gain, float eps, int qw, int kvw,
+                           int head_dim, const float2* rot, void* q, const PagedRef& cache, int layer, int pos,
+                           hipStream_t s);
 
 // top-k plus the layer's row maps in one launch (kept rows, then the nq suffix rows):
 // gmap[i] (source row), rowpos[i] (position), for i < k + nq; copy (nullable)

@@ -509,6 +509,47 @@ __global__ __launch_bounds__(256) void lmhead_kernel(const float* a, const T* w,
   }
 }
 
+// bf16 rows of NL * 512 columns: a wave takes two rows at a time and has all
+// 2 NL of its 16-byte weight loads in flight before it sums.
+template <int NL>
+__global__ __launch_bounds__(256) void lmhead_bf16_kernel(const float* a, const bf16_t* w, int vocab, float* logits) {
+  constexpr int d = NL * 512;
+  __shared__ float sa[d];
+  for (int e = threadIdx.x; e < d; e += 256) sa[e] = a[e];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int waves = gridDim.x * 4;
+  for (int v0 = 2 * (blockIdx.x * 4 + (threadIdx.x >> 6)); v0 < vocab; v0 += 2 * waves) {
+    const int v1 = min(v0 + 1, vocab - 1);
+    uint4 u[2][NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      u[0][i] = ld_stream(reinterpret_cast<const uint4*>(w + static_cast<int64_t>(v0) * d + i * 512 + lane * 8));
+      u[1][i] = ld_stream(reinterpret_cast<const uint4*>(w + static_cast<int64_t>(v1) * d + i * 512 + lane * 8));
+    }
+    float acc[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const float4 s0 = *reinterpret_cast<const float4*>(&sa[i * 512 + lane * 8]);
+      const float4 s1 = *reinterpret_cast<const float4*>(&sa[i * 512 + lane * 8 + 4]);
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        float f[8];
+        unpack(u[r][i], f);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[r] += f[j] * sv[j];
+      }
+    }
+    acc[0] = wave_sum(acc[0]);
+    acc[1] = wave_sum(acc[1]);
+    if (lane == 0) {
+      logits[v0] = acc[0];
+      if (v0 + 1 < vocab) logits[v0 + 1] = acc[1];
+    }
+  }
+}
+
 __global__ void iota_kernel(int32_t* out, int n, int32_t base) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) out[i] = base + i;
@@ -634,7 +675,11 @@ hipError_t launch_scatter_kv(cb_dtype dt, const float* kvf, int64_t ldf, const i
 hipError_t launch_lmhead(cb_dtype dt, const float* a, const void* w, int vocab, int d, float* logits, hipStream_t s) {
   const int grid = std::min(2048, cdiv(vocab, 4));
   const size_t lds = static_cast<size_t>(d) * sizeof(float);
-  if (dt == CB_BF16)
+  if (dt == CB_BF16 && d == 4096) {
+    lmhead_bf16_kernel<8><<<std::min(2048, cdiv(vocab, 8)), 256, 0, s>>>(a, static_cast<const bf16_t*>(w), vocab, logits);
+  } else if (dt == CB_BF16 && d == 8192) {
+    lmhead_bf16_kernel<16><<<std::min(2048, cdiv(vocab, 8)), 256, 0, s>>>(a, static_cast<const bf16_t*>(w), vocab, logits);
+  } else if (dt == CB_BF16)
     lmhead_kernel<bf16_t><<<grid, 256, lds, s>>>(a, static_cast<const bf16_t*>(w), vocab, d, logits);
   else
     lmhead_kernel<float><<<grid, 256, lds, s>>>(a, static_cast<const float*>(w), vocab, d, logits);

@@ -425,3 +425,70 @@ def torch_device_chunk_kv(shape: ModelShape, lens: Sequence[int], seed: int, dev
         v = (torch.randn(dims, generator=gen, device=device) * s).to(td)
         out.append((k, v))
     return out
+
+
+@dataclass
+class FragmentWorkload:
+    """Stored chunks and requests for fragment matching: requests assembled from
+    cached documents (whole or in part, at any alignment) plus new text, as in the
+    RAG setting the pages describe.  Numbers only -- no hashing here."""
+    chunk_size: int
+    stored_tokens: np.ndarray      # [n_stored, chunk_size] int32
+    stored_ids: np.ndarray         # [n_stored] int64 chunk ids
+    stored_offsets: np.ndarray     # [n_stored] int32 stored position (-1: unknown)
+    queries: List[np.ndarray]      # int32 token arrays
+    prefix_lens: np.ndarray        # [n_queries] int32 prefix-cache coverage
+
+
+def fragment_workload(seed: int, n_docs: int = 32, chunk_size: int = 256, chunks_per_doc: int = 4,
+                      n_queries: int = 4, docs_per_query: int = 4, query_tail: int = 64,
+                      vocab: int = 128256, dup_docs: int = 2, unknown_chunks: int = 2) -> FragmentWorkload:
+    """Documents of chunks_per_doc chunks are stored chunk by chunk (stored offset =
+    the document's start in the request that stored it + the chunk's place in the
+    document); dup_docs documents are stored a second time under new ids and
+    offsets; unknown_chunks chunks carry the unknown offset.  Each request: random
+    filler, then docs_per_query documents (the last one truncated to a random
+    length, one placed twice, one chunk copied with a token changed), random
+    filler between them, and query_tail new tokens at the end; its prefix
+    coverage is 0 or a random length below the first document's start."""
+    rng = _rng(seed, 31, 0)
+    C = int(chunk_size)
+    docs = [rng.integers(0, vocab, size=chunks_per_doc * C, dtype=np.int64).astype(np.int32) for _ in range(n_docs)]
+    toks, ids, offs = [], [], []
+    next_id = int(rng.integers(1 << 40, 1 << 41))
+    for d, doc in enumerate(docs):
+        base = int(rng.integers(0, 8)) * 97
+        for j in range(chunks_per_doc):
+            toks.append(doc[j * C:(j + 1) * C])
+            ids.append(next_id)
+            offs.append(base + j * C)
+            next_id += int(rng.integers(1, 1000))
+    for d in rng.choice(n_docs, size=min(dup_docs, n_docs), replace=False):
+        base = 5000 + int(rng.integers(0, 100))
+        for j in range(chunks_per_doc):
+            toks.append(docs[d][j * C:(j + 1) * C])
+            ids.append(next_id)
+            offs.append(base + j * C)
+            next_id += 1
+    for i in rng.choice(len(offs), size=min(unknown_chunks, len(offs)), replace=False):
+        offs[i] = -1
+    queries, prefix = [], []
+    for _ in range(n_queries):
+        parts = [rng.integers(0, vocab, size=int(rng.integers(0, 300)), dtype=np.int64).astype(np.int32)]
+        first_start = len(parts[0])
+        picks = list(rng.choice(n_docs, size=min(docs_per_query, n_docs), replace=False))
+        picks.append(picks[0])                                    # one document twice
+        for i, d in enumerate(picks):
+            doc = docs[d]
+            if i == len(picks) - 2:
+                doc = doc[:int(rng.integers(C // 2, len(doc) + 1))]   # a truncated document
+            parts.append(doc)
+            parts.append(rng.integers(0, vocab, size=int(rng.integers(0, 40)), dtype=np.int64).astype(np.int32))
+        near = docs[picks[1]][:C].copy()
+        near[int(rng.integers(0, C))] ^= 1                        # one token away from a stored chunk
+        parts.append(near)
+        parts.append(rng.integers(0, vocab, size=query_tail, dtype=np.int64).astype(np.int32))
+        queries.append(np.concatenate(parts).astype(np.int32))
+        prefix.append(0 if rng.random() < 0.5 else int(rng.integers(0, first_start + 1)))
+    return FragmentWorkload(C, np.stack(toks).astype(np.int32), np.array(ids, dtype=np.int64),
+                            np.array(offs, dtype=np.int32), queries, np.array(prefix, dtype=np.int32))

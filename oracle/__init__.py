@@ -11,7 +11,7 @@ Sources ("the pages"):
   [KV]  LMCache KV-cache essay (blog.thunguo.space), "KV 容量" formula S_token.
   [BI]  LMCache coordinator "Blend Index" article (nxmr.cn), section 6.2 -- the
         (chunk_hash, old_st, cur_st) match tuple: old_st is the re-RoPE source,
-        cur_st the target.
+        cur_st the target; sections 3-7 -- fragment matching (``oracle/match.py``).
 
 Precision: every computation runs in float64 (``dtype`` argument); values the
 method *stores* (the KV cache, in the model's storage dtype) are rounded to that
@@ -28,3 +28,4 @@ from .blend import (  # noqa: F401
     assemble_blended, full_reuse_prefill, blend_prefill, blend_prefill_masked,
     blend_layer, flop_count, decode_step,
 )
+from .match import POLY_BASE, UNKNOWN_TOKEN_OFFSET  # noqa: F401  (the matcher itself: oracle.match)

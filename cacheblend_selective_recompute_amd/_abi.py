@@ -66,6 +66,15 @@ class cb_blend_params(ctypes.Structure):
                 ("trace", POINTER(cb_trace))]
 
 
+class cb_blend_index_info(ctypes.Structure):
+    _fields_ = [("chunk_size", c_int32), ("n_entries", c_int32), ("n_occupants", c_int32), ("n_skipped", c_int32),
+                ("slot_bits", c_int32), ("table_bits", c_int32), ("image_bytes", ctypes.c_uint64)]
+
+
+CB_UNKNOWN_TOKEN_OFFSET = -1
+CB_MATCH_MAX_CONTENTS = 4096
+
+
 KINDS = ["rerope", "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention", "deviation", "select",
          "scatter", "norm", "lm_head", "other"]
 
@@ -91,6 +100,13 @@ _PROTOS = {
     "cb_decode_step": (c_int, [POINTER(cb_model), POINTER(cb_paged_kv), c_int32, c_void_p, c_void_p, c_void_p,
                                c_size_t, c_void_p]),
     "cb_decode_workspace_bytes": (c_size_t, [POINTER(cb_model_cfg)]),
+    "cb_blend_index_image_bytes": (c_size_t, [c_int32, c_int32]),
+    "cb_blend_index_build": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_size_t,
+                                     POINTER(cb_blend_index_info)]),
+    "cb_blend_match_workspace_bytes": (c_size_t, [c_int64]),
+    "cb_blend_match": (c_int, [c_void_p, POINTER(cb_blend_index_info), c_void_p, c_void_p, c_int32, c_int64, c_int32,
+                               c_int32, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                               c_void_p, c_size_t, c_void_p]),
     "cb_pack_weight": (c_int, [c_int, c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]),
     "cb_packed_weight_bytes": (c_size_t, [c_int, c_int64, c_int64]),
     "cb_workspace_bytes": (c_size_t, [POINTER(cb_model_cfg), c_int32, c_int32, c_int32]),

@@ -372,3 +372,68 @@ def cb_blend_prefill(model: DeviceModel, chunks: Sequence[ChunkSource], query_to
                                 int(query_tokens.numel()), ctypes.byref(params.c), ctypes.byref(blended.c),
                                 _p(logits), _p(hkvd_out), _p(dev_out), w.ptr, w.nbytes, _stream(stream)),
            "cb_blend_prefill")
+
+
+# ----------------------------------------------------------------------------
+# fragment matching
+# ----------------------------------------------------------------------------
+
+def cb_blend_index_image_bytes(n_chunks: int, chunk_size: int) -> int:
+    return int(_abi.load().cb_blend_index_image_bytes(int(n_chunks), int(chunk_size)))
+
+
+def cb_blend_index_build(tokens: np.ndarray, chunk_ids: np.ndarray, token_offsets: np.ndarray):
+    """Host build of the index image: returns (cb_blend_index_info, uint8 host array of
+    info.image_bytes)."""
+    lib = _abi.load()
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    if tokens.ndim != 2:
+        raise ValueError("tokens must be [n_chunks][chunk_size]")
+    n, C = tokens.shape
+    ids = np.ascontiguousarray(chunk_ids, dtype=np.int64)
+    offs = np.ascontiguousarray(token_offsets, dtype=np.int32)
+    if ids.shape != (n,) or offs.shape != (n,):
+        raise ValueError("chunk_ids and token_offsets must have one entry per chunk")
+    nbytes = cb_blend_index_image_bytes(n, C)
+    image = np.zeros(max(nbytes, 1), dtype=np.uint8)
+    info = _abi.cb_blend_index_info()
+    _check(lib.cb_blend_index_build(tokens.ctypes.data if n else None, ids.ctypes.data if n else None,
+                                    offs.ctypes.data if n else None, n, C, image.ctypes.data, nbytes,
+                                    ctypes.byref(info)), "cb_blend_index_build")
+    return info, image[:info.image_bytes].copy()
+
+
+class BlendIndexImage:
+    """An index image built on the host and copied to device memory as it is."""
+
+    def __init__(self, tokens: np.ndarray, chunk_ids: np.ndarray, token_offsets: np.ndarray, device="cuda"):
+        self.info, self.host = cb_blend_index_build(tokens, chunk_ids, token_offsets)
+        self.dev = torch.empty(max(self.host.size, 256), dtype=torch.uint8, device=device)
+        self.dev[:self.host.size].copy_(torch.from_numpy(self.host))
+
+
+def cb_blend_match_workspace_bytes(total_tokens: int) -> int:
+    return int(_abi.load().cb_blend_match_workspace_bytes(int(total_tokens)))
+
+
+def cb_blend_match(index: BlendIndexImage, query_tokens: torch.Tensor, query_starts: torch.Tensor, total_tokens: int,
+                   max_query_len: int, probe_stride: int = 1, prefix_lens: Optional[torch.Tensor] = None,
+                   max_matches: int = 64, ws: Optional[Workspace] = None, stream=None, out: Optional[dict] = None):
+    """Match a batch of requests (tokens back to back, int32 starts [n+1] on the device).
+    Returns the device outputs: chunk [n][max_matches] int64, old_st / cur_st int32,
+    kept uint8 and count [n] int32."""
+    lib = _abi.load()
+    n = int(query_starts.numel()) - 1
+    dev = query_starts.device
+    if out is None:
+        out = {"chunk": torch.empty((n, max_matches), dtype=torch.int64, device=dev),
+               "old_st": torch.empty((n, max_matches), dtype=torch.int32, device=dev),
+               "cur_st": torch.empty((n, max_matches), dtype=torch.int32, device=dev),
+               "kept": torch.empty((n, max_matches), dtype=torch.uint8, device=dev),
+               "count": torch.empty(max(n, 0), dtype=torch.int32, device=dev)}
+    w = _ws(ws, cb_blend_match_workspace_bytes(total_tokens), dev)
+    _check(lib.cb_blend_match(_p(index.dev), ctypes.byref(index.info), _p(query_tokens), _p(query_starts), n,
+                              int(total_tokens), int(max_query_len), int(probe_stride), _p(prefix_lens),
+                              int(max_matches), _p(out["chunk"]), _p(out["old_st"]), _p(out["cur_st"]),
+                              _p(out["kept"]), _p(out["count"]), w.ptr, w.nbytes, _stream(stream)), "cb_blend_match")
+    return out

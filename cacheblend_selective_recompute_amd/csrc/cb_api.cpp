@@ -18,6 +18,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "cb_internal.h"
@@ -999,6 +1000,149 @@ cb_status cb_decode_step(const cb_model* model, const cb_paged_kv* kv, int32_t p
   }
   CB_TRY(launch_rmsnorm(c.dtype, w.x0, nullptr, d, 1, d, model->final_norm, c.rms_eps, w.a_last, d, 1, s), "final norm");
   CB_TRY(launch_lmhead(c.dtype, w.a_last, model->lm_head, c.vocab, d, logits, s), "lm head");
+  return ok();
+}
+
+size_t cb_blend_index_image_bytes(int32_t n_chunks, int32_t chunk_size) {
+  if (n_chunks < 0 || chunk_size < 1) return 0;
+  return index_layout(chunk_size, n_chunks, n_chunks, index_slot_bits(n_chunks), index_table_bits(n_chunks)).end;
+}
+
+cb_status cb_blend_index_build(const int32_t* tokens, const int64_t* chunk_ids, const int32_t* token_offsets,
+                               int32_t n_chunks, int32_t chunk_size, void* image, size_t image_bytes,
+                               cb_blend_index_info* info) {
+  if (n_chunks < 0 || chunk_size < 1) return fail(CB_ERR_INVALID, "n_chunks %d, chunk_size %d", n_chunks, chunk_size);
+  if (!image || !info || (n_chunks > 0 && (!tokens || !chunk_ids || !token_offsets)))
+    return fail(CB_ERR_INVALID, "NULL pointer");
+  const size_t C = static_cast<size_t>(chunk_size);
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    if (token_offsets[i] < CB_UNKNOWN_TOKEN_OFFSET) return fail(CB_ERR_INVALID, "chunk %d: offset %d", i, token_offsets[i]);
+    for (size_t t = 0; t < C; ++t)
+      if (tokens[i * C + t] < 0) return fail(CB_ERR_INVALID, "chunk %d: negative token", i);
+  }
+  // contents in first-indexed order; occupants per content in input order
+  std::unordered_map<uint64_t, int32_t> by_fp;
+  std::vector<int32_t> first_chunk;                 // the chunk whose tokens an entry holds
+  std::vector<uint64_t> fps;
+  std::vector<std::vector<int32_t>> occ;            // chunk indices per entry
+  int32_t skipped = 0;
+  for (int32_t i = 0; i < n_chunks; ++i) {
+    if (token_offsets[i] == CB_UNKNOWN_TOKEN_OFFSET) { ++skipped; continue; }
+    const int32_t* t = tokens + i * C;
+    uint64_t h = 0;
+    for (size_t j = 0; j < C; ++j) h = h * kPolyBase + static_cast<uint32_t>(t[j]);
+    auto it = by_fp.find(h);
+    if (it == by_fp.end()) {
+      by_fp.emplace(h, static_cast<int32_t>(fps.size()));
+      fps.push_back(h);
+      first_chunk.push_back(i);
+      occ.push_back({i});
+      continue;
+    }
+    const int32_t e = it->second;
+    if (std::memcmp(tokens + first_chunk[e] * C, t, C * 4) != 0) { ++skipped; continue; }   // fingerprint taken
+    bool dup = false;
+    for (int32_t o : occ[e]) dup = dup || chunk_ids[o] == chunk_ids[i];
+    if (!dup) occ[e].push_back(i);
+  }
+  const int64_t n_e = static_cast<int64_t>(fps.size());
+  int64_t n_o = 0;
+  for (const auto& v : occ) n_o += static_cast<int64_t>(v.size());
+  const int sb = index_slot_bits(n_e), tb = index_table_bits(n_e);
+  const IndexLayout L = index_layout(chunk_size, n_e, n_o, sb, tb);
+  if (image_bytes < L.end) return fail(CB_ERR_WORKSPACE, "image %zu bytes, %zu needed", image_bytes, L.end);
+  char* b = static_cast<char*>(image);
+  std::memset(b, 0, L.end);
+  const int32_t hdr[8] = {0x58494243, 1, chunk_size, static_cast<int32_t>(n_e), static_cast<int32_t>(n_o), sb, tb, 0};
+  std::memcpy(b, hdr, sizeof(hdr));
+  uint8_t* slots = reinterpret_cast<uint8_t*>(b + L.slots);
+  uint64_t* tfp = reinterpret_cast<uint64_t*>(b + L.table_fp);
+  int32_t* tent = reinterpret_cast<int32_t*>(b + L.table_entry);
+  int32_t* etok = reinterpret_cast<int32_t*>(b + L.entry_tokens);
+  int32_t* eocc = reinterpret_cast<int32_t*>(b + L.entry_occ);
+  int64_t* ochunk = reinterpret_cast<int64_t*>(b + L.occ_chunk);
+  int32_t* ooff = reinterpret_cast<int32_t*>(b + L.occ_offset);
+  const uint64_t tmask = (uint64_t(1) << tb) - 1;
+  for (uint64_t i = 0; i <= tmask; ++i) tent[i] = -1;
+  int32_t o = 0;
+  for (int64_t e = 0; e < n_e; ++e) {
+    const uint64_t h = fps[e];
+    slots[h >> (64 - sb)] = 1;
+    uint64_t at = h >> (64 - tb);
+    while (tent[at] >= 0) at = (at + 1) & tmask;
+    tfp[at] = h;
+    tent[at] = static_cast<int32_t>(e);
+    std::memcpy(etok + e * C, tokens + first_chunk[e] * C, C * 4);
+    eocc[e] = o;
+    for (int32_t c : occ[e]) {
+      ochunk[o] = chunk_ids[c];
+      ooff[o] = token_offsets[c];
+      ++o;
+    }
+  }
+  eocc[n_e] = o;
+  info->chunk_size = chunk_size;
+  info->n_entries = static_cast<int32_t>(n_e);
+  info->n_occupants = static_cast<int32_t>(n_o);
+  info->n_skipped = skipped;
+  info->slot_bits = sb;
+  info->table_bits = tb;
+  info->image_bytes = L.end;
+  return ok();
+}
+
+size_t cb_blend_match_workspace_bytes(int64_t total_tokens) {
+  if (total_tokens < 0) return 0;
+  return static_cast<size_t>(((std::max<int64_t>(total_tokens, 1) * 4 + 255) / 256) * 256);
+}
+
+cb_status cb_blend_match(const void* index_image, const cb_blend_index_info* info, const int32_t* query_tokens,
+                         const int32_t* query_starts, int32_t n_queries, int64_t total_tokens, int32_t max_query_len,
+                         int32_t probe_stride, const int32_t* prefix_lens, int32_t max_matches, int64_t* out_chunk,
+                         int32_t* out_old_st, int32_t* out_cur_st, uint8_t* out_kept, int32_t* out_count, void* ws,
+                         size_t ws_bytes, cb_stream_t stream) {
+  if (!index_image || !info) return fail(CB_ERR_INVALID, "NULL index image or info");
+  if (n_queries < 0 || n_queries > 65535) return fail(CB_ERR_INVALID, "n_queries %d (0 .. 65535)", n_queries);
+  if (probe_stride < 1) return fail(CB_ERR_INVALID, "probe_stride %d < 1", probe_stride);
+  if (max_matches < 0 || total_tokens < 0 || max_query_len < 0)
+    return fail(CB_ERR_INVALID, "negative max_matches, total_tokens or max_query_len");
+  const cb_blend_index_info& I = *info;
+  if (I.chunk_size < 1 || I.n_entries < 0 || I.n_occupants < I.n_entries || I.slot_bits != index_slot_bits(I.n_entries) ||
+      I.table_bits != index_table_bits(I.n_entries))
+    return fail(CB_ERR_INVALID, "index info inconsistent with its sizes");
+  const IndexLayout L = index_layout(I.chunk_size, I.n_entries, I.n_occupants, I.slot_bits, I.table_bits);
+  if (I.image_bytes != L.end) return fail(CB_ERR_INVALID, "index info: image_bytes %llu, layout %zu",
+                                          (unsigned long long)I.image_bytes, L.end);
+  if (I.chunk_size > kMatchMaxChunk)
+    return fail(CB_ERR_UNSUPPORTED, "chunk_size %d above %d", I.chunk_size, kMatchMaxChunk);
+  if (n_queries > 0 && (!query_starts || !out_count)) return fail(CB_ERR_INVALID, "NULL query_starts or out_count");
+  if (n_queries > 0 && total_tokens > 0 && !query_tokens) return fail(CB_ERR_INVALID, "NULL query_tokens");
+  if (n_queries > 0 && max_matches > 0 && (!out_chunk || !out_old_st || !out_cur_st || !out_kept))
+    return fail(CB_ERR_INVALID, "NULL match outputs");
+  if (reinterpret_cast<uintptr_t>(index_image) % 256 != 0) return fail(CB_ERR_INVALID, "index image not 256-byte aligned");
+  const size_t need = cb_blend_match_workspace_bytes(total_tokens);
+  if (!ws || ws_bytes < need) return fail(CB_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, need);
+  if (n_queries == 0) return ok();
+  const char* b = static_cast<const char*>(index_image);
+  MatchIndexRef ix{};
+  ix.slots = reinterpret_cast<const uint8_t*>(b + L.slots);
+  ix.table_fp = reinterpret_cast<const uint64_t*>(b + L.table_fp);
+  ix.table_entry = reinterpret_cast<const int32_t*>(b + L.table_entry);
+  ix.entry_tokens = reinterpret_cast<const int32_t*>(b + L.entry_tokens);
+  ix.entry_occ = reinterpret_cast<const int32_t*>(b + L.entry_occ);
+  ix.occ_chunk = reinterpret_cast<const int64_t*>(b + L.occ_chunk);
+  ix.occ_offset = reinterpret_cast<const int32_t*>(b + L.occ_offset);
+  ix.chunk_size = I.chunk_size;
+  ix.slot_bits = I.slot_bits;
+  ix.table_bits = I.table_bits;
+  ix.n_entries = I.n_entries;
+  uint64_t top = 1;
+  for (int i = 1; i < I.chunk_size; ++i) top *= kPolyBase;
+  ix.top_pow = top;
+  const MatchOut out{out_chunk, out_old_st, out_cur_st, out_kept, out_count};
+  CB_TRY(launch_blend_match(ix, query_tokens, query_starts, n_queries, total_tokens, max_query_len, probe_stride,
+                            prefix_lens, max_matches, out, static_cast<int32_t*>(ws), reinterpret_cast<hipStream_t>(stream)),
+         "blend match");
   return ok();
 }
 

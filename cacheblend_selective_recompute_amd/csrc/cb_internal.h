@@ -7,6 +7,8 @@
 
 #include "cacheblend.h"
 
+#include <algorithm>
+
 namespace cb {
 
 // bf16 is carried as its 16-bit pattern; arithmetic is always fp32.
@@ -256,5 +258,64 @@ constexpr int64_t kAttnPartialRows = int64_t(kAttnMaxSplits) * 32768;   // (spli
 constexpr int kAttnSplitCap = 64;   // key splits of one launch (a single decode row uses many)
 inline int64_t attn_partial_floats(int head_dim) { return kAttnPartialRows * head_dim; }
 bool attention_supported(cb_dtype dt, int n_q_heads, int n_kv_heads, int head_dim);
+
+// ---------------------------------------------------------------------------
+// Fragment-matching index image: sections at 256-byte aligned offsets from the
+// image base (a header, the occupancy filter, the fingerprint table, entry
+// tokens, entry occupant ranges, occupant chunk ids and offsets).
+// ---------------------------------------------------------------------------
+constexpr uint64_t kPolyBase = 0x9E3779B97F4A7C15ull;
+constexpr int kMatchMaxChunk = 8192;      // longest chunk_size the scan kernel stages in LDS
+constexpr int kMatchMaxContents = 4096;   // distinct contents one request may match
+struct IndexLayout {
+  size_t slots, table_fp, table_entry, entry_tokens, entry_occ, occ_chunk, occ_offset, end;
+};
+inline IndexLayout index_layout(int chunk_size, int64_t n_entries, int64_t n_occ, int slot_bits, int table_bits) {
+  IndexLayout L{};
+  size_t off = 64;                               // header
+  auto take = [&](size_t bytes) { off = (off + 255) & ~size_t(255); const size_t at = off; off += bytes; return at; };
+  L.slots = take(size_t(1) << slot_bits);
+  L.table_fp = take((size_t(1) << table_bits) * 8);
+  L.table_entry = take((size_t(1) << table_bits) * 4);
+  L.entry_tokens = take(size_t(n_entries) * chunk_size * 4);
+  L.entry_occ = take(size_t(n_entries + 1) * 4);
+  L.occ_chunk = take(size_t(n_occ) * 8);
+  L.occ_offset = take(size_t(n_occ) * 4);
+  L.end = (off + 255) & ~size_t(255);
+  return L;
+}
+// the filter: smallest k >= 4 with 2^k >= 16 x entries; the table: load at most 1/2
+inline int index_slot_bits(int64_t n_entries) {
+  int k = 4;
+  while ((int64_t(1) << k) < 16 * std::max<int64_t>(n_entries, 1)) ++k;
+  return k;
+}
+inline int index_table_bits(int64_t n_entries) {
+  int k = 4;
+  while ((int64_t(1) << k) < 2 * std::max<int64_t>(n_entries, 1)) ++k;
+  return k;
+}
+struct MatchIndexRef {
+  const uint8_t* slots;
+  const uint64_t* table_fp;
+  const int32_t* table_entry;     // -1: empty slot
+  const int32_t* entry_tokens;    // [n_entries][chunk_size]
+  const int32_t* entry_occ;       // [n_entries + 1] occupant ranges
+  const int64_t* occ_chunk;
+  const int32_t* occ_offset;
+  int chunk_size, slot_bits, table_bits, n_entries;
+  uint64_t top_pow;               // kPolyBase^(chunk_size - 1) mod 2^64
+};
+struct MatchOut {
+  int64_t* chunk;
+  int32_t* old_st;
+  int32_t* cur_st;
+  uint8_t* kept;
+  int32_t* count;
+};
+// cand: workspace int32 [total] (per token position: verified entry or -1)
+hipError_t launch_blend_match(const MatchIndexRef& ix, const int32_t* tokens, const int32_t* starts, int n_queries,
+                              int64_t total, int max_len, int stride, const int32_t* prefix, int max_matches,
+                              const MatchOut& out, int32_t* cand, hipStream_t s);
 
 }  // namespace cb

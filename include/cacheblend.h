@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 4
+#define CB_ABI_VERSION 5
 
 /* A HIP stream (hipStream_t); NULL is the null stream. */
 typedef struct ihipStream_t* cb_stream_t;
@@ -342,6 +342,89 @@ cb_status cb_decode_step(const cb_model* model, const cb_paged_kv* kv, int32_t p
 
 /* Workspace bytes of cb_decode_step (0 for an invalid cfg). */
 size_t cb_decode_workspace_bytes(const cb_model_cfg* cfg);
+
+/* ---------------------------------------------------------------------------
+ * Fragment matching: which stored chunks a request contains, and where
+ * (LMCache coordinator "Blend Index" article, nxmr.cn).  The match tuples
+ * (chunk, old_st, cur_st) are the (old_start, new_start) of cb_chunk.
+ * ------------------------------------------------------------------------- */
+#define CB_UNKNOWN_TOKEN_OFFSET (-1)
+
+/* Shape of an index image written by cb_blend_index_build. */
+typedef struct cb_blend_index_info {
+  int32_t chunk_size;   /* tokens per indexed chunk */
+  int32_t n_entries;    /* distinct contents (fingerprints) indexed */
+  int32_t n_occupants;  /* chunks indexed, over all entries */
+  int32_t n_skipped;    /* chunks not indexed: unknown offset, or their fingerprint taken by other content */
+  int32_t slot_bits;    /* occupancy filter: 2^slot_bits one-byte slots */
+  int32_t table_bits;   /* fingerprint table: 2^table_bits slots, linear probing */
+  uint64_t image_bytes; /* bytes of the image actually used */
+} cb_blend_index_info;
+
+/* Bytes that suffice for the image of up to n_chunks chunks (0 for n_chunks < 0
+ * or chunk_size < 1). */
+size_t cb_blend_index_image_bytes(int32_t n_chunks, int32_t chunk_size);
+
+/* cb_blend_index_build -- the index of the article's sections 3.1, 4.1 and 5,
+ * built on the host into a position-independent image that the caller copies
+ * to device memory as it is.
+ *   tokens: host int32 [n_chunks][chunk_size] (token ids >= 0); chunk_ids: host
+ *     int64 [n_chunks]; token_offsets: host int32 [n_chunks], each chunk's
+ *     position in the sequence that stored it (its re-RoPE source), or
+ *     CB_UNKNOWN_TOKEN_OFFSET, which is not indexed (section 5).
+ *   A chunk is keyed by the 64-bit polynomial hash of its tokens, Horner's rule
+ *   h = h * 0x9E3779B97F4A7C15 + token mod 2^64 from h = 0 (section 3.1).  Chunks
+ *   with equal tokens become occupants of one entry, in input order; a chunk
+ *   whose fingerprint is taken by different tokens is not indexed (section
+ *   4.5).  The filter has 2^k slots, k the smallest value >= 4 with 2^k >= 16 x
+ *   entries (growth 16, section 4.4), the slot of a fingerprint being its top k
+ *   bits.
+ *   image: host buffer of image_bytes >= cb_blend_index_image_bytes(n_chunks,
+ *   chunk_size); info: receives the shape (needed by cb_blend_match).
+ * Errors: CB_ERR_INVALID for NULL pointers (with n_chunks > 0), n_chunks < 0,
+ * chunk_size < 1, a negative token or offset below -1; CB_ERR_WORKSPACE for a
+ * small image.  Synchronous host code; no GPU call. */
+cb_status cb_blend_index_build(const int32_t* tokens, const int64_t* chunk_ids, const int32_t* token_offsets,
+                               int32_t n_chunks, int32_t chunk_size, void* image, size_t image_bytes,
+                               cb_blend_index_info* info);
+
+/* Workspace bytes of cb_blend_match for total_tokens query tokens (0 if < 0). */
+size_t cb_blend_match_workspace_bytes(int64_t total_tokens);
+
+/* Most distinct contents one query may match (more: its count is -1). */
+#define CB_MATCH_MAX_CONTENTS 4096
+
+/* cb_blend_match -- match a batch of requests against an index (section 4.2)
+ * and resolve overlaps leftmost-greedy (sections 6.2, 7).
+ *   index_image: device copy of the image; info: its shape (host).
+ *   query_tokens: device int32, the requests back to back; query_starts: device
+ *     int32 [n_queries + 1], request q is tokens [starts[q], starts[q+1]).
+ *     total_tokens (host) = starts[n_queries]; max_query_len (host) bounds
+ *     every request's length (longer requests are cut there; starts are
+ *     clamped to [0, total_tokens]).
+ *   probe_stride: windows start at 0, probe_stride, 2 probe_stride, ... (>= 1).
+ *   prefix_lens: device int32 [n_queries] or NULL (0): the prefix-cache coverage.
+ *   Matching: every window of chunk_size tokens at a probed start is hashed,
+ *   tested against the filter, resolved exactly in the fingerprint table, and
+ *   compared token by token with the entry's tokens; a verified window takes
+ *   the first occupant of the entry that this request has not matched yet.
+ *   Outputs per request q, in ascending cur_st (capacity max_matches each):
+ *     out_chunk[q * max_matches + i] (int64 chunk id), out_old_st (int32 stored
+ *     offset), out_cur_st (int32 start in the request), out_kept (uint8: 1 for
+ *     the matches leftmost-greedy keeps -- drop those starting before the
+ *     prefix length, then keep a match only if it starts at or after the end of
+ *     the last kept one); out_count[q] = matches found (may exceed max_matches,
+ *     of which the first max_matches are written), or -1 when the request
+ *     matched more than CB_MATCH_MAX_CONTENTS distinct contents.
+ *   ws: cb_blend_match_workspace_bytes(total_tokens) bytes.
+ * Errors: CB_ERR_INVALID for NULL pointers, n_queries < 0, probe_stride < 1,
+ * max_matches < 0, an info inconsistent with its own sizes; CB_ERR_WORKSPACE
+ * for a small workspace.  Nothing is written on error. */
+cb_status cb_blend_match(const void* index_image, const cb_blend_index_info* info, const int32_t* query_tokens,
+                         const int32_t* query_starts, int32_t n_queries, int64_t total_tokens, int32_t max_query_len,
+                         int32_t probe_stride, const int32_t* prefix_lens, int32_t max_matches, int64_t* out_chunk,
+                         int32_t* out_old_st, int32_t* out_cur_st, uint8_t* out_kept, int32_t* out_count, void* ws,
+                         size_t ws_bytes, cb_stream_t stream);
 
 /* ---------------------------------------------------------------------------
  * cb_pack_weight -- one layer matrix of a CB_BF16 model into the layout its

@@ -65,6 +65,19 @@ def fingerprint(tokens) -> int:
     return h
 
 
+def fingerprints(rows) -> list[int]:
+    """fingerprint() of every row of a [n][chunk_size] array, Horner's rule run on
+    all rows at once in uint64 arithmetic (which wraps mod 2^64)."""
+    import numpy as np
+    a = np.asarray(rows, dtype=np.uint64)
+    h = np.zeros(a.shape[0], dtype=np.uint64)
+    base = np.uint64(POLY_BASE)
+    with np.errstate(over="ignore"):
+        for j in range(a.shape[1]):
+            h = h * base + a[:, j]
+    return [int(x) for x in h]
+
+
 def window_fingerprints(query, chunk_size: int) -> list[int]:
     """Fingerprint of every window query[s:s+chunk_size], s = 0 .. n - chunk_size,
     rolled (section 4.2): drop the oldest token's term, shift, add the new one."""
@@ -100,8 +113,21 @@ class BlendIndex:
         """Index one stored chunk; False when it is not indexed (sections 4.5, 5)."""
         if int(token_offset) == UNKNOWN_TOKEN_OFFSET or len(tokens) != self.chunk_size:
             return False
+        return self._add(tokens, chunk_id, token_offset, fingerprint(tokens))
+
+    def add_all(self, tokens, chunk_ids, token_offsets) -> int:
+        """add() of every row in order, fingerprints computed together; returns the
+        number indexed."""
+        fps = fingerprints(tokens) if len(tokens) else []
+        n = 0
+        for t, fp, cid, off in zip(tokens, fps, chunk_ids, token_offsets):
+            n += self._add(t, int(cid), int(off), fp)
+        return n
+
+    def _add(self, tokens, chunk_id: int, token_offset: int, fp: int) -> bool:
+        if int(token_offset) == UNKNOWN_TOKEN_OFFSET or len(tokens) != self.chunk_size:
+            return False
         toks = tuple(int(t) for t in tokens)
-        fp = fingerprint(toks)
         entry = self.contents.get(fp)
         if entry is None:
             self.contents[fp] = {"tokens": toks, "occupants": [(int(chunk_id), int(token_offset))]}

@@ -34,7 +34,8 @@ def test_exports_every_declared_function(lib):
             "cb_workspace_bytes", "cb_status_string", "cb_last_error", "cb_abi_version",
             "cb_pack_weight", "cb_packed_weight_bytes", "cb_blend_prefill_streamed",
             "cb_streamed_workspace_bytes", "cb_loading_ratio", "cb_decode_step",
-            "cb_decode_workspace_bytes"} <= set(names)
+            "cb_decode_workspace_bytes", "cb_blend_index_image_bytes", "cb_blend_index_build",
+            "cb_blend_match_workspace_bytes", "cb_blend_match"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", _abi.LIB_PATH], capture_output=True, text=True).stdout
@@ -59,6 +60,7 @@ int main(void) {
   P(cb_blend_params) O(cb_blend_params, flags) O(cb_blend_params, trace)
   P(cb_trace) O(cb_trace, used) O(cb_trace, kinds)
   P(cb_host_chunk) O(cb_host_chunk, v) O(cb_host_chunk, len) O(cb_host_chunk, new_start)
+  P(cb_blend_index_info) O(cb_blend_index_info, table_bits) O(cb_blend_index_info, image_bytes)
   return 0;
 }
 '''
@@ -70,7 +72,7 @@ int main(void) {
         lines = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
     got = dict(l.split() for l in lines if l.strip())
     for name in ("cb_model_cfg", "cb_layer_w", "cb_model", "cb_paged_kv", "cb_chunk", "cb_blend_params", "cb_trace",
-                 "cb_host_chunk"):
+                 "cb_host_chunk", "cb_blend_index_info"):
         cls = getattr(_abi, name)
         assert ctypes.sizeof(cls) == int(got[name]), name
     for key, v in got.items():
@@ -80,7 +82,7 @@ int main(void) {
 
 
 def test_status_strings_and_version(lib):
-    assert lib.cb_abi_version() == 4
+    assert lib.cb_abi_version() == 5
     for code, name in [(0, "CB_OK"), (-1, "CB_ERR_INVALID"), (-2, "CB_ERR_UNSUPPORTED"),
                        (-3, "CB_ERR_WORKSPACE"), (-4, "CB_ERR_DEVICE")]:
         assert lib.cb_status_string(code).decode() == name

@@ -69,6 +69,18 @@ def test_thue_morse_collision_of_the_mod_2_64_hash():
     assert om.match(idx, q1) == [(11, 0, 10)]
 
 
+def test_vectorised_fingerprints_equal_scalar():
+    rng = np.random.default_rng(7)
+    rows = rng.integers(0, 1 << 31, size=(50, 37))
+    assert om.fingerprints(rows) == [om.fingerprint(r) for r in rows]
+    w = cbinputs.fragment_workload(2, n_docs=6, chunk_size=32, n_queries=1)
+    a, b = om.BlendIndex(32), om.BlendIndex(32)
+    for t, i, o in zip(w.stored_tokens, w.stored_ids, w.stored_offsets):
+        a.add(t, int(i), int(o))
+    b.add_all(w.stored_tokens, w.stored_ids, w.stored_offsets)
+    assert a.contents == b.contents
+
+
 def test_rolling_equals_direct_at_every_window():
     rng = np.random.default_rng(2)
     q = rng.integers(0, 128256, size=300)

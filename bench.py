@@ -49,6 +49,8 @@ def parse():
                     help="decode steps timed on the blended cache after the runs (0: skip)")
     ap.add_argument("--streamed-runs", type=int, default=3,
                     help="runs of the layer-pipelined prefill from host memory (0: skip)")
+    ap.add_argument("--match-runs", type=int, default=20,
+                    help="timed runs of fragment matching on a 64-request batch (0: skip)")
     ap.add_argument("--sweep", action="store_true",
                     help="only the size sweep of cb_rerope_k and cb_kv_deviation (one JSON line per size)")
     ap.add_argument("--no-peaks", dest="peaks", action="store_false",
@@ -143,6 +145,74 @@ def work_per_kind(shape, N, Q, ks, sets, chunk_lens):
     w["lm_head"] += shape.vocab * d * es
     w["rerope"] += sum(chunk_lens) * L * kvw * es * 4        # K and V, read + write
     return w
+
+
+MATCH_CHUNK = 256           # the pages' default chunk_size
+
+
+def match_workload(seed):
+    """64 requests of the 4 x 1024 + 64 shape (documents of 4 chunks of 256 tokens,
+    one placed twice, new text between them) over 16448 stored documents."""
+    import cbinputs
+    return cbinputs.fragment_workload(seed + 5, n_docs=16384, chunk_size=MATCH_CHUNK, n_queries=64, docs_per_query=4,
+                                      dup_docs=64, unknown_chunks=64)
+
+
+def match_runs(torch, api, seed, runs):
+    """Fragment matching of one request batch against the index: the index is
+    built on the host once (timed apart), the batch sits in HBM, and `runs`
+    back-to-back cb_blend_match calls are timed with events."""
+    import numpy as np
+    w = match_workload(seed)
+    t0 = time.perf_counter()
+    index = api.BlendIndexImage(w.stored_tokens, w.stored_ids, w.stored_offsets)
+    build_s = time.perf_counter() - t0
+    lens = [len(q) for q in w.queries]
+    starts = np.zeros(len(lens) + 1, dtype=np.int32)
+    starts[1:] = np.cumsum(lens)
+    tq = torch.from_numpy(np.concatenate(w.queries).astype(np.int32)).cuda()
+    ts = torch.from_numpy(starts).cuda()
+    pl = torch.from_numpy(w.prefix_lens).cuda()
+    total, mx = int(starts[-1]), max(lens)
+    ws = api.Workspace(api.cb_blend_match_workspace_bytes(total))
+    out = api.cb_blend_match(index, tq, ts, total, mx, 1, pl, 64, ws)
+    for _ in range(3):
+        api.cb_blend_match(index, tq, ts, total, mx, 1, pl, 64, ws, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(runs):
+        api.cb_blend_match(index, tq, ts, total, mx, 1, pl, 64, ws, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / runs
+    cnt = out["count"].cpu().numpy()
+    kept = out["kept"].cpu().numpy()
+    n_kept = sum(int(kept[q, :max(0, min(int(c), kept.shape[1]))].sum()) for q, c in enumerate(cnt))
+    windows = sum(max(0, n - MATCH_CHUNK + 1) for n in lens)
+    return {"requests": len(lens), "tokens": total, "windows": int(windows), "chunk_size": MATCH_CHUNK,
+            "index_chunks": int(len(w.stored_ids)), "index_entries": int(index.info.n_entries),
+            "image_mb": round(index.info.image_bytes / 1e6, 1), "host_index_build_s": round(build_s, 3),
+            "ms_per_batch": round(ms, 4), "requests_per_s": round(len(lens) / (ms * 1e-3), 1),
+            "tokens_per_s": round(total / (ms * 1e-3), 1), "windows_per_s": round(windows / (ms * 1e-3), 1),
+            "matches": int(cnt.sum()), "kept": n_kept, "runs": runs}
+
+
+def match_cpu_baseline(seed, n_sample=4):
+    """The oracle matcher on a sample of the same request batch (host cores)."""
+    from oracle import match as om
+    w = match_workload(seed)
+    idx = om.BlendIndex(MATCH_CHUNK)
+    t0 = time.perf_counter()
+    idx.add_all(w.stored_tokens, w.stored_ids, w.stored_offsets)
+    build = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for q in w.queries[:n_sample]:
+        om.resolve_leftmost_greedy(om.match(idx, q, 1), MATCH_CHUNK)
+    per_req = (time.perf_counter() - t0) / n_sample
+    return {"value": round(1.0 / per_req, 2), "unit": "requests/s", "cores": 1, "kind": "oracle",
+            "sample": f"pure-Python oracle matcher, {n_sample} of the 64 requests ({per_req * 1e3:.0f} ms each); "
+                      f"oracle index build {build:.1f} s"}
 
 
 def cpu_baseline(wl, seed):
@@ -486,6 +556,7 @@ def main():
     del evict
     peaks = measured_peaks(torch, dev) if args.peaks else None
     decode = decode_runs(torch, api, model, shape, blended, logits, T, args.decode_steps) if args.decode_steps else None
+    match = match_runs(torch, api, args.seed, args.match_runs) if args.match_runs > 0 else None
     streamed = None
     if args.streamed_runs > 0 and not wl.paged:
         streamed = streamed_runs(torch, api, model, chunks, qtok, plain, blended, logits, hkvd, N, args.streamed_runs)
@@ -531,10 +602,13 @@ def main():
         "measured_peaks": peaks,
         "streamed": streamed,
         "decode": decode,
+        "match": match,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.seed)
+        if match is not None:
+            out["cpu_baseline"]["match"] = match_cpu_baseline(args.seed)
     print(json.dumps(out), flush=True)
 
 

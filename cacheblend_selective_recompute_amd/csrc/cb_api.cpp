@@ -1136,9 +1136,9 @@ cb_status cb_blend_match(const void* index_image, const cb_blend_index_info* inf
   ix.slot_bits = I.slot_bits;
   ix.table_bits = I.table_bits;
   ix.n_entries = I.n_entries;
-  uint64_t top = 1;
-  for (int i = 1; i < I.chunk_size; ++i) top *= kPolyBase;
-  ix.top_pow = top;
+  uint64_t pw = 1;
+  for (int i = 0; i < I.chunk_size; ++i) pw *= kPolyBase;
+  ix.pow_c = pw;
   const MatchOut out{out_chunk, out_old_st, out_cur_st, out_kept, out_count};
   CB_TRY(launch_blend_match(ix, query_tokens, query_starts, n_queries, total_tokens, max_query_len, probe_stride,
                             prefix_lens, max_matches, out, static_cast<int32_t*>(ws), reinterpret_cast<hipStream_t>(stream)),

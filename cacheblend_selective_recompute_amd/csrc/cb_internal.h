@@ -265,7 +265,7 @@ bool attention_supported(cb_dtype dt, int n_q_heads, int n_kv_heads, int head_di
 // tokens, entry occupant ranges, occupant chunk ids and offsets).
 // ---------------------------------------------------------------------------
 constexpr uint64_t kPolyBase = 0x9E3779B97F4A7C15ull;
-constexpr int kMatchMaxChunk = 8192;      // longest chunk_size the scan kernel stages in LDS
+constexpr int kMatchMaxChunk = 4096;      // longest chunk_size the scan kernel stages in LDS
 constexpr int kMatchMaxContents = 4096;   // distinct contents one request may match
 struct IndexLayout {
   size_t slots, table_fp, table_entry, entry_tokens, entry_occ, occ_chunk, occ_offset, end;
@@ -284,7 +284,7 @@ inline IndexLayout index_layout(int chunk_size, int64_t n_entries, int64_t n_occ
   L.end = (off + 255) & ~size_t(255);
   return L;
 }
-// the filter: smallest k >= 4 with 2^k >= 16 x entries; the table: load at most 1/2
+// the filter: smallest k >= 4 with 2^k >= 16 x entries; the table: load at most 1/4
 inline int index_slot_bits(int64_t n_entries) {
   int k = 4;
   while ((int64_t(1) << k) < 16 * std::max<int64_t>(n_entries, 1)) ++k;
@@ -292,7 +292,7 @@ inline int index_slot_bits(int64_t n_entries) {
 }
 inline int index_table_bits(int64_t n_entries) {
   int k = 4;
-  while ((int64_t(1) << k) < 2 * std::max<int64_t>(n_entries, 1)) ++k;
+  while ((int64_t(1) << k) < 4 * std::max<int64_t>(n_entries, 1)) ++k;
   return k;
 }
 struct MatchIndexRef {
@@ -304,7 +304,7 @@ struct MatchIndexRef {
   const int64_t* occ_chunk;
   const int32_t* occ_offset;
   int chunk_size, slot_bits, table_bits, n_entries;
-  uint64_t top_pow;               // kPolyBase^(chunk_size - 1) mod 2^64
+  uint64_t pow_c;                 // kPolyBase^chunk_size mod 2^64
 };
 struct MatchOut {
   int64_t* chunk;

@@ -357,7 +357,7 @@ typedef struct cb_blend_index_info {
   int32_t n_occupants;  /* chunks indexed, over all entries */
   int32_t n_skipped;    /* chunks not indexed: unknown offset, or their fingerprint taken by other content */
   int32_t slot_bits;    /* occupancy filter: 2^slot_bits one-byte slots */
-  int32_t table_bits;   /* fingerprint table: 2^table_bits slots, linear probing */
+  int32_t table_bits;   /* fingerprint table: 2^table_bits slots (>= 4 per entry), linear probing */
   uint64_t image_bytes; /* bytes of the image actually used */
 } cb_blend_index_info;
 
@@ -417,9 +417,10 @@ size_t cb_blend_match_workspace_bytes(int64_t total_tokens);
  *     of which the first max_matches are written), or -1 when the request
  *     matched more than CB_MATCH_MAX_CONTENTS distinct contents.
  *   ws: cb_blend_match_workspace_bytes(total_tokens) bytes.
- * Errors: CB_ERR_INVALID for NULL pointers, n_queries < 0, probe_stride < 1,
- * max_matches < 0, an info inconsistent with its own sizes; CB_ERR_WORKSPACE
- * for a small workspace.  Nothing is written on error. */
+ * Errors: CB_ERR_INVALID for NULL pointers, n_queries outside [0, 65535],
+ * probe_stride < 1, max_matches < 0, an info inconsistent with its own sizes,
+ * an image not 256-byte aligned; CB_ERR_UNSUPPORTED for chunk_size above
+ * 4096; CB_ERR_WORKSPACE for a small workspace.  Nothing is written on error. */
 cb_status cb_blend_match(const void* index_image, const cb_blend_index_info* info, const int32_t* query_tokens,
                          const int32_t* query_starts, int32_t n_queries, int64_t total_tokens, int32_t max_query_len,
                          int32_t probe_stride, const int32_t* prefix_lens, int32_t max_matches, int64_t* out_chunk,

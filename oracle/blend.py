@@ -41,14 +41,36 @@ F64 = np.float64
 # storage rounding
 # ----------------------------------------------------------------------------
 
-def store_round(x: np.ndarray, storage: str) -> np.ndarray:
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3(x: np.ndarray) -> np.ndarray:
+    """Nearest value of the OCP FP8 E4M3 grid (1 sign, 4 exponent bits with bias
+    7, 3 mantissa bits; subnormals down to 2^-9; largest finite 448, no
+    infinities), ties to even, magnitudes beyond 448 saturated to 448.
+    A value of magnitude a in binade [2^e, 2^(e+1)) (e >= -6; below that the
+    subnormal spacing) sits on the grid of step 2^(e-3)."""
+    x = np.asarray(x, dtype=F64)
+    a = np.abs(x)
+    _, E = np.frexp(a)                       # a = f * 2^E, f in [0.5, 1)
+    e = np.clip(E - 1, -6, 8)
+    step = np.ldexp(1.0, e - 3)
+    r = np.minimum(np.rint(a / step) * step, FP8_E4M3_MAX)
+    return np.where(x < 0, -r, r)
+
+
+def store_round(x: np.ndarray, storage: str, scale: float = 1.0) -> np.ndarray:
     """Round ``x`` to the storage dtype and return it as float64.
 
     'f32' rounds to IEEE single (nearest even); 'bf16' keeps 7 explicit
     mantissa bits, rounding the float64 value directly to nearest, ties to
-    even (normal range only, which is all this method produces).
+    even (normal range only, which is all this method produces); 'fp8' stores
+    fp8_e4m3(x / scale) and the value it stands for is that times ``scale``
+    (one scale per cache tensor).
     """
     x = np.asarray(x, dtype=F64)
+    if storage == "fp8":
+        return fp8_e4m3(x / float(scale)) * float(scale)
     if storage == "f32":
         return x.astype(np.float32).astype(F64)
     if storage == "bf16":
@@ -104,7 +126,7 @@ def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
     return out
 
 
-def rerope(k: np.ndarray, delta: int, theta: float, storage: str) -> np.ndarray:
+def rerope(k: np.ndarray, delta: int, theta: float, storage: str, scale: float = 1.0) -> np.ndarray:
     """Re-RoPE cached keys from their stored offset to the new one.
 
     [CB] "位置恢复": k' = R_{n-p} k_p = R_n k.  ``k`` is [..., n, H, d_h]
@@ -115,7 +137,7 @@ def rerope(k: np.ndarray, delta: int, theta: float, storage: str) -> np.ndarray:
     shp = k.shape
     flat = k.reshape(-1, shp[-2], shp[-1])
     out = rope(flat, np.full(flat.shape[0], delta, dtype=F64), theta)
-    return store_round(out.reshape(shp), storage)
+    return store_round(out.reshape(shp), storage, scale)
 
 
 def causal_attention(q: np.ndarray, q_pos: np.ndarray, k: np.ndarray, v: np.ndarray,
@@ -186,6 +208,15 @@ class OracleModel:
     storage: str
     layer: Callable[[int], Dict[str, np.ndarray]]
     glob: Dict[str, np.ndarray]
+    kv_storage: Optional[str] = None   # the KV cache's storage ('fp8' or the model dtype when None)
+    k_scale: float = 1.0               # fp8 cache: stored K = k_scale * grid value
+    v_scale: float = 1.0
+
+    def store_k(self, x: np.ndarray) -> np.ndarray:
+        return store_round(x, self.kv_storage or self.storage, self.k_scale)
+
+    def store_v(self, x: np.ndarray) -> np.ndarray:
+        return store_round(x, self.kv_storage or self.storage, self.v_scale)
 
     @classmethod
     def from_shape(cls, shape, weights_or_fn, glob=None) -> "OracleModel":
@@ -273,8 +304,8 @@ def full_prefill(m: OracleModel, tokens: np.ndarray, start: int = 0) -> Dict[str
     for l in range(m.n_layers):
         w = m.layer(l)
         a = rms_norm(x, w["attn_norm"], m.rms_eps)
-        K[l] = store_round(rope(m.heads(_proj(a, w["wk"]), m.n_kv_heads), pos, m.rope_theta), m.storage)
-        V[l] = store_round(m.heads(_proj(a, w["wv"]), m.n_kv_heads), m.storage)
+        K[l] = m.store_k(rope(m.heads(_proj(a, w["wk"]), m.n_kv_heads), pos, m.rope_theta))
+        V[l] = m.store_v(m.heads(_proj(a, w["wv"]), m.n_kv_heads))
         x = _attn_mlp(m, w, x, a, pos, K[l], V[l], pos)
     return {"K": K, "V": V, "x": x, "logits": _logits(m, x[-1])}
 
@@ -294,8 +325,8 @@ def decode_step(m: OracleModel, Kb: np.ndarray, Vb: np.ndarray, token: int, pos:
     for l in range(m.n_layers):
         w = m.layer(l)
         a = rms_norm(x, w["attn_norm"], m.rms_eps)
-        Kb[l, pos] = store_round(rope(m.heads(_proj(a, w["wk"]), m.n_kv_heads), p, m.rope_theta), m.storage)[0]
-        Vb[l, pos] = store_round(m.heads(_proj(a, w["wv"]), m.n_kv_heads), m.storage)[0]
+        Kb[l, pos] = m.store_k(rope(m.heads(_proj(a, w["wk"]), m.n_kv_heads), p, m.rope_theta))[0]
+        Vb[l, pos] = m.store_v(m.heads(_proj(a, w["wv"]), m.n_kv_heads))[0]
         x = _attn_mlp(m, w, x, a, p, Kb[l, :pos + 1], Vb[l, :pos + 1], keys)
     return _logits(m, x[0])
 
@@ -320,8 +351,8 @@ def assemble_blended(m: OracleModel, chunks: Sequence[Tuple], n_query: int) -> T
     Vb = np.zeros_like(Kb)
     for tokens, Kc, Vc, old, new in chunks:
         ln = len(tokens)
-        Kb[:, new:new + ln] = rerope(Kc, new - old, m.rope_theta, m.storage)
-        Vb[:, new:new + ln] = np.asarray(Vc, dtype=F64)
+        Kb[:, new:new + ln] = rerope(Kc, new - old, m.rope_theta, m.kv_storage or m.storage, m.k_scale)
+        Vb[:, new:new + ln] = m.store_v(Vc)      # a value already on the cache's grid stays as it is
     return Kb, Vb
 
 
@@ -388,8 +419,8 @@ def blend_layer(m: OracleModel, l: int, Kl: np.ndarray, Vl: np.ndarray, x_rows: 
     sel = np.concatenate([slot, nc + np.arange(n_query)])
     wpos = rows_pos[sel]
     # fill: fresh K/V of the kept rows and the suffix replace the cache
-    Kl[wpos] = store_round(kf[sel], m.storage)
-    Vl[wpos] = store_round(vf[sel], m.storage)
+    Kl[wpos] = m.store_k(kf[sel])
+    Vl[wpos] = m.store_v(vf[sel])
     if out_rows is not None:
         sel = sel[np.asarray(out_rows, dtype=np.int64)]
     x_out = _attn_mlp(m, w, x_rows[sel], a[sel], rows_pos[sel], Kl, Vl, np.arange(T))
@@ -425,8 +456,8 @@ def blend_prefill(m: OracleModel, chunks: Sequence[Tuple], query_tokens: np.ndar
     w = m.layer(0)
     x = np.asarray(m.glob["embed"][np.asarray(tokens)], dtype=F64)
     a = rms_norm(x, w["attn_norm"], m.rms_eps)
-    Kb[0, suffix] = store_round(rope(m.heads(_proj(a[N:], w["wk"]), m.n_kv_heads), suffix, m.rope_theta), m.storage)
-    Vb[0, suffix] = store_round(m.heads(_proj(a[N:], w["wv"]), m.n_kv_heads), m.storage)
+    Kb[0, suffix] = m.store_k(rope(m.heads(_proj(a[N:], w["wk"]), m.n_kv_heads), suffix, m.rope_theta))
+    Vb[0, suffix] = m.store_v(m.heads(_proj(a[N:], w["wv"]), m.n_kv_heads))
     x = _attn_mlp(m, w, x, a, pos, Kb[0], Vb[0], pos)
     S = np.arange(N)
     sets = {0: S}
@@ -484,8 +515,8 @@ def blend_prefill_masked(m: OracleModel, chunks: Sequence[Tuple], query_tokens: 
             else:
                 keep = cand.copy()
             write = keep | is_suffix
-        Kb[l] = np.where(write[:, None, None], store_round(kf, m.storage), Kb[l])
-        Vb[l] = np.where(write[:, None, None], store_round(vf, m.storage), Vb[l])
+        Kb[l] = np.where(write[:, None, None], m.store_k(kf), Kb[l])
+        Vb[l] = np.where(write[:, None, None], m.store_v(vf), Vb[l])
         active = keep | is_suffix if l > 0 else np.ones(T, dtype=bool)
         x_new = _attn_mlp(m, w, x, a, pos, Kb[l], Vb[l], pos)
         x = np.where(active[:, None], x_new, x)
@@ -508,8 +539,8 @@ def full_reuse_prefill(m: OracleModel, Kb: np.ndarray, Vb: np.ndarray, query_tok
     for l in range(L):
         w = m.layer(l)
         a = rms_norm(x, w["attn_norm"], m.rms_eps)
-        Kb[l, suffix] = store_round(rope(m.heads(_proj(a, w["wk"]), m.n_kv_heads), suffix, m.rope_theta), m.storage)
-        Vb[l, suffix] = store_round(m.heads(_proj(a, w["wv"]), m.n_kv_heads), m.storage)
+        Kb[l, suffix] = m.store_k(rope(m.heads(_proj(a, w["wk"]), m.n_kv_heads), suffix, m.rope_theta))
+        Vb[l, suffix] = m.store_v(m.heads(_proj(a, w["wv"]), m.n_kv_heads))
         x = _attn_mlp(m, w, x, a, suffix, Kb[l], Vb[l], np.arange(T))
     return {"K": Kb, "V": Vb, "logits": _logits(m, x[-1])}
 

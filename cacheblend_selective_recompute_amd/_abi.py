@@ -40,15 +40,21 @@ class cb_model(ctypes.Structure):
                 ("lm_head", c_void_p), ("layers", POINTER(cb_layer_w)), ("weights_packed", c_int32)]
 
 
+CB_KV_MODEL = 0
+CB_KV_FP8_E4M3 = 1
+
+
 class cb_paged_kv(ctypes.Structure):
     _fields_ = [("k", c_void_p), ("v", c_void_p), ("block_table", c_void_p),
-                ("block_size", c_int32), ("n_logical", c_int32), ("layer_stride", c_int64)]
+                ("block_size", c_int32), ("n_logical", c_int32), ("layer_stride", c_int64),
+                ("kv_format", c_int32), ("k_scale", c_float), ("v_scale", c_float)]
 
 
 class cb_chunk(ctypes.Structure):
     _fields_ = [("tokens", c_void_p), ("k", c_void_p), ("v", c_void_p), ("block_ids", c_void_p),
                 ("len", c_int32), ("old_start", c_int32), ("new_start", c_int32),
-                ("block_size", c_int32), ("layer_stride", c_int64)]
+                ("block_size", c_int32), ("layer_stride", c_int64),
+                ("kv_format", c_int32), ("k_scale", c_float), ("v_scale", c_float)]
 
 
 class cb_host_chunk(ctypes.Structure):

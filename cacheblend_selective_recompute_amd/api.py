@@ -17,7 +17,7 @@ import numpy as np
 import torch
 
 from . import _abi
-from ._abi import (CB_BF16, CB_COPY_V, CB_F32, CB_OK, cb_blend_params, cb_chunk, cb_host_chunk, cb_layer_w, cb_model,
+from ._abi import (CB_BF16, CB_COPY_V, CB_F32, CB_KV_FP8_E4M3, CB_KV_MODEL, CB_OK, cb_blend_params, cb_chunk, cb_host_chunk, cb_layer_w, cb_model,
                    cb_model_cfg, cb_paged_kv)
 
 
@@ -136,11 +136,26 @@ class DeviceModel:
         return cls(shape, t["layers"], t["embed"], t["lm_head"], t["final_norm"])
 
 
+def fp8_encode(x: torch.Tensor, scale: float) -> torch.Tensor:
+    """FP8 E4M3 bytes (torch.uint8) of x / scale, saturated at +-448 (input
+    preparation for 8-bit caches; the library itself rounds on the GPU)."""
+    y = (x.float() / float(scale)).clamp_(-448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def fp8_decode(b: torch.Tensor, scale: float) -> torch.Tensor:
+    """fp32 values of FP8 E4M3 bytes times scale."""
+    return b.view(torch.float8_e4m3fn).float() * float(scale)
+
+
 class PagedKV:
-    """Paged K/V pools [L][n_phys * bs][Hkv][dh] plus a block table."""
+    """Paged K/V pools [L][n_phys * bs][Hkv][dh] plus a block table.  With
+    kv_format CB_KV_FP8_E4M3 the pools hold one FP8 E4M3 byte per element
+    (torch.uint8 storage) standing for element x k_scale (K) or x v_scale (V)."""
 
     def __init__(self, shape, n_tokens: int, block_size: int = 16, block_table: Optional[np.ndarray] = None,
-                 n_phys: Optional[int] = None, device="cuda", fill: Optional[float] = None):
+                 n_phys: Optional[int] = None, device="cuda", fill: Optional[float] = None,
+                 kv_format: int = CB_KV_MODEL, k_scale: float = 1.0, v_scale: float = 1.0):
         self.shape = shape
         self.n_tokens = n_tokens
         self.block_size = block_size
@@ -149,18 +164,24 @@ class PagedKV:
             block_table = np.arange(n_log, dtype=np.int32)
         block_table = np.asarray(block_table, dtype=np.int32)
         self.n_phys = int(n_phys if n_phys is not None else max(int(block_table.max(initial=-1)) + 1, n_log))
-        td = torch_dtype(shape.dtype)
+        self.kv_format, self.k_scale, self.v_scale = int(kv_format), float(k_scale), float(v_scale)
+        fp8 = self.kv_format == CB_KV_FP8_E4M3
+        td = torch.uint8 if fp8 else torch_dtype(shape.dtype)
         dims = (shape.n_layers, self.n_phys * block_size, shape.n_kv_heads, shape.head_dim)
         if fill is None:
             self.k = torch.empty(dims, dtype=td, device=device)
             self.v = torch.empty(dims, dtype=td, device=device)
+        elif fp8:
+            self.k = fp8_encode(torch.full(dims, fill, device=device), self.k_scale)
+            self.v = fp8_encode(torch.full(dims, fill, device=device), self.v_scale)
         else:
             self.k = torch.full(dims, fill, dtype=td, device=device)
             self.v = torch.full(dims, fill, dtype=td, device=device)
         self.block_table_host = block_table
         self.block_table = torch.from_numpy(block_table).to(device)
         self.c = cb_paged_kv(self.k.data_ptr(), self.v.data_ptr(), self.block_table.data_ptr(), block_size,
-                             len(block_table), self.n_phys * block_size * shape.kv_width)
+                             len(block_table), self.n_phys * block_size * shape.kv_width, self.kv_format,
+                             self.k_scale, self.v_scale)
 
     def slots(self, positions) -> torch.Tensor:
         """Physical row of each logical position (host computation on the host copy of the table)."""
@@ -169,9 +190,12 @@ class PagedKV:
         return torch.from_numpy(rows).to(self.k.device)
 
     def logical(self, n: Optional[int] = None):
-        """(K, V) [L][n][Hkv][dh] in logical position order (a copy)."""
+        """(K, V) [L][n][Hkv][dh] in logical position order (a copy; an FP8 cache is
+        returned as the fp32 values it stands for)."""
         n = self.n_tokens if n is None else n
         idx = self.slots(np.arange(n))
+        if self.kv_format == CB_KV_FP8_E4M3:
+            return fp8_decode(self.k[:, idx], self.k_scale), fp8_decode(self.v[:, idx], self.v_scale)
         return self.k[:, idx], self.v[:, idx]
 
 
@@ -187,6 +211,9 @@ class ChunkSource:
     block_ids: Optional[torch.Tensor] = None
     block_size: int = 16
     layer_stride: int = 0
+    kv_format: int = CB_KV_MODEL
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def len(self) -> int:
@@ -196,7 +223,8 @@ class ChunkSource:
         return cb_chunk(self.tokens.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
                         self.block_ids.data_ptr() if self.block_ids is not None else None,
                         self.len, int(self.old_start), int(self.new_start),
-                        int(self.block_size if self.block_ids is not None else 0), int(self.layer_stride))
+                        int(self.block_size if self.block_ids is not None else 0), int(self.layer_stride),
+                        int(self.kv_format), float(self.k_scale), float(self.v_scale))
 
 
 @dataclass

@@ -14,6 +14,7 @@
 // Everything is enqueued on the caller's stream; nothing synchronises, nothing
 // allocates.  Validation runs before the first enqueue.
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -116,7 +117,15 @@ cb_status check_paged(const cb_model_cfg* c, const cb_paged_kv* p, int64_t n_tok
   if (static_cast<int64_t>(p->n_logical) * p->block_size < n_tokens)
     return fail(CB_ERR_INVALID, "%s: block table covers %lld tokens, %lld needed", what,
                 (long long)p->n_logical * p->block_size, (long long)n_tokens);
-  const int64_t vec = 16 / esize(c->dtype);
+  if (p->kv_format != CB_KV_MODEL && p->kv_format != CB_KV_FP8_E4M3)
+    return fail(CB_ERR_INVALID, "%s: unknown kv_format %d", what, p->kv_format);
+  const bool fp8 = p->kv_format == CB_KV_FP8_E4M3;
+  if (fp8 && c->dtype != CB_BF16) return fail(CB_ERR_UNSUPPORTED, "%s: an 8-bit cache needs a CB_BF16 model", what);
+  if (fp8 && !(p->k_scale > 0.f && p->v_scale > 0.f && std::isfinite(p->k_scale) && std::isfinite(p->v_scale)))
+    return fail(CB_ERR_INVALID, "%s: 8-bit cache scales must be positive and finite", what);
+  if (fp8 && (c->n_kv_heads * c->head_dim) % 16)
+    return fail(CB_ERR_UNSUPPORTED, "%s: an 8-bit cache needs n_kv_heads*head_dim a multiple of 16", what);
+  const int64_t vec = fp8 ? 16 : 16 / esize(c->dtype);
   if (p->layer_stride < 0 || p->layer_stride % vec)
     return fail(CB_ERR_INVALID, "%s: layer_stride must be a non-negative multiple of %lld elements", what,
                 (long long)vec);
@@ -126,9 +135,14 @@ cb_status check_paged(const cb_model_cfg* c, const cb_paged_kv* p, int64_t n_tok
 cb_status check_chunk_sources(const cb_model_cfg* c, const cb_chunk* ch, int n, bool need_tokens) {
   if (n < 0) return fail(CB_ERR_INVALID, "n_chunks < 0");
   if (n > 0 && !ch) return fail(CB_ERR_INVALID, "chunks is NULL");
-  const int64_t vec = 16 / esize(c->dtype);
   for (int i = 0; i < n; ++i) {
     const cb_chunk& x = ch[i];
+    if (x.kv_format != CB_KV_MODEL && x.kv_format != CB_KV_FP8_E4M3)
+      return fail(CB_ERR_INVALID, "chunk %d: unknown kv_format %d", i, x.kv_format);
+    const bool fp8 = x.kv_format == CB_KV_FP8_E4M3;
+    if (fp8 && !(x.k_scale > 0.f && x.v_scale > 0.f && std::isfinite(x.k_scale) && std::isfinite(x.v_scale)))
+      return fail(CB_ERR_INVALID, "chunk %d: 8-bit scales must be positive and finite", i);
+    const int64_t vec = fp8 ? 16 : 16 / esize(c->dtype);
     if (x.len < 0) return fail(CB_ERR_INVALID, "chunk %d: len < 0", i);
     if (x.old_start < 0)
       return fail(CB_ERR_INVALID, "chunk %d: unknown stored offset %d (a wrong position gives wrong KV)", i,
@@ -142,6 +156,15 @@ cb_status check_chunk_sources(const cb_model_cfg* c, const cb_chunk* ch, int n, 
     if (x.layer_stride < 0 || x.layer_stride % vec)
       return fail(CB_ERR_INVALID, "chunk %d: layer_stride must be a non-negative multiple of %lld", i, (long long)vec);
   }
+  return CB_OK;
+}
+
+// every chunk must be stored in the destination's element format
+cb_status check_chunk_formats(const cb_chunk* ch, int n, const cb_paged_kv* dst) {
+  for (int i = 0; i < n; ++i)
+    if (ch[i].len > 0 && ch[i].kv_format != dst->kv_format)
+      return fail(CB_ERR_UNSUPPORTED, "chunk %d: kv_format %d differs from the destination's %d", i, ch[i].kv_format,
+                  dst->kv_format);
   return CB_OK;
 }
 
@@ -253,7 +276,9 @@ size_t carve(const cb_model_cfg& c, int64_t N, int64_t Q, int64_t C, void* base,
 }
 
 PagedRef ref_of(const cb_paged_kv& p) {
-  return PagedRef{p.k, p.v, p.block_table, p.block_size, p.layer_stride, block_shift(p.block_size)};
+  const bool fp8 = p.kv_format == CB_KV_FP8_E4M3;
+  return PagedRef{p.k,  p.v,  p.block_table, p.block_size, p.layer_stride, block_shift(p.block_size),
+                  fp8,  fp8 ? p.k_scale : 1.f, fp8 ? p.v_scale : 1.f};
 }
 
 // Chunk descriptors for one launch batch [first, first + count).
@@ -275,6 +300,9 @@ ChunkBatch make_batch(const cb_model_cfg& c, const cb_chunk* ch, int first, int 
     d.block_size = x.block_ids ? x.block_size : 1;
     d.delta = x.new_start - x.old_start;
     d.tile_begin = tiles;
+    d.fp8 = x.kv_format == CB_KV_FP8_E4M3;
+    d.ks = d.fp8 ? x.k_scale : 1.f;
+    d.vs = d.fp8 ? x.v_scale : 1.f;
     tiles += c.n_layers * ((x.len + 15) / 16);
   }
   b.n = count;
@@ -539,6 +567,7 @@ cb_status cb_rerope_k(const cb_model_cfg* cfg, const cb_chunk* chunks, int32_t n
   int64_t end = 0;
   for (int i = 0; i < n_chunks; ++i) end = std::max<int64_t>(end, (int64_t)chunks[i].new_start + chunks[i].len);
   if ((st = check_paged(cfg, dst, end, "dst")) != CB_OK) return st;
+  if ((st = check_chunk_formats(chunks, n_chunks, dst)) != CB_OK) return st;
   if (flags & ~CB_COPY_V) return fail(CB_ERR_INVALID, "unknown flags 0x%x", flags);
   const size_t need = cb_workspace_bytes(cfg, 0, 0, n_chunks);
   if (n_chunks > 0 && (!ws || ws_bytes < need))
@@ -822,6 +851,7 @@ cb_status cb_blend_prefill(const cb_model* model, const cb_chunk* chunks, int32_
   if ((st = check_tiling(chunks, n_chunks, &N64)) != CB_OK) return st;
   const int N = static_cast<int>(N64);
   if ((st = check_blend_call(model, N, query_tokens, n_query, params, blended, logits)) != CB_OK) return st;
+  if ((st = check_chunk_formats(chunks, n_chunks, blended)) != CB_OK) return st;
   const size_t need = cb_workspace_bytes(&c, N, n_query, n_chunks);
   if (!ws || ws_bytes < need) return fail(CB_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, need);
   if (!aligned16(ws)) return fail(CB_ERR_INVALID, "workspace not 16-byte aligned");
@@ -863,6 +893,8 @@ cb_status cb_blend_prefill_streamed(const cb_model* model, const cb_host_chunk* 
   if ((st = check_tiling(dev.data(), n_chunks, &N64)) != CB_OK) return st;
   const int N = static_cast<int>(N64);
   if ((st = check_blend_call(model, N, query_tokens, n_query, params, blended, logits)) != CB_OK) return st;
+  if (blended->kv_format != CB_KV_MODEL)
+    return fail(CB_ERR_UNSUPPORTED, "the layer-pipelined prefill takes caches in the model dtype only");
   if (!events) return fail(CB_ERR_INVALID, "NULL events");
   for (int i = 0; i < 2 * c.n_layers; ++i)
     if (!events[i]) return fail(CB_ERR_INVALID, "event %d is NULL", i);

@@ -15,6 +15,7 @@
 // K blocks are staged row-major in LDS, V blocks transposed.  Query tiles run
 // longest-first (their rows are sorted by position).
 #include <algorithm>
+#include <type_traits>
 
 #include "cb_internal.h"
 
@@ -39,7 +40,9 @@ constexpr int KVB = 64;            // keys per block
 constexpr int kBtCache = 4096;     // block-table entries a workgroup stages in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int DH, int G, bool STAGED, int NG>
+// F8: the cache holds FP8 E4M3 elements; they widen exactly to bf16 when staged
+// into LDS, the K scale joins the softmax scale and the V scale the output.
+template <int DH, int G, bool STAGED, int NG, bool F8 = false>
 __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_bf16_kernel(AttnArgs a, int n_splits, int ksplit) {
   constexpr int QROWS = 64 * NG;         // query rows per workgroup (NG groups of 16 per wave)
   constexpr int QT = QROWS / G;          // query tokens per tile
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_bf16_kernel(AttnArg
     m_run[g] = -INFINITY;
     l_run[g] = 0.f;      // this lane's partial row sum
   }
-  const float sc = a.scale * kLog2e;
+  const float sc = a.scale * kLog2e * (F8 ? a.cache.ks : 1.0f);
 
   // page-table entries of keys [j_begin, j_end) staged once in LDS (the launcher
   // sizes the key splits so they fit), so K/V loads never wait on a table load
@@ -118,8 +121,9 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_bf16_kernel(AttnArg
     const int e = STAGED ? btab[b - blk0] : a.cache.bt[b];
     return sh >= 0 ? (static_cast<int64_t>(e) << sh) + (p & (bs - 1)) : static_cast<int64_t>(e) * bs + (p - b * bs);
   };
-  const bf16_t* kbase = static_cast<const bf16_t*>(a.cache.k) + static_cast<int64_t>(a.layer) * a.cache.layer_stride;
-  const bf16_t* vbase = static_cast<const bf16_t*>(a.cache.v) + static_cast<int64_t>(a.layer) * a.cache.layer_stride;
+  using E = typename std::conditional<F8, fp8_t, bf16_t>::type;   // cache element
+  const E* kbase = static_cast<const E*>(a.cache.k) + static_cast<int64_t>(a.layer) * a.cache.layer_stride;
+  const E* vbase = static_cast<const E*>(a.cache.v) + static_cast<int64_t>(a.layer) * a.cache.layer_stride;
   const int width = a.n_kv_heads * DH;
 
   // staging roles: K chunk c = tid + 256*u -> key c / CPR, dims (c % CPR)*8;
@@ -127,27 +131,47 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_bf16_kernel(AttnArg
   // so the 16 lanes of an LDS write phase cover one V^T row's 64 keys (no bank conflicts)
   const int vkey = 4 * (tid % (KVB / 4));
   const int vdim = 8 * (tid / (KVB / 4));
+  // 8 elements per chunk: 16 bytes of bf16, or 8 bytes of FP8 widened in lstore
+  using R = typename std::conditional<F8, uint2, uint4>::type;
+  R kraw[KCH], vraw[4];
   uint4 kreg[KCH], vreg[4];
   auto gload = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
       const int c = tid + 256 * u;
       const int p = j0 + c / CPR;
-      kreg[u] = make_uint4(0, 0, 0, 0);
+      kraw[u] = R{};
       if (p < j_end)
-        kreg[u] = *reinterpret_cast<const uint4*>(kbase + krow(p) * width + kvh * DH + (c % CPR) * 8);
+        kraw[u] = *reinterpret_cast<const R*>(kbase + krow(p) * width + kvh * DH + (c % CPR) * 8);
     }
     if (tid < VTHREADS) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int p = j0 + vkey + i;
-        vreg[i] = make_uint4(0, 0, 0, 0);
+        vraw[i] = R{};
         if (p < j_end)
-          vreg[i] = *reinterpret_cast<const uint4*>(vbase + krow(p) * width + kvh * DH + vdim);
+          vraw[i] = *reinterpret_cast<const R*>(vbase + krow(p) * width + kvh * DH + vdim);
       }
     }
   };
+  auto widen = [](const R& r) -> uint4 {
+    if constexpr (F8) {
+      float f[8];
+      fp8x4_to_f32(r.x, f);
+      fp8x4_to_f32(r.y, f + 4);
+      return make_uint4(fp8x2_to_bf16x2(f[0], f[1]), fp8x2_to_bf16x2(f[2], f[3]), fp8x2_to_bf16x2(f[4], f[5]),
+                        fp8x2_to_bf16x2(f[6], f[7]));
+    } else {
+      return r;
+    }
+  };
   auto lstore = [&]() {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) kreg[u] = widen(kraw[u]);
+    if (tid < VTHREADS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vreg[i] = widen(vraw[i]);
+    }
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
       const int c = tid + 256 * u;
@@ -266,7 +290,7 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_bf16_kernel(AttnArg
     l_tot += __shfl_xor(l_tot, 32, 64);
     if (!qvalid[g]) continue;
     if (n_splits == 1) {
-      const float inv = 1.0f / l_tot;
+      const float inv = (F8 ? a.cache.vs : 1.0f) / l_tot;
       bf16_t* ob = static_cast<bf16_t*>(a.o);
       const int KO = a.n_q_heads * DH;
       // o[g][dt][i] = O[q][16*dt + 4*kgrp + i]; written fragment-major (4 consecutive columns = 8 bytes)
@@ -281,9 +305,11 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_bf16_kernel(AttnArg
       // unnormalised partial for (split, row, head); m in log2 units
       const int64_t pr = (static_cast<int64_t>(split) * a.R + qtok[g]) * a.n_q_heads + qhead[g];
       float* op = a.part_o + pr * DH;
+      const float vsc = F8 ? a.cache.vs : 1.0f;
 #pragma unroll
       for (int dt = 0; dt < DH / 16; ++dt)
-        *reinterpret_cast<float4*>(op + 16 * dt + 4 * kgrp) = make_float4(o[g][dt][0], o[g][dt][1], o[g][dt][2], o[g][dt][3]);
+        *reinterpret_cast<float4*>(op + 16 * dt + 4 * kgrp) =
+            make_float4(o[g][dt][0] * vsc, o[g][dt][1] * vsc, o[g][dt][2] * vsc, o[g][dt][3] * vsc);
       if (kgrp == 0) a.part_ml[pr] = make_float2(m_run[g], l_tot);
     }
   }
@@ -919,7 +945,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int DH, int G, int NG, int KIND>   // KIND 0 register-staged, 1 LDS-DMA, 2 lean LDS-DMA
+template <int DH, int G, int NG, int KIND, bool F8 = false>   // KIND 0 register-staged, 1 LDS-DMA, 2 lean LDS-DMA
 hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   constexpr int QT = 64 * NG / G;
   const int n_tiles = (a.R + QT - 1) / QT;
@@ -949,9 +975,9 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
     else
       attn_dma_kernel<G, false, NG><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
   } else if (ksplit / a.cache.bs + 2 <= kBtCache) {
-    attn_bf16_kernel<DH, G, true, NG><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
+    attn_bf16_kernel<DH, G, true, NG, F8><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
   } else {
-    attn_bf16_kernel<DH, G, false, NG><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
+    attn_bf16_kernel<DH, G, false, NG, F8><<<grid, 256, 0, s>>>(a, n_splits, ksplit);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;
@@ -970,7 +996,7 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
 // while the scores are made.  Partials (unnormalised sums, running max in
 // log2 units, sum of weights) go to the split-KV buffers.
 // ---------------------------------------------------------------------------
-template <int DH, int G, bool RUN16>
+template <int DH, int G, bool RUN16, bool F8 = false>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int ksplit) {
   static_assert(DH == 128, "two output dims per lane");
   __shared__ uint4 qs[G][DH / 8];        // bf16 query heads, 8 dims per entry
@@ -987,11 +1013,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int ksplit
   const uint4* qrow = reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(a.q) + static_cast<int64_t>(kvh) * G * DH);
   uint4 qv = {};
   if (tid < G * DH / 8) qv = qrow[tid];   // stored to LDS once the first K/V loads are out
-  const float sc_l2 = a.scale * kLog2e;
+  const float sc_l2 = a.scale * kLog2e * (F8 ? a.cache.ks : 1.0f);
   const int width = a.n_kv_heads * DH;
   const int64_t lbase = static_cast<int64_t>(a.layer) * a.cache.layer_stride + kvh * DH;
-  const bf16_t* kc = static_cast<const bf16_t*>(a.cache.k) + lbase;
-  const bf16_t* vc = static_cast<const bf16_t*>(a.cache.v) + lbase;
+  using E = typename std::conditional<F8, fp8_t, bf16_t>::type;   // cache element
+  const E* kc = static_cast<const E*>(a.cache.k) + lbase;
+  const E* vc = static_cast<const E*>(a.cache.v) + lbase;
   const int kk = tid >> 2, quarter = tid & 3;
   // loads run to j_lim without waiting for the row's position; keys past it are masked
   const int j_end = min(a.rowpos[0] + 1, j_lim);
@@ -1021,11 +1048,34 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int ksplit
     }
     uint4 kr[4];
     const uint4* kp = reinterpret_cast<const uint4*>(kc + krow * width + quarter * 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kr[i] = kp[i];
     uint32_t vr[16];
+    if constexpr (F8) {
+      // 32 FP8 dims widen exactly to bf16 pairs; V: two FP8 dims per lane
+      const uint4 k8[2] = {kp[0], kp[1]};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) vr[i] = *reinterpret_cast<const uint32_t*>(vc + vrow[i] * width + 2 * lane);
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t w[4] = {k8[h].x, k8[h].y, k8[h].z, k8[h].w};
+        float f[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fp8x4_to_f32(w[i], f + 4 * i);
+        kr[2 * h] = make_uint4(fp8x2_to_bf16x2(f[0], f[1]), fp8x2_to_bf16x2(f[2], f[3]), fp8x2_to_bf16x2(f[4], f[5]),
+                               fp8x2_to_bf16x2(f[6], f[7]));
+        kr[2 * h + 1] = make_uint4(fp8x2_to_bf16x2(f[8], f[9]), fp8x2_to_bf16x2(f[10], f[11]),
+                                   fp8x2_to_bf16x2(f[12], f[13]), fp8x2_to_bf16x2(f[14], f[15]));
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint16_t b2 = *reinterpret_cast<const uint16_t*>(vc + vrow[i] * width + 2 * lane);
+        float f[4];
+        fp8x4_to_f32(b2, f);
+        vr[i] = fp8x2_to_bf16x2(f[0], f[1]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kr[i] = kp[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) vr[i] = *reinterpret_cast<const uint32_t*>(vc + vrow[i] * width + 2 * lane);
+    }
     if (t0 == j_begin) {
       if (tid < G * DH / 8) qs[tid / (DH / 8)][tid % (DH / 8)] = qv;
       __syncthreads();
@@ -1088,7 +1138,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int ksplit
   for (int e = tid; e < G * DH; e += 256) {
     const int g = e / DH, d = e % DH;
     const int64_t pr = static_cast<int64_t>(split) * a.n_q_heads + kvh * G + g;   // (split, row 0, head)
-    a.part_o[pr * DH + d] = ((red[0][g][d] + red[1][g][d]) + red[2][g][d]) + red[3][g][d];
+    a.part_o[pr * DH + d] = (((red[0][g][d] + red[1][g][d]) + red[2][g][d]) + red[3][g][d]) * (F8 ? a.cache.vs : 1.0f);
     if (d == 0) a.part_ml[pr] = make_float2(m_run[g], l_run[g]);
   }
 }
@@ -1177,10 +1227,17 @@ hipError_t run_decode(const AttnArgs& a, hipStream_t s) {
   const int ksplit = ((kv_blocks + n_splits - 1) / n_splits) * KVB;
   n_splits = (a.kv_bound + ksplit - 1) / ksplit;
   // pages of 16 keys or more (a power of two): a wave's 16 keys are consecutive rows
-  if (a.cache.bt == nullptr || a.cache.bs_shift >= 4)
+  const bool run16 = a.cache.bt == nullptr || a.cache.bs_shift >= 4;
+  if (a.cache.fp8) {
+    if (run16)
+      attn_decode_kernel<128, G, true, true><<<n_splits * a.n_kv_heads, 256, 0, s>>>(a, ksplit);
+    else
+      attn_decode_kernel<128, G, false, true><<<n_splits * a.n_kv_heads, 256, 0, s>>>(a, ksplit);
+  } else if (run16) {
     attn_decode_kernel<128, G, true><<<n_splits * a.n_kv_heads, 256, 0, s>>>(a, ksplit);
-  else
+  } else {
     attn_decode_kernel<128, G, false><<<n_splits * a.n_kv_heads, 256, 0, s>>>(a, ksplit);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   attn_combine_row_kernel<128><<<a.n_q_heads, 256, 0, s>>>(a, ksplit);
@@ -1192,6 +1249,8 @@ hipError_t run_decode(const AttnArgs& a, hipStream_t s) {
 // 5 / 6 = lean LDS-DMA kernel (as 3 / 4, pages a power of two >= 16 keys) with 1 / 2
 template <int DH, int G>
 hipError_t run_bf16_variant(const AttnArgs& a, int variant, hipStream_t s) {
+  // an FP8 cache goes through the register-staged kernel, which widens it while staging
+  if (a.cache.fp8) return variant % 2 ? run_bf16<DH, G, 1, 0, true>(a, s) : run_bf16<DH, G, 2, 0, true>(a, s);
   if constexpr (DH == 128) {
     const bool dma_ok = a.cache.layer_stride * 2 < (int64_t(1) << 31);
     const bool fa_ok = dma_ok && a.cache.bs_shift >= 4;   // pages of 16 or more keys, a power of two

@@ -214,7 +214,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_packed_kernel(GemvArgs g) {
           const bool isv = e >= d.kvw;
           const int64_t off = static_cast<int64_t>(d.layer) * d.cache.layer_stride +
                               paged_row(d.cache, d.pos) * d.kvw + (isv ? e - d.kvw : e);
-          static_cast<bf16_t*>(isv ? d.cache.v : d.cache.k)[off] = f2bf(v);
+          if (d.cache.fp8) {
+            const float sc = isv ? d.cache.vs : d.cache.ks;
+            static_cast<fp8_t*>(isv ? d.cache.v : d.cache.k)[off] =
+                static_cast<fp8_t>(f32_to_fp8x4(v / sc, 0.f, 0.f, 0.f) & 0xFFu);
+          } else {
+            static_cast<bf16_t*>(isv ? d.cache.v : d.cache.k)[off] = f2bf(v);
+          }
         }
       }
     }

@@ -36,6 +36,30 @@ template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
 
+// OCP FP8 E4M3 bytes <-> fp32 through the gfx950 conversion instructions
+// (nearest even); stores clamp to +-448 first so out-of-range values saturate.
+using fp8_t = uint8_t;
+constexpr float kFp8Max = 448.0f;
+typedef float f32x2_cv __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+  const f32x2_cv a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  const f32x2_cv b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  f[0] = a.x;
+  f[1] = a.y;
+  f[2] = b.x;
+  f[3] = b.y;
+}
+__device__ __forceinline__ float fp8_clamp(float x) { return fminf(fmaxf(x, -kFp8Max), kFp8Max); }
+__device__ __forceinline__ uint32_t f32_to_fp8x4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(a), fp8_clamp(b), 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(c), fp8_clamp(d), v, true);
+  return static_cast<uint32_t>(v);
+}
+// an FP8 value has at most 4 significant bits, so its bf16 pattern is exact
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
 // Reference to a paged cache (see cb_paged_kv).
 struct PagedRef {
   void* k;
@@ -44,6 +68,8 @@ struct PagedRef {
   int32_t bs;          // block size
   int64_t layer_stride;
   int32_t bs_shift;    // log2(bs) when bs is a power of two, else -1
+  int32_t fp8;         // 1: FP8 E4M3 elements scaled by ks / vs
+  float ks, vs;
 };
 
 inline int32_t block_shift(int32_t bs) {
@@ -98,6 +124,8 @@ struct ChunkDesc {
   int32_t block_size;
   int32_t delta;          // new_start - old_start
   int32_t tile_begin;     // first flat tile of this chunk (re-RoPE grid)
+  int32_t fp8;            // 1: FP8 E4M3 source scaled by ks / vs
+  float ks, vs;
   int32_t pad;
 };
 struct ChunkBatch {

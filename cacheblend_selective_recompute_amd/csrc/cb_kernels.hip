@@ -35,6 +35,7 @@ __device__ __forceinline__ void st_stream(void* p, const uint4& v) {
 template <typename T> struct V16;
 template <> struct V16<bf16_t> { static constexpr int N = 8; };
 template <> struct V16<float> { static constexpr int N = 4; };
+template <> struct V16<fp8_t> { static constexpr int N = 16; };
 
 __device__ __forceinline__ void unpack(const uint4& v, float (&f)[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -50,6 +51,45 @@ __device__ __forceinline__ uint4 pack(const float (&f)[8]) {
   for (int i = 0; i < 4; ++i)
     w[i] = static_cast<uint32_t>(f2bf(f[2 * i])) | (static_cast<uint32_t>(f2bf(f[2 * i + 1])) << 16);
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// A 16-byte vector of T as VN fp32 values (FP8 elements times `scale`), and back
+// (FP8: times `inv_scale`, then nearest even, saturating).
+template <typename T>
+__device__ __forceinline__ void unpack_v(const uint4& v, float* f, float scale) {
+  if constexpr (sizeof(T) == 1) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fp8x4_to_f32(w[i], f + 4 * i);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f[i] *= scale;
+  } else if constexpr (sizeof(T) == 2) {
+    float g[8];
+    unpack(v, g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = g[i];
+  } else {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+}
+template <typename T>
+__device__ __forceinline__ uint4 pack_v(const float* f, float inv_scale) {
+  if constexpr (sizeof(T) == 1) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = f32_to_fp8x4(f[4 * i] * inv_scale, f[4 * i + 1] * inv_scale, f[4 * i + 2] * inv_scale,
+                          f[4 * i + 3] * inv_scale);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (sizeof(T) == 2) {
+    float g[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g[i] = f[i];
+    return pack(g);
+  } else {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -109,6 +149,9 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
   T* dk = static_cast<T*>(dst.k) + layer * dst.layer_stride;
   T* dv = static_cast<T*>(dst.v) + layer * dst.layer_stride;
   const float2* tab = dtab + static_cast<int64_t>(c) * (dh / 2);
+  // FP8: source elements times the chunk's scales, stored divided by the destination's
+  const float inv_ks = 1.0f / dst.ks, inv_vs = 1.0f / dst.vs;
+  const bool v_requant = sizeof(T) == 1 && cd.vs != dst.vs;
   // source and destination rows of the tile's tokens, looked up once per block
   __shared__ int64_t srow_s[kTokTile], drow_s[kTokTile];
   if (threadIdx.x < ntok) {
@@ -141,13 +184,8 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (!ok[u]) continue;
-      float f[8];
-      if constexpr (VN == 8) {
-        unpack(kv[u], f);
-      } else {
-        f[0] = __uint_as_float(kv[u].x); f[1] = __uint_as_float(kv[u].y);
-        f[2] = __uint_as_float(kv[u].z); f[3] = __uint_as_float(kv[u].w);
-      }
+      float f[VN];
+      unpack_v<T>(kv[u], f, cd.ks);
 #pragma unroll
       for (int j = 0; j < VN; j += 2) {
         const float2 cs = tab[((e0[u] + j) % dh) >> 1];
@@ -155,14 +193,16 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
         f[j] = x0 * cs.x - x1 * cs.y;
         f[j + 1] = x0 * cs.y + x1 * cs.x;
       }
-      uint4 o;
-      if constexpr (VN == 8) {
-        o = pack(f);
-      } else {
-        o = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+      st_stream(dk + dof[u], pack_v<T>(f, inv_ks));
+      if (copy_v) {
+        uint4 o = vv[u];
+        if (v_requant) {                       // FP8 V under a different scale: re-round on the new grid
+          float g[VN];
+          unpack_v<T>(vv[u], g, cd.vs);
+          o = pack_v<T>(g, inv_vs);
+        }
+        st_stream(dv + dof[u], o);
       }
-      st_stream(dk + dof[u], o);
-      if (copy_v) st_stream(dv + dof[u], vv[u]);
     }
   }
 }
@@ -230,7 +270,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const int3
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float (&f)[8]) {
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 1) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    fp8x4_to_f32(u.x, f);
+    fp8x4_to_f32(u.y, f + 4);
+  } else if constexpr (sizeof(T) == 2) {
     unpack(*reinterpret_cast<const uint4*>(p), f);
   } else {
     const float4 a = *reinterpret_cast<const float4*>(p);
@@ -264,6 +308,15 @@ __global__ __launch_bounds__(256) void deviation_kernel(const float* kf, const f
       load8<T>(ck + e, c0[q]);
       load8<T>(cv + e, c1[q]);
     }
+    if constexpr (sizeof(T) == 1) {          // FP8 cache: element times the tensor's scale
+#pragma unroll
+      for (int q = 0; q < P; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          c0[q][j] *= cache.ks;
+          c1[q][j] *= cache.vs;
+        }
+    }
 #pragma unroll
     for (int q = 0; q < P; ++q)
 #pragma unroll
@@ -277,10 +330,20 @@ __global__ __launch_bounds__(256) void deviation_kernel(const float* kf, const f
       const float4 a = *reinterpret_cast<const float4*>(fk + e);
       const float4 b = *reinterpret_cast<const float4*>(fv + e);
       float c0[4], c1[4];
+      if constexpr (sizeof(T) == 1) {
+        fp8x4_to_f32(*reinterpret_cast<const uint32_t*>(ck + e), c0);
+        fp8x4_to_f32(*reinterpret_cast<const uint32_t*>(cv + e), c1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c0[j] = to_f<T>(ck[e + j]);
-        c1[j] = to_f<T>(cv[e + j]);
+        for (int j = 0; j < 4; ++j) {
+          c0[j] *= cache.ks;
+          c1[j] *= cache.vs;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c0[j] = to_f<T>(ck[e + j]);
+          c1[j] = to_f<T>(cv[e + j]);
+        }
       }
       const float dk0 = a.x - c0[0], dk1 = a.y - c0[1], dk2 = a.z - c0[2], dk3 = a.w - c0[3];
       const float dv0 = b.x - c1[0], dv1 = b.y - c1[1], dv2 = b.z - c1[2], dv3 = b.w - c1[3];
@@ -444,7 +507,21 @@ __global__ __launch_bounds__(256) void scatter_kv_kernel(const float* kvf, int64
                       paged_row(cache, rowpos[row]) * width;
   T* ck = static_cast<T*>(cache.k) + off;
   T* cv = static_cast<T*>(cache.v) + off;
-  if constexpr (W > 0 && sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 1) {
+    // FP8: 8 values per lane and pass, divided by the tensor's scale, one 8-byte store
+    const float ik = 1.0f / cache.ks, iv = 1.0f / cache.vs;
+    for (int e = lane * 8; e < width; e += 512) {
+      float a[8], b[8];
+      load8<float>(f + e, a);
+      load8<float>(f + width + e, b);
+      const uint2 u = make_uint2(f32_to_fp8x4(a[0] * ik, a[1] * ik, a[2] * ik, a[3] * ik),
+                                 f32_to_fp8x4(a[4] * ik, a[5] * ik, a[6] * ik, a[7] * ik));
+      const uint2 w = make_uint2(f32_to_fp8x4(b[0] * iv, b[1] * iv, b[2] * iv, b[3] * iv),
+                                 f32_to_fp8x4(b[4] * iv, b[5] * iv, b[6] * iv, b[7] * iv));
+      *reinterpret_cast<uint2*>(ck + e) = u;
+      *reinterpret_cast<uint2*>(cv + e) = w;
+    }
+  } else if constexpr (W > 0 && sizeof(T) == 2) {
     // 8 consecutive values per lane and pass, every load issued first, 16-byte stores
     constexpr int P = W / 512;
     float a[P][8], b[P][8];
@@ -583,7 +660,9 @@ hipError_t launch_rerope(cb_dtype dt, const ChunkBatch& b, const PagedRef& dst_i
   if (b.total_tiles == 0) return hipSuccess;
   PagedRef dst = dst_in;
   dst.bs_shift = block_shift(dst.bs);
-  if (dt == CB_BF16)
+  if (dst.fp8)
+    rerope_kernel<fp8_t><<<b.total_tiles, kRerope, 0, s>>>(b, dst, dtab, n_layers, width, head_dim, copy_v);
+  else if (dt == CB_BF16)
     rerope_kernel<bf16_t><<<b.total_tiles, kRerope, 0, s>>>(b, dst, dtab, n_layers, width, head_dim, copy_v);
   else
     rerope_kernel<float><<<b.total_tiles, kRerope, 0, s>>>(b, dst, dtab, n_layers, width, head_dim, copy_v);
@@ -622,7 +701,12 @@ hipError_t launch_deviation(cb_dtype dt, const float* kf, const float* vf, int64
   PagedRef cache = cache_in;
   cache.bs_shift = block_shift(cache.bs);
   const bool w1k = width == 1024 && ldf % 4 == 0;   // 8 KV heads x 128: 16-byte aligned rows
-  if (dt == CB_BF16) {
+  if (cache.fp8) {
+    if (w1k)
+      deviation_kernel<fp8_t, 1024><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
+    else
+      deviation_kernel<fp8_t, 0><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
+  } else if (dt == CB_BF16) {
     if (w1k)
       deviation_kernel<bf16_t, 1024><<<cdiv(n, 4), 256, 0, s>>>(kf, vf, ldf, pos, n, cache, layer, width, dev, dev_by_pos);
     else
@@ -663,7 +747,9 @@ hipError_t launch_scatter_kv(cb_dtype dt, const float* kvf, int64_t ldf, const i
   if (n == 0) return hipSuccess;
   PagedRef cache = cache_in;
   cache.bs_shift = block_shift(cache.bs);
-  if (dt == CB_BF16 && width == 1024 && ldf % 4 == 0)
+  if (cache.fp8)
+    scatter_kv_kernel<fp8_t, 0><<<cdiv(n, 4), 256, 0, s>>>(kvf, ldf, gmap, rowpos, n, cache, layer, width);
+  else if (dt == CB_BF16 && width == 1024 && ldf % 4 == 0)
     scatter_kv_kernel<bf16_t, 1024><<<cdiv(n, 4), 256, 0, s>>>(kvf, ldf, gmap, rowpos, n, cache, layer, width);
   else if (dt == CB_BF16)
     scatter_kv_kernel<bf16_t, 0><<<cdiv(n, 4), 256, 0, s>>>(kvf, ldf, gmap, rowpos, n, cache, layer, width);

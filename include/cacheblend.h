@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 5
+#define CB_ABI_VERSION 6
 
 /* A HIP stream (hipStream_t); NULL is the null stream. */
 typedef struct ihipStream_t* cb_stream_t;
@@ -104,9 +104,20 @@ typedef struct {
                                (required for CB_BF16); 0: row-major (CB_F32) */
 } cb_model;
 
+/* KV cache element formats (cb_paged_kv.kv_format, cb_chunk.kv_format).  The
+ * pages run their 34B and 70B models 8-bit and note that an FP8 cache adds
+ * quantisation noise to the deviation ranking ("CacheBlend 完全拆解": sections
+ * 评测条件 and 偏差比较的精度); the 8-bit format here is OCP FP8 E4M3 (1 sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, largest finite 448), one byte
+ * per element, standing for (element value) x (the tensor's scale); storing
+ * rounds to nearest, ties to even, and saturates at +-448.  8-bit caches need
+ * a CB_BF16 model. */
+#define CB_KV_MODEL 0     /* elements in the model dtype */
+#define CB_KV_FP8_E4M3 1  /* one FP8 E4M3 byte per element, scaled by k_scale / v_scale */
+
 /* Paged KV cache: K and V pools laid out [layer][physical block][block_size]
- * [n_kv_heads][head_dim] in the model dtype.  Token at logical position p of
- * layer l lives at element offset
+ * [n_kv_heads][head_dim] in the element format kv_format.  Token at logical
+ * position p of layer l lives at element offset
  *   l * layer_stride + (block_table[p / block_size] * block_size + p % block_size) * Hkv * dh. */
 typedef struct {
   void* k;
@@ -115,6 +126,8 @@ typedef struct {
   int32_t block_size;         /* tokens per block, >= 1                */
   int32_t n_logical;          /* entries in block_table                */
   int64_t layer_stride;       /* elements between layers               */
+  int32_t kv_format;          /* CB_KV_MODEL or CB_KV_FP8_E4M3          */
+  float k_scale, v_scale;     /* CB_KV_FP8_E4M3: value = element x scale (> 0) */
 } cb_paged_kv;
 
 /* One cached chunk: tokens and the KV it was prefilled into at old_start.
@@ -132,6 +145,8 @@ typedef struct {
   int32_t len, old_start, new_start;
   int32_t block_size;       /* paged source only */
   int64_t layer_stride;     /* elements; 0 = contiguous default */
+  int32_t kv_format;        /* as cb_paged_kv; must equal the destination's */
+  float k_scale, v_scale;   /* CB_KV_FP8_E4M3 scales of this chunk's K and V */
 } cb_chunk;
 
 /* Launch kinds, for cb_trace. */

@@ -55,8 +55,8 @@ int main(void) {
   P(cb_model_cfg) O(cb_model_cfg, rope_theta) O(cb_model_cfg, rms_eps) O(cb_model_cfg, dtype)
   P(cb_layer_w) O(cb_layer_w, mlp_norm)
   P(cb_model) O(cb_model, embed) O(cb_model, layers) O(cb_model, weights_packed)
-  P(cb_paged_kv) O(cb_paged_kv, block_size) O(cb_paged_kv, layer_stride)
-  P(cb_chunk) O(cb_chunk, len) O(cb_chunk, new_start) O(cb_chunk, layer_stride)
+  P(cb_paged_kv) O(cb_paged_kv, block_size) O(cb_paged_kv, layer_stride) O(cb_paged_kv, kv_format) O(cb_paged_kv, v_scale)
+  P(cb_chunk) O(cb_chunk, len) O(cb_chunk, new_start) O(cb_chunk, layer_stride) O(cb_chunk, kv_format) O(cb_chunk, v_scale)
   P(cb_blend_params) O(cb_blend_params, flags) O(cb_blend_params, trace)
   P(cb_trace) O(cb_trace, used) O(cb_trace, kinds)
   P(cb_host_chunk) O(cb_host_chunk, v) O(cb_host_chunk, len) O(cb_host_chunk, new_start)
@@ -82,7 +82,7 @@ int main(void) {
 
 
 def test_status_strings_and_version(lib):
-    assert lib.cb_abi_version() == 5
+    assert lib.cb_abi_version() == 6
     for code, name in [(0, "CB_OK"), (-1, "CB_ERR_INVALID"), (-2, "CB_ERR_UNSUPPORTED"),
                        (-3, "CB_ERR_WORKSPACE"), (-4, "CB_ERR_DEVICE")]:
         assert lib.cb_status_string(code).decode() == name
@@ -189,6 +189,25 @@ def test_prefill_rejects_bad_shapes(lib):
     assert st == _abi.CB_ERR_INVALID and "n_layers" in msg
     st, msg = _prefill(lib, cfg=cfg8b(n_layers=3, head_dim=96, n_q_heads=32))
     assert st == _abi.CB_ERR_UNSUPPORTED
+
+
+def test_prefill_rejects_bad_8bit_cache(lib):
+    # every case fails validation (nothing is launched)
+    fp8 = _paged(136)
+    fp8.kv_format, fp8.k_scale, fp8.v_scale = _abi.CB_KV_FP8_E4M3, 0.0, 1.0
+    st, msg = _prefill(lib, paged=fp8)
+    assert st == _abi.CB_ERR_INVALID and "scales" in msg
+    fp8.k_scale = 1.0
+    st, msg = _prefill(lib, paged=fp8)                        # chunks in the model dtype
+    assert st == _abi.CB_ERR_UNSUPPORTED and "differs" in msg
+    c32 = cfg8b(n_layers=3)
+    c32.dtype = _abi.CB_F32
+    st, msg = _prefill(lib, cfg=c32, paged=fp8)
+    assert st == _abi.CB_ERR_UNSUPPORTED and "CB_BF16" in msg
+    bad = _paged(136)
+    bad.kv_format = 7
+    st, msg = _prefill(lib, paged=bad)
+    assert st == _abi.CB_ERR_INVALID and "kv_format" in msg
 
 
 def test_prefill_rejects_short_block_table_small_workspace_and_empty_query(lib):

@@ -49,6 +49,8 @@ def parse():
                     help="decode steps timed on the blended cache after the runs (0: skip)")
     ap.add_argument("--streamed-runs", type=int, default=3,
                     help="runs of the layer-pipelined prefill from host memory (0: skip)")
+    ap.add_argument("--fp8-runs", type=int, default=5,
+                    help="timed runs of the same prefill over an 8-bit (FP8) KV cache (0: skip)")
     ap.add_argument("--match-runs", type=int, default=20,
                     help="timed runs of fragment matching on a 64-request batch (0: skip)")
     ap.add_argument("--sweep", action="store_true",
@@ -371,6 +373,35 @@ def decode_runs(torch, api, model, shape, blended, logits, T, steps):
             "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def fp8_runs(torch, api, model, shape, chunks, qtok, params, T, N, runs):
+    """The same blended prefill with 8-bit (FP8 E4M3) chunk caches and blended
+    cache: one K and one V scale, max |value| / 448 over the chunk caches."""
+    import numpy as np
+    ks = max(float(c.k.float().abs().max()) for c in chunks) / 448.0
+    vs = max(float(c.v.float().abs().max()) for c in chunks) / 448.0
+    f8 = [api.ChunkSource(c.tokens, api.fp8_encode(c.k, ks), api.fp8_encode(c.v, vs), c.old_start, c.new_start,
+                          block_ids=c.block_ids, block_size=c.block_size, layer_stride=c.layer_stride,
+                          kv_format=api.CB_KV_FP8_E4M3, k_scale=ks, v_scale=vs) for c in chunks]
+    kv = api.PagedKV(shape, T, 16, kv_format=api.CB_KV_FP8_E4M3, k_scale=ks, v_scale=vs)
+    logits = torch.empty(shape.vocab, device="cuda")
+    ws = api.Workspace(api.cb_workspace_bytes(model.cfg, N, int(qtok.numel()), len(f8)))
+    arr = api._chunk_array(f8)
+    for _ in range(2):
+        api.cb_blend_prefill(model, f8, qtok, params, kv, logits, None, None, ws, _arr=arr)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(runs):
+        api.cb_blend_prefill(model, f8, qtok, params, kv, logits, None, None, ws, _arr=arr)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / runs
+    kv_bytes = sum(2 * c.k.numel() for c in f8)
+    return {"ms_per_step": round(ms, 4), "context_tokens_per_s": round(N / (ms * 1e-3), 1),
+            "chunk_kv_bytes": kv_bytes, "k_scale": ks, "v_scale": vs, "runs": runs,
+            "logits_finite": bool(torch.isfinite(logits).all())}
+
+
 def streamed_runs(torch, api, model, chunks, qtok, params, blended, logits, hkvd, N, runs):
     """The layer-pipelined prefill with the chunk caches in page-locked host
     memory: per-run time (host -> device copies included), the time a plain copy
@@ -557,6 +588,8 @@ def main():
     peaks = measured_peaks(torch, dev) if args.peaks else None
     decode = decode_runs(torch, api, model, shape, blended, logits, T, args.decode_steps) if args.decode_steps else None
     match = match_runs(torch, api, args.seed, args.match_runs) if args.match_runs > 0 else None
+    fp8 = fp8_runs(torch, api, model, shape, chunks, qtok, plain, T, N, args.fp8_runs) \
+        if args.fp8_runs > 0 and shape.dtype == "bf16" else None
     streamed = None
     if args.streamed_runs > 0 and not wl.paged:
         streamed = streamed_runs(torch, api, model, chunks, qtok, plain, blended, logits, hkvd, N, args.streamed_runs)
@@ -603,6 +636,7 @@ def main():
         "streamed": streamed,
         "decode": decode,
         "match": match,
+        "fp8_kv": fp8,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

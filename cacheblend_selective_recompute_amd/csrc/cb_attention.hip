@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_bf16_kernel(AttnArg
     l_tot += __shfl_xor(l_tot, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
     if (!qvalid[g]) continue;
-    if (n_splits == 1) {
+    if (n_splits == 1 || kv_end <= ksplit) {   // the tile's keys lie in split 0: final output
       const float inv = (F8 ? a.cache.vs : 1.0f) / l_tot;
       bf16_t* ob = static_cast<bf16_t*>(a.o);
       const int KO = a.n_q_heads * DH;
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_dma_kernel(AttnArgs
     l_tot += __shfl_xor(l_tot, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
     if (!qvalid[g]) continue;
-    if (n_splits == 1) {
+    if (n_splits == 1 || kv_end <= ksplit) {   // the tile's keys lie in split 0: final output
       const float inv = 1.0f / l_tot;
       bf16_t* ob = static_cast<bf16_t*>(a.o);
       const int KO = a.n_q_heads * DH;
@@ -812,7 +812,7 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs 
   for (int g = 0; g < NG; ++g) {
     if (!qvalid[g]) continue;
     const float l_tot = lsum[g][0];
-    if (n_splits == 1) {
+    if (n_splits == 1 || kv_end <= ksplit) {   // the tile's keys lie in split 0: final output
       const float inv = 1.0f / l_tot;
       bf16_t* ob = static_cast<bf16_t*>(a.o);
       const int KO = a.n_q_heads * DH;
@@ -849,6 +849,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_spl
   const int t_last = min((row / QT + 1) * QT, a.R) - 1;
   const int kv_end = a.rowpos[t_last] + 1;
   const int ns = min(n_splits, (kv_end + ksplit - 1) / ksplit);
+  if (ns <= 1) return;                                   // written whole by the attention kernel
   auto prow = [&](int sp) { return (static_cast<int64_t>(sp) * a.R + row) * a.n_q_heads + head; };
   float M = -INFINITY;
   for (int s0 = 0; s0 < ns; s0 += 64)

@@ -196,17 +196,31 @@ __global__ __launch_bounds__(Tile<CFG>::kThreads, Tile<CFG>::WGS_PER_CU) void ge
   // one stage: t in slot `slot`.  Copies of stage s go out during the second half of
   // stage s-NS and the first half of stage s-NS+1 (slot s % NS), i.e. after every wave
   // has read stage s-NS (its reads all precede the barrier in the middle of s-NS).
+  // A wave whose 64-row slice lies wholly past the last row (the padding of a ragged
+  // last row tile) only makes its share of the copies and leaves the matrix cores
+  // to the other waves of its SIMD.
+  const bool active = m0 + wm * (FM * 32) < g.M;
   auto stage = [&](int kt, int slot) __attribute__((always_inline)) {
-    frag(slot, 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(0, kt + NS - 1, (slot + NS - 1) % NS, H0, H1);
-    __builtin_amdgcn_sched_barrier(0);
+    if (active) {
+      frag(slot, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(0, kt + NS - 1, (slot + NS - 1) % NS, H0, H1);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int c = 0; c < H1; ++c) copy(kt + NS - 1, (slot + NS - 1) % NS, H0 + c);
+    }
     CB_WAIT_VM(DQ * (NS - 2));     // this wave's copies of stage kt+1 have landed
     __syncthreads();               // ... everyone's
-    frag((slot + 1) % NS, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(1, kt + NS, slot, 0, H0);
-    __builtin_amdgcn_sched_barrier(0);
+    if (active) {
+      frag((slot + 1) % NS, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(1, kt + NS, slot, 0, H0);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int c = 0; c < H0; ++c) copy(kt + NS, slot, c);
+    }
   };
 
   // prologue: stages 0 .. NS-2 and the first half of stage NS-1 in flight

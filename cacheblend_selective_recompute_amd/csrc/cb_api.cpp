@@ -425,6 +425,10 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   at.kv_bound = N + Q;
   at.part_o = w.attn_o;
   at.part_ml = w.attn_ml;
+  // the fresh K/V rows are in the cache by now, so their buffer holds the bf16
+  // copy of an FP8 layer
+  at.widen = w.kvf;
+  at.widen_bytes = (int64_t)(N + Q) * 2 * kvw * 4;
   CB_LAUNCH(tr, CB_KIND_ATTENTION, launch_attention(c.dtype, at, s), "attention");
 
   // O projection + residual (rows gathered from x_in), then the MLP
@@ -488,6 +492,10 @@ cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, fl
   at.kv_bound = N + Q;
   at.part_o = w.attn_o;
   at.part_ml = w.attn_ml;
+  // the fresh K/V rows are in the cache by now, so their buffer holds the bf16
+  // copy of an FP8 layer
+  at.widen = w.kvf;
+  at.widen_bytes = (int64_t)(N + Q) * 2 * kvw * 4;
   CB_LAUNCH(tr, CB_KIND_ATTENTION, launch_attention(c.dtype, at, s), "attention");
   g = GemmArgs{};
   g.A = w.o; g.lda = qw; g.B = lw.w_o; g.ldb = qw; g.M = T; g.N = d; g.K = qw;

@@ -582,7 +582,10 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_dma_kernel(AttnArgs
 //  * the 16 keys a wave copies share a page, so one block-table entry per wave
 //    and block gives every copy address, and that entry is fetched a block ahead.
 // ---------------------------------------------------------------------------
-template <int G, int NG>
+// CONTIG: the keys are one contiguous bf16 run per layer (the widened copy of an
+// FP8 layer, see kv_widen_fp8_kernel); the V scale of that cache then multiplies
+// the output.
+template <int G, int NG, bool CONTIG = false>
 __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs a, int n_splits, int ksplit) {
   constexpr int DH = 128;
   constexpr int QROWS = 64 * NG;
@@ -671,13 +674,14 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs 
       wid * 4096);
   const int pmask = (1 << sh) - 1;
   auto page_of = [&](int jb) -> int {   // block-table entry of this wave's 16 keys of block jb
+    if constexpr (CONTIG) return 0;
     const int k0 = jb + 16 * wid;
     return k0 < j_end ? a.cache.bt[k0 >> sh] : 0;
   };
   int pe = page_of(j_begin);
   auto issue = [&](int jb, int stage) {
     const int k0 = jb + 16 * wid;
-    const int rowb = ((pe << sh) + (k0 & pmask)) * width * 2 + kvh * DH * 2;
+    const int rowb = (CONTIG ? k0 : (pe << sh) + (k0 & pmask)) * width * 2 + kvh * DH * 2;
     pe = page_of(jb + KVB);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -813,7 +817,7 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs 
     if (!qvalid[g]) continue;
     const float l_tot = lsum[g][0];
     if (n_splits == 1 || kv_end <= ksplit) {   // the tile's keys lie in split 0: final output
-      const float inv = 1.0f / l_tot;
+      const float inv = (CONTIG ? a.cache.vs : 1.0f) / l_tot;
       bf16_t* ob = static_cast<bf16_t*>(a.o);
       const int KO = a.n_q_heads * DH;
 #pragma unroll
@@ -826,12 +830,47 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs 
     } else {
       const int64_t pr = (static_cast<int64_t>(split) * a.R + qtok[g]) * a.n_q_heads + qhead[g];
       float* op = a.part_o + pr * DH;
+      const float vs = CONTIG ? a.cache.vs : 1.0f;
 #pragma unroll
       for (int dt = 0; dt < DH / 16; ++dt)
-        *reinterpret_cast<float4*>(op + 16 * dt + 4 * kgrp) = make_float4(o[g][dt][0], o[g][dt][1], o[g][dt][2], o[g][dt][3]);
+        *reinterpret_cast<float4*>(op + 16 * dt + 4 * kgrp) =
+            make_float4(o[g][dt][0] * vs, o[g][dt][1] * vs, o[g][dt][2] * vs, o[g][dt][3] * vs);
       if (kgrp == 0) a.part_ml[pr] = make_float2(m_run[g], l_tot);
     }
   }
+}
+
+// Widening of one layer of an FP8 paged cache into contiguous bf16 K and V runs
+// (positions [0, rows), unscaled: every E4M3 value is exact in bf16), so the
+// LDS-staged attention kernel reads it like a bf16 layer; the K scale then goes
+// into the softmax scale and the V scale into the output.  One thread widens
+// 16 bytes of K and of V.
+__global__ __launch_bounds__(256) void kv_widen_fp8_kernel(PagedRef c, int layer, int rows, int width, bf16_t* ko,
+                                                          bf16_t* vo) {
+  const int per_row = width >> 4;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(rows) * per_row) return;
+  const int pos = static_cast<int>(i / per_row);
+  const int e = static_cast<int>(i % per_row) * 16;
+  const int64_t src = static_cast<int64_t>(layer) * c.layer_stride + paged_row(c, pos) * width + e;
+  const uint4 kw = *reinterpret_cast<const uint4*>(static_cast<const fp8_t*>(c.k) + src);
+  const uint4 vw = *reinterpret_cast<const uint4*>(static_cast<const fp8_t*>(c.v) + src);
+  auto widen = [](uint4 w, bf16_t* dst) {
+    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+    uint32_t out[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float f[4];
+      fp8x4_to_f32(in[q], f);
+      out[2 * q] = fp8x2_to_bf16x2(f[0], f[1]);
+      out[2 * q + 1] = fp8x2_to_bf16x2(f[2], f[3]);
+    }
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  };
+  const int64_t dst = static_cast<int64_t>(pos) * width + e;
+  widen(kw, ko + dst);
+  widen(vw, vo + dst);
 }
 
 // Merge the split-KV partials of one (row, q head) per wave.  The lanes take
@@ -946,7 +985,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int DH, int G, int NG, int KIND, bool F8 = false>   // KIND 0 register-staged, 1 LDS-DMA, 2 lean LDS-DMA
+// KIND 0 register-staged, 1 LDS-DMA, 2 lean LDS-DMA; CONTIG (KIND 2): keys in one contiguous run
+template <int DH, int G, int NG, int KIND, bool F8 = false, bool CONTIG = false>
 hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   constexpr int QT = 64 * NG / G;
   const int n_tiles = (a.R + QT - 1) / QT;
@@ -968,7 +1008,7 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   const int ksplit = ((kv_blocks + n_splits - 1) / n_splits) * KVB;
   const dim3 grid(n_tiles * n_splits, a.n_kv_heads);
   if constexpr (KIND == 2) {
-    attn_fa_kernel<G, NG><<<dim3(n_tiles * n_splits * a.n_kv_heads), 256, 0, s>>>(a, n_splits, ksplit);
+    attn_fa_kernel<G, NG, CONTIG><<<dim3(n_tiles * n_splits * a.n_kv_heads), 256, 0, s>>>(a, n_splits, ksplit);
   } else if (KIND == 1) {
     // workgroups stage the table entries of their key range in LDS when they fit
     if (ksplit / a.cache.bs + 2 <= 1024)
@@ -1250,8 +1290,28 @@ hipError_t run_decode(const AttnArgs& a, hipStream_t s) {
 // 5 / 6 = lean LDS-DMA kernel (as 3 / 4, pages a power of two >= 16 keys) with 1 / 2
 template <int DH, int G>
 hipError_t run_bf16_variant(const AttnArgs& a, int variant, hipStream_t s) {
-  // an FP8 cache goes through the register-staged kernel, which widens it while staging
-  if (a.cache.fp8) return variant % 2 ? run_bf16<DH, G, 1, 0, true>(a, s) : run_bf16<DH, G, 2, 0, true>(a, s);
+  if (a.cache.fp8) {
+    // an FP8 layer is widened into the caller's bf16 buffer when it fits there, then
+    // read by the lean LDS-DMA kernel; otherwise the register-staged kernel widens it
+    // while staging
+    const int width = a.n_kv_heads * DH;
+    const int64_t run = (static_cast<int64_t>(a.kv_bound) * width * 2 + 255) & ~int64_t(255);
+    if constexpr (DH == 128) {
+      if (variant >= 5 && a.widen != nullptr && 2 * run <= a.widen_bytes && run < (int64_t(1) << 31) && a.kv_bound > 0) {
+        AttnArgs b = a;
+        bf16_t* kw = static_cast<bf16_t*>(a.widen);
+        bf16_t* vw = reinterpret_cast<bf16_t*>(static_cast<char*>(a.widen) + run);
+        const int64_t threads = static_cast<int64_t>(a.kv_bound) * (width / 16);
+        kv_widen_fp8_kernel<<<static_cast<unsigned>((threads + 255) / 256), 256, 0, s>>>(a.cache, a.layer, a.kv_bound,
+                                                                                          width, kw, vw);
+        b.cache = PagedRef{kw, vw, nullptr, 1, 0, 0, 0, 1.f, a.cache.vs};
+        b.layer = 0;
+        b.scale = a.scale * a.cache.ks;
+        return variant == 5 ? run_bf16<DH, G, 1, 2, false, true>(b, s) : run_bf16<DH, G, 2, 2, false, true>(b, s);
+      }
+    }
+    return variant % 2 ? run_bf16<DH, G, 1, 0, true>(a, s) : run_bf16<DH, G, 2, 0, true>(a, s);
+  }
   if constexpr (DH == 128) {
     const bool dma_ok = a.cache.layer_stride * 2 < (int64_t(1) << 31);
     const bool fa_ok = dma_ok && a.cache.bs_shift >= 4;   // pages of 16 or more keys, a power of two

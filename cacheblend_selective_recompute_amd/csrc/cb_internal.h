@@ -275,6 +275,8 @@ struct AttnArgs {
   float* part_o;           // split-KV partials, attn_partial_floats(head_dim) floats
   float2* part_ml;         // split-KV (max, sum) pairs, attn_partial_rows() entries
   int n_splits_req;        // key splits to use; 0 = chosen by the launcher
+  void* widen;             // nullable: room for a bf16 copy of one FP8 layer's K and V
+  int64_t widen_bytes;     //   (2 x kv_bound x width x 2 bytes, each run 256-byte aligned)
 };
 hipError_t launch_attention(cb_dtype dt, const AttnArgs& a, hipStream_t s);
 // with an explicit kernel variant: 1 / 2 register-staged K/V with 1 / 2 query groups

@@ -43,7 +43,7 @@ def test_rope_equals_complex_multiplication():
 
 
 def test_rerope_inverse_identity():
-    # re-RoPE by delta then -delta is the identity (spec: within 1e-6)
+    # re-RoPE by delta then -delta is the identity within 1e-6
     rng = np.random.default_rng(1)
     k = rng.standard_normal((3, 50, 2, 64))
     for delta in (1, 255, 4096, 31000):

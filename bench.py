@@ -109,10 +109,14 @@ def traffic_from_profile(kind, workload):
         return None
 
 
-def work_per_kind(shape, N, Q, ks, sets, chunk_lens):
+def work_per_kind(shape, N, Q, ks, sets, chunk_lens, fused_keep_all=False):
     """Algorithmic FLOPs (MFMA kinds) or HBM bytes (the others) of one step.
 
-    sets[l]: positions kept at layer l (ascending), for the attention count."""
+    sets[l]: positions kept at layer l (ascending), for the attention count.
+    fused_keep_all: the layers that keep every candidate took their deviations and
+    wrote their fresh K/V inside the Q/K/V product's split-K reduction (no
+    deviation or scatter launch of their own), so those bytes are not counted
+    under the deviation and scatter kinds."""
     d, F = shape.d_model, shape.d_ff
     qw, kvw = shape.q_width, shape.kv_width
     es = 2 if shape.dtype == "bf16" else 4
@@ -137,9 +141,11 @@ def work_per_kind(shape, N, Q, ks, sets, chunk_lens):
         w["gemm_down"] += 2.0 * (k + Q) * F * d
         vis = float(sum(int(p) + 1 for p in sets[l])) + sum(N + i + 1 for i in range(Q))
         w["attention"] += 4.0 * shape.head_dim * shape.n_q_heads * vis
-        w["deviation"] += nc * (kvw * (2 * 4 + 2 * es) + 4 + 4)
+        fused = fused_keep_all and k == nc
+        if not fused:
+            w["deviation"] += nc * (kvw * (2 * 4 + 2 * es) + 4 + 4)
+            w["scatter"] += (k + Q) * kvw * (2 * 4 + 2 * es)
         w["select"] += nc * 8 + k * 8
-        w["scatter"] += (k + Q) * kvw * (2 * 4 + 2 * es)
         if k != nc:
             w["norm"] += (k + Q) * d * (4 + es)     # the kept rows' queries, normalised apart
         nc = k
@@ -527,13 +533,17 @@ def main():
     run(p_all)
     torch.cuda.synchronize()
     sets = {l: hkvd[l, :ks[l]].cpu().numpy() for l in range(1, shape.n_layers)}
-    work = work_per_kind(shape, N, Q, ks, sets, wl.chunk_lens)
     kind_ms = {}
     kind_n = {}
     for i in range(tr_all.used // 2):
         k = _abi.KINDS[kinds_all[i]]
         kind_ms[k] = kind_ms.get(k, 0.0) + hip.elapsed_ms(ev_all[2 * i], ev_all[2 * i + 1])
         kind_n[k] = kind_n.get(k, 0) + 1
+    # one scatter launch per layer, except the layers that keep every candidate when
+    # their Q/K/V reduction wrote the cache
+    keep_all = sum(1 for l in range(1, shape.n_layers) if ks[l] == (N if l == 1 else ks[l - 1]))
+    fused_keep_all = keep_all > 0 and kind_n.get("scatter", 0) == shape.n_layers - keep_all
+    work = work_per_kind(shape, N, Q, ks, sets, wl.chunk_lens, fused_keep_all)
     dominant = max((k for k in kind_ms if k in work), key=lambda k: kind_ms[k])
     dom_id = _abi.KINDS.index(dominant)
 
@@ -630,6 +640,9 @@ def main():
                    "paged": bool(wl.paged), "block_size": 16},
         "roofline": roof,
         "kernels_ms_per_step": breakdown,
+        "deviation_scatter_in_qkv_reduce": {"layers": keep_all if fused_keep_all else 0,
+                                             "note": "layers keeping every candidate take their deviations and write "
+                                                     "their fresh K/V in the Q/K/V split-K reduction (gemm_qkv)"},
         "cold_ms_per_step": ({"median": round(float(np.median(cold)), 4), "min": round(min(cold), 4), "runs": len(cold)}
                              if cold else None),
         "measured_peaks": peaks,

@@ -366,12 +366,21 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   g.head_dim = c.head_dim; g.rope_tab = w.pos_tab; g.row_pos = io.rowpos_in;
   g.part = w.gemm_part;
   g.part_floats = kGemmPartFloats;
+  // with every candidate kept, a split-K reduction of that GEMM also takes the
+  // deviations and writes the fresh K/V rows into the cache
+  bool blend_done = false;
   if (fused_qkv) {
     g.B = lw.w_qkv; g.ldb = d;
     g.N = qw + 2 * kvw;
     g.C = w.q; g.ldc = qw; g.q_cols = qw;
     g.C2 = w.kvf; g.ldc2 = 2 * kvw; g.rope2_cols = kvw;
-    CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_QKV, g, s), "qkv gemm");
+    g.blend = 1;
+    g.blend_layer = l;
+    g.blend_cache = kv;
+    g.blend_nc = check ? nc : 0;
+    g.blend_dev = io.dev_slot ? io.dev_slot : w.dev;
+    g.blend_dev_by_pos = io.dev_by_pos;
+    CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_QKV, g, s, &blend_done), "qkv gemm");
   } else {
     g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * es; g.ldb = d;
     g.N = 2 * kvw;
@@ -385,7 +394,8 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   int32_t* copy_out = io.pos_out;
   if (check) {
     float* dev = io.dev_slot ? io.dev_slot : w.dev;
-    CB_LAUNCH(tr, CB_KIND_DEVIATION, launch_deviation(c.dtype, w.kvf, w.kvf + kvw, 2 * kvw, io.cand_pos, nc, kv, l, kvw, dev, io.dev_by_pos, s), "deviation");
+    if (!blend_done)
+      CB_LAUNCH(tr, CB_KIND_DEVIATION, launch_deviation(c.dtype, w.kvf, w.kvf + kvw, 2 * kvw, io.cand_pos, nc, kv, l, kvw, dev, io.dev_by_pos, s), "deviation");
     // the top-k also writes the row maps of the kept rows and the suffix
     CB_LAUNCH(tr, CB_KIND_SELECT, launch_select_rows(dev, io.cand_pos, nc, k, io.pos_out, w.slot, N, Q, w.gmap,
                                                      io.rowpos_out, io.hkvd_row, s), "select");
@@ -396,7 +406,8 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   }
 
   // fill: fresh K/V of the kept rows and of the suffix replace the cache
-  CB_LAUNCH(tr, CB_KIND_SCATTER, launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, w.gmap, io.rowpos_out, rout, kv, l, kvw, s), "scatter");
+  if (!blend_done)
+    CB_LAUNCH(tr, CB_KIND_SCATTER, launch_scatter_kv(c.dtype, w.kvf, 2 * kvw, w.gmap, io.rowpos_out, rout, kv, l, kvw, s), "scatter");
 
   // queries of the kept rows: when the set shrank, normalise the kept rows into
   // their own (fragment-major) buffer

@@ -442,6 +442,105 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int spli
   }
 }
 
+// Split-K reduction of the fused Q/K/V product of a layer that keeps all of its
+// candidate rows, with the blend's per-row work folded in (GemmArgs::blend): one
+// workgroup per row sums the partials in split order, rotates Q and K at the
+// row's position, stores Q (bf16), and for the K/V columns reads the cached row,
+// adds the squared differences (candidate rows only; per thread in column
+// order, then across the workgroup in a fixed order) and writes the fresh
+// values over it (bf16, or FP8 divided by the tensor's scale).  T: the cache's
+// element type.
+template <typename T, int SP>
+__global__ __launch_bounds__(256) void qkv_reduce_blend_kernel(GemmArgs g, int splits) {
+  if constexpr (SP > 0) splits = SP;
+  __shared__ float red[4];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int kvw = g.rope2_cols;
+  const int wpart = g.q_cols + 2 * kvw;
+  const int n4 = wpart >> 2;
+  const int pos = g.row_pos[row];
+  const int half = g.head_dim >> 1;
+  const PagedRef& c = g.blend_cache;
+  const int64_t off = static_cast<int64_t>(g.blend_layer) * c.layer_stride + paged_row(c, pos) * kvw;
+  const bool cand = row < g.blend_nc;
+  float acc = 0.f;
+  for (int j = tid; j < n4; j += 256) {
+    const int col = j * 4;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int sp = 0; sp < splits; ++sp) {
+      const float4 pv = *reinterpret_cast<const float4*>(g.part + (static_cast<int64_t>(sp) * g.M + row) * wpart + col);
+      sum.x += pv.x; sum.y += pv.y; sum.z += pv.z; sum.w += pv.w;
+    }
+    float v[4] = {sum.x, sum.y, sum.z, sum.w};
+    const bool isq = col < g.q_cols;
+    const int c2 = isq ? col : col - g.q_cols;
+    if (isq || c2 < kvw) {
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        const float2 cs = g.rope_tab[static_cast<int64_t>(pos) * half + (((c2 + e) % g.head_dim) >> 1)];
+        const float x0 = v[e], x1 = v[e + 1];
+        v[e] = x0 * cs.x - x1 * cs.y;
+        v[e + 1] = x0 * cs.y + x1 * cs.x;
+      }
+    }
+    if (isq) {
+      uint2 w;
+      w.x = static_cast<uint32_t>(f2bf(v[0])) | (static_cast<uint32_t>(f2bf(v[1])) << 16);
+      w.y = static_cast<uint32_t>(f2bf(v[2])) | (static_cast<uint32_t>(f2bf(v[3])) << 16);
+      *reinterpret_cast<uint2*>(static_cast<bf16_t*>(g.C) + static_cast<int64_t>(row) * g.ldc + c2) = w;
+      continue;
+    }
+    const bool isk = c2 < kvw;
+    const int e0 = isk ? c2 : c2 - kvw;
+    T* dst = static_cast<T*>(isk ? c.k : c.v) + off + e0;
+    const float sc = isk ? c.ks : c.vs;
+    if constexpr (sizeof(T) == 1) {
+      if (cand) {
+        float f[4];
+        fp8x4_to_f32(*reinterpret_cast<const uint32_t*>(dst), f);
+        const float d0 = v[0] - f[0] * sc, d1 = v[1] - f[1] * sc, d2 = v[2] - f[2] * sc, d3 = v[3] - f[3] * sc;
+        acc += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+      }
+      const float is = 1.0f / sc;
+      *reinterpret_cast<uint32_t*>(dst) = f32_to_fp8x4(v[0] * is, v[1] * is, v[2] * is, v[3] * is);
+    } else {
+      if (cand) {
+        const uint2 o = *reinterpret_cast<const uint2*>(dst);
+        const float d0 = v[0] - bf2f(static_cast<bf16_t>(o.x & 0xFFFFu)), d1 = v[1] - bf2f(static_cast<bf16_t>(o.x >> 16));
+        const float d2 = v[2] - bf2f(static_cast<bf16_t>(o.y & 0xFFFFu)), d3 = v[3] - bf2f(static_cast<bf16_t>(o.y >> 16));
+        acc += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+      }
+      uint2 w;
+      w.x = static_cast<uint32_t>(f2bf(v[0])) | (static_cast<uint32_t>(f2bf(v[1])) << 16);
+      w.y = static_cast<uint32_t>(f2bf(v[2])) | (static_cast<uint32_t>(f2bf(v[3])) << 16);
+      *reinterpret_cast<uint2*>(dst) = w;
+    }
+  }
+  if (!cand) return;                                  // uniform over the workgroup
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    const float d = ((red[0] + red[1]) + red[2]) + red[3];
+    g.blend_dev[row] = d;
+    if (g.blend_dev_by_pos) g.blend_dev_by_pos[pos] = d;
+  }
+}
+
+template <typename T>
+hipError_t launch_qkv_reduce_blend(const GemmArgs& a, int eff, hipStream_t s) {
+  switch (eff) {
+    case 2: qkv_reduce_blend_kernel<T, 2><<<a.M, 256, 0, s>>>(a, eff); break;
+    case 3: qkv_reduce_blend_kernel<T, 3><<<a.M, 256, 0, s>>>(a, eff); break;
+    case 4: qkv_reduce_blend_kernel<T, 4><<<a.M, 256, 0, s>>>(a, eff); break;
+    default: qkv_reduce_blend_kernel<T, 0><<<a.M, 256, 0, s>>>(a, eff); break;
+  }
+  return hipGetLastError();
+}
+
 // Split-K reduction of a residual GEMM fused with the RMSNorm that follows it:
 // one workgroup per row; x = resid + (partials summed in split order) is
 // written fp32, then normalised (same reduction order as the RMSNorm kernel)
@@ -787,7 +886,8 @@ void choose_gemm_cfg(const GemmArgs& a, int epi, int* cfg, int* splits, int* dp_
 
 namespace {
 
-// *normed: set when the RMSNorm of a residual GEMM's output was fused into the reduction
+// *normed: set when the RMSNorm of a residual GEMM's output, or the blend work of a
+// Q/K/V product (GemmArgs::blend), was fused into the reduction
 template <int EPI, int CFG>
 hipError_t run_bm(const GemmArgs& a, int splits, int dp_cols, hipStream_t s, bool* normed) {
   constexpr int BM = Tile<CFG>::BM;
@@ -802,6 +902,10 @@ hipError_t run_bm(const GemmArgs& a, int splits, int dp_cols, hipStream_t s, boo
     const int c_part = dp_cols * BN;
     if (EPI == EPI_RESID && a.norm_out != nullptr && a.N <= kNormChunks * 1024) {
       e = launch_reduce_norm(a, eff, c_part, s);
+      if (e != hipSuccess) return e;
+      *normed = true;
+    } else if (EPI == EPI_QKV && a.blend && c_part == 0) {
+      e = a.blend_cache.fp8 ? launch_qkv_reduce_blend<fp8_t>(a, eff, s) : launch_qkv_reduce_blend<bf16_t>(a, eff, s);
       if (e != hipSuccess) return e;
       *normed = true;
     } else {
@@ -831,7 +935,7 @@ hipError_t run_cfg(const GemmArgs& a, int cfg, int splits, int dp_cols, hipStrea
 }
 
 template <int EPI>
-hipError_t run_gemm(cb_dtype dt, const GemmArgs& a, hipStream_t s) {
+hipError_t run_gemm(cb_dtype dt, const GemmArgs& a, hipStream_t s, bool* blend_done) {
   if (a.M == 0 || a.N == 0) return hipSuccess;
   bool normed = false;
   hipError_t e;
@@ -846,6 +950,7 @@ hipError_t run_gemm(cb_dtype dt, const GemmArgs& a, hipStream_t s) {
     choose_gemm_cfg(a, EPI, &cfg, &splits, &dp_cols);
     e = run_cfg<EPI>(a, cfg, splits, dp_cols, s, &normed);
   }
+  if (EPI == EPI_QKV && blend_done) *blend_done = e == hipSuccess && normed;
   if (e != hipSuccess || EPI != EPI_RESID || a.norm_out == nullptr || normed) return e;
   return launch_rmsnorm(dt, static_cast<const float*>(a.C), nullptr, a.ldc, a.M, a.N, a.norm_gain, a.norm_eps, a.norm_out,
                         a.N, 0, s);
@@ -865,13 +970,14 @@ hipError_t launch_gemm_cfg(GemmEpi epi, const GemmArgs& a, int cfg, int splits, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s, bool* blend_done) {
+  if (blend_done) *blend_done = false;
   switch (epi) {
-    case EPI_STORE_ROPE: return run_gemm<EPI_STORE_ROPE>(dt, a, s);
-    case EPI_F32_ROPE: return run_gemm<EPI_F32_ROPE>(dt, a, s);
-    case EPI_RESID: return run_gemm<EPI_RESID>(dt, a, s);
-    case EPI_SWIGLU: return run_gemm<EPI_SWIGLU>(dt, a, s);
-    case EPI_QKV: return run_gemm<EPI_QKV>(dt, a, s);
+    case EPI_STORE_ROPE: return run_gemm<EPI_STORE_ROPE>(dt, a, s, nullptr);
+    case EPI_F32_ROPE: return run_gemm<EPI_F32_ROPE>(dt, a, s, nullptr);
+    case EPI_RESID: return run_gemm<EPI_RESID>(dt, a, s, nullptr);
+    case EPI_SWIGLU: return run_gemm<EPI_SWIGLU>(dt, a, s, nullptr);
+    case EPI_QKV: return run_gemm<EPI_QKV>(dt, a, s, blend_done);
   }
   return hipErrorInvalidValue;
 }

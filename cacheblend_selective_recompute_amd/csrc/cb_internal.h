@@ -243,9 +243,23 @@ struct GemmArgs {
   int64_t ldc2;
   int q_cols;
   int rope2_cols;
+  // EPI_QKV, optional (blend != 0; bf16 or FP8 cache): every candidate row of the
+  // layer is kept.  When K is split, the reduction then also takes each candidate
+  // row's (rows < blend_nc) squared distance of its fresh K/V from the cached row
+  // at row_pos into blend_dev[row] (and blend_dev_by_pos[pos] when non-null) and
+  // writes every row's fresh K/V into that row of the cache instead of into C2;
+  // launch_gemm reports whether it did (if not, C2 holds them as usual).
+  int blend;
+  int blend_layer;
+  int blend_nc;
+  PagedRef blend_cache;
+  float* blend_dev;
+  float* blend_dev_by_pos;
 };
 constexpr int64_t kGemmPartFloats = int64_t(32) << 20;   // 128 MiB of split-K partials
-hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s);
+// *blend_done (nullable): set when an EPI_QKV product with a.blend did the blend's
+// deviation and cache write in its reduction
+hipError_t launch_gemm(cb_dtype dt, GemmEpi epi, const GemmArgs& a, hipStream_t s, bool* blend_done = nullptr);
 // bf16 block tiles: 256 x 256 with 8 waves (one workgroup per CU) or 128 x 256
 // with 4 waves (two per CU)
 enum GemmCfg : int { GEMM_CFG_256 = 0, GEMM_CFG_128 = 1 };

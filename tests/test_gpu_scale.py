@@ -99,6 +99,13 @@ def test_blend_layer_70b_width_sampled():
     _layer_sampled(cbinputs.SHAPES["llama-70b"], 4096, 64, 614, seed=5, paged=True)
 
 
+def test_blend_layer_8b_width_keep_all_sampled():
+    # every candidate kept: the Q/K/V product's split-K reduction takes the deviations
+    # and writes the fresh K/V rows into the cache itself
+    say("cb_blend_layer: 8B width, layer 1, 614 candidates + 64 query rows, keep all 614, paged")
+    _layer_sampled(cbinputs.SHAPES["llama3-8b"], 614, 64, 614, seed=7, paged=True)
+
+
 def test_blend_layer_32k_context_paged_sampled():
     say("cb_blend_layer: 8B width, layer 1, 32768 candidates + 128 query rows, keep 4915, paged")
     _layer_sampled(cbinputs.SHAPES["llama3-8b"], 32768, 128, 4915, seed=6, paged=True)

@@ -113,10 +113,10 @@ def work_per_kind(shape, N, Q, ks, sets, chunk_lens, fused_keep_all=False):
     """Algorithmic FLOPs (MFMA kinds) or HBM bytes (the others) of one step.
 
     sets[l]: positions kept at layer l (ascending), for the attention count.
-    fused_keep_all: the layers that keep every candidate took their deviations and
-    wrote their fresh K/V inside the Q/K/V product's split-K reduction (no
-    deviation or scatter launch of their own), so those bytes are not counted
-    under the deviation and scatter kinds."""
+    fused_keep_all: the layers that keep every candidate took their deviations,
+    wrote their fresh K/V and their (identity) top-k's row maps inside the Q/K/V
+    product's split-K reduction (no deviation, select or scatter launch of their
+    own), so those bytes are not counted under those kinds."""
     d, F = shape.d_model, shape.d_ff
     qw, kvw = shape.q_width, shape.kv_width
     es = 2 if shape.dtype == "bf16" else 4
@@ -145,7 +145,7 @@ def work_per_kind(shape, N, Q, ks, sets, chunk_lens, fused_keep_all=False):
         if not fused:
             w["deviation"] += nc * (kvw * (2 * 4 + 2 * es) + 4 + 4)
             w["scatter"] += (k + Q) * kvw * (2 * 4 + 2 * es)
-        w["select"] += nc * 8 + k * 8
+            w["select"] += nc * 8 + k * 8
         if k != nc:
             w["norm"] += (k + Q) * d * (4 + es)     # the kept rows' queries, normalised apart
         nc = k
@@ -641,8 +641,9 @@ def main():
         "roofline": roof,
         "kernels_ms_per_step": breakdown,
         "deviation_scatter_in_qkv_reduce": {"layers": keep_all if fused_keep_all else 0,
-                                             "note": "layers keeping every candidate take their deviations and write "
-                                                     "their fresh K/V in the Q/K/V split-K reduction (gemm_qkv)"},
+                                             "note": "layers keeping every candidate take their deviations, write "
+                                                     "their fresh K/V and the identity top-k's row maps in the Q/K/V "
+                                                     "split-K reduction (gemm_qkv)"},
         "cold_ms_per_step": ({"median": round(float(np.median(cold)), 4), "min": round(min(cold), 4), "runs": len(cold)}
                              if cold else None),
         "measured_peaks": peaks,

@@ -380,6 +380,11 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
     g.blend_nc = check ? nc : 0;
     g.blend_dev = io.dev_slot ? io.dev_slot : w.dev;
     g.blend_dev_by_pos = io.dev_by_pos;
+    g.blend_gmap = w.gmap;
+    g.blend_rowpos = io.rowpos_out;
+    g.blend_pos_out = io.pos_out;
+    g.blend_slot = check ? w.slot : nullptr;
+    g.blend_copy = io.hkvd_row;
     CB_LAUNCH(tr, CB_KIND_GEMM_QKV, launch_gemm(c.dtype, EPI_QKV, g, s, &blend_done), "qkv gemm");
   } else {
     g.B = static_cast<const char*>(lw.w_qkv) + (int64_t)qw * d * es; g.ldb = d;
@@ -392,10 +397,12 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
   const int32_t* sel_slot = nullptr;
   const int32_t* sel_pos = io.cand_pos;
   int32_t* copy_out = io.pos_out;
-  if (check) {
+  if (blend_done) {
+    // the Q/K/V reduction took the deviations, wrote the cache and, the top-k of all
+    // candidates being the identity, the row maps
+  } else if (check) {
     float* dev = io.dev_slot ? io.dev_slot : w.dev;
-    if (!blend_done)
-      CB_LAUNCH(tr, CB_KIND_DEVIATION, launch_deviation(c.dtype, w.kvf, w.kvf + kvw, 2 * kvw, io.cand_pos, nc, kv, l, kvw, dev, io.dev_by_pos, s), "deviation");
+    CB_LAUNCH(tr, CB_KIND_DEVIATION, launch_deviation(c.dtype, w.kvf, w.kvf + kvw, 2 * kvw, io.cand_pos, nc, kv, l, kvw, dev, io.dev_by_pos, s), "deviation");
     // the top-k also writes the row maps of the kept rows and the suffix
     CB_LAUNCH(tr, CB_KIND_SELECT, launch_select_rows(dev, io.cand_pos, nc, k, io.pos_out, w.slot, N, Q, w.gmap,
                                                      io.rowpos_out, io.hkvd_row, s), "select");

@@ -444,7 +444,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int spli
 
 // Split-K reduction of the fused Q/K/V product of a layer that keeps all of its
 // candidate rows, with the blend's per-row work folded in (GemmArgs::blend): one
-// workgroup per row sums the partials in split order, rotates Q and K at the
+// workgroup per row writes the row maps of the (identity) top-k, sums the partials
+// in split order, rotates Q and K at the
 // row's position, stores Q (bf16), and for the K/V columns reads the cached row,
 // adds the squared differences (candidate rows only; per thread in column
 // order, then across the workgroup in a fixed order) and writes the fresh
@@ -464,6 +465,15 @@ __global__ __launch_bounds__(256) void qkv_reduce_blend_kernel(GemmArgs g, int s
   const PagedRef& c = g.blend_cache;
   const int64_t off = static_cast<int64_t>(g.blend_layer) * c.layer_stride + paged_row(c, pos) * kvw;
   const bool cand = row < g.blend_nc;
+  if (tid == 0) {                                     // the row maps of an identity top-k
+    if (g.blend_gmap) g.blend_gmap[row] = row;
+    if (g.blend_rowpos) g.blend_rowpos[row] = pos;
+    if (cand) {
+      if (g.blend_pos_out) g.blend_pos_out[row] = pos;
+      if (g.blend_slot) g.blend_slot[row] = row;
+      if (g.blend_copy) g.blend_copy[row] = pos;
+    }
+  }
   float acc = 0.f;
   for (int j = tid; j < n4; j += 256) {
     const int col = j * 4;

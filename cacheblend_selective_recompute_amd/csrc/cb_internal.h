@@ -248,13 +248,22 @@ struct GemmArgs {
   // row's (rows < blend_nc) squared distance of its fresh K/V from the cached row
   // at row_pos into blend_dev[row] (and blend_dev_by_pos[pos] when non-null) and
   // writes every row's fresh K/V into that row of the cache instead of into C2;
-  // launch_gemm reports whether it did (if not, C2 holds them as usual).
+  // launch_gemm reports whether it did (if not, C2 holds them as usual).  Keeping
+  // every candidate, the top-k is the identity, so the same reduction also writes
+  // the layer's row maps: row r's source row (r) into blend_gmap and position into
+  // blend_rowpos; for candidate rows the kept position into blend_pos_out and
+  // blend_copy and the slot (r) into blend_slot (each nullable).
   int blend;
   int blend_layer;
   int blend_nc;
   PagedRef blend_cache;
   float* blend_dev;
   float* blend_dev_by_pos;
+  int32_t* blend_gmap;
+  int32_t* blend_rowpos;
+  int32_t* blend_pos_out;
+  int32_t* blend_slot;
+  int32_t* blend_copy;
 };
 constexpr int64_t kGemmPartFloats = int64_t(32) << 20;   // 128 MiB of split-K partials
 // *blend_done (nullable): set when an EPI_QKV product with a.blend did the blend's

@@ -109,3 +109,26 @@ def check_sets(gpu_set, ora_set, cand, dev_ora, k, kv_scale_sq, label=""):
     assert frac >= 0.99, f"{label}: the keep/drop decision agrees on only {frac:.4f} of the candidates"
     say(f"  {label}: {inter}/{k} kept positions shared, decision agreement {frac:.4f}")
     return frac
+
+
+def fp8_grid_step(x, scale):
+    """Spacing of the E4M3 grid (times scale) at each |x|."""
+    a = np.abs(np.asarray(x, dtype=np.float64)) / scale
+    _, E = np.frexp(np.maximum(a, 2.0 ** -9))
+    return np.ldexp(1.0, np.clip(E - 1, -6, 8) - 3) * scale
+
+
+def fp8_close(g, o, scale, label, min_equal=0.97):
+    """Stored FP8 values against the oracle's: every element within one grid step
+    (times scale) plus 2e-2 of the largest value, and min_equal of them on the
+    same grid point."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    d = np.abs(g - o)
+    atol = 2e-2 * float(np.max(np.abs(o), initial=0.0))
+    ok = d <= 1.0001 * np.maximum(fp8_grid_step(o, scale), fp8_grid_step(g, scale)) + atol
+    # equal = the same grid point; the GPU side is dequantised as code x scale in fp32
+    eq = float(np.mean(d <= 1e-6 * np.abs(o))) if d.size else 1.0
+    say(f"  {label}: {eq:.4f} of the elements equal, all within one grid step: {bool(ok.all())}")
+    assert ok.all(), f"{label}: {int((~ok).sum())} elements beyond one grid step"
+    assert eq >= min_equal, f"{label}: only {eq:.4f} equal"

@@ -21,7 +21,7 @@ import oracle
 from oracle.blend import fp8_e4m3
 from cacheblend_selective_recompute_amd import api
 
-from gpu_helpers import ints, rel, say, to_dev, to_np
+from gpu_helpers import fp8_close as _fp8_close, ints, rel, say, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -30,26 +30,6 @@ MINI8B = cbinputs.ModelShape("mini-8b-heads", 3, 1024, 8, 2, 128, 3584, 32000, 5
 # (head_dim 128 layers are widened to bf16 first and read by the LDS-staged one)
 MINI64 = cbinputs.ModelShape("mini-hd64", 3, 512, 8, 2, 64, 1792, 32000, 10000.0, dtype="bf16")
 KS, VS = 2.0 ** -5, 2.0 ** -5          # grid up to 14: the K/V of unit-RMS rows fit
-
-
-def _grid_step(x, scale):
-    """Spacing of the E4M3 grid (times scale) at each |x|."""
-    a = np.abs(np.asarray(x, dtype=np.float64)) / scale
-    _, E = np.frexp(np.maximum(a, 2.0 ** -9))
-    return np.ldexp(1.0, np.clip(E - 1, -6, 8) - 3) * scale
-
-
-def _fp8_close(g, o, scale, label, min_equal=0.97):
-    g = np.asarray(g, dtype=np.float64)
-    o = np.asarray(o, dtype=np.float64)
-    d = np.abs(g - o)
-    atol = 2e-2 * float(np.max(np.abs(o), initial=0.0))
-    ok = d <= 1.0001 * np.maximum(_grid_step(o, scale), _grid_step(g, scale)) + atol
-    # equal = the same grid point; the GPU side is dequantised as code x scale in fp32
-    eq = float(np.mean(d <= 1e-6 * np.abs(o))) if d.size else 1.0
-    say(f"  {label}: {eq:.4f} of the elements equal, all within one grid step: {bool(ok.all())}")
-    assert ok.all(), f"{label}: {int((~ok).sum())} elements beyond one grid step"
-    assert eq >= min_equal, f"{label}: only {eq:.4f} equal"
 
 
 def _om(shape, w, ks=KS, vs=VS):

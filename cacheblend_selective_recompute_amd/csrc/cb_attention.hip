@@ -923,6 +923,56 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_spl
   for (int e = 0; e < PER; ++e) ob[pk_off(row, head * DH + lane * PER + e, KO)] = f2bf(acc[e] * inv);
 }
 
+// The same merge with one workgroup per row: thread t takes CPT consecutive
+// output columns (inside one head) of the row, so every split's (max, sum) pair
+// and partial columns of the row are loaded at once; sums run in split order.
+// For rows of H_q x DH = 256 x CPT columns (CPT a multiple of 8 dividing DH).
+template <int DH, int CPT>
+__global__ __launch_bounds__(256) void attn_combine_wide_kernel(AttnArgs a, int n_splits, int ksplit, int QT) {
+  static_assert(CPT % 8 == 0 && DH % CPT == 0, "whole 8-column chunks inside one head");
+  const int row = blockIdx.x;
+  const int t_last = min((row / QT + 1) * QT, a.R) - 1;
+  const int kv_end = a.rowpos[t_last] + 1;
+  const int ns = min(n_splits, (kv_end + ksplit - 1) / ksplit);
+  if (ns <= 1) return;                                   // written whole by the attention kernel
+  const int col = threadIdx.x * CPT;
+  const int head = col / DH;
+  auto prow = [&](int sp) { return (static_cast<int64_t>(sp) * a.R + row) * a.n_q_heads + head; };
+  float M = -INFINITY;
+  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, a.part_ml[prow(sp)].x);
+  float acc[CPT];
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) acc[e] = 0.f;
+  float lsum = 0.f;
+#pragma unroll 2
+  for (int sp = 0; sp < ns; ++sp) {
+    const float2 ml = a.part_ml[prow(sp)];
+    const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
+    lsum += w * ml.y;
+    const float4* po = reinterpret_cast<const float4*>(a.part_o + prow(sp) * DH + (col % DH));
+#pragma unroll
+    for (int e = 0; e < CPT / 4; ++e) {
+      const float4 v = po[e];
+      acc[4 * e] += w * v.x;
+      acc[4 * e + 1] += w * v.y;
+      acc[4 * e + 2] += w * v.z;
+      acc[4 * e + 3] += w * v.w;
+    }
+  }
+  const float inv = 1.0f / lsum;
+  bf16_t* ob = static_cast<bf16_t*>(a.o);
+  const int KO = a.n_q_heads * DH;
+#pragma unroll
+  for (int c = 0; c < CPT / 8; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f2bf(acc[8 * c + 2 * i] * inv)) |
+             (static_cast<uint32_t>(f2bf(acc[8 * c + 2 * i + 1] * inv)) << 16);
+    *reinterpret_cast<uint4*>(ob + pk_off(row, col + 8 * c, KO)) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 path: one wave per (query row, query head), keys in blocks of 64 with
 // an online softmax; each lane owns head_dim/64 output dims (head_dim <= 256).
@@ -1022,8 +1072,15 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;
-  const int pairs = a.R * a.n_q_heads;
-  attn_combine_kernel<DH><<<(pairs + 3) / 4, 256, 0, s>>>(a, n_splits, ksplit, QT);
+  const int width = a.n_q_heads * DH;
+  if (width == 256 * 16) {
+    attn_combine_wide_kernel<DH, 16><<<a.R, 256, 0, s>>>(a, n_splits, ksplit, QT);
+  } else if (width == 256 * 32 && DH % 32 == 0) {
+    attn_combine_wide_kernel<DH, (DH % 32 == 0 ? 32 : 16)><<<a.R, 256, 0, s>>>(a, n_splits, ksplit, QT);
+  } else {
+    const int pairs = a.R * a.n_q_heads;
+    attn_combine_kernel<DH><<<(pairs + 3) / 4, 256, 0, s>>>(a, n_splits, ksplit, QT);
+  }
   return hipGetLastError();
 }
 

@@ -673,10 +673,17 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs 
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(&kv[0][0]))) +
       wid * 4096);
   const int pmask = (1 << sh) - 1;
+  // the entry is the same for the whole wave: a scalar load, counted apart from the
+  // vector-memory counter that the block copies raise, so waiting for it never
+  // waits for copies in flight
+  // (clamped to the last key of the range, so the load is unconditional; copies past
+  // the range read zeros whatever the entry)
+  const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+  const int j_last = __builtin_amdgcn_readfirstlane(j_end - 1);
   auto page_of = [&](int jb) -> int {   // block-table entry of this wave's 16 keys of block jb
     if constexpr (CONTIG) return 0;
-    const int k0 = jb + 16 * wid;
-    return k0 < j_end ? a.cache.bt[k0 >> sh] : 0;
+    const int k0 = __builtin_amdgcn_readfirstlane(min(jb + 16 * wid_u, j_last));
+    return a.cache.bt[k0 >> sh];
   };
   int pe = page_of(j_begin);
   auto issue = [&](int jb, int stage) {

@@ -597,13 +597,16 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs 
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int n_tiles = (a.R + QT - 1) / QT;
-  // one-dimensional grid over (KV head, tile, split): each XCD takes a contiguous run
-  // of work items, i.e. mostly one KV head, whose K/V stream then stays in its L2
+  // one-dimensional grid over (KV head, split, tile): each XCD takes a contiguous run
+  // of work items, i.e. mostly one KV head, whose K/V stream then stays in its L2.
+  // Within a head the first split of every tile (longest tile first) comes before
+  // the second split of any: the later splits exist only for the longer tiles, so
+  // the empty items trail and the items that run start together.
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int per_head = n_tiles * n_splits;
   const int kvh = w / per_head;
-  const int split = (w % per_head) % n_splits;
-  const int tile = n_tiles - 1 - (w % per_head) / n_splits;   // longest first
+  const int split = (w % per_head) / n_tiles;
+  const int tile = n_tiles - 1 - (w % per_head) % n_tiles;
   const int t0 = tile * QT;
   const int t_last = min(t0 + QT, a.R) - 1;
   const int kv_end = a.rowpos[t_last] + 1;
@@ -1042,6 +1045,28 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// Key splits of the lean LDS-DMA kernel when the (tile, head) grid cannot fill the
+// chip: from `from` splits up, the most whose non-empty work items still fit the
+// chip's 512 resident workgroups (two per CU) at once, so none waits for a second
+// round.  Item counts are estimated with the tiles' key ranges spread evenly up to
+// the last key (sorted rows of a blend: tile t ends near (t + 1) / n_tiles of the
+// keys); a wrong estimate costs time, never correctness.
+int fa_splits(int from, int n_tiles, int kv_blocks, int n_kv_heads, int R, int n_q_heads) {
+  int best = from;
+  for (int ns = from + 1; ns <= kAttnSplitCap && ns <= kv_blocks; ++ns) {
+    if (static_cast<int64_t>(ns) * R * n_q_heads > kAttnPartialRows) break;
+    const int per = (kv_blocks + ns - 1) / ns;
+    int64_t items = 0;
+    for (int t = 0; t < n_tiles; ++t) {
+      const int bt = static_cast<int>((static_cast<int64_t>(kv_blocks) * (t + 1) + n_tiles - 1) / n_tiles);
+      items += (bt + per - 1) / per;
+    }
+    if (items * n_kv_heads > 512) break;
+    best = ns;
+  }
+  return best;
+}
+
 // KIND 0 register-staged, 1 LDS-DMA, 2 lean LDS-DMA; CONTIG (KIND 2): keys in one contiguous run
 template <int DH, int G, int NG, int KIND, bool F8 = false, bool CONTIG = false>
 hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
@@ -1062,6 +1087,8 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_splits_req > 0 && a.part_o != nullptr &&
       static_cast<int64_t>(a.n_splits_req) * a.R * a.n_q_heads <= kAttnPartialRows)
     n_splits = std::min(a.n_splits_req, kv_blocks);
+  if (KIND == 2 && a.n_splits_req == 0 && n_splits > 1)
+    n_splits = fa_splits(n_splits, n_tiles, kv_blocks, a.n_kv_heads, a.R, a.n_q_heads);
   const int ksplit = ((kv_blocks + n_splits - 1) / n_splits) * KVB;
   const dim3 grid(n_tiles * n_splits, a.n_kv_heads);
   if constexpr (KIND == 2) {

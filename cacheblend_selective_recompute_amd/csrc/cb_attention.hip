@@ -1075,9 +1075,10 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   const int base = n_tiles * a.n_kv_heads;
   const int kv_blocks = (a.kv_bound + KVB - 1) / KVB;
   // split the keys only when the (tile, head) grid cannot fill the chip; tiles of sparse
-  // rows end at spread-out positions, so about half the splits of a tile have keys, and
-  // ~2 x 256 workgroups in all measured best (678 rows over 4K keys: 3 splits 63 us,
-  // 5 splits 67 us, 2 splits 70 us)
+  // rows end at spread-out positions, so only the longer tiles have keys in the later
+  // splits: start from ~2 x 256 workgroups in all, and the lean kernel then takes as
+  // many more splits as keep its non-empty items within one round (678 rows over 4K
+  // keys, split-major order: 3 splits 60-63 us, 4 splits 54-57 us, 5 splits 64-66 us)
   int n_splits = 1;
   if (base < 512 && a.part_o != nullptr) {
     n_splits = std::min(kAttnSplitCap, std::max(1, (512 + base - 1) / base));

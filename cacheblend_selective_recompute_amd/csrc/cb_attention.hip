@@ -1047,11 +1047,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 
 // Key splits of the lean LDS-DMA kernel when the (tile, head) grid cannot fill the
 // chip: from `from` splits up, the most whose non-empty work items still fit the
-// chip's 512 resident workgroups (two per CU) at once, so none waits for a second
-// round.  Item counts are estimated with the tiles' key ranges spread evenly up to
+// chip's `slots` resident workgroups (two per CU, three with one query group per
+// wave) at once, so none waits for a second round.  Item counts are estimated with the tiles' key ranges spread evenly up to
 // the last key (sorted rows of a blend: tile t ends near (t + 1) / n_tiles of the
 // keys); a wrong estimate costs time, never correctness.
-int fa_splits(int from, int n_tiles, int kv_blocks, int n_kv_heads, int R, int n_q_heads) {
+int fa_splits(int from, int n_tiles, int kv_blocks, int n_kv_heads, int R, int n_q_heads, int slots) {
   int best = from;
   for (int ns = from + 1; ns <= kAttnSplitCap && ns <= kv_blocks; ++ns) {
     if (static_cast<int64_t>(ns) * R * n_q_heads > kAttnPartialRows) break;
@@ -1061,7 +1061,7 @@ int fa_splits(int from, int n_tiles, int kv_blocks, int n_kv_heads, int R, int n
       const int bt = static_cast<int>((static_cast<int64_t>(kv_blocks) * (t + 1) + n_tiles - 1) / n_tiles);
       items += (bt + per - 1) / per;
     }
-    if (items * n_kv_heads > 512) break;
+    if (items * n_kv_heads > slots) break;
     best = ns;
   }
   return best;
@@ -1089,7 +1089,7 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
       static_cast<int64_t>(a.n_splits_req) * a.R * a.n_q_heads <= kAttnPartialRows)
     n_splits = std::min(a.n_splits_req, kv_blocks);
   if (KIND == 2 && a.n_splits_req == 0 && n_splits > 1)
-    n_splits = fa_splits(n_splits, n_tiles, kv_blocks, a.n_kv_heads, a.R, a.n_q_heads);
+    n_splits = fa_splits(n_splits, n_tiles, kv_blocks, a.n_kv_heads, a.R, a.n_q_heads, NG == 1 ? 768 : 512);
   const int ksplit = ((kv_blocks + n_splits - 1) / n_splits) * KVB;
   const dim3 grid(n_tiles * n_splits, a.n_kv_heads);
   if constexpr (KIND == 2) {

@@ -798,21 +798,32 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs 
       for (int s2 = 0; s2 < 2; ++s2) lsum[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[g][s2], lsum[g], 0, 0, 0);
     }
 
-    // O^T += V^T P^T (fragment layout as in attn_dma_kernel)
+    // O^T += V^T P^T (fragment layout as in attn_dma_kernel); the V^T fragment of the
+    // next step is read before this step's products issue, so LDS latency overlaps them
+    auto vread = [&](int st) __attribute__((always_inline)) -> bf16x8_t {
+      const int dt = st >> 1, s2 = st & 1;
+      s16x4_t half[2];
 #pragma unroll
-    for (int dt = 0; dt < DH / 16; ++dt) {
+      for (int h = 0; h < 2; ++h) {
+        const uint8_t* src = Vb + voffs[dt] + (32 * s2 + 16 * h) * 256;
+        half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4_t*)(const __attribute__((address_space(3))) void*)(src));
+      }
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int NST = 2 * (DH / 16);
+    bf16x8_t vq[3];
+    vq[0] = vread(0);
+    vq[1] = vread(1);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        s16x4_t half[2];
+    for (int st = 0; st < NST; ++st) {
+      if (st + 2 < NST) vq[(st + 2) % 3] = vread(st + 2);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint8_t* src = Vb + voffs[dt] + (32 * s2 + 16 * h) * 256;
-          half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4_t*)(const __attribute__((address_space(3))) void*)(src));
-        }
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int g = 0; g < NG; ++g) o[g][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[g][s2], o[g][dt], 0, 0, 0);
+      for (int g = 0; g < NG; ++g)
+        o[g][st >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vq[st % 3], pf[g][st & 1], o[g][st >> 1], 0, 0, 0);
+      if (st + 2 < NST) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // this step's two reads (step st + 2)
+        __builtin_amdgcn_sched_group_barrier(0x008, NG, 0);  // then its products
       }
     }
   };

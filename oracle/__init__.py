@@ -13,17 +13,19 @@ Sources ("the pages"):
         (chunk_hash, old_st, cur_st) match tuple: old_st is the re-RoPE source,
         cur_st the target; sections 3-7 -- fragment matching (``oracle/match.py``).
 
-Precision: every computation runs in float64 (``dtype`` argument); values the
-method *stores* (the KV cache, in the model's storage dtype) are rounded to that
-dtype (bf16 = round to nearest even) at the point of storage, exactly where the
-method writes them.
+Precision: every computation runs in float32 (NumPy arrays, OpenBLAS sgemm);
+the RoPE angles and their cos/sin are evaluated in float64 and rounded once to
+float32.  Values the method *stores* (the KV cache, in the model's storage
+dtype) are rounded to that dtype (bf16 = round to nearest even) at the point of
+storage, exactly where the method writes them.  ``precision("f64")`` runs the
+same code in float64; the tests use it only as an extra pin.
 
 Parity status of each function is listed in ``oracle/blend.py``; every function
 there is pinned by at least one test under ``tests/`` that does not re-use the
 oracle's own formulas (library special cases, closed forms, brute force).
 """
 from .blend import (  # noqa: F401
-    OracleModel, store_round, rms_norm, rope_cos_sin, rope, rerope, causal_attention,
+    OracleModel, precision, ct, store_round, rms_norm, rope_cos_sin, rope, rerope, causal_attention,
     swiglu_mlp, kv_deviation, select_hkvd, full_prefill, chunk_prefill,
     assemble_blended, full_reuse_prefill, blend_prefill, blend_prefill_masked,
     blend_layer, flop_count, decode_step,

@@ -1,4 +1,4 @@
-"""Plain CPU oracle of the CacheBlend blended prefill (float64, NumPy).
+"""Plain CPU oracle of the CacheBlend blended prefill (NumPy, float32).
 
 TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the CPU
 baseline of the benchmark; never by the GPU library.
@@ -8,17 +8,26 @@ with the section it comes from.  Model block: the Llama-3-shaped pre-norm
 decoder that the workloads name; the pages give only Q=hW_Q, K=hW_K (then
 RoPE), V=hW_V ([CB] "问题：拼接的 KV 缓存到底少了什么").
 
+Precision: every array is float32 and every product a float32 (OpenBLAS sgemm)
+product; the RoPE angles pos*theta_i and their cos/sin are evaluated in float64
+and rounded once to float32, the rotation itself is float32 arithmetic.  Values
+the method stores (the KV cache, in its storage dtype) are rounded from float32
+to that dtype (bf16: round to nearest even) where the method writes them.
+``precision("f64")`` runs the same code in float64 (cos/sin unrounded, storage
+rounding straight from float64); the tests use it as an extra pin only.
+
 Readings taken where the pages are silent (all listed in the design notes):
   * layer 0 runs in full over every row; its context K/V are the re-RoPE'd
     cache (they depend on the token alone); the first checked layer is 1;
   * deviation = squared L2 over the concatenated K and V of all KV heads, K
-    compared after RoPE at the new position, fresh values unrounded;
+    compared after RoPE at the new position, fresh values unrounded, summed in
+    the compute precision;
   * r counts context tokens only: k = floor(r*N + 0.5); the query suffix is
     recomputed at every layer, written to the cache, never ranked;
   * ties in the top-k go to the smaller position; sets are reported ascending;
   * rows written at layer l are exactly S_l plus the suffix, before attention;
   * RoPE rotates adjacent pairs (2i, 2i+1) by pos*theta_i,
-    theta_i = base^(-2i/d_h), angles and cos/sin in float64;
+    theta_i = base^(-2i/d_h);
   * RMSNorm eps from the model, gains as given; SiLU-gated MLP; no biases;
     untied LM head after a final RMSNorm; attention scale 1/sqrt(d_h).
 
@@ -29,12 +38,35 @@ the method's own special cases r=0% / r=100% / single chunk).
 """
 from __future__ import annotations
 
+import contextlib
+import os
 from dataclasses import dataclass
 from typing import Callable, Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
 F64 = np.float64
+_CT = [np.float32]          # compute precision (one-element list: set by ``precision``)
+
+
+def ct():
+    """The compute dtype: numpy.float32 unless inside ``precision("f64")``."""
+    return _CT[0]
+
+
+@contextlib.contextmanager
+def precision(name: str):
+    """Run the oracle in "f32" (the default) or "f64" inside the block."""
+    old = _CT[0]
+    _CT[0] = {"f32": np.float32, "f64": np.float64}[name]
+    try:
+        yield
+    finally:
+        _CT[0] = old
+
+
+def _a(x) -> np.ndarray:
+    return np.asarray(x, dtype=ct())
 
 
 # ----------------------------------------------------------------------------
@@ -50,30 +82,37 @@ def fp8_e4m3(x: np.ndarray) -> np.ndarray:
     infinities), ties to even, magnitudes beyond 448 saturated to 448.
     A value of magnitude a in binade [2^e, 2^(e+1)) (e >= -6; below that the
     subnormal spacing) sits on the grid of step 2^(e-3)."""
-    x = np.asarray(x, dtype=F64)
+    x = _a(x)
     a = np.abs(x)
     _, E = np.frexp(a)                       # a = f * 2^E, f in [0.5, 1)
     e = np.clip(E - 1, -6, 8)
-    step = np.ldexp(1.0, e - 3)
-    r = np.minimum(np.rint(a / step) * step, FP8_E4M3_MAX)
+    step = np.ldexp(np.ones_like(a), e - 3)  # a power of two: a / step and the product are exact
+    r = np.minimum(np.rint(a / step) * step, a.dtype.type(FP8_E4M3_MAX))
     return np.where(x < 0, -r, r)
 
 
 def store_round(x: np.ndarray, storage: str, scale: float = 1.0) -> np.ndarray:
-    """Round ``x`` to the storage dtype and return it as float64.
+    """Round ``x`` to the storage dtype; the result is in the compute dtype.
 
-    'f32' rounds to IEEE single (nearest even); 'bf16' keeps 7 explicit
-    mantissa bits, rounding the float64 value directly to nearest, ties to
-    even (normal range only, which is all this method produces); 'fp8' stores
-    fp8_e4m3(x / scale) and the value it stands for is that times ``scale``
-    (one scale per cache tensor).
+    'f32' rounds to IEEE single (nearest even; nothing to do in float32);
+    'bf16' keeps 7 explicit mantissa bits, rounding the compute-precision value
+    directly to nearest, ties to even (normal range only, which is all this
+    method produces); 'fp8' stores fp8_e4m3(x / scale) and the value it stands
+    for is that times ``scale`` (one scale per cache tensor); 'f64' keeps the
+    value.
     """
-    x = np.asarray(x, dtype=F64)
+    x = _a(x)
     if storage == "fp8":
-        return fp8_e4m3(x / float(scale)) * float(scale)
+        s = x.dtype.type(scale)
+        return fp8_e4m3(x / s) * s
     if storage == "f32":
-        return x.astype(np.float32).astype(F64)
+        return x.astype(np.float32).astype(x.dtype)
     if storage == "bf16":
+        if x.dtype == np.float32:
+            u = np.ascontiguousarray(x).view(np.uint32).astype(np.uint64)
+            lsb = (u >> np.uint64(16)) & np.uint64(1)
+            r = ((u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)).astype(np.uint32)
+            return r.view(np.float32).reshape(x.shape)
         u = np.ascontiguousarray(x).view(np.uint64)
         drop = np.uint64(52 - 7)
         lsb = (u >> drop) & np.uint64(1)
@@ -91,13 +130,14 @@ def store_round(x: np.ndarray, storage: str, scale: float = 1.0) -> np.ndarray:
 
 def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm: x / sqrt(mean(x^2) + eps) * g, per row."""
-    x = np.asarray(x, dtype=F64)
+    x = _a(x)
     ms = np.mean(x * x, axis=-1, keepdims=True)
-    return x / np.sqrt(ms + eps) * np.asarray(g, dtype=F64)
+    return x / np.sqrt(ms + x.dtype.type(eps)) * _a(g)
 
 
 def rope_cos_sin(pos: np.ndarray, head_dim: int, theta: float) -> Tuple[np.ndarray, np.ndarray]:
-    """cos/sin of pos * theta_i, theta_i = base^(-2i/d_h), i < d_h/2, in float64.
+    """cos/sin of pos * theta_i, theta_i = base^(-2i/d_h), i < d_h/2: the angle
+    and its cos/sin evaluated in float64, then rounded to the compute dtype.
 
     [CB] "位置恢复": R_m is block diagonal with entries cos(m theta_i),
     sin(m theta_i); d/2 rotation pairs.
@@ -105,7 +145,7 @@ def rope_cos_sin(pos: np.ndarray, head_dim: int, theta: float) -> Tuple[np.ndarr
     i = np.arange(head_dim // 2, dtype=F64)
     inv = np.power(F64(theta), -(2.0 * i) / head_dim)
     ang = np.asarray(pos, dtype=F64)[:, None] * inv[None, :]
-    return np.cos(ang), np.sin(ang)
+    return np.cos(ang).astype(ct()), np.sin(ang).astype(ct())
 
 
 def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
@@ -113,7 +153,7 @@ def rope(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
 
     Pair (x_2i, x_2i+1) -> (x_2i c - x_2i+1 s, x_2i s + x_2i+1 c).
     """
-    x = np.asarray(x, dtype=F64)
+    x = _a(x)
     n, H, dh = x.shape
     c, s = rope_cos_sin(pos, dh, theta)
     c = c[:, None, :]
@@ -133,11 +173,21 @@ def rerope(k: np.ndarray, delta: int, theta: float, storage: str, scale: float =
     (leading layer axis allowed); every token moves by the same ``delta`` =
     n - p.  The result is rounded to the storage dtype.  V is never rotated.
     """
-    k = np.asarray(k, dtype=F64)
+    k = _a(k)
     shp = k.shape
     flat = k.reshape(-1, shp[-2], shp[-1])
     out = rope(flat, np.full(flat.shape[0], delta, dtype=F64), theta)
     return store_round(out.reshape(shp), storage, scale)
+
+
+def _host_threads() -> int:
+    """Worker threads for the per-head attention loop: the cores this process may
+    use, at most 16 (the host share of one GPU on the machines this runs on)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:       # pragma: no cover - non-Linux hosts
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def causal_attention(q: np.ndarray, q_pos: np.ndarray, k: np.ndarray, v: np.ndarray,
@@ -145,45 +195,65 @@ def causal_attention(q: np.ndarray, q_pos: np.ndarray, k: np.ndarray, v: np.ndar
     """softmax(q k^T / sqrt(d_h)) v over keys with k_pos <= q_pos, per head.
 
     q [n, Hq, d_h]; k, v [P, Hkv, d_h]; GQA: q head h reads kv head
-    floor(h * Hkv / Hq).  Softmax subtracts the row maximum.
+    floor(h * Hkv / Hq).  Softmax subtracts the row maximum.  Rows are taken in
+    blocks of ``row_block`` (each block sees the keys up to its last row; the
+    others are masked), and the (block, head) pairs, which share nothing, run on
+    several threads when the problem is large; each pair's arithmetic is the
+    same either way.
     """
-    q = np.asarray(q, dtype=F64)
-    k = np.asarray(k, dtype=F64)
-    v = np.asarray(v, dtype=F64)
+    q = _a(q)
+    k = _a(k)
+    v = _a(v)
     n, Hq, dh = q.shape
     Hkv = k.shape[1]
-    scale = 1.0 / np.sqrt(dh)
-    out = np.zeros((n, Hq, dh), dtype=F64)
+    scale = q.dtype.type(1.0 / np.sqrt(dh))
+    out = np.zeros((n, Hq, dh), dtype=q.dtype)
     q_pos = np.asarray(q_pos)
     k_pos = np.asarray(k_pos)
+    blocks = []
     for r0 in range(0, n, row_block):
         r1 = min(n, r0 + row_block)
         qp = q_pos[r0:r1]
         # keys any row of this block may see
-        kmax = qp.max()
-        kmask = k_pos <= kmax
-        kp = k_pos[kmask]
-        allowed = kp[None, :] <= qp[:, None]
-        for h in range(Hq):
-            g = (h * Hkv) // Hq
-            kk = k[kmask, g, :]
-            vv = v[kmask, g, :]
-            s = (q[r0:r1, h, :] @ kk.T) * scale
-            s = np.where(allowed, s, -np.inf)
-            m = np.max(s, axis=1, keepdims=True)
-            p = np.exp(s - m)
-            p /= np.sum(p, axis=1, keepdims=True)
-            out[r0:r1, h, :] = p @ vv
+        kmask = k_pos <= qp.max()
+        allowed = k_pos[kmask][None, :] <= qp[:, None]
+        blocks.append((r0, r1, kmask, allowed))
+
+    def one(task):
+        (r0, r1, kmask, allowed), h = task
+        g = (h * Hkv) // Hq
+        kk = k[kmask, g, :]
+        vv = v[kmask, g, :]
+        s = (q[r0:r1, h, :] @ kk.T) * scale
+        s = np.where(allowed, s, -np.inf)
+        m = np.max(s, axis=1, keepdims=True)
+        p = np.exp(s - m)
+        p /= np.sum(p, axis=1, keepdims=True)
+        out[r0:r1, h, :] = p @ vv
+
+    tasks = [(b, h) for b in blocks for h in range(Hq)]
+    work = sum(int(b[3].size) for b in blocks) * Hq
+    nt = _host_threads()
+    if nt == 1 or work < (1 << 26):
+        for t in tasks:
+            one(t)
+        return out
+    # one BLAS thread per worker: the workers already fill the cores
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=nt) as ex:
+        list(ex.map(one, tasks))
     return out
 
 
 def swiglu_mlp(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
     """W_down (SiLU(a W_gate) * (a W_up)), SiLU(z) = z / (1 + e^-z)."""
-    a = np.asarray(a, dtype=F64)
-    g = a @ np.asarray(w_gate, dtype=F64).T
-    u = a @ np.asarray(w_up, dtype=F64).T
-    h = g / (1.0 + np.exp(-g)) * u
-    return h @ np.asarray(w_down, dtype=F64).T
+    a = _a(a)
+    g = a @ _a(w_gate).T
+    u = a @ _a(w_up).T
+    with np.errstate(over="ignore"):         # exp(-g) = inf for g << 0 gives SiLU = -0, its limit
+        h = g / (a.dtype.type(1.0) + np.exp(-g)) * u
+    return h @ _a(w_down).T
 
 
 # ----------------------------------------------------------------------------
@@ -235,7 +305,7 @@ class OracleModel:
 
 
 def _proj(a: np.ndarray, w: np.ndarray) -> np.ndarray:
-    return a @ np.asarray(w, dtype=F64).T
+    return _a(a) @ _a(w).T
 
 
 def _logits(m: OracleModel, x_last: np.ndarray) -> np.ndarray:
@@ -252,10 +322,10 @@ def kv_deviation(k_fresh, v_fresh, k_cached, v_cached) -> np.ndarray:
 
     [CB] "核心思想", eq. Δkv: Δ[j] = || KV_i[j] - KV_i^full[j] ||, taken over
     the concatenation of K and V across every KV head; the square ranks the
-    same as the norm.  Inputs [n, H_kv, d_h]; output float64 [n].
+    same as the norm.  Inputs [n, H_kv, d_h]; output [n] in the compute dtype.
     """
-    dk = np.asarray(k_fresh, F64) - np.asarray(k_cached, F64)
-    dv = np.asarray(v_fresh, F64) - np.asarray(v_cached, F64)
+    dk = _a(k_fresh) - _a(k_cached)
+    dv = _a(v_fresh) - _a(v_cached)
     ax = tuple(range(1, dk.ndim))
     return np.sum(dk * dk, axis=ax) + np.sum(dv * dv, axis=ax)
 
@@ -266,7 +336,7 @@ def select_hkvd(dev: np.ndarray, cand_pos: np.ndarray, k: int) -> np.ndarray:
     [CB] "选 token": rank the candidates by deviation and keep the top ones.
     Ties go to the smaller position.  Returns the positions ascending.
     """
-    dev = np.asarray(dev, dtype=F64)
+    dev = np.asarray(dev)
     cand_pos = np.asarray(cand_pos, dtype=np.int64)
     if not (0 <= k <= len(cand_pos)):
         raise ValueError("k out of range")
@@ -298,8 +368,8 @@ def full_prefill(m: OracleModel, tokens: np.ndarray, start: int = 0) -> Dict[str
     tokens = np.asarray(tokens)
     n = len(tokens)
     pos = np.arange(start, start + n)
-    x = np.asarray(m.glob["embed"][np.asarray(tokens)], dtype=F64)
-    K = np.zeros((m.n_layers, n, m.n_kv_heads, m.head_dim), dtype=F64)
+    x = _a(m.glob["embed"][np.asarray(tokens)])
+    K = np.zeros((m.n_layers, n, m.n_kv_heads, m.head_dim), dtype=ct())
     V = np.zeros_like(K)
     for l in range(m.n_layers):
         w = m.layer(l)
@@ -319,7 +389,7 @@ def decode_step(m: OracleModel, Kb: np.ndarray, Vb: np.ndarray, token: int, pos:
     own K/V (storage dtype) are written at ``pos`` in place, then it attends to
     [0, pos].  Returns the token's logits.
     """
-    x = np.asarray(m.glob["embed"][[int(token)]], dtype=F64)
+    x = _a(m.glob["embed"][[int(token)]])
     p = np.array([int(pos)])
     keys = np.arange(int(pos) + 1)
     for l in range(m.n_layers):
@@ -347,7 +417,7 @@ def assemble_blended(m: OracleModel, chunks: Sequence[Tuple], n_query: int) -> T
     """
     N = sum(len(c[0]) for c in chunks)
     T = N + n_query
-    Kb = np.zeros((m.n_layers, T, m.n_kv_heads, m.head_dim), dtype=F64)
+    Kb = np.zeros((m.n_layers, T, m.n_kv_heads, m.head_dim), dtype=ct())
     Vb = np.zeros_like(Kb)
     for tokens, Kc, Vc, old, new in chunks:
         ln = len(tokens)
@@ -454,7 +524,7 @@ def blend_prefill(m: OracleModel, chunks: Sequence[Tuple], query_tokens: np.ndar
     suffix = np.arange(N, T)
     # layer 0: every row; context K/V are the re-RoPE'd cache
     w = m.layer(0)
-    x = np.asarray(m.glob["embed"][np.asarray(tokens)], dtype=F64)
+    x = _a(m.glob["embed"][np.asarray(tokens)])
     a = rms_norm(x, w["attn_norm"], m.rms_eps)
     Kb[0, suffix] = m.store_k(rope(m.heads(_proj(a[N:], w["wk"]), m.n_kv_heads), suffix, m.rope_theta))
     Vb[0, suffix] = m.store_v(m.heads(_proj(a[N:], w["wv"]), m.n_kv_heads))
@@ -489,7 +559,7 @@ def blend_prefill_masked(m: OracleModel, chunks: Sequence[Tuple], query_tokens: 
     Kb, Vb = assemble_blended(m, chunks, Q)
     tokens = np.concatenate([_context_tokens(chunks), np.asarray(query_tokens)])
     pos = np.arange(T)
-    x = np.asarray(m.glob["embed"][np.asarray(tokens)], dtype=F64)
+    x = _a(m.glob["embed"][np.asarray(tokens)])
     cand = np.ones(T, dtype=bool)
     cand[N:] = False
     is_suffix = ~cand.copy()
@@ -535,7 +605,7 @@ def full_reuse_prefill(m: OracleModel, Kb: np.ndarray, Vb: np.ndarray, query_tok
     Q = len(query_tokens)
     N = T - Q
     suffix = np.arange(N, T)
-    x = np.asarray(m.glob["embed"][np.asarray(query_tokens)], dtype=F64)
+    x = _a(m.glob["embed"][np.asarray(query_tokens)])
     for l in range(L):
         w = m.layer(l)
         a = rms_norm(x, w["attn_norm"], m.rms_eps)

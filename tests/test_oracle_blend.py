@@ -8,6 +8,12 @@
 * sets nest, have the scheduled sizes, never contain the suffix ([CB] "核心思想")
 * a masked-dense formulation agrees with the gathered-rows one  ([CB] Fig. 5)
 * the compute share at the 8B, 4K, 15% point is about 18%      ([CB] "把账算细")
+
+Each pin runs in the oracle's float32 and again in float64.  Where two
+formulations agree only up to rounding order (the blend computes a row inside a
+larger or smaller batch than the reference does, so BLAS sums in another order)
+the float32 bound is 1e-5 normwise, the float64 bound 1e-12; bitwise claims hold
+in both.
 """
 import json
 import os
@@ -17,8 +23,13 @@ import pytest
 
 import cbinputs
 from oracle import (OracleModel, assemble_blended, blend_layer, blend_prefill, blend_prefill_masked,
-                    chunk_prefill, flop_count, full_prefill, full_reuse_prefill, kv_deviation,
+                    chunk_prefill, flop_count, full_prefill, full_reuse_prefill, kv_deviation, precision,
                     store_round)
+
+PREC = pytest.mark.parametrize("prec", ["f32", "f64"])
+# agreement up to rounding order; "r100" is the benchmark spec's bound for r = 100%
+TOL = {"f32": {"order": 1e-5, "r100": 1e-5, "dev_floor": 1e-6},
+       "f64": {"order": 1e-12, "r100": 1e-5, "dev_floor": 1e-6}}
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -60,8 +71,14 @@ def _full_tokens(chunks, q):
     return np.concatenate([chunks[c][0] for c in order] + [q])
 
 
+@PREC
 @pytest.mark.parametrize("shape_name", ["gqa", "tiny"])
-def test_r100_equals_full_prefill(shape_name):
+def test_r100_equals_full_prefill(shape_name, prec):
+    with precision(prec):
+        _r100(shape_name, TOL[prec]["r100"])
+
+
+def _r100(shape_name, tol):
     if shape_name == "gqa":
         m, chunks, q = _setup(GQA, [20, 13, 17], [5, 0, 31], [17, 37, 0], 6, 1)
     else:
@@ -75,14 +92,20 @@ def test_r100_equals_full_prefill(shape_name):
     ks, ch = _sched(m.n_layers, N, N)
     b = blend_prefill(m, chunks, q, ks, ch)
     f = full_prefill(m, _full_tokens(chunks, q), 0)
-    assert _rel(b["K"], f["K"]) < 1e-5
-    assert _rel(b["V"], f["V"]) < 1e-5
-    assert _rel(b["logits"], f["logits"]) < 1e-5
+    assert _rel(b["K"], f["K"]) < tol
+    assert _rel(b["V"], f["V"]) < tol
+    assert _rel(b["logits"], f["logits"]) < tol
     for l in range(1, m.n_layers):
         assert b["sets"][l].tolist() == list(range(N))
 
 
-def test_r0_equals_concatenation_and_full_reuse():
+@PREC
+def test_r0_equals_concatenation_and_full_reuse(prec):
+    with precision(prec):
+        _r0(TOL[prec]["order"])
+
+
+def _r0(tol):
     m, chunks, q = _setup(GQA, [20, 13, 17], [5, 0, 31], [17, 37, 0], 6, 2)
     N = 50
     ks, ch = _sched(m.n_layers, N, 0)
@@ -91,47 +114,64 @@ def test_r0_equals_concatenation_and_full_reuse():
     assert np.array_equal(b["K"][:, :N], Kc[:, :N])     # bitwise
     assert np.array_equal(b["V"][:, :N], Vc[:, :N])
     r = full_reuse_prefill(m, Kc, Vc, q)
-    assert _rel(b["logits"], r["logits"]) < 1e-12
-    assert _rel(b["K"], r["K"]) < 1e-12
+    assert _rel(b["logits"], r["logits"]) < tol
+    assert _rel(b["K"], r["K"]) < tol
     # and the reuse really differs from the full prefill (cross-chunk attention is missing)
     f = full_prefill(m, _full_tokens(chunks, q), 0)
     assert _rel(r["logits"], f["logits"]) > 1e-3
 
 
+@PREC
 @pytest.mark.parametrize("ratio", [0.0, 0.15, 0.5, 1.0])
-def test_single_chunk_prefix_reuse(ratio):
+def test_single_chunk_prefix_reuse(ratio, prec):
+    with precision(prec):
+        _single_chunk(ratio, TOL[prec]["r100"], TOL[prec]["dev_floor"])
+
+
+def _single_chunk(ratio, tol, dev_floor):
     m, chunks, q = _setup(GQA, [40], [0], [0], 5, 3)
     N = 40
     k = cbinputs.recompute_count(ratio, N)
     ks, ch = _sched(m.n_layers, N, k)
     b = blend_prefill(m, chunks, q, ks, ch)
     f = full_prefill(m, _full_tokens(chunks, q), 0)
-    assert _rel(b["K"], f["K"]) < 1e-5
-    assert _rel(b["V"], f["V"]) < 1e-5
-    assert _rel(b["logits"], f["logits"]) < 1e-5
-    # every deviation is at the level of storage rounding
+    assert _rel(b["K"], f["K"]) < tol
+    assert _rel(b["V"], f["V"]) < tol
+    assert _rel(b["logits"], f["logits"]) < tol
+    # every deviation is at the level of rounding (fp32 storage: the cache holds what a
+    # recomputation gives, up to the order of the sums)
     for l, (cand, dev) in b["devs"].items():
         if len(cand) == 0:
             continue
         scale = np.mean(np.sum(b["K"][l, cand] ** 2, axis=(1, 2)) + np.sum(b["V"][l, cand] ** 2, axis=(1, 2)))
-        assert np.max(dev) <= 1e-6 * scale
+        assert np.max(dev) <= dev_floor * scale
 
 
-def test_rerope_of_chunk_prefill_is_position_shift():
+@PREC
+def test_rerope_of_chunk_prefill_is_position_shift(prec):
     # a chunk prefilled at p, re-RoPE'd by -p, equals the same chunk prefilled at 0
     shape = GQA.with_dtype("f64")
     w = _sharpen(cbinputs.model_weights(shape, 4))
     m = OracleModel.from_shape(shape, w)
     toks = np.random.default_rng(4).integers(0, shape.vocab, size=30)
-    K0, V0 = chunk_prefill(m, toks, 0)
-    Kp, Vp = chunk_prefill(m, toks, 777)
     from oracle import rerope
-    assert _rel(rerope(Kp, -777, shape.rope_theta, "f64"), K0) < 1e-10
-    assert _rel(Vp, V0) < 1e-10
+    with precision(prec):
+        K0, V0 = chunk_prefill(m, toks, 0)
+        Kp, Vp = chunk_prefill(m, toks, 777)
+        back = rerope(Kp, -777, shape.rope_theta, "f64")
+    tol = 1e-5 if prec == "f32" else 1e-10
+    assert _rel(back, K0) < tol
+    assert _rel(Vp, V0) < tol
     assert _rel(Kp, K0) > 1e-2        # the stored keys do carry their position
 
 
-def test_sets_nest_and_masked_twin_agrees():
+@PREC
+def test_sets_nest_and_masked_twin_agrees(prec):
+    with precision(prec):
+        _twin(TOL[prec]["order"])
+
+
+def _twin(tol):
     m, chunks, q = _setup(GQA, [20, 13, 17], [5, 0, 31], [17, 37, 0], 6, 5)
     N = 50
     ks = [N, 30, 22]
@@ -147,19 +187,21 @@ def test_sets_nest_and_masked_twin_agrees():
         assert np.all(s < N)
         assert s.tolist() == t["sets"][l].tolist()
         prev = set(s.tolist())
-    assert _rel(b["K"], t["K"]) < 1e-12
-    assert _rel(b["V"], t["V"]) < 1e-12
-    assert _rel(b["logits"], t["logits"]) < 1e-12
+    assert _rel(b["K"], t["K"]) < tol
+    assert _rel(b["V"], t["V"]) < tol
+    assert _rel(b["logits"], t["logits"]) < tol
     for l in b["devs"]:
-        np.testing.assert_allclose(b["devs"][l][1], t["devs"][l][1], rtol=1e-12)
+        np.testing.assert_allclose(b["devs"][l][1], t["devs"][l][1], rtol=100 * tol)
 
 
-def test_selected_rows_get_fresh_kv_others_keep_cache():
+@PREC
+def test_selected_rows_get_fresh_kv_others_keep_cache(prec):
     m, chunks, q = _setup(GQA, [20, 13, 17], [5, 0, 31], [17, 37, 0], 6, 6)
     N = 50
     ks, ch = _sched(m.n_layers, N, 8)
-    b = blend_prefill(m, chunks, q, ks, ch)
-    Kc, Vc = assemble_blended(m, chunks, len(q))
+    with precision(prec):
+        b = blend_prefill(m, chunks, q, ks, ch)
+        Kc, Vc = assemble_blended(m, chunks, len(q))
     for l in range(1, m.n_layers):
         s = set(b["sets"][l].tolist())
         others = [j for j in range(N) if j not in s]
@@ -171,11 +213,13 @@ def test_selected_rows_get_fresh_kv_others_keep_cache():
     assert np.array_equal(b["K"][0, :N], Kc[0, :N])
 
 
-def test_deviation_is_top_ranked_set():
+@PREC
+def test_deviation_is_top_ranked_set(prec):
     m, chunks, q = _setup(GQA, [20, 13, 17], [5, 0, 31], [17, 37, 0], 6, 7)
     N = 50
     ks, ch = _sched(m.n_layers, N, 10)
-    b = blend_prefill(m, chunks, q, ks, ch)
+    with precision(prec):
+        b = blend_prefill(m, chunks, q, ks, ch)
     cand, dev = b["devs"][1]
     thr = np.sort(dev)[::-1][9]
     chosen = set(b["sets"][1].tolist())
@@ -211,9 +255,15 @@ def test_kv_bytes_per_token_golden():
     assert cbinputs.SHAPES["llama3-8b"].kv_bytes_per_token() == 128 * 1024
 
 
-def test_blend_layer_out_rows_are_rows_of_the_full_call():
+@PREC
+def test_blend_layer_out_rows_are_rows_of_the_full_call(prec):
+    with precision(prec):
+        _out_rows(TOL[prec]["order"])
+
+
+def _out_rows(tol):
     # a row's output depends on its own hidden state and the updated cache
-    # only, so computing a subset must return exactly those rows
+    # only, so computing a subset must return those rows (up to the order of sums)
     w = _sharpen(cbinputs.model_weights(GQA, 9))
     m = OracleModel.from_shape(GQA, w)
     rng = np.random.default_rng(9)
@@ -228,13 +278,19 @@ def test_blend_layer_out_rows_are_rows_of_the_full_call():
     K2, V2 = Kl.copy(), Vl.copy()
     part = blend_layer(m, 1, K2, V2, x, cand, Q, True, k, out_rows=rows)
     assert np.array_equal(part[1], full[1])
-    np.testing.assert_allclose(part[0], full[0][rows], rtol=1e-12, atol=1e-12)
+    assert _rel(part[0], full[0][rows]) < tol
     K3, V3 = Kl.copy(), Vl.copy()
     blend_layer(m, 1, K3, V3, x, cand, Q, True, k)
     assert np.array_equal(K2, K3) and np.array_equal(V2, V3)
 
 
-def test_decode_step_continues_a_full_prefill():
+@PREC
+def test_decode_step_continues_a_full_prefill(prec):
+    with precision(prec):
+        _decode(TOL[prec]["order"])
+
+
+def _decode(tol):
     # causality: the last row of a one-shot prefill over t_0..t_T is a decode step of
     # t_T on the cache the prefill of t_0..t_{T-1} wrote (and writes the same K/V row)
     from oracle import decode_step
@@ -246,13 +302,13 @@ def test_decode_step_continues_a_full_prefill():
     ref = full_prefill(m, toks[:T + 1])
     part = full_prefill(m, toks[:T])
     L, _, H, dh = part["K"].shape
-    Kb = np.zeros((L, T + 3, H, dh))
+    Kb = np.zeros((L, T + 3, H, dh), dtype=part["K"].dtype)
     Vb = np.zeros_like(Kb)
     Kb[:, :T], Vb[:, :T] = part["K"], part["V"]
     lg = decode_step(m, Kb, Vb, int(toks[T]), T)
-    assert _rel(lg, ref["logits"]) < 1e-10
-    assert _rel(Kb[:, T], ref["K"][:, T]) < 1e-12 and _rel(Vb[:, T], ref["V"][:, T]) < 1e-12
+    assert _rel(lg, ref["logits"]) < tol
+    assert _rel(Kb[:, T], ref["K"][:, T]) < tol and _rel(Vb[:, T], ref["V"][:, T]) < tol
     # two more steps equal the prefill over the longer sequence
     decode_step(m, Kb, Vb, int(toks[T + 1]), T + 1)
     lg2 = decode_step(m, Kb, Vb, int(toks[T + 2]), T + 2)
-    assert _rel(lg2, full_prefill(m, toks[:T + 3])["logits"]) < 1e-10
+    assert _rel(lg2, full_prefill(m, toks[:T + 3])["logits"]) < tol

@@ -10,7 +10,12 @@ import torch
 
 import cbinputs
 from oracle.blend import (OracleModel, assemble_blended, blend_prefill, chunk_prefill, fp8_e4m3, full_prefill,
-                          full_reuse_prefill, rerope, store_round)
+                          full_reuse_prefill, precision, rerope, store_round)
+
+# every pin runs in the oracle's float32 and again in float64; ORDER is the bound for
+# two computations that differ only in the order of their sums
+PREC = pytest.mark.parametrize("prec", ["f32", "f64"])
+ORDER = {"f32": 1e-5, "f64": 1e-12}
 
 
 def _grid():
@@ -26,7 +31,13 @@ def _grid():
     return sorted(set(vals))
 
 
-def test_every_grid_value_is_kept_and_midpoints_go_to_even():
+@PREC
+def test_every_grid_value_is_kept_and_midpoints_go_to_even(prec):
+    with precision(prec):
+        _grid_checks()
+
+
+def _grid_checks():
     g = _grid()
     v = np.array([x for x, _ in g])
     assert v[-1] == 448.0 and v[1] == 2.0 ** -9 and len(v) == 127       # +0 and 126 positive values
@@ -40,32 +51,43 @@ def test_every_grid_value_is_kept_and_midpoints_go_to_even():
         assert fp8_e4m3(np.array([a + (b - a) * 0.51]))[0] == b
 
 
-def test_saturation():
+@PREC
+def test_saturation(prec):
     x = np.array([449.0, 464.0, 480.0, 1e6, -500.0, -1e30])
-    assert np.array_equal(fp8_e4m3(x), np.array([448.0, 448.0, 448.0, 448.0, -448.0, -448.0]))
+    with precision(prec):
+        assert np.array_equal(fp8_e4m3(x), np.array([448.0, 448.0, 448.0, 448.0, -448.0, -448.0]))
 
 
-def test_matches_torch_float8_in_range():
+@PREC
+def test_matches_torch_float8_in_range(prec):
     rng = np.random.default_rng(0)
     x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.uniform(-4, 2.6, 20000),
                         rng.uniform(-448, 448, 5000)])
     x = x[np.abs(x) <= 448]
+    if prec == "f32":
+        x = x.astype(np.float32)
     ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
-    assert np.array_equal(fp8_e4m3(x), ref)
+    with precision(prec):
+        assert np.array_equal(fp8_e4m3(x), ref)
 
 
-def test_store_round_scale():
+@PREC
+def test_store_round_scale(prec):
     rng = np.random.default_rng(1)
     x = rng.standard_normal(1000) * 3
-    for s in (1.0, 0.25, 1 / 64):                                          # powers of two: exact
-        y = store_round(x, "fp8", s)
-        assert np.array_equal(y / s, fp8_e4m3(x / s))
-        assert np.array_equal(store_round(y, "fp8", s), y)                  # idempotent on the grid
-    y = store_round(x, "fp8", 0.013)
-    assert np.allclose(y / 0.013, fp8_e4m3(x / 0.013), rtol=1e-12, atol=0)
-    # 3 mantissa bits: half a step is at most 2^-4 of the value in the normal range
-    xn = x[np.abs(x / (1 / 16)) >= 2.0 ** -6]
-    assert np.max(np.abs(store_round(xn, "fp8", 1 / 16) - xn) / np.abs(xn)) <= 2.0 ** -4 + 1e-12
+    dt = np.float32 if prec == "f32" else np.float64
+    x = x.astype(dt)
+    with precision(prec):
+        for s in (1.0, 0.25, 1 / 64):                                      # powers of two: exact
+            y = store_round(x, "fp8", s)
+            assert np.array_equal(y / dt(s), fp8_e4m3(x / dt(s)))
+            assert np.array_equal(store_round(y, "fp8", s), y)              # idempotent on the grid
+        y = store_round(x, "fp8", 0.013)
+        # the grid value times the scale, rounded once in the compute precision
+        assert np.array_equal(y, fp8_e4m3(x / dt(0.013)) * dt(0.013))
+        # 3 mantissa bits: half a step is at most 2^-4 of the value in the normal range
+        xn = x[np.abs(x / dt(1 / 16)) >= 2.0 ** -6]
+        assert np.max(np.abs(store_round(xn, "fp8", 1 / 16) - xn) / np.abs(xn)) <= 2.0 ** -4 + 1e-12
 
 
 def _fp8_model(shape, seed, ks, vs):
@@ -90,7 +112,13 @@ def _chunks(m, lens, old, new, nq, seed):
 GQA = cbinputs.ModelShape("gqa-small", 3, 64, 4, 2, 16, 96, 101, 10000.0, dtype="f32")
 
 
-def test_chunk_cache_is_on_the_fp8_grid():
+@PREC
+def test_chunk_cache_is_on_the_fp8_grid(prec):
+    with precision(prec):
+        _on_grid()
+
+
+def _on_grid():
     m = _fp8_model(GQA, 2, 1 / 32, 1 / 128)
     chunks, _ = _chunks(m, [20], [3], [0], 0, 2)
     K, V = chunks[0][1], chunks[0][2]
@@ -99,7 +127,13 @@ def test_chunk_cache_is_on_the_fp8_grid():
     assert len(np.unique(np.abs(K / m.k_scale))) <= 127
 
 
-def test_fp8_r0_is_rerope_concatenation_and_full_reuse():
+@PREC
+def test_fp8_r0_is_rerope_concatenation_and_full_reuse(prec):
+    with precision(prec):
+        _fp8_r0(ORDER[prec])
+
+
+def _fp8_r0(tol):
     m = _fp8_model(GQA, 3, 1 / 32, 1 / 128)
     chunks, q = _chunks(m, [20, 13, 17], [5, 0, 31], [17, 37, 0], 6, 3)
     N = 50
@@ -112,11 +146,17 @@ def test_fp8_r0_is_rerope_concatenation_and_full_reuse():
     for t, K, V, p, n in chunks:
         assert np.array_equal(Kc[:, n:n + len(t)], rerope(K, n - p, m.rope_theta, "fp8", m.k_scale))
     r = full_reuse_prefill(m, Kc, Vc, q)
-    assert np.max(np.abs(b["logits"] - r["logits"])) <= 1e-12 * np.max(np.abs(r["logits"]))
+    assert np.max(np.abs(b["logits"] - r["logits"])) <= tol * np.max(np.abs(r["logits"]))
 
 
+@PREC
 @pytest.mark.parametrize("ratio", [0.0, 0.5, 1.0])
-def test_fp8_single_chunk_prefix_reuse_equals_full_prefill(ratio):
+def test_fp8_single_chunk_prefix_reuse_equals_full_prefill(ratio, prec):
+    with precision(prec):
+        _fp8_single(ratio, ORDER[prec])
+
+
+def _fp8_single(ratio, tol):
     # one chunk reused at the offset it was stored at: the re-RoPE rotates by 0, which
     # leaves grid values on the grid, so every stored K/V is what a full prefill stores
     m = _fp8_model(GQA, 5, 1 / 32, 1 / 128)
@@ -126,12 +166,12 @@ def test_fp8_single_chunk_prefix_reuse_equals_full_prefill(ratio):
     b = blend_prefill(m, chunks, q, [N, k, k], [0, 1, 1])
     f = full_prefill(m, np.concatenate([chunks[0][0], q]), 0)
     assert np.array_equal(b["K"], f["K"]) and np.array_equal(b["V"], f["V"])
-    assert np.max(np.abs(b["logits"] - f["logits"])) <= 1e-9 * np.max(np.abs(f["logits"]))
+    assert np.max(np.abs(b["logits"] - f["logits"])) <= max(tol, 1e-9) * np.max(np.abs(f["logits"]))
     # the fresh values are unrounded, so a deviation is the cache's own rounding error:
     # at most half a step per element (2^-4 of the value, or half the subnormal step)
     for l, (cand, dev) in b["devs"].items():
         n_el = f["K"].shape[2] * f["K"].shape[3]
         bound = 2.0 ** -8 * (np.sum(f["K"][l, cand] ** 2, axis=(1, 2)) + np.sum(f["V"][l, cand] ** 2, axis=(1, 2))) \
             + n_el * ((2.0 ** -10 * m.k_scale) ** 2 + (2.0 ** -10 * m.v_scale) ** 2)
-        assert np.all(dev <= bound * (1 + 1e-9))
+        assert np.all(dev <= bound * (1 + max(tol, 1e-9)))
         assert len(dev) == 0 or np.max(dev) > 0

@@ -290,16 +290,22 @@ def cb_workspace_bytes(cfg: cb_model_cfg, n_ctx: int, n_query: int, n_chunks: in
     return int(_abi.load().cb_workspace_bytes(ctypes.byref(cfg), n_ctx, n_query, n_chunks))
 
 
-def _ws(ws: Optional[Workspace], need: int, device) -> Workspace:
+def _ws(ws: Optional[Workspace], need: int, device, stream=None) -> Workspace:
+    """The caller's workspace, or a temporary one.  A temporary workspace is freed
+    when the call returns, while the kernels may still run: it is marked as used
+    on the call's stream, so the caching allocator hands its memory out again only
+    after that stream's work up to this point has finished."""
     if ws is None or ws.nbytes < need:
         ws = Workspace(need, device)
+        if stream is not None:
+            ws.t.record_stream(stream)
     return ws
 
 
 def cb_rerope_k(cfg: cb_model_cfg, chunks: Sequence[ChunkSource], dst: PagedKV, flags: int = CB_COPY_V,
                 ws: Optional[Workspace] = None, stream=None) -> None:
     lib = _abi.load()
-    w = _ws(ws, cb_workspace_bytes(cfg, 0, 0, len(chunks)), dst.k.device)
+    w = _ws(ws, cb_workspace_bytes(cfg, 0, 0, len(chunks)), dst.k.device, stream)
     arr = _chunk_array(chunks)
     _check(lib.cb_rerope_k(ctypes.byref(cfg), arr, len(chunks), ctypes.byref(dst.c), flags, w.ptr, w.nbytes,
                            _stream(stream)), "cb_rerope_k")
@@ -327,7 +333,7 @@ def cb_blend_layer(model: DeviceModel, layer: int, kv: PagedKV, pos_in: torch.Te
                    x: torch.Tensor, check_flag: bool, k_keep: int, pos_out: torch.Tensor,
                    dev_out: Optional[torch.Tensor] = None, ws: Optional[Workspace] = None, stream=None) -> None:
     lib = _abi.load()
-    w = _ws(ws, cb_workspace_bytes(model.cfg, n_ctx, n_query, 0), x.device)
+    w = _ws(ws, cb_workspace_bytes(model.cfg, n_ctx, n_query, 0), x.device, stream)
     _check(lib.cb_blend_layer(ctypes.byref(model.c), layer, ctypes.byref(kv.c), _p(pos_in), int(pos_in.numel()),
                               n_ctx, n_query, _p(x), int(bool(check_flag)), int(k_keep), _p(pos_out), _p(dev_out),
                               w.ptr, w.nbytes, _stream(stream)), "cb_blend_layer")
@@ -361,7 +367,7 @@ def cb_blend_prefill_streamed(model: DeviceModel, chunks: Sequence[HostChunk], q
     lib = _abi.load()
     n_ctx = sum(c.len for c in chunks)
     w = _ws(ws, cb_streamed_workspace_bytes(model.cfg, n_ctx, int(query_tokens.numel()), len(chunks)),
-            logits.device)
+            logits.device, stream)
     arr = (cb_host_chunk * max(1, len(chunks)))()
     for i, c in enumerate(chunks):
         arr[i] = c.c()
@@ -383,7 +389,7 @@ def cb_decode_step(model: DeviceModel, kv: PagedKV, pos: int, token: torch.Tenso
                    ws: Optional[Workspace] = None, stream=None) -> None:
     """One token at position `pos` through every layer over the cache [0, pos); its K/V land at pos."""
     lib = _abi.load()
-    w = _ws(ws, cb_decode_workspace_bytes(model.cfg), logits.device)
+    w = _ws(ws, cb_decode_workspace_bytes(model.cfg), logits.device, stream)
     _check(lib.cb_decode_step(ctypes.byref(model.c), ctypes.byref(kv.c), int(pos), _p(token), _p(logits), w.ptr,
                               w.nbytes, _stream(stream)), "cb_decode_step")
 
@@ -394,7 +400,7 @@ def cb_blend_prefill(model: DeviceModel, chunks: Sequence[ChunkSource], query_to
                      ws: Optional[Workspace] = None, stream=None, _arr=None) -> None:
     lib = _abi.load()
     n_ctx = sum(c.len for c in chunks)
-    w = _ws(ws, cb_workspace_bytes(model.cfg, n_ctx, int(query_tokens.numel()), len(chunks)), logits.device)
+    w = _ws(ws, cb_workspace_bytes(model.cfg, n_ctx, int(query_tokens.numel()), len(chunks)), logits.device, stream)
     arr = _arr if _arr is not None else _chunk_array(chunks)
     _check(lib.cb_blend_prefill(ctypes.byref(model.c), arr, len(chunks), _p(query_tokens),
                                 int(query_tokens.numel()), ctypes.byref(params.c), ctypes.byref(blended.c),
@@ -459,7 +465,7 @@ def cb_blend_match(index: BlendIndexImage, query_tokens: torch.Tensor, query_sta
                "cur_st": torch.empty((n, max_matches), dtype=torch.int32, device=dev),
                "kept": torch.empty((n, max_matches), dtype=torch.uint8, device=dev),
                "count": torch.empty(max(n, 0), dtype=torch.int32, device=dev)}
-    w = _ws(ws, cb_blend_match_workspace_bytes(total_tokens), dev)
+    w = _ws(ws, cb_blend_match_workspace_bytes(total_tokens), dev, stream)
     _check(lib.cb_blend_match(_p(index.dev), ctypes.byref(index.info), _p(query_tokens), _p(query_starts), n,
                               int(total_tokens), int(max_query_len), int(probe_stride), _p(prefix_lens),
                               int(max_matches), _p(out["chunk"]), _p(out["old_st"]), _p(out["cur_st"]),

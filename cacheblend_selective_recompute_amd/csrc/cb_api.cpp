@@ -377,7 +377,8 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
     g.blend = 1;
     g.blend_layer = l;
     g.blend_cache = kv;
-    g.blend_nc = check ? nc : 0;
+    g.blend_nc = nc;
+    g.blend_check = check;
     g.blend_dev = io.dev_slot ? io.dev_slot : w.dev;
     g.blend_dev_by_pos = io.dev_by_pos;
     g.blend_gmap = w.gmap;
@@ -772,6 +773,11 @@ cb_status blend_run(const cb_model* model, const cb_chunk* chunks, int32_t n_chu
   if (!feed) {
     if ((st = enqueue_rerope(c, chunks, n_chunks, *blended, 1, w.dtab, s, tr)) != CB_OK) return st;
   } else {
+    // the ring may still be read by work enqueued earlier on the compute stream (a
+    // previous call with the same workspace): the copy stream starts after it.  The
+    // consumed event of layer 0 is free until feed_layer(0) records it again.
+    if (hipEventRecord(feed->ev[feed->L], s) != hipSuccess || hipStreamWaitEvent(feed->copy, feed->ev[feed->L], 0) != hipSuccess)
+      return fail(CB_ERR_DEVICE, "copy stream: wait for earlier work on the compute stream");
     for (int l = 0; l < feed->S; ++l)
       if ((st = feed_copy(*feed, l)) != CB_OK) return st;
   }

@@ -447,8 +447,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int spli
 // workgroup per row writes the row maps of the (identity) top-k, sums the partials
 // in split order, rotates Q and K at the
 // row's position, stores Q (bf16), and for the K/V columns reads the cached row,
-// adds the squared differences (candidate rows only; per thread in column
-// order, then across the workgroup in a fixed order) and writes the fresh
+// adds the squared differences (candidate rows of a checked layer only; per
+// thread in column order, then across the workgroup in a fixed order) and writes the fresh
 // values over it (bf16, or FP8 divided by the tensor's scale).  T: the cache's
 // element type.
 template <typename T, int SP>
@@ -465,6 +465,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_blend_kernel(GemmArgs g, int s
   const PagedRef& c = g.blend_cache;
   const int64_t off = static_cast<int64_t>(g.blend_layer) * c.layer_stride + paged_row(c, pos) * kvw;
   const bool cand = row < g.blend_nc;
+  const bool measure = cand && g.blend_check;       // uniform over the workgroup
   if (tid == 0) {                                     // the row maps of an identity top-k
     if (g.blend_gmap) g.blend_gmap[row] = row;
     if (g.blend_rowpos) g.blend_rowpos[row] = pos;
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_blend_kernel(GemmArgs g, int s
     T* dst = static_cast<T*>(isk ? c.k : c.v) + off + e0;
     const float sc = isk ? c.ks : c.vs;
     if constexpr (sizeof(T) == 1) {
-      if (cand) {
+      if (measure) {
         float f[4];
         fp8x4_to_f32(*reinterpret_cast<const uint32_t*>(dst), f);
         const float d0 = v[0] - f[0] * sc, d1 = v[1] - f[1] * sc, d2 = v[2] - f[2] * sc, d3 = v[3] - f[3] * sc;
@@ -516,7 +517,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_blend_kernel(GemmArgs g, int s
       const float is = 1.0f / sc;
       *reinterpret_cast<uint32_t*>(dst) = f32_to_fp8x4(v[0] * is, v[1] * is, v[2] * is, v[3] * is);
     } else {
-      if (cand) {
+      if (measure) {
         const uint2 o = *reinterpret_cast<const uint2*>(dst);
         const float d0 = v[0] - bf2f(static_cast<bf16_t>(o.x & 0xFFFFu)), d1 = v[1] - bf2f(static_cast<bf16_t>(o.x >> 16));
         const float d2 = v[2] - bf2f(static_cast<bf16_t>(o.y & 0xFFFFu)), d3 = v[3] - bf2f(static_cast<bf16_t>(o.y >> 16));
@@ -528,7 +529,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_blend_kernel(GemmArgs g, int s
       *reinterpret_cast<uint2*>(dst) = w;
     }
   }
-  if (!cand) return;                                  // uniform over the workgroup
+  if (!measure) return;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
   if ((tid & 63) == 0) red[tid >> 6] = acc;

@@ -244,10 +244,11 @@ struct GemmArgs {
   int q_cols;
   int rope2_cols;
   // EPI_QKV, optional (blend != 0; bf16 or FP8 cache): every candidate row of the
-  // layer is kept.  When K is split, the reduction then also takes each candidate
-  // row's (rows < blend_nc) squared distance of its fresh K/V from the cached row
-  // at row_pos into blend_dev[row] (and blend_dev_by_pos[pos] when non-null) and
-  // writes every row's fresh K/V into that row of the cache instead of into C2;
+  // layer is kept.  When K is split, the reduction then also takes, if
+  // blend_check, each candidate row's (rows < blend_nc) squared distance of its
+  // fresh K/V from the cached row at row_pos into blend_dev[row] (and
+  // blend_dev_by_pos[pos] when non-null), and writes every row's fresh K/V into
+  // that row of the cache instead of into C2;
   // launch_gemm reports whether it did (if not, C2 holds them as usual).  Keeping
   // every candidate, the top-k is the identity, so the same reduction also writes
   // the layer's row maps: row r's source row (r) into blend_gmap and position into
@@ -256,6 +257,7 @@ struct GemmArgs {
   int blend;
   int blend_layer;
   int blend_nc;
+  int blend_check;
   PagedRef blend_cache;
   float* blend_dev;
   float* blend_dev_by_pos;

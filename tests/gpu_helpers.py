@@ -132,3 +132,32 @@ def fp8_close(g, o, scale, label, min_equal=0.97):
     say(f"  {label}: {eq:.4f} of the elements equal, all within one grid step: {bool(ok.all())}")
     assert ok.all(), f"{label}: {int((~ok).sum())} elements beyond one grid step"
     assert eq >= min_equal, f"{label}: only {eq:.4f} equal"
+
+
+def host_layer(t, shape):
+    """Oracle-layout fp32 host copies of a library-layout (unpacked) layer."""
+    qw, kvw, F = shape.q_width, shape.kv_width, shape.d_ff
+    h = lambda x: x.float().cpu().numpy()
+    qkv = h(t["w_qkv"])
+    gu = h(t["w_gate_up"])
+    return {"wq": qkv[:qw], "wk": qkv[qw:qw + kvw], "wv": qkv[qw + kvw:], "wo": h(t["w_o"]),
+            "w_gate": gu[:F], "w_up": gu[F:], "w_down": h(t["w_down"]),
+            "attn_norm": h(t["attn_norm"]), "mlp_norm": h(t["mlp_norm"])}
+
+
+def paged_chunks(shape, wl, kvs, seed):
+    """Chunk sources whose device K/V ([L][len][Hkv][dh] each) are moved into
+    private pools of 16-token blocks under random block lists."""
+    out = []
+    for c, (K, V) in enumerate(kvs):
+        ln = wl.chunk_lens[c]
+        nb = (ln + 15) // 16
+        ids, n_phys = cbinputs.paged_layout(ln, 16, seed, key=1000 + c, spare_blocks=2)
+        Kp = torch.zeros((shape.n_layers, n_phys * 16, shape.n_kv_heads, shape.head_dim), dtype=K.dtype, device=DEV)
+        Vp = torch.zeros_like(Kp)
+        rows = torch.from_numpy((np.repeat(ids.astype(np.int64), 16) * 16 + np.tile(np.arange(16), nb))[:ln]).to(DEV)
+        Kp[:, rows] = K
+        Vp[:, rows] = V
+        out.append(api.ChunkSource(ints(wl.chunk_tokens[c]), Kp, Vp, wl.old_starts[c], wl.new_starts[c],
+                                   block_ids=ints(ids), block_size=16, layer_stride=n_phys * 16 * shape.kv_width))
+    return out

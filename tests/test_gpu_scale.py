@@ -24,29 +24,20 @@ import cbinputs
 import oracle
 from cacheblend_selective_recompute_amd import api
 
-from gpu_helpers import blended_cache, check_sets, fp8_close, ints, rel, say, to_dev, to_np
+from gpu_helpers import (blended_cache, check_sets, fp8_close, host_layer, ints, paged_chunks, rel, say, to_dev,
+                         to_np)
 from oracle.blend import fp8_e4m3
 
 pytestmark = pytest.mark.gpu
 
 
-def _host_layer(t, shape):
-    """Oracle-layout fp32 host copies of a library-layout (unpacked) layer."""
-    qw, kvw, F = shape.q_width, shape.kv_width, shape.d_ff
-    h = lambda x: x.float().cpu().numpy()
-    qkv = h(t["w_qkv"])
-    gu = h(t["w_gate_up"])
-    return {"wq": qkv[:qw], "wk": qkv[qw:qw + kvw], "wv": qkv[qw + kvw:], "wo": h(t["w_o"]),
-            "w_gate": gu[:F], "w_up": gu[F:], "w_down": h(t["w_down"]),
-            "attn_norm": h(t["attn_norm"]), "mlp_norm": h(t["mlp_norm"])}
-
-
-def _layer_sampled(base, N, Q, k, seed, paged, n_sample=24, kv8=None):
-    """kv8 = (k_scale, v_scale): the cache holds FP8 E4M3 (oracle and GPU)."""
+def _layer_sampled(base, N, Q, k, seed, paged, n_sample=24, kv8=None, check=True):
+    """kv8 = (k_scale, v_scale): the cache holds FP8 E4M3 (oracle and GPU).
+    check=False: an unchecked layer (keeps every candidate, measures nothing)."""
     shape = dataclasses.replace(base, n_layers=2, vocab=64)
     T = N + Q
     lt = cbinputs.torch_device_layer(shape, seed)
-    lw = _host_layer(lt, shape)
+    lw = host_layer(lt, shape)
     glob = cbinputs.global_weights(shape, seed)
     m_ora = oracle.OracleModel.from_shape(shape, {"layers": [lw, lw], **glob})
     if kv8:
@@ -74,23 +65,29 @@ def _layer_sampled(base, N, Q, k, seed, paged, n_sample=24, kv8=None):
         kv.v[1, idx] = to_dev(Vc, "bf16")
     xg = torch.from_numpy(x).cuda()
     pos_out = torch.full((k,), -1, dtype=torch.int32, device="cuda")
-    dev = torch.empty(N, device="cuda")
-    api.cb_blend_layer(m_gpu, 1, kv, ints(np.arange(N)), N, Q, xg, True, k, pos_out, dev)
+    dev = torch.full((N,), -1.0, device="cuda")
+    api.cb_blend_layer(m_gpu, 1, kv, ints(np.arange(N)), N, Q, xg, check, k, pos_out, dev)
     torch.cuda.synchronize()
     gpos = pos_out.cpu().numpy()
     assert np.all(np.diff(gpos) > 0) and gpos[0] >= 0 and gpos[-1] < N
+    if not check:
+        assert np.array_equal(gpos, np.arange(N))              # every candidate, in order
+        assert bool((dev == -1.0).all())                        # nothing measured
     # the oracle with the GPU's kept set imposed; its deviations are its own
     rows = np.unique(np.concatenate([np.linspace(0, k - 1, n_sample).astype(np.int64),
                                      k + np.array([0, Q // 2, Q - 1])]))
     Kl = Kc.astype(np.float64)
     Vl = Vc.astype(np.float64)
-    x_ora, keep, dev_ora = oracle.blend_layer(m_ora, 1, Kl, Vl, x.astype(np.float64), np.arange(N), Q, True, k,
-                                              force=gpos, out_rows=rows)
-    own = oracle.select_hkvd(dev_ora, np.arange(N), k)
-    sc = float(np.mean(np.sum(Kc.astype(np.float64) ** 2, axis=(1, 2)) +
-                       np.sum(Vc.astype(np.float64) ** 2, axis=(1, 2))))
-    frac = check_sets(gpos, own, np.arange(N), dev_ora, k, sc, "layer 1")
-    ed = rel(to_np(dev), dev_ora)
+    x_ora, keep, dev_ora = oracle.blend_layer(m_ora, 1, Kl, Vl, x.astype(np.float64), np.arange(N), Q, check, k,
+                                              force=gpos if check else None, out_rows=rows)
+    if check:
+        own = oracle.select_hkvd(dev_ora, np.arange(N), k)
+        sc = float(np.mean(np.sum(Kc.astype(np.float64) ** 2, axis=(1, 2)) +
+                           np.sum(Vc.astype(np.float64) ** 2, axis=(1, 2))))
+        frac = check_sets(gpos, own, np.arange(N), dev_ora, k, sc, "layer 1")
+        ed = rel(to_np(dev), dev_ora)
+    else:
+        frac, ed = 1.0, 0.0
     xo = to_np(xg[torch.from_numpy(rows).cuda()])
     ex = rel(xo, x_ora)
     K1, V1 = kv.logical(T)
@@ -130,6 +127,13 @@ def test_blend_layer_8b_width_keep_all_sampled():
     _layer_sampled(cbinputs.SHAPES["llama3-8b"], 614, 64, 614, seed=7, paged=True)
 
 
+def test_blend_layer_8b_width_unchecked_keep_all_sampled():
+    # an unchecked layer at a shape whose Q/K/V product is split: the reduction writes
+    # the row maps and pos_out of every candidate and measures no deviation
+    say("cb_blend_layer: 8B width, layer 1 unchecked, 614 candidates + 64 query rows, keep all 614, paged")
+    _layer_sampled(cbinputs.SHAPES["llama3-8b"], 614, 64, 614, seed=9, paged=True, check=False)
+
+
 def test_blend_layer_8b_width_keep_all_fp8_sampled():
     say("cb_blend_layer: 8B width, FP8 cache (scales 0.029, 0.037), layer 1 keeping all 614 candidates + 64 rows")
     _layer_sampled(cbinputs.SHAPES["llama3-8b"], 614, 64, 614, seed=8, paged=True, kv8=(0.029, 0.037))
@@ -140,29 +144,12 @@ def test_blend_layer_32k_context_paged_sampled():
     _layer_sampled(cbinputs.SHAPES["llama3-8b"], 32768, 128, 4915, seed=6, paged=True)
 
 
-def _paged_chunks(shape, wl, kvs, seed):
-    """Chunk sources whose K/V sit in private pools of 16-token blocks."""
-    out = []
-    for c, (K, V) in enumerate(kvs):
-        ln = wl.chunk_lens[c]
-        nb = (ln + 15) // 16
-        ids, n_phys = cbinputs.paged_layout(ln, 16, seed, key=1000 + c, spare_blocks=2)
-        Kp = torch.zeros((shape.n_layers, n_phys * 16, shape.n_kv_heads, shape.head_dim), dtype=K.dtype, device="cuda")
-        Vp = torch.zeros_like(Kp)
-        rows = torch.from_numpy((np.repeat(ids.astype(np.int64), 16) * 16 + np.tile(np.arange(16), nb))[:ln]).cuda()
-        Kp[:, rows] = K
-        Vp[:, rows] = V
-        out.append(api.ChunkSource(ints(wl.chunk_tokens[c]), Kp, Vp, wl.old_starts[c], wl.new_starts[c],
-                                   block_ids=ints(ids), block_size=16, layer_stride=n_phys * 16 * shape.kv_width))
-    return out
-
-
 def test_blend_full_32k_paged_properties():
     say("blend: full 8B shape, 32 x 1024 + 128, paged source and destination, r 15% (properties)")
     wl = cbinputs.make_workload("8b-32x1024-q128-paged", seed=0)
     shape = wl.shape
     m = api.DeviceModel.from_tensors(shape, cbinputs.torch_device_weights(shape, 0))
-    chunks = _paged_chunks(shape, wl, cbinputs.torch_device_chunk_kv(shape, wl.chunk_lens, 0), 0)
+    chunks = paged_chunks(shape, wl, cbinputs.torch_device_chunk_kv(shape, wl.chunk_lens, 0), 0)
     T, N = wl.n_total, wl.n_ctx
     kv = blended_cache(shape, T, paged=True, seed=3, fill=0.0)
     ks, ch = wl.schedule()

@@ -12,7 +12,12 @@ of the dominant kernel (its duration measured with HIP events on the library's
 stream during the timed region), a per-kind breakdown from an untimed traced
 step, and the CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps 10] [--warmup 3] [--workload 8b-4x1024-q64] [--ratio 0.15]
+    python bench.py [--steps 10] [--warmup 3] [--workload 70b-4x1024-q64] [--ratio 0.15]
+
+The default workload is the largest that fits one GPU: the 70B-shaped decoder
+(80 layers, d 8192, 64 q / 8 kv heads, F 28672) over 4 chunks x 1024 tokens
+plus a 64-token query.  The 8B 4 x 1024 + 64 and the 8B 32 x 1024 + 128 paged
+workloads are timed after it and reported under "other_workloads".
 """
 from __future__ import annotations
 
@@ -34,12 +39,20 @@ PEAK_F32_TFLOPS = 157.3        # fp32 vector
 MFMA_KINDS = {"gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention"}
 
 
+def log(msg):
+    """Progress on stderr (the JSON line alone goes to stdout)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="8b-4x1024-q64")
+    ap.add_argument("--workload", default="70b-4x1024-q64")
+    ap.add_argument("--other-workloads", default="8b-4x1024-q64,8b-32x1024-q128-paged",
+                    help="comma-separated workloads timed after the main one (empty: none)")
+    ap.add_argument("--other-steps", type=int, default=5)
     ap.add_argument("--ratio", type=float, default=0.15)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -223,12 +236,38 @@ def match_cpu_baseline(seed, n_sample=4):
                       f"oracle index build {build:.1f} s"}
 
 
-def cpu_baseline(wl, seed):
-    """The oracle on a bounded sample of the same workload: layers 0..2 timed
-    (2 and 3 layers, the difference gives one selective layer), extrapolated to
-    the full depth."""
-    import numpy as np
-    import cbinputs
+def host_layer(t, shape):
+    """fp32 host copies of one library-layout (unpacked) device layer, in the
+    oracle's layout."""
+    qw, kvw, F = shape.q_width, shape.kv_width, shape.d_ff
+    h = lambda x: x.float().cpu().numpy()
+    qkv = h(t["w_qkv"])
+    gu = h(t["w_gate_up"])
+    return {"wq": qkv[:qw], "wk": qkv[qw:qw + kvw], "wv": qkv[qw + kvw:], "wo": h(t["w_o"]),
+            "w_gate": gu[:F], "w_up": gu[F:], "w_down": h(t["w_down"]),
+            "attn_norm": h(t["attn_norm"]), "mlp_norm": h(t["mlp_norm"])}
+
+
+class DeviceRows:
+    """Rows of a device matrix gathered on demand (the oracle reads only the
+    embedding rows of the request's tokens)."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, idx):
+        import numpy as np
+        import torch
+        i = torch.from_numpy(np.asarray(idx, dtype=np.int64)).to(self.t.device)
+        return self.t[i].float().cpu().numpy()
+
+
+def cpu_baseline(wl, sample):
+    """The oracle (float32 NumPy, OpenBLAS sgemm on the host cores) on a bounded
+    sample of the same workload, with the same weights and chunk caches as the
+    GPU run (host copies of the first three layers): layers 0..2 timed (2 and 3
+    layers; the difference gives one selective layer), extrapolated to the full
+    depth."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -238,10 +277,8 @@ def cpu_baseline(wl, seed):
         cores = os.cpu_count()
     L = wl.shape.n_layers
     sh3 = wl.shape.with_layers(3)
-    glob = cbinputs.global_weights(sh3, seed)
-    layers = [cbinputs.layer_weights(sh3, seed, l) for l in range(3)]
-    m = oracle.OracleModel.from_shape(sh3, {"layers": layers, **glob})
-    kvs = cbinputs.synthetic_chunk_kv(sh3, wl.chunk_lens, seed)
+    layers, glob, kvs = sample
+    m = oracle.OracleModel.from_shape(sh3, lambda l: layers[l], glob)
     chunks = [(wl.chunk_tokens[c], kvs[c][0], kvs[c][1], wl.old_starts[c], wl.new_starts[c]) for c in range(len(kvs))]
     ks, ch = wl.schedule()
     times = {}
@@ -252,9 +289,9 @@ def cpu_baseline(wl, seed):
     per_layer = max(times[3] - times[2], 1e-9)
     total = times[3] + (L - 3) * per_layer
     return {"value": wl.n_ctx / total, "unit": "context tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"float64 NumPy oracle, layers 0-2 of the {wl.name} blend timed ({times[3]:.1f} s; "
-                       f"one selective layer {per_layer:.2f} s), extrapolated to {L} layers "
-                       f"({total:.1f} s per request)")}
+            "sample": (f"float32 NumPy oracle (sgemm), layers 0-2 of the {wl.name} blend on the GPU run's own "
+                       f"weights and chunk caches timed ({times[3]:.1f} s; one selective layer {per_layer:.2f} s), "
+                       f"extrapolated to {L} layers ({total:.1f} s per request)")}
 
 
 def measured_peaks(torch, dev):
@@ -452,6 +489,151 @@ def streamed_runs(torch, api, model, chunks, qtok, params, blended, logits, hkvd
             "note": "chunk caches in page-locked host memory, copied layer by layer inside the timed call"}
 
 
+class Inputs:
+    """One workload resident in HBM: packed model, chunk caches, blended cache,
+    tokens, outputs and workspace."""
+
+    def __init__(self, torch, api, wl, seed, dev, host_sample=False):
+        import numpy as np
+        import cbinputs
+        shape = wl.shape
+        N, Q, T = wl.n_ctx, wl.n_query, wl.n_total
+        weights = cbinputs.torch_device_weights(shape, seed, dev)
+        self.sample = None
+        if host_sample:          # the oracle's copy of layers 0..2 before the library packs them
+            layers = [host_layer(weights["layers"][l], shape) for l in range(3)]
+            glob = {"embed": DeviceRows(weights["embed"]), "lm_head": weights["lm_head"].float().cpu().numpy(),
+                    "final_norm": weights["final_norm"].float().cpu().numpy()}
+        self.model = api.DeviceModel.from_tensors(shape, weights)
+        del weights
+        kvs = cbinputs.torch_device_chunk_kv(shape, wl.chunk_lens, seed, dev)
+        if host_sample:
+            self.sample = (layers, glob, [(k[:3].float().cpu().numpy(), v[:3].float().cpu().numpy()) for k, v in kvs])
+        ints = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+        if wl.paged:
+            chunks = []
+            for c, (K, V) in enumerate(kvs):
+                ln = wl.chunk_lens[c]
+                nb = (ln + 15) // 16
+                ids, n_phys = cbinputs.paged_layout(ln, 16, seed, key=1000 + c, spare_blocks=2)
+                Kp = torch.zeros((shape.n_layers, n_phys * 16, shape.n_kv_heads, shape.head_dim), dtype=K.dtype,
+                                 device=dev)
+                Vp = torch.zeros_like(Kp)
+                rows = torch.from_numpy((np.repeat(ids.astype(np.int64), 16) * 16
+                                         + np.tile(np.arange(16), nb))[:ln]).to(dev)
+                Kp[:, rows] = K
+                Vp[:, rows] = V
+                chunks.append(api.ChunkSource(ints(wl.chunk_tokens[c]), Kp, Vp, wl.old_starts[c], wl.new_starts[c],
+                                              block_ids=ints(ids), block_size=16,
+                                              layer_stride=n_phys * 16 * shape.kv_width))
+            del kvs
+            table, n_phys = cbinputs.paged_layout(T + 64, 16, seed, key=77, spare_blocks=8)
+            self.blended = api.PagedKV(shape, T + 64, 16, table, n_phys)
+        else:
+            chunks = [api.ChunkSource(ints(wl.chunk_tokens[c]), kvs[c][0], kvs[c][1], wl.old_starts[c],
+                                      wl.new_starts[c]) for c in range(len(kvs))]
+            self.blended = api.PagedKV(shape, T + 64, 16)   # room for the decode steps after the prefill
+        self.chunks = chunks
+        self.qtok = ints(wl.query_tokens)
+        self.logits = torch.empty(shape.vocab, device=dev)
+        self.hkvd = torch.empty((shape.n_layers, N), dtype=torch.int32, device=dev)
+        self.ws = api.Workspace(api.cb_workspace_bytes(self.model.cfg, N, Q, len(chunks)), dev)
+        self.arr = api._chunk_array(chunks)
+
+    def run(self, api, params):
+        api.cb_blend_prefill(self.model, self.chunks, self.qtok, params, self.blended, self.logits, self.hkvd, None,
+                             self.ws, _arr=self.arr)
+
+
+def time_blend(torch, api, _abi, hip, inp, wl, steps, warmup):
+    """Warm-up (the last warm-up step traced for the per-kind breakdown), then
+    `steps` timed steps with the dominant kind bracketed by events on the
+    library's stream.  Returns (ms_per_step, roofline dict, breakdown, keep-all
+    layer count, fused flag)."""
+    shape = wl.shape
+    N, Q = wl.n_ctx, wl.n_query
+    ks, ch = wl.schedule()
+    plain = api.BlendParams(ks, ch)
+    for _ in range(max(0, warmup - 1)):
+        inp.run(api, plain)
+    cap = 4096 if shape.n_layers <= 40 else 8192
+    ev_all = hip.events(cap)
+    kinds_all = (ctypes.c_int32 * (cap // 2))()
+    tr_all = _abi.cb_trace(ev_all, cap, 0, (1 << len(_abi.KINDS)) - 1, kinds_all)
+    p_all = api.BlendParams(ks, ch)
+    p_all.c.trace = ctypes.pointer(tr_all)
+    inp.run(api, p_all)
+    torch.cuda.synchronize()
+    sets = {l: inp.hkvd[l, :ks[l]].cpu().numpy() for l in range(1, shape.n_layers)}
+    kind_ms, kind_n = {}, {}
+    for i in range(tr_all.used // 2):
+        k = _abi.KINDS[kinds_all[i]]
+        kind_ms[k] = kind_ms.get(k, 0.0) + hip.elapsed_ms(ev_all[2 * i], ev_all[2 * i + 1])
+        kind_n[k] = kind_n.get(k, 0) + 1
+    # one scatter launch per layer, except the layers that keep every candidate when
+    # their Q/K/V reduction wrote the cache
+    keep_all = sum(1 for l in range(1, shape.n_layers) if ks[l] == (N if l == 1 else ks[l - 1]))
+    fused_keep_all = keep_all > 0 and kind_n.get("scatter", 0) == shape.n_layers - keep_all
+    work = work_per_kind(shape, N, Q, ks, sets, wl.chunk_lens, fused_keep_all)
+    dominant = max((k for k in kind_ms if k in work), key=lambda k: kind_ms[k])
+    dom_id = _abi.KINDS.index(dominant)
+
+    per_step = 2 * kind_n[dominant]
+    ev = hip.events(per_step * steps)
+    traces, params = [], []
+    for s in range(steps):
+        sub = ctypes.cast(ctypes.byref(ev, s * per_step * ctypes.sizeof(ctypes.c_void_p)),
+                          ctypes.POINTER(ctypes.c_void_p))
+        t = _abi.cb_trace(sub, per_step, 0, 1 << dom_id, None)
+        p = api.BlendParams(ks, ch)
+        p.c.trace = ctypes.pointer(t)
+        traces.append(t)
+        params.append(p)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        inp.run(api, params[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000.0 / steps
+    dom_ms, launches = 0.0, 0
+    for s in range(steps):
+        for i in range(traces[s].used // 2):
+            dom_ms += hip.elapsed_ms(ev[s * per_step + 2 * i], ev[s * per_step + 2 * i + 1])
+            launches += 1
+    avg_launch_ms = dom_ms / max(launches, 1)
+    work_per_launch = work[dominant] / kind_n[dominant]
+    if dominant in MFMA_KINDS:
+        peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
+        achieved = work_per_launch / (avg_launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "unit": "TFLOP/s"}
+    else:
+        peak = PEAK_HBM_GBS
+        achieved = work_per_launch / (avg_launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "unit": "GB/s"}
+    roof.update({"kernel": dominant, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
+                 "traffic": traffic_from_profile(dominant, wl.name), "launches_per_step": kind_n[dominant],
+                 "avg_launch_ms": round(avg_launch_ms, 4), "work_per_launch": work_per_launch})
+    breakdown = {}
+    for k, ms in sorted(kind_ms.items(), key=lambda kv: -kv[1]):
+        e = {"ms": round(ms, 4), "launches": kind_n[k]}
+        if k in work and ms > 0:
+            if k in MFMA_KINDS:
+                e["tflops"] = round(work[k] / (ms * 1e-3) / 1e12, 1)
+            else:
+                e["gbs"] = round(work[k] / (ms * 1e-3) / 1e9, 1)
+        breakdown[k] = e
+    return ms_per_step, roof, breakdown, keep_all, fused_keep_all
+
+
+def config_of(wl, ratio, n_chunks):
+    shape = wl.shape
+    return {"workload": wl.name, "shape": f"{shape.n_layers}L d{shape.d_model} {shape.n_q_heads}q/"
+                                          f"{shape.n_kv_heads}kv x{shape.head_dim} F{shape.d_ff}",
+            "n_ctx": wl.n_ctx, "n_query": wl.n_query, "chunks": n_chunks, "ratio": ratio, "k": wl.k,
+            "paged": bool(wl.paged), "block_size": 16}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -484,104 +666,13 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    weights = cbinputs.torch_device_weights(shape, args.seed, dev)
-    model = api.DeviceModel.from_tensors(shape, weights)
-    kvs = cbinputs.torch_device_chunk_kv(shape, wl.chunk_lens, args.seed, dev)
-    ints = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
-    if wl.paged:
-        chunks = []
-        for c, (K, V) in enumerate(kvs):
-            ln = wl.chunk_lens[c]
-            nb = (ln + 15) // 16
-            ids, n_phys = cbinputs.paged_layout(ln, 16, args.seed, key=1000 + c, spare_blocks=2)
-            Kp = torch.zeros((shape.n_layers, n_phys * 16, shape.n_kv_heads, shape.head_dim), dtype=K.dtype, device=dev)
-            Vp = torch.zeros_like(Kp)
-            rows = torch.from_numpy((np.repeat(ids.astype(np.int64), 16) * 16 + np.tile(np.arange(16), nb))[:ln]).to(dev)
-            Kp[:, rows] = K
-            Vp[:, rows] = V
-            chunks.append(api.ChunkSource(ints(wl.chunk_tokens[c]), Kp, Vp, wl.old_starts[c], wl.new_starts[c],
-                                          block_ids=ints(ids), block_size=16,
-                                          layer_stride=n_phys * 16 * shape.kv_width))
-        del kvs
-        table, n_phys = cbinputs.paged_layout(T + 64, 16, args.seed, key=77, spare_blocks=8)
-        blended = api.PagedKV(shape, T + 64, 16, table, n_phys)
-    else:
-        chunks = [api.ChunkSource(ints(wl.chunk_tokens[c]), kvs[c][0], kvs[c][1], wl.old_starts[c], wl.new_starts[c])
-                  for c in range(len(kvs))]
-        blended = api.PagedKV(shape, T + 64, 16)   # room for the decode steps after the prefill
-    qtok = ints(wl.query_tokens)
-    logits = torch.empty(shape.vocab, device=dev)
-    hkvd = torch.empty((shape.n_layers, N), dtype=torch.int32, device=dev)
-    ws = api.Workspace(api.cb_workspace_bytes(model.cfg, N, Q, len(chunks)), dev)
-    arr = api._chunk_array(chunks)
     hip = Hip()
-
-    def run(params):
-        api.cb_blend_prefill(model, chunks, qtok, params, blended, logits, hkvd, None, ws, _arr=arr)
-
+    log(f"{wl.name}: weights, chunk caches and buffers")
+    inp = Inputs(torch, api, wl, args.seed, dev, host_sample=not args.no_cpu_baseline)
+    log(f"{wl.name}: {args.warmup} warm-up and {args.steps} timed steps")
+    ms_per_step, roof, breakdown, keep_all, fused_keep_all = time_blend(torch, api, _abi, hip, inp, wl, args.steps,
+                                                                         args.warmup)
     plain = api.BlendParams(ks, ch)
-
-    # warmup; the last warmup step traces every launch kind for the breakdown
-    for _ in range(max(0, args.warmup - 1)):
-        run(plain)
-    cap = 4096
-    ev_all = hip.events(cap)
-    kinds_all = (ctypes.c_int32 * (cap // 2))()
-    tr_all = _abi.cb_trace(ev_all, cap, 0, (1 << len(_abi.KINDS)) - 1, kinds_all)
-    p_all = api.BlendParams(ks, ch)
-    p_all.c.trace = ctypes.pointer(tr_all)
-    run(p_all)
-    torch.cuda.synchronize()
-    sets = {l: hkvd[l, :ks[l]].cpu().numpy() for l in range(1, shape.n_layers)}
-    kind_ms = {}
-    kind_n = {}
-    for i in range(tr_all.used // 2):
-        k = _abi.KINDS[kinds_all[i]]
-        kind_ms[k] = kind_ms.get(k, 0.0) + hip.elapsed_ms(ev_all[2 * i], ev_all[2 * i + 1])
-        kind_n[k] = kind_n.get(k, 0) + 1
-    # one scatter launch per layer, except the layers that keep every candidate when
-    # their Q/K/V reduction wrote the cache
-    keep_all = sum(1 for l in range(1, shape.n_layers) if ks[l] == (N if l == 1 else ks[l - 1]))
-    fused_keep_all = keep_all > 0 and kind_n.get("scatter", 0) == shape.n_layers - keep_all
-    work = work_per_kind(shape, N, Q, ks, sets, wl.chunk_lens, fused_keep_all)
-    dominant = max((k for k in kind_ms if k in work), key=lambda k: kind_ms[k])
-    dom_id = _abi.KINDS.index(dominant)
-
-    # timed region: K steps; the dominant kind is bracketed by events on the library's stream
-    per_step = 2 * kind_n[dominant]
-    ev = hip.events(per_step * args.steps)
-    traces, params = [], []
-    for s in range(args.steps):
-        sub = ctypes.cast(ctypes.byref(ev, s * per_step * ctypes.sizeof(ctypes.c_void_p)),
-                          ctypes.POINTER(ctypes.c_void_p))
-        t = _abi.cb_trace(sub, per_step, 0, 1 << dom_id, None)
-        p = api.BlendParams(ks, ch)
-        p.c.trace = ctypes.pointer(t)
-        traces.append(t)
-        params.append(p)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        run(params[s])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1000.0 / args.steps
-    dom_ms = 0.0
-    launches = 0
-    for s in range(args.steps):
-        for i in range(traces[s].used // 2):
-            dom_ms += hip.elapsed_ms(ev[s * per_step + 2 * i], ev[s * per_step + 2 * i + 1])
-            launches += 1
-    avg_launch_ms = dom_ms / max(launches, 1)
-    work_per_launch = work[dominant] / kind_n[dominant]
-    if dominant in MFMA_KINDS:
-        peak = PEAK_BF16_TFLOPS if shape.dtype == "bf16" else PEAK_F32_TFLOPS
-        achieved = work_per_launch / (avg_launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "unit": "TFLOP/s"}
-    else:
-        peak = PEAK_HBM_GBS
-        achieved = work_per_launch / (avg_launch_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "unit": "GB/s"}
     # cold runs: a 512 MiB read between runs evicts the 256 MiB Infinity Cache (the
     # chunk caches and weights then come from HBM, as for a request that just arrived)
     evict = torch.ones(128 << 20, dtype=torch.float32, device=dev)
@@ -590,12 +681,14 @@ def main():
         evict.sum()
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         c0.record()
-        run(plain)
+        inp.run(api, plain)
         c1.record()
         torch.cuda.synchronize()
         cold.append(c0.elapsed_time(c1))
     del evict
+    log(f"{wl.name}: {ms_per_step:.3f} ms per step; measured peaks, decode, matching, FP8, streamed legs")
     peaks = measured_peaks(torch, dev) if args.peaks else None
+    model, chunks, qtok, blended, logits, hkvd = inp.model, inp.chunks, inp.qtok, inp.blended, inp.logits, inp.hkvd
     decode = decode_runs(torch, api, model, shape, blended, logits, T, args.decode_steps) if args.decode_steps else None
     match = match_runs(torch, api, args.seed, args.match_runs) if args.match_runs > 0 else None
     fp8 = fp8_runs(torch, api, model, shape, chunks, qtok, plain, T, N, args.fp8_runs) \
@@ -603,23 +696,26 @@ def main():
     streamed = None
     if args.streamed_runs > 0 and not wl.paged:
         streamed = streamed_runs(torch, api, model, chunks, qtok, plain, blended, logits, hkvd, N, args.streamed_runs)
-
-    roof.update({"kernel": dominant, "achieved": round(achieved, 2), "peak": peak, "frac": round(achieved / peak, 4),
-                 "traffic": traffic_from_profile(dominant, wl.name), "launches_per_step": kind_n[dominant], "avg_launch_ms": round(avg_launch_ms, 4),
-                 "work_per_launch": work_per_launch})
     if peaks:
         mp = peaks["bf16_gemm_tflops"] if roof["bound"] == "mfma" else peaks["copy_gbs"]
-        roof["frac_of_measured_peak"] = round(achieved / mp, 4)
+        roof["frac_of_measured_peak"] = round(roof["achieved"] / mp, 4)
+    sample = inp.sample
+    n_chunks = len(chunks)
+    del inp, model, chunks, qtok, blended, logits, hkvd
+    torch.cuda.empty_cache()
 
-    breakdown = {}
-    for k, ms in sorted(kind_ms.items(), key=lambda kv: -kv[1]):
-        e = {"ms": round(ms, 4), "launches": kind_n[k]}
-        if k in work and ms > 0:
-            if k in MFMA_KINDS:
-                e["tflops"] = round(work[k] / (ms * 1e-3) / 1e12, 1)
-            else:
-                e["gbs"] = round(work[k] / (ms * 1e-3) / 1e9, 1)
-        breakdown[k] = e
+    others = {}
+    for name in [w for w in args.other_workloads.split(",") if w and w != wl.name]:
+        owl = cbinputs.make_workload(name, seed=args.seed, ratio=args.ratio)
+        log(f"{name}: setup and {args.other_steps} timed steps")
+        oinp = Inputs(torch, api, owl, args.seed, dev)
+        oms, oroof, obd, _, _ = time_blend(torch, api, _abi, hip, oinp, owl, args.other_steps, 2)
+        others[name] = {"value": round(owl.n_ctx / (oms * 1e-3), 1), "unit": "context tokens/s",
+                        "ms_per_step": round(oms, 4), "steps": args.other_steps,
+                        "config": config_of(owl, args.ratio, len(oinp.chunks)), "roofline": oroof,
+                        "kernels_ms_per_step": obd}
+        del oinp
+        torch.cuda.empty_cache()
 
     out = {
         "metric": METRIC,
@@ -634,10 +730,7 @@ def main():
         "vs_baseline": None,
         "dtype": shape.dtype,
         "data": "synthetic (seeded random-init weights and chunk caches drawn on the GPU)",
-        "config": {"workload": wl.name, "shape": f"{shape.n_layers}L d{shape.d_model} {shape.n_q_heads}q/"
-                                                   f"{shape.n_kv_heads}kv x{shape.head_dim} F{shape.d_ff}",
-                   "n_ctx": N, "n_query": Q, "chunks": len(chunks), "ratio": args.ratio, "k": ks[1],
-                   "paged": bool(wl.paged), "block_size": 16},
+        "config": config_of(wl, args.ratio, n_chunks),
         "roofline": roof,
         "kernels_ms_per_step": breakdown,
         "deviation_scatter_in_qkv_reduce": {"layers": keep_all if fused_keep_all else 0,
@@ -647,6 +740,7 @@ def main():
         "cold_ms_per_step": ({"median": round(float(np.median(cold)), 4), "min": round(min(cold), 4), "runs": len(cold)}
                              if cold else None),
         "measured_peaks": peaks,
+        "other_workloads": others,
         "streamed": streamed,
         "decode": decode,
         "match": match,
@@ -654,7 +748,8 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.seed)
+        log(f"{wl.name}: oracle on the host cores (layers 0-2)")
+        out["cpu_baseline"] = cpu_baseline(wl, sample)
         if match is not None:
             out["cpu_baseline"]["match"] = match_cpu_baseline(args.seed)
     print(json.dumps(out), flush=True)

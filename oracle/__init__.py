@@ -19,13 +19,15 @@ float32.  Values the method *stores* (the KV cache, in the model's storage
 dtype) are rounded to that dtype (bf16 = round to nearest even) at the point of
 storage, exactly where the method writes them.  ``precision("f64")`` runs the
 same code in float64; the tests use it only as an extra pin.
+``operands("bf16")`` rounds the operands of every matrix product to bf16 (fp32
+sums): the arithmetic of a bf16 model computed with bf16 operands.
 
 Parity status of each function is listed in ``oracle/blend.py``; every function
 there is pinned by at least one test under ``tests/`` that does not re-use the
 oracle's own formulas (library special cases, closed forms, brute force).
 """
 from .blend import (  # noqa: F401
-    OracleModel, precision, ct, store_round, rms_norm, rope_cos_sin, rope, rerope, causal_attention,
+    OracleModel, precision, operands, ct, store_round, rms_norm, rope_cos_sin, rope, rerope, causal_attention,
     swiglu_mlp, kv_deviation, select_hkvd, full_prefill, chunk_prefill,
     assemble_blended, full_reuse_prefill, blend_prefill, blend_prefill_masked,
     blend_layer, flop_count, decode_step,

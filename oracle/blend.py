@@ -16,6 +16,16 @@ to that dtype (bf16: round to nearest even) where the method writes them.
 ``precision("f64")`` runs the same code in float64 (cos/sin unrounded, storage
 rounding straight from float64); the tests use it as an extra pin only.
 
+``operands("bf16")`` is the arithmetic of a bf16 model computed with bf16
+operands and fp32 accumulation: every operand of a matrix product is rounded
+to bf16 first (the normalised rows and the SwiGLU hidden rows going into the
+projections, the attention output going into W_O, the rotated queries, the
+softmax weights going into the product with V, whose normaliser is the sum of
+the same rounded weights), sums and everything else stay float32; the LM head
+multiplies the bf16 weights by the float32 normalised row.  Weights and cached
+K/V of a bf16 model are bf16 values already and are used as they are.  The
+default ("f32") rounds no operand.
+
 Readings taken where the pages are silent (all listed in the design notes):
   * layer 0 runs in full over every row; its context K/V are the re-RoPE'd
     cache (they depend on the token alone); the first checked layer is 1;
@@ -67,6 +77,29 @@ def precision(name: str):
 
 def _a(x) -> np.ndarray:
     return np.asarray(x, dtype=ct())
+
+
+_OPS = ["f32"]              # operand rounding of matrix products (set by ``operands``)
+
+
+@contextlib.contextmanager
+def operands(name: str):
+    """Round the operands of every matrix product to bf16 ("bf16") or not ("f32",
+    the default) inside the block."""
+    if name not in ("f32", "bf16"):
+        raise ValueError(name)
+    old = _OPS[0]
+    _OPS[0] = name
+    try:
+        yield
+    finally:
+        _OPS[0] = old
+
+
+def _op(x) -> np.ndarray:
+    """A matrix-product operand: rounded to bf16 under ``operands("bf16")``."""
+    x = _a(x)
+    return store_round(x, "bf16") if _OPS[0] == "bf16" else x
 
 
 # ----------------------------------------------------------------------------
@@ -224,12 +257,11 @@ def causal_attention(q: np.ndarray, q_pos: np.ndarray, k: np.ndarray, v: np.ndar
         g = (h * Hkv) // Hq
         kk = k[kmask, g, :]
         vv = v[kmask, g, :]
-        s = (q[r0:r1, h, :] @ kk.T) * scale
+        s = (_op(q[r0:r1, h, :]) @ kk.T) * scale
         s = np.where(allowed, s, -np.inf)
         m = np.max(s, axis=1, keepdims=True)
-        p = np.exp(s - m)
-        p /= np.sum(p, axis=1, keepdims=True)
-        out[r0:r1, h, :] = p @ vv
+        p = _op(np.exp(s - m))
+        out[r0:r1, h, :] = (p @ vv) / np.sum(p, axis=1, keepdims=True)
 
     tasks = [(b, h) for b in blocks for h in range(Hq)]
     work = sum(int(b[3].size) for b in blocks) * Hq
@@ -248,12 +280,12 @@ def causal_attention(q: np.ndarray, q_pos: np.ndarray, k: np.ndarray, v: np.ndar
 
 def swiglu_mlp(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
     """W_down (SiLU(a W_gate) * (a W_up)), SiLU(z) = z / (1 + e^-z)."""
-    a = _a(a)
+    a = _op(a)
     g = a @ _a(w_gate).T
     u = a @ _a(w_up).T
     with np.errstate(over="ignore"):         # exp(-g) = inf for g << 0 gives SiLU = -0, its limit
         h = g / (a.dtype.type(1.0) + np.exp(-g)) * u
-    return h @ _a(w_down).T
+    return _op(h) @ _a(w_down).T
 
 
 # ----------------------------------------------------------------------------
@@ -305,12 +337,13 @@ class OracleModel:
 
 
 def _proj(a: np.ndarray, w: np.ndarray) -> np.ndarray:
-    return _a(a) @ _a(w).T
+    return _op(a) @ _a(w).T
 
 
 def _logits(m: OracleModel, x_last: np.ndarray) -> np.ndarray:
+    # a matrix-vector product: the normalised row stays float32 in either operand mode
     a = rms_norm(x_last[None, :], m.glob["final_norm"], m.rms_eps)
-    return _proj(a, m.glob["lm_head"])[0]
+    return (a @ _a(m.glob["lm_head"]).T)[0]
 
 
 # ----------------------------------------------------------------------------

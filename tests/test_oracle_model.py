@@ -231,3 +231,78 @@ def test_attention_worker_threads_change_no_row():
     rows = np.sort(rng.choice(T, size=24, replace=False))
     sub = causal_attention(q[rows], rows, k, v, pos, row_block=3)
     assert _rel(dense[rows], sub) < 1e-6
+
+
+def _torch_bf16_operand_prefill(shape, weights, tokens):
+    """The decoder forward written with torch routines in float64, every operand of a
+    matrix product cast to torch.bfloat16 and back (torch's round to nearest even):
+    normalised rows, rotated queries, softmax weights (normalised by their rounded
+    sum), the attention output, the SwiGLU hidden rows; K and V stored as bf16.  The
+    LM head takes the float64 normalised row."""
+    d = torch.float64
+    bf = lambda t: t.to(torch.bfloat16).to(d)
+    tok = torch.as_tensor(np.asarray(tokens), dtype=torch.long)
+    x = torch.as_tensor(weights["embed"], dtype=d)[tok]
+    n = len(tokens)
+    dh = shape.head_dim
+    pos = torch.arange(n, dtype=d)
+    inv = shape.rope_theta ** (-torch.arange(0, dh, 2, dtype=d) / dh)
+    ang = pos[:, None] * inv[None, :]
+    c32, s32 = torch.cos(ang).float().to(d), torch.sin(ang).float().to(d)
+
+    def rope(t):
+        a0, a1 = t[..., 0::2], t[..., 1::2]
+        out = torch.empty_like(t)
+        out[..., 0::2] = a0 * c32[:, None] - a1 * s32[:, None]
+        out[..., 1::2] = a0 * s32[:, None] + a1 * c32[:, None]
+        return out
+
+    Ks, Vs = [], []
+    G = shape.n_q_heads // shape.n_kv_heads
+    mask = torch.tril(torch.ones(n, n, dtype=torch.bool))
+    for l in range(shape.n_layers):
+        w = {k: torch.as_tensor(v, dtype=d) for k, v in weights["layers"][l].items()}
+        a = bf(F.rms_norm(x, (shape.d_model,), w["attn_norm"], eps=shape.rms_eps))
+        q = bf(rope(F.linear(a, w["wq"]).reshape(n, shape.n_q_heads, dh)))
+        k = bf(rope(F.linear(a, w["wk"]).reshape(n, shape.n_kv_heads, dh)))
+        v = bf(F.linear(a, w["wv"]).reshape(n, shape.n_kv_heads, dh))
+        Ks.append(k.numpy().copy())
+        Vs.append(v.numpy().copy())
+        o = torch.empty(n, shape.n_q_heads, dh, dtype=d)
+        for h in range(shape.n_q_heads):
+            sc = (q[:, h] @ k[:, h // G].T) / np.sqrt(dh)
+            sc = sc.masked_fill(~mask, float("-inf"))
+            p = bf(torch.exp(sc - sc.max(dim=1, keepdim=True).values))
+            o[:, h] = (p @ v[:, h // G]) / p.sum(dim=1, keepdim=True)
+        x = x + F.linear(bf(o.reshape(n, -1)), w["wo"])
+        hn = bf(F.rms_norm(x, (shape.d_model,), w["mlp_norm"], eps=shape.rms_eps))
+        x = x + F.linear(bf(F.silu(F.linear(hn, w["w_gate"])) * F.linear(hn, w["w_up"])), w["w_down"])
+    hl = F.rms_norm(x[-1:], (shape.d_model,), torch.as_tensor(weights["final_norm"], dtype=d), eps=shape.rms_eps)
+    logits = F.linear(hl, torch.as_tensor(weights["lm_head"], dtype=d))[0]
+    return np.stack(Ks), np.stack(Vs), logits.numpy()
+
+
+def test_bf16_operand_mode_rounds_at_the_product_inputs():
+    # The stored K/V are bf16 values: with the operands rounded where the reference rounds
+    # them, almost every stored element is the same bf16 number (a float32-vs-float64 sum
+    # can land on the other side of a rounding boundary now and then); without the
+    # operand rounding, the first layer's products already move many elements by an ulp.
+    from oracle import operands
+    shape = cbinputs.ModelShape("small-bf16", 2, 128, 4, 2, 32, 192, 97, 10000.0, dtype="bf16")
+    w = cbinputs.model_weights(shape, seed=31)
+    for lw in w["layers"]:
+        for k in ("wq", "wk"):
+            lw[k] = cbinputs.to_bf16_values(lw[k] * 8.0)
+    m = OracleModel.from_shape(shape, w)
+    tokens = np.random.default_rng(32).integers(0, shape.vocab, size=48)
+    K, V, logits = _torch_bf16_operand_prefill(shape, w, tokens)
+    with operands("bf16"):
+        ours = full_prefill(m, tokens, 0)
+    plain = full_prefill(m, tokens, 0)
+    for l in range(shape.n_layers):
+        eq = float(np.mean(ours["K"][l] == K[l])), float(np.mean(ours["V"][l] == V[l]))
+        eq_plain = float(np.mean(plain["K"][l] == K[l])), float(np.mean(plain["V"][l] == V[l]))
+        assert min(eq) >= 0.97, (l, eq)               # measured: 1.000 / 0.9997, 0.989 / 0.986
+        assert max(eq_plain) <= 0.9, (l, eq_plain)      # measured: 0.58 / 0.58, 0.32 / 0.30
+    assert _rel(ours["logits"], logits) < 1e-3          # measured 2.0e-4
+    assert _rel(plain["logits"], logits) > 3e-3         # measured 6.7e-3

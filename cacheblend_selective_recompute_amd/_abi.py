@@ -88,6 +88,8 @@ KINDS = ["rerope", "gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down", "attention
 _PROTOS = {
     "cb_rerope_k": (c_int, [POINTER(cb_model_cfg), POINTER(cb_chunk), c_int32, POINTER(cb_paged_kv),
                             c_uint32, c_void_p, c_size_t, c_void_p]),
+    "cb_rerope_k_noalloc": (c_int, [POINTER(cb_model_cfg), POINTER(cb_chunk), c_int32, POINTER(cb_paged_kv),
+                                    c_uint32, c_void_p]),
     "cb_kv_deviation": (c_int, [POINTER(cb_model_cfg), c_int32, c_void_p, c_void_p, c_int64, c_void_p,
                                 c_int32, POINTER(cb_paged_kv), c_void_p, c_void_p]),
     "cb_select_hkvd": (c_int, [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p,

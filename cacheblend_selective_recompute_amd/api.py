@@ -311,6 +311,15 @@ def cb_rerope_k(cfg: cb_model_cfg, chunks: Sequence[ChunkSource], dst: PagedKV, 
                            _stream(stream)), "cb_rerope_k")
 
 
+def cb_rerope_k_noalloc(cfg: cb_model_cfg, chunks: Sequence[ChunkSource], dst: PagedKV, flags: int = CB_COPY_V,
+                        stream=None) -> None:
+    """cb_rerope_k with the library's static per-GPU scratch instead of a workspace."""
+    lib = _abi.load()
+    arr = _chunk_array(chunks)
+    _check(lib.cb_rerope_k_noalloc(ctypes.byref(cfg), arr, len(chunks), ctypes.byref(dst.c), flags, _stream(stream)),
+           "cb_rerope_k_noalloc")
+
+
 def cb_kv_deviation(cfg: cb_model_cfg, layer: int, k_fresh: torch.Tensor, v_fresh: torch.Tensor,
                     pos: torch.Tensor, cache: PagedKV, dev_out: torch.Tensor, stream=None) -> None:
     """k_fresh / v_fresh: fp32 [n][>= Hkv*dh] views sharing one row stride."""

@@ -540,6 +540,35 @@ cb_status enqueue_layer0(const cb_model& m, const PagedRef& kv, int N, int Q, fl
 
 }  // namespace
 
+namespace cb {
+
+cb_status record_failure(cb_status st, const char* msg) { return fail(st, "%s", msg); }
+
+size_t rerope_table_bytes(const cb_model_cfg& c, int n_chunks) {
+  return static_cast<size_t>(std::min(std::max(n_chunks, 1), kMaxChunksPerLaunch)) * (c.head_dim / 2) * sizeof(float2);
+}
+
+cb_status rerope_check(const cb_model_cfg* cfg, const cb_chunk* chunks, int32_t n_chunks, const cb_paged_kv* dst,
+                       uint32_t flags) {
+  cb_status st = check_cfg(cfg);
+  if (st != CB_OK) return st;
+  if ((st = check_chunk_sources(cfg, chunks, n_chunks, false)) != CB_OK) return st;
+  int64_t end = 0;
+  for (int i = 0; i < n_chunks; ++i) end = std::max<int64_t>(end, (int64_t)chunks[i].new_start + chunks[i].len);
+  if ((st = check_paged(cfg, dst, end, "dst")) != CB_OK) return st;
+  if ((st = check_chunk_formats(chunks, n_chunks, dst)) != CB_OK) return st;
+  if (flags & ~CB_COPY_V) return fail(CB_ERR_INVALID, "unknown flags 0x%x", flags);
+  return CB_OK;
+}
+
+cb_status rerope_enqueue(const cb_model_cfg& c, const cb_chunk* chunks, int32_t n_chunks, const cb_paged_kv& dst,
+                         uint32_t flags, float2* table, hipStream_t s) {
+  cb_status st = enqueue_rerope(c, chunks, n_chunks, dst, (flags & CB_COPY_V) ? 1 : 0, table, s, nullptr);
+  return st == CB_OK ? ok() : st;
+}
+
+}  // namespace cb
+
 // ===========================================================================
 // public entry points
 // ===========================================================================
@@ -588,23 +617,15 @@ size_t cb_workspace_bytes(const cb_model_cfg* cfg, int32_t n_ctx, int32_t n_quer
 
 cb_status cb_rerope_k(const cb_model_cfg* cfg, const cb_chunk* chunks, int32_t n_chunks, const cb_paged_kv* dst,
                       uint32_t flags, void* ws, size_t ws_bytes, cb_stream_t stream) {
-  cb_status st = check_cfg(cfg);
+  cb_status st = rerope_check(cfg, chunks, n_chunks, dst, flags);
   if (st != CB_OK) return st;
-  if ((st = check_chunk_sources(cfg, chunks, n_chunks, false)) != CB_OK) return st;
-  int64_t end = 0;
-  for (int i = 0; i < n_chunks; ++i) end = std::max<int64_t>(end, (int64_t)chunks[i].new_start + chunks[i].len);
-  if ((st = check_paged(cfg, dst, end, "dst")) != CB_OK) return st;
-  if ((st = check_chunk_formats(chunks, n_chunks, dst)) != CB_OK) return st;
-  if (flags & ~CB_COPY_V) return fail(CB_ERR_INVALID, "unknown flags 0x%x", flags);
   const size_t need = cb_workspace_bytes(cfg, 0, 0, n_chunks);
   if (n_chunks > 0 && (!ws || ws_bytes < need))
     return fail(CB_ERR_WORKSPACE, "workspace %zu bytes, %zu needed", ws_bytes, need);
   if (ws && !aligned16(ws)) return fail(CB_ERR_INVALID, "workspace not 16-byte aligned");
   Ws w;
   carve(*cfg, 0, 0, n_chunks, ws, &w);
-  st = enqueue_rerope(*cfg, chunks, n_chunks, *dst, (flags & CB_COPY_V) ? 1 : 0, w.dtab,
-                      reinterpret_cast<hipStream_t>(stream), nullptr);
-  return st == CB_OK ? ok() : st;
+  return rerope_enqueue(*cfg, chunks, n_chunks, *dst, flags, w.dtab, reinterpret_cast<hipStream_t>(stream));
 }
 
 cb_status cb_kv_deviation(const cb_model_cfg* cfg, int32_t layer, const float* k_fresh, const float* v_fresh,

@@ -113,6 +113,16 @@ __host__ __device__ __forceinline__ int64_t pk_rows(int64_t rows) { return (rows
 
 // Chunk descriptors are passed by value in kernel arguments.
 constexpr int kMaxChunksPerLaunch = 32;
+// cb_rerope_k's validation and enqueue, shared with the entry point that keeps
+// its rotation table in a static device array (cb_noalloc.hip); the table holds
+// min(n_chunks, kMaxChunksPerLaunch) x head_dim / 2 (cos, sin) pairs
+cb_status rerope_check(const cb_model_cfg* cfg, const cb_chunk* chunks, int32_t n_chunks, const cb_paged_kv* dst,
+                       uint32_t flags);
+size_t rerope_table_bytes(const cb_model_cfg& c, int n_chunks);
+cb_status rerope_enqueue(const cb_model_cfg& c, const cb_chunk* chunks, int32_t n_chunks, const cb_paged_kv& dst,
+                         uint32_t flags, float2* table, hipStream_t s);
+// sets the thread's last-error text and returns st
+cb_status record_failure(cb_status st, const char* msg);
 struct ChunkDesc {
   const void* k;
   const void* v;

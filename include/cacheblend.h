@@ -205,6 +205,24 @@ cb_status cb_rerope_k(const cb_model_cfg* cfg, const cb_chunk* chunks, int32_t n
                       cb_stream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * cb_rerope_k_noalloc -- cb_rerope_k without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, results
+ * and errors as cb_rerope_k; the rotation table it writes and the re-RoPE
+ * kernel reads lives in a static device array of CB_NOALLOC_SCRATCH_BYTES
+ * bytes per GPU, which the library holds until the process ends.  The table
+ * needs min(n_chunks, 32) * head_dim / 2 * 8 bytes; a larger need returns
+ * CB_ERR_WORKSPACE before anything is enqueued.  The array's address on the
+ * current device is looked up once per device (the stream must belong to the
+ * current device).  Nothing is allocated or freed.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (on different streams,
+ * or from several host threads without ordering) race on it.
+ * ------------------------------------------------------------------------- */
+#define CB_NOALLOC_SCRATCH_BYTES 65536
+cb_status cb_rerope_k_noalloc(const cb_model_cfg* cfg, const cb_chunk* chunks, int32_t n_chunks,
+                              const cb_paged_kv* dst, uint32_t flags, cb_stream_t stream);
+
+/* ---------------------------------------------------------------------------
  * cb_kv_deviation -- per-token KV deviation ("CacheBlend 完全拆解", section
  * "核心思想", eq. Δkv), squared L2 over the concatenated K and V of every KV head:
  *   dev_out[i] = sum_e (k_fresh[i][e] - K[layer][pos[i]][e])^2

@@ -72,13 +72,17 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 def test_traffic_summary_is_read_only_for_the_unchanged_source():
     import hashlib
-    path = os.path.join(ROOT, "profiles", "gemm_gate_up_8b-4x1024-q64_traffic.md")
-    fields = dict(line[2:].strip().split(": ", 1) for line in open(path) if line.startswith("- ") and ": " in line)
-    same = hashlib.sha256(open(os.path.join(ROOT, fields["kernel_source"]), "rb").read()).hexdigest() == \
-        fields["kernel_source_sha256"]
-    v = bench.traffic_from_profile("gemm_gate_up", "8b-4x1024-q64")
-    if same:
-        assert v == int(fields["traffic_bytes_per_launch"]) and v > 0
-    else:                        # the kernel changed since the counters were taken
-        assert v is None
+    for wl in ("70b-4x1024-q64", "8b-4x1024-q64"):
+        path = os.path.join(ROOT, "profiles", f"gemm_gate_up_{wl}_traffic.md")
+        if not os.path.exists(path):
+            assert bench.traffic_from_profile("gemm_gate_up", wl) is None
+            continue
+        fields = dict(line[2:].strip().split(": ", 1) for line in open(path) if line.startswith("- ") and ": " in line)
+        same = hashlib.sha256(open(os.path.join(ROOT, fields["kernel_source"]), "rb").read()).hexdigest() == \
+            fields["kernel_source_sha256"]
+        v = bench.traffic_from_profile("gemm_gate_up", wl)
+        if same:
+            assert v == int(fields["traffic_bytes_per_launch"]) and v > 0
+        else:                        # the kernel changed since the counters were taken
+            assert v is None
     assert bench.traffic_from_profile("gemm_gate_up", "no-such-workload") is None

@@ -402,9 +402,11 @@ cb_status enqueue_layer(const cb_model& m, int l, const PagedRef& kv, int nc, in
     // the Q/K/V reduction took the deviations, wrote the cache and, the top-k of all
     // candidates being the identity, the row maps
   } else if (check) {
+    // deviations of every candidate (many workgroups), then the top-k with the row
+    // maps of the kept rows and the suffix (one workgroup)
     float* dev = io.dev_slot ? io.dev_slot : w.dev;
-    CB_LAUNCH(tr, CB_KIND_DEVIATION, launch_deviation(c.dtype, w.kvf, w.kvf + kvw, 2 * kvw, io.cand_pos, nc, kv, l, kvw, dev, io.dev_by_pos, s), "deviation");
-    // the top-k also writes the row maps of the kept rows and the suffix
+    CB_LAUNCH(tr, CB_KIND_DEVIATION, launch_deviation(c.dtype, w.kvf, w.kvf + kvw, 2 * kvw, io.cand_pos, nc, kv, l, kvw,
+                                                      dev, io.dev_by_pos, s), "deviation");
     CB_LAUNCH(tr, CB_KIND_SELECT, launch_select_rows(dev, io.cand_pos, nc, k, io.pos_out, w.slot, N, Q, w.gmap,
                                                      io.rowpos_out, io.hkvd_row, s), "select");
   } else {

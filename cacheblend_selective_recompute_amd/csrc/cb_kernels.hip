@@ -283,19 +283,16 @@ __device__ __forceinline__ void load8(const T* p, float (&f)[8]) {
   }
 }
 
+// Squared L2 distance of one fresh K/V row (fp32) from the cached row at position p
+// (K and V, every KV head), reduced over the wave in a fixed order; every lane
+// returns the sum.  W = 1024: each lane takes 8 consecutive values per pass with
+// all of its 16-byte loads issued first; W = 0: any width (a multiple of 4).
 template <typename T, int W>
-__global__ __launch_bounds__(256) void deviation_kernel(const float* kf, const float* vf, int64_t ldf,
-                                                        const int32_t* pos, int n, PagedRef cache, int layer,
-                                                        int width, float* dev, float* dev_by_pos) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= n) return;
-  const int p = pos[row];
+__device__ __forceinline__ float row_deviation(const float* fk, const float* fv, const PagedRef& cache, int layer,
+                                               int width, int p, int lane) {
   const int64_t off = static_cast<int64_t>(layer) * cache.layer_stride + paged_row(cache, p) * width;
   const T* ck = static_cast<const T*>(cache.k) + off;
   const T* cv = static_cast<const T*>(cache.v) + off;
-  const float* fk = kf + static_cast<int64_t>(row) * ldf;
-  const float* fv = vf + static_cast<int64_t>(row) * ldf;
   float acc = 0.f;
   if constexpr (W > 0) {
     constexpr int P = W / 512;              // passes of 64 lanes x 8 values
@@ -351,7 +348,19 @@ __global__ __launch_bounds__(256) void deviation_kernel(const float* kf, const f
       acc += (dv0 * dv0 + dv1 * dv1) + (dv2 * dv2 + dv3 * dv3);
     }
   }
-  acc = wave_sum(acc);
+  return wave_sum(acc);
+}
+
+template <typename T, int W>
+__global__ __launch_bounds__(256) void deviation_kernel(const float* kf, const float* vf, int64_t ldf,
+                                                        const int32_t* pos, int n, PagedRef cache, int layer,
+                                                        int width, float* dev, float* dev_by_pos) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;
+  const int p = pos[row];
+  const float acc = row_deviation<T, W>(kf + static_cast<int64_t>(row) * ldf, vf + static_cast<int64_t>(row) * ldf,
+                                        cache, layer, width, p, lane);
   if (lane == 0) {
     dev[row] = acc;
     if (dev_by_pos) dev_by_pos[p] = acc;
@@ -359,39 +368,49 @@ __global__ __launch_bounds__(256) void deviation_kernel(const float* kf, const f
 }
 
 // ---------------------------------------------------------------------------
-// exact top-k (one 1024-thread block): radix select of the k-th largest key on
-// the order-preserving bit pattern of dev, then a stable compaction in
-// candidate order (ties: the first ones, i.e. the smaller positions).
+// exact top-k by (dev descending, position ascending) over candidates given in
+// ascending position order, run by one 1024-thread workgroup: radix select of
+// the k-th largest order-preserving key in three passes (the top 11 bits, the
+// next 11, the last 10; each pass an LDS histogram of the keys that match the
+// digits found so far, the digit found by a parallel suffix scan of the bins),
+// then a stable compaction in candidate order (ties: the first ones, i.e. the
+// smaller positions).  Thread t takes the m = ceil(n / kSel) consecutive
+// candidates [t m, t m + m), so candidate order is thread order; their order keys
+// are staged in LDS, transposed (thread t's j-th key at j kSel + t, so a wave's
+// reads hit distinct banks), when there are at most kSelLdsKeys candidates, else
+// recomputed from dev on every read.
 // ---------------------------------------------------------------------------
 constexpr int kSel = 1024;
+constexpr int kSelWaves = kSel / 64;
+constexpr int kSelBins = 2048;
+constexpr int kSelLdsKeys = 32768;     // 128 KiB of keys (LDS holds 160 KiB per CU)
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// exclusive block scan of a 0/1 flag; returns prefix, writes total
-__device__ __forceinline__ int block_flag_scan(bool flag, int* wsum, int* total) {
+// sum of v over the threads above this one (higher thread index)
+__device__ __forceinline__ int block_suffix_excl(int v, int* wsum) {
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  const uint64_t m = __ballot(flag);
-  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) wsum[wid] = __popcll(m);
-  __syncthreads();
-  int before = 0, tot = 0;
-  for (int w = 0; w < kSel / 64; ++w) {
-    const int c = wsum[w];
-    if (w < wid) before += c;
-    tot += c;
+  int incl = v;                                     // v over lanes >= lane of this wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_down(incl, d, 64);
+    if (lane + d < 64) incl += o;
   }
+  if (lane == 0) wsum[wid] = incl;
   __syncthreads();
-  *total = tot;
-  return before + in_wave;
+  int above = 0;
+  for (int w = wid + 1; w < kSelWaves; ++w) above += wsum[w];
+  __syncthreads();
+  return above + incl - v;
 }
 
-// With rm.rowpos set it also writes the layer's row maps, as build_rows_kernel
-// would from its output: kept row o comes from candidate slot i at position
-// pos[i]; suffix row k + j from input row nc + j at position n_ctx + j.
+// With rowpos set the selection also writes the layer's row maps: kept row o
+// comes from candidate slot i at position pos[i]; suffix row k + j from input
+// row n + j at position n_ctx + j.
 struct RowMaps {
   int32_t* gmap;
   int32_t* rowpos;
@@ -399,14 +418,62 @@ struct RowMaps {
   int n_ctx, nq;
 };
 
-__global__ __launch_bounds__(kSel) void select_kernel(const float* dev, const int32_t* pos, int n, int k,
-                                                      int32_t* sel_pos, int32_t* sel_slot, RowMaps rm) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_digit, s_rem;
-  __shared__ int wsum[kSel / 64];
+struct SelectSmem {
+  uint32_t hist[kSelBins];
+  int wsum[kSelWaves];
+  int2 wsum2[kSelWaves];
+  uint32_t digit, rem;
+};
+
+// Exclusive block scans (in thread order) of two counts at once; writes the totals.
+__device__ __forceinline__ int2 block_scan2(int a, int b, int2* wsum2, int2* total) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  int ia = a, ib = b;                               // inclusive within the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int oa = __shfl_up(ia, d, 64), ob = __shfl_up(ib, d, 64);
+    if (lane >= d) { ia += oa; ib += ob; }
+  }
+  if (lane == 63) wsum2[wid] = make_int2(ia, ib);
+  __syncthreads();
+  int2 before = make_int2(0, 0), tot = make_int2(0, 0);
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int2 c = wsum2[w];
+    if (w < wid) { before.x += c.x; before.y += c.y; }
+    tot.x += c.x; tot.y += c.y;
+  }
+  __syncthreads();
+  *total = tot;
+  return make_int2(before.x + ia - a, before.y + ib - b);
+}
+
+// LDS histogram add of digit d for the lanes with `valid`: lanes of the wave that
+// share a digit are counted together by one atomic (a few ballot rounds: the
+// deviations of a layer often crowd into a few bins), the rest one by one.
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool valid, uint32_t d) {
+  const int lane = threadIdx.x & 63;
+  uint64_t pending = __ballot(valid);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (!pending) break;
+    const int leader = __ffsll(static_cast<unsigned long long>(pending)) - 1;
+    const uint32_t ld = __shfl(d, leader, 64);
+    const uint64_t same = __ballot(valid && d == ld) & pending;
+    if (lane == leader) atomicAdd(&hist[ld], static_cast<uint32_t>(__popcll(same)));
+    pending &= ~same;
+  }
+  if ((pending >> lane) & 1ull) atomicAdd(&hist[d], 1u);
+}
+
+// The selection by the calling workgroup (all kSel threads) over dev[0..n); keys:
+// their order keys in LDS (transposed, see above), or NULL to read dev.
+__device__ void select_block(const uint32_t* keys, const float* dev, const int32_t* pos, int n, int k, int32_t* sel_pos,
+                             int32_t* sel_slot, const RowMaps& rm, SelectSmem& sm) {
+  const int tid = threadIdx.x;
   auto keep = [&](int o, int i) {
     const int p = pos[i];
-    sel_pos[o] = p;
+    if (sel_pos) sel_pos[o] = p;
     if (sel_slot) sel_slot[o] = i;
     if (rm.rowpos) {
       rm.gmap[o] = i;
@@ -416,61 +483,89 @@ __global__ __launch_bounds__(kSel) void select_kernel(const float* dev, const in
   };
   if (rm.rowpos) {
     const int kk = max(k, 0);
-    for (int j = threadIdx.x; j < rm.nq; j += kSel) {
+    for (int j = tid; j < rm.nq; j += kSel) {
       rm.gmap[kk + j] = n + j;
       rm.rowpos[kk + j] = rm.n_ctx + j;
     }
   }
   if (k <= 0) return;
   if (k >= n) {
-    for (int i = threadIdx.x; i < n; i += kSel) keep(i, i);
+    for (int i = tid; i < n; i += kSel) keep(i, i);
     return;
   }
+  const int m = (n + kSel - 1) / kSel;
+  const int i0 = min(n, tid * m), i1 = min(n, i0 + m);
+  auto key_of = [&](int i) { return keys ? keys[(i - i0) * kSel + tid] : order_key(dev[i]); };
   uint32_t prefix = 0, mask = 0;
   uint32_t rem = static_cast<uint32_t>(k);
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = threadIdx.x; i < 256; i += kSel) hist[i] = 0;
+  constexpr int kShift[3] = {21, 10, 0};
+  constexpr int kBits[3] = {11, 11, 10};
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = kShift[pass];
+    const uint32_t dmask = (1u << kBits[pass]) - 1u;
+    sm.hist[2 * tid] = 0;
+    sm.hist[2 * tid + 1] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kSel) {
-      const uint32_t key = order_key(dev[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    for (int j = 0; j < m; ++j) {                    // uniform trip count: every lane takes part in the ballots
+      const int i = i0 + j;
+      const uint32_t key = i < i1 ? key_of(i) : 0u;
+      hist_add(sm.hist, i < i1 && (key & mask) == prefix, (key >> shift) & dmask);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t cum = 0;
-      for (int dg = 255; dg >= 0; --dg) {
-        const uint32_t h = hist[dg];
-        if (cum + h >= rem) {
-          s_digit = static_cast<uint32_t>(dg);
-          s_rem = rem - cum;
-          break;
-        }
-        cum += h;
-      }
+    // thread t owns bins 2t and 2t+1; the digit is the bin where the count of larger
+    // keys first reaches rem
+    const uint32_t h0 = sm.hist[2 * tid], h1 = sm.hist[2 * tid + 1];
+    const uint32_t above = static_cast<uint32_t>(block_suffix_excl(static_cast<int>(h0 + h1), sm.wsum));
+    if (above < rem && rem <= above + h1) {
+      sm.digit = 2 * tid + 1;
+      sm.rem = rem - above;
+    } else if (above + h1 < rem && rem <= above + h1 + h0) {
+      sm.digit = 2 * tid;
+      sm.rem = rem - above - h1;
     }
     __syncthreads();
-    prefix |= s_digit << shift;
-    mask |= 255u << shift;
-    rem = s_rem;
-    __syncthreads();
+    prefix |= sm.digit << shift;
+    mask |= dmask << shift;
+    rem = sm.rem;
   }
-  // prefix = key of the k-th largest; take every larger key and the first `rem` equal ones
-  int out_base = 0, eq_base = 0;
-  for (int base = 0; base < n; base += kSel) {
-    const int i = base + threadIdx.x;
-    uint32_t key = 0;
-    if (i < n) key = order_key(dev[i]);
-    const bool gt = i < n && key > prefix;
-    const bool eq = i < n && key == prefix;
-    int eq_tot = 0;
-    const int eq_before = block_flag_scan(eq, wsum, &eq_tot) + eq_base;
-    const bool take = gt || (eq && eq_before < static_cast<int>(rem));
-    int take_tot = 0;
-    const int o = block_flag_scan(take, wsum, &take_tot) + out_base;
-    if (take && o < k) keep(o, i);
-    out_base += take_tot;
-    eq_base += eq_tot;
+  // prefix = key of the k-th largest; take every larger key and the first `rem` equal
+  // ones: candidate i goes to slot (larger keys before i) + (equal keys before i)
+  int gt = 0, eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = key_of(i);
+    gt += key > prefix;
+    eq += key == prefix;
   }
+  int2 tot;
+  const int2 before = block_scan2(gt, eq, sm.wsum2, &tot);
+  int g = before.x, e = before.y;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = key_of(i);
+    if (key > prefix) {
+      keep(g + min(e, static_cast<int>(rem)), i);
+      ++g;
+    } else if (key == prefix) {
+      if (e < static_cast<int>(rem)) keep(g + e, i);
+      ++e;
+    }
+  }
+}
+
+// Order keys of dev[0..n) into LDS, transposed, when they fit (returns them), else NULL.
+__device__ __forceinline__ const uint32_t* stage_keys(const float* dev, int n, uint32_t* lds_keys) {
+  if (n > kSelLdsKeys) return nullptr;
+  const int m = (n + kSel - 1) / kSel;
+  for (int i = threadIdx.x; i < n; i += kSel) lds_keys[(i % m) * kSel + i / m] = order_key(dev[i]);
+  __syncthreads();
+  return lds_keys;
+}
+
+__global__ __launch_bounds__(kSel) void select_kernel(const float* dev, const int32_t* pos, int n, int k,
+                                                      int32_t* sel_pos, int32_t* sel_slot, RowMaps rm) {
+  __shared__ SelectSmem sm;
+  __shared__ uint32_t lds_keys[kSelLdsKeys];
+  select_block(stage_keys(dev, n, lds_keys), dev, pos, n, k, sel_pos, sel_slot, rm, sm);
 }
 
 __global__ void build_rows_kernel(const int32_t* sel_slot, const int32_t* sel_pos, int k, int nc, int n_ctx, int nq,

@@ -118,19 +118,22 @@ def fp8_grid_step(x, scale):
     return np.ldexp(1.0, np.clip(E - 1, -6, 8) - 3) * scale
 
 
-def fp8_close(g, o, scale, label, min_equal=0.97):
+def fp8_close(g, o, scale, label, min_equal=0.99, extra=0.0):
     """Stored FP8 values against the oracle's: every element within one grid step
-    (times scale) plus 2e-2 of the largest value, and min_equal of them on the
-    same grid point."""
+    (times scale) of the larger of the two values, plus `extra` (0 by default: both
+    sides rounded the same float32 arithmetic up to the order of its sums; a caller
+    comparing with a different arithmetic passes how far that arithmetic itself
+    moves the values), and at least min_equal of them on the same grid point."""
     g = np.asarray(g, dtype=np.float64)
     o = np.asarray(o, dtype=np.float64)
     d = np.abs(g - o)
-    atol = 2e-2 * float(np.max(np.abs(o), initial=0.0))
-    ok = d <= 1.0001 * np.maximum(fp8_grid_step(o, scale), fp8_grid_step(g, scale)) + atol
+    step = np.maximum(fp8_grid_step(o, scale), fp8_grid_step(g, scale))
+    ok = d <= 1.0001 * step + extra
     # equal = the same grid point; the GPU side is dequantised as code x scale in fp32
     eq = float(np.mean(d <= 1e-6 * np.abs(o))) if d.size else 1.0
-    say(f"  {label}: {eq:.4f} of the elements equal, all within one grid step: {bool(ok.all())}")
-    assert ok.all(), f"{label}: {int((~ok).sum())} elements beyond one grid step"
+    say(f"  {label}: {eq:.4f} of the elements equal, the largest difference {float(np.max(d / step, initial=0.0)):.2f} "
+        f"grid steps, all within the bound: {bool(ok.all())}")
+    assert ok.all(), f"{label}: {int((~ok).sum())} elements beyond the bound"
     assert eq >= min_equal, f"{label}: only {eq:.4f} equal"
 
 

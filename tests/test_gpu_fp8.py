@@ -1,17 +1,16 @@
 """GPU parity with an 8-bit (FP8 E4M3) KV cache, through the C ABI.
 
-Element rule for stored FP8 values: the GPU's stored value differs from the
-oracle's by at most one grid step at that value plus the bf16 path's own
-normwise error (2e-2 of the tensor's largest value, the tolerance of the bf16
-cache tests: fresh values computed from bf16 activations differ from the
-oracle's fp64 ones by that much in absolute terms, which small elements see
-as several of their grid steps), and at least 97% of the elements are equal.  Where the input is already on the grid (re-RoPE
-with rotation 0, V moved between caches with power-of-two scales) the bytes are
-equal.  Logits: normwise within 5e-2 (two bf16 paths over FP8 caches whose
-elements may differ by one step).  Deviations are compared normwise (2e-2);
-HKVD sets by the usual rule with the tie band widened to the FP8 noise of the
-deviations (section on deviation precision of the CacheBlend page: FP8 caches
-make the ranking jitter)."""
+Stored FP8 values are compared element by element with the oracle run with bf16
+operands (the arithmetic the GPU performs): both round nearly the same float32
+value, so every element lies within one grid step and at least 99% sit on the
+same grid point.  Deeper in a blend two bf16 computations drift apart (see the
+end-to-end tests), so there the bound adds the largest distance between the
+bf16-operand and the float32 oracle runs of the same layer, and 97% must be
+equal.  Where the input is already on the grid (re-RoPE with rotation 0, V moved
+between caches with power-of-two scales) the bytes are equal.  HKVD sets: the
+usual rule (99% of the keep/drop decisions equal, disagreements within the
+oracle's tie band) against both oracle runs.  Deviations and logits: normwise
+within 2e-2."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +20,7 @@ import oracle
 from oracle.blend import fp8_e4m3
 from cacheblend_selective_recompute_amd import api
 
-from gpu_helpers import fp8_close as _fp8_close, ints, rel, say, to_dev, to_np
+from gpu_helpers import check_sets, fp8_close as _fp8_close, ints, rel, say, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -65,7 +64,7 @@ def test_rerope_fp8():
     for c, (Kc, Vc) in enumerate(kvs):
         n, p, ln = wl.new_starts[c], wl.old_starts[c], wl.chunk_lens[c]
         ref_k = oracle.rerope(Kc, n - p, shape.rope_theta, "fp8", 2 ** -5)
-        _fp8_close(K[:, n:n + ln], ref_k, 2 ** -5, f"chunk {c} K (delta {n - p})", min_equal=0.995)
+        _fp8_close(K[:, n:n + ln], ref_k, 2 ** -5, f"chunk {c} K (delta {n - p})", min_equal=0.995)   # one step
         # V: moved from the 2^-4 grid to the 2^-6 grid; power-of-two scales make it exact
         assert np.array_equal(V[:, n:n + ln], oracle.store_round(Vc, "fp8", 2 ** -6))
     # rotation 0 and equal scales: a byte copy
@@ -121,22 +120,6 @@ def _blend(shape, wl, w, kvs, ks, ch, seed, steps=0, kscale=KS, vscale=VS):
     return m, kv, logits, hk.cpu().numpy(), to_np(dv)
 
 
-def _tie_band_sets(gset, cand, dev_o, dev_g, k, label):
-    """Keep/drop agreement >= 97%; every disagreement lies where the GPU's and the
-    oracle's deviations of the token both sit within their noise of the k-th."""
-    g = set(int(x) for x in gset)
-    o = set(int(x) for x in oracle.select_hkvd(dev_o, cand, k))
-    assert len(g) == k
-    dmap_o = {int(p): float(d) for p, d in zip(cand, dev_o)}
-    dk = np.sort(np.asarray(dev_o))[::-1][k - 1]
-    noise = float(np.max(np.abs(dev_g - dev_o)))
-    for p in g ^ o:
-        assert abs(dmap_o[p] - dk) <= 2 * noise + 1e-3 * dk, f"{label}: disagreement at {p} outside the noise band"
-    frac = 1.0 - len(g ^ o) / len(cand)
-    say(f"  {label}: decision agreement {frac:.4f} (deviation noise {noise / dk:.2e} of the k-th)")
-    assert frac >= 0.97
-
-
 @pytest.mark.parametrize("shape,kscale,vscale", [(MINI8B, KS, VS), (MINI8B, 0.029, 0.037), (MINI64, 0.029, 0.037)],
                          ids=["hd128-pow2", "hd128-scaled", "hd64-scaled"])
 def test_blend_mini8b_fp8(shape, kscale, vscale):
@@ -149,23 +132,34 @@ def test_blend_mini8b_fp8(shape, kscale, vscale):
     ks, ch = wl.schedule()
     m, kv, logits, hk, dv = _blend(shape, wl, w, kvs, ks, ch, 6, kscale=kscale, vscale=vscale)
     force = {l: hk[l, :ks[l]] for l in range(1, shape.n_layers) if ch[l]}
-    o = oracle.blend_prefill(om, [(wl.chunk_tokens[c], kvs[c][0], kvs[c][1], wl.old_starts[c], wl.new_starts[c])
-                                  for c in range(len(kvs))], wl.query_tokens, ks, ch, force_sets=force)
+    chunks = [(wl.chunk_tokens[c], kvs[c][0], kvs[c][1], wl.old_starts[c], wl.new_starts[c]) for c in range(len(kvs))]
+    with oracle.operands("bf16"):
+        o16 = oracle.blend_prefill(om, chunks, wl.query_tokens, ks, ch, force_sets=force)
+    o32 = oracle.blend_prefill(om, chunks, wl.query_tokens, ks, ch, force_sets=force)
     for l in range(1, shape.n_layers):
-        cand, dev = o["devs"][l]
-        gd = dv[l, cand]
-        e = rel(gd, dev)
-        say(f"  layer {l}: deviation rel {e:.2e}")
-        assert e < 2e-2
-        _tie_band_sets(hk[l, :ks[l]], cand, dev, gd, ks[l], f"layer {l}")
+        for lab, o in (("bf16 operands", o16), ("float32", o32)):
+            cand, dev = o["devs"][l]
+            gd = dv[l, cand]
+            e = rel(gd, dev)
+            say(f"  layer {l} [{lab}]: deviation rel {e:.2e}")
+            assert e < 2e-2
+            sc = float(np.mean(np.sum(o["K"][l, cand].astype(np.float64) ** 2, axis=(1, 2)) +
+                               np.sum(o["V"][l, cand].astype(np.float64) ** 2, axis=(1, 2))))
+            check_sets(hk[l, :ks[l]], oracle.select_hkvd(dev, cand, ks[l]), cand, dev, ks[l], sc, f"layer {l} [{lab}]")
     K, V = kv.logical(wl.n_total)
     K, V = to_np(K), to_np(V)
     for l in range(shape.n_layers):
-        _fp8_close(K[l], o["K"][l], kscale, f"layer {l} K")
-        _fp8_close(V[l], o["V"][l], vscale, f"layer {l} V")
-    el = rel(to_np(logits), o["logits"])
-    say(f"  logits rel {el:.2e}")
-    assert el < 5e-2
+        if l == 0:
+            _fp8_close(K[l], o16["K"][l], kscale, f"layer {l} K")
+            _fp8_close(V[l], o16["V"][l], vscale, f"layer {l} V")
+        else:
+            dk = float(np.max(np.abs(o16["K"][l] - o32["K"][l])))
+            dvv = float(np.max(np.abs(o16["V"][l] - o32["V"][l])))
+            _fp8_close(K[l], o16["K"][l], kscale, f"layer {l} K", min_equal=0.97, extra=dk)
+            _fp8_close(V[l], o16["V"][l], vscale, f"layer {l} V", min_equal=0.97, extra=dvv)
+    el, el32 = rel(to_np(logits), o16["logits"]), rel(to_np(logits), o32["logits"])
+    say(f"  logits rel {el:.2e} (bf16 operands), {el32:.2e} (float32)")
+    assert el < 2e-2 and el32 < 2e-2
 
 
 def test_blend_r0_fp8_keeps_reroped_context():
@@ -207,14 +201,28 @@ def test_decode_fp8():
         tok, pos = int(rng.integers(0, shape.vocab)), T + i
         api.cb_decode_step(m, kv, pos, ints([tok]), logits, ws)
         torch.cuda.synchronize()
+        # both oracle runs decode on the GPU's cache (every row up to pos - 1 as stored)
+        K16, V16 = Kb.copy(), Vb.copy()
+        with oracle.operands("bf16"):
+            lo16 = oracle.decode_step(om, K16, V16, tok, pos)
         lo = oracle.decode_step(om, Kb, Vb, tok, pos)
         K, V = kv.logical(pos + 1)
-        el = rel(to_np(logits), lo)
-        say(f"  step {i} (pos {pos}): logits {el:.2e}")
-        assert el < 5e-2
-        # every element of a decode row is fresh (no re-RoPE'd context to share), after
-        # three bf16 layers: ~1e-2 relative difference against a 1/8 relative grid step
-        # moves roughly one element in ten to a neighbouring grid value
-        _fp8_close(to_np(K[:, pos]), Kb[:, pos], KS, f"step {i} K row", min_equal=0.8)
-        _fp8_close(to_np(V[:, pos]), Vb[:, pos], VS, f"step {i} V row", min_equal=0.8)
-        Kb[:, pos], Vb[:, pos] = to_np(K[:, pos]), to_np(V[:, pos])
+        el, el32 = rel(to_np(logits), lo16), rel(to_np(logits), lo)
+        say(f"  step {i} (pos {pos}): logits {el:.2e} (bf16 operands), {el32:.2e} (float32)")
+        assert el < 2e-2 and el32 < 2e-2
+        # the appended row: layer 0 within one grid step of the bf16-operand oracle (99%
+        # equal).  The decode kernel weights V with float32 softmax weights (the prefill
+        # rounds them to bf16 for the matrix cores), so from layer 1 on a decode row is
+        # about as far from either oracle run as the two runs are from each other (88%
+        # of the elements on the same grid point): one grid step plus the distance
+        # between the runs, and 80% equal
+        gk, gv = to_np(K[:, pos]), to_np(V[:, pos])
+        _fp8_close(gk[0], K16[0, pos], KS, f"step {i} K row, layer 0")
+        _fp8_close(gv[0], V16[0, pos], VS, f"step {i} V row, layer 0")
+        for l in range(1, shape.n_layers):
+            for lab, g, o16r, o32r, sc in (("K", gk[l], K16[l, pos], Kb[l, pos], KS), ("V", gv[l], V16[l, pos], Vb[l, pos], VS)):
+                say(f"  step {i} {lab} row, layer {l}: the two oracle runs share {float(np.mean(o16r == o32r)):.4f} "
+                    f"of the grid points, the GPU and the float32 run {float(np.mean(g == o32r)):.4f}")
+                _fp8_close(g, o16r, sc, f"step {i} {lab} row, layer {l}", min_equal=0.8,
+                           extra=float(np.max(np.abs(o16r - o32r))))
+        Kb[:, pos], Vb[:, pos] = gk, gv

@@ -84,6 +84,19 @@ def _layer_sampled(base, N, Q, k, seed, paged, n_sample=24, kv8=None, check=True
         with oracle.operands("bf16"):
             oracle.blend_layer(m_ora, 1, K16, V16, x.astype(np.float64), np.arange(N), Q, check, k,
                                force=gpos if check else None, out_rows=rows[:1])
+        # The same fresh values before rounding, with float32 and with float64 sums: the
+        # GPU sums the same bf16 products in another order, so near zero (where the FP8
+        # grid is finest) the two float32 results may differ by more than a grid step.
+        # Each side is within about the float32-vs-float64 distance of the exact sums.
+        m_ora.kv_storage = "f32"
+        fresh = {}
+        for prec in ("f32", "f64"):
+            Kf, Vf = Kc.astype(np.float64), Vc.astype(np.float64)
+            with oracle.operands("bf16"), oracle.precision(prec):
+                oracle.blend_layer(m_ora, 1, Kf, Vf, x.astype(np.float64), np.arange(N), Q, check, k,
+                                   force=gpos if check else None, out_rows=rows[:1])
+            fresh[prec] = (Kf, Vf)
+        m_ora.kv_storage = "fp8"
     x_ora, keep, dev_ora = oracle.blend_layer(m_ora, 1, Kl, Vl, x.astype(np.float64), np.arange(N), Q, check, k,
                                               force=gpos if check else None, out_rows=rows)
     if check:
@@ -102,10 +115,14 @@ def _layer_sampled(base, N, Q, k, seed, paged, n_sample=24, kv8=None, check=True
     written = np.concatenate([gpos, np.arange(N, T)])
     if kv8:
         # the fresh values come from one layer's products: against the bf16-operand
-        # oracle every element within one grid step, 99% on the same grid point;
-        # against float32, plus how far the float32 products move them
-        fp8_close(K1[written], K16[written], kv8[0], "scattered K (bf16 operands)")
-        fp8_close(V1[written], V16[written], kv8[1], "scattered V (bf16 operands)")
+        # oracle every element within one grid step plus twice the float32 summation
+        # distance, 99% on the same grid point; against float32, plus how far the
+        # float32 products move them
+        ordK = 2 * float(np.max(np.abs(fresh["f32"][0][written] - fresh["f64"][0][written])))
+        ordV = 2 * float(np.max(np.abs(fresh["f32"][1][written] - fresh["f64"][1][written])))
+        say(f"  float32 summation order: up to {ordK:.2e} (K) and {ordV:.2e} (V) between two float32 results")
+        fp8_close(K1[written], K16[written], kv8[0], "scattered K (bf16 operands)", extra=ordK)
+        fp8_close(V1[written], V16[written], kv8[1], "scattered V (bf16 operands)", extra=ordV)
         fp8_close(K1[written], Kl[written], kv8[0], "scattered K (float32)", min_equal=0.9,
                   extra=float(np.max(np.abs(K16[written] - Kl[written]))))
         fp8_close(V1[written], Vl[written], kv8[1], "scattered V (float32)", min_equal=0.9,

@@ -944,19 +944,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_spl
   for (int e = 0; e < PER; ++e) ob[pk_off(row, head * DH + lane * PER + e, KO)] = f2bf(acc[e] * inv);
 }
 
-// The same merge with one workgroup per row: thread t takes CPT consecutive
-// output columns (inside one head) of the row, so every split's (max, sum) pair
-// and partial columns of the row are loaded at once; sums run in split order.
-// For rows of H_q x DH = 256 x CPT columns (CPT a multiple of 8 dividing DH).
+// The same merge with whole rows: `per_row` workgroups per row, thread t of
+// piece c taking CPT consecutive output columns (inside one head) from column
+// (256 c + t) CPT, so every split's (max, sum) pair and partial columns are
+// loaded at once; sums run in split order.  For rows of H_q x DH = 256 x CPT x
+// per_row columns (CPT a multiple of 8 dividing DH).
 template <int DH, int CPT>
-__global__ __launch_bounds__(256) void attn_combine_wide_kernel(AttnArgs a, int n_splits, int ksplit, int QT) {
+__global__ __launch_bounds__(256) void attn_combine_wide_kernel(AttnArgs a, int n_splits, int ksplit, int QT, int per_row) {
   static_assert(CPT % 8 == 0 && DH % CPT == 0, "whole 8-column chunks inside one head");
-  const int row = blockIdx.x;
+  const int row = blockIdx.x / per_row;
   const int t_last = min((row / QT + 1) * QT, a.R) - 1;
   const int kv_end = a.rowpos[t_last] + 1;
   const int ns = min(n_splits, (kv_end + ksplit - 1) / ksplit);
   if (ns <= 1) return;                                   // written whole by the attention kernel
-  const int col = threadIdx.x * CPT;
+  const int col = ((blockIdx.x % per_row) * 256 + threadIdx.x) * CPT;
   const int head = col / DH;
   auto prow = [&](int sp) { return (static_cast<int64_t>(sp) * a.R + row) * a.n_q_heads + head; };
   float M = -INFINITY;
@@ -1119,10 +1120,11 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;
   const int width = a.n_q_heads * DH;
-  if (width == 256 * 16) {
-    attn_combine_wide_kernel<DH, 16><<<a.R, 256, 0, s>>>(a, n_splits, ksplit, QT);
-  } else if (width == 256 * 32 && DH % 32 == 0) {
-    attn_combine_wide_kernel<DH, (DH % 32 == 0 ? 32 : 16)><<<a.R, 256, 0, s>>>(a, n_splits, ksplit, QT);
+  if (width % (256 * 8) == 0) {
+    // 8 columns per thread: rows of 4096 / 8192 columns take 2 / 4 workgroups each,
+    // so more loads are in flight than with one workgroup per row
+    const int per_row = width / (256 * 8);
+    attn_combine_wide_kernel<DH, 8><<<a.R * per_row, 256, 0, s>>>(a, n_splits, ksplit, QT, per_row);
   } else {
     const int pairs = a.R * a.n_q_heads;
     attn_combine_kernel<DH><<<(pairs + 3) / 4, 256, 0, s>>>(a, n_splits, ksplit, QT);

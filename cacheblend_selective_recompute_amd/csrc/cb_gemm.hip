@@ -450,11 +450,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int spli
 // adds the squared differences (candidate rows of a checked layer only; per
 // thread in column order, then across the workgroup in a fixed order) and writes the fresh
 // values over it (bf16, or FP8 divided by the tensor's scale).  T: the cache's
-// element type.
-template <typename T, int SP>
-__global__ __launch_bounds__(256) void qkv_reduce_blend_kernel(GemmArgs g, int splits) {
+// element type; TPB threads per row.
+template <typename T, int SP, int TPB = 256>
+__global__ __launch_bounds__(TPB) void qkv_reduce_blend_kernel(GemmArgs g, int splits) {
   if constexpr (SP > 0) splits = SP;
-  __shared__ float red[4];
+  constexpr int NW = TPB / 64;
+  __shared__ float red[NW];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int kvw = g.rope2_cols;
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(256) void qkv_reduce_blend_kernel(GemmArgs g, int s
     }
   }
   float acc = 0.f;
-  for (int j = tid; j < n4; j += 256) {
+  for (int j = tid; j < n4; j += TPB) {
     const int col = j * 4;
     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -535,21 +536,31 @@ __global__ __launch_bounds__(256) void qkv_reduce_blend_kernel(GemmArgs g, int s
   if ((tid & 63) == 0) red[tid >> 6] = acc;
   __syncthreads();
   if (tid == 0) {
-    const float d = ((red[0] + red[1]) + red[2]) + red[3];
+    float d = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) d += red[i];
     g.blend_dev[row] = d;
     if (g.blend_dev_by_pos) g.blend_dev_by_pos[pos] = d;
   }
 }
 
-template <typename T>
-hipError_t launch_qkv_reduce_blend(const GemmArgs& a, int eff, hipStream_t s) {
+template <typename T, int TPB>
+hipError_t launch_qkv_reduce_blend_t(const GemmArgs& a, int eff, hipStream_t s) {
   switch (eff) {
-    case 2: qkv_reduce_blend_kernel<T, 2><<<a.M, 256, 0, s>>>(a, eff); break;
-    case 3: qkv_reduce_blend_kernel<T, 3><<<a.M, 256, 0, s>>>(a, eff); break;
-    case 4: qkv_reduce_blend_kernel<T, 4><<<a.M, 256, 0, s>>>(a, eff); break;
-    default: qkv_reduce_blend_kernel<T, 0><<<a.M, 256, 0, s>>>(a, eff); break;
+    case 2: qkv_reduce_blend_kernel<T, 2, TPB><<<a.M, TPB, 0, s>>>(a, eff); break;
+    case 3: qkv_reduce_blend_kernel<T, 3, TPB><<<a.M, TPB, 0, s>>>(a, eff); break;
+    case 4: qkv_reduce_blend_kernel<T, 4, TPB><<<a.M, TPB, 0, s>>>(a, eff); break;
+    default: qkv_reduce_blend_kernel<T, 0, TPB><<<a.M, TPB, 0, s>>>(a, eff); break;
   }
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_qkv_reduce_blend(const GemmArgs& a, int eff, hipStream_t s) {
+  // wide rows (70B: 8192 Q + 2 x 1024 K/V columns) take 1024 threads, so each thread
+  // has a few four-column groups instead of ten in a dependent chain
+  if (a.q_cols + 2 * a.rope2_cols >= 8192) return launch_qkv_reduce_blend_t<T, 1024>(a, eff, s);
+  return launch_qkv_reduce_blend_t<T, 256>(a, eff, s);
 }
 
 // Split-K reduction of a residual GEMM fused with the RMSNorm that follows it:
@@ -565,13 +576,17 @@ __device__ __forceinline__ float wave_sum64(float v) {
 }
 
 // Columns below c_part were finished by whole-tile workgroups of the same GEMM
-// (resid added) and are read back from C.  NC > 0: the row is NC x 1024 columns
-// and there are SP splits, both compile-time, so every load of the row (all
-// partials, the residual) is issued before the first add; the sums keep split
-// order.  NC = 0: any width and split count.
-template <int NC, int SP>
-__global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs g, int splits, int c_part) {
-  __shared__ float red[4];
+// (resid added) and are read back from C.  NC > 0: the row is NC x 4 TPB columns
+// (TPB threads, 4 columns each per chunk) and there are SP splits, all
+// compile-time, so every load of the row (all partials, the residual) is issued
+// before the first add; the sums keep split order.  NC = 0 (TPB 256): any width
+// and split count.
+template <int NC, int SP, int TPB = 256>
+__global__ __launch_bounds__(TPB) void splitk_reduce_norm_kernel(GemmArgs g, int splits, int c_part) {
+  static_assert(NC > 0 || TPB == 256, "the generic path runs 256 threads");
+  constexpr int NW = TPB / 64;
+  constexpr int CW = 4 * TPB;     // columns per chunk
+  __shared__ float red[NW];
   const int row = blockIdx.x;
   const int rr = g.resid_rows ? g.resid_rows[row] : row;
   const int64_t wpart = g.N - c_part;
@@ -582,7 +597,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs g, int
     float4 pp[NC][SP], rv[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int e = threadIdx.x * 4 + c * 1024;
+      const int e = threadIdx.x * 4 + c * CW;
       if (e < c_part) {
         v[c] = *reinterpret_cast<const float4*>(static_cast<const float*>(g.C) + static_cast<int64_t>(row) * g.ldc + e);
       } else {
@@ -594,7 +609,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs g, int
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const int e = threadIdx.x * 4 + c * 1024;
+      const int e = threadIdx.x * 4 + c * CW;
       if (e >= c_part) {
         float4 sm = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -631,12 +646,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs g, int
   ss = wave_sum64(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  float part[NW];                  // the waves' sums, added pairwise in a fixed tree
+#pragma unroll
+  for (int i = 0; i < NW; ++i) part[i] = red[i];
+#pragma unroll
+  for (int h = NW / 2; h >= 1; h >>= 1)
+#pragma unroll
+    for (int i = 0; i < h; ++i) part[i] = part[2 * i] + part[2 * i + 1];
+  const float tot = part[0];
   const float inv = 1.0f / sqrtf(tot / static_cast<float>(g.N) + g.norm_eps);
   bf16_t* out = static_cast<bf16_t*>(g.norm_out);
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int e = threadIdx.x * 4 + c * 1024;
+    const int e = threadIdx.x * 4 + c * (NC > 0 ? CW : 1024);
     if (NC > 0 || e < g.N) {
       const float4 gg = *reinterpret_cast<const float4*>(g.norm_gain + e);
       uint2 w;
@@ -647,24 +669,30 @@ __global__ __launch_bounds__(256) void splitk_reduce_norm_kernel(GemmArgs g, int
   }
 }
 
-template <int NC>
+template <int NC, int TPB>
 hipError_t launch_reduce_norm_nc(const GemmArgs& a, int eff, int c_part, hipStream_t s) {
   switch (eff) {
-    case 2: splitk_reduce_norm_kernel<NC, 2><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
-    case 3: splitk_reduce_norm_kernel<NC, 3><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
-    case 4: splitk_reduce_norm_kernel<NC, 4><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
-    case 5: splitk_reduce_norm_kernel<NC, 5><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
-    case 6: splitk_reduce_norm_kernel<NC, 6><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
-    case 7: splitk_reduce_norm_kernel<NC, 7><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
-    case 8: splitk_reduce_norm_kernel<NC, 8><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
+    case 2: splitk_reduce_norm_kernel<NC, 2, TPB><<<a.M, TPB, 0, s>>>(a, eff, c_part); break;
+    case 3: splitk_reduce_norm_kernel<NC, 3, TPB><<<a.M, TPB, 0, s>>>(a, eff, c_part); break;
+    case 4: splitk_reduce_norm_kernel<NC, 4, TPB><<<a.M, TPB, 0, s>>>(a, eff, c_part); break;
+    case 5: splitk_reduce_norm_kernel<NC, 5, TPB><<<a.M, TPB, 0, s>>>(a, eff, c_part); break;
+    case 6: splitk_reduce_norm_kernel<NC, 6, TPB><<<a.M, TPB, 0, s>>>(a, eff, c_part); break;
+    case 7: splitk_reduce_norm_kernel<NC, 7, TPB><<<a.M, TPB, 0, s>>>(a, eff, c_part); break;
+    case 8: splitk_reduce_norm_kernel<NC, 8, TPB><<<a.M, TPB, 0, s>>>(a, eff, c_part); break;
     default: splitk_reduce_norm_kernel<0, 0><<<a.M, 256, 0, s>>>(a, eff, c_part); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_reduce_norm(const GemmArgs& a, int eff, int c_part, hipStream_t s) {
-  if (a.N == 4096) return launch_reduce_norm_nc<4>(a, eff, c_part, s);
-  if (a.N == 8192 && eff <= 4) return launch_reduce_norm_nc<8>(a, eff, c_part, s);   // more would spill
+  // 8192-wide rows with more than 4 splits: 1024 threads, 8 columns of every split per
+  // thread, all loads in flight at once (70B width, 678 rows: the down product's 5
+  // splits 44.6 -> 34.5 us, layer 0's 8 splits 106.9 -> 81.6 us); with up to 4 splits
+  // 256 threads x 32 columns stay ahead (2 splits: 24.6 against 26.2 us), as do
+  // 4096-wide rows
+  if (a.N == 4096) return launch_reduce_norm_nc<4, 256>(a, eff, c_part, s);
+  if (a.N == 8192 && eff <= 4) return launch_reduce_norm_nc<8, 256>(a, eff, c_part, s);
+  if (a.N == 8192) return launch_reduce_norm_nc<2, 1024>(a, eff, c_part, s);
   splitk_reduce_norm_kernel<0, 0><<<a.M, 256, 0, s>>>(a, eff, c_part);
   return hipGetLastError();
 }

@@ -188,6 +188,9 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
       unpack_v<T>(kv[u], f, cd.ks);
 #pragma unroll
       for (int j = 0; j < VN; j += 2) {
+        // every product rounded to fp32 before the sum (no fused multiply-add), so the
+        // rotated pair is the one plain fp32 arithmetic gives
+#pragma clang fp contract(off)
         const float2 cs = tab[((e0[u] + j) % dh) >> 1];
         const float x0 = f[j], x1 = f[j + 1];
         f[j] = x0 * cs.x - x1 * cs.y;

@@ -40,22 +40,15 @@ def _rerope_case(shape, wl, paged_src, paged_dst, seed, sample=None):
         ref_v = V[:, toks].astype(np.float64)
         assert np.array_equal(gv, ref_v), f"chunk {c}: V must be copied bitwise"
         # both sides rotate with the same float32 cos/sin (float64 angle, rounded once)
-        # in float32 arithmetic; they may differ only in how the two products and the
-        # sum are rounded (a fused multiply-add on the GPU), i.e. by at most 2^-22 of
-        # |x_2i| + |x_2i+1|.  Rounded to bf16 that is one bf16 ulp of the result, plus
-        # that float32 difference, which exceeds an ulp only where the two products
-        # cancel to a result near zero.
-        src = np.abs(K[:, toks]).astype(np.float64)
-        pair = np.repeat(src[..., 0::2] + src[..., 1::2], 2, axis=-1)
-        bound = 2.0 ** -22 * pair + (_bf16_ulp(ref_k) if shape.dtype == "bf16" else 0.0)
-        if shape.dtype == "bf16":
-            beyond_ulp = float(np.mean(np.abs(gk - ref_k) > _bf16_ulp(ref_k)))
-            assert beyond_ulp <= 1e-4, f"chunk {c}: {beyond_ulp:.2e} of K beyond one bf16 ulp"
-        excess = np.abs(gk - ref_k) - bound
-        assert np.max(excess) <= 0.0, f"chunk {c}: K error exceeds the bound by {np.max(excess)}"
-        if shape.dtype == "bf16":
-            ulps = np.abs(gk - ref_k) / _bf16_ulp(ref_k)
-            say(f"  chunk {c}: {np.mean(ulps == 0):.4f} of K bitwise equal, max {np.max(ulps):.0f} ulp")
+        # and the same float32 operations (each product rounded, then the sum: the
+        # kernel fuses no multiply-add there), then round to the storage dtype, so K is
+        # bitwise the oracle's
+        diff = gk != ref_k
+        if shape.dtype == "bf16" and diff.any():
+            say(f"  chunk {c}: {int(diff.sum())} K elements differ, largest "
+                f"{float(np.max(np.abs(gk - ref_k)[diff] / _bf16_ulp(ref_k)[diff])):.1f} bf16 ulp")
+        assert not diff.any(), f"chunk {c}: {int(diff.sum())} of {diff.size} K elements differ from the oracle"
+        say(f"  chunk {c}: K and V bitwise equal to the oracle ({gk.size} elements)")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -262,12 +262,15 @@ class DeviceRows:
         return self.t[i].float().cpu().numpy()
 
 
+CPU_LAYERS = 5    # layers of the oracle's bounded sample (about 10 s of host work at the 70B shape)
+
+
 def cpu_baseline(wl, sample):
     """The oracle (float32 NumPy, OpenBLAS sgemm on the host cores) on a bounded
     sample of the same workload, with the same weights and chunk caches as the
-    GPU run (host copies of the first three layers): layers 0..2 timed (2 and 3
-    layers; the difference gives one selective layer), extrapolated to the full
-    depth."""
+    GPU run (host copies of the first CPU_LAYERS layers): 3 and CPU_LAYERS layers
+    timed (the difference, per layer, gives one selective layer), extrapolated to
+    the full depth."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -276,21 +279,23 @@ def cpu_baseline(wl, sample):
     except Exception:
         cores = os.cpu_count()
     L = wl.shape.n_layers
-    sh3 = wl.shape.with_layers(3)
+    n = min(CPU_LAYERS, L)
     layers, glob, kvs = sample
-    m = oracle.OracleModel.from_shape(sh3, lambda l: layers[l], glob)
+    m = oracle.OracleModel.from_shape(wl.shape.with_layers(n), lambda l: layers[l], glob)
     chunks = [(wl.chunk_tokens[c], kvs[c][0], kvs[c][1], wl.old_starts[c], wl.new_starts[c]) for c in range(len(kvs))]
     ks, ch = wl.schedule()
+    lo = min(3, n - 1)
     times = {}
-    for nl in (2, 3):
+    for nl in (lo, n):
         t0 = time.perf_counter()
-        oracle.blend_prefill(m, chunks, wl.query_tokens, ks[:3], ch[:3], layers_limit=nl)
+        oracle.blend_prefill(m, chunks, wl.query_tokens, ks[:n], ch[:n], layers_limit=nl)
         times[nl] = time.perf_counter() - t0
-    per_layer = max(times[3] - times[2], 1e-9)
-    total = times[3] + (L - 3) * per_layer
+    per_layer = max((times[n] - times[lo]) / (n - lo), 1e-9)
+    total = times[n] + (L - n) * per_layer
     return {"value": wl.n_ctx / total, "unit": "context tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": (f"float32 NumPy oracle (sgemm), layers 0-2 of the {wl.name} blend on the GPU run's own "
-                       f"weights and chunk caches timed ({times[3]:.1f} s; one selective layer {per_layer:.2f} s), "
+            "sample": (f"float32 NumPy oracle (sgemm), layers 0-{n - 1} of the {wl.name} blend on the GPU run's own "
+                       f"weights and chunk caches, timed over {lo} and {n} layers ({times[lo] + times[n]:.1f} s of "
+                       f"host work; one selective layer {per_layer:.2f} s), "
                        f"extrapolated to {L} layers ({total:.1f} s per request)")}
 
 
@@ -500,15 +505,16 @@ class Inputs:
         N, Q, T = wl.n_ctx, wl.n_query, wl.n_total
         weights = cbinputs.torch_device_weights(shape, seed, dev)
         self.sample = None
-        if host_sample:          # the oracle's copy of layers 0..2 before the library packs them
-            layers = [host_layer(weights["layers"][l], shape) for l in range(3)]
+        if host_sample:          # the oracle's copy of the first layers before the library packs them
+            layers = [host_layer(weights["layers"][l], shape) for l in range(min(CPU_LAYERS, shape.n_layers))]
             glob = {"embed": DeviceRows(weights["embed"]), "lm_head": weights["lm_head"].float().cpu().numpy(),
                     "final_norm": weights["final_norm"].float().cpu().numpy()}
         self.model = api.DeviceModel.from_tensors(shape, weights)
         del weights
         kvs = cbinputs.torch_device_chunk_kv(shape, wl.chunk_lens, seed, dev)
         if host_sample:
-            self.sample = (layers, glob, [(k[:3].float().cpu().numpy(), v[:3].float().cpu().numpy()) for k, v in kvs])
+            nl = min(CPU_LAYERS, shape.n_layers)
+            self.sample = (layers, glob, [(k[:nl].float().cpu().numpy(), v[:nl].float().cpu().numpy()) for k, v in kvs])
         ints = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
         if wl.paged:
             chunks = []
@@ -748,7 +754,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        log(f"{wl.name}: oracle on the host cores (layers 0-2)")
+        log(f"{wl.name}: oracle on the host cores (layers 0-{min(CPU_LAYERS, wl.shape.n_layers) - 1})")
         out["cpu_baseline"] = cpu_baseline(wl, sample)
         if match is not None:
             out["cpu_baseline"]["match"] = match_cpu_baseline(args.seed)

@@ -90,7 +90,16 @@ def oracle_chunks(wl, kvs):
 
 
 def check_sets(gpu_set, ora_set, cand, dev_ora, k, kv_scale_sq, label=""):
-    """HKVD set rule; returns the agreement fraction."""
+    """HKVD set rule; returns the agreement fraction.
+
+    The GPU's k kept positions must be candidates, and every position where the
+    GPU and the oracle decide differently must lie in the tie band around the
+    oracle's k-th largest deviation (|d - d_k| <= 1e-3 d_k + 1e-6 mean |k|^2+|v|^2).
+    The keep/drop decisions must then agree on at least 99% of the candidates,
+    unless more than 1% of the candidates lie in that band: then the deviations
+    do not single out one set (e.g. a single chunk, whose cached K/V differ from
+    fresh ones only by rounding), any top-k within the band is correct, and only
+    its validity is checked."""
     g = set(int(x) for x in gpu_set)
     o = set(int(x) for x in ora_set)
     assert len(g) == k, f"{label}: GPU kept {len(g)} != {k}"
@@ -98,16 +107,22 @@ def check_sets(gpu_set, ora_set, cand, dev_ora, k, kv_scale_sq, label=""):
         return 1.0
     inter = len(g & o)
     cand = np.asarray(cand)
-    dmap = {int(p): float(d) for p, d in zip(cand, dev_ora)}
-    dk = np.sort(np.asarray(dev_ora))[::-1][k - 1]
-    eps_abs = 1e-6 * kv_scale_sq
+    devs = np.asarray(dev_ora, dtype=np.float64)
+    dmap = {int(p): float(d) for p, d in zip(cand, devs)}
+    dk = np.sort(devs)[::-1][k - 1]
+    band = 1e-3 * dk + 1e-6 * kv_scale_sq
     for p in g ^ o:
         assert p in dmap, f"{label}: position {p} is not a candidate"
-        assert abs(dmap[p] - dk) <= 1e-3 * dk + eps_abs, \
-            f"{label}: disagreement at {p}: dev {dmap[p]:.6g} vs k-th {dk:.6g}"
+        assert abs(dmap[p] - dk) <= band, f"{label}: disagreement at {p}: dev {dmap[p]:.6g} vs k-th {dk:.6g}"
     frac = 1.0 - len(g ^ o) / len(cand)
-    assert frac >= 0.99, f"{label}: the keep/drop decision agrees on only {frac:.4f} of the candidates"
-    say(f"  {label}: {inter}/{k} kept positions shared, decision agreement {frac:.4f}")
+    if frac >= 0.99:
+        say(f"  {label}: {inter}/{k} kept positions shared, decision agreement {frac:.4f}")
+    else:
+        in_band = int(np.sum(np.abs(devs - dk) <= band))
+        assert in_band > 0.01 * len(cand), \
+            f"{label}: the keep/drop decision agrees on only {frac:.4f} of the candidates"
+        say(f"  {label}: {in_band} of {len(cand)} candidates tie within the band; the GPU's set is a valid "
+            f"top-{k} of them ({inter}/{k} shared with the oracle's)")
     return frac
 
 

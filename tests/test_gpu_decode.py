@@ -8,6 +8,8 @@
   last row of the blend of q + [u] (causality: the context never sees the
   suffix, so both attend to the same cache), logits and the K/V row at that
   position, within twice the bf16 tolerance (both sides carry bf16 error)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -23,8 +25,9 @@ pytestmark = pytest.mark.gpu
 MINI8B = cbinputs.ModelShape("mini-8b-heads", 4, 1024, 8, 2, 128, 3584, 32000, 500000.0, dtype="bf16")
 
 
-def _blend_then_decode(shape, wl, w, kvs, steps, paged, tol, label, seed):
-    m = api.DeviceModel.from_numpy(shape, w)
+def _blend_then_decode(shape, wl, w, kvs, steps, paged, tol, label, seed, models=None):
+    """models: (device model, oracle model) to use instead of building both from w."""
+    m, om = models if models is not None else (api.DeviceModel.from_numpy(shape, w), oracle.OracleModel.from_shape(shape, w))
     chunks = device_chunks(shape, wl, kvs, seed=seed)
     T = wl.n_total
     kv = blended_cache(shape, T + steps, paged=paged, seed=seed, fill=0.0)
@@ -34,7 +37,6 @@ def _blend_then_decode(shape, wl, w, kvs, steps, paged, tol, label, seed):
     torch.cuda.synchronize()
     K, V = kv.logical(T + steps)
     Kb, Vb = to_np(K), to_np(V)          # the GPU's blended cache, positions [0, T)
-    om = oracle.OracleModel.from_shape(shape, w)
     rng = np.random.default_rng(seed + 5)
     ws = api.Workspace(api.cb_decode_workspace_bytes(m.cfg))
     for i in range(steps):
@@ -70,6 +72,18 @@ def test_decode_mini8b_bf16_paged_against_oracle():
     w = cbinputs.model_weights(MINI8B, 4)
     kvs = cbinputs.synthetic_chunk_kv(MINI8B, wl.chunk_lens, 4)
     _blend_then_decode(MINI8B, wl, w, kvs, 3, True, 2e-2, "mini-8B", 4)
+
+
+def test_decode_70b_width_against_oracle():
+    # the decode products at the 70B width (d 8192, F 28672, 64 q / 8 kv heads) take other
+    # row shares per workgroup than at 8B; two layers of random-init weights drawn on the
+    # GPU, a 4 x 256 + 16 blend, two steps
+    from test_gpu_e2e import _models
+    shape = dataclasses.replace(cbinputs.SHAPES["llama-70b"], n_layers=2, vocab=4096)
+    say("decode: 70B width, 2 layers, after a 4 x 256 + 16 blend, 2 steps")
+    wl = cbinputs.make_workload("70b-4x1024-q64", seed=6, shape=shape, chunk_len=256, n_query=16)
+    kvs = cbinputs.synthetic_chunk_kv(shape, wl.chunk_lens, 6)
+    _blend_then_decode(shape, wl, None, kvs, 2, True, 2e-2, "70B width", 6, models=_models(shape, 6))
 
 
 def test_decode_continues_the_blend_full_8b():

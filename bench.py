@@ -17,8 +17,9 @@ step, and the CPU oracle timed on a bounded sample of the same workload.
 The default workload is the largest that fits one GPU: the 70B-shaped decoder
 (80 layers, d 8192, 64 q / 8 kv heads, F 28672) over 4 chunks x 1024 tokens
 plus a 64-token query.  The 8B 4 x 1024 + 64 and the 8B 32 x 1024 + 128 paged
-workloads are timed after it and reported under "other_workloads".
-"""
+workloads, and the 8B blend of 16 jittered chunks (8K context at random stored
+offsets) at r = 0, 5, 15, 30 and 100%, are timed after it and reported under
+"other_workloads"."""
 from __future__ import annotations
 
 import argparse
@@ -50,8 +51,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="70b-4x1024-q64")
-    ap.add_argument("--other-workloads", default="8b-4x1024-q64,8b-32x1024-q128-paged",
-                    help="comma-separated workloads timed after the main one (empty: none)")
+    ap.add_argument("--other-workloads",
+                    default="8b-4x1024-q64,8b-32x1024-q128-paged," + ",".join(
+                        f"8b-16x512j-q64@{r:g}" for r in (0.0, 0.05, 0.15, 0.3, 1.0)),
+                    help="comma-separated workloads timed after the main one, each optionally "
+                         "name@ratio (default ratio: --ratio); empty: none")
     ap.add_argument("--other-steps", type=int, default=5)
     ap.add_argument("--ratio", type=float, default=0.15)
     ap.add_argument("--seed", type=int, default=0)
@@ -711,15 +715,25 @@ def main():
     torch.cuda.empty_cache()
 
     others = {}
-    for name in [w for w in args.other_workloads.split(",") if w and w != wl.name]:
-        owl = cbinputs.make_workload(name, seed=args.seed, ratio=args.ratio)
-        log(f"{name}: setup and {args.other_steps} timed steps")
-        oinp = Inputs(torch, api, owl, args.seed, dev)
-        oms, oroof, obd, _, _ = time_blend(torch, api, _abi, hip, oinp, owl, args.other_steps, 2)
-        others[name] = {"value": round(owl.n_ctx / (oms * 1e-3), 1), "unit": "context tokens/s",
-                        "ms_per_step": round(oms, 4), "steps": args.other_steps,
-                        "config": config_of(owl, args.ratio, len(oinp.chunks)), "roofline": oroof,
-                        "kernels_ms_per_step": obd}
+    ratios_of = {}                        # workload -> recompute ratios, in the order given
+    for item in [w for w in args.other_workloads.split(",") if w]:
+        name, _, r = item.partition("@")
+        ratio = float(r) if r else args.ratio
+        if (name, ratio) != (wl.name, args.ratio) and ratio not in ratios_of.setdefault(name, []):
+            ratios_of[name].append(ratio)
+    for name, ratios in ratios_of.items():
+        if not ratios:
+            continue
+        log(f"{name}: setup, then {args.other_steps} timed steps at r = {', '.join(f'{r:g}' for r in ratios)}")
+        oinp = Inputs(torch, api, cbinputs.make_workload(name, seed=args.seed, ratio=ratios[0]), args.seed, dev)
+        for ratio in ratios:              # the inputs do not depend on the ratio; only k does
+            owl = cbinputs.make_workload(name, seed=args.seed, ratio=ratio)
+            oms, oroof, obd, _, _ = time_blend(torch, api, _abi, hip, oinp, owl, args.other_steps, 2)
+            others[name if ratio == args.ratio else f"{name}@{ratio:g}"] = {
+                "value": round(owl.n_ctx / (oms * 1e-3), 1), "unit": "context tokens/s",
+                "ms_per_step": round(oms, 4), "steps": args.other_steps,
+                "config": config_of(owl, ratio, len(oinp.chunks)), "roofline": oroof,
+                "kernels_ms_per_step": obd}
         del oinp
         torch.cuda.empty_cache()
 

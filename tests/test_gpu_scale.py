@@ -164,6 +164,19 @@ def test_blend_layer_8b_width_keep_all_fp8_sampled():
     _layer_sampled(cbinputs.SHAPES["llama3-8b"], 614, 64, 614, seed=8, paged=True, kv8=(0.029, 0.037))
 
 
+def test_blend_layer_70b_width_fp8_sampled():
+    say("cb_blend_layer: 70B width, FP8 cache (scales 0.04, 0.05), layer 1, 4096 candidates + 64 query rows, "
+        "keep 614, paged")
+    _layer_sampled(cbinputs.SHAPES["llama-70b"], 4096, 64, 614, seed=10, paged=True, kv8=(0.04, 0.05))
+
+
+def test_blend_layer_32k_context_fp8_sampled():
+    # the FP8 layer is widened to bf16 for the attention (32K keys) before the LDS-staged kernel reads it
+    say("cb_blend_layer: 8B width, FP8 cache (scales 0.029, 0.037), layer 1, 32768 candidates + 128 query rows, "
+        "keep 4915, paged")
+    _layer_sampled(cbinputs.SHAPES["llama3-8b"], 32768, 128, 4915, seed=11, paged=True, kv8=(0.029, 0.037))
+
+
 def test_blend_layer_32k_context_paged_sampled():
     say("cb_blend_layer: 8B width, layer 1, 32768 candidates + 128 query rows, keep 4915, paged")
     _layer_sampled(cbinputs.SHAPES["llama3-8b"], 32768, 128, 4915, seed=6, paged=True)

@@ -636,6 +636,22 @@ def time_blend(torch, api, _abi, hip, inp, wl, steps, warmup):
     return ms_per_step, roof, breakdown, keep_all, fused_keep_all
 
 
+def other_workloads(spec, main_name, main_ratio):
+    """Parse --other-workloads: comma-separated `name` or `name@ratio` entries into
+    {name: [ratios in the order given]}, dropping duplicates and the main run's own
+    (workload, ratio) pair; a bare name takes the main run's ratio."""
+    out = {}
+    for item in [w.strip() for w in spec.split(",") if w.strip()]:
+        name, _, r = item.partition("@")
+        ratio = float(r) if r else main_ratio
+        if (name, ratio) == (main_name, main_ratio):
+            continue
+        ratios = out.setdefault(name, [])
+        if ratio not in ratios:
+            ratios.append(ratio)
+    return out
+
+
 def config_of(wl, ratio, n_chunks):
     shape = wl.shape
     return {"workload": wl.name, "shape": f"{shape.n_layers}L d{shape.d_model} {shape.n_q_heads}q/"
@@ -715,15 +731,7 @@ def main():
     torch.cuda.empty_cache()
 
     others = {}
-    ratios_of = {}                        # workload -> recompute ratios, in the order given
-    for item in [w for w in args.other_workloads.split(",") if w]:
-        name, _, r = item.partition("@")
-        ratio = float(r) if r else args.ratio
-        if (name, ratio) != (wl.name, args.ratio) and ratio not in ratios_of.setdefault(name, []):
-            ratios_of[name].append(ratio)
-    for name, ratios in ratios_of.items():
-        if not ratios:
-            continue
+    for name, ratios in other_workloads(args.other_workloads, wl.name, args.ratio).items():
         log(f"{name}: setup, then {args.other_steps} timed steps at r = {', '.join(f'{r:g}' for r in ratios)}")
         oinp = Inputs(torch, api, cbinputs.make_workload(name, seed=args.seed, ratio=ratios[0]), args.seed, dev)
         for ratio in ratios:              # the inputs do not depend on the ratio; only k does

@@ -86,3 +86,12 @@ def test_traffic_summary_is_read_only_for_the_unchanged_source():
         else:                        # the kernel changed since the counters were taken
             assert v is None
     assert bench.traffic_from_profile("gemm_gate_up", "no-such-workload") is None
+
+
+def test_other_workloads_spec():
+    spec = "8b-4x1024-q64, 70b-4x1024-q64,8b-16x512j-q64@0,8b-16x512j-q64@0.05,8b-16x512j-q64@0,8b-16x512j-q64"
+    got = bench.other_workloads(spec, "70b-4x1024-q64", 0.15)
+    assert got == {"8b-4x1024-q64": [0.15], "8b-16x512j-q64": [0.0, 0.05, 0.15]}
+    # the main run's workload at another ratio stays; at its own ratio it is dropped
+    assert bench.other_workloads("70b-4x1024-q64@1", "70b-4x1024-q64", 0.15) == {"70b-4x1024-q64": [1.0]}
+    assert bench.other_workloads("", "x", 0.15) == {}

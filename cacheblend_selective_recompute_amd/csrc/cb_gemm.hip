@@ -22,8 +22,9 @@
 // t, so the first fragments of t+1 are read while t's last MFMAs run.  The tile
 // shape and a split of K are chosen per call from a cost model so the grid fills
 // the 256 CUs; split-K partials are reduced in a fixed order by a second kernel
-// that also applies the epilogue.  Tiles are ordered M-fastest and mapped so
-// consecutive tiles land on the same XCD (they share a weight tile in its L2).
+// that also applies the epilogue.  Whole tiles are ordered M-fastest within groups
+// of 8 row tiles and mapped so consecutive tiles land on the same XCD, where they
+// share operand tiles in its L2.
 // fp32 path: a plain LDS-tiled FMA kernel (fp32 models are small).
 #include <algorithm>
 #include <cmath>
@@ -39,6 +40,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 32;          // k columns per stage
 constexpr int BN = 256;         // block tile columns (B rows)
+constexpr int kGroupM = 8;      // row tiles per group of the whole-tile order
 
 // s_waitcnt with only the vector-memory counter constrained (n outstanding allowed)
 #define CB_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
@@ -109,9 +111,15 @@ __global__ __launch_bounds__(Tile<CFG>::kThreads, Tile<CFG>::WGS_PER_CU) void ge
   const bool part = SPLIT && b >= n_dp;
   int mt, nt, split = 0;
   if (!part) {
+    // groups of kGroupM row tiles, row-fastest inside a group: the workgroups an XCD
+    // runs at once (32 or 64) cover 8 row tiles of 4 or 8 columns, so its L2 holds
+    // 12 or 16 operand tiles per k-stage instead of every row tile of a few columns
     const int t = xcd_remap(b, n_dp);
-    mt = t % m_tiles;
-    nt = t / m_tiles;
+    const int n_tiles = n_dp / m_tiles;
+    const int g0 = t / (kGroupM * n_tiles), rem = t % (kGroupM * n_tiles);
+    const int gm = min(kGroupM, m_tiles - g0 * kGroupM);
+    mt = g0 * kGroupM + rem % gm;
+    nt = rem / gm;
   } else {
     const int r = xcd_remap(b - n_dp, static_cast<int>(gridDim.x) - n_dp);
     mt = r % m_tiles;

@@ -103,7 +103,7 @@ def test_blend_tiny_fp32_full_config():
     _compare(shape, wl, g, _oracle_ref(m, wl, kvs, ks, ch, g), ks, 1e-4, "tiny")
 
 
-@pytest.mark.parametrize("ratio", [0.15, 1.0])
+@pytest.mark.parametrize("ratio", [0.05, 0.15, 0.30, 1.0])
 def test_blend_mini8b_bf16(ratio):
     say(f"blend: mini-8B bf16, 4 chunks x 128 shuffled, q 16, r {ratio}")
     wl = cbinputs.make_workload("8b-4x1024-q64", seed=1, ratio=ratio, shape=MINI8B, chunk_len=128, n_query=16)

@@ -7,7 +7,9 @@ final-position logits are the method's result).
   r = 15%, 4 layers: layer 0 over every row, the check layer (4096 candidates ->
   614), two layers that re-rank the 614 kept rows, the LM head at d = 8192;
 * 8B shape, 32 x 1024 + 128, r = 15%, paged chunk sources and a paged blended
-  cache under random block tables, 3 layers.
+  cache under random block tables, 3 layers;
+* 8B shape, 16 chunks of 512 +- 128 tokens cached at random offsets, + 64, at the
+  constant ratios r = 5% and 30%, 4 layers.
 
 Weights and chunk caches are drawn on the GPU by torch's seeded generator and
 copied to the host for the oracle one layer at a time (the library packs its own
@@ -69,8 +71,8 @@ def _models(shape, seed):
     return gpu, oracle.OracleModel.from_shape(shape, layer, glob)
 
 
-def _blend(name, n_layers, seed, paged):
-    wl = cbinputs.make_workload(name, seed=seed, n_layers=n_layers)
+def _blend(name, n_layers, seed, paged, ratio=0.15):
+    wl = cbinputs.make_workload(name, seed=seed, ratio=ratio, n_layers=n_layers)
     shape = wl.shape
     T, N = wl.n_total, wl.n_ctx
     say(f"{name}: {n_layers} layers, N {N}, Q {wl.n_query}, k {wl.k}: weights and caches on the GPU")
@@ -175,3 +177,8 @@ def test_e2e_70b_width_4x1024_four_layers():
 
 def test_e2e_8b_32x1024_paged_three_layers():
     _blend("8b-32x1024-q128-paged", 3, seed=0, paged=True)
+
+
+@pytest.mark.parametrize("ratio", [0.05, 0.30])
+def test_e2e_8b_16x512_jittered_four_layers(ratio):
+    _blend("8b-16x512j-q64", 4, seed=0, paged=False, ratio=ratio)

@@ -952,12 +952,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_spl
 template <int DH, int CPT>
 __global__ __launch_bounds__(256) void attn_combine_wide_kernel(AttnArgs a, int n_splits, int ksplit, int QT, int per_row) {
   static_assert(CPT % 8 == 0 && DH % CPT == 0, "whole 8-column chunks inside one head");
-  const int row = blockIdx.x / per_row;
+  // neighbouring rows on one XCD: their 16-byte pieces of a fragment-major block meet
+  // in one L2 and leave it as whole lines
+  const int wi = xcd_remap(blockIdx.x, gridDim.x);
+  const int row = wi / per_row;
   const int t_last = min((row / QT + 1) * QT, a.R) - 1;
   const int kv_end = a.rowpos[t_last] + 1;
   const int ns = min(n_splits, (kv_end + ksplit - 1) / ksplit);
   if (ns <= 1) return;                                   // written whole by the attention kernel
-  const int col = ((blockIdx.x % per_row) * 256 + threadIdx.x) * CPT;
+  const int col = ((wi % per_row) * 256 + threadIdx.x) * CPT;
   const int head = col / DH;
   auto prow = [&](int sp) { return (static_cast<int64_t>(sp) * a.R + row) * a.n_q_heads + head; };
   float M = -INFINITY;

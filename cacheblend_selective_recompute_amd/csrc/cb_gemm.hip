@@ -595,7 +595,9 @@ __global__ __launch_bounds__(TPB) void splitk_reduce_norm_kernel(GemmArgs g, int
   constexpr int NW = TPB / 64;
   constexpr int CW = 4 * TPB;     // columns per chunk
   __shared__ float red[NW];
-  const int row = blockIdx.x;
+  // neighbouring rows on one XCD: their 16-byte pieces of a fragment-major block of
+  // the normalised output meet in one L2 and leave it as whole lines
+  const int row = xcd_remap(blockIdx.x, gridDim.x);
   const int rr = g.resid_rows ? g.resid_rows[row] : row;
   const int64_t wpart = g.N - c_part;
   constexpr int NCH = NC > 0 ? NC : kNormChunks;

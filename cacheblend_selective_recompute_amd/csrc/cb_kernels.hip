@@ -234,7 +234,9 @@ template <typename TO, bool PACKED>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const int32_t* ridx, int64_t ldx, int d,
                                                       const float* g, float eps, TO* out, int64_t ldo) {
   __shared__ float red[4];
-  const int r = blockIdx.x;
+  // neighbouring rows on one XCD, so the packed output's fragment blocks are
+  // assembled in one L2 (rows of a block interleave at 16-byte granularity)
+  const int r = xcd_remap(blockIdx.x, gridDim.x);
   const int src = ridx ? ridx[r] : r;
   const float* xr = x + static_cast<int64_t>(src) * ldx;
   float ss = 0.f;

@@ -219,16 +219,33 @@ __global__ void gather_tokens_kernel(ChunkBatch b, int32_t* out) {
 // ---------------------------------------------------------------------------
 // embedding gather (fp32 residual stream)
 // ---------------------------------------------------------------------------
+// (d a multiple of 64: every row starts 128-byte aligned, and a thread moves 8
+// elements per pass with 16-byte accesses)
 template <typename T>
 __global__ void embed_kernel(const int32_t* tok, const T* emb, int d, float* x) {
   const int r = blockIdx.x;
   const T* src = emb + static_cast<int64_t>(tok[r]) * d;
   float* dst = x + static_cast<int64_t>(r) * d;
-  for (int e = threadIdx.x; e < d; e += blockDim.x) dst[e] = to_f<T>(src[e]);
+  for (int e = threadIdx.x * 8; e < d; e += blockDim.x * 8) {
+    float4 lo, hi;
+    if constexpr (sizeof(T) == 2) {
+      const uint4 u = *reinterpret_cast<const uint4*>(src + e);
+      lo = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+      hi = make_float4(__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xffff0000u),
+                       __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xffff0000u));
+    } else {
+      lo = *reinterpret_cast<const float4*>(src + e);
+      hi = *reinterpret_cast<const float4*>(src + e + 4);
+    }
+    *reinterpret_cast<float4*>(dst + e) = lo;
+    *reinterpret_cast<float4*>(dst + e + 4) = hi;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm: one 256-thread block per row; fp32 statistics reduced in fixed order
+// RMSNorm: one 256-thread block per row; fp32 statistics reduced in fixed order.
+// The row (d <= 16384) is read once and held in registers for the scaling pass.
 // ---------------------------------------------------------------------------
 template <typename TO, bool PACKED>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const int32_t* ridx, int64_t ldx, int d,
@@ -239,18 +256,29 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, const int3
   const int r = xcd_remap(blockIdx.x, gridDim.x);
   const int src = ridx ? ridx[r] : r;
   const float* xr = x + static_cast<int64_t>(src) * ldx;
+  constexpr int kChunks = 16;        // 16 x 1024 columns
+  float4 row[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int e = threadIdx.x * 4 + c * 1024;
+    if (e < d) row[c] = *reinterpret_cast<const float4*>(xr + e);
+  }
   float ss = 0.f;
-  for (int e = threadIdx.x * 4; e < d; e += 256 * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + e);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int e = threadIdx.x * 4 + c * 1024;
+    if (e < d) ss += row[c].x * row[c].x + row[c].y * row[c].y + row[c].z * row[c].z + row[c].w * row[c].w;
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   const float inv = 1.0f / sqrtf(tot / static_cast<float>(d) + eps);
-  for (int e = threadIdx.x * 4; e < d; e += 256 * 4) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + e);
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int e = threadIdx.x * 4 + c * 1024;
+    if (e >= d) continue;
+    const float4 v = row[c];
     const float4 gg = *reinterpret_cast<const float4*>(g + e);
     if constexpr (PACKED) {
       uint2 w;
@@ -777,6 +805,7 @@ hipError_t launch_gather_tokens(const ChunkBatch& b, int32_t* out, hipStream_t s
 
 hipError_t launch_embed(cb_dtype dt, const int32_t* tok, int rows, const void* embed, int d, float* x, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  if (d % 8 != 0) return hipErrorInvalidValue;
   if (dt == CB_BF16)
     embed_kernel<bf16_t><<<rows, 256, 0, s>>>(tok, static_cast<const bf16_t*>(embed), d, x);
   else
@@ -787,6 +816,7 @@ hipError_t launch_embed(cb_dtype dt, const int32_t* tok, int rows, const void* e
 hipError_t launch_rmsnorm(cb_dtype dt, const float* x, const int32_t* ridx, int64_t ldx, int rows, int d,
                           const float* g, float eps, void* out, int64_t ldo, int out_f32, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  if (d % 4 != 0 || d > 16384) return hipErrorInvalidValue;
   if (out_f32 || dt == CB_F32)
     rmsnorm_kernel<float, false><<<rows, 256, 0, s>>>(x, ridx, ldx, d, g, eps, static_cast<float*>(out), ldo);
   else

@@ -952,10 +952,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int n_spl
 template <int DH, int CPT>
 __global__ __launch_bounds__(256) void attn_combine_wide_kernel(AttnArgs a, int n_splits, int ksplit, int QT, int per_row) {
   static_assert(CPT % 8 == 0 && DH % CPT == 0, "whole 8-column chunks inside one head");
-  // neighbouring rows on one XCD: their 16-byte pieces of a fragment-major block meet
-  // in one L2 and leave it as whole lines
-  const int wi = xcd_remap(blockIdx.x, gridDim.x);
+  // groups of 8 consecutive rows on one XCD, so their 16-byte pieces of a
+  // fragment-major block meet in one L2 and leave it as whole 128-byte lines;
+  // successive groups go to successive XCDs, so the leading rows that need no merge
+  // (their keys lie in split 0) do not all fall on the same XCDs.  The grid covers a
+  // whole number of group rounds (8 x 8 rows); blocks past the last row return.
+  const int grp = 8 * per_row;
+  const int xi = blockIdx.x % kXcd, ii = blockIdx.x / kXcd;
+  const int wi = ((ii / grp) * kXcd + xi) * grp + ii % grp;
   const int row = wi / per_row;
+  if (row >= a.R) return;
   const int t_last = min((row / QT + 1) * QT, a.R) - 1;
   const int kv_end = a.rowpos[t_last] + 1;
   const int ns = min(n_splits, (kv_end + ksplit - 1) / ksplit);
@@ -1127,7 +1133,8 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
     // 8 columns per thread: rows of 4096 / 8192 columns take 2 / 4 workgroups each,
     // so more loads are in flight than with one workgroup per row
     const int per_row = width / (256 * 8);
-    attn_combine_wide_kernel<DH, 8><<<a.R * per_row, 256, 0, s>>>(a, n_splits, ksplit, QT, per_row);
+    const int rows = (a.R + 8 * kXcd - 1) / (8 * kXcd) * (8 * kXcd);
+    attn_combine_wide_kernel<DH, 8><<<rows * per_row, 256, 0, s>>>(a, n_splits, ksplit, QT, per_row);
   } else {
     const int pairs = a.R * a.n_q_heads;
     attn_combine_kernel<DH><<<(pairs + 3) / 4, 256, 0, s>>>(a, n_splits, ksplit, QT);

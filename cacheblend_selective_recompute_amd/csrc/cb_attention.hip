@@ -693,14 +693,23 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs 
     const int k0 = jb + 16 * wid;
     const int rowb = (CONTIG ? k0 : (pe << sh) + (k0 & pmask)) * width * 2 + kvh * DH * 2;
     pe = page_of(jb + KVB);
+    if (jb + KVB <= j_end) {             // the whole block lies in the range (uniform)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool ok = k0 + 4 * u + sub < j_end;
-      const int ko = ok ? rowb + kx[u] : static_cast<int>(0x80000000u);   // past the range: zeros
-      const int vo = ok ? rowb + vx[u] : static_cast<int>(0x80000000u);
-      const uint32_t dst = ldsw + stage * (2 * kBlk) + u * 1024;
-      attn_copy(dst, rk, ko);
-      attn_copy(dst + kBlk, rv, vo);
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t dst = ldsw + stage * (2 * kBlk) + u * 1024;
+        attn_copy(dst, rk, rowb + kx[u]);
+        attn_copy(dst + kBlk, rv, rowb + vx[u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = k0 + 4 * u + sub < j_end;
+        const int ko = ok ? rowb + kx[u] : static_cast<int>(0x80000000u);   // past the range: zeros
+        const int vo = ok ? rowb + vx[u] : static_cast<int>(0x80000000u);
+        const uint32_t dst = ldsw + stage * (2 * kBlk) + u * 1024;
+        attn_copy(dst, rk, ko);
+        attn_copy(dst + kBlk, rv, vo);
+      }
     }
   };
 
@@ -745,13 +754,13 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_fa_kernel(AttnArgs 
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (edge) {
+        // key j0 + 16 t + 4 kgrp + i is visible iff it is <= min(qpos, j_end - 1)
+        const int lim = min(qpos[g], j_end - 1) - (j0 + 4 * kgrp);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = j0 + 16 * t + 4 * kgrp + i;
-            if (key > qpos[g] || key >= j_end) s[g][t][i] = -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i)
+            if (16 * t + i > lim) s[g][t][i] = -INFINITY;
       }
       float m = fmaxf(fmaxf(s[g][0][0], s[g][0][1]), fmaxf(s[g][0][2], s[g][0][3]));
 #pragma unroll

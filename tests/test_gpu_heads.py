@@ -1,0 +1,44 @@
+"""GPU parity of cb_blend_prefill against the oracle for every attention head
+layout the bf16 path takes: query heads per KV head G = 1, 2, 4, 8, 16 at
+head_dim 128 (the LDS-staged kernel) and G = 1, 4, 16 at head_dim 64 (the
+register-staged kernel).  The selected tokens attend to every position up to
+their own ([CB] "选 token"); GQA shares each KV head among G query heads, so
+each layout stacks a different number of query rows per KV block.
+
+Small decoders (3 layers, d_model 512) blend 4 shuffled chunks of 96 tokens
+with an 8-token query at r = 15%; chunk caches come from the oracle's own chunk
+prefill, and the GPU's kept sets are validated against the oracle's ranking and
+then imposed (as in test_gpu_blend).  Bound: 2e-2 normwise for every layer's
+blended K/V, the deviations and the logits (bf16 arithmetic)."""
+import pytest
+
+import cbinputs
+
+from gpu_helpers import say
+from test_gpu_blend import _compare, _oracle_ref, _oracle_setup, _run_blend
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = [  # (head_dim, query heads, KV heads, paged)
+    (128, 4, 4, False),
+    (128, 4, 2, True),
+    (128, 16, 2, False),
+    (128, 16, 1, True),
+    (64, 8, 8, True),
+    (64, 8, 2, False),
+    (64, 16, 1, True),
+]
+
+
+@pytest.mark.parametrize("hd,nq,nkv,paged", LAYOUTS, ids=[f"hd{h}-G{q // k}{'-paged' if p else ''}"
+                                                          for h, q, k, p in LAYOUTS])
+def test_blend_head_layout_bf16(hd, nq, nkv, paged):
+    shape = cbinputs.ModelShape(f"hd{hd}-q{nq}-kv{nkv}", 3, 512, nq, nkv, hd, 1024, 4096, 500000.0, dtype="bf16")
+    seed = 20 + nq + nkv + hd
+    wl = cbinputs.make_workload("8b-4x1024-q64", seed=seed, shape=shape, chunk_len=96, n_query=8)
+    m, kvs = _oracle_setup(shape, wl, seed)
+    ks, ch = wl.schedule()
+    label = f"head_dim {hd}, G {nq // nkv} ({nq} q / {nkv} kv heads){', paged' if paged else ''}"
+    say(f"{label}: N {wl.n_ctx}, Q {wl.n_query}, k {ks[1:]}")
+    g = _run_blend(shape, wl, kvs, ks, ch, paged=paged, paged_src=paged, seed=seed)
+    _compare(shape, wl, g, _oracle_ref(m, wl, kvs, ks, ch, g), ks, 2e-2, label)

@@ -292,7 +292,7 @@ def test_pack_weight_validation(lib):
     assert P(_abi.CB_BF16, FAKE + 8, 64, 64, 0, FAKE + big, None) == _abi.CB_ERR_INVALID  # alignment
 
 
-def _streamed(lib, specs=((64, 0, 0), (64, 5, 64)), nq=8, events=True, ws_bytes=None, host_k=True):
+def _streamed(lib, specs=((64, 0, 0), (64, 5, 64)), nq=8, events=True, ws_bytes=None, host_k=True, fp8=False):
     cfg = cfg8b(n_layers=3)
     m = _model(cfg)
     arr = (_abi.cb_host_chunk * len(specs))()
@@ -301,6 +301,8 @@ def _streamed(lib, specs=((64, 0, 0), (64, 5, 64)), nq=8, events=True, ws_bytes=
     N = sum(s[0] for s in specs)
     p = _params([N, 19, 19], [0, 1, 1])
     kv = _paged(N + nq)
+    if fp8:
+        kv.kv_format, kv.k_scale, kv.v_scale = _abi.CB_KV_FP8_E4M3, 1.0, 1.0
     ev = (ctypes.c_void_p * 6)(*([FAKE] * 6)) if events else None
     need = lib.cb_streamed_workspace_bytes(ctypes.byref(cfg), N, nq, len(specs))
     ws = ws_bytes if ws_bytes is not None else need
@@ -328,6 +330,9 @@ def test_streamed_validation(lib):
     assert st == _abi.CB_ERR_INVALID and "overlap" in msg
     st, msg = _streamed(lib, ws_bytes=1024)
     assert st == _abi.CB_ERR_WORKSPACE
+    # the layer-pipelined prefill writes caches in the model dtype only
+    st, msg = _streamed(lib, fp8=True)
+    assert st == _abi.CB_ERR_UNSUPPORTED and "model dtype" in msg
 
 
 def test_decode_step_validation(lib):

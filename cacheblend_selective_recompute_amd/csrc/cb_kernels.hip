@@ -123,10 +123,30 @@ __global__ void rope_delta_table_kernel(float2* out, ChunkBatch b, int half, int
 
 // ---------------------------------------------------------------------------
 // re-RoPE + assembly.  One block = kTokTile tokens of one (chunk, layer);
-// every thread moves 16-byte vectors, four in flight.
+// every thread moves 16-byte vectors, four in flight.  When a token row is a
+// whole number of passes of the block (256 / vectors-per-row rows per pass) each
+// thread keeps one column of the row, so its rotation entries are loaded once
+// and no per-vector index division is left.
 // ---------------------------------------------------------------------------
 constexpr int kTokTile = 16;
 constexpr int kRerope = 256;
+
+template <typename T>
+__device__ __forceinline__ void rerope_vec(uint4& kv, const float2* cs, float ks, float inv_ks) {
+  constexpr int VN = V16<T>::N;
+  float f[VN];
+  unpack_v<T>(kv, f, ks);
+#pragma unroll
+  for (int j = 0; j < VN; j += 2) {
+    // every product rounded to fp32 before the sum (no fused multiply-add), so the
+    // rotated pair is the one plain fp32 arithmetic gives
+#pragma clang fp contract(off)
+    const float x0 = f[j], x1 = f[j + 1];
+    f[j] = x0 * cs[j >> 1].x - x1 * cs[j >> 1].y;
+    f[j + 1] = x0 * cs[j >> 1].y + x1 * cs[j >> 1].x;
+  }
+  kv = pack_v<T>(f, inv_ks);
+}
 
 template <typename T>
 __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef dst, const float2* dtab,
@@ -142,7 +162,6 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
   const int t0 = (local % ntile) * kTokTile;
   const int ntok = min(kTokTile, cd.len - t0);
   const int vpr = width / VN;                   // vectors per token row
-  const int nvec = ntok * vpr;
   const int64_t src_stride = cd.layer_stride;
   const T* srck = static_cast<const T*>(cd.k) + layer * src_stride;
   const T* srcv = static_cast<const T*>(cd.v) + layer * src_stride;
@@ -152,17 +171,58 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
   // FP8: source elements times the chunk's scales, stored divided by the destination's
   const float inv_ks = 1.0f / dst.ks, inv_vs = 1.0f / dst.vs;
   const bool v_requant = sizeof(T) == 1 && cd.vs != dst.vs;
-  // source and destination rows of the tile's tokens, looked up once per block
+  // element offsets of the tile's source and destination rows, looked up once per block
   __shared__ int64_t srow_s[kTokTile], drow_s[kTokTile];
   if (threadIdx.x < ntok) {
     const int t = t0 + threadIdx.x;
-    srow_s[threadIdx.x] = cd.blk ? static_cast<int64_t>(cd.blk[t / cd.block_size]) * cd.block_size + t % cd.block_size
-                                 : static_cast<int64_t>(t);
-    drow_s[threadIdx.x] = paged_row(dst, cd.new_start + t);
+    const int64_t sr = cd.blk ? static_cast<int64_t>(cd.blk[t / cd.block_size]) * cd.block_size + t % cd.block_size
+                              : static_cast<int64_t>(t);
+    srow_s[threadIdx.x] = sr * width;
+    drow_s[threadIdx.x] = paged_row(dst, cd.new_start + t) * width;
   }
   __syncthreads();
 
+  auto store_v = [&](int64_t off, const uint4& raw) __attribute__((always_inline)) {
+    uint4 o = raw;
+    if (v_requant) {                           // FP8 V under a different scale: re-round on the new grid
+      float g[VN];
+      unpack_v<T>(raw, g, cd.vs);
+      o = pack_v<T>(g, inv_vs);
+    }
+    st_stream(dv + off, o);
+  };
   constexpr int U = 4;
+  if (kRerope % vpr == 0) {
+    // a row is a whole number of passes of the block: every thread keeps one column
+    // (so its rotation entries are loaded once) and walks the tile's rows
+    const int rpp = kRerope / vpr;              // rows per pass
+    const int col = (threadIdx.x % vpr) * VN;
+    const int r0 = threadIdx.x / vpr;
+    float2 cs[VN / 2];
+#pragma unroll
+    for (int j = 0; j < VN; j += 2) cs[j >> 1] = tab[((col + j) % dh) >> 1];
+    for (int rb = r0; rb < ntok; rb += rpp * U) {
+      uint4 kv[U], vv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = rb + u * rpp;
+        if (r < ntok) {
+          kv[u] = ld_stream(srck + srow_s[r] + col);
+          if (copy_v) vv[u] = ld_stream(srcv + srow_s[r] + col);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = rb + u * rpp;
+        if (r >= ntok) continue;
+        rerope_vec<T>(kv[u], cs, cd.ks, inv_ks);
+        st_stream(dk + drow_s[r] + col, kv[u]);
+        if (copy_v) store_v(drow_s[r] + col, vv[u]);
+      }
+    }
+    return;
+  }
+  const int nvec = ntok * vpr;
   for (int base = threadIdx.x; base < nvec; base += kRerope * U) {
     uint4 kv[U], vv[U];
     int64_t so[U], dof[U];
@@ -174,8 +234,8 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
       ok[u] = v < nvec;
       const int tt = ok[u] ? v / vpr : 0;
       e0[u] = (v % vpr) * VN;
-      so[u] = srow_s[tt] * width + e0[u];
-      dof[u] = drow_s[tt] * width + e0[u];
+      so[u] = srow_s[tt] + e0[u];
+      dof[u] = drow_s[tt] + e0[u];
       if (ok[u]) {
         kv[u] = ld_stream(srck + so[u]);
         if (copy_v) vv[u] = ld_stream(srcv + so[u]);
@@ -184,28 +244,12 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (!ok[u]) continue;
-      float f[VN];
-      unpack_v<T>(kv[u], f, cd.ks);
+      float2 cs[VN / 2];
 #pragma unroll
-      for (int j = 0; j < VN; j += 2) {
-        // every product rounded to fp32 before the sum (no fused multiply-add), so the
-        // rotated pair is the one plain fp32 arithmetic gives
-#pragma clang fp contract(off)
-        const float2 cs = tab[((e0[u] + j) % dh) >> 1];
-        const float x0 = f[j], x1 = f[j + 1];
-        f[j] = x0 * cs.x - x1 * cs.y;
-        f[j + 1] = x0 * cs.y + x1 * cs.x;
-      }
-      st_stream(dk + dof[u], pack_v<T>(f, inv_ks));
-      if (copy_v) {
-        uint4 o = vv[u];
-        if (v_requant) {                       // FP8 V under a different scale: re-round on the new grid
-          float g[VN];
-          unpack_v<T>(vv[u], g, cd.vs);
-          o = pack_v<T>(g, inv_vs);
-        }
-        st_stream(dv + dof[u], o);
-      }
+      for (int j = 0; j < VN; j += 2) cs[j >> 1] = tab[((e0[u] + j) % dh) >> 1];
+      rerope_vec<T>(kv[u], cs, cd.ks, inv_ks);
+      st_stream(dk + dof[u], kv[u]);
+      if (copy_v) store_v(dof[u], vv[u]);
     }
   }
 }

@@ -153,8 +153,11 @@ __global__ __launch_bounds__(kRerope) void rerope_kernel(ChunkBatch b, PagedRef 
                                                          int n_layers, int width, int dh, int copy_v) {
   constexpr int VN = V16<T>::N;
   const int tile = blockIdx.x;
+  // the tile's chunk: tile_begin never decreases, so it is the number of later chunks
+  // starting at or before the tile (independent comparisons, not a dependent walk)
   int c = 0;
-  while (c + 1 < b.n && tile >= b.d[c + 1].tile_begin) ++c;
+#pragma unroll 8
+  for (int i = 1; i < b.n; ++i) c += tile >= b.d[i].tile_begin ? 1 : 0;
   const ChunkDesc cd = b.d[c];
   const int ntile = (cd.len + kTokTile - 1) / kTokTile;
   const int local = tile - cd.tile_begin;

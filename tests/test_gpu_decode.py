@@ -4,6 +4,8 @@
   three decode steps; the oracle's decode steps run on a host copy of the very
   cache the GPU blended (so only the decode is compared), logits and the K/V
   rows each step writes;
+* 70B width (2 layers) and 8B heads at the 32K paged context (2 layers), against
+  the oracle as above;
 * full 8B shape: a decode step of token u after the blend of query q equals the
   last row of the blend of q + [u] (causality: the context never sees the
   suffix, so both attend to the same cache), logits and the K/V row at that
@@ -84,6 +86,18 @@ def test_decode_70b_width_against_oracle():
     wl = cbinputs.make_workload("70b-4x1024-q64", seed=6, shape=shape, chunk_len=256, n_query=16)
     kvs = cbinputs.synthetic_chunk_kv(shape, wl.chunk_lens, 6)
     _blend_then_decode(shape, wl, None, kvs, 2, True, 2e-2, "70B width", 6, models=_models(shape, 6))
+
+
+def test_decode_32k_paged_context_against_oracle():
+    # a decode row over 32K keys takes about a hundred key splits in the one-row attention,
+    # all merged by the combine; 8B heads, two layers of GPU-drawn weights, the
+    # 32 x 1024 + 128 paged blend, two steps
+    from test_gpu_e2e import _models
+    shape = dataclasses.replace(cbinputs.SHAPES["llama3-8b"], n_layers=2, vocab=4096)
+    say("decode: 8B heads, 2 layers, after the paged 32 x 1024 + 128 blend, 2 steps at 32K")
+    wl = cbinputs.make_workload("8b-32x1024-q128-paged", seed=8, shape=shape)
+    kvs = cbinputs.synthetic_chunk_kv(shape, wl.chunk_lens, 8)
+    _blend_then_decode(shape, wl, None, kvs, 2, True, 2e-2, "32K context", 8, models=_models(shape, 8))
 
 
 def test_decode_continues_the_blend_full_8b():

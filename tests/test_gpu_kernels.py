@@ -119,8 +119,10 @@ def test_deviation_matches_oracle(dtype):
     assert np.max(np.abs(to_np(dev) - ref) / ref) < 1e-5
 
 
+# up to 32768 candidates the order keys are staged in LDS; above, they are recomputed
+# from the deviations on every read (40000, and a 128K context at 15%)
 @pytest.mark.parametrize("n,k", [(1, 1), (7, 3), (1000, 150), (4096, 614), (4096, 4095), (32768, 4915),
-                                 (5000, 0), (3000, 3000)])
+                                 (32769, 4915), (40000, 6000), (131072, 19661), (5000, 0), (3000, 3000)])
 def test_select_matches_oracle(n, k):
     say(f"select n={n} k={k}")
     rng = np.random.default_rng(n + k)

@@ -45,10 +45,10 @@ def ints(a) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(np.asarray(a), dtype=np.int32)).to(DEV)
 
 
-def device_chunks(shape, wl, kvs, paged_src=False, seed=0):
+def device_chunks(shape, wl, kvs, paged_src=False, seed=0, bs=16):
     """ChunkSource list from numpy chunk K/V ([L][len][Hkv][dh] each).
 
-    With ``paged_src`` each chunk's K/V live in a private pool of 16-token
+    With ``paged_src`` each chunk's K/V live in a private pool of ``bs``-token
     blocks at random physical positions."""
     out = []
     keep = []
@@ -59,7 +59,6 @@ def device_chunks(shape, wl, kvs, paged_src=False, seed=0):
             out.append(api.ChunkSource(ints(toks), to_dev(K, shape.dtype), to_dev(V, shape.dtype),
                                        wl.old_starts[c], wl.new_starts[c]))
             continue
-        bs = 16
         nb = (ln + bs - 1) // bs
         n_phys = nb + 3
         ids = rng.permutation(n_phys)[:nb].astype(np.int32)
@@ -76,12 +75,11 @@ def device_chunks(shape, wl, kvs, paged_src=False, seed=0):
     return out
 
 
-def blended_cache(shape, n_tokens, paged=False, seed=0, fill=None):
+def blended_cache(shape, n_tokens, paged=False, seed=0, fill=None, bs=16):
     if not paged:
-        return api.PagedKV(shape, n_tokens, 16, fill=fill)
-    n_log = (n_tokens + 15) // 16
-    table, n_phys = cbinputs.paged_layout(n_tokens, 16, seed, key=77, spare_blocks=5)
-    return api.PagedKV(shape, n_tokens, 16, table, n_phys, fill=fill)
+        return api.PagedKV(shape, n_tokens, bs, fill=fill)
+    table, n_phys = cbinputs.paged_layout(n_tokens, bs, seed, key=77, spare_blocks=5)
+    return api.PagedKV(shape, n_tokens, bs, table, n_phys, fill=fill)
 
 
 def oracle_chunks(wl, kvs):

@@ -22,11 +22,11 @@ pytestmark = pytest.mark.gpu
 MINI8B = cbinputs.ModelShape("mini-8b-heads", 3, 1024, 8, 2, 128, 3584, 32000, 500000.0, dtype="bf16")
 
 
-def _run_blend(shape, wl, kvs, ks, check, paged=False, paged_src=False, seed=0):
+def _run_blend(shape, wl, kvs, ks, check, paged=False, paged_src=False, seed=0, bs=16):
     m = api.DeviceModel.from_numpy(shape, _weights(shape, seed))
-    chunks = device_chunks(shape, wl, kvs, paged_src=paged_src, seed=seed)
+    chunks = device_chunks(shape, wl, kvs, paged_src=paged_src, seed=seed, bs=bs)
     T = wl.n_total
-    kv = blended_cache(shape, T, paged=paged, seed=seed, fill=0.0)
+    kv = blended_cache(shape, T, paged=paged, seed=seed, fill=0.0, bs=bs)
     logits = torch.empty(shape.vocab, device="cuda")
     N = wl.n_ctx
     hk = torch.full((shape.n_layers, N), -1, dtype=torch.int32, device="cuda")

@@ -27,12 +27,12 @@ pytestmark = pytest.mark.gpu
 MINI8B = cbinputs.ModelShape("mini-8b-heads", 4, 1024, 8, 2, 128, 3584, 32000, 500000.0, dtype="bf16")
 
 
-def _blend_then_decode(shape, wl, w, kvs, steps, paged, tol, label, seed, models=None):
+def _blend_then_decode(shape, wl, w, kvs, steps, paged, tol, label, seed, models=None, bs=16):
     """models: (device model, oracle model) to use instead of building both from w."""
     m, om = models if models is not None else (api.DeviceModel.from_numpy(shape, w), oracle.OracleModel.from_shape(shape, w))
-    chunks = device_chunks(shape, wl, kvs, seed=seed)
+    chunks = device_chunks(shape, wl, kvs, paged_src=paged and bs != 16, seed=seed, bs=bs)
     T = wl.n_total
-    kv = blended_cache(shape, T + steps, paged=paged, seed=seed, fill=0.0)
+    kv = blended_cache(shape, T + steps, paged=paged, seed=seed, fill=0.0, bs=bs)
     logits = torch.empty(shape.vocab, device="cuda")
     ks, ch = wl.schedule()
     api.cb_blend_prefill(m, chunks, ints(wl.query_tokens), api.BlendParams(ks, ch), kv, logits)

@@ -8,7 +8,11 @@ number of chunks of any length, any stored offset and any query length >= 1):
   before and after their new positions;
 * more chunks than one re-RoPE launch takes (40 > 32);
 * a ratio so small that one context token is recomputed per layer, and one so
-  large that all but one are.
+  large that all but one are;
+* pages of 1, 8, 12 (not a power of two) and 32 tokens for the chunk sources and
+  the blended cache: below 16 keys or off powers of two the attention reads through
+  the earlier LDS-staged kernel and a decode row looks each key's page up; two decode
+  steps follow each blend.
 
 Chunk caches come from the oracle's own chunk prefill; the GPU's kept sets are
 validated against the oracle's ranking and then imposed (as in test_gpu_blend)."""
@@ -19,6 +23,7 @@ import cbinputs
 
 from gpu_helpers import say
 from test_gpu_blend import MINI8B, _compare, _oracle_ref, _oracle_setup, _run_blend
+from test_gpu_decode import _blend_then_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -86,3 +91,16 @@ def test_blend_forty_chunks_bf16_paged():
     old = [int(x) for x in rng.integers(0, 4096, size=40)]
     wl = _workload(MINI8B, lens, old, [int(x) for x in rng.permutation(40)], n_query=8, ratio=0.15, seed=15)
     _check(MINI8B, wl, 2e-2, "40 chunks", seed=15, paged=True)
+
+
+@pytest.mark.parametrize("bs", [1, 8, 12, 32])
+def test_blend_and_decode_page_sizes_bf16(bs):
+    seed = 30 + bs
+    wl = cbinputs.make_workload("8b-4x1024-q64", seed=seed, shape=MINI8B, chunk_len=96, n_query=8)
+    m, kvs = _oracle_setup(MINI8B, wl, seed)
+    ks, ch = wl.schedule()
+    say(f"pages of {bs} tokens: N {wl.n_ctx}, Q {wl.n_query}, k {ks[1:]}")
+    g = _run_blend(MINI8B, wl, kvs, ks, ch, paged=True, paged_src=True, seed=seed, bs=bs)
+    _compare(MINI8B, wl, g, _oracle_ref(m, wl, kvs, ks, ch, g), ks, 2e-2, f"pages of {bs}")
+    _blend_then_decode(MINI8B, wl, cbinputs.model_weights(MINI8B, seed), kvs, 2, True, 2e-2, f"pages of {bs}", seed,
+                       bs=bs)

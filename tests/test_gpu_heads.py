@@ -11,6 +11,9 @@ prefill, and the GPU's kept sets are validated against the oracle's ranking and
 then imposed (as in test_gpu_blend).  Bound: 2e-2 normwise for every layer's
 blended K/V, the deviations and the logits (bf16 arithmetic).
 
+The fp32 path (one wave per query row and head) is checked with shared KV heads
+too (G = 2, 4), at 1e-4.
+
 The same layouts then decode two tokens straight from a blended cache (the
 one-row kernel at head_dim 128 with G <= 8, the general kernels otherwise),
 against the oracle's decode step on a host copy of that cache (as in
@@ -65,3 +68,18 @@ def test_decode_head_layout_bf16(hd, nq, nkv, paged):
     w = cbinputs.model_weights(shape, seed)
     kvs = cbinputs.synthetic_chunk_kv(shape, wl.chunk_lens, seed)
     _blend_then_decode(shape, wl, w, kvs, 2, paged, 2e-2, f"hd{hd} G{nq // nkv}", seed)
+
+
+@pytest.mark.parametrize("nq,nkv", [(4, 2), (8, 2)], ids=["G2", "G4"])
+def test_blend_gqa_fp32(nq, nkv):
+    # the fp32 path's attention (one wave per query row and head) with shared KV heads
+    shape = cbinputs.ModelShape(f"f32-q{nq}-kv{nkv}", 2, 256, nq, nkv, 64, 512, 1000, 10000.0, dtype="f32")
+    seed = 60 + nq
+    wl = cbinputs.make_workload("8b-4x1024-q64", seed=seed, shape=shape, chunk_len=80, n_query=6)
+    m, kvs = _oracle_setup(shape, wl, seed)
+    ks, ch = wl.schedule()
+    label = f"fp32, G {nq // nkv}"
+    say(f"{label}: N {wl.n_ctx}, Q {wl.n_query}, k {ks[1:]}")
+    g = _run_blend(shape, wl, kvs, ks, ch, paged=True, paged_src=True, seed=seed)
+    _compare(shape, wl, g, _oracle_ref(m, wl, kvs, ks, ch, g), ks, 1e-4, label)
+

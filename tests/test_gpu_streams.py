@@ -1,7 +1,10 @@
 """Two blended prefills in flight at once on two streams, each with its own
 workspace, caches and outputs, give bitwise the results of the same calls run
 one after the other: the library keeps no state between calls and launches
-nothing outside the stream it is given (the C ABI's ownership rule)."""
+nothing outside the stream it is given (the C ABI's ownership rule).  And the
+workspace's prior contents do not matter: a blend and two decode steps give the
+same bits with the workspace filled with zeros and with 0xFF bytes (NaN floats,
+-1 integers)."""
 import pytest
 import torch
 
@@ -23,6 +26,10 @@ class _Case:
         self.chunks = device_chunks(MINI8B, self.wl, kvs, paged_src=paged, seed=seed)
         self.paged, self.seed = paged, seed
         wl = self.wl
+        # inputs stay alive until every call's stream has finished (the caller owns them):
+        # a temporary freed at return could be handed to the other stream's next call
+        # while this stream's kernels still read it
+        self.q = ints(wl.query_tokens)
         self.ws = api.Workspace(api.cb_workspace_bytes(self.model.cfg, wl.n_ctx, wl.n_query, len(self.chunks)))
 
     def outputs(self):
@@ -36,7 +43,7 @@ class _Case:
     def run(self, out, stream=None):
         kv, logits, hk, dv = out
         ks, ch = self.wl.schedule()
-        api.cb_blend_prefill(self.model, self.chunks, ints(self.wl.query_tokens), api.BlendParams(ks, ch), kv,
+        api.cb_blend_prefill(self.model, self.chunks, self.q, api.BlendParams(ks, ch), kv,
                              logits, hk, dv, ws=self.ws, stream=stream)
 
     def result(self, out):
@@ -67,3 +74,31 @@ def test_two_streams_equal_sequential_runs():
         for name, a, b in zip(names, c.result(out), ref[i]):
             assert torch.equal(a, b), f"case {i}: {name} differs from the sequential run"
         say(f"  case {i}: every output bitwise equal to the sequential run")
+
+
+def test_workspace_contents_do_not_matter():
+    say("a mini-8B blend and two decode steps with the workspaces filled with 0x00, then 0xFF")
+    c = _Case(3, 0.15, True)
+    dws = api.Workspace(api.cb_decode_workspace_bytes(c.model.cfg))
+    wl = c.wl
+    res = []
+    for fill in (0x00, 0xFF):
+        c.ws.t.fill_(fill)
+        dws.t.fill_(fill)
+        kv = blended_cache(MINI8B, wl.n_total + 2, paged=True, seed=3, fill=0.0)
+        logits = torch.empty(MINI8B.vocab, device="cuda")
+        hk = torch.full((MINI8B.n_layers, wl.n_ctx), -1, dtype=torch.int32, device="cuda")
+        dv = torch.full((MINI8B.n_layers, wl.n_ctx), -1.0, device="cuda")
+        c.run((kv, logits, hk, dv))
+        outs = [logits.clone(), hk.clone(), dv.clone()]
+        for i, tok in enumerate((17, 4242)):
+            api.cb_decode_step(c.model, kv, wl.n_total + i, ints([tok]), logits, dws)
+            outs.append(logits.clone())
+        torch.cuda.synchronize()
+        K, V = kv.logical(wl.n_total + 2)
+        res.append([K, V] + outs)
+    names = ["K", "V", "logits", "hkvd", "dev", "decode logits 0", "decode logits 1"]
+    for name, a, b in zip(names, res[0], res[1]):
+        assert torch.equal(a, b), f"{name} depends on the workspace's prior contents"
+    say("  every output bitwise the same with either fill")
+

@@ -3,7 +3,9 @@ the chunk caches in page-locked host memory, fed one layer at a time on a copy
 stream, every output must be bitwise the one cb_blend_prefill produces from
 the same caches on the device; on the tiny fp32 decoder it is also compared
 with the oracle.  Models with more layers than ring slots (3) exercise the
-slot reuse and its waits."""
+slot reuse and its waits; two calls enqueued back to back on one stream with
+one workspace exercise the wait of a call's first copies for the previous
+call's use of the ring."""
 import numpy as np
 import pytest
 import torch
@@ -101,3 +103,48 @@ def test_streamed_equals_device_prefill_full_8b():
     ks, ch = wl.schedule()
     a, b = _both(shape, m, chunks, wl, ks, ch, True, 0)
     _assert_same(a, b, "8B")
+
+
+def test_streamed_back_to_back_shared_workspace():
+    say("streamed prefill: two mini-8B calls back to back on a side stream, one workspace, one copy stream")
+    m = api.DeviceModel.from_numpy(MINI8B, cbinputs.model_weights(MINI8B, 21))
+    cases = []
+    for seed in (21, 22):
+        wl = cbinputs.make_workload("8b-4x1024-q64", seed=seed, shape=MINI8B, chunk_len=128, n_query=16)
+        kvs = cbinputs.synthetic_chunk_kv(MINI8B, wl.chunk_lens, seed)
+        chunks = device_chunks(MINI8B, wl, kvs)
+        cases.append((wl, chunks, _host_chunks(chunks), ints(wl.query_tokens)))
+    wl0 = cases[0][0]
+    need = api.cb_streamed_workspace_bytes(m.cfg, wl0.n_ctx, wl0.n_query, len(cases[0][1]))
+    ws = api.Workspace(need)
+
+    def outputs(wl):
+        kv = blended_cache(MINI8B, wl.n_total, paged=True, seed=5, fill=0.0)
+        return (kv, torch.empty(MINI8B.vocab, device="cuda"),
+                torch.full((MINI8B.n_layers, wl.n_ctx), -1, dtype=torch.int32, device="cuda"),
+                torch.full((MINI8B.n_layers, wl.n_ctx), -1.0, device="cuda"))
+
+    refs = []
+    for wl, chunks, _, q in cases:
+        kv, lg, hk, dv = outputs(wl)
+        ks, ch = wl.schedule()
+        api.cb_blend_prefill(m, chunks, q, api.BlendParams(ks, ch), kv, lg, hk, dv)
+        torch.cuda.synchronize()
+        K, V = kv.logical(wl.n_total)
+        refs.append((K.clone(), V.clone(), lg.clone(), hk.clone(), dv.clone()))
+    outs = [outputs(wl) for wl, _, _, _ in cases]
+    s, cs = torch.cuda.Stream(), torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    keep = []
+    for (wl, _, host, q), (kv, lg, hk, dv) in zip(cases, outs):
+        ks, ch = wl.schedule()
+        keep.append(api.cb_blend_prefill_streamed(m, host, q, api.BlendParams(ks, ch), kv, lg, hk, dv, ws=ws,
+                                                  stream=s, copy_stream=cs))
+    torch.cuda.synchronize()
+    del keep
+    for i, ((wl, _, _, _), (kv, lg, hk, dv), ref) in enumerate(zip(cases, outs, refs)):
+        K, V = kv.logical(wl.n_total)
+        for name, a, b in zip(("K", "V", "logits", "hkvd", "dev"), (K, V, lg, hk, dv), ref):
+            assert torch.equal(a, b), f"call {i}: {name} differs from the device prefill"
+        say(f"  call {i}: streamed == device prefill, bitwise")
+
